@@ -1,0 +1,203 @@
+/*
+ * kamera.h — C ABI of libkamera.so, the Kamera KV reuse operator for AMD MI355X (gfx950).
+ *
+ * The operator (technical summary of "Kamera: Unified Position-Invariant Multimodal KV Cache
+ * for Training-Free Reuse", §2 Methodology, the reuse equation):
+ *
+ *     KV^(B|A) = R(delta) . KV(B|empty) + U_m V_m^T
+ *
+ *   - KV(B|empty) is a chunk's canonical, position-free KV: keys carry RoPE at chunk-local
+ *     positions 0..n_tokens-1, so one shift delta moves every token of the chunk.
+ *   - R(delta) is the exact RoPE phase shift of the keys to the new position (same section:
+ *     relocation is an algebraic rotation, not a forward pass). Values are not rotated.
+ *   - U_m V_m^T is the rank-m conditioning patch (same section, "Rank-m Conditioning Patch"),
+ *     added after the rotation, in the target frame, to both channels.
+ *   - GQA and MHA rotate the whole key; MLA rotates only the 64-dim k_rope and reuses c_KV
+ *     unchanged (same section, "Unified Architecture Support"; the Irminsul abstract on the
+ *     authors' publication page gives the same delta-rotation rule for k_r).
+ *
+ * Channels. Every model has two channels:
+ *   channel 0 (KAMERA_CH_ROT)   GQA/MHA keys, or MLA k_rope: rotated by R(delta), then patched;
+ *   channel 1 (KAMERA_CH_PLAIN) GQA/MHA values, or MLA c_KV: not rotated, then patched. With
+ *                               m = 0 this channel is moved bit for bit (integer copy).
+ *
+ * Element types. KAMERA_DTYPE_F32 or KAMERA_DTYPE_BF16; canonical KV, patch factors and the
+ * cache all use the model's type. Arithmetic is fp32; cos/sin(delta*theta_i) are formed in
+ * fp64 on the device and rounded to fp32 once; the result is rounded once (RNE) on store.
+ *
+ * Memory. Every tensor pointer in these structs is device memory owned by the caller. The
+ * structs themselves and the chunk array are host memory, read only during the call. The
+ * library never allocates device memory: the caller passes a workspace of at least
+ * kamera_workspace_bytes(n_chunks) bytes (device memory, 256-byte aligned).
+ *
+ * Streams. The compute calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
+ * and return without synchronising. A device fault surfaces at the caller's next sync. The
+ * workspace must not be reused by another call until this call's work has finished on the
+ * stream (calls on one stream serialise by themselves).
+ *
+ * Errors. Compute calls validate every argument on the host before anything is enqueued; on
+ * any error they return a status != KAMERA_OK, enqueue nothing, and set a per-thread message
+ * readable with kamera_last_error(). No C++ exception crosses this ABI.
+ *
+ * Thread safety. Calls are reentrant; the only mutable global state is the per-thread error
+ * message.
+ */
+#ifndef KAMERA_H_
+#define KAMERA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KAMERA_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+typedef enum kamera_status {
+  KAMERA_OK = 0,
+  KAMERA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent geometry */
+  KAMERA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (dtype, head width, m > 256) */
+  KAMERA_ERR_OVERLAP = 3,          /* a chunk's source range overlaps the destination pool */
+  KAMERA_ERR_WORKSPACE = 4,        /* workspace missing, misaligned or too small */
+  KAMERA_ERR_HIP = 5               /* a HIP runtime call failed (message holds its text) */
+} kamera_status;
+
+typedef enum kamera_family {
+  KAMERA_FAMILY_GQA = 0, /* GQA and MHA (MHA is GQA with n_kv_heads == n_q_heads) */
+  KAMERA_FAMILY_MLA = 1  /* latent c_KV (head_dim wide) + decoupled k_rope (rope_dim wide) */
+} kamera_family;
+
+typedef enum kamera_dtype { KAMERA_DTYPE_F32 = 0, KAMERA_DTYPE_BF16 = 1 } kamera_dtype;
+
+/* Which features form a RoPE pair. HALF_SPLIT: (i, i + rot/2). INTERLEAVED: (2i, 2i + 1).
+ * Pair i turns by angle delta * theta^(-2i/rot); a pair (x, y) becomes
+ * (x cos - y sin, y cos + x sin); positive delta moves the chunk later. */
+typedef enum kamera_rope_layout {
+  KAMERA_ROPE_HALF_SPLIT = 0,
+  KAMERA_ROPE_INTERLEAVED = 1
+} kamera_rope_layout;
+
+enum { KAMERA_CH_ROT = 0, KAMERA_CH_PLAIN = 1, KAMERA_N_CHANNELS = 2 };
+
+#define KAMERA_MAX_RANK 256
+
+/* Model geometry.
+ *   GQA/MHA: n_kv_heads heads per channel, each head_dim wide; rope_dim must equal head_dim
+ *            (the whole key rotates). Supported head_dim: 64 or 128 (bf16 MFMA path), any even
+ *            value <= 512 on the fp32 path.
+ *   MLA:     n_kv_heads must be 1; channel 1 (c_KV) is head_dim wide (kv_lora_rank, e.g. 512),
+ *            channel 0 (k_rope) is rope_dim wide (e.g. 64). */
+typedef struct kamera_model {
+  int32_t family;      /* kamera_family */
+  int32_t dtype;       /* kamera_dtype */
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t rope_dim;
+  int32_t rope_layout; /* kamera_rope_layout */
+  int32_t reserved0;
+  double rope_theta;   /* RoPE base, > 1 and finite */
+} kamera_model;
+
+/* Paged destination cache, one pool per channel (for MLA both pools may live in one
+ * allocation: pool[1] = rows base (c_KV), pool[0] = rows base + head_dim (k_rope)).
+ * Element (layer l, physical page P, slot s, head h, feature f) of channel c is at
+ *     pool[c] + l*layer_stride + (P*page_size + s)*token_stride + h*width_c + f
+ * (in elements), width_c = head_dim, or rope_dim for MLA channel 0.
+ * Logical token p of the cache lives in physical page page_table[p / page_size], slot
+ * p % page_size. page_table == NULL means the identity table (a dense cache).
+ * Table entries outside [0, n_pages) are never written through: the rows they address are
+ * skipped and counted (kamera_read_fault_count). */
+typedef struct kamera_cache {
+  void* pool[2];
+  int64_t layer_stride;       /* elements */
+  int64_t token_stride;       /* elements between consecutive slots */
+  const int32_t* page_table;  /* device memory, n_logical_pages entries, or NULL */
+  int32_t n_logical_pages;    /* logical pages addressable through the table */
+  int32_t page_size;          /* tokens per page, > 0 */
+  int32_t n_pages;            /* physical pages per layer in each pool */
+  int32_t reserved0;
+} kamera_cache;
+
+/* Canonical rows of one chunk, one channel. Element (layer l, token t, head h, feature f) is at
+ *     ptr + l*layer_stride + t*token_stride + h*width_c + f   (elements). */
+typedef struct kamera_src {
+  const void* ptr;
+  int64_t layer_stride;
+  int64_t token_stride;
+} kamera_src;
+
+/* Rank-m patch of one chunk, one channel: per layer and head, U (n_tokens x m) and
+ * V (width_c x m), both with rows m-contiguous:
+ *     U(l, h, t, r) at U + l*u_layer_stride + h*u_head_stride + t*m + r
+ *     V(l, h, f, r) at V + l*v_layer_stride + h*v_head_stride + f*m + r
+ * The patch adds sum_r U(l,h,t,r) * V(l,h,f,r) to output element (l, t, h, f).
+ * m = 0 means no patch (U and V are then ignored and may be NULL). */
+typedef struct kamera_patch_ref {
+  int32_t m;
+  int32_t reserved0;
+  const void* U;
+  int64_t u_layer_stride;
+  int64_t u_head_stride;
+  const void* V;
+  int64_t v_layer_stride;
+  int64_t v_head_stride;
+} kamera_patch_ref;
+
+/* One chunk: its canonical source, the shift, where it lands and its patch per channel. */
+typedef struct kamera_chunk {
+  int32_t n_tokens;          /* >= 0; 0 is a no-op */
+  int32_t dst_token_offset;  /* logical cache token of the chunk's token 0, >= 0 */
+  int64_t delta;             /* target position minus canonical position, |delta| < 2^31 */
+  kamera_src src[2];         /* per channel */
+  kamera_patch_ref patch[2]; /* per channel */
+} kamera_chunk;
+
+/* Bytes of workspace the compute calls need for n_chunks chunks (0 if n_chunks < 0). */
+size_t kamera_workspace_bytes(int32_t n_chunks);
+
+/* The reuse operator (reuse equation above) for every chunk, both channels, all layers:
+ *     dst(l, p, h, :) = R(delta) src(l, t, h, :) + U V^T   with p = dst_token_offset + t.
+ * Serves reuse, reorder (same patch, another delta), sliding-window survival (m = 0) and
+ * recall (a fresh patch) — the three window operations of §3 — in one launch, whatever mix of
+ * delta and m the chunks carry. Chunks must not write the same cache token (results would
+ * race). src must not overlap the destination pools (KAMERA_ERR_OVERLAP). */
+kamera_status kamera_reuse_batch(const kamera_model* model, const kamera_cache* cache,
+                                 const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Relocation only, R(delta) with no patch (patch fields are ignored). Bit-identical to
+ * kamera_reuse_batch with every m set to 0; channel 1 is then an exact bit copy. */
+kamera_status kamera_relocate(const kamera_model* model, const kamera_cache* cache,
+                              const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Patch only, in place on the destination: dst = round(dst + U V^T). src, delta are ignored.
+ * kamera_relocate then kamera_patch may differ from the fused kamera_reuse_batch by one
+ * rounding of the intermediate (one ulp of the element type). */
+kamera_status kamera_patch(const kamera_model* model, const kamera_cache* cache,
+                           const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Rows skipped since the workspace was last set up because their page-table entry was outside
+ * [0, n_pages). Synchronises `stream`. Returns KAMERA_ERR_INVALID_ARGUMENT on NULL args. */
+kamera_status kamera_read_fault_count(const void* workspace, void* stream, uint32_t* count);
+
+/* Bytes of one chunk's patch factors (U and V, both channels, all layers and heads) for a
+ * chunk of n_tokens tokens at rank m, in the model's element type; 0 on invalid input.
+ * Patch-footprint helper (technical summary §4, "Efficiency: Memory"). */
+size_t kamera_patch_bytes(const kamera_model* model, int32_t n_tokens, int32_t m);
+
+/* Bytes of one chunk's canonical KV (both channels, all layers); 0 on invalid input. */
+size_t kamera_kv_bytes(const kamera_model* model, int32_t n_tokens);
+
+const char* kamera_status_string(kamera_status status);
+const char* kamera_last_error(void); /* per-thread; "" if none */
+int32_t kamera_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAMERA_H_ */
