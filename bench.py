@@ -1,0 +1,236 @@
+"""Benchmark of the Kamera reuse operator on one MI355X.
+
+One step = one kamera_reuse_batch call over the whole batch: work decomposition, fp64 phase
+generation, streaming of the canonical KV, rotation, the rank-m patch, and the page-table
+scatter, for every chunk, layer, channel and head. Inputs are resident in HBM before timing.
+
+Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s).
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+DEFAULT_WORKLOAD = "qwen25vl_gqa_bf16"
+METRIC = "relocated+patched KV tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
+KERNEL_SOURCES = ["position_invariant_kv_kamera_amd/csrc/kamera_kernels.hip",
+                  "position_invariant_kv_kamera_amd/csrc/kamera_api.cpp",
+                  "position_invariant_kv_kamera_amd/csrc/kamera_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(p) -> dict:
+    """What the method itself must move: canonical KV read once, output written once, patch
+    factors read once, page table read once."""
+    es = p.elem_bytes
+    kv = 0
+    patch = 0
+    for c, L in enumerate(p.chunk_tokens):
+        for ch, m in ((0, p.m_rot[c]), (1, p.m_plain[c])):
+            H, W = p.heads(ch), p.width(ch)
+            kv += p.n_layers * L * H * W * es
+            patch += p.n_layers * H * (L + W) * m * es
+    table = 0 if p.page_table is None else p.page_table.size * 4
+    return {"read_kv": kv, "write_kv": kv, "patch": patch, "page_table": table,
+            "total": 2 * kv + patch + table}
+
+
+def patch_flops(p) -> float:
+    f = 0.0
+    for c, L in enumerate(p.chunk_tokens):
+        for ch, m in ((0, p.m_rot[c]), (1, p.m_plain[c])):
+            f += 2.0 * m * p.n_layers * L * p.heads(ch) * p.width(ch)
+    return f
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources."""
+    f = ROOT / "profiles" / f"traffic_{workload}.json"
+    if not f.exists():
+        return None, None
+    d = json.loads(f.read_text())
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None, "stale"
+    return d.get("traffic_bytes"), d.get("kernel")
+
+
+def cpu_baseline(batch, budget_s: float) -> dict:
+    """The oracle, as it is, on the first chunks of the same batch (all layers, channels and
+    heads) until about `budget_s` seconds of CPU work, scaled to tokens/s."""
+    import numpy as np
+    import torch
+    import oracle
+
+    p = batch.plan
+    layout = 0 if p.rope_layout == "half_split" else 1
+
+    def host(t):
+        t = t.detach().contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    busy = 0.0
+    tokens = 0
+    chunks = 0
+    for c in range(p.n_chunks):
+        ct = batch.chunks[c]
+        srcs = [host(ct.src[ch]) for ch in range(2)]
+        Us = [host(ct.U[ch]) if ct.U[ch] is not None else None for ch in range(2)]
+        Vs = [host(ct.V[ch]) if ct.V[ch] is not None else None for ch in range(2)]
+        t0 = time.perf_counter()
+        for l in range(p.n_layers):
+            for ch in range(2):
+                W = p.width(ch)
+                for h in range(p.heads(ch)):
+                    x = np.ascontiguousarray(srcs[ch][l][:, h * W:(h + 1) * W])
+                    U = None if Us[ch] is None else Us[ch][l, h]
+                    V = None if Vs[ch] is None else Vs[ch][l, h]
+                    e = oracle.expected_head(x, rotate=(ch == 0), layout=layout,
+                                             delta=p.deltas[c], theta=p.theta, U=U, V=V)
+                    if not e["copy"]:
+                        oracle.to_bf16(e["z"]) if p.dtype == "bf16" else oracle.to_f32(e["z"])
+        busy += time.perf_counter() - t0
+        tokens += p.chunk_tokens[c]
+        chunks += 1
+        if busy >= budget_s:
+            break
+    return {"value": tokens / busy, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"first {chunks} of {p.n_chunks} chunks ({tokens} tokens x {p.n_layers} "
+                      f"layers x 2 channels), {busy:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the operator has no cross-GPU step and this "
+              "build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+    from position_invariant_kv_kamera_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kb.load_library()   # raises if the HIP library is missing
+
+    p = wl.plan(args.workload)
+    print(f"[bench] materializing {args.workload} on cuda:0", file=sys.stderr, flush=True)
+    batch = wl.materialize(p, "cuda")
+    ws = kb.Workspace(p.n_chunks)
+    model, cache, chunks = kb.model_of(p), kb.cache_of(batch), kb.chunks_of(batch)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step():
+        kb.check(kb.kamera_reuse_batch(model, cache, chunks, p.n_chunks, ws.ptr, ws.nbytes, sptr))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ev_avg = sum(ev_ms) / len(ev_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    ab = algorithmic_bytes(p)
+    gbps = ab["total"] / (ev_avg * 1e-3) / 1e9
+    tokens = p.total_tokens
+    value = tokens / (ms_per_step * 1e-3)
+
+    # measured device-to-device copy ceiling (read + write), for context
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(buf)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, dst
+
+    traffic, tinfo = traffic_from_profile(args.workload)
+    flops = patch_flops(p)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "family": p.family, "layers": p.n_layers,
+                   "kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rope_dim": p.rope_dim,
+                   "rope_layout": p.rope_layout, "chunks": p.n_chunks,
+                   "chunk_tokens": p.chunk_tokens[0], "rank": max(p.m_rot + p.m_plain),
+                   "cache": "dense" if p.page_table is None else f"paged{p.page_size}",
+                   "parallelism": "none (1 GPU)"},
+        "achieved_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
+        "kernel_ms": {"mean": round(ev_avg, 4), "p10": round(ev_ms[len(ev_ms) // 10], 4),
+                      "p50": round(ev_ms[len(ev_ms) // 2], 4),
+                      "p90": round(ev_ms[(9 * len(ev_ms)) // 10], 4)},
+        "mfma_util": round(flops / (ev_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab["total"],
+                     "kernel": "kamera_mfma_kernel", "timed_with": "hip events on the launch stream"},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if tinfo == "stale":
+        out["roofline"]["traffic_note"] = "counters were taken on older kernel sources"
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

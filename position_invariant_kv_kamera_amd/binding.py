@@ -1,0 +1,239 @@
+"""ctypes binding of libkamera.so (include/kamera.h): argument marshalling only.
+
+The functions keep the C names. Every step of the operator runs in the library's HIP kernels;
+PyTorch is used only for device memory and streams. If libkamera.so is missing this module
+raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libkamera.so"
+HEADER = PKG.parent / "include" / "kamera.h"
+
+KAMERA_OK = 0
+KAMERA_ERR_INVALID_ARGUMENT = 1
+KAMERA_ERR_UNSUPPORTED = 2
+KAMERA_ERR_OVERLAP = 3
+KAMERA_ERR_WORKSPACE = 4
+KAMERA_ERR_HIP = 5
+
+FAMILY = {"gqa": 0, "mla": 1}
+DTYPE = {"f32": 0, "bf16": 1}
+LAYOUT = {"half_split": 0, "interleaved": 1}
+MAX_RANK = 256
+
+c_i32, c_i64, c_dbl, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                                      ctypes.c_void_p, ctypes.c_size_t)
+
+
+class KameraModel(ctypes.Structure):
+    _fields_ = [("family", c_i32), ("dtype", c_i32), ("n_layers", c_i32), ("n_kv_heads", c_i32),
+                ("head_dim", c_i32), ("rope_dim", c_i32), ("rope_layout", c_i32),
+                ("reserved0", c_i32), ("rope_theta", c_dbl)]
+
+
+class KameraCache(ctypes.Structure):
+    _fields_ = [("pool", c_vp * 2), ("layer_stride", c_i64), ("token_stride", c_i64),
+                ("page_table", c_vp), ("n_logical_pages", c_i32), ("page_size", c_i32),
+                ("n_pages", c_i32), ("reserved0", c_i32)]
+
+
+class KameraSrc(ctypes.Structure):
+    _fields_ = [("ptr", c_vp), ("layer_stride", c_i64), ("token_stride", c_i64)]
+
+
+class KameraPatchRef(ctypes.Structure):
+    _fields_ = [("m", c_i32), ("reserved0", c_i32), ("U", c_vp), ("u_layer_stride", c_i64),
+                ("u_head_stride", c_i64), ("V", c_vp), ("v_layer_stride", c_i64),
+                ("v_head_stride", c_i64)]
+
+
+class KameraChunk(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i32), ("dst_token_offset", c_i32), ("delta", c_i64),
+                ("src", KameraSrc * 2), ("patch", KameraPatchRef * 2)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkamera.so from the package directory; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m position_invariant_kv_kamera_amd.build` (there is no "
+                           "fallback path)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    compute = [ctypes.POINTER(KameraModel), ctypes.POINTER(KameraCache),
+               ctypes.POINTER(KameraChunk), c_i32, c_vp, c_size, c_vp]
+    for name in ("kamera_reuse_batch", "kamera_relocate", "kamera_patch"):
+        fn = getattr(lib, name)
+        fn.argtypes = compute
+        fn.restype = ctypes.c_int
+    lib.kamera_workspace_bytes.argtypes = [c_i32]
+    lib.kamera_workspace_bytes.restype = c_size
+    lib.kamera_read_fault_count.argtypes = [c_vp, c_vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.kamera_read_fault_count.restype = ctypes.c_int
+    lib.kamera_patch_bytes.argtypes = [ctypes.POINTER(KameraModel), c_i32, c_i32]
+    lib.kamera_patch_bytes.restype = c_size
+    lib.kamera_kv_bytes.argtypes = [ctypes.POINTER(KameraModel), c_i32]
+    lib.kamera_kv_bytes.restype = c_size
+    lib.kamera_status_string.argtypes = [ctypes.c_int]
+    lib.kamera_status_string.restype = ctypes.c_char_p
+    lib.kamera_last_error.argtypes = []
+    lib.kamera_last_error.restype = ctypes.c_char_p
+    lib.kamera_version.argtypes = []
+    lib.kamera_version.restype = c_i32
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/kamera.h declares."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kamera_[a-z_]+)\s*\(",
+                                 text, re.M)))
+
+
+class KameraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kamera status {status}: {message}")
+        self.status = status
+
+
+# ---- the C calls, same names -----------------------------------------------------------
+
+def kamera_workspace_bytes(n_chunks: int) -> int:
+    return int(load_library().kamera_workspace_bytes(n_chunks))
+
+
+def _compute(name, model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):
+    fn = getattr(load_library(), name)
+    return int(fn(ctypes.byref(model) if model is not None else None,
+                  ctypes.byref(cache) if cache is not None else None,
+                  chunks, int(n_chunks), workspace, int(workspace_bytes), stream))
+
+
+def kamera_reuse_batch(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):
+    return _compute("kamera_reuse_batch", model, cache, chunks, n_chunks, workspace,
+                    workspace_bytes, stream)
+
+
+def kamera_relocate(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):
+    return _compute("kamera_relocate", model, cache, chunks, n_chunks, workspace,
+                    workspace_bytes, stream)
+
+
+def kamera_patch(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):
+    return _compute("kamera_patch", model, cache, chunks, n_chunks, workspace,
+                    workspace_bytes, stream)
+
+
+def kamera_read_fault_count(workspace, stream) -> tuple[int, int]:
+    out = ctypes.c_uint32(0)
+    st = int(load_library().kamera_read_fault_count(workspace, stream, ctypes.byref(out)))
+    return st, int(out.value)
+
+
+def kamera_patch_bytes(model, n_tokens, m) -> int:
+    return int(load_library().kamera_patch_bytes(ctypes.byref(model), n_tokens, m))
+
+
+def kamera_kv_bytes(model, n_tokens) -> int:
+    return int(load_library().kamera_kv_bytes(ctypes.byref(model), n_tokens))
+
+
+def kamera_status_string(status: int) -> str:
+    return load_library().kamera_status_string(status).decode()
+
+
+def kamera_last_error() -> str:
+    return load_library().kamera_last_error().decode()
+
+
+def kamera_version() -> int:
+    return int(load_library().kamera_version())
+
+
+# ---- marshalling of torch tensors (workloads.Batch) into descriptors --------------------
+
+def model_of(plan) -> KameraModel:
+    return KameraModel(FAMILY[plan.family], DTYPE[plan.dtype], plan.n_layers, plan.n_kv_heads,
+                       plan.head_dim, plan.rope_dim, LAYOUT[plan.rope_layout], 0,
+                       float(plan.theta))
+
+
+def cache_of(batch) -> KameraCache:
+    p = batch.plan
+    pools = batch.pools
+    c = KameraCache()
+    c.pool[0] = pools[0].data_ptr()
+    c.pool[1] = pools[1].data_ptr()
+    c.layer_stride = pools[0].stride(0)
+    c.token_stride = pools[0].stride(2)
+    c.page_table = None if batch.page_table is None else batch.page_table.data_ptr()
+    c.n_logical_pages = p.n_logical_pages
+    c.page_size = p.page_size
+    c.n_pages = p.n_pages
+    return c
+
+
+def chunks_of(batch, m_override: int | None = None):
+    """One KameraChunk per chunk of the batch (ctypes array)."""
+    p = batch.plan
+    arr = (KameraChunk * max(1, p.n_chunks))()
+    for c, ct in enumerate(batch.chunks):
+        k = arr[c]
+        k.n_tokens = p.chunk_tokens[c]
+        k.dst_token_offset = p.dst_offsets[c]
+        k.delta = p.deltas[c]
+        for ch in range(2):
+            s = ct.src[ch]
+            k.src[ch] = KameraSrc(s.data_ptr(), s.stride(0), s.stride(1))
+            U, V = ct.U[ch], ct.V[ch]
+            if U is not None and m_override != 0:
+                k.patch[ch] = KameraPatchRef(U.shape[-1], 0, U.data_ptr(), U.stride(0),
+                                             U.stride(1), V.data_ptr(), V.stride(0), V.stride(1))
+            else:
+                k.patch[ch] = KameraPatchRef()
+    return arr
+
+
+class Workspace:
+    """Device workspace for up to `n_chunks` chunks (torch uint8 tensor, 256-byte aligned)."""
+
+    def __init__(self, n_chunks: int, device="cuda"):
+        import torch
+        self.nbytes = kamera_workspace_bytes(n_chunks)
+        self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        base = self._buf.data_ptr()
+        self.ptr = (base + 255) // 256 * 256
+
+
+def current_stream_ptr():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def check(status: int):
+    if status != KAMERA_OK:
+        raise KameraError(status, f"{kamera_status_string(status)}: {kamera_last_error()}")
+
+
+def run_batch(op: str, batch, workspace: Workspace | None = None, stream=None, *,
+              m_override: int | None = None):
+    """Describe `batch` and run one of "reuse", "relocate", "patch" on it (asynchronous)."""
+    model = model_of(batch.plan)
+    cache = cache_of(batch)
+    chunks = chunks_of(batch, m_override)
+    ws = workspace or Workspace(batch.plan.n_chunks)
+    s = current_stream_ptr() if stream is None else stream
+    fn = {"reuse": kamera_reuse_batch, "relocate": kamera_relocate, "patch": kamera_patch}[op]
+    check(fn(model, cache, chunks, batch.plan.n_chunks, ws.ptr, ws.nbytes, s))
+    return ws

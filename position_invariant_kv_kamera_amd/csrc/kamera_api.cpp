@@ -1,0 +1,543 @@
+// kamera_api.cpp — host runtime behind include/kamera.h: argument validation, work packing
+// and kernel launch. Every check runs before the first HIP call, so a rejected call has no
+// side effect on the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kamera.h"
+#include "kamera_internal.h"
+
+using kamera::JobDesc;
+using kamera::LaunchParams;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kamera_status fail(kamera_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t kHeaderBytes = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Geometry of one channel: heads and features per head.
+struct Channel {
+  int32_t heads;
+  int32_t width;
+  bool rotate;
+};
+
+Channel channel_of(const kamera_model& m, int c) {
+  if (m.family == KAMERA_FAMILY_MLA)
+    return c == KAMERA_CH_ROT ? Channel{1, m.rope_dim, true} : Channel{1, m.head_dim, false};
+  return Channel{m.n_kv_heads, m.head_dim, c == KAMERA_CH_ROT};
+}
+
+// Byte range [lo, hi) touched by a (layer, token, row) view.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range view_range(const void* p, int64_t ls, int64_t n_layers, int64_t ts, int64_t n_tokens,
+                 int64_t row_elems, int64_t esize) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  const int64_t last = (n_layers - 1) * ls + (n_tokens - 1) * ts + row_elems;
+  return Range{b, b + static_cast<uintptr_t>(last * esize)};
+}
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+kamera_status validate_model(const kamera_model* m) {
+  if (!m) return fail(KAMERA_ERR_INVALID_ARGUMENT, "model is NULL");
+  if (m->family != KAMERA_FAMILY_GQA && m->family != KAMERA_FAMILY_MLA)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "unknown model family %d", m->family);
+  if (m->dtype != KAMERA_DTYPE_F32 && m->dtype != KAMERA_DTYPE_BF16)
+    return fail(KAMERA_ERR_UNSUPPORTED, "unsupported dtype %d", m->dtype);
+  if (m->n_layers <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_layers must be > 0");
+  if (m->rope_layout != KAMERA_ROPE_HALF_SPLIT && m->rope_layout != KAMERA_ROPE_INTERLEAVED)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "unknown rope_layout %d", m->rope_layout);
+  if (!std::isfinite(m->rope_theta) || !(m->rope_theta > 1.0))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 1");
+  if (m->head_dim <= 0 || m->head_dim % 2)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "head_dim must be even and > 0 (got %d)",
+                m->head_dim);
+  if (m->rope_dim <= 0 || m->rope_dim % 2)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_dim must be even and > 0 (got %d)",
+                m->rope_dim);
+  if (m->rope_dim > 2 * kamera::kMaxPairs)
+    return fail(KAMERA_ERR_UNSUPPORTED, "rope_dim %d exceeds %d", m->rope_dim,
+                2 * kamera::kMaxPairs);
+  if (m->family == KAMERA_FAMILY_GQA) {
+    if (m->n_kv_heads <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_kv_heads must be > 0");
+    if (m->rope_dim != m->head_dim)
+      return fail(KAMERA_ERR_UNSUPPORTED,
+                  "GQA/MHA rotate the whole head: rope_dim (%d) must equal head_dim (%d)",
+                  m->rope_dim, m->head_dim);
+  } else if (m->n_kv_heads != 1) {
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "MLA needs n_kv_heads == 1 (got %d)",
+                m->n_kv_heads);
+  }
+  return KAMERA_OK;
+}
+
+kamera_status validate_cache(const kamera_model& m, const kamera_cache* c) {
+  if (!c) return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->pool[0] || !c->pool[1]) return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache pool is NULL");
+  if (c->page_size <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "page_size must be > 0");
+  if (c->n_pages <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_pages must be > 0");
+  if (c->n_logical_pages <= 0)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_logical_pages must be > 0");
+  if (!c->page_table && c->n_logical_pages > c->n_pages)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                "identity page table needs n_logical_pages (%d) <= n_pages (%d)",
+                c->n_logical_pages, c->n_pages);
+  if ((int64_t)c->n_logical_pages * c->page_size > INT32_MAX)
+    return fail(KAMERA_ERR_UNSUPPORTED, "cache holds more than 2^31-1 logical tokens");
+  if (c->token_stride <= 0 || c->layer_stride < 0)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache strides must be positive");
+  const int64_t slots = (int64_t)c->n_pages * c->page_size;
+  for (int ch = 0; ch < 2; ++ch) {
+    const Channel g = channel_of(m, ch);
+    if ((int64_t)g.heads * g.width > c->token_stride)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                  "cache token_stride (%lld) is shorter than channel %d's row (%d)",
+                  (long long)c->token_stride, ch, g.heads * g.width);
+  }
+  if (m.n_layers > 1 && c->layer_stride < slots * c->token_stride)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache layer_stride overlaps the next layer");
+  // the two channel pools may share rows (MLA), but must not write the same elements
+  const int64_t es = m.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  const Channel g0 = channel_of(m, 0), g1 = channel_of(m, 1);
+  const Range r0 = view_range(c->pool[0], c->layer_stride, m.n_layers, c->token_stride, slots,
+                              (int64_t)g0.heads * g0.width, es);
+  const Range r1 = view_range(c->pool[1], c->layer_stride, m.n_layers, c->token_stride, slots,
+                              (int64_t)g1.heads * g1.width, es);
+  if (overlaps(r0, r1)) {
+    const int64_t d = ((int64_t)reinterpret_cast<intptr_t>(c->pool[0]) -
+                       (int64_t)reinterpret_cast<intptr_t>(c->pool[1]));
+    const int64_t w0 = (int64_t)g0.heads * g0.width * es, w1 = (int64_t)g1.heads * g1.width * es;
+    const int64_t row = c->token_stride * es;
+    const bool disjoint_rows = (d >= w1 && d + w0 <= row) || (-d >= w0 && -d + w1 <= row);
+    if (!disjoint_rows)
+      return fail(KAMERA_ERR_OVERLAP, "the two channel pools write the same elements");
+  }
+  return KAMERA_OK;
+}
+
+enum class Op { Reuse, Relocate, Patch };
+
+kamera_status validate_chunks(const kamera_model& m, const kamera_cache& c,
+                              const kamera_chunk* chunks, int32_t n_chunks, Op op) {
+  if (n_chunks < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 0");
+  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
+  const int64_t es = m.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  const int64_t capacity = (int64_t)c.n_logical_pages * c.page_size;
+  const int64_t slots = (int64_t)c.n_pages * c.page_size;
+  Range pools[2];
+  for (int ch = 0; ch < 2; ++ch) {
+    const Channel g = channel_of(m, ch);
+    pools[ch] = view_range(c.pool[ch], c.layer_stride, m.n_layers, c.token_stride, slots,
+                           (int64_t)g.heads * g.width, es);
+  }
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  spans.reserve(n_chunks);
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_chunk& k = chunks[i];
+    if (k.n_tokens < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: n_tokens < 0", i);
+    if (k.n_tokens == 0) continue;
+    if (k.dst_token_offset < 0)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: dst_token_offset < 0", i);
+    if ((int64_t)k.dst_token_offset + k.n_tokens > capacity)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                  "chunk %d: tokens [%d, %lld) run past the cache's %lld logical tokens", i,
+                  k.dst_token_offset, (long long)k.dst_token_offset + k.n_tokens,
+                  (long long)capacity);
+    if (op != Op::Patch && (k.delta >= (int64_t(1) << 31) || k.delta <= -(int64_t(1) << 31)))
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
+    spans.emplace_back(k.dst_token_offset, (int64_t)k.dst_token_offset + k.n_tokens);
+    for (int ch = 0; ch < 2; ++ch) {
+      const Channel g = channel_of(m, ch);
+      const int64_t row = (int64_t)g.heads * g.width;
+      if (op != Op::Patch) {
+        const kamera_src& s = k.src[ch];
+        if (!s.ptr) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: src is NULL", i, ch);
+        if (s.layer_stride < 0 || s.token_stride < row)
+          return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                      "chunk %d channel %d: src token_stride %lld shorter than the row (%lld)",
+                      i, ch, (long long)s.token_stride, (long long)row);
+        const Range sr = view_range(s.ptr, s.layer_stride, m.n_layers, s.token_stride,
+                                    k.n_tokens, row, es);
+        if (overlaps(sr, pools[0]) || overlaps(sr, pools[1]))
+          return fail(KAMERA_ERR_OVERLAP, "chunk %d channel %d: src overlaps the cache", i, ch);
+      }
+      const kamera_patch_ref& p = k.patch[ch];
+      if (op == Op::Relocate) continue;
+      if (p.m < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: m < 0", i, ch);
+      if (p.m > KAMERA_MAX_RANK)
+        return fail(KAMERA_ERR_UNSUPPORTED, "chunk %d channel %d: m = %d exceeds %d", i, ch,
+                    p.m, KAMERA_MAX_RANK);
+      if (p.m == 0) continue;
+      if (!p.U || !p.V)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: m > 0 but U or V is NULL",
+                    i, ch);
+      if (p.u_layer_stride < 0 || p.u_head_stride < 0 || p.v_layer_stride < 0 ||
+          p.v_head_stride < 0)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: negative patch stride", i, ch);
+      // U: layers x heads x (n_tokens x m); V: layers x heads x (width x m)
+      const Range ur = view_range(p.U, p.u_layer_stride, m.n_layers, p.u_head_stride, g.heads,
+                                  (int64_t)k.n_tokens * p.m, es);
+      const Range vr = view_range(p.V, p.v_layer_stride, m.n_layers, p.v_head_stride, g.heads,
+                                  (int64_t)g.width * p.m, es);
+      if (overlaps(ur, pools[0]) || overlaps(ur, pools[1]) || overlaps(vr, pools[0]) ||
+          overlaps(vr, pools[1]))
+        return fail(KAMERA_ERR_OVERLAP, "chunk %d channel %d: patch factors overlap the cache",
+                    i, ch);
+    }
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                  "two chunks write logical cache token %lld", (long long)spans[i].first);
+  return KAMERA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// pinned staging ring for the job table (host -> workspace copy)
+// ---------------------------------------------------------------------------------------
+
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+struct DeviceRing {
+  std::mutex mu;
+  StagingSlot slot[4];
+  unsigned next = 0;
+};
+
+DeviceRing* ring_for(int device) {
+  static DeviceRing rings[64];   // process lifetime; never torn down (no exit-time HIP calls)
+  return (device >= 0 && device < 64) ? &rings[device] : nullptr;
+}
+
+kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  DeviceRing* ring = ring_for(dev);
+  if (!ring) return fail(KAMERA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(ring->mu);
+  StagingSlot& s = ring->slot[ring->next++ % 4];
+  if (s.pending) {
+    e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    s.pending = false;
+  }
+  if (!s.done) {
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
+  if (s.cap < bytes.size()) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = round_up(bytes.size(), size_t(1) << 16);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipHostMalloc: %s", hipGetErrorString(e));
+    s.cap = cap;
+  }
+  std::memcpy(s.host, bytes.data(), bytes.size());
+  e = hipMemcpyAsync(workspace, s.host, bytes.size(), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  s.pending = true;
+  return KAMERA_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+// ---------------------------------------------------------------------------------------
+// packing
+// ---------------------------------------------------------------------------------------
+
+struct Plan {
+  std::vector<JobDesc> mfma, valu;
+  int mfma_max_steps = 0;
+  int64_t mfma_blocks = 0, valu_blocks = 0;
+};
+
+// Can this job use the MFMA path? Sets the window width.
+bool mfma_eligible(const kamera_model& m, const kamera_cache& c, const kamera_chunk& k,
+                   const Channel& g, Op op, int ch, int* win_width) {
+  if (m.dtype != KAMERA_DTYPE_BF16) return false;
+  if (env_int("KAMERA_FORCE_VALU", 0)) return false;
+  int w;
+  if (g.rotate && op != Op::Patch) {
+    if (g.width != 64 && g.width != 128) return false;
+    w = g.width;
+  } else if (g.width % 128 == 0) {
+    w = 128;
+  } else if (g.width % 64 == 0) {
+    w = 64;
+  } else {
+    return false;
+  }
+  // 16-byte loads and stores of token rows
+  if (!aligned16(c.pool[ch]) || c.layer_stride % 8 || c.token_stride % 8) return false;
+  if (op != Op::Patch) {
+    const kamera_src& s = k.src[ch];
+    if (!aligned16(s.ptr) || s.layer_stride % 8 || s.token_stride % 8) return false;
+  }
+  *win_width = w;
+  return true;
+}
+
+kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kamera_chunk* chunks,
+                         int32_t n_chunks, Op op, Plan* plan) {
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_chunk& k = chunks[i];
+    if (k.n_tokens == 0) continue;
+    for (int ch = 0; ch < 2; ++ch) {
+      const Channel g = channel_of(m, ch);
+      const kamera_patch_ref& p = k.patch[ch];
+      const int mm = op == Op::Relocate ? 0 : p.m;
+      if (op == Op::Patch && mm == 0) continue;
+      JobDesc j;
+      std::memset(&j, 0, sizeof j);
+      j.src = op == Op::Patch ? nullptr : k.src[ch].ptr;
+      j.src_ls = op == Op::Patch ? 0 : k.src[ch].layer_stride;
+      j.src_ts = op == Op::Patch ? 0 : k.src[ch].token_stride;
+      j.pool = c.pool[ch];
+      j.m = mm;
+      if (mm > 0) {
+        j.U = p.U;
+        j.V = p.V;
+        j.u_ls = p.u_layer_stride;
+        j.u_hs = p.u_head_stride;
+        j.v_ls = p.v_layer_stride;
+        j.v_hs = p.v_head_stride;
+      }
+      j.delta = k.delta;
+      j.n_tokens = k.n_tokens;
+      j.dst_offset = k.dst_token_offset;
+      j.rotate = (g.rotate && op != Op::Patch) ? 1 : 0;
+      j.head_width = g.width;
+      j.rot_dim = m.family == KAMERA_FAMILY_MLA ? m.rope_dim : m.head_dim;
+      int w = 0;
+      if (mfma_eligible(m, c, k, g, op, ch, &w)) {
+        j.win_width = w;
+        j.wph = g.width / w;
+        j.n_windows = g.heads * j.wph;
+        j.n_wgroups = (j.n_windows + 3) / 4;
+        j.n_tiles = (k.n_tokens + kamera::kTileTokens - 1) / kamera::kTileTokens;
+        const int nwin_blk = std::min(4, j.n_windows);
+        const int sub = 4 / nwin_blk;
+        const int tpg = kamera::kTilesPerWave * sub;
+        j.n_tgroups = std::max(1, (j.n_tiles + tpg - 1) / tpg);
+        j.vec_uv = mm > 0 && mm % 8 == 0 && aligned16(p.U) && aligned16(p.V) &&
+                   p.u_layer_stride % 8 == 0 && p.u_head_stride % 8 == 0 &&
+                   p.v_layer_stride % 8 == 0 && p.v_head_stride % 8 == 0;
+        plan->mfma.push_back(j);
+        plan->mfma_max_steps = std::max(plan->mfma_max_steps, (mm + 31) / 32);
+      } else {
+        j.win_width = g.width;
+        j.wph = 1;
+        j.n_windows = g.heads;
+        j.n_wgroups = (g.heads + 3) / 4;
+        j.n_tiles = k.n_tokens;
+        j.n_tgroups = (k.n_tokens + kamera::kValuTokensPerBlock - 1) / kamera::kValuTokensPerBlock;
+        plan->valu.push_back(j);
+      }
+    }
+  }
+  // heaviest jobs first so that a mixed batch does not end on a tail of patched work
+  auto heavier = [](const JobDesc& a, const JobDesc& b) { return a.m > b.m; };
+  std::stable_sort(plan->mfma.begin(), plan->mfma.end(), heavier);
+  std::stable_sort(plan->valu.begin(), plan->valu.end(), heavier);
+  auto assign = [&](std::vector<JobDesc>& jobs, int64_t* total) -> bool {
+    int64_t b = 0;
+    for (JobDesc& j : jobs) {
+      j.block_start = (int32_t)b;
+      b += (int64_t)m.n_layers * j.n_wgroups * j.n_tgroups;
+      if (b > INT32_MAX) return false;
+    }
+    *total = b;
+    return true;
+  };
+  if (!assign(plan->mfma, &plan->mfma_blocks) || !assign(plan->valu, &plan->valu_blocks))
+    return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
+  return KAMERA_OK;
+}
+
+kamera_status run(const kamera_model* model, const kamera_cache* cache, const kamera_chunk* chunks,
+                  int32_t n_chunks, void* workspace, size_t workspace_bytes, void* stream_ptr,
+                  Op op) {
+  g_last_error.clear();
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  st = validate_cache(*model, cache);
+  if (st != KAMERA_OK) return st;
+  st = validate_chunks(*model, *cache, chunks, n_chunks, op);
+  if (st != KAMERA_OK) return st;
+  if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = kamera_workspace_bytes(n_chunks);
+  if (workspace_bytes < need)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  Plan plan;
+  st = build_plan(*model, *cache, chunks, n_chunks, op, &plan);
+  if (st != KAMERA_OK) return st;
+
+  // workspace: [header | MFMA jobs | VALU jobs]
+  const size_t mfma_off = kHeaderBytes;
+  const size_t valu_off = mfma_off + plan.mfma.size() * sizeof(JobDesc);
+  const size_t bytes = valu_off + plan.valu.size() * sizeof(JobDesc);
+  std::vector<uint8_t> staging(bytes, 0);
+  if (!plan.mfma.empty())
+    std::memcpy(staging.data() + mfma_off, plan.mfma.data(), plan.mfma.size() * sizeof(JobDesc));
+  if (!plan.valu.empty())
+    std::memcpy(staging.data() + valu_off, plan.valu.data(), plan.valu.size() * sizeof(JobDesc));
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  st = upload(staging, workspace, stream);
+  if (st != KAMERA_OK) return st;
+
+  LaunchParams lp;
+  std::memset(&lp, 0, sizeof lp);
+  lp.page_table = cache->page_table;
+  lp.n_logical_pages = cache->n_logical_pages;
+  lp.page_size = cache->page_size;
+  lp.n_pages = cache->n_pages;
+  lp.layout = model->rope_layout;
+  lp.pool_ls = cache->layer_stride;
+  lp.pool_ts = cache->token_stride;
+  lp.theta = model->rope_theta;
+  lp.fault_counter = static_cast<uint32_t*>(workspace);
+  lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
+  lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 1);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (!plan.mfma.empty()) {
+    lp.jobs = reinterpret_cast<const JobDesc*>(ws + mfma_off);
+    lp.n_jobs = (int32_t)plan.mfma.size();
+    lp.total_blocks = (int32_t)plan.mfma_blocks;
+    const int steps = plan.mfma_max_steps <= 2 ? plan.mfma_max_steps : -1;
+    hipError_t e = kamera::launch_mfma(lp, steps, stream);
+    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "MFMA kernel launch: %s", hipGetErrorString(e));
+  }
+  if (!plan.valu.empty()) {
+    lp.jobs = reinterpret_cast<const JobDesc*>(ws + valu_off);
+    lp.n_jobs = (int32_t)plan.valu.size();
+    lp.total_blocks = (int32_t)plan.valu_blocks;
+    hipError_t e = kamera::launch_valu(lp, model->dtype == KAMERA_DTYPE_F32 ? 0 : 1, stream);
+    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "VALU kernel launch: %s", hipGetErrorString(e));
+  }
+  return KAMERA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kamera_workspace_bytes(int32_t n_chunks) {
+  if (n_chunks < 0) return 0;
+  return round_up(kHeaderBytes + (size_t)n_chunks * 2 * sizeof(JobDesc), 256);
+}
+
+kamera_status kamera_reuse_batch(const kamera_model* model, const kamera_cache* cache,
+                                 const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream, Op::Reuse);
+}
+
+kamera_status kamera_relocate(const kamera_model* model, const kamera_cache* cache,
+                              const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return run(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream, Op::Relocate);
+}
+
+kamera_status kamera_patch(const kamera_model* model, const kamera_cache* cache,
+                           const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return run(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream, Op::Patch);
+}
+
+kamera_status kamera_read_fault_count(const void* workspace, void* stream, uint32_t* count) {
+  g_last_error.clear();
+  if (!workspace || !count) return fail(KAMERA_ERR_INVALID_ARGUMENT, "NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(count, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "reading the fault count: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+size_t kamera_patch_bytes(const kamera_model* model, int32_t n_tokens, int32_t m) {
+  if (!model || n_tokens < 0 || m < 0) return 0;
+  if (validate_model(model) != KAMERA_OK) return 0;
+  const size_t es = model->dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  size_t total = 0;
+  for (int ch = 0; ch < 2; ++ch) {
+    const Channel g = channel_of(*model, ch);
+    total += (size_t)model->n_layers * g.heads * ((size_t)n_tokens + g.width) * m * es;
+  }
+  return total;
+}
+
+size_t kamera_kv_bytes(const kamera_model* model, int32_t n_tokens) {
+  if (!model || n_tokens < 0) return 0;
+  if (validate_model(model) != KAMERA_OK) return 0;
+  const size_t es = model->dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  size_t total = 0;
+  for (int ch = 0; ch < 2; ++ch) {
+    const Channel g = channel_of(*model, ch);
+    total += (size_t)model->n_layers * n_tokens * g.heads * g.width * es;
+  }
+  return total;
+}
+
+const char* kamera_status_string(kamera_status status) {
+  switch (status) {
+    case KAMERA_OK: return "ok";
+    case KAMERA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KAMERA_ERR_UNSUPPORTED: return "unsupported";
+    case KAMERA_ERR_OVERLAP: return "source overlaps destination";
+    case KAMERA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KAMERA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kamera_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kamera_version(void) { return KAMERA_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// kamera_internal.h — types shared by the host runtime (kamera_api.cpp) and the kernels
+// (kamera_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kamera {
+
+// One unit of work packed by the host: one chunk, one channel, every layer.
+// The kernels split it into blocks of (layer, window group, token group).
+struct alignas(16) JobDesc {
+  const void* src;   // canonical rows of the channel (unused in patch-only mode)
+  const void* U;     // patch factors (m > 0)
+  const void* V;
+  void* pool;        // destination pool of the channel
+  int64_t src_ls;    // src layer stride (elements)
+  int64_t src_ts;    // src token stride
+  int64_t u_ls, u_hs;
+  int64_t v_ls, v_hs;
+  int64_t delta;
+  int32_t n_tokens;
+  int32_t dst_offset;
+  int32_t m;
+  int32_t rotate;      // 1: R(delta) on this channel
+  int32_t head_width;  // features per head of this channel
+  int32_t win_width;   // features one wave handles at a time (a window of a head)
+  int32_t wph;         // windows per head
+  int32_t n_windows;   // heads * wph
+  int32_t n_wgroups;   // windows are taken 4 at a time (one per wave)
+  int32_t n_tgroups;   // token groups
+  int32_t n_tiles;     // token tiles (16 tokens on the MFMA path, 1 token on the VALU path)
+  int32_t block_start; // first block of this job in the launch
+  int32_t vec_uv;      // U and V rows may be read with 16-byte loads
+  int32_t rot_dim;     // length of the frequency ladder (2 x pairs)
+};
+
+enum Mode : int32_t { MODE_REUSE = 0, MODE_PATCH = 1 };
+
+struct LaunchParams {
+  const JobDesc* jobs;      // device (inside the workspace)
+  int32_t n_jobs;
+  int32_t total_blocks;
+  const int32_t* page_table;
+  int32_t n_logical_pages;
+  int32_t page_size;
+  int32_t n_pages;
+  int32_t layout;           // kamera_rope_layout
+  int64_t pool_ls;          // pool layer stride (elements)
+  int64_t pool_ts;          // pool token stride
+  double theta;
+  uint32_t* fault_counter;  // device (workspace header)
+  int32_t mode;             // Mode
+  int32_t xcd_remap;        // 1: consecutive logical blocks run on the same XCD
+};
+
+// Kernel geometry
+constexpr int kBlockThreads = 256;      // 4 waves of 64
+constexpr int kTileTokens = 16;         // MFMA N dimension
+constexpr int kTilesPerWave = 16;       // target tiles per wave on the MFMA path
+constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
+constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
+
+// max_steps: K-steps of 32 kept in registers (0: no patch in the launch, 1: m <= 32,
+// 2: m <= 64); -1 streams the V operand from memory for any m <= 256.
+hipError_t launch_mfma(const LaunchParams& p, int max_steps, hipStream_t stream);
+// dtype: 0 = fp32, 1 = bf16
+hipError_t launch_valu(const LaunchParams& p, int dtype, hipStream_t stream);
+
+}  // namespace kamera

@@ -1,0 +1,457 @@
+// kamera_kernels.hip — gfx950 kernels of the Kamera reuse operator.
+//
+//   out(l, t, h, f) = [R(delta) src](l, t, h, f) + sum_r U(l, h, t, r) V(l, h, f, r)
+//
+// (technical summary of "Kamera: Unified Position-Invariant Multimodal KV Cache for
+// Training-Free Reuse", §2 Methodology, reuse equation; R(delta) is the exact RoPE phase
+// shift, the patch is added after it.) The result is stored through the page table into
+// the destination pool.
+//
+// Two kernels:
+//   * kamera_mfma_kernel  — bf16, windows of 64 or 128 features. The pass is HBM-bound: each
+//     lane streams 16-byte pieces of token rows, rotates in fp32 with cos/sin from an LDS
+//     table, and, when a patch is present, lets one 16x16x32 bf16 MFMA per window tile add
+//     U V^T onto the rotated values held in the accumulator. The rows of the MFMA A operand
+//     (V) are permuted so that the accumulator a lane receives covers exactly the features
+//     it loaded: 8 contiguous features per 32-feature run, which keeps both RoPE pair layouts
+//     lane-local and every load and store 16 bytes wide.
+//   * kamera_valu_kernel  — fp32 (and bf16 shapes the MFMA path does not take): one thread
+//     per pair of features, fp32 FMA for the patch.
+//
+// Lane map of the MFMA path (one wave, one 16-token tile of one window of width W):
+//   lane = 16 g + n   (g = 0..3, n = 0..15): token t0 + n, features 32 r + 8 g + (0..7),
+//   r = 0..W/32-1. MFMA tile T = 2 r + q holds, in accumulator i of lane (g, n), feature
+//   32 r + 8 g + 4 q + i of token t0 + n.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kamera_internal.h"
+
+namespace kamera {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (RNE, hardware conversion) and pack them, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return lo | (hi << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Logical block -> block index so that each XCD (blocks are dealt round-robin over the 8
+// XCDs) works through one contiguous range of logical blocks: neighbouring blocks share
+// patch factors and page-table lines, which then stay in that XCD's L2.
+__device__ __forceinline__ int remap_block(int b, int total, int enable) {
+  if (!enable) return b;
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Binary search: the job whose block range holds `blk` (jobs sorted by block_start).
+__device__ __forceinline__ int find_job(const JobDesc* jobs, int n_jobs, int blk) {
+  int lo = 0, hi = n_jobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (jobs[mid].block_start <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// cos/sin(delta * theta^(-2i/rot_dim)) for every pair i: angle and range reduction in fp64,
+// one rounding to fp32 each.
+__device__ __forceinline__ void fill_phases(float2* cs, int64_t delta, double theta, int rot_dim) {
+  for (int i = threadIdx.x; i < rot_dim / 2; i += kBlockThreads) {
+    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    double s, c;
+    sincos((double)delta * inv, &s, &c);
+    cs[i] = make_float2((float)c, (float)s);
+  }
+}
+
+// Destination row (element offset of feature 0 of the row's first head) of logical token p,
+// or -1 when the page-table entry is outside [0, n_pages).
+__device__ __forceinline__ int64_t dst_row(const LaunchParams& P, int64_t p) {
+  const int64_t page = p / P.page_size;
+  const int64_t phys = P.page_table ? (int64_t)P.page_table[page] : page;
+  if (phys < 0 || phys >= P.n_pages) return -1;
+  return (phys * P.page_size + (p - page * P.page_size)) * P.pool_ts;
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA path
+// ---------------------------------------------------------------------------------------
+
+template <int W>
+struct TileIn {
+  u32x4 raw[W / 32];   // token t0+n, features 32r + 8g .. +8 (bf16)
+  bf16x8 ub[2];        // B operand (U rows) for up to 2 register-resident K-steps
+  int64_t drow;        // destination element offset, -1 = skip
+};
+
+template <int W, int MAXS>
+struct WindowCtx {
+  const uint16_t* src;   // src of this layer/head/window, token 0, feature 0
+  uint16_t* pool;        // pool of this layer, + head/window feature offset
+  const uint16_t* U;     // U of this layer/head (row t at + t*m)
+  const uint16_t* V;     // V of this layer/head, + window feature offset (row f at + f*m)
+  int64_t src_ts;
+  int32_t n_tokens, dst_offset, m, steps, vec_uv, rotate, copy, patch_mode;
+};
+
+// 8 consecutive bf16 of a U or V row starting at k0 (zeros past m).
+__device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, int vec) {
+  if (vec) {
+    if (k0 < m) return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + k0));
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = (k0 + 2 * j < m) ? row[k0 + 2 * j] : 0u;
+    const uint32_t b = (k0 + 2 * j + 1 < m) ? row[k0 + 2 * j + 1] : 0u;
+    w[j] = a | (b << 16);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+// Feature (within the window) that MFMA tile T row rho stands for: rows 4g..4g+3 of tile
+// T = 2r + q land in lane group g as features 32r + 8g + 4q + (0..3).
+__device__ __forceinline__ int tile_row_feature(int T, int rho) {
+  return 32 * (T >> 1) + 8 * (rho >> 2) + 4 * (T & 1) + (rho & 3);
+}
+
+template <int W, int MAXS>
+__device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx<W, MAXS>& C,
+                                          int tile, int g, int n, TileIn<W>& in) {
+  constexpr int NR = W / 32;
+  const int t = tile * kTileTokens + n;
+  const bool valid = t < C.n_tokens;
+  in.drow = valid ? dst_row(P, (int64_t)C.dst_offset + t) : -1;
+  const uint16_t* row = C.patch_mode ? (in.drow >= 0 ? C.pool + in.drow : nullptr)
+                                     : C.src + (int64_t)t * C.src_ts;
+  const bool have = valid && row != nullptr;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    in.raw[r] = have ? *reinterpret_cast<const u32x4*>(row + 32 * r + 8 * g)
+                     : u32x4{0u, 0u, 0u, 0u};
+  if constexpr (MAXS > 0) {
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      if (s < C.steps && valid)
+        in.ub[s] = load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv);
+      else
+        in.ub[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+}
+
+template <int W, int MAXS>
+__device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCtx<W, MAXS>& C,
+                                           const float2* cs, int tile_lo, int tile_hi) {
+  constexpr int NR = W / 32;   // 32-feature runs per lane
+  constexpr int NT = W / 16;   // MFMA tiles per window
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, n = lane & 15;
+  const bool interleaved = P.layout != 0;
+
+  // A operand: V rows of this window, permuted to the lane map, register resident
+  bf16x8 va[MAXS > 0 ? MAXS : 1][NT];
+  if constexpr (MAXS > 0) {
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        if (s < C.steps)
+          va[s][T] = load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m, 32 * s + 8 * g, C.m,
+                             C.vec_uv);
+        else
+          va[s][T] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
+  }
+
+  TileIn<W> cur, nxt;
+  if (tile_lo < tile_hi) load_tile<W, MAXS>(P, C, tile_lo, g, n, cur);
+  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+    if (tile + 1 < tile_hi) load_tile<W, MAXS>(P, C, tile + 1, g, n, nxt);
+
+    u32x4 out[NR];
+    if (C.copy) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) out[r] = cur.raw[r];
+    } else {
+      float v[NR][8];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[r][2 * j] = bf_lo(cur.raw[r][j]);
+          v[r][2 * j + 1] = bf_hi(cur.raw[r][j]);
+        }
+      }
+      if (C.rotate) {
+        if (interleaved) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x = v[r][2 * j], y = v[r][2 * j + 1];
+              // pair 16r + 4g + j owns features (2i, 2i+1) = 32r + 8g + (2j, 2j+1)
+              const float2 p = cs[16 * r + 4 * g + j];
+              const float c = p.x, s = p.y;
+              v[r][2 * j] = fmaf(x, c, -(y * s));
+              v[r][2 * j + 1] = fmaf(y, c, x * s);
+            }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NR / 2; ++r)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              // pair 32r + 8g + jj owns features (i, i + W/2)
+              const float x = v[r][jj], y = v[r + NR / 2][jj];
+              const float2 p = cs[32 * r + 8 * g + jj];
+              v[r][jj] = fmaf(x, p.x, -(y * p.y));
+              v[r + NR / 2][jj] = fmaf(y, p.x, x * p.y);
+            }
+        }
+      }
+      if (MAXS != 0 && C.steps > 0) {
+        f32x4 acc[NT];
+#pragma unroll
+        for (int T = 0; T < NT; ++T)
+          acc[T] = f32x4{v[T >> 1][4 * (T & 1)], v[T >> 1][4 * (T & 1) + 1],
+                         v[T >> 1][4 * (T & 1) + 2], v[T >> 1][4 * (T & 1) + 3]};
+        if constexpr (MAXS == 0) {
+          // no patch anywhere in this launch
+        } else if constexpr (MAXS > 0) {
+#pragma unroll
+          for (int s = 0; s < MAXS; ++s) {
+            if (s < C.steps) {
+#pragma unroll
+              for (int T = 0; T < NT; ++T)
+                acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[s][T], cur.ub[s], acc[T], 0,
+                                                                 0, 0);
+            }
+          }
+        } else {
+          // streamed: any m <= 256, both operands read per tile (V from L1/L2)
+          const int t = tile * kTileTokens + n;
+          const bool valid = t < C.n_tokens;
+          for (int s = 0; s < C.steps; ++s) {
+            const bf16x8 b = valid ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv)
+                                   : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+            for (int T = 0; T < NT; ++T) {
+              const bf16x8 a = load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m, 32 * s + 8 * g,
+                                       C.m, C.vec_uv);
+              acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[T], 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int T = 0; T < NT; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[T >> 1][4 * (T & 1) + i] = acc[T][i];
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        out[r] = u32x4{pack_bf16(v[r][0], v[r][1]), pack_bf16(v[r][2], v[r][3]),
+                       pack_bf16(v[r][4], v[r][5]), pack_bf16(v[r][6], v[r][7])};
+    }
+
+    const int t = tile * kTileTokens + n;
+    if (t < C.n_tokens) {
+      if (cur.drow >= 0) {
+        uint16_t* row = C.pool + cur.drow;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) *reinterpret_cast<u32x4*>(row + 32 * r + 8 * g) = out[r];
+      } else if (g == 0) {
+        atomicAdd(P.fault_counter, 1u);
+      }
+    }
+    cur = nxt;
+  }
+}
+
+template <int MAXS>
+__global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const LaunchParams P) {
+  __shared__ float2 cs[64];
+  const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
+  const JobDesc& J = P.jobs[find_job(P.jobs, P.n_jobs, blk)];
+
+  int local = blk - J.block_start;
+  const int tg = local % J.n_tgroups;
+  local /= J.n_tgroups;
+  const int wg = local % J.n_wgroups;
+  const int layer = local / J.n_wgroups;
+
+  const int rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
+  if (rotate) {
+    fill_phases(cs, J.delta, P.theta, J.rot_dim);
+    __syncthreads();
+  }
+
+  const int wave = threadIdx.x >> 6;
+  const int nwin = min(4, J.n_windows - 4 * wg);
+  const int sub = 4 / nwin;                       // waves sharing one window
+  if (wave >= nwin * sub) return;
+  const int win = 4 * wg + wave % nwin;
+  const int part = wave / nwin;
+
+  const int g_lo = (int)((int64_t)tg * J.n_tiles / J.n_tgroups);
+  const int g_hi = (int)((int64_t)(tg + 1) * J.n_tiles / J.n_tgroups);
+  const int tile_lo = g_lo + (g_hi - g_lo) * part / sub;
+  const int tile_hi = g_lo + (g_hi - g_lo) * (part + 1) / sub;
+
+  const int head = win / J.wph;
+  const int f0 = (win % J.wph) * J.win_width;
+  const int64_t feat = (int64_t)head * J.head_width + f0;
+
+  const int steps = (J.m + 31) / 32;
+  auto make = [&](auto wtag) {
+    constexpr int Wv = decltype(wtag)::value;
+    WindowCtx<Wv, MAXS> C;
+    C.src = static_cast<const uint16_t*>(J.src) + (J.src ? layer * J.src_ls + feat : 0);
+    C.pool = static_cast<uint16_t*>(J.pool) + layer * P.pool_ls + feat;
+    C.U = J.m > 0 ? static_cast<const uint16_t*>(J.U) + layer * J.u_ls + head * J.u_hs : nullptr;
+    C.V = J.m > 0 ? static_cast<const uint16_t*>(J.V) + layer * J.v_ls + head * J.v_hs +
+                        (int64_t)f0 * J.m
+                  : nullptr;
+    C.src_ts = J.src_ts;
+    C.n_tokens = J.n_tokens;
+    C.dst_offset = J.dst_offset;
+    C.m = J.m;
+    C.steps = steps;
+    C.vec_uv = J.vec_uv;
+    C.rotate = rotate;
+    C.copy = (!rotate && J.m == 0) ? 1 : 0;
+    C.patch_mode = P.mode == MODE_PATCH;
+    run_window<Wv, MAXS>(P, C, cs, tile_lo, tile_hi);
+  };
+  if (J.win_width == 128) make(std::integral_constant<int, 128>{});
+  else make(std::integral_constant<int, 64>{});
+}
+
+// ---------------------------------------------------------------------------------------
+// VALU path
+// ---------------------------------------------------------------------------------------
+
+template <typename T> __device__ __forceinline__ float ld(const T* p);
+template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <typename T> __device__ __forceinline__ void st(T* p, float v);
+template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const LaunchParams P) {
+  __shared__ float2 cs[kMaxPairs];
+  const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
+  const JobDesc& J = P.jobs[find_job(P.jobs, P.n_jobs, blk)];
+
+  int local = blk - J.block_start;
+  const int tg = local % J.n_tgroups;
+  local /= J.n_tgroups;
+  const int wg = local % J.n_wgroups;
+  const int layer = local / J.n_wgroups;
+
+  const int rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
+  if (rotate) {
+    fill_phases(cs, J.delta, P.theta, J.rot_dim);
+    __syncthreads();
+  }
+  const bool interleaved = P.layout != 0;
+  const int D = J.head_width;
+  const int half = D / 2;
+  const int h_lo = 4 * wg;
+  const int nh = min(4, J.n_windows - h_lo);
+  const int t_lo = (int)((int64_t)tg * J.n_tokens / J.n_tgroups);
+  const int t_hi = (int)((int64_t)(tg + 1) * J.n_tokens / J.n_tgroups);
+  const int nt = t_hi - t_lo;
+  const int64_t items = (int64_t)nh * nt * half;
+  const int m = J.m;
+
+  const T* src = static_cast<const T*>(J.src);
+  T* pool = static_cast<T*>(J.pool) + layer * P.pool_ls;
+  const T* U = static_cast<const T*>(J.U);
+  const T* V = static_cast<const T*>(J.V);
+
+  for (int64_t it = threadIdx.x; it < items; it += kBlockThreads) {
+    const int q = (int)(it % half);
+    const int64_t rest = it / half;
+    const int t = t_lo + (int)(rest % nt);
+    const int head = h_lo + (int)(rest / nt);
+    // the two features this item owns
+    int fa, fb;
+    if (rotate && !interleaved) { fa = q; fb = q + half; } else { fa = 2 * q; fb = 2 * q + 1; }
+
+    const int64_t drow = dst_row(P, (int64_t)J.dst_offset + t);
+    if (drow < 0) {
+      if (q == 0) atomicAdd(P.fault_counter, 1u);
+      continue;
+    }
+    T* out = pool + drow + (int64_t)head * D;
+    const T* in = P.mode == MODE_PATCH ? out
+                                       : src + layer * J.src_ls + (int64_t)t * J.src_ts +
+                                             (int64_t)head * D;
+    if (!rotate && m == 0) {   // bit copy
+      out[fa] = in[fa];
+      out[fb] = in[fb];
+      continue;
+    }
+    float xa = ld<T>(in + fa), xb = ld<T>(in + fb);
+    if (rotate) {
+      const float2 p = cs[q];
+      const float ra = fmaf(xa, p.x, -(xb * p.y));
+      const float rb = fmaf(xb, p.x, xa * p.y);
+      xa = ra;
+      xb = rb;
+    }
+    if (m > 0) {
+      const T* urow = U + layer * J.u_ls + head * J.u_hs + (int64_t)t * m;
+      const T* vbase = V + layer * J.v_ls + head * J.v_hs;
+      float pa = 0.f, pb = 0.f;
+      for (int r = 0; r < m; ++r) {
+        const float u = ld<T>(urow + r);
+        pa = fmaf(u, ld<T>(vbase + (int64_t)fa * m + r), pa);
+        pb = fmaf(u, ld<T>(vbase + (int64_t)fb * m + r), pb);
+      }
+      xa += pa;
+      xb += pb;
+    }
+    st<T>(out + fa, xa);
+    st<T>(out + fb, xb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const LaunchParams& p, int max_steps, hipStream_t stream) {
+  const dim3 grid(p.total_blocks), block(kBlockThreads);
+  switch (max_steps) {
+    case 0: hipLaunchKernelGGL(kamera_mfma_kernel<0>, grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(kamera_mfma_kernel<1>, grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(kamera_mfma_kernel<2>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(kamera_mfma_kernel<-1>, grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_valu(const LaunchParams& p, int dtype, hipStream_t stream) {
+  const dim3 grid(p.total_blocks), block(kBlockThreads);
+  if (dtype == 0) hipLaunchKernelGGL(kamera_valu_kernel<float>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(kamera_valu_kernel<uint16_t>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kamera

@@ -1,0 +1,213 @@
+"""Comparison of the GPU operator's output with the oracle (test helper, not a test file).
+
+Rules (all elementwise):
+  * copy channels (unrotated, m = 0): output bits == input bits.
+  * fp32:  |g - z| <= 1e-5 * S, z the fp64 oracle value and S the sum of the absolute values of
+    its terms (S >= |z|, so this is relative error except where the terms cancel).
+  * bf16:  |g - o| <= 2 ulp_bf16(|o|) + 2 (K + 1) u S, with o = bf16(fp32(z)) (the fp32 oracle
+    rounded to bf16), u = 2^-24 and K = m + 3 the length of the GPU's fp32 operation chain
+    (two rotation products, one FMA, m patch products). The second term is the fp32 rounding
+    bound of that chain; it only matters where the terms cancel and |o| is tiny. Reports
+    count the elements that needed it ("cancel") and the largest error in ulps.
+  * placement: every chunk token is read back from page_table[p / page_size], slot
+    p % page_size; every slot no chunk addresses still holds the sentinel bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+from position_invariant_kv_kamera_amd import workloads as wl
+
+U32 = 2.0 ** -24
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |v| (normal range: 2^(floor(log2 |v|) - 7))."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
+    """Element bits of a device/host tensor (uint16 for bf16, float32 for fp32)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@dataclass
+class Report:
+    elements: int = 0
+    copies: int = 0
+    copy_mismatches: int = 0
+    float_fail: int = 0
+    cancel: int = 0              # bf16 elements that needed the cancellation term
+    max_ulp: float = 0.0         # bf16: max |g - o| / ulp(|o|)
+    max_rel_s: float = 0.0       # fp32: max |g - z| / S
+    sentinel_bad: int = 0
+    details: list = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return self.copy_mismatches == 0 and self.float_fail == 0 and self.sentinel_bad == 0
+
+    def merge(self, o: "Report"):
+        self.elements += o.elements
+        self.copies += o.copies
+        self.copy_mismatches += o.copy_mismatches
+        self.float_fail += o.float_fail
+        self.cancel += o.cancel
+        self.max_ulp = max(self.max_ulp, o.max_ulp)
+        self.max_rel_s = max(self.max_rel_s, o.max_rel_s)
+        self.sentinel_bad += o.sentinel_bad
+        self.details.extend(o.details[:5])
+
+
+def compare_head(exp: dict, got: np.ndarray, dtype: str, m: int, where: str) -> Report:
+    r = Report(elements=got.size)
+    if exp["copy"]:
+        r.copies = got.size
+        same = np.array_equal(np.ascontiguousarray(got).view(np.uint8),
+                              np.ascontiguousarray(exp["bits"]).view(np.uint8))
+        if not same:
+            r.copy_mismatches = int(np.sum(got.view(np.uint16 if dtype == "bf16" else np.uint32)
+                                           != exp["bits"].view(got.dtype)))
+            r.details.append(f"{where}: copy differs in {r.copy_mismatches} elements")
+        return r
+    z, S = exp["z"], exp["S"]
+    if dtype == "f32":
+        g = got.astype(np.float64)
+        err = np.abs(g - z)
+        bad = ~(err <= 1e-5 * S)
+        r.float_fail = int(bad.sum())
+        with np.errstate(invalid="ignore", divide="ignore"):
+            r.max_rel_s = float(np.nanmax(np.where(S > 0, err / S, 0.0)))
+    else:
+        o_bits = oracle.to_bf16(z)
+        o = bf16_bits_to_f64(o_bits)
+        g = bf16_bits_to_f64(got)
+        err = np.abs(g - o)
+        u = ulp_bf16(o)
+        strict = err <= 2 * u
+        K = m + 3
+        bad = ~(err <= 2 * u + 2 * (K + 1) * U32 * S)
+        r.float_fail = int(bad.sum())
+        r.cancel = int((~strict & ~bad).sum())
+        r.max_ulp = float(np.max(err / u)) if err.size else 0.0
+    if r.float_fail:
+        idx = np.argwhere(bad)[:3]
+        r.details.append(f"{where}: {r.float_fail} out of tolerance, e.g. at {idx.tolist()}")
+    return r
+
+
+def _pool_rows(pool_l: torch.Tensor) -> torch.Tensor:
+    """[n_pages, page_size, row] view -> [n_pages * page_size, row]."""
+    return pool_l.view(pool_l.shape[0] * pool_l.shape[1], pool_l.shape[2])
+
+
+def compare_batch(batch: wl.Batch, op: str = "reuse", layers=None, chunks=None,
+                  check_sentinel: bool = True, patch_inputs=None) -> Report:
+    """Compare every element of the chosen chunks/layers (all by default).
+
+    op: "reuse" (R(delta) + patch), "relocate" (R(delta) only), "patch" (patch only, the
+    input being `patch_inputs[c][ch]` — per chunk and channel a host array [layers, L, row]
+    of what the pool held before the call).
+    """
+    p = batch.plan
+    rep = Report()
+    layers = range(p.n_layers) if layers is None else layers
+    chunks = range(p.n_chunks) if chunks is None else chunks
+    table = p.page_table
+    for c in chunks:
+        L = p.chunk_tokens[c]
+        if L == 0:
+            continue
+        slots = torch.from_numpy(oracle.slots(table, p.page_size, p.dst_offsets[c], L))
+        ct = batch.chunks[c]
+        for l in layers:
+            for ch in range(2):
+                W, H = p.width(ch), p.heads(ch)
+                got_rows = to_numpy_bits(_pool_rows(batch.pools[ch][l]).index_select(
+                    0, slots.to(batch.pools[ch].device)))
+                if op == "patch":
+                    src_rows = patch_inputs[c][ch][l]
+                else:
+                    src_rows = to_numpy_bits(ct.src[ch][l])
+                m = 0 if op == "relocate" or ct.U[ch] is None else ct.U[ch].shape[-1]
+                if op == "patch" and m == 0:
+                    continue
+                Uh = to_numpy_bits(ct.U[ch][l]) if m else None
+                Vh = to_numpy_bits(ct.V[ch][l]) if m else None
+                for h in range(H):
+                    exp = oracle.expected_head(
+                        np.ascontiguousarray(src_rows[:, h * W:(h + 1) * W]),
+                        rotate=(ch == 0 and op != "patch"),
+                        layout=0 if p.rope_layout == wl.HALF_SPLIT else 1,
+                        delta=p.deltas[c], theta=p.theta,
+                        U=None if not m else np.ascontiguousarray(Uh[h]),
+                        V=None if not m else np.ascontiguousarray(Vh[h]))
+                    got = np.ascontiguousarray(got_rows[:, h * W:(h + 1) * W])
+                    rep.merge(compare_head(exp, got, p.dtype, m, f"chunk {c} layer {l} ch {ch} head {h}"))
+    if check_sentinel:
+        rep.sentinel_bad = count_sentinel_damage(batch, layers)
+    return rep
+
+
+def count_sentinel_damage(batch: wl.Batch, layers=None) -> int:
+    """Slots no chunk addresses must still hold the sentinel in every layer and channel."""
+    p = batch.plan
+    layers = range(p.n_layers) if layers is None else layers
+    n_slots = p.n_pages * p.page_size
+    written = np.zeros(n_slots, bool)
+    for c in range(p.n_chunks):
+        if p.chunk_tokens[c]:
+            written[oracle.slots(p.page_table, p.page_size, p.dst_offsets[c],
+                                 p.chunk_tokens[c])] = True
+    free = torch.from_numpy(np.nonzero(~written)[0]).to(batch.pools[0].device)
+    if free.numel() == 0:
+        return 0
+    bad = 0
+    for ch in range(2):
+        for l in layers:
+            rows = _pool_rows(batch.pools[ch][l]).index_select(0, free)
+            if rows.dtype == torch.bfloat16:
+                bad += int((rows.view(torch.int16) != wl.SENTINEL_BF16).sum().item())
+            else:
+                bad += int((rows.view(torch.int32) != wl.SENTINEL_F32).sum().item())
+    return bad
+
+
+def sample_rows(batch: wl.Batch, n_rows: int, seed: int = 0, op: str = "reuse") -> Report:
+    """Oracle check of n_rows random (chunk, layer, channel, head, token) rows of a batch of
+    any size: the oracle computes just those rows."""
+    p = batch.plan
+    rng = np.random.default_rng(seed)
+    rep = Report()
+    for _ in range(n_rows):
+        c = int(rng.integers(p.n_chunks))
+        L = p.chunk_tokens[c]
+        if L == 0:
+            continue
+        l, ch = int(rng.integers(p.n_layers)), int(rng.integers(2))
+        h, t = int(rng.integers(p.heads(ch))), int(rng.integers(L))
+        W = p.width(ch)
+        ct = batch.chunks[c]
+        slot = int(oracle.slots(p.page_table, p.page_size, p.dst_offsets[c] + t, 1)[0])
+        got = to_numpy_bits(_pool_rows(batch.pools[ch][l])[slot, h * W:(h + 1) * W])[None]
+        src = to_numpy_bits(ct.src[ch][l, t, h * W:(h + 1) * W])[None]
+        m = 0 if op == "relocate" or ct.U[ch] is None else ct.U[ch].shape[-1]
+        U = to_numpy_bits(ct.U[ch][l, h, t:t + 1]) if m else None
+        V = to_numpy_bits(ct.V[ch][l, h]) if m else None
+        exp = oracle.expected_head(src, rotate=(ch == 0), delta=p.deltas[c], theta=p.theta,
+                                   layout=0 if p.rope_layout == wl.HALF_SPLIT else 1, U=U, V=V)
+        rep.merge(compare_head(exp, got, p.dtype, m, f"chunk {c} layer {l} ch {ch} head {h} token {t}"))
+    return rep
