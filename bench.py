@@ -117,8 +117,96 @@ def cpu_baseline(batch, budget_s: float) -> dict:
                       f"layers x 2 channels), {busy:.1f} s of oracle time"}
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(prof_dir: str, workload: str, command: str) -> None:
+    """Turn rocprofv3 CSV output (a kernel-trace --stats run named `kt`, and --pmc runs named
+    `fetch` (FETCH_SIZE) and `write` (WRITE_SIZE), all on `bench.py --workload <workload>`) into
+    the committed summaries under profiles/."""
+    d = Path(prof_dir)
+    p = __import__("position_invariant_kv_kamera_amd.workloads", fromlist=["plan"]).plan(workload)
+    ab = algorithmic_bytes(p)["total"]
+    lines = [f"# kamera_mfma_kernel on {workload}", "",
+             f"Command (repository root on the GPU box): `{command}`", ""]
+    stats = sorted(d.glob("**/kt_kernel_stats.csv"))
+    avg_ns = None
+    if stats:
+        rows = _read_csv(stats[0])
+        lines += ["## rocprofv3 --kernel-trace --stats", "",
+                  "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0)))[:8]:
+            name = r["Name"][:70].replace("|", "/")
+            lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.1f} |")
+            if "kamera_mfma_kernel" in r["Name"] and avg_ns is None:
+                avg_ns = float(r["AverageNs"])
+        if avg_ns:
+            lines += ["", f"kamera_mfma_kernel average {avg_ns / 1e3:.1f} us; algorithmic bytes "
+                          f"per launch {ab} -> {ab / avg_ns:.1f} GB/s "
+                          f"({ab / avg_ns / HBM_PEAK_GBPS:.3f} of 8 TB/s)."]
+    counters = {}
+    for tag, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        files = sorted(d.glob(f"**/{tag}_counter_collection.csv"))
+        if not files:
+            continue
+        per = {}
+        for r in _read_csv(files[0]):
+            if r.get("Counter_Name") != cname:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[cname] = per
+    traffic = None
+    if counters:
+        lines += ["", "## rocprofv3 --pmc (KiB per dispatch, averaged over dispatches)", "",
+                  "| kernel | counter | dispatches | KiB / dispatch |", "|---|---|---|---|"]
+
+        def pick(per, key):
+            vals = [v for k, vs in per.items() if key(k) for v in vs]
+            return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+        copy_key = lambda k: "copy" in k.lower() and "kamera" not in k
+        kam_key = lambda k: "kamera_mfma_kernel" in k
+        fig = {}
+        for cname, per in counters.items():
+            for label, key in (("kamera_mfma_kernel", kam_key), ("device copy (calibration)", copy_key)):
+                v, n = pick(per, key)
+                if v is not None:
+                    lines.append(f"| {label} | {cname} | {n} | {v:.0f} |")
+                    fig[(label, cname)] = v
+        copy_bytes = 2 << 30   # the calibration copy moves 2 GiB in and 2 GiB out per dispatch
+        kf = fig.get(("kamera_mfma_kernel", "FETCH_SIZE"))
+        kw = fig.get(("kamera_mfma_kernel", "WRITE_SIZE"))
+        cf = fig.get(("device copy (calibration)", "FETCH_SIZE"))
+        cw = fig.get(("device copy (calibration)", "WRITE_SIZE"))
+        if None not in (kf, kw, cf, cw):
+            sf, sw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+            traffic = kf * 1024 * sf + kw * 1024 * sw
+            lines += ["", f"Calibration: a 2 GiB device copy reads {cf * 1024 / copy_bytes:.3f}x "
+                          f"and writes {cw * 1024 / copy_bytes:.3f}x its size by these counters; "
+                          f"scale factors {sf:.3f} (fetch), {sw:.3f} (write).",
+                      f"kamera_mfma_kernel HBM traffic per launch: {traffic / 1e9:.3f} GB "
+                      f"(fetch {kf * 1024 * sf / 1e9:.3f} + write {kw * 1024 * sw / 1e9:.3f}) "
+                      f"vs algorithmic {ab / 1e9:.3f} GB: ratio {traffic / ab:.3f}."]
+    out_md = ROOT / "profiles" / f"kamera_mfma_kernel_{workload}.md"
+    out_md.write_text("\n".join(lines) + "\n")
+    if traffic is not None:
+        (ROOT / "profiles" / f"traffic_{workload}.json").write_text(json.dumps(
+            {"kernel": "kamera_mfma_kernel", "workload": workload,
+             "kernel_source_sha": kernel_source_hash(), "traffic_bytes": int(traffic),
+             "algorithmic_bytes": ab, "command": command}, indent=1) + "\n")
+    print(out_md.read_text())
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 CSV output in DIR and exit")
+    ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
@@ -126,6 +214,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.profile_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the operator has no cross-GPU step and this "

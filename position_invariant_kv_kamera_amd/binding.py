@@ -7,11 +7,14 @@ raises instead of falling back to anything else.
 from __future__ import annotations
 
 import ctypes
+import os
 import re
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
-LIB_PATH = PKG / "libkamera.so"
+# KAMERA_LIBRARY selects another build of the same library (e.g. one built with different
+# tuning macros); the default is the in-tree build.
+LIB_PATH = Path(os.environ.get("KAMERA_LIBRARY", PKG / "libkamera.so"))
 HEADER = PKG.parent / "include" / "kamera.h"
 
 KAMERA_OK = 0

@@ -24,10 +24,14 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> Path:
+def build(verbose: bool = False, out: Path | None = None, defines: dict | None = None) -> Path:
+    """Compile the library to `out` (default: the in-tree libkamera.so). `defines` sets the
+    kernels' build-time knobs, e.g. {"KAMERA_PREFETCH_TILES": 3, "KAMERA_NONTEMPORAL": 0}."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
-    cmd = [hipcc, *FLAGS, "-o", str(tmp), *map(str, SOURCES)]
+    target = Path(out) if out else LIB
+    tmp = target.with_suffix(f".so.tmp{os.getpid()}")
+    macro = [f"-D{k}={v}" for k, v in (defines or {}).items()]
+    cmd = [hipcc, *FLAGS, *macro, "-o", str(tmp), *map(str, SOURCES)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,8 +42,8 @@ def build(verbose: bool = False) -> Path:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

@@ -289,9 +289,18 @@ int env_int(const char* name, int dflt) {
 
 struct Plan {
   std::vector<JobDesc> mfma, valu;
-  int mfma_max_steps = 0;
+  int mfma_max_m = 0;
   int64_t mfma_blocks = 0, valu_blocks = 0;
 };
+
+// Kernel variant for the largest rank in an MFMA launch (see launch_mfma).
+int kmode_for(int max_m) {
+  if (max_m == 0) return 0;
+  if (max_m <= 16) return 16;
+  if (max_m <= 32) return 32;
+  if (max_m <= 64) return 64;
+  return -1;
+}
 
 // Can this job use the MFMA path? Sets the window width.
 bool mfma_eligible(const kamera_model& m, const kamera_cache& c, const kamera_chunk& k,
@@ -357,15 +366,12 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
         j.n_windows = g.heads * j.wph;
         j.n_wgroups = (j.n_windows + 3) / 4;
         j.n_tiles = (k.n_tokens + kamera::kTileTokens - 1) / kamera::kTileTokens;
-        const int nwin_blk = std::min(4, j.n_windows);
-        const int sub = 4 / nwin_blk;
-        const int tpg = kamera::kTilesPerWave * sub;
-        j.n_tgroups = std::max(1, (j.n_tiles + tpg - 1) / tpg);
+        // n_tgroups is set below, once the whole batch's size is known
         j.vec_uv = mm > 0 && mm % 8 == 0 && aligned16(p.U) && aligned16(p.V) &&
                    p.u_layer_stride % 8 == 0 && p.u_head_stride % 8 == 0 &&
                    p.v_layer_stride % 8 == 0 && p.v_head_stride % 8 == 0;
         plan->mfma.push_back(j);
-        plan->mfma_max_steps = std::max(plan->mfma_max_steps, (mm + 31) / 32);
+        plan->mfma_max_m = std::max(plan->mfma_max_m, mm);
       } else {
         j.win_width = g.width;
         j.wph = 1;
@@ -377,6 +383,19 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
       }
     }
   }
+  // Token groups of the MFMA jobs: each wave gets `tpw` tiles of one window. Small batches
+  // take short waves (more blocks to spread over 256 CUs), large ones long waves (less
+  // per-block set-up): measured best at 8 tiles up to ~30K blocks, 16 up to ~120K, else 32.
+  auto tgroups = [](const JobDesc& j, int tpw) {
+    const int sub = 4 / std::min(4, j.n_windows);
+    return std::max(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
+  };
+  int64_t blocks8 = 0;
+  for (const JobDesc& j : plan->mfma) blocks8 += (int64_t)m.n_layers * j.n_wgroups * tgroups(j, 8);
+  int tpw = blocks8 > 120000 ? 32 : blocks8 > 30000 ? 16 : 8;
+  tpw = std::max(1, env_int("KAMERA_TILES_PER_WAVE", tpw));
+  for (JobDesc& j : plan->mfma) j.n_tgroups = tgroups(j, tpw);
+
   // heaviest jobs first so that a mixed batch does not end on a tail of patched work
   auto heavier = [](const JobDesc& a, const JobDesc& b) { return a.m > b.m; };
   std::stable_sort(plan->mfma.begin(), plan->mfma.end(), heavier);
@@ -417,15 +436,22 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   st = build_plan(*model, *cache, chunks, n_chunks, op, &plan);
   if (st != KAMERA_OK) return st;
 
-  // workspace: [header | MFMA jobs | VALU jobs]
+  // workspace: [header | MFMA jobs | VALU jobs | MFMA block starts | VALU block starts]
   const size_t mfma_off = kHeaderBytes;
   const size_t valu_off = mfma_off + plan.mfma.size() * sizeof(JobDesc);
-  const size_t bytes = valu_off + plan.valu.size() * sizeof(JobDesc);
+  const size_t mfma_bs_off = valu_off + plan.valu.size() * sizeof(JobDesc);
+  const size_t valu_bs_off = mfma_bs_off + plan.mfma.size() * sizeof(int32_t);
+  const size_t bytes = valu_bs_off + plan.valu.size() * sizeof(int32_t);
   std::vector<uint8_t> staging(bytes, 0);
-  if (!plan.mfma.empty())
-    std::memcpy(staging.data() + mfma_off, plan.mfma.data(), plan.mfma.size() * sizeof(JobDesc));
-  if (!plan.valu.empty())
-    std::memcpy(staging.data() + valu_off, plan.valu.data(), plan.valu.size() * sizeof(JobDesc));
+  auto put = [&](size_t off, const std::vector<JobDesc>& jobs, size_t bs_off) {
+    if (jobs.empty()) return;
+    std::memcpy(staging.data() + off, jobs.data(), jobs.size() * sizeof(JobDesc));
+    for (size_t i = 0; i < jobs.size(); ++i)
+      std::memcpy(staging.data() + bs_off + i * sizeof(int32_t), &jobs[i].block_start,
+                  sizeof(int32_t));
+  };
+  put(mfma_off, plan.mfma, mfma_bs_off);
+  put(valu_off, plan.valu, valu_bs_off);
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   st = upload(staging, workspace, stream);
@@ -443,18 +469,19 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   lp.theta = model->rope_theta;
   lp.fault_counter = static_cast<uint32_t*>(workspace);
   lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
-  lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 1);
+  lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   if (!plan.mfma.empty()) {
     lp.jobs = reinterpret_cast<const JobDesc*>(ws + mfma_off);
+    lp.block_starts = reinterpret_cast<const int32_t*>(ws + mfma_bs_off);
     lp.n_jobs = (int32_t)plan.mfma.size();
     lp.total_blocks = (int32_t)plan.mfma_blocks;
-    const int steps = plan.mfma_max_steps <= 2 ? plan.mfma_max_steps : -1;
-    hipError_t e = kamera::launch_mfma(lp, steps, stream);
+    hipError_t e = kamera::launch_mfma(lp, kmode_for(plan.mfma_max_m), stream);
     if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "MFMA kernel launch: %s", hipGetErrorString(e));
   }
   if (!plan.valu.empty()) {
     lp.jobs = reinterpret_cast<const JobDesc*>(ws + valu_off);
+    lp.block_starts = reinterpret_cast<const int32_t*>(ws + valu_bs_off);
     lp.n_jobs = (int32_t)plan.valu.size();
     lp.total_blocks = (int32_t)plan.valu_blocks;
     hipError_t e = kamera::launch_valu(lp, model->dtype == KAMERA_DTYPE_F32 ? 0 : 1, stream);
@@ -469,7 +496,7 @@ extern "C" {
 
 size_t kamera_workspace_bytes(int32_t n_chunks) {
   if (n_chunks < 0) return 0;
-  return round_up(kHeaderBytes + (size_t)n_chunks * 2 * sizeof(JobDesc), 256);
+  return round_up(kHeaderBytes + (size_t)n_chunks * 2 * (sizeof(JobDesc) + sizeof(int32_t)), 256);
 }
 
 kamera_status kamera_reuse_batch(const kamera_model* model, const kamera_cache* cache,

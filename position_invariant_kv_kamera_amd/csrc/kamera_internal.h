@@ -39,6 +39,7 @@ enum Mode : int32_t { MODE_REUSE = 0, MODE_PATCH = 1 };
 
 struct LaunchParams {
   const JobDesc* jobs;      // device (inside the workspace)
+  const int32_t* block_starts;  // device: jobs[i].block_start, compact (one int per job)
   int32_t n_jobs;
   int32_t total_blocks;
   const int32_t* page_table;
@@ -57,13 +58,25 @@ struct LaunchParams {
 // Kernel geometry
 constexpr int kBlockThreads = 256;      // 4 waves of 64
 constexpr int kTileTokens = 16;         // MFMA N dimension
-constexpr int kTilesPerWave = 16;       // target tiles per wave on the MFMA path
 constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
 constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 
-// max_steps: K-steps of 32 kept in registers (0: no patch in the launch, 1: m <= 32,
-// 2: m <= 64); -1 streams the V operand from memory for any m <= 256.
-hipError_t launch_mfma(const LaunchParams& p, int max_steps, hipStream_t stream);
+// Tiles a wave keeps in flight ahead of the one it computes (the m <= 64 variant holds its V
+// operand in 64 more registers and keeps one), and whether streamed rows use nontemporal
+// loads and stores. Build-time knobs; the defaults are the measured best on MI355X.
+#ifndef KAMERA_PREFETCH_TILES
+#define KAMERA_PREFETCH_TILES 3
+#endif
+#ifndef KAMERA_PREFETCH_TILES_RANK64
+#define KAMERA_PREFETCH_TILES_RANK64 1
+#endif
+#ifndef KAMERA_NONTEMPORAL
+#define KAMERA_NONTEMPORAL 0
+#endif
+
+// kmode: largest rank in the launch, rounded up: 0 (no patch), 16, 32 or 64 keep the V
+// operand in registers; -1 streams it from memory for any m <= 256.
+hipError_t launch_mfma(const LaunchParams& p, int kmode, hipStream_t stream);
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_valu(const LaunchParams& p, int dtype, hipStream_t stream);
 

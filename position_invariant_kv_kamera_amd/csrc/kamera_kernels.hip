@@ -9,21 +9,25 @@
 //
 // Two kernels:
 //   * kamera_mfma_kernel  — bf16, windows of 64 or 128 features. The pass is HBM-bound: each
-//     lane streams 16-byte pieces of token rows, rotates in fp32 with cos/sin from an LDS
-//     table, and, when a patch is present, lets one 16x16x32 bf16 MFMA per window tile add
-//     U V^T onto the rotated values held in the accumulator. The rows of the MFMA A operand
-//     (V) are permuted so that the accumulator a lane receives covers exactly the features
-//     it loaded: 8 contiguous features per 32-feature run, which keeps both RoPE pair layouts
-//     lane-local and every load and store 16 bytes wide.
+//     lane streams 16-byte pieces of token rows (several tiles in flight per wave),
+//     rotates in fp32 with cos/sin from an LDS table, and, when a patch is present, lets one
+//     bf16 MFMA per 16x16 output tile add U V^T onto the rotated values held in the
+//     accumulator. The rows of the MFMA A operand (V) are permuted so that the accumulator a
+//     lane receives covers exactly the features it loaded: 8 contiguous features per
+//     32-feature run, which keeps both RoPE pair layouts lane-local and every load and store
+//     16 bytes wide.
 //   * kamera_valu_kernel  — fp32 (and bf16 shapes the MFMA path does not take): one thread
 //     per pair of features, fp32 FMA for the patch.
 //
 // Lane map of the MFMA path (one wave, one 16-token tile of one window of width W):
 //   lane = 16 g + n   (g = 0..3, n = 0..15): token t0 + n, features 32 r + 8 g + (0..7),
 //   r = 0..W/32-1. MFMA tile T = 2 r + q holds, in accumulator i of lane (g, n), feature
-//   32 r + 8 g + 4 q + i of token t0 + n.
+//   32 r + 8 g + 4 q + i of token t0 + n (16x16x16 and 16x16x32 bf16 MFMAs share this
+//   output layout: lane (g, n) holds rows 4g..4g+3 of column n).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kamera_internal.h"
 
@@ -31,8 +35,12 @@ namespace kamera {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr bool kNT = KAMERA_NONTEMPORAL != 0;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -46,6 +54,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Streamed 16-byte row pieces: read once, written once.
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  if constexpr (kNT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+__device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
+  u32x4* q = reinterpret_cast<u32x4*>(p);
+  if constexpr (kNT) __builtin_nontemporal_store(v, q);
+  else *q = v;
+}
+
 // Logical block -> block index so that each XCD (blocks are dealt round-robin over the 8
 // XCDs) works through one contiguous range of logical blocks: neighbouring blocks share
 // patch factors and page-table lines, which then stay in that XCD's L2.
@@ -56,14 +76,17 @@ __device__ __forceinline__ int remap_block(int b, int total, int enable) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-// Binary search: the job whose block range holds `blk` (jobs sorted by block_start).
-__device__ __forceinline__ int find_job(const JobDesc* jobs, int n_jobs, int blk) {
-  int lo = 0, hi = n_jobs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (jobs[mid].block_start <= blk) lo = mid; else hi = mid - 1;
+// The job whose block range holds `blk`: block_starts is ascending, so the job index is the
+// number of starts <= blk, minus one. Each wave counts with one ballot per 64 jobs.
+__device__ __forceinline__ int find_job(const int32_t* block_starts, int n_jobs, int blk) {
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < n_jobs; base += 64) {
+    const int j = base + lane;
+    const bool le = j < n_jobs && block_starts[j] <= blk;
+    count += __popcll(__ballot(le));
   }
-  return lo;
+  return count - 1;
 }
 
 // cos/sin(delta * theta^(-2i/rot_dim)) for every pair i: angle and range reduction in fp64,
@@ -90,27 +113,39 @@ __device__ __forceinline__ int64_t dst_row(const LaunchParams& P, int64_t p) {
 // MFMA path
 // ---------------------------------------------------------------------------------------
 
-template <int W>
-struct TileIn {
-  u32x4 raw[W / 32];   // token t0+n, features 32r + 8g .. +8 (bf16)
-  bf16x8 ub[2];        // B operand (U rows) for up to 2 register-resident K-steps
-  int64_t drow;        // destination element offset, -1 = skip
+// KM: 0 = no patch in the launch; 16 = one 16x16x16 step (m <= 16); 32 / 64 = one / two
+// 16x16x32 steps (m <= 32 / 64), V operand in registers; -1 = streamed V, any m <= 256.
+template <int KM>
+struct KTraits {
+  static constexpr bool k16 = KM == 16;
+  static constexpr int s32 = KM == 32 ? 1 : (KM == 64 ? 2 : 0);
+  static constexpr bool streamed = KM < 0;
 };
 
-template <int W, int MAXS>
+template <int W, int KM>
+struct TileIn {
+  u32x4 raw[W / 32];                                  // token t0+n, features 32r + 8g .. +8
+  short4_t u16;                                       // B operand, KM == 16
+  bf16x8 u32[KTraits<KM>::s32 > 0 ? KTraits<KM>::s32 : 1];  // B operand, KM == 32 / 64
+  int64_t drow;                                       // destination element offset, -1 = skip
+};
+
 struct WindowCtx {
   const uint16_t* src;   // src of this layer/head/window, token 0, feature 0
   uint16_t* pool;        // pool of this layer, + head/window feature offset
   const uint16_t* U;     // U of this layer/head (row t at + t*m)
   const uint16_t* V;     // V of this layer/head, + window feature offset (row f at + f*m)
   int64_t src_ts;
-  int32_t n_tokens, dst_offset, m, steps, vec_uv, rotate, copy, patch_mode;
+  int32_t n_tokens, dst_offset, m, vec_uv, rotate, copy, patch_mode, steps32;
 };
 
 // 8 consecutive bf16 of a U or V row starting at k0 (zeros past m).
-__device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, int vec) {
+__device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, int vec, bool nt) {
   if (vec) {
-    if (k0 < m) return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + k0));
+    if (k0 < m) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(row + k0);
+      return __builtin_bit_cast(bf16x8, nt && kNT ? __builtin_nontemporal_load(q) : *q);
+    }
     return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
   uint32_t w[4];
@@ -123,16 +158,29 @@ __device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, in
   return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
 }
 
+// 4 consecutive bf16 of a U or V row starting at k0 (zeros past m).
+__device__ __forceinline__ short4_t load_k4(const uint16_t* row, int k0, int m, int vec) {
+  if (vec) {
+    if (k0 < m) return __builtin_bit_cast(short4_t, *reinterpret_cast<const u32x2*>(row + k0));
+    return short4_t{0, 0, 0, 0};
+  }
+  short4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (k0 + j < m) ? (short)row[k0 + j] : (short)0;
+  return r;
+}
+
 // Feature (within the window) that MFMA tile T row rho stands for: rows 4g..4g+3 of tile
 // T = 2r + q land in lane group g as features 32r + 8g + 4q + (0..3).
 __device__ __forceinline__ int tile_row_feature(int T, int rho) {
   return 32 * (T >> 1) + 8 * (rho >> 2) + 4 * (T & 1) + (rho & 3);
 }
 
-template <int W, int MAXS>
-__device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx<W, MAXS>& C,
-                                          int tile, int g, int n, TileIn<W>& in) {
+template <int W, int KM>
+__device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx& C, int tile,
+                                          int g, int n, TileIn<W, KM>& in) {
   constexpr int NR = W / 32;
+  using K = KTraits<KM>;
   const int t = tile * kTileTokens + n;
   const bool valid = t < C.n_tokens;
   in.drow = valid ? dst_row(P, (int64_t)C.dst_offset + t) : -1;
@@ -141,117 +189,127 @@ __device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx
   const bool have = valid && row != nullptr;
 #pragma unroll
   for (int r = 0; r < NR; ++r)
-    in.raw[r] = have ? *reinterpret_cast<const u32x4*>(row + 32 * r + 8 * g)
-                     : u32x4{0u, 0u, 0u, 0u};
-  if constexpr (MAXS > 0) {
+    in.raw[r] = have ? ld_stream(row + 32 * r + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+  if constexpr (K::k16) {
+    in.u16 = (valid && C.m > 0) ? load_k4(C.U + (int64_t)t * C.m, 4 * g, C.m, C.vec_uv)
+                                : short4_t{0, 0, 0, 0};
+  }
+  if constexpr (K::s32 > 0) {
 #pragma unroll
-    for (int s = 0; s < MAXS; ++s) {
-      if (s < C.steps && valid)
-        in.ub[s] = load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv);
-      else
-        in.ub[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int s = 0; s < K::s32; ++s)
+      in.u32[s] = (s < C.steps32 && valid)
+                      ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv, true)
+                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 }
 
-template <int W, int MAXS>
-__device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCtx<W, MAXS>& C,
-                                           const float2* cs, int tile_lo, int tile_hi) {
+template <int W, int KM>
+struct VFrags {
+  short4_t a16[KTraits<KM>::k16 ? W / 16 : 1];
+  bf16x8 a32[KTraits<KM>::s32 > 0 ? KTraits<KM>::s32 : 1][KTraits<KM>::s32 > 0 ? W / 16 : 1];
+};
+
+template <int W, int KM>
+__device__ __forceinline__ void load_vfrags(const WindowCtx& C, int g, int n, VFrags<W, KM>& vf) {
+  constexpr int NT = W / 16;
+  using K = KTraits<KM>;
+  if (C.m == 0) return;
+  if constexpr (K::k16) {
+#pragma unroll
+    for (int T = 0; T < NT; ++T)
+      vf.a16[T] = load_k4(C.V + (int64_t)tile_row_feature(T, n) * C.m, 4 * g, C.m, C.vec_uv);
+  }
+  if constexpr (K::s32 > 0) {
+#pragma unroll
+    for (int s = 0; s < K::s32; ++s)
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+        vf.a32[s][T] = s < C.steps32 ? load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m,
+                                               32 * s + 8 * g, C.m, C.vec_uv, false)
+                                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// Rotate, patch, round and store one tile whose rows are in `in`.
+template <int W, int KM>
+__device__ __forceinline__ void compute_store(const LaunchParams& P, const WindowCtx& C,
+                                              const float2* cs, const VFrags<W, KM>& vf,
+                                              int tile, int g, int n, const TileIn<W, KM>& in) {
   constexpr int NR = W / 32;   // 32-feature runs per lane
   constexpr int NT = W / 16;   // MFMA tiles per window
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, n = lane & 15;
-  const bool interleaved = P.layout != 0;
-
-  // A operand: V rows of this window, permuted to the lane map, register resident
-  bf16x8 va[MAXS > 0 ? MAXS : 1][NT];
-  if constexpr (MAXS > 0) {
+  using K = KTraits<KM>;
+  u32x4 out[NR];
+  if (C.copy) {
 #pragma unroll
-    for (int s = 0; s < MAXS; ++s)
+    for (int r = 0; r < NR; ++r) out[r] = in.raw[r];
+  } else {
+    float v[NR][8];
 #pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        if (s < C.steps)
-          va[s][T] = load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m, 32 * s + 8 * g, C.m,
-                             C.vec_uv);
-        else
-          va[s][T] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[r][2 * j] = bf_lo(in.raw[r][j]);
+        v[r][2 * j + 1] = bf_hi(in.raw[r][j]);
       }
-  }
-
-  TileIn<W> cur, nxt;
-  if (tile_lo < tile_hi) load_tile<W, MAXS>(P, C, tile_lo, g, n, cur);
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    if (tile + 1 < tile_hi) load_tile<W, MAXS>(P, C, tile + 1, g, n, nxt);
-
-    u32x4 out[NR];
-    if (C.copy) {
+    }
+    if (C.rotate) {
+      if (P.layout != 0) {
+        // interleaved: pair 16r + 4g + j owns features 32r + 8g + (2j, 2j+1)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) out[r] = cur.raw[r];
-    } else {
-      float v[NR][8];
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
+          for (int j = 0; j < 4; ++j) {
+            const float x = v[r][2 * j], y = v[r][2 * j + 1];
+            const float2 p = cs[16 * r + 4 * g + j];
+            v[r][2 * j] = fmaf(x, p.x, -(y * p.y));
+            v[r][2 * j + 1] = fmaf(y, p.x, x * p.y);
+          }
+      } else {
+        // half-split: pair 32r + 8g + jj owns features (i, i + W/2) = runs r and r + NR/2
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[r][2 * j] = bf_lo(cur.raw[r][j]);
-          v[r][2 * j + 1] = bf_hi(cur.raw[r][j]);
-        }
+        for (int r = 0; r < NR / 2; ++r)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float x = v[r][jj], y = v[r + NR / 2][jj];
+            const float2 p = cs[32 * r + 8 * g + jj];
+            v[r][jj] = fmaf(x, p.x, -(y * p.y));
+            v[r + NR / 2][jj] = fmaf(y, p.x, x * p.y);
+          }
       }
-      if (C.rotate) {
-        if (interleaved) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x = v[r][2 * j], y = v[r][2 * j + 1];
-              // pair 16r + 4g + j owns features (2i, 2i+1) = 32r + 8g + (2j, 2j+1)
-              const float2 p = cs[16 * r + 4 * g + j];
-              const float c = p.x, s = p.y;
-              v[r][2 * j] = fmaf(x, c, -(y * s));
-              v[r][2 * j + 1] = fmaf(y, c, x * s);
-            }
-        } else {
-#pragma unroll
-          for (int r = 0; r < NR / 2; ++r)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              // pair 32r + 8g + jj owns features (i, i + W/2)
-              const float x = v[r][jj], y = v[r + NR / 2][jj];
-              const float2 p = cs[32 * r + 8 * g + jj];
-              v[r][jj] = fmaf(x, p.x, -(y * p.y));
-              v[r + NR / 2][jj] = fmaf(y, p.x, x * p.y);
-            }
-        }
-      }
-      if (MAXS != 0 && C.steps > 0) {
+    }
+    if constexpr (KM != 0) {
+      if (C.m > 0) {
         f32x4 acc[NT];
 #pragma unroll
         for (int T = 0; T < NT; ++T)
           acc[T] = f32x4{v[T >> 1][4 * (T & 1)], v[T >> 1][4 * (T & 1) + 1],
                          v[T >> 1][4 * (T & 1) + 2], v[T >> 1][4 * (T & 1) + 3]};
-        if constexpr (MAXS == 0) {
-          // no patch anywhere in this launch
-        } else if constexpr (MAXS > 0) {
+        if constexpr (K::k16) {
 #pragma unroll
-          for (int s = 0; s < MAXS; ++s) {
-            if (s < C.steps) {
+          for (int T = 0; T < NT; ++T)
+            acc[T] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf.a16[T], in.u16, acc[T], 0, 0, 0);
+        } else if constexpr (K::s32 > 0) {
+#pragma unroll
+          for (int s = 0; s < K::s32; ++s) {
+            if (s < C.steps32) {
 #pragma unroll
               for (int T = 0; T < NT; ++T)
-                acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[s][T], cur.ub[s], acc[T], 0,
-                                                                 0, 0);
+                acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.a32[s][T], in.u32[s], acc[T],
+                                                                 0, 0, 0);
             }
           }
         } else {
           // streamed: any m <= 256, both operands read per tile (V from L1/L2)
           const int t = tile * kTileTokens + n;
           const bool valid = t < C.n_tokens;
-          for (int s = 0; s < C.steps; ++s) {
-            const bf16x8 b = valid ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv)
+          for (int s = 0; s < C.steps32; ++s) {
+            const bf16x8 b = valid ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m,
+                                             C.vec_uv, true)
                                    : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
             for (int T = 0; T < NT; ++T) {
-              const bf16x8 a = load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m, 32 * s + 8 * g,
-                                       C.m, C.vec_uv);
+              const bf16x8 a = load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m,
+                                       32 * s + 8 * g, C.m, C.vec_uv, false);
               acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[T], 0, 0, 0);
             }
           }
@@ -261,31 +319,68 @@ __device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCt
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[T >> 1][4 * (T & 1) + i] = acc[T][i];
       }
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-        out[r] = u32x4{pack_bf16(v[r][0], v[r][1]), pack_bf16(v[r][2], v[r][3]),
-                       pack_bf16(v[r][4], v[r][5]), pack_bf16(v[r][6], v[r][7])};
     }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      out[r] = u32x4{pack_bf16(v[r][0], v[r][1]), pack_bf16(v[r][2], v[r][3]),
+                     pack_bf16(v[r][4], v[r][5]), pack_bf16(v[r][6], v[r][7])};
+  }
 
-    const int t = tile * kTileTokens + n;
-    if (t < C.n_tokens) {
-      if (cur.drow >= 0) {
-        uint16_t* row = C.pool + cur.drow;
+  const int t = tile * kTileTokens + n;
+  if (t < C.n_tokens) {
+    if (in.drow >= 0) {
+      uint16_t* row = C.pool + in.drow;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) *reinterpret_cast<u32x4*>(row + 32 * r + 8 * g) = out[r];
-      } else if (g == 0) {
-        atomicAdd(P.fault_counter, 1u);
-      }
+      for (int r = 0; r < NR; ++r) st_stream(row + 32 * r + 8 * g, out[r]);
+    } else if (g == 0) {
+      atomicAdd(P.fault_counter, 1u);
     }
-    cur = nxt;
   }
 }
 
-template <int MAXS>
+// One wave's share of a block: one window, tiles [tile_lo, tile_hi). Every thread of the
+// block calls this (the phase table barrier is inside); inactive waves only join the barrier.
+template <int W, int KM>
+__device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCtx& C,
+                                           const JobDesc& J, float2* cs, bool active,
+                                           int tile_lo, int tile_hi) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, n = lane & 15;
+  // tiles loaded ahead of the one computed, and the ring of tile buffers
+  constexpr int kDepth = KM == 64 ? KAMERA_PREFETCH_TILES_RANK64 : KAMERA_PREFETCH_TILES;
+  constexpr int R = kDepth + 1;
+
+  VFrags<W, KM> vf;
+  TileIn<W, KM> ring[R];
+  if (active) {
+    // first loads go out before the phase table is built, so their latency overlaps it
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      if (tile_lo + k < tile_hi) load_tile<W, KM>(P, C, tile_lo + k, g, n, ring[k]);
+    if constexpr (KM != 0) load_vfrags<W, KM>(C, g, n, vf);
+  }
+  if (C.rotate) {
+    fill_phases(cs, J.delta, P.theta, J.rot_dim);
+    __syncthreads();
+  }
+  if (!active) return;
+
+  for (int base = tile_lo; base < tile_hi; base += R) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int tile = base + k;
+      if (tile + kDepth < tile_hi)
+        load_tile<W, KM>(P, C, tile + kDepth, g, n, ring[(k + kDepth) % R]);
+      if (tile < tile_hi) compute_store<W, KM>(P, C, cs, vf, tile, g, n, ring[k]);
+    }
+  }
+}
+
+template <int KM>
 __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const LaunchParams P) {
   __shared__ float2 cs[64];
   const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
-  const JobDesc& J = P.jobs[find_job(P.jobs, P.n_jobs, blk)];
+  const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
   int local = blk - J.block_start;
   const int tg = local % J.n_tgroups;
@@ -293,16 +388,10 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const Launch
   const int wg = local % J.n_wgroups;
   const int layer = local / J.n_wgroups;
 
-  const int rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
-  if (rotate) {
-    fill_phases(cs, J.delta, P.theta, J.rot_dim);
-    __syncthreads();
-  }
-
   const int wave = threadIdx.x >> 6;
   const int nwin = min(4, J.n_windows - 4 * wg);
   const int sub = 4 / nwin;                       // waves sharing one window
-  if (wave >= nwin * sub) return;
+  const bool active = wave < nwin * sub;
   const int win = 4 * wg + wave % nwin;
   const int part = wave / nwin;
 
@@ -315,29 +404,25 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const Launch
   const int f0 = (win % J.wph) * J.win_width;
   const int64_t feat = (int64_t)head * J.head_width + f0;
 
-  const int steps = (J.m + 31) / 32;
-  auto make = [&](auto wtag) {
-    constexpr int Wv = decltype(wtag)::value;
-    WindowCtx<Wv, MAXS> C;
-    C.src = static_cast<const uint16_t*>(J.src) + (J.src ? layer * J.src_ls + feat : 0);
-    C.pool = static_cast<uint16_t*>(J.pool) + layer * P.pool_ls + feat;
-    C.U = J.m > 0 ? static_cast<const uint16_t*>(J.U) + layer * J.u_ls + head * J.u_hs : nullptr;
-    C.V = J.m > 0 ? static_cast<const uint16_t*>(J.V) + layer * J.v_ls + head * J.v_hs +
-                        (int64_t)f0 * J.m
-                  : nullptr;
-    C.src_ts = J.src_ts;
-    C.n_tokens = J.n_tokens;
-    C.dst_offset = J.dst_offset;
-    C.m = J.m;
-    C.steps = steps;
-    C.vec_uv = J.vec_uv;
-    C.rotate = rotate;
-    C.copy = (!rotate && J.m == 0) ? 1 : 0;
-    C.patch_mode = P.mode == MODE_PATCH;
-    run_window<Wv, MAXS>(P, C, cs, tile_lo, tile_hi);
-  };
-  if (J.win_width == 128) make(std::integral_constant<int, 128>{});
-  else make(std::integral_constant<int, 64>{});
+  WindowCtx C;
+  C.rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
+  C.src = J.src ? static_cast<const uint16_t*>(J.src) + layer * J.src_ls + feat : nullptr;
+  C.pool = static_cast<uint16_t*>(J.pool) + layer * P.pool_ls + feat;
+  C.U = J.m > 0 ? static_cast<const uint16_t*>(J.U) + layer * J.u_ls + head * J.u_hs : nullptr;
+  C.V = J.m > 0 ? static_cast<const uint16_t*>(J.V) + layer * J.v_ls + head * J.v_hs +
+                      (int64_t)f0 * J.m
+                : nullptr;
+  C.src_ts = J.src_ts;
+  C.n_tokens = J.n_tokens;
+  C.dst_offset = J.dst_offset;
+  C.m = J.m;
+  C.steps32 = (J.m + 31) / 32;
+  C.vec_uv = J.vec_uv;
+  C.copy = (!C.rotate && J.m == 0) ? 1 : 0;
+  C.patch_mode = P.mode == MODE_PATCH;
+
+  if (J.win_width == 128) run_window<128, KM>(P, C, J, cs, active, tile_lo, tile_hi);
+  else run_window<64, KM>(P, C, J, cs, active, tile_lo, tile_hi);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -357,7 +442,7 @@ template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const LaunchParams P) {
   __shared__ float2 cs[kMaxPairs];
   const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
-  const JobDesc& J = P.jobs[find_job(P.jobs, P.n_jobs, blk)];
+  const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
   int local = blk - J.block_start;
   const int tg = local % J.n_tgroups;
@@ -436,12 +521,13 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
 
 }  // namespace
 
-hipError_t launch_mfma(const LaunchParams& p, int max_steps, hipStream_t stream) {
+hipError_t launch_mfma(const LaunchParams& p, int kmode, hipStream_t stream) {
   const dim3 grid(p.total_blocks), block(kBlockThreads);
-  switch (max_steps) {
+  switch (kmode) {
     case 0: hipLaunchKernelGGL(kamera_mfma_kernel<0>, grid, block, 0, stream, p); break;
-    case 1: hipLaunchKernelGGL(kamera_mfma_kernel<1>, grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(kamera_mfma_kernel<2>, grid, block, 0, stream, p); break;
+    case 16: hipLaunchKernelGGL(kamera_mfma_kernel<16>, grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(kamera_mfma_kernel<32>, grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(kamera_mfma_kernel<64>, grid, block, 0, stream, p); break;
     default: hipLaunchKernelGGL(kamera_mfma_kernel<-1>, grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
