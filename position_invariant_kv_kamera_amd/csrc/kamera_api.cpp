@@ -462,6 +462,9 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   lp.page_table = cache->page_table;
   lp.n_logical_pages = cache->n_logical_pages;
   lp.page_size = cache->page_size;
+  lp.page_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if (cache->page_size == (1 << b)) lp.page_shift = b;
   lp.n_pages = cache->n_pages;
   lp.layout = model->rope_layout;
   lp.pool_ls = cache->layer_stride;

@@ -45,6 +45,7 @@ struct LaunchParams {
   const int32_t* page_table;
   int32_t n_logical_pages;
   int32_t page_size;
+  int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t n_pages;
   int32_t layout;           // kamera_rope_layout
   int64_t pool_ls;          // pool layer stride (elements)
@@ -62,8 +63,10 @@ constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
 constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 
 // Tiles a wave keeps in flight ahead of the one it computes (the m <= 64 variant holds its V
-// operand in 64 more registers and keeps one), and whether streamed rows use nontemporal
-// loads and stores. Build-time knobs; the defaults are the measured best on MI355X.
+// operand in 64 more registers and keeps one); whether streamed rows use nontemporal loads
+// and stores; whether rows are staged through LDS so that every global access instruction
+// covers whole cache lines. Build-time knobs; the defaults are the measured best on MI355X
+// (nontemporal access only pays once rows are staged: half-line accesses defeat L2 merging).
 #ifndef KAMERA_PREFETCH_TILES
 #define KAMERA_PREFETCH_TILES 3
 #endif
@@ -71,7 +74,13 @@ constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 #define KAMERA_PREFETCH_TILES_RANK64 1
 #endif
 #ifndef KAMERA_NONTEMPORAL
-#define KAMERA_NONTEMPORAL 0
+#define KAMERA_NONTEMPORAL 1
+#endif
+#ifndef KAMERA_LDS_STAGE
+#define KAMERA_LDS_STAGE 1
+#endif
+#ifndef KAMERA_PHASE_RELOAD
+#define KAMERA_PHASE_RELOAD 0
 #endif
 
 // kmode: largest rank in the launch, rounded up: 0 (no patch), 16, 32 or 64 keep the V

@@ -42,6 +42,36 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr bool kNT = KAMERA_NONTEMPORAL != 0;
 
+// Device-memory accesses go through address-space-1 pointers: the row pointers come from the
+// job table, so the compiler cannot tell them from LDS and would otherwise emit FLAT
+// instructions, whose completion also counts against the LDS wait counter and would make
+// every LDS wait of the staging transpose drain the prefetched loads.
+#define KGLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const KGLOBAL T* gp(const T* p) { return (const KGLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ KGLOBAL T* gp(T* p) { return (KGLOBAL T*)p; }
+// Row staging: global loads and stores use a row-contiguous lane map (each instruction covers
+// whole 128-byte lines), and a padded wave-private LDS tile transposes rows to and from the
+// MFMA lane map.
+constexpr bool kStage = KAMERA_LDS_STAGE != 0;
+constexpr int kStageRowBytes = 2 * 128 + 16;                // padded row of a 128-wide window
+constexpr int kStageWaveBytes = kTileTokens * kStageRowBytes;
+
+// Orders this wave's LDS accesses across lanes: writes before the fence are seen by reads
+// after it (a wave's LDS operations complete in order; this stops the compiler reordering).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src_lane) {
+  const int lo = __shfl((int)(uint32_t)(uint64_t)v, src_lane, 64);
+  const int hi = __shfl((int)(uint32_t)((uint64_t)v >> 32), src_lane, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -56,12 +86,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 // Streamed 16-byte row pieces: read once, written once.
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const KGLOBAL u32x4* q = gp(reinterpret_cast<const u32x4*>(p));
   if constexpr (kNT) return __builtin_nontemporal_load(q);
   else return *q;
 }
 __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
-  u32x4* q = reinterpret_cast<u32x4*>(p);
+  KGLOBAL u32x4* q = gp(reinterpret_cast<u32x4*>(p));
   if constexpr (kNT) __builtin_nontemporal_store(v, q);
   else *q = v;
 }
@@ -83,7 +113,7 @@ __device__ __forceinline__ int find_job(const int32_t* block_starts, int n_jobs,
   int count = 0;
   for (int base = 0; base < n_jobs; base += 64) {
     const int j = base + lane;
-    const bool le = j < n_jobs && block_starts[j] <= blk;
+    const bool le = j < n_jobs && gp(block_starts)[j] <= blk;
     count += __popcll(__ballot(le));
   }
   return count - 1;
@@ -100,13 +130,24 @@ __device__ __forceinline__ void fill_phases(float2* cs, int64_t delta, double th
   }
 }
 
+__device__ __forceinline__ void count_fault(const LaunchParams& P) {
+  __hip_atomic_fetch_add(gp(P.fault_counter), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Destination row (element offset of feature 0 of the row's first head) of logical token p,
 // or -1 when the page-table entry is outside [0, n_pages).
 __device__ __forceinline__ int64_t dst_row(const LaunchParams& P, int64_t p) {
-  const int64_t page = p / P.page_size;
-  const int64_t phys = P.page_table ? (int64_t)P.page_table[page] : page;
+  int64_t page, slot;
+  if (P.page_shift >= 0) {
+    page = p >> P.page_shift;
+    slot = p & ((int64_t(1) << P.page_shift) - 1);
+  } else {
+    page = p / P.page_size;
+    slot = p - page * P.page_size;
+  }
+  const int64_t phys = P.page_table ? (int64_t)gp(P.page_table)[page] : page;
   if (phys < 0 || phys >= P.n_pages) return -1;
-  return (phys * P.page_size + (p - page * P.page_size)) * P.pool_ts;
+  return (phys * P.page_size + slot) * P.pool_ts;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -124,7 +165,7 @@ struct KTraits {
 
 template <int W, int KM>
 struct TileIn {
-  u32x4 raw[W / 32];                                  // token t0+n, features 32r + 8g .. +8
+  u32x4 raw[W / 32];   // token t0+n, features 32r + 8g .. +8 (row staging: row-map pieces)
   short4_t u16;                                       // B operand, KM == 16
   bf16x8 u32[KTraits<KM>::s32 > 0 ? KTraits<KM>::s32 : 1];  // B operand, KM == 32 / 64
   int64_t drow;                                       // destination element offset, -1 = skip
@@ -135,6 +176,7 @@ struct WindowCtx {
   uint16_t* pool;        // pool of this layer, + head/window feature offset
   const uint16_t* U;     // U of this layer/head (row t at + t*m)
   const uint16_t* V;     // V of this layer/head, + window feature offset (row f at + f*m)
+  uint8_t* stage;        // this wave's LDS tile (row staging)
   int64_t src_ts;
   int32_t n_tokens, dst_offset, m, vec_uv, rotate, copy, patch_mode, steps32;
 };
@@ -143,7 +185,7 @@ struct WindowCtx {
 __device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, int vec, bool nt) {
   if (vec) {
     if (k0 < m) {
-      const u32x4* q = reinterpret_cast<const u32x4*>(row + k0);
+      const KGLOBAL u32x4* q = gp(reinterpret_cast<const u32x4*>(row + k0));
       return __builtin_bit_cast(bf16x8, nt && kNT ? __builtin_nontemporal_load(q) : *q);
     }
     return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -151,8 +193,8 @@ __device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, in
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t a = (k0 + 2 * j < m) ? row[k0 + 2 * j] : 0u;
-    const uint32_t b = (k0 + 2 * j + 1 < m) ? row[k0 + 2 * j + 1] : 0u;
+    const uint32_t a = (k0 + 2 * j < m) ? gp(row)[k0 + 2 * j] : 0u;
+    const uint32_t b = (k0 + 2 * j + 1 < m) ? gp(row)[k0 + 2 * j + 1] : 0u;
     w[j] = a | (b << 16);
   }
   return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
@@ -161,12 +203,12 @@ __device__ __forceinline__ bf16x8 load_k8(const uint16_t* row, int k0, int m, in
 // 4 consecutive bf16 of a U or V row starting at k0 (zeros past m).
 __device__ __forceinline__ short4_t load_k4(const uint16_t* row, int k0, int m, int vec) {
   if (vec) {
-    if (k0 < m) return __builtin_bit_cast(short4_t, *reinterpret_cast<const u32x2*>(row + k0));
+    if (k0 < m) return __builtin_bit_cast(short4_t, *gp(reinterpret_cast<const u32x2*>(row + k0)));
     return short4_t{0, 0, 0, 0};
   }
   short4_t r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = (k0 + j < m) ? (short)row[k0 + j] : (short)0;
+  for (int j = 0; j < 4; ++j) r[j] = (k0 + j < m) ? (short)gp(row)[k0 + j] : (short)0;
   return r;
 }
 
@@ -184,12 +226,33 @@ __device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx
   const int t = tile * kTileTokens + n;
   const bool valid = t < C.n_tokens;
   in.drow = valid ? dst_row(P, (int64_t)C.dst_offset + t) : -1;
-  const uint16_t* row = C.patch_mode ? (in.drow >= 0 ? C.pool + in.drow : nullptr)
-                                     : C.src + (int64_t)t * C.src_ts;
-  const bool have = valid && row != nullptr;
+  if constexpr (kStage) {
+    // row map: instruction k, lane l -> token TPI*k + l/PR of the tile, 16-byte piece l%PR
+    constexpr int PR = W / 8, TPI = 64 / PR;
+    const int lane = threadIdx.x & 63;
+    const int piece = lane % PR, tsub = lane / PR;
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
-    in.raw[r] = have ? ld_stream(row + 32 * r + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < NR; ++k) {
+      const int tl = TPI * k + tsub;
+      const int tt = tile * kTileTokens + tl;
+      const uint16_t* row;
+      if (C.patch_mode) {
+        const int64_t d = shfl64(in.drow, tl);
+        row = d >= 0 ? C.pool + d : nullptr;
+      } else {
+        row = C.src + (int64_t)tt * C.src_ts;
+      }
+      in.raw[k] = (tt < C.n_tokens && row != nullptr) ? ld_stream(row + 8 * piece)
+                                                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    const uint16_t* row = C.patch_mode ? (in.drow >= 0 ? C.pool + in.drow : nullptr)
+                                       : C.src + (int64_t)t * C.src_ts;
+    const bool have = valid && row != nullptr;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      in.raw[r] = have ? ld_stream(row + 32 * r + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+  }
   if constexpr (K::k16) {
     in.u16 = (valid && C.m > 0) ? load_k4(C.U + (int64_t)t * C.m, 4 * g, C.m, C.vec_uv)
                                 : short4_t{0, 0, 0, 0};
@@ -238,18 +301,37 @@ __device__ __forceinline__ void compute_store(const LaunchParams& P, const Windo
   constexpr int NR = W / 32;   // 32-feature runs per lane
   constexpr int NT = W / 16;   // MFMA tiles per window
   using K = KTraits<KM>;
+  constexpr int PR = W / 8, TPI = 64 / PR;
+  const int lane = threadIdx.x & 63;
+  const int piece = lane % PR, tsub = lane / PR;
+  constexpr int RS = 2 * W + 16;   // padded LDS row (bytes): conflict-free column reads
+  u32x4 mraw[NR];                  // the tile in the MFMA lane map
+  if constexpr (kStage) {
+    if (!C.copy) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        *reinterpret_cast<u32x4*>(C.stage + (TPI * k + tsub) * RS + 16 * piece) = in.raw[k];
+      wave_lds_sync();
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        mraw[r] = *reinterpret_cast<const u32x4*>(C.stage + n * RS + 64 * r + 16 * g);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) mraw[r] = in.raw[r];
+  }
   u32x4 out[NR];
   if (C.copy) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) out[r] = in.raw[r];
+    for (int r = 0; r < NR; ++r) out[r] = in.raw[r];   // either lane map: stored as loaded
   } else {
     float v[NR][8];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[r][2 * j] = bf_lo(in.raw[r][j]);
-        v[r][2 * j + 1] = bf_hi(in.raw[r][j]);
+        v[r][2 * j] = bf_lo(mraw[r][j]);
+        v[r][2 * j + 1] = bf_hi(mraw[r][j]);
       }
     }
     if (C.rotate) {
@@ -327,13 +409,37 @@ __device__ __forceinline__ void compute_store(const LaunchParams& P, const Windo
   }
 
   const int t = tile * kTileTokens + n;
-  if (t < C.n_tokens) {
-    if (in.drow >= 0) {
-      uint16_t* row = C.pool + in.drow;
+  if constexpr (kStage) {
+    u32x4 orow[NR];
+    if (C.copy) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) st_stream(row + 32 * r + 8 * g, out[r]);
-    } else if (g == 0) {
-      atomicAdd(P.fault_counter, 1u);
+      for (int k = 0; k < NR; ++k) orow[k] = out[k];
+    } else {
+      wave_lds_sync();
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        *reinterpret_cast<u32x4*>(C.stage + n * RS + 64 * r + 16 * g) = out[r];
+      wave_lds_sync();
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        orow[k] = *reinterpret_cast<const u32x4*>(C.stage + (TPI * k + tsub) * RS + 16 * piece);
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int tl = TPI * k + tsub;
+      const int64_t d = shfl64(in.drow, tl);
+      if (tile * kTileTokens + tl < C.n_tokens && d >= 0) st_stream(C.pool + d + 8 * piece, orow[k]);
+    }
+    if (t < C.n_tokens && in.drow < 0 && g == 0) count_fault(P);
+  } else {
+    if (t < C.n_tokens) {
+      if (in.drow >= 0) {
+        uint16_t* row = C.pool + in.drow;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) st_stream(row + 32 * r + 8 * g, out[r]);
+      } else if (g == 0) {
+        count_fault(P);
+      }
     }
   }
 }
@@ -369,6 +475,10 @@ __device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCt
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int tile = base + k;
+#if KAMERA_PHASE_RELOAD
+      // re-read the phase table every tile instead of pinning 32 VGPRs for it
+      asm volatile("" ::: "memory");
+#endif
       if (tile + kDepth < tile_hi)
         load_tile<W, KM>(P, C, tile + kDepth, g, n, ring[(k + kDepth) % R]);
       if (tile < tile_hi) compute_store<W, KM>(P, C, cs, vf, tile, g, n, ring[k]);
@@ -379,6 +489,7 @@ __device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCt
 template <int KM>
 __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const LaunchParams P) {
   __shared__ float2 cs[64];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStage ? 4 * kStageWaveBytes : 16];
   const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
   const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
@@ -420,6 +531,7 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const Launch
   C.vec_uv = J.vec_uv;
   C.copy = (!C.rotate && J.m == 0) ? 1 : 0;
   C.patch_mode = P.mode == MODE_PATCH;
+  C.stage = stage + (kStage ? wave * kStageWaveBytes : 0);
 
   if (J.win_width == 128) run_window<128, KM>(P, C, J, cs, active, tile_lo, tile_hi);
   else run_window<64, KM>(P, C, J, cs, active, tile_lo, tile_hi);
@@ -429,12 +541,14 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const Launch
 // VALU path
 // ---------------------------------------------------------------------------------------
 
-template <typename T> __device__ __forceinline__ float ld(const T* p);
-template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
-template <typename T> __device__ __forceinline__ void st(T* p, float v);
-template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
-template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float v) {
+template <typename T> __device__ __forceinline__ float ld(const KGLOBAL T* p);
+template <> __device__ __forceinline__ float ld<float>(const KGLOBAL float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const KGLOBAL uint16_t* p) {
+  return bf16_to_f32(*p);
+}
+template <typename T> __device__ __forceinline__ void st(KGLOBAL T* p, float v);
+template <> __device__ __forceinline__ void st<float>(KGLOBAL float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<uint16_t>(KGLOBAL uint16_t* p, float v) {
   *p = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
@@ -466,10 +580,10 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
   const int64_t items = (int64_t)nh * nt * half;
   const int m = J.m;
 
-  const T* src = static_cast<const T*>(J.src);
-  T* pool = static_cast<T*>(J.pool) + layer * P.pool_ls;
-  const T* U = static_cast<const T*>(J.U);
-  const T* V = static_cast<const T*>(J.V);
+  const KGLOBAL T* src = gp(static_cast<const T*>(J.src));
+  KGLOBAL T* pool = gp(static_cast<T*>(J.pool)) + layer * P.pool_ls;
+  const KGLOBAL T* U = gp(static_cast<const T*>(J.U));
+  const KGLOBAL T* V = gp(static_cast<const T*>(J.V));
 
   for (int64_t it = threadIdx.x; it < items; it += kBlockThreads) {
     const int q = (int)(it % half);
@@ -482,11 +596,11 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
 
     const int64_t drow = dst_row(P, (int64_t)J.dst_offset + t);
     if (drow < 0) {
-      if (q == 0) atomicAdd(P.fault_counter, 1u);
+      if (q == 0) count_fault(P);
       continue;
     }
-    T* out = pool + drow + (int64_t)head * D;
-    const T* in = P.mode == MODE_PATCH ? out
+    KGLOBAL T* out = pool + drow + (int64_t)head * D;
+    const KGLOBAL T* in = P.mode == MODE_PATCH ? out
                                        : src + layer * J.src_ls + (int64_t)t * J.src_ts +
                                              (int64_t)head * D;
     if (!rotate && m == 0) {   // bit copy
@@ -503,8 +617,8 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
       xb = rb;
     }
     if (m > 0) {
-      const T* urow = U + layer * J.u_ls + head * J.u_hs + (int64_t)t * m;
-      const T* vbase = V + layer * J.v_ls + head * J.v_hs;
+      const KGLOBAL T* urow = U + layer * J.u_ls + head * J.u_hs + (int64_t)t * m;
+      const KGLOBAL T* vbase = V + layer * J.v_ls + head * J.v_hs;
       float pa = 0.f, pb = 0.f;
       for (int r = 0; r < m; ++r) {
         const float u = ld<T>(urow + r);
