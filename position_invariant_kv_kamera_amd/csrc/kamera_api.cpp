@@ -34,6 +34,7 @@ kamera_status fail(kamera_status st, const char* fmt, ...) {
 }
 
 constexpr size_t kHeaderBytes = 256;
+constexpr int64_t kTargetBlocks = 72 * 1024;   // grid size the tiles-per-wave choice aims under
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -383,24 +384,36 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
       }
     }
   }
-  // Token groups of the MFMA jobs: each wave gets `tpw` tiles of one window. Small batches
-  // take short waves (more blocks to spread over 256 CUs), large ones long waves (less
-  // per-block set-up): measured best at 8 tiles up to ~30K blocks, 16 up to ~120K, else 32.
+  // Token groups of the MFMA jobs: each wave gets `tpw` tiles of one window. Equal blocks end
+  // on a partly filled last round, so short waves (many blocks) shrink that tail; but every
+  // block reloads its V operand (16 KB per window at m = 64), so rank > 32 takes long waves.
+  // Measured on MI355X: the smallest tpw in {4, 8, 16, 32, 64} whose grid stays within
+  // ~72K blocks, at least 32 when some m > 32.
   auto tgroups = [](const JobDesc& j, int tpw) {
     const int sub = 4 / std::min(4, j.n_windows);
     return std::max(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
   };
-  int64_t blocks8 = 0;
-  for (const JobDesc& j : plan->mfma) blocks8 += (int64_t)m.n_layers * j.n_wgroups * tgroups(j, 8);
-  int tpw = blocks8 > 120000 ? 32 : blocks8 > 30000 ? 16 : 8;
+  auto blocks_at = [&](int tpw) {
+    int64_t b = 0;
+    for (const JobDesc& j : plan->mfma) b += (int64_t)m.n_layers * j.n_wgroups * tgroups(j, tpw);
+    return b;
+  };
+  int tpw = plan->mfma_max_m > 32 ? 32 : 4;
+  while (tpw < 64 && blocks_at(tpw) > kTargetBlocks) tpw *= 2;
   tpw = std::max(1, env_int("KAMERA_TILES_PER_WAVE", tpw));
   for (JobDesc& j : plan->mfma) j.n_tgroups = tgroups(j, tpw);
 
-  // heaviest jobs first so that a mixed batch does not end on a tail of patched work
-  auto heavier = [](const JobDesc& a, const JobDesc& b) { return a.m > b.m; };
+  // grouped by window width (one launch each), heaviest jobs first inside a group so that a
+  // mixed batch does not end on a tail of patched work
+  auto heavier = [](const JobDesc& a, const JobDesc& b) {
+    if (a.win_width != b.win_width) return a.win_width > b.win_width;
+    return a.m > b.m;
+  };
   std::stable_sort(plan->mfma.begin(), plan->mfma.end(), heavier);
   std::stable_sort(plan->valu.begin(), plan->valu.end(), heavier);
   auto assign = [&](std::vector<JobDesc>& jobs, int64_t* total) -> bool {
+    // block_start counts from the first job of the vector; a launch over a sub-range of it
+    // numbers its blocks from that range's first start (LaunchParams::block_base)
     int64_t b = 0;
     for (JobDesc& j : jobs) {
       j.block_start = (int32_t)b;
@@ -474,14 +487,24 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
   lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (!plan.mfma.empty()) {
-    lp.jobs = reinterpret_cast<const JobDesc*>(ws + mfma_off);
-    lp.block_starts = reinterpret_cast<const int32_t*>(ws + mfma_bs_off);
-    lp.n_jobs = (int32_t)plan.mfma.size();
-    lp.total_blocks = (int32_t)plan.mfma_blocks;
-    hipError_t e = kamera::launch_mfma(lp, kmode_for(plan.mfma_max_m), stream);
+  // MFMA jobs: one launch per window width (jobs are grouped by width in build_plan)
+  for (size_t lo = 0; lo < plan.mfma.size();) {
+    size_t hi = lo;
+    int max_m = 0;
+    while (hi < plan.mfma.size() && plan.mfma[hi].win_width == plan.mfma[lo].win_width)
+      max_m = std::max(max_m, plan.mfma[hi++].m);
+    lp.jobs = reinterpret_cast<const JobDesc*>(ws + mfma_off) + lo;
+    lp.block_starts = reinterpret_cast<const int32_t*>(ws + mfma_bs_off) + lo;
+    lp.n_jobs = (int32_t)(hi - lo);
+    const int32_t first = plan.mfma[lo].block_start;
+    const int64_t last = hi < plan.mfma.size() ? plan.mfma[hi].block_start : plan.mfma_blocks;
+    lp.block_base = first;
+    lp.total_blocks = (int32_t)(last - first);
+    hipError_t e = kamera::launch_mfma(lp, plan.mfma[lo].win_width, kmode_for(max_m), stream);
     if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "MFMA kernel launch: %s", hipGetErrorString(e));
+    lo = hi;
   }
+  lp.block_base = 0;
   if (!plan.valu.empty()) {
     lp.jobs = reinterpret_cast<const JobDesc*>(ws + valu_off);
     lp.block_starts = reinterpret_cast<const int32_t*>(ws + valu_bs_off);

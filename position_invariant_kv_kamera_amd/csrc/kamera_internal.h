@@ -42,6 +42,7 @@ struct LaunchParams {
   const int32_t* block_starts;  // device: jobs[i].block_start, compact (one int per job)
   int32_t n_jobs;
   int32_t total_blocks;
+  int32_t block_base;       // block_start of jobs[0]: job block ranges are offset by it
   const int32_t* page_table;
   int32_t n_logical_pages;
   int32_t page_size;
@@ -62,13 +63,19 @@ constexpr int kTileTokens = 16;         // MFMA N dimension
 constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
 constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 
-// Tiles a wave keeps in flight ahead of the one it computes (the m <= 64 variant holds its V
-// operand in 64 more registers and keeps one); whether streamed rows use nontemporal loads
-// and stores; whether rows are staged through LDS so that every global access instruction
-// covers whole cache lines. Build-time knobs; the defaults are the measured best on MI355X
-// (nontemporal access only pays once rows are staged: half-line accesses defeat L2 merging).
+// Build-time knobs; the defaults are the measured best on MI355X.
+//   KAMERA_PREFETCH_TILES(_RANK64): tiles a wave keeps loaded ahead of the one it computes
+//     (ring of PREFETCH+1 tile buffers in registers). Deeper rings cost occupancy and did
+//     not pay.
+//   KAMERA_NONTEMPORAL: streamed rows use nontemporal loads and stores (pays only once rows
+//     are staged: half-line accesses defeat L2 merging).
+//   KAMERA_LDS_STAGE: rows go through a padded LDS tile so every global access instruction
+//     covers whole 128-byte lines.
+//   KAMERA_RING_SHIFT: one copy of the tile body per loop iteration, the ring advancing by
+//     register moves (instead of one unrolled body per ring slot).
+//   KAMERA_WAVES_PER_EU: occupancy the compiler is asked to fit (0 = its own choice).
 #ifndef KAMERA_PREFETCH_TILES
-#define KAMERA_PREFETCH_TILES 3
+#define KAMERA_PREFETCH_TILES 1
 #endif
 #ifndef KAMERA_PREFETCH_TILES_RANK64
 #define KAMERA_PREFETCH_TILES_RANK64 1
@@ -79,13 +86,17 @@ constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 #ifndef KAMERA_LDS_STAGE
 #define KAMERA_LDS_STAGE 1
 #endif
-#ifndef KAMERA_PHASE_RELOAD
-#define KAMERA_PHASE_RELOAD 0
+#ifndef KAMERA_RING_SHIFT
+#define KAMERA_RING_SHIFT 1
+#endif
+#ifndef KAMERA_WAVES_PER_EU
+#define KAMERA_WAVES_PER_EU 0
 #endif
 
-// kmode: largest rank in the launch, rounded up: 0 (no patch), 16, 32 or 64 keep the V
-// operand in registers; -1 streams it from memory for any m <= 256.
-hipError_t launch_mfma(const LaunchParams& p, int kmode, hipStream_t stream);
+// One launch covers jobs of one window width (64 or 128). kmode: largest rank in the launch,
+// rounded up: 0 (no patch), 16, 32 or 64 keep the V operand in registers; -1 streams it from
+// memory for any m <= 256.
+hipError_t launch_mfma(const LaunchParams& p, int win_width, int kmode, hipStream_t stream);
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_valu(const LaunchParams& p, int dtype, hipStream_t stream);
 

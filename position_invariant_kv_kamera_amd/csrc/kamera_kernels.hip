@@ -471,26 +471,42 @@ __device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCt
   }
   if (!active) return;
 
+#if KAMERA_RING_SHIFT
+  // one copy of the tile body; the ring advances by register moves
+#pragma unroll 1
+  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+    if (tile + kDepth < tile_hi) load_tile<W, KM>(P, C, tile + kDepth, g, n, ring[kDepth]);
+    compute_store<W, KM>(P, C, cs, vf, tile, g, n, ring[0]);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) ring[k] = ring[k + 1];
+  }
+#else
   for (int base = tile_lo; base < tile_hi; base += R) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int tile = base + k;
-#if KAMERA_PHASE_RELOAD
-      // re-read the phase table every tile instead of pinning 32 VGPRs for it
-      asm volatile("" ::: "memory");
-#endif
       if (tile + kDepth < tile_hi)
         load_tile<W, KM>(P, C, tile + kDepth, g, n, ring[(k + kDepth) % R]);
       if (tile < tile_hi) compute_store<W, KM>(P, C, cs, vf, tile, g, n, ring[k]);
     }
   }
+#endif
 }
 
-template <int KM>
-__global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const LaunchParams P) {
+// Waves per SIMD the compiler must fit: the m <= 64 variant keeps 64 more registers of V
+// operand and stays at 2; the others fit 3 once the accumulators live in VGPRs.
+#if KAMERA_WAVES_PER_EU > 0
+#define KAMERA_OCCUPANCY(KM) \
+  __attribute__((amdgpu_waves_per_eu((KM) == 64 ? 2 : KAMERA_WAVES_PER_EU, 8)))
+#else
+#define KAMERA_OCCUPANCY(KM)
+#endif
+
+template <int W, int KM>
+__global__ __launch_bounds__(kBlockThreads) KAMERA_OCCUPANCY(KM) void kamera_mfma_kernel(const LaunchParams P) {
   __shared__ float2 cs[64];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStage ? 4 * kStageWaveBytes : 16];
-  const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
+  const int blk = P.block_base + remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
   const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
   int local = blk - J.block_start;
@@ -533,8 +549,7 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_mfma_kernel(const Launch
   C.patch_mode = P.mode == MODE_PATCH;
   C.stage = stage + (kStage ? wave * kStageWaveBytes : 0);
 
-  if (J.win_width == 128) run_window<128, KM>(P, C, J, cs, active, tile_lo, tile_hi);
-  else run_window<64, KM>(P, C, J, cs, active, tile_lo, tile_hi);
+  run_window<W, KM>(P, C, J, cs, active, tile_lo, tile_hi);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -555,7 +570,7 @@ template <> __device__ __forceinline__ void st<uint16_t>(KGLOBAL uint16_t* p, fl
 template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const LaunchParams P) {
   __shared__ float2 cs[kMaxPairs];
-  const int blk = remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
+  const int blk = P.block_base + remap_block((int)blockIdx.x, P.total_blocks, P.xcd_remap);
   const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
   int local = blk - J.block_start;
@@ -635,15 +650,21 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
 
 }  // namespace
 
-hipError_t launch_mfma(const LaunchParams& p, int kmode, hipStream_t stream) {
+template <int W>
+void launch_mfma_w(const LaunchParams& p, int kmode, hipStream_t stream) {
   const dim3 grid(p.total_blocks), block(kBlockThreads);
   switch (kmode) {
-    case 0: hipLaunchKernelGGL(kamera_mfma_kernel<0>, grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(kamera_mfma_kernel<16>, grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(kamera_mfma_kernel<32>, grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(kamera_mfma_kernel<64>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(kamera_mfma_kernel<-1>, grid, block, 0, stream, p); break;
+    case 0: hipLaunchKernelGGL((kamera_mfma_kernel<W, 0>), grid, block, 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((kamera_mfma_kernel<W, 16>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((kamera_mfma_kernel<W, 32>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((kamera_mfma_kernel<W, 64>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((kamera_mfma_kernel<W, -1>), grid, block, 0, stream, p); break;
   }
+}
+
+hipError_t launch_mfma(const LaunchParams& p, int win_width, int kmode, hipStream_t stream) {
+  if (win_width == 128) launch_mfma_w<128>(p, kmode, stream);
+  else launch_mfma_w<64>(p, kmode, stream);
   return hipGetLastError();
 }
 
