@@ -34,7 +34,7 @@ kamera_status fail(kamera_status st, const char* fmt, ...) {
 }
 
 constexpr size_t kHeaderBytes = 256;
-constexpr int64_t kTargetBlocks = 72 * 1024;   // grid size the tiles-per-wave choice aims under
+constexpr int64_t kTargetBlocks = 70000;   // grid size the tiles-per-wave choice aims under
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -388,7 +388,7 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
   // on a partly filled last round, so short waves (many blocks) shrink that tail; but every
   // block reloads its V operand (16 KB per window at m = 64), so rank > 32 takes long waves.
   // Measured on MI355X: the smallest tpw in {4, 8, 16, 32, 64} whose grid stays within
-  // ~72K blocks, at least 32 when some m > 32.
+  // ~70K blocks, at least 32 when some m > 32.
   auto tgroups = [](const JobDesc& j, int tpw) {
     const int sub = 4 / std::min(4, j.n_windows);
     return std::max(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
@@ -486,6 +486,8 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   lp.fault_counter = static_cast<uint32_t*>(workspace);
   lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
   lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 0);
+  lp.n_layers = model->n_layers;
+  lp.block_order = env_int("KAMERA_BLOCK_ORDER", 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   // MFMA jobs: one launch per window width (jobs are grouped by width in build_plan)
   for (size_t lo = 0; lo < plan.mfma.size();) {

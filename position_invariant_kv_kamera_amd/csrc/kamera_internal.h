@@ -54,6 +54,8 @@ struct LaunchParams {
   double theta;
   uint32_t* fault_counter;  // device (workspace header)
   int32_t mode;             // Mode
+  int32_t n_layers;
+  int32_t block_order;      // MFMA path: how a job's blocks map to (layer, window group, tokens)
   int32_t xcd_remap;        // 1: consecutive logical blocks run on the same XCD
 };
 

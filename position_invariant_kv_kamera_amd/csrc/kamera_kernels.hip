@@ -510,10 +510,23 @@ __global__ __launch_bounds__(kBlockThreads) KAMERA_OCCUPANCY(KM) void kamera_mfm
   const JobDesc& J = P.jobs[find_job(P.block_starts, P.n_jobs, blk)];
 
   int local = blk - J.block_start;
-  const int tg = local % J.n_tgroups;
-  local /= J.n_tgroups;
-  const int wg = local % J.n_wgroups;
-  const int layer = local / J.n_wgroups;
+  int tg, wg, layer;
+  if (P.block_order == 0) {          // token groups fastest
+    tg = local % J.n_tgroups;
+    local /= J.n_tgroups;
+    wg = local % J.n_wgroups;
+    layer = local / J.n_wgroups;
+  } else if (P.block_order == 1) {   // layers fastest
+    layer = local % P.n_layers;
+    local /= P.n_layers;
+    wg = local % J.n_wgroups;
+    tg = local / J.n_wgroups;
+  } else {                           // window groups, then layers, token groups slowest
+    wg = local % J.n_wgroups;
+    local /= J.n_wgroups;
+    layer = local % P.n_layers;
+    tg = local / P.n_layers;
+  }
 
   const int wave = threadIdx.x >> 6;
   const int nwin = min(4, J.n_windows - 4 * wg);
