@@ -85,6 +85,9 @@ constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 #ifndef KAMERA_NONTEMPORAL
 #define KAMERA_NONTEMPORAL 1
 #endif
+#ifndef KAMERA_NT_MASK
+#define KAMERA_NT_MASK 3   // bit 0: nontemporal row loads, bit 1: nontemporal row stores
+#endif
 #ifndef KAMERA_LDS_STAGE
 #define KAMERA_LDS_STAGE 1
 #endif

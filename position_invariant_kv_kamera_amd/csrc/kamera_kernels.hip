@@ -41,6 +41,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr bool kNT = KAMERA_NONTEMPORAL != 0;
+constexpr bool kNTLoad = kNT && (KAMERA_NT_MASK & 1);    // streamed row loads
+constexpr bool kNTStore = kNT && (KAMERA_NT_MASK & 2);   // row stores
 
 // Device-memory accesses go through address-space-1 pointers: the row pointers come from the
 // job table, so the compiler cannot tell them from LDS and would otherwise emit FLAT
@@ -87,12 +89,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 // Streamed 16-byte row pieces: read once, written once.
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
   const KGLOBAL u32x4* q = gp(reinterpret_cast<const u32x4*>(p));
-  if constexpr (kNT) return __builtin_nontemporal_load(q);
+  if constexpr (kNTLoad) return __builtin_nontemporal_load(q);
   else return *q;
 }
 __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
   KGLOBAL u32x4* q = gp(reinterpret_cast<u32x4*>(p));
-  if constexpr (kNT) __builtin_nontemporal_store(v, q);
+  if constexpr (kNTStore) __builtin_nontemporal_store(v, q);
   else *q = v;
 }
 
