@@ -185,3 +185,35 @@ def expected_head(src: np.ndarray, *, rotate: bool, layout: int, delta: int, the
         return {"copy": True, "bits": src}
     z, S = segment(src, rotate=rotate, layout=layout, delta=delta, theta=theta, U=U, V=V)
     return {"copy": False, "z": z, "S": S}
+
+
+# ----------------------------------------------------------------------------------------
+# patch compile (technical summary §1: the deficit Delta = KV(B|A) - KV(B|empty), taken in
+# the target frame; §2: the patch is the top-m SVD factors of one conditioned pass)
+# ----------------------------------------------------------------------------------------
+
+def values(x: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of an f32 / f64 / bf16-bits array."""
+    z, _ = segment(np.ascontiguousarray(x).reshape(-1, x.shape[-1]), rotate=False)
+    return z.reshape(x.shape)
+
+
+def deficit(conditioned: np.ndarray, canonical: np.ndarray, *, rotate: bool, layout: int = HALF_SPLIT,
+            delta: int = 0, theta: float = 1e4) -> np.ndarray:
+    """Delta = KV(B|A) - R(delta) KV(B|empty) for one head (tokens x features), fp64."""
+    reloc, _ = segment(canonical, rotate=rotate, layout=layout, delta=delta, theta=theta)
+    return values(conditioned) - reloc
+
+
+def compile_patch(conditioned: np.ndarray, canonical: np.ndarray, *, m: int, rotate: bool,
+                  layout: int = HALF_SPLIT, delta: int = 0, theta: float = 1e4) -> dict:
+    """Top-m SVD factors of the deficit of one head (LAPACK through numpy).
+
+    Returns U (tokens x m) = left singular vectors times the singular values, V (features x m)
+    = right singular vectors, the product UV (= the best rank-m approximation of Delta,
+    Eckart-Young), all singular values `s`, and Delta itself."""
+    d = deficit(conditioned, canonical, rotate=rotate, layout=layout, delta=delta, theta=theta)
+    u, s, vt = np.linalg.svd(d, full_matrices=False)
+    U = u[:, :m] * s[:m]
+    V = vt[:m].T.copy()
+    return {"U": U, "V": V, "UV": U @ V.T, "s": s, "delta": d}

@@ -399,3 +399,53 @@ def test_slots_brute_force_and_bijection():
     assert np.array_equal(ident, np.arange(77, 87))
     with pytest.raises(ValueError):
         oracle.slots(table, ps, n_logical * ps - 3, 4)
+
+
+# ----------------------------------------------------------------------------------------
+# patch compile: deficit and top-m factors
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_deficit_is_conditioned_minus_relocated_canonical(layout):
+    """Delta of KV(B|A) = RoPE(k, j + delta) + E against KV(B|empty) = RoPE(k, j) is E
+    (RoPE from the transformers routines, E arbitrary)."""
+    rng = np.random.default_rng(20)
+    L, D, theta, delta = 24, 64, 1e4, 3000
+    raw = rng.standard_normal((L, 1, D))
+    j = np.arange(L)
+    E = rng.standard_normal((L, D)) * 0.1
+    canonical = LIB[layout](raw, j, theta)[:, 0]
+    conditioned = LIB[layout](raw, j + delta, theta)[:, 0] + E
+    d = oracle.deficit(conditioned, canonical, rotate=True, layout=layout, delta=delta, theta=theta)
+    np.testing.assert_allclose(d, E, rtol=0, atol=1e-11)
+    # unrotated channel: a plain difference
+    d2 = oracle.deficit(conditioned, canonical, rotate=False)
+    np.testing.assert_allclose(d2, conditioned - canonical, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_compile_recovers_exact_rank_m_deficit(m):
+    rng = np.random.default_rng(21 + m)
+    L, D = 40, 128
+    canonical = rng.standard_normal((L, D))
+    E = rng.standard_normal((L, m)) @ rng.standard_normal((m, D))
+    reloc, _ = oracle.segment(canonical, rotate=True, delta=-777, theta=1e6)
+    r = oracle.compile_patch(reloc + E, canonical, m=m, rotate=True, delta=-777, theta=1e6)
+    np.testing.assert_allclose(r["UV"], E, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(r["V"].T @ r["V"], np.eye(m), atol=1e-12)     # orthonormal V
+    np.testing.assert_allclose(r["U"], r["delta"] @ r["V"], atol=1e-10)       # U = Delta V
+
+
+def test_compile_is_the_best_rank_m_approximation():
+    """Eckart-Young: the residual's squared Frobenius norm is the sum of the discarded
+    squared singular values, and a random rank-m projection does worse."""
+    rng = np.random.default_rng(30)
+    L, D, m = 60, 64, 8
+    canonical = rng.standard_normal((L, D))
+    conditioned = rng.standard_normal((L, D))
+    r = oracle.compile_patch(conditioned, canonical, m=m, rotate=False)
+    resid = np.sum((r["delta"] - r["UV"]) ** 2)
+    assert abs(resid - np.sum(r["s"][m:] ** 2)) < 1e-9 * resid
+    q, _ = np.linalg.qr(rng.standard_normal((D, m)))
+    other = r["delta"] @ q @ q.T
+    assert np.sum((r["delta"] - other) ** 2) > resid
