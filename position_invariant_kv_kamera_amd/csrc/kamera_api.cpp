@@ -19,7 +19,8 @@
 using kamera::JobDesc;
 using kamera::LaunchParams;
 
-namespace {
+namespace kamera {
+namespace host {
 
 thread_local std::string g_last_error;
 
@@ -33,6 +34,9 @@ kamera_status fail(kamera_status st, const char* fmt, ...) {
   return st;
 }
 
+void clear_error() { g_last_error.clear(); }
+const char* last_error() { return g_last_error.c_str(); }
+
 constexpr size_t kHeaderBytes = 256;
 constexpr int64_t kTargetBlocks = 70000;   // grid size the tiles-per-wave choice aims under
 
@@ -40,23 +44,11 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Geometry of one channel: heads and features per head.
-struct Channel {
-  int32_t heads;
-  int32_t width;
-  bool rotate;
-};
-
 Channel channel_of(const kamera_model& m, int c) {
   if (m.family == KAMERA_FAMILY_MLA)
     return c == KAMERA_CH_ROT ? Channel{1, m.rope_dim, true} : Channel{1, m.head_dim, false};
   return Channel{m.n_kv_heads, m.head_dim, c == KAMERA_CH_ROT};
 }
-
-// Byte range [lo, hi) touched by a (layer, token, row) view.
-struct Range {
-  uintptr_t lo, hi;
-};
 
 Range view_range(const void* p, int64_t ls, int64_t n_layers, int64_t ts, int64_t n_tokens,
                  int64_t row_elems, int64_t esize) {
@@ -283,6 +275,13 @@ int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
   return v && *v ? std::atoi(v) : dflt;
 }
+
+}  // namespace host
+}  // namespace kamera
+
+using namespace kamera::host;
+
+namespace {
 
 // ---------------------------------------------------------------------------------------
 // packing
