@@ -10,7 +10,7 @@
  *     positions 0..n_tokens-1, so one shift delta moves every token of the chunk.
  *   - R(delta) is the exact RoPE phase shift of the keys to the new position (same section:
  *     relocation is an algebraic rotation, not a forward pass). Values are not rotated.
- *   - U_m V_m^T is the rank-m conditioning patch (same section, "Rank-m Conditioning Patch"),
+ *   - U_m V_m^T is the rank-m conditioning patch (same section, its rank-m patch subsection),
  *     added after the rotation, in the target frame, to both channels.
  *   - GQA and MHA rotate the whole key; MLA rotates only the 64-dim k_rope and reuses c_KV
  *     unchanged (same section, "Unified Architecture Support"; the Irminsul abstract on the
@@ -191,6 +191,67 @@ size_t kamera_patch_bytes(const kamera_model* model, int32_t n_tokens, int32_t m
 
 /* Bytes of one chunk's canonical KV (both channels, all layers); 0 on invalid input. */
 size_t kamera_kv_bytes(const kamera_model* model, int32_t n_tokens);
+
+/* ---- Patch compile ------------------------------------------------------------------------
+ * The technical summary (§2) forms each chunk's patch once, from one conditioned pass over
+ * [A, B]: the deficit Delta = KV(B|A) - R(delta) KV(B|empty) (the deficit of §1, taken in the
+ * frame of the conditioned pass) is reduced to its top-m factors by SVD. kamera_patch_compile
+ * takes KV(B|A) as given (the forward pass that produces it is outside this library) and writes
+ * per layer and head
+ *     V (width x m): an orthonormal basis of Delta's top-m right singular subspace,
+ *     U (n_tokens x m) = Delta V,
+ * so that U V^T is the best rank-m approximation of Delta (Eckart-Young) once the subspace
+ * iteration has converged. Factors are written in the model's element type and can be passed
+ * to kamera_reuse_batch as they are. Method on the device: G = Delta^T Delta (fp32 MFMA), block
+ * power iteration on G from a fixed start with CholeskyQR2 re-orthonormalisation (n_iter
+ * rounds), then U = Delta V. Singular values are not returned; U carries them. */
+
+/* Where kamera_patch_compile writes one channel's factors (device memory, model element type):
+ *     U(l, h, t, r) at U + l*u_layer_stride + h*u_head_stride + t*m + r
+ *     V(l, h, f, r) at V + l*v_layer_stride + h*v_head_stride + f*m + r */
+typedef struct kamera_factors_out {
+  void* U;
+  int64_t u_layer_stride;
+  int64_t u_head_stride;
+  void* V;
+  int64_t v_layer_stride;
+  int64_t v_head_stride;
+} kamera_factors_out;
+
+/* One chunk to compile: its canonical KV(B|empty), its conditioned KV(B|A) (same layout rules
+ * as kamera_src), the shift delta between the two (position of the chunk in the conditioned
+ * pass minus its canonical position), the rank m (both channels) and the output factors.
+ * Supported: rotated channel width a multiple of 32 up to 128; unrotated width that, or a
+ * multiple of 128 up to 512; m in [1, 64], m <= width, and m <= 32 for widths above 128. Input
+ * rows must start on 16-byte boundaries (pointer and strides), else KAMERA_ERR_UNSUPPORTED.
+ * A chunk with n_tokens == 0 is skipped and its outputs are not written. Where Delta offers
+ * fewer than m independent directions (Delta = 0, n_tokens < m), the surplus columns of V are
+ * zero or directions on which Delta vanishes to rounding, and U's columns there are ~0. */
+typedef struct kamera_compile_chunk {
+  int32_t n_tokens;
+  int32_t m;
+  int64_t delta;
+  kamera_src canonical[2];
+  kamera_src conditioned[2];
+  kamera_factors_out out[2];
+} kamera_compile_chunk;
+
+#define KAMERA_COMPILE_MAX_RANK 64
+
+/* Bytes of workspace kamera_patch_compile needs for these chunks (fp32 Gram matrices and bases
+ * of every layer and head, plus the job table); depends only on the model and each chunk's
+ * n_tokens and m (pointers are not read). 0 if the arguments are invalid. */
+size_t kamera_compile_workspace_bytes(const kamera_model* model,
+                                      const kamera_compile_chunk* chunks, int32_t n_chunks);
+
+/* Compile the patches of `chunks` (see above) on `stream`. n_iter: rounds of subspace
+ * iteration, 1..100 (8 is plenty when the deficit's spectrum drops by 10x after rank m).
+ * The extent of every U and V must be disjoint from every other output's and from every input's
+ * extent (KAMERA_ERR_OVERLAP). Results are deterministic and do not depend on which other
+ * chunks share the call. Same validation, stream and error conventions as the compute calls. */
+kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compile_chunk* chunks,
+                                   int32_t n_chunks, int32_t n_iter, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 const char* kamera_status_string(kamera_status status);
 const char* kamera_last_error(void); /* per-thread; "" if none */

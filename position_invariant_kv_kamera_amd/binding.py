@@ -60,6 +60,20 @@ class KameraChunk(ctypes.Structure):
                 ("src", KameraSrc * 2), ("patch", KameraPatchRef * 2)]
 
 
+class KameraFactorsOut(ctypes.Structure):
+    _fields_ = [("U", c_vp), ("u_layer_stride", c_i64), ("u_head_stride", c_i64),
+                ("V", c_vp), ("v_layer_stride", c_i64), ("v_head_stride", c_i64)]
+
+
+class KameraCompileChunk(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i32), ("m", c_i32), ("delta", c_i64),
+                ("canonical", KameraSrc * 2), ("conditioned", KameraSrc * 2),
+                ("out", KameraFactorsOut * 2)]
+
+
+COMPILE_MAX_RANK = 64
+
+
 _lib = None
 
 
@@ -93,6 +107,13 @@ def load_library() -> ctypes.CDLL:
     lib.kamera_last_error.restype = ctypes.c_char_p
     lib.kamera_version.argtypes = []
     lib.kamera_version.restype = c_i32
+    lib.kamera_compile_workspace_bytes.argtypes = [ctypes.POINTER(KameraModel),
+                                                   ctypes.POINTER(KameraCompileChunk), c_i32]
+    lib.kamera_compile_workspace_bytes.restype = c_size
+    lib.kamera_patch_compile.argtypes = [ctypes.POINTER(KameraModel),
+                                         ctypes.POINTER(KameraCompileChunk), c_i32, c_i32, c_vp,
+                                         c_size, c_vp]
+    lib.kamera_patch_compile.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -164,6 +185,17 @@ def kamera_version() -> int:
     return int(load_library().kamera_version())
 
 
+def kamera_compile_workspace_bytes(model, chunks, n_chunks) -> int:
+    return int(load_library().kamera_compile_workspace_bytes(
+        ctypes.byref(model) if model is not None else None, chunks, int(n_chunks)))
+
+
+def kamera_patch_compile(model, chunks, n_chunks, n_iter, workspace, workspace_bytes, stream):
+    return int(load_library().kamera_patch_compile(
+        ctypes.byref(model) if model is not None else None, chunks, int(n_chunks), int(n_iter),
+        workspace, int(workspace_bytes), stream))
+
+
 # ---- marshalling of torch tensors (workloads.Batch) into descriptors --------------------
 
 def model_of(plan) -> KameraModel:
@@ -209,11 +241,12 @@ def chunks_of(batch, m_override: int | None = None):
 
 
 class Workspace:
-    """Device workspace for up to `n_chunks` chunks (torch uint8 tensor, 256-byte aligned)."""
+    """Device workspace for up to `n_chunks` chunks (torch uint8 tensor, 256-byte aligned), or
+    of `nbytes` bytes when given."""
 
-    def __init__(self, n_chunks: int, device="cuda"):
+    def __init__(self, n_chunks: int = 0, device="cuda", *, nbytes: int | None = None):
         import torch
-        self.nbytes = kamera_workspace_bytes(n_chunks)
+        self.nbytes = kamera_workspace_bytes(n_chunks) if nbytes is None else int(nbytes)
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
         base = self._buf.data_ptr()
         self.ptr = (base + 255) // 256 * 256
@@ -239,4 +272,44 @@ def run_batch(op: str, batch, workspace: Workspace | None = None, stream=None, *
     s = current_stream_ptr() if stream is None else stream
     fn = {"reuse": kamera_reuse_batch, "relocate": kamera_relocate, "patch": kamera_patch}[op]
     check(fn(model, cache, chunks, batch.plan.n_chunks, ws.ptr, ws.nbytes, s))
+    return ws
+
+
+# ---- patch compile ------------------------------------------------------------------------
+
+class CompileItem:
+    """Tensors of one chunk to compile. Per channel c: canonical[c] and conditioned[c] are
+    [layers, tokens, heads*width] views (unit inner stride); U[c] is [layers, heads, tokens, m]
+    and V[c] [layers, heads, width, m], written by the call."""
+
+    def __init__(self, n_tokens, m, delta, canonical, conditioned, U, V):
+        self.n_tokens, self.m, self.delta = int(n_tokens), int(m), int(delta)
+        self.canonical, self.conditioned, self.U, self.V = canonical, conditioned, U, V
+
+
+def compile_chunks_of(items):
+    arr = (KameraCompileChunk * max(1, len(items)))()
+    for i, it in enumerate(items):
+        k = arr[i]
+        k.n_tokens, k.m, k.delta = it.n_tokens, it.m, it.delta
+        for ch in range(2):
+            a, b = it.canonical[ch], it.conditioned[ch]
+            k.canonical[ch] = KameraSrc(a.data_ptr(), a.stride(0), a.stride(1))
+            k.conditioned[ch] = KameraSrc(b.data_ptr(), b.stride(0), b.stride(1))
+            U, V = it.U[ch], it.V[ch]
+            k.out[ch] = KameraFactorsOut(U.data_ptr(), U.stride(0), U.stride(1), V.data_ptr(),
+                                         V.stride(0), V.stride(1))
+    return arr
+
+
+def run_compile(model: KameraModel, items, *, n_iter: int = 8, workspace: Workspace | None = None,
+                stream=None) -> Workspace:
+    """kamera_patch_compile over `items` (asynchronous on the stream); returns the workspace."""
+    chunks = compile_chunks_of(items)
+    need = kamera_compile_workspace_bytes(model, chunks, len(items))
+    if need == 0:
+        raise KameraError(KAMERA_ERR_INVALID_ARGUMENT, kamera_last_error())
+    ws = workspace if workspace is not None and workspace.nbytes >= need else Workspace(nbytes=need)
+    s = current_stream_ptr() if stream is None else stream
+    check(kamera_patch_compile(model, chunks, len(items), n_iter, ws.ptr, ws.nbytes, s))
     return ws

@@ -1,0 +1,877 @@
+// kamera_compile.hip — the patch compile of the Kamera reuse operator on gfx950 (CDNA4).
+//
+// Per chunk, channel, layer and head the deficit is
+//     Delta = KV(B|A) - R(delta) KV(B|empty)                      (n_tokens x width)
+// (Kamera technical summary: §1 names the deficit a chunk's context leaves in its KV; §2
+// Methodology forms the patch once from one conditioned pass over [A, B] and keeps its top-m
+// SVD factors). The library takes KV(B|A) and KV(B|empty) and returns
+//     V (width x m)     an orthonormal basis of Delta's dominant right singular subspace,
+//     U (n_tokens x m)  = Delta V,
+// so that U V^T is the rank-m truncation of Delta once the subspace has converged.
+//
+// Kernels (one launch per class of tile / LDS size present in the batch):
+//   gram      partial Gram tiles Delta_s^T Delta_s over token splits s with fp32 MFMA
+//             16x16x4; one tile pair (bi <= bj) of G per block; Delta is formed on the fly
+//             (canonical rows rotated in fp32 with cos/sin from fp64, as the reuse kernels do);
+//   subspace  one block per head: sums the partials into G, then block power iteration
+//             X <- orth(G X) from a fixed +-1 start. orth() is a Cholesky QR: S = Y^T Y, its
+//             Cholesky factor L and L^-1 in fp64, X = Y L^-T accumulated in fp64. Columns that
+//             collapse (Y rank deficient) are re-seeded between rounds and zero after the last;
+//             a final orth() of X alone restores orthonormality to fp32 rounding;
+//   project   U = Delta X with the fp32 X kept in the workspace (a second pass over the inputs).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "kamera_internal.h"
+
+using namespace kamera::host;
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kStepTokens = 32;      // tokens of Delta staged in LDS per step
+constexpr int kProjTokens = 128;     // tokens per projection block
+constexpr int kMinSplitTokens = 256; // Gram split never shorter than this (except the tail)
+constexpr int kGramBlocksPerJob = 1024;
+constexpr double kDeadTol = 1e-12;   // pivot^2 / column norm^2 below this: column collapsed
+
+// One chunk, one channel, all layers and heads (a "unit" is one layer and head).
+struct alignas(16) CJob {
+  const void* canon;
+  const void* cond;
+  void* U;
+  void* V;
+  int64_t canon_ls, canon_ts, cond_ls, cond_ts;
+  int64_t u_ls, u_hs, v_ls, v_hs;
+  int64_t delta;
+  int64_t gpart;   // float offset of the partial Gram tiles [unit][pair][split][te][te]
+  int64_t gfull;   // float offset of the assembled G [unit][width][width], or -1 (partial is G)
+  int64_t xbase;   // float offset of the fp32 bases [unit][width][mp]
+  int32_t n_tokens, m, mp, width, heads, rotate, te, nb, n_pairs, splits, split_tokens, n_units;
+};
+
+struct CParams {
+  const CJob* jobs;
+  const int32_t* starts;   // first block of each entry, ascending
+  const int32_t* job_of;   // job index of each entry
+  float* ws;               // float view of the workspace's data region
+  double theta;
+  int32_t n_entries;
+  int32_t layout;
+  int32_t n_iter;
+  int32_t pad0;
+};
+
+// ---------------------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int find_entry(const CParams& P, int b) {
+  int lo = 0, hi = P.n_entries - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.starts[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// cos/sin(delta * theta^(-2i/rot_dim)) per pair: angle and reduction in fp64, one rounding.
+__device__ void fill_phases(float2* cs, int64_t delta, double theta, int rot_dim) {
+  for (int i = threadIdx.x; i < rot_dim / 2; i += kThreads) {
+    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    double s, c;
+    sincos((double)delta * inv, &s, &c);
+    cs[i] = make_float2((float)c, (float)s);
+  }
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(w[k] << 16);
+    o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, (__bf16)v);   // RNE
+}
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+
+// Rows [tok0, tok0 + kStepTokens) of Delta, columns [col0, col0 + ncols), into dst (fp32, row
+// stride ds); rows at or past tok_end are zero. A rotated head is always staged whole
+// (col0 = 0, ncols = width) so that both members of every pair are at hand.
+template <typename T>
+__device__ void stage_delta(const CJob& J, int layout, const float2* cs, int layer, int head,
+                            int tok0, int tok_end, int col0, int ncols, float* dst, int ds) {
+  const int W = J.width;
+  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + (int64_t)head * W;
+  const T* cond = static_cast<const T*>(J.cond) + layer * J.cond_ls + (int64_t)head * W;
+  if (J.rotate) {
+    const int gpr = W / 16;   // groups of 8 pairs per row
+    for (int g = threadIdx.x; g < kStepTokens * gpr; g += kThreads) {
+      const int r = g / gpr, q = g - r * gpr;
+      const int tok = tok0 + r;
+      float* d = dst + r * ds;
+      const int fa = layout == KAMERA_ROPE_HALF_SPLIT ? 8 * q : 16 * q;
+      const int fb = layout == KAMERA_ROPE_HALF_SPLIT ? W / 2 + 8 * q : 16 * q + 8;
+      if (tok >= tok_end) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[fa + k] = d[fb + k] = 0.f;
+        continue;
+      }
+      float xa[8], xb[8], ca[8], cb[8];
+      load8(canon + tok * J.canon_ts + fa, xa);
+      load8(canon + tok * J.canon_ts + fb, xb);
+      load8(cond + tok * J.cond_ts + fa, ca);
+      load8(cond + tok * J.cond_ts + fb, cb);
+      if (layout == KAMERA_ROPE_HALF_SPLIT) {
+        // pair 8q+k = (feature fa+k, feature fb+k)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float c = cs[8 * q + k].x, s = cs[8 * q + k].y;
+          const float x = xa[k], y = xb[k];
+          d[fa + k] = ca[k] - (x * c - y * s);
+          d[fb + k] = cb[k] - (y * c + x * s);
+        }
+      } else {
+        // pairs 8q..8q+3 are adjacent features in piece a, 8q+4..8q+7 in piece b
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float c = cs[8 * q + k].x, s = cs[8 * q + k].y;
+          const float x = xa[2 * k], y = xa[2 * k + 1];
+          d[fa + 2 * k] = ca[2 * k] - (x * c - y * s);
+          d[fa + 2 * k + 1] = ca[2 * k + 1] - (y * c + x * s);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float c = cs[8 * q + 4 + k].x, s = cs[8 * q + 4 + k].y;
+          const float x = xb[2 * k], y = xb[2 * k + 1];
+          d[fb + 2 * k] = cb[2 * k] - (x * c - y * s);
+          d[fb + 2 * k + 1] = cb[2 * k + 1] - (y * c + x * s);
+        }
+      }
+    }
+  } else {
+    const int gpr = ncols / 8;
+    for (int g = threadIdx.x; g < kStepTokens * gpr; g += kThreads) {
+      const int r = g / gpr, q = g - r * gpr;
+      const int tok = tok0 + r;
+      float* d = dst + r * ds + 8 * q;
+      if (tok >= tok_end) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = 0.f;
+        continue;
+      }
+      float x[8], c[8];
+      load8(canon + tok * J.canon_ts + col0 + 8 * q, x);
+      load8(cond + tok * J.cond_ts + col0 + 8 * q, c);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) d[k] = c[k] - x[k];
+    }
+  }
+}
+
+// Tile pair index -> (bi, bj), bi <= bj, row-major over the upper triangle of nb x nb tiles.
+__device__ __forceinline__ void pair_tiles(int pair, int nb, int* bi, int* bj) {
+  int p = pair;
+  for (int r = 0; r < nb; ++r) {
+    const int len = nb - r;
+    if (p < len) {
+      *bi = r;
+      *bj = r + p;
+      return;
+    }
+    p -= len;
+  }
+  *bi = *bj = 0;
+}
+
+// ---------------------------------------------------------------------------------------
+// gram: partial G tiles. Tile edge TE = 32*NB; four waves own the 2x2 quadrants of the tile,
+// each NB x NB MFMA blocks of 16x16. MFMA 16x16x4 fp32 operands: lane l gives A[l%16][l/16]
+// (feature i, token k) and B[l/16][l%16] (token k, feature j); it receives C rows
+// 4(l/16)..4(l/16)+3 of column l%16.
+// ---------------------------------------------------------------------------------------
+
+template <typename T, int NB>
+__global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
+  constexpr int TE = 32 * NB;
+  constexpr int DS = TE + 16;   // row stride: the four token rows of an operand fall in
+                                // different LDS banks
+  __shared__ float di[kStepTokens * DS];
+  __shared__ float dj[kStepTokens * DS];
+  __shared__ float2 cs[64];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  int local = blockIdx.x - P.starts[e];
+  const int split = local % J.splits;
+  local /= J.splits;
+  const int pair = local % J.n_pairs;
+  const int unit = local / J.n_pairs;
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  int bi, bj;
+  pair_tiles(pair, J.nb, &bi, &bj);
+  if (J.rotate) fill_phases(cs, J.delta, P.theta, J.width);
+
+  const int t_lo = split * J.split_tokens;
+  const int t_hi = min(J.n_tokens, t_lo + J.split_tokens);
+  const float* A = di;
+  const float* B = bi == bj ? di : dj;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = (wave >> 1) * (TE / 2), c0 = (wave & 1) * (TE / 2);
+
+  f32x4 acc[NB][NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+    __syncthreads();
+    stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
+    if (bi != bj) stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
+    __syncthreads();
+#pragma unroll 2
+    for (int kk = 0; kk < kStepTokens / 4; ++kk) {
+      const int row = (kk * 4 + (lane >> 4)) * DS + (lane & 15);
+      float a[NB], b[NB];
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        a[x] = A[row + r0 + 16 * x];
+        b[x] = B[row + c0 + 16 * x];
+      }
+#pragma unroll
+      for (int x = 0; x < NB; ++x)
+#pragma unroll
+        for (int y = 0; y < NB; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
+  }
+
+  float* out = P.ws + J.gpart +
+               ((int64_t)(unit * J.n_pairs + pair) * J.splits + split) * (TE * TE);
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[(r0 + 16 * x + 4 * (lane >> 4) + i) * TE + c0 + 16 * y + (lane & 15)] = acc[x][y][i];
+}
+
+// ---------------------------------------------------------------------------------------
+// subspace: one block per unit. DMAX >= width, MMAX >= mp (a multiple of 16).
+// LDS: xs [width][mp] fp32 (row-major), ys [mp][width+1] fp32 (column-major, padded),
+//      ss [m][m] fp64 (S, then L in its lower triangle), li [mp][mp] fp64 (L^-1).
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float seed_value(int i, int j, int round) {
+  uint32_t h = (uint32_t)i * 0x9E3779B1u ^ ((uint32_t)j + 0x7F4A7C15u) * 0x85EBCA77u ^
+               (uint32_t)round * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  h *= 0x297A2D39u;
+  h ^= h >> 15;
+  return (h & 1u) ? 1.f : -1.f;
+}
+
+// X = orth(Y): Cholesky QR with S, L and L^-1 in fp64. Dead (collapsed) columns become a fresh
+// +-1 vector when `reseed_round` >= 0, zero otherwise.
+__device__ void orth(const float* ys, float* xs, double* ss, double* li, int* dead, int D, int m,
+                     int mp, int reseed_round) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int YS = D + 1;
+  // S = Y^T Y (lower triangle, mirrored); fp32 products are exact in fp64
+  const int npair = m * (m + 1) / 2;
+  for (int q = tid; q < npair; q += kThreads) {
+    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
+    while (a * (a + 1) / 2 > q) --a;
+    while ((a + 1) * (a + 2) / 2 <= q) ++a;
+    const int b = q - a * (a + 1) / 2;
+    const float* ya = ys + a * YS;
+    const float* yb = ys + b * YS;
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) acc += (double)ya[i] * (double)yb[i];
+    ss[a * m + b] = acc;
+    ss[b * m + a] = acc;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int i = lane;
+    // right-looking Cholesky of S (lower triangle), lane i owns row i
+    double diag_i = i < m ? ss[i * m + i] : 0.0;
+    for (int k = 0; k < m; ++k) {
+      wave_lds_sync();
+      const double d = ss[k * m + k];
+      const double d0 = __shfl(diag_i, k, 64);
+      const bool dk = d <= kDeadTol * d0;
+      const double lkk = dk ? 0.0 : sqrt(d);
+      const double inv = dk ? 0.0 : 1.0 / lkk;
+      double lik = 0.0;
+      if (i > k && i < m) {
+        lik = ss[i * m + k] * inv;
+        ss[i * m + k] = lik;
+      }
+      if (i == k) {
+        ss[k * m + k] = lkk;
+        dead[k] = dk ? 1 : 0;
+      }
+      wave_lds_sync();
+      if (i > k && i < m && !dk)
+        for (int j = k + 1; j <= i; ++j) ss[i * m + j] -= lik * ss[j * m + k];
+    }
+    wave_lds_sync();
+    // li = L^-1, lane j fills column j; rows >= m and the strict upper triangle are zero
+    if (i < mp) {
+      const int j = i;
+      for (int r = 0; r < mp; ++r) li[r * mp + j] = 0.0;
+      if (j < m) {
+        const double ljj = ss[j * m + j];
+        li[j * mp + j] = ljj > 0.0 ? 1.0 / ljj : 0.0;
+        for (int r = j + 1; r < m; ++r) {
+          const double lrr = ss[r * m + r];
+          if (!(lrr > 0.0)) continue;   // dead row stays zero
+          double acc = 0.0;
+          for (int a = j; a < r; ++a) acc += ss[r * m + a] * li[a * mp + j];
+          li[r * mp + j] = -acc / lrr;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // X = Y L^-T: x[i][j] = sum_{a <= j} y[i][a] * li[j][a], accumulated in fp64
+  const int groups = (m + 15) / 16;
+  for (int u = tid; u < D * groups; u += kThreads) {
+    const int i = u % D, jg = u / D;
+    double acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.0;
+    const int a_end = min(m, 16 * jg + 16);
+    for (int a = 0; a < a_end; ++a) {
+      const double y = (double)ys[a * YS + i];
+      const double* lr = li + (16 * jg) * mp + a;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] += y * lr[c * mp];
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int j = 16 * jg + c;
+      if (j < m) {
+        float v = (float)acc[c];
+        if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
+        xs[i * mp + j] = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <typename T, int DMAX, int MMAX>
+__global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
+  __shared__ __align__(16) float xs[DMAX * MMAX];
+  __shared__ float ys[MMAX * (DMAX + 1)];
+  __shared__ double ss[MMAX * MMAX];
+  __shared__ double li[MMAX * MMAX];
+  __shared__ int dead[MMAX];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int unit = blockIdx.x - P.starts[e];
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
+
+  // G: the single partial, or the sum of the partial tiles assembled in the workspace
+  const float* G;
+  if (J.gfull < 0) {
+    G = P.ws + J.gpart + (int64_t)unit * D * D;
+  } else {
+    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
+    const int te = J.te, te2 = te * te;
+    for (int pair = 0; pair < J.n_pairs; ++pair) {
+      int bi, bj;
+      pair_tiles(pair, J.nb, &bi, &bj);
+      const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
+      for (int idx = tid; idx < te2; idx += kThreads) {
+        float v = 0.f;
+        for (int s = 0; s < J.splits; ++s) v += part[(int64_t)s * te2 + idx];
+        const int ii = idx / te, jj = idx - ii * te;
+        gf[(bi * te + ii) * D + bj * te + jj] = v;
+        if (bi != bj) gf[(bj * te + jj) * D + bi * te + ii] = v;
+      }
+    }
+    __syncthreads();
+    G = gf;
+  }
+
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int i = idx / mp, j = idx - i * mp;
+    xs[idx] = j < m ? seed_value(i, j, 0) : 0.f;
+  }
+  __syncthreads();
+
+  const int YS = D + 1;
+  const int groups = mp / 16;
+  for (int round = 0; round < P.n_iter; ++round) {
+    // Y = G X (G symmetric: column i read as row i, coalesced)
+    for (int u = tid; u < D * groups; u += kThreads) {
+      const int i = u % D, cg = u / D;
+      float acc[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+      for (int k = 0; k < D; ++k) {
+        const float g = G[(int64_t)k * D + i];
+        const float4* xr = reinterpret_cast<const float4*>(xs + k * mp + 16 * cg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 x = xr[q];
+          acc[4 * q] += g * x.x;
+          acc[4 * q + 1] += g * x.y;
+          acc[4 * q + 2] += g * x.z;
+          acc[4 * q + 3] += g * x.w;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) ys[(16 * cg + c) * YS + i] = acc[c];
+    }
+    __syncthreads();
+    orth(ys, xs, ss, li, dead, D, m, mp, round);
+  }
+  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
+  for (int idx = tid; idx < D * m; idx += kThreads) {
+    const int i = idx / m, j = idx - i * m;
+    ys[j * YS + i] = xs[i * mp + j];
+  }
+  __syncthreads();
+  orth(ys, xs, ss, li, dead, D, m, mp, -1);
+
+  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
+  float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int i = idx / mp, j = idx - i * mp;
+    const float v = xs[idx];
+    xg[idx] = v;
+    if (j < m) store_elem(V + i * m + j, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// project: U = Delta X for kProjTokens tokens of one unit per block.
+// ---------------------------------------------------------------------------------------
+
+template <typename T, int DMAX, int MPMAX>
+__global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
+  __shared__ __align__(16) float vs[DMAX * MPMAX];
+  __shared__ float dl[kStepTokens * (DMAX + 16)];
+  __shared__ float2 cs[64];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int local = blockIdx.x - P.starts[e];
+  const int tblocks = (J.n_tokens + kProjTokens - 1) / kProjTokens;
+  const int unit = local / tblocks, tb = local - unit * tblocks;
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
+  const int DSt = D + 16;
+  if (J.rotate) fill_phases(cs, J.delta, P.theta, D);
+  const float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
+  for (int idx = tid; idx < D * mp; idx += kThreads) vs[idx] = xg[idx];
+
+  T* U = static_cast<T*>(J.U) + layer * J.u_ls + head * J.u_hs;
+  const int t_lo = tb * kProjTokens, t_hi = min(J.n_tokens, t_lo + kProjTokens);
+  const int rgroups = mp / 4;
+  for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+    __syncthreads();
+    stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, 0, D, dl, DSt);
+    __syncthreads();
+    for (int u = tid; u < kStepTokens * rgroups; u += kThreads) {
+      const int r = u / rgroups, rg = u - r * rgroups;
+      const int tok = tok0 + r;
+      if (tok >= t_hi || 4 * rg >= m) continue;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      const float* drow = dl + r * DSt;
+      for (int f = 0; f < D; ++f) {
+        const float d = drow[f];
+        const float4 v = *reinterpret_cast<const float4*>(vs + f * mp + 4 * rg);
+        a0 += d * v.x;
+        a1 += d * v.y;
+        a2 += d * v.z;
+        a3 += d * v.w;
+      }
+      T* ur = U + (int64_t)tok * m + 4 * rg;
+      const float a[4] = {a0, a1, a2, a3};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (4 * rg + c < m) store_elem(ur + c, a[c]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// host: validation, plan, launches
+// ---------------------------------------------------------------------------------------
+
+enum Kind { kGram = 0, kSubspace = 1, kProject = 2 };
+
+struct Launch {
+  int kind;
+  int cls;                          // gram: NB; subspace: 0..4; project: 0..1
+  std::vector<int32_t> starts, job_of;
+  int64_t blocks = 0;
+  size_t off = 0;                   // byte offset of starts (job_of follows)
+};
+
+struct CPlan {
+  std::vector<CJob> jobs;
+  std::vector<Launch> launches;
+  size_t table_bytes = 0;
+  size_t data_off = 0;
+  size_t total_bytes = 0;
+};
+
+// subspace LDS classes: (DMAX, MMAX)
+constexpr int kSubD[5] = {128, 128, 128, 512, 512};
+constexpr int kSubM[5] = {16, 32, 64, 16, 32};
+
+int subspace_class(int D, int mp) {
+  for (int c = 0; c < 5; ++c)
+    if (D <= kSubD[c] && mp <= kSubM[c]) return c;
+  return -1;
+}
+
+bool width_supported(const Channel& g) {
+  if (g.width % 32) return false;
+  if (g.rotate) return g.width <= 128;
+  return g.width <= 128 || (g.width % 128 == 0 && g.width <= 512);
+}
+
+// Views whose elements are base + a*sa + b*sb + [0, size) for a < na, b < nb must not
+// overlap themselves (they are written).
+bool strided_disjoint(int64_t sa, int64_t na, int64_t sb, int64_t nb, int64_t size) {
+  if (na <= 1) { sa = 0; na = 1; }
+  if (nb <= 1) { sb = 0; nb = 1; }
+  if (na > 1 && nb > 1 && sa > sb) { std::swap(sa, sb); std::swap(na, nb); }
+  if (na > 1 && sa < size) return false;
+  if (nb > 1) {
+    const int64_t inner = na > 1 ? (na - 1) * sa + size : size;
+    if (sb < inner) return false;
+  }
+  return true;
+}
+
+kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* chunks,
+                           int32_t n_chunks, CPlan* plan) {
+  if (n_chunks < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 0");
+  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
+  const int64_t es = M.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  int64_t floats = 0;
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_compile_chunk& k = chunks[i];
+    if (k.n_tokens < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: n_tokens < 0", i);
+    if (k.n_tokens == 0) continue;
+    if (k.m < 1) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: m must be >= 1", i);
+    if (k.m > KAMERA_COMPILE_MAX_RANK)
+      return fail(KAMERA_ERR_UNSUPPORTED, "chunk %d: m = %d exceeds %d", i, k.m,
+                  KAMERA_COMPILE_MAX_RANK);
+    if (k.delta >= (int64_t(1) << 31) || k.delta <= -(int64_t(1) << 31))
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
+    for (int ch = 0; ch < 2; ++ch) {
+      const Channel g = channel_of(M, ch);
+      if (!width_supported(g))
+        return fail(KAMERA_ERR_UNSUPPORTED,
+                    "chunk %d channel %d: width %d not supported by the compile (rotated: a "
+                    "multiple of 32 up to 128; unrotated: that or a multiple of 128 up to 512)",
+                    i, ch, g.width);
+      if (k.m > g.width)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: m = %d exceeds width %d",
+                    i, ch, k.m, g.width);
+      if (g.width > 128 && k.m > 32)
+        return fail(KAMERA_ERR_UNSUPPORTED,
+                    "chunk %d channel %d: m = %d above 32 needs width <= 128", i, ch, k.m);
+      CJob J{};
+      J.canon = k.canonical[ch].ptr;
+      J.cond = k.conditioned[ch].ptr;
+      J.U = k.out[ch].U;
+      J.V = k.out[ch].V;
+      J.canon_ls = k.canonical[ch].layer_stride;
+      J.canon_ts = k.canonical[ch].token_stride;
+      J.cond_ls = k.conditioned[ch].layer_stride;
+      J.cond_ts = k.conditioned[ch].token_stride;
+      J.u_ls = k.out[ch].u_layer_stride;
+      J.u_hs = k.out[ch].u_head_stride;
+      J.v_ls = k.out[ch].v_layer_stride;
+      J.v_hs = k.out[ch].v_head_stride;
+      J.delta = k.delta;
+      J.n_tokens = k.n_tokens;
+      J.m = k.m;
+      J.mp = (k.m + 15) / 16 * 16;
+      J.width = g.width;
+      J.heads = g.heads;
+      J.rotate = g.rotate ? 1 : 0;
+      J.te = std::min(g.width, 128);
+      J.nb = g.width / J.te;
+      J.n_pairs = J.nb * (J.nb + 1) / 2;
+      J.n_units = M.n_layers * g.heads;
+      // token splits depend on this job alone, so a chunk compiles to the same bits in any batch
+      const int64_t tiles = (int64_t)J.n_units * J.n_pairs;
+      int splits = (int)std::max<int64_t>(1, (kGramBlocksPerJob + tiles - 1) / tiles);
+      splits = std::min(splits, std::max(1, (k.n_tokens + kMinSplitTokens - 1) / kMinSplitTokens));
+      int st = (k.n_tokens + splits - 1) / splits;
+      st = (st + kStepTokens - 1) / kStepTokens * kStepTokens;
+      J.split_tokens = st;
+      J.splits = (k.n_tokens + st - 1) / st;
+      const int64_t te2 = (int64_t)J.te * J.te;
+      J.gpart = floats;
+      floats += (int64_t)J.n_units * J.n_pairs * J.splits * te2;
+      if (J.n_pairs > 1 || J.splits > 1) {
+        J.gfull = floats;
+        floats += (int64_t)J.n_units * J.width * J.width;
+      } else {
+        J.gfull = -1;
+      }
+      J.xbase = floats;
+      floats += (int64_t)J.n_units * J.width * J.mp;
+      floats = (floats + 63) / 64 * 64;
+      plan->jobs.push_back(J);
+    }
+  }
+  (void)es;
+  // launches: one per kernel class present
+  auto add = [&](int kind, int cls, int job, int64_t blocks) -> bool {
+    Launch* L = nullptr;
+    for (auto& l : plan->launches)
+      if (l.kind == kind && l.cls == cls) L = &l;
+    if (!L) {
+      plan->launches.push_back(Launch{});
+      L = &plan->launches.back();
+      L->kind = kind;
+      L->cls = cls;
+    }
+    if (L->blocks + blocks > INT32_MAX) return false;
+    L->starts.push_back((int32_t)L->blocks);
+    L->job_of.push_back(job);
+    L->blocks += blocks;
+    return true;
+  };
+  for (size_t j = 0; j < plan->jobs.size(); ++j) {
+    const CJob& J = plan->jobs[j];
+    const int tblocks = (J.n_tokens + kProjTokens - 1) / kProjTokens;
+    bool ok = add(kGram, J.te / 32, (int)j, (int64_t)J.n_units * J.n_pairs * J.splits) &&
+              add(kSubspace, subspace_class(J.width, J.mp), (int)j, J.n_units) &&
+              add(kProject, J.width <= 128 ? 0 : 1, (int)j, (int64_t)J.n_units * tblocks);
+    if (!ok) return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
+  }
+  size_t off = round_up(plan->jobs.size() * sizeof(CJob), 16);
+  for (auto& l : plan->launches) {
+    l.off = off;
+    off += 2 * l.starts.size() * sizeof(int32_t);
+    off = round_up(off, 16);
+  }
+  plan->table_bytes = off;
+  plan->data_off = round_up(off, 256);
+  plan->total_bytes = plan->data_off + (size_t)floats * sizeof(float);
+  return KAMERA_OK;
+}
+
+kamera_status validate_compile_pointers(const kamera_model& M, const kamera_compile_chunk* chunks,
+                                        int32_t n_chunks) {
+  const int64_t es = M.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+  struct Tagged {
+    Range r;
+    int chunk, ch;
+    const char* what;
+  };
+  std::vector<Tagged> outs, ins;
+  auto a16 = [&](int64_t stride) { return (stride * es) % 16 == 0; };
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_compile_chunk& k = chunks[i];
+    if (k.n_tokens == 0) continue;
+    for (int ch = 0; ch < 2; ++ch) {
+      const Channel g = channel_of(M, ch);
+      const int64_t row = (int64_t)g.heads * g.width;
+      const kamera_src* srcs[2] = {&k.canonical[ch], &k.conditioned[ch]};
+      const char* names[2] = {"canonical", "conditioned"};
+      for (int s = 0; s < 2; ++s) {
+        const kamera_src& x = *srcs[s];
+        if (!x.ptr)
+          return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: %s is NULL", i, ch,
+                      names[s]);
+        if (x.layer_stride < 0 || x.token_stride < row)
+          return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                      "chunk %d channel %d: %s token_stride %lld shorter than the row (%lld)", i,
+                      ch, names[s], (long long)x.token_stride, (long long)row);
+        if (!aligned16(x.ptr) || !a16(x.layer_stride) || !a16(x.token_stride))
+          return fail(KAMERA_ERR_UNSUPPORTED,
+                      "chunk %d channel %d: %s rows must start on 16-byte boundaries", i, ch,
+                      names[s]);
+        ins.push_back({view_range(x.ptr, x.layer_stride, M.n_layers, x.token_stride, k.n_tokens,
+                                  row, es),
+                       i, ch, names[s]});
+      }
+      const kamera_factors_out& o = k.out[ch];
+      if (!o.U || !o.V)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: U or V is NULL", i, ch);
+      if (o.u_layer_stride < 0 || o.u_head_stride < 0 || o.v_layer_stride < 0 ||
+          o.v_head_stride < 0)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: negative factor stride",
+                    i, ch);
+      const int64_t usz = (int64_t)k.n_tokens * k.m, vsz = (int64_t)g.width * k.m;
+      if (!strided_disjoint(o.u_layer_stride, M.n_layers, o.u_head_stride, g.heads, usz))
+        return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                    "chunk %d channel %d: U strides make layers or heads overlap", i, ch);
+      if (!strided_disjoint(o.v_layer_stride, M.n_layers, o.v_head_stride, g.heads, vsz))
+        return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                    "chunk %d channel %d: V strides make layers or heads overlap", i, ch);
+      // extent of a (layers x heads) strided view
+      auto extent = [&](const void* p, int64_t ls, int64_t hs, int64_t size) {
+        const int64_t last = (M.n_layers - 1) * ls + (g.heads - 1) * hs + size;
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+        return Range{b, b + (uintptr_t)(last * es)};
+      };
+      outs.push_back({extent(o.U, o.u_layer_stride, o.u_head_stride, usz), i, ch, "U"});
+      outs.push_back({extent(o.V, o.v_layer_stride, o.v_head_stride, vsz), i, ch, "V"});
+    }
+  }
+  std::sort(outs.begin(), outs.end(),
+            [](const Tagged& a, const Tagged& b) { return a.r.lo < b.r.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i].r.lo < outs[i - 1].r.hi)
+      return fail(KAMERA_ERR_OVERLAP, "chunk %d channel %d %s overlaps chunk %d channel %d %s",
+                  outs[i].chunk, outs[i].ch, outs[i].what, outs[i - 1].chunk, outs[i - 1].ch,
+                  outs[i - 1].what);
+  for (const Tagged& in : ins) {
+    // first output whose end lies past the input's start (ends ascend with starts here,
+    // since the outputs are disjoint)
+    auto it = std::upper_bound(outs.begin(), outs.end(), in.r.lo,
+                               [](uintptr_t v, const Tagged& o) { return v < o.r.hi; });
+    if (it != outs.end() && it->r.lo < in.r.hi)
+      return fail(KAMERA_ERR_OVERLAP, "chunk %d channel %d %s overlaps chunk %d channel %d %s",
+                  it->chunk, it->ch, it->what, in.chunk, in.ch, in.what);
+  }
+  return KAMERA_OK;
+}
+
+template <typename T>
+hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
+  const dim3 grid((unsigned)L.blocks), block(kThreads);
+  switch (L.kind) {
+    case kGram:
+      switch (L.cls) {
+        case 1: gram_kernel<T, 1><<<grid, block, 0, stream>>>(P); break;
+        case 2: gram_kernel<T, 2><<<grid, block, 0, stream>>>(P); break;
+        case 3: gram_kernel<T, 3><<<grid, block, 0, stream>>>(P); break;
+        case 4: gram_kernel<T, 4><<<grid, block, 0, stream>>>(P); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    case kSubspace:
+      switch (L.cls) {
+        case 0: subspace_kernel<T, 128, 16><<<grid, block, 0, stream>>>(P); break;
+        case 1: subspace_kernel<T, 128, 32><<<grid, block, 0, stream>>>(P); break;
+        case 2: subspace_kernel<T, 128, 64><<<grid, block, 0, stream>>>(P); break;
+        case 3: subspace_kernel<T, 512, 16><<<grid, block, 0, stream>>>(P); break;
+        case 4: subspace_kernel<T, 512, 32><<<grid, block, 0, stream>>>(P); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    case kProject:
+      if (L.cls == 0) project_kernel<T, 128, 64><<<grid, block, 0, stream>>>(P);
+      else project_kernel<T, 512, 32><<<grid, block, 0, stream>>>(P);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kamera_compile_workspace_bytes(const kamera_model* model,
+                                      const kamera_compile_chunk* chunks, int32_t n_chunks) {
+  if (validate_model(model) != KAMERA_OK) return 0;
+  CPlan plan;
+  if (plan_compile(*model, chunks, n_chunks, &plan) != KAMERA_OK) return 0;
+  return round_up(std::max<size_t>(plan.total_bytes, 256), 256);
+}
+
+kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compile_chunk* chunks,
+                                   int32_t n_chunks, int32_t n_iter, void* workspace,
+                                   size_t workspace_bytes, void* stream_ptr) {
+  clear_error();
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  if (n_iter < 1 || n_iter > 100)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_iter must be in [1, 100] (got %d)", n_iter);
+  CPlan plan;
+  st = plan_compile(*model, chunks, n_chunks, &plan);
+  if (st != KAMERA_OK) return st;
+  st = validate_compile_pointers(*model, chunks, n_chunks);
+  if (st != KAMERA_OK) return st;
+  if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = round_up(std::max<size_t>(plan.total_bytes, 256), 256);
+  if (workspace_bytes < need)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (plan.jobs.empty()) return KAMERA_OK;
+
+  std::vector<uint8_t> table(plan.table_bytes, 0);
+  std::memcpy(table.data(), plan.jobs.data(), plan.jobs.size() * sizeof(CJob));
+  for (const Launch& l : plan.launches) {
+    std::memcpy(table.data() + l.off, l.starts.data(), l.starts.size() * sizeof(int32_t));
+    std::memcpy(table.data() + l.off + l.starts.size() * sizeof(int32_t), l.job_of.data(),
+                l.job_of.size() * sizeof(int32_t));
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  st = upload(table, workspace, stream);
+  if (st != KAMERA_OK) return st;
+
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  CParams P{};
+  P.jobs = reinterpret_cast<const CJob*>(base);
+  P.ws = reinterpret_cast<float*>(base + plan.data_off);
+  P.theta = model->rope_theta;
+  P.layout = model->rope_layout;
+  P.n_iter = n_iter;
+  // kernels in dependency order: every Gram tile, then every subspace, then every projection
+  for (int kind = kGram; kind <= kProject; ++kind) {
+    for (const Launch& l : plan.launches) {
+      if (l.kind != kind || l.blocks == 0) continue;
+      P.starts = reinterpret_cast<const int32_t*>(base + l.off);
+      P.job_of = P.starts + l.starts.size();
+      P.n_entries = (int32_t)l.starts.size();
+      const hipError_t e = model->dtype == KAMERA_DTYPE_BF16 ? launch_one<uint16_t>(l, P, stream)
+                                                             : launch_one<float>(l, P, stream);
+      if (e != hipSuccess)
+        return fail(KAMERA_ERR_HIP, "compile kernel launch: %s", hipGetErrorString(e));
+    }
+  }
+  return KAMERA_OK;
+}
+
+}  // extern "C"
