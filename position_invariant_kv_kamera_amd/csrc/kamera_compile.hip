@@ -38,8 +38,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kStepTokens = 32;      // tokens of Delta staged in LDS per step
 constexpr int kProjTokens = 128;     // tokens per projection block
-constexpr int kMinSplitTokens = 256; // Gram split never shorter than this (except the tail)
-constexpr int kGramBlocksPerJob = 1024;
+constexpr int kMinSplitTokens = 1024; // Gram split never shorter than this (except the tail)
+constexpr int kGramTilesPerJob = 64;   // jobs with fewer Gram tiles split their tokens
 constexpr double kDeadTol = 1e-12;   // pivot^2 / column norm^2 below this: column collapsed
 
 // One chunk, one channel, all layers and heads (a "unit" is one layer and head).
@@ -66,7 +66,7 @@ struct CParams {
   int32_t n_entries;
   int32_t layout;
   int32_t n_iter;
-  int32_t pad0;
+  int32_t n_total;         // units covered by a per-wave launch
 };
 
 // ---------------------------------------------------------------------------------------
@@ -120,10 +120,10 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) {
 }
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
-// Rows [tok0, tok0 + kStepTokens) of Delta, columns [col0, col0 + ncols), into dst (fp32, row
-// stride ds); rows at or past tok_end are zero. A rotated head is always staged whole
-// (col0 = 0, ncols = width) so that both members of every pair are at hand.
-template <typename T>
+// Rows [tok0, tok0 + ROWS) of Delta, columns [col0, col0 + ncols), into dst (fp32, row stride
+// ds); rows at or past tok_end are zero. A rotated head is always staged whole (col0 = 0,
+// ncols = width) so that both members of every pair are at hand.
+template <typename T, int ROWS>
 __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int layer, int head,
                             int tok0, int tok_end, int col0, int ncols, float* dst, int ds) {
   const int W = J.width;
@@ -131,7 +131,7 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
   const T* cond = static_cast<const T*>(J.cond) + layer * J.cond_ls + (int64_t)head * W;
   if (J.rotate) {
     const int gpr = W / 16;   // groups of 8 pairs per row
-    for (int g = threadIdx.x; g < kStepTokens * gpr; g += kThreads) {
+    for (int g = threadIdx.x; g < ROWS * gpr; g += kThreads) {
       const int r = g / gpr, q = g - r * gpr;
       const int tok = tok0 + r;
       float* d = dst + r * ds;
@@ -176,7 +176,7 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
     }
   } else {
     const int gpr = ncols / 8;
-    for (int g = threadIdx.x; g < kStepTokens * gpr; g += kThreads) {
+    for (int g = threadIdx.x; g < ROWS * gpr; g += kThreads) {
       const int r = g / gpr, q = g - r * gpr;
       const int tok = tok0 + r;
       float* d = dst + r * ds + 8 * q;
@@ -252,8 +252,9 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
 
   for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
     __syncthreads();
-    stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
-    if (bi != bj) stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
+    stage_delta<T, kStepTokens>(J, P.layout, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
+    if (bi != bj)
+      stage_delta<T, kStepTokens>(J, P.layout, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
     __syncthreads();
 #pragma unroll 2
     for (int kk = 0; kk < kStepTokens / 4; ++kk) {
@@ -284,9 +285,11 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
 }
 
 // ---------------------------------------------------------------------------------------
-// subspace: one block per unit. DMAX >= width, MMAX >= mp (a multiple of 16).
+// subspace: one block per unit, for widths above 128 (an MLA latent). DMAX >= width,
+// MMAX >= mp (a multiple of 16). G is read from the workspace (L2) in every round.
 // LDS: xs [width][mp] fp32 (row-major), ys [mp][width+1] fp32 (column-major, padded),
-//      ss [m][m] fp64 (S, then L in its lower triangle), li [mp][mp] fp64 (L^-1).
+//      ss [m][MMAX+1] fp64: S = Y^T Y, overwritten column by column with its Cholesky factor L,
+//      li [mp][MMAX+1] fp64: L^-1.
 // ---------------------------------------------------------------------------------------
 
 __device__ __forceinline__ float seed_value(int i, int j, int round) {
@@ -300,13 +303,17 @@ __device__ __forceinline__ float seed_value(int i, int j, int round) {
   return (h & 1u) ? 1.f : -1.f;
 }
 
-// X = orth(Y): Cholesky QR with S, L and L^-1 in fp64. Dead (collapsed) columns become a fresh
-// +-1 vector when `reseed_round` >= 0, zero otherwise.
-__device__ void orth(const float* ys, float* xs, double* ss, double* li, int* dead, int D, int m,
-                     int mp, int reseed_round) {
+// X = orth(Y), a Cholesky QR in fp64: S = Y^T Y (fp32 products are exact in fp64), L L^T = S
+// (left-looking, lane i of wave 0 owns row i), L^-1 (lane j owns column j), then
+// X = Y L^-T with fp64 accumulation, so nothing is rounded before the final fp32 store.
+// Collapsed columns (pivot^2 <= kDeadTol * S_jj) give x_j = 0, or a fresh +-1 column when
+// reseed_round >= 0 (the next round's G X spreads it).
+template <int MMAX>
+__device__ void orth(const float* ys, float* xs, double* ss, double* li, double* inv, int* dead,
+                     int D, int m, int mp, int reseed_round) {
+  constexpr int SS = MMAX + 1;   // padded row stride of S, L and L^-1 (doubles)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int YS = D + 1;
-  // S = Y^T Y (lower triangle, mirrored); fp32 products are exact in fp64
   const int npair = m * (m + 1) / 2;
   for (int q = tid; q < npair; q += kThreads) {
     int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
@@ -315,56 +322,50 @@ __device__ void orth(const float* ys, float* xs, double* ss, double* li, int* de
     const int b = q - a * (a + 1) / 2;
     const float* ya = ys + a * YS;
     const float* yb = ys + b * YS;
-    double acc = 0.0;
-    for (int i = 0; i < D; ++i) acc += (double)ya[i] * (double)yb[i];
-    ss[a * m + b] = acc;
-    ss[b * m + a] = acc;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
+#pragma unroll 2
+    for (int i = 0; i < D; i += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += (double)ya[i + k] * (double)yb[i + k];
+    }
+    ss[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);   // lower triangle, a >= b
   }
   __syncthreads();
   if (wave == 0) {
     const int i = lane;
-    // right-looking Cholesky of S (lower triangle), lane i owns row i
-    double diag_i = i < m ? ss[i * m + i] : 0.0;
-    for (int k = 0; k < m; ++k) {
-      wave_lds_sync();
-      const double d = ss[k * m + k];
-      const double d0 = __shfl(diag_i, k, 64);
-      const bool dk = d <= kDeadTol * d0;
-      const double lkk = dk ? 0.0 : sqrt(d);
-      const double inv = dk ? 0.0 : 1.0 / lkk;
-      double lik = 0.0;
-      if (i > k && i < m) {
-        lik = ss[i * m + k] * inv;
-        ss[i * m + k] = lik;
-      }
-      if (i == k) {
-        ss[k * m + k] = lkk;
-        dead[k] = dk ? 1 : 0;
+    for (int j = 0; j < m; ++j) {
+      double dot = 0.0;
+      if (i >= j && i < m)
+        for (int a = 0; a < j; ++a) dot += ss[i * SS + a] * ss[j * SS + a];
+      if (i == j) {
+        const double sjj = ss[j * SS + j];
+        const double d = sjj - dot;
+        const bool dk = d <= kDeadTol * sjj;
+        const double ljj = dk ? 0.0 : sqrt(d);
+        ss[j * SS + j] = ljj;
+        inv[j] = dk ? 0.0 : 1.0 / ljj;
+        dead[j] = dk ? 1 : 0;
       }
       wave_lds_sync();
-      if (i > k && i < m && !dk)
-        for (int j = k + 1; j <= i; ++j) ss[i * m + j] -= lik * ss[j * m + k];
+      if (i > j && i < m) ss[i * SS + j] = (ss[i * SS + j] - dot) * inv[j];
+      wave_lds_sync();
     }
-    wave_lds_sync();
-    // li = L^-1, lane j fills column j; rows >= m and the strict upper triangle are zero
+    // L^-1: lane j solves L z = e_j; rows >= m and the strict upper triangle are zero
     if (i < mp) {
       const int j = i;
-      for (int r = 0; r < mp; ++r) li[r * mp + j] = 0.0;
+      for (int r = 0; r < mp; ++r) li[r * SS + j] = 0.0;
       if (j < m) {
-        const double ljj = ss[j * m + j];
-        li[j * mp + j] = ljj > 0.0 ? 1.0 / ljj : 0.0;
+        li[j * SS + j] = inv[j];
         for (int r = j + 1; r < m; ++r) {
-          const double lrr = ss[r * m + r];
-          if (!(lrr > 0.0)) continue;   // dead row stays zero
           double acc = 0.0;
-          for (int a = j; a < r; ++a) acc += ss[r * m + a] * li[a * mp + j];
-          li[r * mp + j] = -acc / lrr;
+          for (int a = j; a < r; ++a) acc += ss[r * SS + a] * li[a * SS + j];
+          li[r * SS + j] = -acc * inv[r];
         }
       }
     }
   }
   __syncthreads();
-  // X = Y L^-T: x[i][j] = sum_{a <= j} y[i][a] * li[j][a], accumulated in fp64
+  // X = Y L^-T: x[i][j] = sum_{a <= j} y[i][a] * li[j][a]
   const int groups = (m + 15) / 16;
   for (int u = tid; u < D * groups; u += kThreads) {
     const int i = u % D, jg = u / D;
@@ -372,11 +373,12 @@ __device__ void orth(const float* ys, float* xs, double* ss, double* li, int* de
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[c] = 0.0;
     const int a_end = min(m, 16 * jg + 16);
+#pragma unroll 2
     for (int a = 0; a < a_end; ++a) {
       const double y = (double)ys[a * YS + i];
-      const double* lr = li + (16 * jg) * mp + a;
+      const double* lr = li + (16 * jg) * SS + a;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) acc[c] += y * lr[c * mp];
+      for (int c = 0; c < 16; ++c) acc[c] += y * lr[c * SS];
     }
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -395,8 +397,9 @@ template <typename T, int DMAX, int MMAX>
 __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
   __shared__ __align__(16) float xs[DMAX * MMAX];
   __shared__ float ys[MMAX * (DMAX + 1)];
-  __shared__ double ss[MMAX * MMAX];
-  __shared__ double li[MMAX * MMAX];
+  __shared__ double ss[MMAX * (MMAX + 1)];
+  __shared__ double li[MMAX * (MMAX + 1)];
+  __shared__ double inv[MMAX];
   __shared__ int dead[MMAX];
 
   const int e = find_entry(P, blockIdx.x);
@@ -416,12 +419,25 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
       int bi, bj;
       pair_tiles(pair, J.nb, &bi, &bj);
       const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
-      for (int idx = tid; idx < te2; idx += kThreads) {
-        float v = 0.f;
-        for (int s = 0; s < J.splits; ++s) v += part[(int64_t)s * te2 + idx];
-        const int ii = idx / te, jj = idx - ii * te;
-        gf[(bi * te + ii) * D + bj * te + jj] = v;
-        if (bi != bj) gf[(bj * te + jj) * D + bi * te + ii] = v;
+      const float4* part4 = reinterpret_cast<const float4*>(part);
+#pragma unroll 4
+      for (int i4 = tid; i4 < te2 / 4; i4 += kThreads) {
+        float4 v = part4[i4];
+#pragma unroll 4
+        for (int s = 1; s < J.splits; ++s) {
+          const float4 w = part4[(int64_t)s * (te2 / 4) + i4];
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        const int ii = (4 * i4) / te, jj = 4 * i4 - ii * te;
+        *reinterpret_cast<float4*>(gf + (bi * te + ii) * D + bj * te + jj) = v;
+        if (bi != bj) {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) gf[(bj * te + jj + c) * D + bi * te + ii] = vv[c];
+        }
       }
     }
     __syncthreads();
@@ -432,17 +448,19 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
     const int i = idx / mp, j = idx - i * mp;
     xs[idx] = j < m ? seed_value(i, j, 0) : 0.f;
   }
-  __syncthreads();
 
   const int YS = D + 1;
   const int groups = mp / 16;
+  __syncthreads();
+
   for (int round = 0; round < P.n_iter; ++round) {
-    // Y = G X (G symmetric: column i read as row i, coalesced)
+    // Y = G X (G symmetric: column i read as row i)
     for (int u = tid; u < D * groups; u += kThreads) {
       const int i = u % D, cg = u / D;
       float acc[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+#pragma unroll 8
       for (int k = 0; k < D; ++k) {
         const float g = G[(int64_t)k * D + i];
         const float4* xr = reinterpret_cast<const float4*>(xs + k * mp + 16 * cg);
@@ -459,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
       for (int c = 0; c < 16; ++c) ys[(16 * cg + c) * YS + i] = acc[c];
     }
     __syncthreads();
-    orth(ys, xs, ss, li, dead, D, m, mp, round);
+    orth<MMAX>(ys, xs, ss, li, inv, dead, D, m, mp, round);
   }
   // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
   for (int idx = tid; idx < D * m; idx += kThreads) {
@@ -467,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
     ys[j * YS + i] = xs[i * mp + j];
   }
   __syncthreads();
-  orth(ys, xs, ss, li, dead, D, m, mp, -1);
+  orth<MMAX>(ys, xs, ss, li, inv, dead, D, m, mp, -1);
 
   T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
   float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
@@ -480,13 +498,217 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
 }
 
 // ---------------------------------------------------------------------------------------
-// project: U = Delta X for kProjTokens tokens of one unit per block.
+// subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
+// wave-synchronous. MP = mp exactly. Per wave in LDS:
+//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (the
+//       triangular step runs over columns from last to first, so each x_j only replaces a
+//       y_j no later column needs);
+//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), then its Cholesky factor L (lower) and L^-1
+//       (strict upper, transposed: (L^-1)_rj at [j][r]); its diagonal is inv.
+// Lane l owns rows l and l + 64.
 // ---------------------------------------------------------------------------------------
 
-template <typename T, int DMAX, int MPMAX>
+__device__ __forceinline__ void wave_global_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int MP>
+__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
+                          int reseed_round) {
+  constexpr int BS = MP + 4, SS = MP + 1;
+  const int lane = threadIdx.x & 63;
+  // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
+  const int npair = m * (m + 1) / 2;
+  for (int q = lane; q < npair; q += 64) {
+    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
+    while (a * (a + 1) / 2 > q) --a;
+    while ((a + 1) * (a + 2) / 2 <= q) ++a;
+    const int b = q - a * (a + 1) / 2;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
+#pragma unroll 2
+    for (int r = 0; r < D; r += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
+    }
+    lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  wave_lds_sync();
+  // Cholesky, left-looking: lane i owns row i
+  const int i = lane;
+  for (int j = 0; j < m; ++j) {
+    double dot = 0.0;
+    if (i >= j && i < m)
+      for (int a = 0; a < j; ++a) dot += lm[i * SS + a] * lm[j * SS + a];
+    if (i == j) {
+      const double sjj = lm[j * SS + j];
+      const double d = sjj - dot;
+      const bool dk = d <= kDeadTol * sjj;
+      const double ljj = dk ? 0.0 : sqrt(d);
+      lm[j * SS + j] = ljj;
+      inv[j] = dk ? 0.0 : 1.0 / ljj;
+      dead[j] = dk ? 1 : 0;
+    }
+    wave_lds_sync();
+    if (i > j && i < m) lm[i * SS + j] = (lm[i * SS + j] - dot) * inv[j];
+    wave_lds_sync();
+  }
+  // L^-1: lane j solves L z = e_j; z_r (r > j) goes to lm[j][r]
+  if (i < m) {
+    const int j = i;
+    for (int r = j + 1; r < m; ++r) {
+      double acc = lm[r * SS + j] * inv[j];
+      for (int a = j + 1; a < r; ++a) acc += lm[r * SS + a] * lm[j * SS + a];
+      lm[j * SS + r] = -acc * inv[r];
+    }
+  }
+  wave_lds_sync();
+  // X = Y L^-T: x_rj = y_rj inv_j + sum_{a<j} y_ra (L^-1)_ja, columns last to first, in place
+  for (int h = 0; h < 2; ++h) {
+    const int r = lane + 64 * h;
+    if (r >= D) continue;
+    float* row = buf + r * BS;
+    for (int j = m - 1; j >= 0; --j) {
+      double acc = (double)row[j] * inv[j];
+#pragma unroll 4
+      for (int a = 0; a < j; ++a) acc += (double)row[a] * lm[a * SS + j];
+      float v = (float)acc;
+      if (reseed_round >= 0 && dead[j]) v = seed_value(r, j, reseed_round + 1);
+      row[j] = v;
+    }
+  }
+  wave_lds_sync();
+}
+
+template <typename T, int MP, int WPB>
+__global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
+  constexpr int BS = MP + 4, SS = MP + 1;
+  __shared__ __align__(16) float buf_s[WPB][128 * BS];
+  __shared__ double lm_s[WPB][MP * SS];
+  __shared__ double inv_s[WPB][MP];
+  __shared__ int dead_s[WPB][MP];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int u = blockIdx.x * WPB + w;
+  if (u >= P.n_total) return;   // whole wave; no block-wide barrier follows
+  float* buf = buf_s[w];
+  double* lm = lm_s[w];
+  double* inv = inv_s[w];
+  int* dead = dead_s[w];
+
+  const int e = find_entry(P, u);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int unit = u - P.starts[e];
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int D = J.width, m = J.m;
+
+  const float* G;
+  if (J.gfull < 0) {
+    G = P.ws + J.gpart + (int64_t)unit * D * D;
+  } else {
+    // width <= 128 is a single tile pair: sum the token splits
+    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
+    const float4* part4 = reinterpret_cast<const float4*>(P.ws + J.gpart +
+                                                          (int64_t)unit * J.splits * D * D);
+    const int n4 = D * D / 4;
+#pragma unroll 4
+    for (int i4 = lane; i4 < n4; i4 += 64) {
+      float4 v = part4[i4];
+      for (int s = 1; s < J.splits; ++s) {
+        const float4 x = part4[(int64_t)s * n4 + i4];
+        v.x += x.x;
+        v.y += x.y;
+        v.z += x.z;
+        v.w += x.w;
+      }
+      reinterpret_cast<float4*>(gf)[i4] = v;
+    }
+    wave_global_sync();
+    G = gf;
+  }
+
+  const int r0 = lane, r1 = lane + 64;
+  const int c0 = r0 < D ? r0 : 0, c1 = r1 < D ? r1 : 0;
+  for (int h = 0; h < 2; ++h) {
+    const int r = lane + 64 * h;
+    if (r >= D) continue;
+#pragma unroll
+    for (int j = 0; j < MP; ++j) buf[r * BS + j] = j < m ? seed_value(r, j, 0) : 0.f;
+  }
+  wave_lds_sync();
+
+  for (int round = 0; round < P.n_iter; ++round) {
+    // Y = G X for rows r0, r1 (G symmetric: column r read as row r)
+    float y0[MP], y1[MP];
+#pragma unroll
+    for (int c = 0; c < MP; ++c) y0[c] = y1[c] = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const float g0 = G[(int64_t)k * D + c0];
+      const float g1 = G[(int64_t)k * D + c1];
+      const float4* xr = reinterpret_cast<const float4*>(buf + k * BS);
+#pragma unroll
+      for (int q = 0; q < MP / 4; ++q) {
+        const float4 x = xr[q];
+        y0[4 * q] += g0 * x.x;
+        y0[4 * q + 1] += g0 * x.y;
+        y0[4 * q + 2] += g0 * x.z;
+        y0[4 * q + 3] += g0 * x.w;
+        y1[4 * q] += g1 * x.x;
+        y1[4 * q + 1] += g1 * x.y;
+        y1[4 * q + 2] += g1 * x.z;
+        y1[4 * q + 3] += g1 * x.w;
+      }
+    }
+    wave_lds_sync();   // every lane has read X
+    if (r0 < D) {
+      float4* row = reinterpret_cast<float4*>(buf + r0 * BS);
+#pragma unroll
+      for (int q = 0; q < MP / 4; ++q)
+        row[q] = make_float4(y0[4 * q], y0[4 * q + 1], y0[4 * q + 2], y0[4 * q + 3]);
+    }
+    if (r1 < D) {
+      float4* row = reinterpret_cast<float4*>(buf + r1 * BS);
+#pragma unroll
+      for (int q = 0; q < MP / 4; ++q)
+        row[q] = make_float4(y1[4 * q], y1[4 * q + 1], y1[4 * q + 2], y1[4 * q + 3]);
+    }
+    wave_lds_sync();
+    orth_wave<MP>(buf, lm, inv, dead, D, m, round);
+  }
+  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
+  orth_wave<MP>(buf, lm, inv, dead, D, m, -1);
+
+  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
+  float* xg = P.ws + J.xbase + (int64_t)unit * D * MP;
+  for (int h = 0; h < 2; ++h) {
+    const int r = lane + 64 * h;
+    if (r >= D) continue;
+#pragma unroll
+    for (int j = 0; j < MP; ++j) {
+      const float v = buf[r * BS + j];
+      xg[r * MP + j] = v;
+      if (j < m) store_elem(V + r * m + j, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// project: U = Delta X for kProjTokens tokens of one unit per block, fp32 MFMA 16x16x4.
+// Each step stages 16*TG tokens of Delta (row stride width+4: the 16 rows an MFMA operand
+// reads fall in distinct LDS banks); wave w takes token group w % TG and every (4/TG)-th
+// 16-column block of X. X sits in LDS with row stride SV (16, or 80 for wider mp at widths
+// up to 128, or mp for wider heads).
+// ---------------------------------------------------------------------------------------
+
+template <typename T, int DMAX, int TG>
 __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
-  __shared__ __align__(16) float vs[DMAX * MPMAX];
-  __shared__ float dl[kStepTokens * (DMAX + 16)];
+  constexpr int RG = 4 / TG;
+  constexpr int STEP = 16 * TG;
+  constexpr int SVMAX = DMAX <= 128 ? 80 : 32;
+  __shared__ __align__(16) float vs[DMAX * SVMAX];
+  __shared__ __align__(16) float dl[STEP * (DMAX + 4)];
   __shared__ float2 cs[64];
 
   const int e = find_entry(P, blockIdx.x);
@@ -496,37 +718,52 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
   const int unit = local / tblocks, tb = local - unit * tblocks;
   const int layer = unit / J.heads, head = unit - layer * J.heads;
   const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
-  const int DSt = D + 16;
+  const int DS = D + 4;
+  const int SV = mp == 16 ? 16 : (DMAX <= 128 ? 80 : mp);
   if (J.rotate) fill_phases(cs, J.delta, P.theta, D);
   const float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
-  for (int idx = tid; idx < D * mp; idx += kThreads) vs[idx] = xg[idx];
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int f = idx / mp, r = idx - f * mp;
+    vs[f * SV + r] = xg[idx];
+  }
 
   T* U = static_cast<T*>(J.U) + layer * J.u_ls + head * J.u_hs;
   const int t_lo = tb * kProjTokens, t_hi = min(J.n_tokens, t_lo + kProjTokens);
-  const int rgroups = mp / 4;
-  for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int tg = wave % TG, rg = wave / TG;
+  const int nrb = mp / 16;
+  const int arow = (16 * tg + (lane & 15)) * DS + (lane >> 4);
+  const int brow = (lane >> 4) * SV + (lane & 15);
+  for (int tok0 = t_lo; tok0 < t_hi; tok0 += STEP) {
     __syncthreads();
-    stage_delta<T>(J, P.layout, cs, layer, head, tok0, t_hi, 0, D, dl, DSt);
+    stage_delta<T, STEP>(J, P.layout, cs, layer, head, tok0, t_hi, 0, D, dl, DS);
     __syncthreads();
-    for (int u = tid; u < kStepTokens * rgroups; u += kThreads) {
-      const int r = u / rgroups, rg = u - r * rgroups;
-      const int tok = tok0 + r;
-      if (tok >= t_hi || 4 * rg >= m) continue;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      const float* drow = dl + r * DSt;
-      for (int f = 0; f < D; ++f) {
-        const float d = drow[f];
-        const float4 v = *reinterpret_cast<const float4*>(vs + f * mp + 4 * rg);
-        a0 += d * v.x;
-        a1 += d * v.y;
-        a2 += d * v.z;
-        a3 += d * v.w;
-      }
-      T* ur = U + (int64_t)tok * m + 4 * rg;
-      const float a[4] = {a0, a1, a2, a3};
+    f32x4 acc[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (4 * rg + c < m) store_elem(ur + c, a[c]);
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const float a = dl[arow + k0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rb = rg + q * RG;
+        if (rb < nrb) {
+          const float b = vs[brow + k0 * SV + 16 * rb];
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[q], 0, 0, 0);
+        }
+      }
+    }
+    // lane holds U rows tok0 + 16 tg + 4 (lane / 16) + i, column 16 rb + lane % 16
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rb = rg + q * RG;
+      const int col = 16 * rb + (lane & 15);
+      if (rb < nrb && col < m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tok0 + 16 * tg + 4 * (lane >> 4) + i;
+          if (tok < t_hi) store_elem(U + (int64_t)tok * m + col, acc[q][i]);
+        }
+      }
     }
   }
 }
@@ -553,14 +790,14 @@ struct CPlan {
   size_t total_bytes = 0;
 };
 
-// subspace LDS classes: (DMAX, MMAX)
-constexpr int kSubD[5] = {128, 128, 128, 512, 512};
-constexpr int kSubM[5] = {16, 32, 64, 16, 32};
+// subspace classes: 0..3 one wave per unit (width <= 128, mp = 16, 32, 48, 64); 4, 5 one block
+// per unit (width up to 512, mp <= 16, <= 32)
+constexpr int kWaveClasses = 4;
+constexpr int kWavesPerBlock[kWaveClasses] = {4, 2, 1, 1};   // LDS per block <= 54 KB, 69 KB
 
 int subspace_class(int D, int mp) {
-  for (int c = 0; c < 5; ++c)
-    if (D <= kSubD[c] && mp <= kSubM[c]) return c;
-  return -1;
+  if (D <= 128) return mp / 16 - 1;
+  return mp <= 16 ? 4 : 5;
 }
 
 bool width_supported(const Channel& g) {
@@ -636,9 +873,10 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
       J.nb = g.width / J.te;
       J.n_pairs = J.nb * (J.nb + 1) / 2;
       J.n_units = M.n_layers * g.heads;
-      // token splits depend on this job alone, so a chunk compiles to the same bits in any batch
+      // token splits depend on this job alone, so a chunk compiles to the same bits in any
+      // batch; only jobs with few Gram tiles split (a split costs a partial G in HBM)
       const int64_t tiles = (int64_t)J.n_units * J.n_pairs;
-      int splits = (int)std::max<int64_t>(1, (kGramBlocksPerJob + tiles - 1) / tiles);
+      int splits = (int)std::max<int64_t>(1, (kGramTilesPerJob + tiles - 1) / tiles);
       splits = std::min(splits, std::max(1, (k.n_tokens + kMinSplitTokens - 1) / kMinSplitTokens));
       int st = (k.n_tokens + splits - 1) / splits;
       st = (st + kStepTokens - 1) / kStepTokens * kStepTokens;
@@ -788,19 +1026,27 @@ hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
         default: return hipErrorInvalidValue;
       }
       break;
-    case kSubspace:
-      switch (L.cls) {
-        case 0: subspace_kernel<T, 128, 16><<<grid, block, 0, stream>>>(P); break;
-        case 1: subspace_kernel<T, 128, 32><<<grid, block, 0, stream>>>(P); break;
-        case 2: subspace_kernel<T, 128, 64><<<grid, block, 0, stream>>>(P); break;
-        case 3: subspace_kernel<T, 512, 16><<<grid, block, 0, stream>>>(P); break;
-        case 4: subspace_kernel<T, 512, 32><<<grid, block, 0, stream>>>(P); break;
-        default: return hipErrorInvalidValue;
+    case kSubspace: {
+      if (L.cls < kWaveClasses) {
+        const int wpb = kWavesPerBlock[L.cls];
+        const dim3 wgrid((unsigned)((L.blocks + wpb - 1) / wpb)), wblock(64 * wpb);
+        P.n_total = (int32_t)L.blocks;
+        switch (L.cls) {
+          case 0: subspace_wave_kernel<T, 16, 4><<<wgrid, wblock, 0, stream>>>(P); break;
+          case 1: subspace_wave_kernel<T, 32, 2><<<wgrid, wblock, 0, stream>>>(P); break;
+          case 2: subspace_wave_kernel<T, 48, 1><<<wgrid, wblock, 0, stream>>>(P); break;
+          case 3: subspace_wave_kernel<T, 64, 1><<<wgrid, wblock, 0, stream>>>(P); break;
+        }
+      } else if (L.cls == 4) {
+        subspace_kernel<T, 512, 16><<<grid, block, 0, stream>>>(P);
+      } else {
+        subspace_kernel<T, 512, 32><<<grid, block, 0, stream>>>(P);
       }
       break;
+    }
     case kProject:
-      if (L.cls == 0) project_kernel<T, 128, 64><<<grid, block, 0, stream>>>(P);
-      else project_kernel<T, 512, 32><<<grid, block, 0, stream>>>(P);
+      if (L.cls == 0) project_kernel<T, 128, 4><<<grid, block, 0, stream>>>(P);
+      else project_kernel<T, 512, 2><<<grid, block, 0, stream>>>(P);
       break;
     default: return hipErrorInvalidValue;
   }

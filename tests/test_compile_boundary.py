@@ -91,19 +91,23 @@ def test_well_formed_call_reaches_the_workspace_check():
 
 def test_workspace_bytes_closed_form():
     """Sizing depends on geometry only: partial Gram tiles per token split, the assembled G
-    where there is more than one partial, and the fp32 basis (width x mp) per layer and head."""
+    where there is more than one partial, and the fp32 basis (width x mp) per layer and head.
+    Jobs with 64 or more Gram tiles do not split their tokens."""
     m = _model(n_layers=28, n_kv_heads=4)
     one = _chunks(m, n_tokens=1296, m=16)
     need = kb.kamera_compile_workspace_bytes(m, one, 1)
     units = 28 * 4
-    splits = min(-(-1024 // units), -(-1296 // 256))            # 10 vs 6 -> 6
-    st = -(-1296 // splits)
-    st = -(-st // 32) * 32
-    splits = -(-1296 // st)
-    per_ch = units * (splits * 128 * 128 + 128 * 128 + 128 * 16)
-    per_ch = -(-per_ch // 64) * 64
+    per_ch = units * (128 * 128 + 128 * 16)                     # one split, one tile pair
     data = 2 * per_ch * 4
     assert data < need < data + 64 * 1024
+    # 2 layers x 2 heads = 4 tiles per job: split into ceil(3000 / 1024) = 3 partials
+    small = _model()
+    ch3 = _chunks(small, n_tokens=3000, m=16)
+    units = 2 * 2
+    per_ch = units * (3 * 128 * 128 + 128 * 128 + 128 * 16)
+    data = 2 * per_ch * 4
+    got = kb.kamera_compile_workspace_bytes(small, ch3, 1)
+    assert data < got < data + 64 * 1024
     two = _chunks(m, n=2, n_tokens=1296, m=16)
     assert kb.kamera_compile_workspace_bytes(m, two, 2) > need
     empty = _chunks(m, n_tokens=0)
