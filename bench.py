@@ -4,8 +4,11 @@ One step = one kamera_reuse_batch call over the whole batch: work decomposition,
 generation, streaming of the canonical KV, rotation, the rank-m patch, and the page-table
 scatter, for every chunk, layer, channel and head. Inputs are resident in HBM before timing.
 
-Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s).
+Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s). The
+line also carries "patch_compile": the time kamera_patch_compile takes to form the same
+batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--compile-steps N]
 """
 from __future__ import annotations
 
@@ -118,6 +121,61 @@ def cpu_baseline(batch, budget_s: float) -> dict:
                       f"layers x 2 channels), {busy:.1f} s of oracle time"}
 
 
+FP32_PEAK_TFLOPS = 157.3       # dense fp32 (MFMA and vector alike)
+
+
+def compile_leg(p, batch, reuse_ms: float, steps: int, stream) -> dict:
+    """Time kamera_patch_compile over the same chunks (one step = the whole batch's patches at
+    the workload's largest rank). The conditioned KV is the canonical KV plus Gaussian noise;
+    the compile does the same work whatever the values."""
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+
+    m = max(p.m_rot + p.m_plain) or 16
+    n_iter = 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    items = []
+    es = p.elem_bytes
+    io_bytes = in_bytes = gram_flops = proj_flops = 0
+    for c, ct in enumerate(batch.chunks):
+        T = p.chunk_tokens[c]
+        cond, U, V = [], [], []
+        for ch in range(2):
+            src = ct.src[ch]
+            noise = torch.randn(src.shape, generator=gen, device="cuda", dtype=torch.float32)
+            cond.append((src.float() + 0.05 * noise).to(src.dtype))
+            H, W = p.heads(ch), p.width(ch)
+            U.append(torch.empty((p.n_layers, H, T, m), dtype=src.dtype, device="cuda"))
+            V.append(torch.empty((p.n_layers, H, W, m), dtype=src.dtype, device="cuda"))
+            units = p.n_layers * H
+            in_bytes += 2 * units * T * W * es
+            io_bytes += 2 * 2 * units * T * W * es + units * (T + W) * m * es
+            gram_flops += 2.0 * units * T * W * W
+            proj_flops += 2.0 * units * T * W * m
+        items.append(kb.CompileItem(T, m, p.deltas[c], list(ct.src), cond, U, V))
+    model = kb.model_of(p)
+    ws = kb.run_compile(model, items, n_iter=n_iter)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        kb.run_compile(model, items, n_iter=n_iter, workspace=ws, stream=stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    floor_ms = max(io_bytes / (HBM_PEAK_GBPS * 1e9),
+                   (gram_flops + proj_flops) / (FP32_PEAK_TFLOPS * 1e12)) * 1e3
+    return {"ms_per_batch": round(ms, 3), "steps": steps, "rank": m, "n_iter": n_iter,
+            "input_bytes": in_bytes,
+            "reuse_ms_per_batch": round(reuse_ms, 4),
+            "compile_over_reuse": round(ms / reuse_ms, 2),
+            "io_bytes": io_bytes, "gram_flops": gram_flops, "project_flops": proj_flops,
+            "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4),
+            "floor": "max(bytes / 8 TB/s, (Gram + projection flops) / 157.3 TFLOP/s fp32)",
+            "timed_with": "hip events on the launch stream"}
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -212,10 +270,66 @@ def summarize_profile(prof_dir: str, workload: str, command: str, bench_log: str
     print(out_md.read_text())
 
 
+def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_log: str) -> None:
+    """profiles/patch_compile_<workload>.md from a rocprofv3 --kernel-trace --stats run (named
+    `kt`) of bench.py and that run's JSON line (per-step bytes and flops of the compile)."""
+    d = Path(prof_dir)
+    rec = [json.loads(l) for l in Path(bench_log).read_text().splitlines()
+           if l.startswith("{") and '"metric"' in l][-1]
+    pc = rec["patch_compile"]
+    calls = pc["steps"] + 1                     # one untimed call, then the timed ones
+    rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
+    kinds = {"gram_kernel": [], "subspace": [], "project_kernel": []}
+    for r in rows:
+        for k in kinds:
+            if k in r["Name"]:
+                kinds[k].append(r)
+    io = pc["io_bytes"]
+    lines = [f"# patch compile on {workload}", "",
+             "Commands (R = repository root on the GPU box):", ""]
+    lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
+    lines += [f"Per compile call: rank {pc['rank']}, {pc['n_iter']} subspace rounds; "
+              f"{pc['ms_per_batch']} ms by HIP events in this run "
+              f"(one reuse pass over the same batch: {pc['reuse_ms_per_batch']} ms).", "",
+              "| kernel | launches | us per call | bound | achieved | of peak |",
+              "|---|---|---|---|---|---|"]
+    gram_f, proj_f = pc["gram_flops"], pc["project_flops"]
+    read2 = pc["input_bytes"]      # canonical + conditioned, read once by each streaming pass
+    for k, rs in kinds.items():
+        if not rs:
+            continue
+        tot_ns = sum(float(r["TotalDurationNs"]) for r in rs)
+        n = sum(int(r["Calls"]) for r in rs)
+        per_call_us = tot_ns / calls / 1e3
+        if k == "gram_kernel":
+            tf = gram_f / (per_call_us * 1e-6) / 1e12
+            lines.append(f"| gram (Delta^T Delta, fp32 MFMA) | {n} | {per_call_us:.1f} | mfma fp32 | "
+                         f"{tf:.1f} TFLOP/s | {tf / FP32_PEAK_TFLOPS:.3f} |")
+        elif k == "project_kernel":
+            gbps = read2 / (per_call_us * 1e-6) / 1e9
+            lines.append(f"| project (U = Delta V) | {n} | {per_call_us:.1f} | hbm | "
+                         f"{gbps:.0f} GB/s | {gbps / HBM_PEAK_GBPS:.3f} |")
+        else:
+            lines.append(f"| subspace iteration | {n} | {per_call_us:.1f} | latency | - | - |")
+    lines += ["", "Gram flops per call: 2 n D^2 per head (full product) = "
+              f"{gram_f / 1e9:.1f} GFLOP; projection bytes per call: both inputs once = "
+              f"{read2 / 1e9:.3f} GB.", "",
+              "## rocprofv3 --kernel-trace --stats (top kernels)", "",
+              "| kernel | calls | avg us | total % |", "|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0)))[:8]:
+        lines.append(f"| `{r['Name'][:70].replace('|', '/')}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    out_md = ROOT / "profiles" / f"patch_compile_{workload}.md"
+    out_md.write_text("\n".join(lines) + "\n")
+    print(out_md.read_text())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 CSV output in DIR and exit")
+    ap.add_argument("--summarize-compile-profile", metavar="DIR",
+                    help="write the patch-compile summary from rocprofv3 CSV output in DIR and exit")
     ap.add_argument("--profile-command", default="", help="commands recorded in the summary (';'-separated)")
     ap.add_argument("--profile-bench-log", default="", help="stdout of the profiled kernel-trace run")
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,7 +338,13 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compile-steps", type=int, default=5,
+                    help="timed kamera_patch_compile calls over the same batch (0: skip)")
     args = ap.parse_args()
+    if args.summarize_compile_profile:
+        summarize_compile_profile(args.summarize_compile_profile, args.workload,
+                                  args.profile_command, args.profile_bench_log)
+        return
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.profile_command,
                           args.profile_bench_log)
@@ -337,6 +457,9 @@ def main():
     }
     if tinfo == "stale":
         out["roofline"]["traffic_note"] = "counters were taken on older kernel sources"
+    if args.compile_steps > 0:
+        print("[bench] timing the patch compile over the same batch", file=sys.stderr, flush=True)
+        out["patch_compile"] = compile_leg(p, batch, ev_avg, args.compile_steps, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)
