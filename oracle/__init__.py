@@ -58,6 +58,10 @@ def _load():
     lib.kamera_oracle_segment.argtypes = [c_i32, c_vp, c_i64, c_i32, c_i32, c_i32, c_i32, c_i64,
                                           c_dbl, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]
     lib.kamera_oracle_segment.restype = ctypes.c_int
+    lib.kamera_oracle_segment_ex.argtypes = [c_i32, c_vp, c_i64, c_i32, c_i32, c_i32, c_i32,
+                                             c_i32, c_vp, c_vp, c_i64, c_dbl, c_i32, c_vp,
+                                             c_i64, c_vp, c_i64, c_vp, c_vp]
+    lib.kamera_oracle_segment_ex.restype = ctypes.c_int
     lib.kamera_oracle_to_f32.argtypes = [c_vp, c_i64, c_vp]
     lib.kamera_oracle_to_bf16.argtypes = [c_vp, c_i64, c_vp]
     lib.kamera_oracle_slots.argtypes = [c_vp, c_i32, c_i32, c_i64, c_i32, c_vp]
@@ -106,13 +110,24 @@ def _rows(a: np.ndarray, name: str) -> tuple[np.ndarray, int]:
     return a, a.strides[0] // a.itemsize
 
 
+def pair_deltas(pair_section, section_delta) -> np.ndarray:
+    """Per-pair shift of a multimodal (sectioned) RoPE: pair i turns by the shift of the
+    position component it encodes."""
+    sec = np.asarray(pair_section, np.int64)
+    return np.asarray(section_delta, np.int64)[sec]
+
+
 def segment(src: np.ndarray, *, rotate: bool, layout: int = HALF_SPLIT, delta: int = 0,
             theta: float = 1e4, U: np.ndarray | None = None,
-            V: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+            V: np.ndarray | None = None, rot_dim: int | None = None,
+            inv_freq: np.ndarray | None = None,
+            pair_delta: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
     """One head: src (tokens x width) -> (out, abs_sum), both fp64 (tokens x width).
 
-    out = R(delta) src + U V^T, R applied to pairs of ``layout`` when ``rotate``; U is
-    tokens x m and V width x m, in the element type of src.
+    out = R src + U V^T, R applied to the pairs (of ``layout``) of the first ``rot_dim``
+    features (default: all) when ``rotate``; pair i turns by pair_delta[i] (default: delta)
+    times inv_freq[i] (default: theta^(-2i/rot_dim)). U is tokens x m and V width x m, in the
+    element type of src.
     """
     dt = dtype_of(src)
     src, src_stride = _rows(src, "src")
@@ -131,10 +146,17 @@ def segment(src: np.ndarray, *, rotate: bool, layout: int = HALF_SPLIT, delta: i
         U = V = None
     out = np.empty((n_tokens, width), np.float64)
     mag = np.empty((n_tokens, width), np.float64)
-    rc = _load().kamera_oracle_segment(_DTYPE_CODE[dt], _ptr(src), src_stride, n_tokens, width,
-                                       int(bool(rotate)), int(layout), int(delta), float(theta),
-                                       m, _ptr(U), u_stride, _ptr(V), v_stride, _ptr(out),
-                                       _ptr(mag))
+    rd = width if rot_dim is None else int(rot_dim)
+    freq = None if inv_freq is None else np.ascontiguousarray(inv_freq, np.float64)
+    pdel = None if pair_delta is None else np.ascontiguousarray(pair_delta, np.int64)
+    for name, arr in (("inv_freq", freq), ("pair_delta", pdel)):
+        if arr is not None and arr.shape != (rd // 2,):
+            raise ValueError(f"oracle: {name} needs {rd // 2} entries, got {arr.shape}")
+    rc = _load().kamera_oracle_segment_ex(_DTYPE_CODE[dt], _ptr(src), src_stride, n_tokens,
+                                          width, int(bool(rotate)), int(layout), rd,
+                                          _ptr(freq), _ptr(pdel), int(delta), float(theta),
+                                          m, _ptr(U), u_stride, _ptr(V), v_stride, _ptr(out),
+                                          _ptr(mag))
     if rc != 0:
         raise ValueError("oracle: kamera_oracle_segment rejected its arguments")
     return out, mag
@@ -173,7 +195,7 @@ def slots(page_table: np.ndarray | None, page_size: int, dst_offset: int,
 
 
 def expected_head(src: np.ndarray, *, rotate: bool, layout: int, delta: int, theta: float,
-                  U: np.ndarray | None, V: np.ndarray | None) -> dict:
+                  U: np.ndarray | None, V: np.ndarray | None, **rope) -> dict:
     """What the operator must produce for one head of one chunk/layer/channel.
 
     Returns a dict with ``copy`` (True when the channel is unrotated and unpatched, so the
@@ -183,7 +205,7 @@ def expected_head(src: np.ndarray, *, rotate: bool, layout: int, delta: int, the
     m = 0 if U is None else U.shape[-1]
     if not rotate and m == 0:
         return {"copy": True, "bits": src}
-    z, S = segment(src, rotate=rotate, layout=layout, delta=delta, theta=theta, U=U, V=V)
+    z, S = segment(src, rotate=rotate, layout=layout, delta=delta, theta=theta, U=U, V=V, **rope)
     return {"copy": False, "z": z, "S": S}
 
 
@@ -199,20 +221,21 @@ def values(x: np.ndarray) -> np.ndarray:
 
 
 def deficit(conditioned: np.ndarray, canonical: np.ndarray, *, rotate: bool, layout: int = HALF_SPLIT,
-            delta: int = 0, theta: float = 1e4) -> np.ndarray:
+            delta: int = 0, theta: float = 1e4, **rope) -> np.ndarray:
     """Delta = KV(B|A) - R(delta) KV(B|empty) for one head (tokens x features), fp64."""
-    reloc, _ = segment(canonical, rotate=rotate, layout=layout, delta=delta, theta=theta)
+    reloc, _ = segment(canonical, rotate=rotate, layout=layout, delta=delta, theta=theta, **rope)
     return values(conditioned) - reloc
 
 
 def compile_patch(conditioned: np.ndarray, canonical: np.ndarray, *, m: int, rotate: bool,
-                  layout: int = HALF_SPLIT, delta: int = 0, theta: float = 1e4) -> dict:
+                  layout: int = HALF_SPLIT, delta: int = 0, theta: float = 1e4, **rope) -> dict:
     """Top-m SVD factors of the deficit of one head (LAPACK through numpy).
 
     Returns U (tokens x m) = left singular vectors times the singular values, V (features x m)
     = right singular vectors, the product UV (= the best rank-m approximation of Delta,
     Eckart-Young), all singular values `s`, and Delta itself."""
-    d = deficit(conditioned, canonical, rotate=rotate, layout=layout, delta=delta, theta=theta)
+    d = deficit(conditioned, canonical, rotate=rotate, layout=layout, delta=delta, theta=theta,
+                **rope)
     u, s, vt = np.linalg.svd(d, full_matrices=False)
     U = u[:, :m] * s[:m]
     V = vt[:m].T.copy()

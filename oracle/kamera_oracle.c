@@ -66,30 +66,44 @@ void kamera_oracle_phase(int64_t delta, double theta, int32_t rot_dim, double* c
 }
 
 /*
- * One head of one chunk, one layer, one channel.
+ * One head of one chunk, one layer, one channel, with the RoPE variants real backbones use.
  *   src      rows of `width` elements, row t at src + t*src_row_stride (elements, dtype)
- *   rotate   1: apply R(delta) with the given pair layout; 0: identity
+ *   rotate   1: turn the pairs of the first rot_dim features; 0: identity
+ *   rot_dim  features that carry RoPE (even, <= width); the rest pass through unchanged
+ *            (partial rotary, as GPT-NeoX-style models apply it)
+ *   inv_freq rot_dim/2 frequencies, or NULL for the ladder theta^(-2i/rot_dim)
+ *   pair_delta  the shift of each pair (multimodal sections: each pair turns by the shift of
+ *            its position component), or NULL for `delta` on every pair
  *   U        n_tokens x m, row t at U + t*u_row_stride (dtype); V width x m, row f at
  *            V + f*v_row_stride; ignored when m == 0
  *   out, abs_sum   n_tokens x width, dense, fp64
+ * Pair i of the rotated block turns by angle pair_delta[i] * inv_freq[i]:
+ * (x, y) -> (x cos - y sin, y cos + x sin).
  * Returns 0, or -1 on an invalid argument.
  */
-int kamera_oracle_segment(int32_t dtype, const void* src, int64_t src_row_stride,
-                          int32_t n_tokens, int32_t width, int32_t rotate, int32_t layout,
-                          int64_t delta, double theta, int32_t m, const void* U,
-                          int64_t u_row_stride, const void* V, int64_t v_row_stride,
-                          double* out, double* abs_sum) {
+int kamera_oracle_segment_ex(int32_t dtype, const void* src, int64_t src_row_stride,
+                             int32_t n_tokens, int32_t width, int32_t rotate, int32_t layout,
+                             int32_t rot_dim, const double* inv_freq, const int64_t* pair_delta,
+                             int64_t delta, double theta, int32_t m, const void* U,
+                             int64_t u_row_stride, const void* V, int64_t v_row_stride,
+                             double* out, double* abs_sum) {
   if (n_tokens < 0 || width <= 0 || m < 0) return -1;
   if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64) return -1;
-  if (rotate && (width % 2 != 0 || (layout != OR_HALF_SPLIT && layout != OR_INTERLEAVED)))
+  if (rotate && (rot_dim <= 0 || rot_dim % 2 != 0 || rot_dim > width ||
+                 (layout != OR_HALF_SPLIT && layout != OR_INTERLEAVED)))
     return -1;
   if (m > 0 && (U == NULL || V == NULL)) return -1;
 
-  const int32_t half = width / 2;
+  const int32_t half = rot_dim / 2;
   double c[1024], s[1024];
   if (rotate) {
     if (half > 1024) return -1;
-    kamera_oracle_phase(delta, theta, width, c, s);
+    for (int32_t i = 0; i < half; ++i) {
+      const double inv = inv_freq ? inv_freq[i] : pow(theta, -2.0 * (double)i / (double)rot_dim);
+      const double angle = (double)(pair_delta ? pair_delta[i] : delta) * inv;
+      c[i] = cos(angle);
+      s[i] = sin(angle);
+    }
   }
 
 #pragma omp parallel for schedule(static)
@@ -97,7 +111,7 @@ int kamera_oracle_segment(int32_t dtype, const void* src, int64_t src_row_stride
     for (int32_t f = 0; f < width; ++f) {
       const double x = decode(dtype, src, (int64_t)t * src_row_stride + f);
       double value, mag;
-      if (rotate) {
+      if (rotate && f < rot_dim) {
         /* pair index i, the partner feature, and whether f is the pair's first element */
         int32_t i, partner, first;
         if (layout == OR_HALF_SPLIT) {
@@ -131,6 +145,17 @@ int kamera_oracle_segment(int32_t dtype, const void* src, int64_t src_row_stride
     }
   }
   return 0;
+}
+
+/* The plain operator: every feature of the head rotates, the theta ladder, one shift. */
+int kamera_oracle_segment(int32_t dtype, const void* src, int64_t src_row_stride,
+                          int32_t n_tokens, int32_t width, int32_t rotate, int32_t layout,
+                          int64_t delta, double theta, int32_t m, const void* U,
+                          int64_t u_row_stride, const void* V, int64_t v_row_stride,
+                          double* out, double* abs_sum) {
+  return kamera_oracle_segment_ex(dtype, src, src_row_stride, n_tokens, width, rotate, layout,
+                                  width, NULL, NULL, delta, theta, m, U, u_row_stride, V,
+                                  v_row_stride, out, abs_sum);
 }
 
 /* fp64 -> binary32, round to nearest even (the C conversion under the default FP mode). */
