@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KAMERA_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define KAMERA_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 typedef enum kamera_status {
   KAMERA_OK = 0,
@@ -82,12 +82,27 @@ enum { KAMERA_CH_ROT = 0, KAMERA_CH_PLAIN = 1, KAMERA_N_CHANNELS = 2 };
 
 #define KAMERA_MAX_RANK 256
 
+#define KAMERA_MAX_SECTIONS 3
+
 /* Model geometry.
- *   GQA/MHA: n_kv_heads heads per channel, each head_dim wide; rope_dim must equal head_dim
- *            (the whole key rotates). Supported head_dim: 64 or 128 (bf16 MFMA path), any even
- *            value <= 512 on the fp32 path.
+ *   GQA/MHA: n_kv_heads heads per channel, each head_dim wide. The first rope_dim features of
+ *            every key head carry RoPE (even, <= head_dim); the others pass through unchanged
+ *            (partial rotary, as GPT-NeoX-style models apply it; rope_dim == head_dim rotates
+ *            the whole key). bf16 heads take the MFMA path when rope_dim is 64 or 128 and
+ *            head_dim - rope_dim is a multiple of 64; other even shapes up to 512 take the
+ *            VALU path.
  *   MLA:     n_kv_heads must be 1; channel 1 (c_KV) is head_dim wide (kv_lora_rank, e.g. 512),
- *            channel 0 (k_rope) is rope_dim wide (e.g. 64). */
+ *            channel 0 (k_rope) is rope_dim wide (e.g. 64).
+ * Frequencies: pair i turns by its shift times inv_freq[i]; inv_freq == NULL means the plain
+ * ladder theta^(-2i/rope_dim). A table carries model-specific frequencies (llama3, yarn,
+ * linear scaling ...). The table is host memory, rope_dim/2 finite values >= 0, read during
+ * the call only.
+ * Multimodal positions (M-RoPE): n_sections > 0 gives each pair the position component it
+ * encodes, pair_section[i] in [0, n_sections) (host memory, rope_dim/2 entries; contiguous
+ * sections as in Qwen2-VL, interleaved as in Qwen3-VL). Pair i then turns by the chunk's shift
+ * of that component (kamera_chunk.delta for section 0, delta_sections[s-1] for s >= 1). A
+ * chunk moved along the sequence shifts every component alike, which is plain RoPE
+ * relocation; sections matter when the components move by different amounts. */
 typedef struct kamera_model {
   int32_t family;      /* kamera_family */
   int32_t dtype;       /* kamera_dtype */
@@ -96,8 +111,10 @@ typedef struct kamera_model {
   int32_t head_dim;
   int32_t rope_dim;
   int32_t rope_layout; /* kamera_rope_layout */
-  int32_t reserved0;
-  double rope_theta;   /* RoPE base, > 1 and finite */
+  int32_t n_sections;  /* 0: one position per token; 1..KAMERA_MAX_SECTIONS: see above */
+  double rope_theta;   /* RoPE base, > 1 and finite (unused when inv_freq is given) */
+  const double* inv_freq;       /* host: rope_dim/2 frequencies, or NULL */
+  const uint8_t* pair_section;  /* host: rope_dim/2 section indices; NULL iff n_sections == 0 */
 } kamera_model;
 
 /* Paged destination cache, one pool per channel (for MLA both pools may live in one
@@ -149,7 +166,9 @@ typedef struct kamera_patch_ref {
 typedef struct kamera_chunk {
   int32_t n_tokens;          /* >= 0; 0 is a no-op */
   int32_t dst_token_offset;  /* logical cache token of the chunk's token 0, >= 0 */
-  int64_t delta;             /* target position minus canonical position, |delta| < 2^31 */
+  int64_t delta;             /* target position minus canonical position, |delta| < 2^31
+                                (section 0's shift when the model has sections) */
+  int64_t delta_sections[2]; /* shifts of sections 1 and 2 (read only when n_sections > 1) */
   kamera_src src[2];         /* per channel */
   kamera_patch_ref patch[2]; /* per channel */
 } kamera_chunk;
@@ -230,7 +249,8 @@ typedef struct kamera_factors_out {
 typedef struct kamera_compile_chunk {
   int32_t n_tokens;
   int32_t m;
-  int64_t delta;
+  int64_t delta;              /* as in kamera_chunk */
+  int64_t delta_sections[2];  /* as in kamera_chunk */
   kamera_src canonical[2];
   kamera_src conditioned[2];
   kamera_factors_out out[2];

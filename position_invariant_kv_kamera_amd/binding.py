@@ -36,7 +36,8 @@ c_i32, c_i64, c_dbl, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_do
 class KameraModel(ctypes.Structure):
     _fields_ = [("family", c_i32), ("dtype", c_i32), ("n_layers", c_i32), ("n_kv_heads", c_i32),
                 ("head_dim", c_i32), ("rope_dim", c_i32), ("rope_layout", c_i32),
-                ("reserved0", c_i32), ("rope_theta", c_dbl)]
+                ("n_sections", c_i32), ("rope_theta", c_dbl), ("inv_freq", c_vp),
+                ("pair_section", c_vp)]
 
 
 class KameraCache(ctypes.Structure):
@@ -57,7 +58,8 @@ class KameraPatchRef(ctypes.Structure):
 
 class KameraChunk(ctypes.Structure):
     _fields_ = [("n_tokens", c_i32), ("dst_token_offset", c_i32), ("delta", c_i64),
-                ("src", KameraSrc * 2), ("patch", KameraPatchRef * 2)]
+                ("delta_sections", c_i64 * 2), ("src", KameraSrc * 2),
+                ("patch", KameraPatchRef * 2)]
 
 
 class KameraFactorsOut(ctypes.Structure):
@@ -67,6 +69,7 @@ class KameraFactorsOut(ctypes.Structure):
 
 class KameraCompileChunk(ctypes.Structure):
     _fields_ = [("n_tokens", c_i32), ("m", c_i32), ("delta", c_i64),
+                ("delta_sections", c_i64 * 2),
                 ("canonical", KameraSrc * 2), ("conditioned", KameraSrc * 2),
                 ("out", KameraFactorsOut * 2)]
 
@@ -198,10 +201,31 @@ def kamera_patch_compile(model, chunks, n_chunks, n_iter, workspace, workspace_b
 
 # ---- marshalling of torch tensors (workloads.Batch) into descriptors --------------------
 
+def make_model(family, dtype, n_layers, n_kv_heads, head_dim, rope_dim, rope_layout, theta, *,
+               inv_freq=None, pair_section=None) -> KameraModel:
+    """A KameraModel; the optional host tables are copied and kept alive by the struct."""
+    import numpy as np
+    m = KameraModel(FAMILY.get(family, family), DTYPE.get(dtype, dtype), n_layers, n_kv_heads,
+                    head_dim, rope_dim, LAYOUT.get(rope_layout, rope_layout), 0, float(theta),
+                    None, None)
+    if inv_freq is not None:
+        m._inv_freq = np.ascontiguousarray(inv_freq, np.float64)
+        m.inv_freq = m._inv_freq.ctypes.data
+    if pair_section is not None:
+        m._pair_section = np.ascontiguousarray(pair_section, np.uint8)
+        m.pair_section = m._pair_section.ctypes.data
+        m.n_sections = int(m._pair_section.max()) + 1 if m._pair_section.size else 0
+    return m
+
+
 def model_of(plan) -> KameraModel:
-    return KameraModel(FAMILY[plan.family], DTYPE[plan.dtype], plan.n_layers, plan.n_kv_heads,
-                       plan.head_dim, plan.rope_dim, LAYOUT[plan.rope_layout], 0,
-                       float(plan.theta))
+    m = make_model(plan.family, plan.dtype, plan.n_layers, plan.n_kv_heads, plan.head_dim,
+                   plan.rope_dim, plan.rope_layout, plan.theta,
+                   inv_freq=getattr(plan, "inv_freq", None),
+                   pair_section=getattr(plan, "pair_section", None))
+    if getattr(plan, "n_sections", None):
+        m.n_sections = int(plan.n_sections)
+    return m
 
 
 def cache_of(batch) -> KameraCache:
@@ -228,6 +252,9 @@ def chunks_of(batch, m_override: int | None = None):
         k.n_tokens = p.chunk_tokens[c]
         k.dst_token_offset = p.dst_offsets[c]
         k.delta = p.deltas[c]
+        ds = getattr(p, "delta_sections", None)
+        if ds is not None:
+            k.delta_sections[0], k.delta_sections[1] = int(ds[c][0]), int(ds[c][1])
         for ch in range(2):
             s = ct.src[ch]
             k.src[ch] = KameraSrc(s.data_ptr(), s.stride(0), s.stride(1))
@@ -282,8 +309,9 @@ class CompileItem:
     [layers, tokens, heads*width] views (unit inner stride); U[c] is [layers, heads, tokens, m]
     and V[c] [layers, heads, width, m], written by the call."""
 
-    def __init__(self, n_tokens, m, delta, canonical, conditioned, U, V):
+    def __init__(self, n_tokens, m, delta, canonical, conditioned, U, V, delta_sections=(0, 0)):
         self.n_tokens, self.m, self.delta = int(n_tokens), int(m), int(delta)
+        self.delta_sections = tuple(int(d) for d in delta_sections)
         self.canonical, self.conditioned, self.U, self.V = canonical, conditioned, U, V
 
 
@@ -292,6 +320,7 @@ def compile_chunks_of(items):
     for i, it in enumerate(items):
         k = arr[i]
         k.n_tokens, k.m, k.delta = it.n_tokens, it.m, it.delta
+        k.delta_sections[0], k.delta_sections[1] = it.delta_sections
         for ch in range(2):
             a, b = it.canonical[ch], it.conditioned[ch]
             k.canonical[ch] = KameraSrc(a.data_ptr(), a.stride(0), a.stride(1))

@@ -37,7 +37,10 @@ kamera_status fail(kamera_status st, const char* fmt, ...) {
 void clear_error() { g_last_error.clear(); }
 const char* last_error() { return g_last_error.c_str(); }
 
-constexpr size_t kHeaderBytes = 256;
+using kamera::kHeaderBytes;
+using kamera::kFreqOffset;
+using kamera::kSectionOffset;
+using kamera::kTablesEnd;
 constexpr int64_t kTargetBlocks = 70000;   // grid size the tiles-per-wave choice aims under
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -81,13 +84,30 @@ kamera_status validate_model(const kamera_model* m) {
                 2 * kamera::kMaxPairs);
   if (m->family == KAMERA_FAMILY_GQA) {
     if (m->n_kv_heads <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_kv_heads must be > 0");
-    if (m->rope_dim != m->head_dim)
-      return fail(KAMERA_ERR_UNSUPPORTED,
-                  "GQA/MHA rotate the whole head: rope_dim (%d) must equal head_dim (%d)",
+    if (m->rope_dim > m->head_dim)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_dim (%d) exceeds head_dim (%d)",
                   m->rope_dim, m->head_dim);
   } else if (m->n_kv_heads != 1) {
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "MLA needs n_kv_heads == 1 (got %d)",
                 m->n_kv_heads);
+  }
+  const int pairs = m->rope_dim / 2;
+  if (m->inv_freq) {
+    for (int i = 0; i < pairs; ++i)
+      if (!std::isfinite(m->inv_freq[i]) || m->inv_freq[i] < 0.0)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "inv_freq[%d] must be finite and >= 0", i);
+  }
+  if (m->n_sections < 0 || m->n_sections > KAMERA_MAX_SECTIONS)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_sections must be in [0, %d] (got %d)",
+                KAMERA_MAX_SECTIONS, m->n_sections);
+  if ((m->n_sections > 0) != (m->pair_section != nullptr))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                "pair_section must be given exactly when n_sections > 0");
+  if (m->pair_section) {
+    for (int i = 0; i < pairs; ++i)
+      if (m->pair_section[i] >= m->n_sections)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "pair_section[%d] = %d is not below n_sections",
+                    i, (int)m->pair_section[i]);
   }
   return KAMERA_OK;
 }
@@ -164,8 +184,14 @@ kamera_status validate_chunks(const kamera_model& m, const kamera_cache& c,
                   "chunk %d: tokens [%d, %lld) run past the cache's %lld logical tokens", i,
                   k.dst_token_offset, (long long)k.dst_token_offset + k.n_tokens,
                   (long long)capacity);
-    if (op != Op::Patch && (k.delta >= (int64_t(1) << 31) || k.delta <= -(int64_t(1) << 31)))
-      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
+    if (op != Op::Patch) {
+      auto big = [](int64_t d) { return d >= (int64_t(1) << 31) || d <= -(int64_t(1) << 31); };
+      if (big(k.delta)) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
+      for (int sct = 1; sct < m.n_sections; ++sct)
+        if (big(k.delta_sections[sct - 1]))
+          return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                      "chunk %d: |delta_sections[%d]| must be < 2^31", i, sct - 1);
+    }
     spans.emplace_back(k.dst_token_offset, (int64_t)k.dst_token_offset + k.n_tokens);
     for (int ch = 0; ch < 2; ++ch) {
       const Channel g = channel_of(m, ch);
@@ -304,7 +330,7 @@ int kmode_for(int max_m) {
 
 // Can this job use the MFMA path? Sets the window width.
 bool mfma_eligible(const kamera_model& m, const kamera_cache& c, const kamera_chunk& k,
-                   const Channel& g, Op op, int ch, int* win_width) {
+                   const Channel& g, Op op, int ch, int f_base, int* win_width) {
   if (m.dtype != KAMERA_DTYPE_BF16) return false;
   if (env_int("KAMERA_FORCE_VALU", 0)) return false;
   int w;
@@ -318,11 +344,17 @@ bool mfma_eligible(const kamera_model& m, const kamera_cache& c, const kamera_ch
   } else {
     return false;
   }
-  // 16-byte loads and stores of token rows
-  if (!aligned16(c.pool[ch]) || c.layer_stride % 8 || c.token_stride % 8) return false;
+  // 16-byte loads and stores of token rows (of the job's sub-head, and of every head)
+  const int64_t off = (int64_t)f_base * 2;
+  if (f_base % 8 || channel_of(m, ch).width % 8) return false;
+  if (!aligned16(static_cast<const uint8_t*>(c.pool[ch]) + off) || c.layer_stride % 8 ||
+      c.token_stride % 8)
+    return false;
   if (op != Op::Patch) {
     const kamera_src& s = k.src[ch];
-    if (!aligned16(s.ptr) || s.layer_stride % 8 || s.token_stride % 8) return false;
+    if (!aligned16(static_cast<const uint8_t*>(s.ptr) + off) || s.layer_stride % 8 ||
+        s.token_stride % 8)
+      return false;
   }
   *win_width = w;
   return true;
@@ -330,6 +362,7 @@ bool mfma_eligible(const kamera_model& m, const kamera_cache& c, const kamera_ch
 
 kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kamera_chunk* chunks,
                          int32_t n_chunks, Op op, Plan* plan) {
+  const int64_t es = m.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
   for (int32_t i = 0; i < n_chunks; ++i) {
     const kamera_chunk& k = chunks[i];
     if (k.n_tokens == 0) continue;
@@ -338,48 +371,62 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
       const kamera_patch_ref& p = k.patch[ch];
       const int mm = op == Op::Relocate ? 0 : p.m;
       if (op == Op::Patch && mm == 0) continue;
-      JobDesc j;
-      std::memset(&j, 0, sizeof j);
-      j.src = op == Op::Patch ? nullptr : k.src[ch].ptr;
-      j.src_ls = op == Op::Patch ? 0 : k.src[ch].layer_stride;
-      j.src_ts = op == Op::Patch ? 0 : k.src[ch].token_stride;
-      j.pool = c.pool[ch];
-      j.m = mm;
-      if (mm > 0) {
-        j.U = p.U;
-        j.V = p.V;
-        j.u_ls = p.u_layer_stride;
-        j.u_hs = p.u_head_stride;
-        j.v_ls = p.v_layer_stride;
-        j.v_hs = p.v_head_stride;
-      }
-      j.delta = k.delta;
-      j.n_tokens = k.n_tokens;
-      j.dst_offset = k.dst_token_offset;
-      j.rotate = (g.rotate && op != Op::Patch) ? 1 : 0;
-      j.head_width = g.width;
-      j.rot_dim = m.family == KAMERA_FAMILY_MLA ? m.rope_dim : m.head_dim;
-      int w = 0;
-      if (mfma_eligible(m, c, k, g, op, ch, &w)) {
-        j.win_width = w;
-        j.wph = g.width / w;
-        j.n_windows = g.heads * j.wph;
-        j.n_wgroups = (j.n_windows + 3) / 4;
-        j.n_tiles = (k.n_tokens + kamera::kTileTokens - 1) / kamera::kTileTokens;
-        // n_tgroups is set below, once the whole batch's size is known
-        j.vec_uv = mm > 0 && mm % 8 == 0 && aligned16(p.U) && aligned16(p.V) &&
-                   p.u_layer_stride % 8 == 0 && p.u_head_stride % 8 == 0 &&
-                   p.v_layer_stride % 8 == 0 && p.v_head_stride % 8 == 0;
-        plan->mfma.push_back(j);
-        plan->mfma_max_m = std::max(plan->mfma_max_m, mm);
-      } else {
-        j.win_width = g.width;
-        j.wph = 1;
-        j.n_windows = g.heads;
-        j.n_wgroups = (g.heads + 3) / 4;
-        j.n_tiles = k.n_tokens;
-        j.n_tgroups = (k.n_tokens + kamera::kValuTokensPerBlock - 1) / kamera::kValuTokensPerBlock;
-        plan->valu.push_back(j);
+      // A partially rotary key head is two jobs: features [0, rope_dim) turn, the rest pass
+      // through. Each job sees its sub-head through offset pointers and the head stride.
+      const bool partial = g.rotate && m.family == KAMERA_FAMILY_GQA && m.rope_dim < g.width;
+      const int n_parts = partial ? 2 : 1;
+      for (int part = 0; part < n_parts; ++part) {
+        const int f_base = part == 0 ? 0 : m.rope_dim;
+        const int width = partial ? (part == 0 ? m.rope_dim : g.width - m.rope_dim) : g.width;
+        const bool rot = g.rotate && part == 0;
+        JobDesc j;
+        std::memset(&j, 0, sizeof j);
+        j.src = op == Op::Patch ? nullptr
+                                : static_cast<const uint8_t*>(k.src[ch].ptr) + f_base * es;
+        j.src_ls = op == Op::Patch ? 0 : k.src[ch].layer_stride;
+        j.src_ts = op == Op::Patch ? 0 : k.src[ch].token_stride;
+        j.pool = static_cast<uint8_t*>(c.pool[ch]) + f_base * es;
+        j.m = mm;
+        if (mm > 0) {
+          j.U = p.U;
+          j.V = static_cast<const uint8_t*>(p.V) + (int64_t)f_base * mm * es;
+          j.u_ls = p.u_layer_stride;
+          j.u_hs = p.u_head_stride;
+          j.v_ls = p.v_layer_stride;
+          j.v_hs = p.v_head_stride;
+        }
+        j.delta = k.delta;
+        j.delta_s1 = m.n_sections > 1 ? k.delta_sections[0] : k.delta;
+        j.delta_s2 = m.n_sections > 2 ? k.delta_sections[1] : k.delta;
+        j.n_tokens = k.n_tokens;
+        j.dst_offset = k.dst_token_offset;
+        j.rotate = (rot && op != Op::Patch) ? 1 : 0;
+        j.head_width = width;
+        j.head_stride = g.width;
+        j.rot_dim = m.rope_dim;
+        const Channel sub{g.heads, width, rot};
+        int w = 0;
+        if (mfma_eligible(m, c, k, sub, op, ch, f_base, &w)) {
+          j.win_width = w;
+          j.wph = width / w;
+          j.n_windows = g.heads * j.wph;
+          j.n_wgroups = (j.n_windows + 3) / 4;
+          j.n_tiles = (k.n_tokens + kamera::kTileTokens - 1) / kamera::kTileTokens;
+          // n_tgroups is set below, once the whole batch's size is known
+          j.vec_uv = mm > 0 && mm % 8 == 0 && aligned16(j.U) && aligned16(j.V) &&
+                     p.u_layer_stride % 8 == 0 && p.u_head_stride % 8 == 0 &&
+                     p.v_layer_stride % 8 == 0 && p.v_head_stride % 8 == 0;
+          plan->mfma.push_back(j);
+          plan->mfma_max_m = std::max(plan->mfma_max_m, mm);
+        } else {
+          j.win_width = width;
+          j.wph = 1;
+          j.n_windows = g.heads;
+          j.n_wgroups = (g.heads + 3) / 4;
+          j.n_tiles = k.n_tokens;
+          j.n_tgroups = (k.n_tokens + kamera::kValuTokensPerBlock - 1) / kamera::kValuTokensPerBlock;
+          plan->valu.push_back(j);
+        }
       }
     }
   }
@@ -448,8 +495,9 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   st = build_plan(*model, *cache, chunks, n_chunks, op, &plan);
   if (st != KAMERA_OK) return st;
 
-  // workspace: [header | MFMA jobs | VALU jobs | MFMA block starts | VALU block starts]
-  const size_t mfma_off = kHeaderBytes;
+  // workspace: [header | inv_freq | pair sections | MFMA jobs | VALU jobs | MFMA block starts |
+  //             VALU block starts]
+  const size_t mfma_off = kTablesEnd;
   const size_t valu_off = mfma_off + plan.mfma.size() * sizeof(JobDesc);
   const size_t mfma_bs_off = valu_off + plan.valu.size() * sizeof(JobDesc);
   const size_t valu_bs_off = mfma_bs_off + plan.mfma.size() * sizeof(int32_t);
@@ -464,6 +512,11 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   };
   put(mfma_off, plan.mfma, mfma_bs_off);
   put(valu_off, plan.valu, valu_bs_off);
+  const int pairs = model->rope_dim / 2;
+  if (model->inv_freq)
+    std::memcpy(staging.data() + kFreqOffset, model->inv_freq, pairs * sizeof(double));
+  if (model->pair_section)
+    std::memcpy(staging.data() + kSectionOffset, model->pair_section, pairs);
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   st = upload(staging, workspace, stream);
@@ -482,6 +535,11 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   lp.pool_ls = cache->layer_stride;
   lp.pool_ts = cache->token_stride;
   lp.theta = model->rope_theta;
+  lp.inv_freq = model->inv_freq
+                    ? reinterpret_cast<const double*>(static_cast<uint8_t*>(workspace) + kFreqOffset)
+                    : nullptr;
+  lp.pair_section = model->pair_section ? static_cast<uint8_t*>(workspace) + kSectionOffset
+                                        : nullptr;
   lp.fault_counter = static_cast<uint32_t*>(workspace);
   lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
   lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 0);
@@ -523,7 +581,8 @@ extern "C" {
 
 size_t kamera_workspace_bytes(int32_t n_chunks) {
   if (n_chunks < 0) return 0;
-  return round_up(kHeaderBytes + (size_t)n_chunks * 2 * (sizeof(JobDesc) + sizeof(int32_t)), 256);
+  // up to three jobs per chunk: channel 0 (two when a key head is partially rotary), channel 1
+  return round_up(kTablesEnd + (size_t)n_chunks * 3 * (sizeof(JobDesc) + sizeof(int32_t)), 256);
 }
 
 kamera_status kamera_reuse_batch(const kamera_model* model, const kamera_cache* cache,

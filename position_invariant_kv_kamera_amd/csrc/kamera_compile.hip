@@ -50,11 +50,15 @@ struct alignas(16) CJob {
   void* V;
   int64_t canon_ls, canon_ts, cond_ls, cond_ts;
   int64_t u_ls, u_hs, v_ls, v_hs;
-  int64_t delta;
+  int64_t delta;    // shift of section 0 (of every pair without sections)
+  int64_t delta_s1; // shifts of sections 1 and 2
+  int64_t delta_s2;
   int64_t gpart;   // float offset of the partial Gram tiles [unit][pair][split][te][te]
   int64_t gfull;   // float offset of the assembled G [unit][width][width], or -1 (partial is G)
   int64_t xbase;   // float offset of the fp32 bases [unit][width][mp]
   int32_t n_tokens, m, mp, width, heads, rotate, te, nb, n_pairs, splits, split_tokens, n_units;
+  int32_t rot_dim;  // features of each head that turn (the rest pass through); pairs rot_dim/2
+  int32_t pad0;
 };
 
 struct CParams {
@@ -62,6 +66,8 @@ struct CParams {
   const int32_t* starts;   // first block of each entry, ascending
   const int32_t* job_of;   // job index of each entry
   float* ws;               // float view of the workspace's data region
+  const double* inv_freq;  // device: frequency table, or NULL (theta ladder)
+  const uint8_t* pair_section;  // device: section of each pair, or NULL
   double theta;
   int32_t n_entries;
   int32_t layout;
@@ -89,10 +95,16 @@ __device__ __forceinline__ int find_entry(const CParams& P, int b) {
   return lo;
 }
 
-// cos/sin(delta * theta^(-2i/rot_dim)) per pair: angle and reduction in fp64, one rounding.
-__device__ void fill_phases(float2* cs, int64_t delta, double theta, int rot_dim) {
+// cos/sin(shift * frequency) per pair: angle and reduction in fp64, one rounding. The
+// frequency is the table entry when the model gives one, else theta^(-2i/rot_dim); the shift
+// is that of the pair's position component (multimodal sections), else the chunk's.
+__device__ void fill_phases(float2* cs, const CJob& J, const CParams& P) {
+  const int rot_dim = J.rot_dim;
   for (int i = threadIdx.x; i < rot_dim / 2; i += kThreads) {
-    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    const double inv = P.inv_freq ? P.inv_freq[i]
+                                  : pow(P.theta, -2.0 * (double)i / (double)rot_dim);
+    const int sec = P.pair_section ? (int)P.pair_section[i] : 0;
+    const int64_t delta = sec == 0 ? J.delta : (sec == 1 ? J.delta_s1 : J.delta_s2);
     double s, c;
     sincos((double)delta * inv, &s, &c);
     cs[i] = make_float2((float)c, (float)s);
@@ -122,7 +134,8 @@ __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
 // Rows [tok0, tok0 + ROWS) of Delta, columns [col0, col0 + ncols), into dst (fp32, row stride
 // ds); rows at or past tok_end are zero. A rotated head is always staged whole (col0 = 0,
-// ncols = width) so that both members of every pair are at hand.
+// ncols = width) so that both members of every pair are at hand; its pairs lie in the first
+// rot_dim features, the others pass through.
 template <typename T, int ROWS>
 __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int layer, int head,
                             int tok0, int tok_end, int col0, int ncols, float* dst, int ds) {
@@ -130,13 +143,30 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
   const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + (int64_t)head * W;
   const T* cond = static_cast<const T*>(J.cond) + layer * J.cond_ls + (int64_t)head * W;
   if (J.rotate) {
-    const int gpr = W / 16;   // groups of 8 pairs per row
+    // groups of 8 pairs over the turning features [0, R), then groups of 8 features passing
+    // through over [R, W)
+    const int R = J.rot_dim;
+    const int gr = R / 16, gpr = gr + (W - R) / 8;
     for (int g = threadIdx.x; g < ROWS * gpr; g += kThreads) {
       const int r = g / gpr, q = g - r * gpr;
       const int tok = tok0 + r;
       float* d = dst + r * ds;
+      if (q >= gr) {
+        const int f = R + 8 * (q - gr);
+        if (tok >= tok_end) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) d[f + k] = 0.f;
+          continue;
+        }
+        float x[8], c[8];
+        load8(canon + tok * J.canon_ts + f, x);
+        load8(cond + tok * J.cond_ts + f, c);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[f + k] = c[k] - x[k];
+        continue;
+      }
       const int fa = layout == KAMERA_ROPE_HALF_SPLIT ? 8 * q : 16 * q;
-      const int fb = layout == KAMERA_ROPE_HALF_SPLIT ? W / 2 + 8 * q : 16 * q + 8;
+      const int fb = layout == KAMERA_ROPE_HALF_SPLIT ? R / 2 + 8 * q : 16 * q + 8;
       if (tok >= tok_end) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) d[fa + k] = d[fb + k] = 0.f;
@@ -235,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
   const int layer = unit / J.heads, head = unit - layer * J.heads;
   int bi, bj;
   pair_tiles(pair, J.nb, &bi, &bj);
-  if (J.rotate) fill_phases(cs, J.delta, P.theta, J.width);
+  if (J.rotate) fill_phases(cs, J, P);
 
   const int t_lo = split * J.split_tokens;
   const int t_hi = min(J.n_tokens, t_lo + J.split_tokens);
@@ -720,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
   const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
   const int DS = D + 4;
   const int SV = mp == 16 ? 16 : (DMAX <= 128 ? 80 : mp);
-  if (J.rotate) fill_phases(cs, J.delta, P.theta, D);
+  if (J.rotate) fill_phases(cs, J, P);
   const float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
   for (int idx = tid; idx < D * mp; idx += kThreads) {
     const int f = idx / mp, r = idx - f * mp;
@@ -785,6 +815,8 @@ struct Launch {
 struct CPlan {
   std::vector<CJob> jobs;
   std::vector<Launch> launches;
+  size_t freq_off = 0;   // frequency table (kMaxPairs doubles) and pair sections (kMaxPairs bytes)
+  size_t sec_off = 0;
   size_t table_bytes = 0;
   size_t data_off = 0;
   size_t total_bytes = 0;
@@ -834,10 +866,19 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
     if (k.m > KAMERA_COMPILE_MAX_RANK)
       return fail(KAMERA_ERR_UNSUPPORTED, "chunk %d: m = %d exceeds %d", i, k.m,
                   KAMERA_COMPILE_MAX_RANK);
-    if (k.delta >= (int64_t(1) << 31) || k.delta <= -(int64_t(1) << 31))
+    auto big = [](int64_t d) { return d >= (int64_t(1) << 31) || d <= -(int64_t(1) << 31); };
+    if (big(k.delta))
       return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
+    for (int sct = 1; sct < M.n_sections; ++sct)
+      if (big(k.delta_sections[sct - 1]))
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta_sections[%d]| must be < 2^31",
+                    i, sct - 1);
     for (int ch = 0; ch < 2; ++ch) {
       const Channel g = channel_of(M, ch);
+      if (g.rotate && M.rope_dim < g.width && (M.rope_dim % 16 || (g.width - M.rope_dim) % 8))
+        return fail(KAMERA_ERR_UNSUPPORTED,
+                    "chunk %d channel %d: partial rotary needs rope_dim a multiple of 16 and "
+                    "the pass-through width a multiple of 8", i, ch);
       if (!width_supported(g))
         return fail(KAMERA_ERR_UNSUPPORTED,
                     "chunk %d channel %d: width %d not supported by the compile (rotated: a "
@@ -863,6 +904,9 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
       J.v_ls = k.out[ch].v_layer_stride;
       J.v_hs = k.out[ch].v_head_stride;
       J.delta = k.delta;
+      J.delta_s1 = M.n_sections > 1 ? k.delta_sections[0] : k.delta;
+      J.delta_s2 = M.n_sections > 2 ? k.delta_sections[1] : k.delta;
+      J.rot_dim = g.rotate ? M.rope_dim : 0;
       J.n_tokens = k.n_tokens;
       J.m = k.m;
       J.mp = (k.m + 15) / 16 * 16;
@@ -924,6 +968,10 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
     if (!ok) return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
   }
   size_t off = round_up(plan->jobs.size() * sizeof(CJob), 16);
+  plan->freq_off = off;
+  off += kamera::kMaxPairs * sizeof(double);
+  plan->sec_off = off;
+  off = round_up(off + kamera::kMaxPairs, 16);
   for (auto& l : plan->launches) {
     l.off = off;
     off += 2 * l.starts.size() * sizeof(int32_t);
@@ -1088,6 +1136,11 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
 
   std::vector<uint8_t> table(plan.table_bytes, 0);
   std::memcpy(table.data(), plan.jobs.data(), plan.jobs.size() * sizeof(CJob));
+  const int pairs = model->rope_dim / 2;
+  if (model->inv_freq)
+    std::memcpy(table.data() + plan.freq_off, model->inv_freq, pairs * sizeof(double));
+  if (model->pair_section)
+    std::memcpy(table.data() + plan.sec_off, model->pair_section, pairs);
   for (const Launch& l : plan.launches) {
     std::memcpy(table.data() + l.off, l.starts.data(), l.starts.size() * sizeof(int32_t));
     std::memcpy(table.data() + l.off + l.starts.size() * sizeof(int32_t), l.job_of.data(),
@@ -1102,6 +1155,8 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
   P.jobs = reinterpret_cast<const CJob*>(base);
   P.ws = reinterpret_cast<float*>(base + plan.data_off);
   P.theta = model->rope_theta;
+  P.inv_freq = model->inv_freq ? reinterpret_cast<const double*>(base + plan.freq_off) : nullptr;
+  P.pair_section = model->pair_section ? base + plan.sec_off : nullptr;
   P.layout = model->rope_layout;
   P.n_iter = n_iter;
   // kernels in dependency order: every Gram tile, then every subspace, then every projection

@@ -18,12 +18,15 @@ struct alignas(16) JobDesc {
   int64_t src_ts;    // src token stride
   int64_t u_ls, u_hs;
   int64_t v_ls, v_hs;
-  int64_t delta;
+  int64_t delta;       // shift of section 0 (of every pair when the model has no sections)
+  int64_t delta_s1;    // shifts of sections 1 and 2
+  int64_t delta_s2;
   int32_t n_tokens;
   int32_t dst_offset;
   int32_t m;
-  int32_t rotate;      // 1: R(delta) on this channel
-  int32_t head_width;  // features per head of this channel
+  int32_t rotate;      // 1: R(delta) on this job's features
+  int32_t head_width;  // features per head this job covers (src, pool, V already offset to them)
+  int32_t head_stride; // features between consecutive heads of the channel's rows
   int32_t win_width;   // features one wave handles at a time (a window of a head)
   int32_t wph;         // windows per head
   int32_t n_windows;   // heads * wph
@@ -33,6 +36,7 @@ struct alignas(16) JobDesc {
   int32_t block_start; // first block of this job in the launch
   int32_t vec_uv;      // U and V rows may be read with 16-byte loads
   int32_t rot_dim;     // length of the frequency ladder (2 x pairs)
+  int32_t pad0;
 };
 
 enum Mode : int32_t { MODE_REUSE = 0, MODE_PATCH = 1 };
@@ -52,6 +56,8 @@ struct LaunchParams {
   int64_t pool_ls;          // pool layer stride (elements)
   int64_t pool_ts;          // pool token stride
   double theta;
+  const double* inv_freq;       // device (workspace): rot_dim/2 frequencies, or NULL (ladder)
+  const uint8_t* pair_section;  // device (workspace): section of each pair, or NULL
   uint32_t* fault_counter;  // device (workspace header)
   int32_t mode;             // Mode
   int32_t n_layers;
@@ -64,6 +70,12 @@ constexpr int kBlockThreads = 256;      // 4 waves of 64
 constexpr int kTileTokens = 16;         // MFMA N dimension
 constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
 constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
+// Workspace front: [header (fault counter) | inv_freq table (kMaxPairs doubles) |
+// pair sections (kMaxPairs bytes) | job tables ...]
+constexpr size_t kHeaderBytes = 256;
+constexpr size_t kFreqOffset = kHeaderBytes;
+constexpr size_t kSectionOffset = kFreqOffset + kMaxPairs * sizeof(double);
+constexpr size_t kTablesEnd = kSectionOffset + kMaxPairs;
 
 // Build-time knobs; the defaults are the measured best on MI355X.
 //   KAMERA_PREFETCH_TILES(_RANK64): tiles a wave keeps loaded ahead of the one it computes

@@ -123,9 +123,15 @@ __device__ __forceinline__ int find_job(const int32_t* block_starts, int n_jobs,
 
 // cos/sin(delta * theta^(-2i/rot_dim)) for every pair i: angle and range reduction in fp64,
 // one rounding to fp32 each.
-__device__ __forceinline__ void fill_phases(float2* cs, int64_t delta, double theta, int rot_dim) {
+// The frequency is the model's table entry when one is given, else theta^(-2i/rot_dim); the
+// shift is that of the pair's position component (multimodal sections), else the chunk's.
+__device__ __forceinline__ void fill_phases(float2* cs, const JobDesc& J, const LaunchParams& P) {
+  const int rot_dim = J.rot_dim;
   for (int i = threadIdx.x; i < rot_dim / 2; i += kBlockThreads) {
-    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    const double inv = P.inv_freq ? gp(P.inv_freq)[i]
+                                  : pow(P.theta, -2.0 * (double)i / (double)rot_dim);
+    const int sec = P.pair_section ? (int)gp(P.pair_section)[i] : 0;
+    const int64_t delta = sec == 0 ? J.delta : (sec == 1 ? J.delta_s1 : J.delta_s2);
     double s, c;
     sincos((double)delta * inv, &s, &c);
     cs[i] = make_float2((float)c, (float)s);
@@ -468,7 +474,7 @@ __device__ __forceinline__ void run_window(const LaunchParams& P, const WindowCt
     if constexpr (KM != 0) load_vfrags<W, KM>(C, g, n, vf);
   }
   if (C.rotate) {
-    fill_phases(cs, J.delta, P.theta, J.rot_dim);
+    fill_phases(cs, J, P);
     __syncthreads();
   }
   if (!active) return;
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(kBlockThreads) KAMERA_OCCUPANCY(KM) void kamera_mfm
 
   const int head = win / J.wph;
   const int f0 = (win % J.wph) * J.win_width;
-  const int64_t feat = (int64_t)head * J.head_width + f0;
+  const int64_t feat = (int64_t)head * J.head_stride + f0;
 
   WindowCtx C;
   C.rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
 
   const int rotate = P.mode == MODE_PATCH ? 0 : J.rotate;
   if (rotate) {
-    fill_phases(cs, J.delta, P.theta, J.rot_dim);
+    fill_phases(cs, J, P);
     __syncthreads();
   }
   const bool interleaved = P.layout != 0;
@@ -629,10 +635,10 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
       if (q == 0) count_fault(P);
       continue;
     }
-    KGLOBAL T* out = pool + drow + (int64_t)head * D;
+    KGLOBAL T* out = pool + drow + (int64_t)head * J.head_stride;
     const KGLOBAL T* in = P.mode == MODE_PATCH ? out
                                        : src + layer * J.src_ls + (int64_t)t * J.src_ts +
-                                             (int64_t)head * D;
+                                             (int64_t)head * J.head_stride;
     if (!rotate && m == 0) {   // bit copy
       out[fa] = in[fa];
       out[fb] = in[fb];

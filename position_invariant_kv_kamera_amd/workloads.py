@@ -57,6 +57,12 @@ class Plan:
     kv_channel_scale: bool = False
     patch_sigma: float = 0.05
     notes: dict = field(default_factory=dict)
+    # RoPE variants: an explicit frequency table (rope_dim/2 entries), multimodal sections
+    # (section index per pair) with per-chunk shifts of sections 1 and 2
+    inv_freq: np.ndarray | None = None
+    pair_section: np.ndarray | None = None
+    n_sections: int = 0
+    delta_sections: list | None = None    # per chunk (shift of section 1, of section 2)
 
     @property
     def n_chunks(self) -> int:
@@ -197,12 +203,64 @@ def qwen3vl_window_bf16(seed=0, n_layers=36, n_slots=256, chunk_len=256, n_recal
     return dataclasses.replace(p, **kw)
 
 
+def qwen25vl_mrope_bf16(seed=0, n_layers=28, chunk_tokens=(1296,) * 32, interleaved_map=False,
+                        **kw) -> Plan:
+    """The Qwen2.5-VL-like batch with multimodal 3-D positions: pairs 0-15 encode time, 16-39
+    height, 40-63 width (contiguous sections; or every third pair per component with
+    interleaved_map, the map Qwen3-VL uses), and each chunk moves its three components by
+    different seeded amounts."""
+    p = qwen25vl_gqa_bf16(seed=seed, n_layers=n_layers, chunk_tokens=chunk_tokens)
+    rng = np.random.Generator(np.random.PCG64(seed + 101))
+    n = len(p.chunk_tokens)
+    if interleaved_map:
+        sec = np.array([i % 3 for i in range(64)], np.uint8)
+    else:
+        sec = np.repeat(np.array([0, 1, 2], np.uint8), [16, 24, 24])
+    ds = [(int(a), int(b)) for a, b in rng.integers(-4096, 4096, size=(n, 2), endpoint=True)]
+    name = "qwen3vl_mrope_bf16" if interleaved_map else "qwen25vl_mrope_bf16"
+    return dataclasses.replace(p, name=name, pair_section=sec, n_sections=3, delta_sections=ds,
+                               **kw)
+
+
+def neox_partial_bf16(seed=0, n_layers=4, chunk_tokens=(512,) * 8, rope_dim=64,
+                      rope_layout=HALF_SPLIT, **kw) -> Plan:
+    """Partial rotary: 8 KV heads x 128 of which the first rope_dim features carry RoPE
+    (GPT-NeoX style), theta 1e4, rank-16 patches, dense cache."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    chunk_tokens = list(chunk_tokens)
+    n = len(chunk_tokens)
+    deltas = [int(d) for d in rng.integers(0, 65536, size=n)]
+    offs, n_logical = _dense_layout(chunk_tokens, 16)
+    p = Plan("neox_partial_bf16", GQA, "bf16", n_layers, 8, 128, rope_dim, rope_layout, 1e4,
+             chunk_tokens, deltas, offs, [16] * n, [16] * n, 16, n_logical, None, n_logical, seed)
+    return dataclasses.replace(p, **kw)
+
+
+def scaled_table_bf16(seed=0, n_layers=4, chunk_tokens=(1024,) * 8, dtype="bf16", **kw) -> Plan:
+    """An explicit per-pair frequency table (a seeded, decreasing table spanning [1e-6, 1],
+    standing in for a model's scaled frequencies), 4 KV heads x 128, rank-16 patches,
+    shifts up to 2^20."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    chunk_tokens = list(chunk_tokens)
+    n = len(chunk_tokens)
+    deltas = [int(d) for d in rng.integers(-(1 << 20), 1 << 20, size=n)]
+    offs, n_logical = _dense_layout(chunk_tokens, 16)
+    table = np.sort(10.0 ** rng.uniform(-6.0, 0.0, size=64))[::-1].copy()
+    p = Plan("scaled_table_" + dtype, GQA, dtype, n_layers, 4, 128, 128, HALF_SPLIT, 5e5,
+             chunk_tokens, deltas, offs, [16] * n, [16] * n, 16, n_logical, None, n_logical, seed,
+             inv_freq=table)
+    return dataclasses.replace(p, **kw)
+
+
 PLANS = {
     "tiny_gqa_f32": tiny_gqa_f32,
     "qwen25vl_gqa_bf16": qwen25vl_gqa_bf16,
     "dsv2lite_mla_bf16": dsv2lite_mla_bf16,
     "mha7b_reorder_bf16": mha7b_reorder_bf16,
     "qwen3vl_window_bf16": qwen3vl_window_bf16,
+    "qwen25vl_mrope_bf16": qwen25vl_mrope_bf16,
+    "neox_partial_bf16": neox_partial_bf16,
+    "scaled_table_bf16": scaled_table_bf16,
 }
 
 

@@ -47,6 +47,7 @@ class ChunkSpec:
     spread: float = 2.0
     level: float = 0.15
     same_as_canonical: bool = False   # conditioned = canonical bits (delta should be 0)
+    delta_sections: tuple | None = None   # shifts of sections 1, 2 (default: delta)
 
 
 @dataclass
@@ -81,7 +82,24 @@ def _orthonormal(rng, rows: int, cols: int) -> np.ndarray:
     return q
 
 
-def build(case: Case) -> list[dict]:
+def oracle_rope(case: Case, spec: ChunkSpec, ch: int, rope: dict | None) -> dict:
+    """Oracle arguments of the RoPE variant `rope` ({"inv_freq", "pair_section"}, optional)
+    for channel ch; a GQA case with rope_dim < head_dim is partially rotary."""
+    if ch != 0:
+        return {}
+    rope = rope or {}
+    kw = {}
+    if case.family == "gqa" and case.rope_dim < case.head_dim:
+        kw["rot_dim"] = case.rope_dim
+    if rope.get("inv_freq") is not None:
+        kw["inv_freq"] = rope["inv_freq"]
+    if rope.get("pair_section") is not None:
+        s1, s2 = spec.delta_sections or (spec.delta, spec.delta)
+        kw["pair_delta"] = oracle.pair_deltas(rope["pair_section"], (spec.delta, s1, s2))
+    return kw
+
+
+def build(case: Case, rope: dict | None = None) -> list[dict]:
     """Per chunk: {"canonical": [ch] array [L, T, H*W], "conditioned": same}; the arrays hold
     element bits (uint16 for bf16, float32 for fp32)."""
     rng = np.random.default_rng(case.seed)
@@ -108,7 +126,8 @@ def build(case: Case) -> list[dict]:
                         s = s1 * spec.spread ** (-np.arange(r) / max(1, r - 1))
                         planted = (_orthonormal(rng, T, r) * s) @ _orthonormal(rng, W, r).T
                     moved, _ = oracle.segment(head, rotate=rot, layout=case.layout,
-                                              delta=spec.delta, theta=case.theta)
+                                              delta=spec.delta, theta=case.theta,
+                                              **oracle_rope(case, spec, ch, rope))
                     cond[l, :, h * W:(h + 1) * W] = _store(moved + planted, case.dtype)
             item["canonical"].append(canon)
             item["conditioned"].append(cond)
@@ -116,7 +135,8 @@ def build(case: Case) -> list[dict]:
     return out
 
 
-def expected(case: Case, inputs: list[dict], c: int, ch: int, layer: int, head: int) -> dict:
+def expected(case: Case, inputs: list[dict], c: int, ch: int, layer: int, head: int,
+             rope: dict | None = None) -> dict:
     """oracle.compile_patch for one head (with the tolerance terms that depend on it)."""
     spec = case.chunks[c]
     H, W, rot = case.geometry(ch)
@@ -124,7 +144,8 @@ def expected(case: Case, inputs: list[dict], c: int, ch: int, layer: int, head: 
     cond = inputs[c]["conditioned"][ch][layer, :, sl]
     canon = inputs[c]["canonical"][ch][layer, :, sl]
     e = oracle.compile_patch(cond, canon, m=spec.m, rotate=rot, layout=case.layout,
-                             delta=spec.delta, theta=case.theta)
+                             delta=spec.delta, theta=case.theta,
+                             **oracle_rope(case, spec, ch, rope))
     s2 = e["s"] ** 2
     m_eff = min(spec.m, len(s2))
     gap = s2[m_eff - 1] - (s2[m_eff] if m_eff < len(s2) else 0.0)

@@ -114,6 +114,23 @@ def _pool_rows(pool_l: torch.Tensor) -> torch.Tensor:
     return pool_l.view(pool_l.shape[0] * pool_l.shape[1], pool_l.shape[2])
 
 
+def rope_kwargs(p: wl.Plan, c: int, ch: int, op: str = "reuse") -> dict:
+    """The oracle's RoPE-variant arguments for chunk c, channel ch of plan p: the rotary part
+    of a partially rotary key head, the model's frequency table, and per-pair shifts from the
+    multimodal sections."""
+    if ch != 0 or op == "patch":
+        return {}
+    kw = {}
+    if p.family == wl.GQA and p.rope_dim < p.head_dim:
+        kw["rot_dim"] = p.rope_dim
+    if p.inv_freq is not None:
+        kw["inv_freq"] = p.inv_freq
+    if p.pair_section is not None:
+        d1, d2 = p.delta_sections[c] if p.delta_sections else (p.deltas[c], p.deltas[c])
+        kw["pair_delta"] = oracle.pair_deltas(p.pair_section, (p.deltas[c], d1, d2))
+    return kw
+
+
 def compare_batch(batch: wl.Batch, op: str = "reuse", layers=None, chunks=None,
                   check_sentinel: bool = True, patch_inputs=None) -> Report:
     """Compare every element of the chosen chunks/layers (all by default).
@@ -154,7 +171,8 @@ def compare_batch(batch: wl.Batch, op: str = "reuse", layers=None, chunks=None,
                         layout=0 if p.rope_layout == wl.HALF_SPLIT else 1,
                         delta=p.deltas[c], theta=p.theta,
                         U=None if not m else np.ascontiguousarray(Uh[h]),
-                        V=None if not m else np.ascontiguousarray(Vh[h]))
+                        V=None if not m else np.ascontiguousarray(Vh[h]),
+                        **rope_kwargs(p, c, ch, op))
                     got = np.ascontiguousarray(got_rows[:, h * W:(h + 1) * W])
                     rep.merge(compare_head(exp, got, p.dtype, m, f"chunk {c} layer {l} ch {ch} head {h}"))
     if check_sentinel:
@@ -207,7 +225,9 @@ def sample_rows(batch: wl.Batch, n_rows: int, seed: int = 0, op: str = "reuse") 
         m = 0 if op == "relocate" or ct.U[ch] is None else ct.U[ch].shape[-1]
         U = to_numpy_bits(ct.U[ch][l, h, t:t + 1]) if m else None
         V = to_numpy_bits(ct.V[ch][l, h]) if m else None
-        exp = oracle.expected_head(src, rotate=(ch == 0), delta=p.deltas[c], theta=p.theta,
-                                   layout=0 if p.rope_layout == wl.HALF_SPLIT else 1, U=U, V=V)
+        exp = oracle.expected_head(src, rotate=(ch == 0 and op != "patch"), delta=p.deltas[c],
+                                   theta=p.theta,
+                                   layout=0 if p.rope_layout == wl.HALF_SPLIT else 1, U=U, V=V,
+                                   **rope_kwargs(p, c, ch, op))
         rep.merge(compare_head(exp, got, p.dtype, m, f"chunk {c} layer {l} ch {ch} head {h} token {t}"))
     return rep

@@ -30,7 +30,7 @@ def test_every_header_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kb.kamera_version() == 10000
+    assert kb.kamera_version() == 10100
     for st in range(6):
         assert kb.kamera_status_string(st) not in ("", "unknown status")
     assert kb.kamera_status_string(99) == "unknown status"
@@ -44,7 +44,7 @@ def test_workspace_bytes():
 
 def _model(**kw):
     d = dict(family=0, dtype=1, n_layers=28, n_kv_heads=4, head_dim=128, rope_dim=128,
-             rope_layout=0, reserved0=0, rope_theta=1e6)
+             rope_layout=0, n_sections=0, rope_theta=1e6)
     d.update(kw)
     return kb.KameraModel(**d)
 
@@ -122,7 +122,9 @@ def test_workspace_misaligned_and_too_small():
     (dict(rope_theta=math.nan), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(rope_theta=1.0), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(head_dim=127, rope_dim=127), kb.KAMERA_ERR_INVALID_ARGUMENT),
-    (dict(rope_dim=64), kb.KAMERA_ERR_UNSUPPORTED),            # GQA rotates the whole head
+    (dict(rope_dim=130), kb.KAMERA_ERR_INVALID_ARGUMENT),      # rotary part wider than the head
+    (dict(n_sections=4), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(n_sections=3), kb.KAMERA_ERR_INVALID_ARGUMENT),      # sections without a pair map
     (dict(head_dim=2048, rope_dim=2048), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(n_kv_heads=0), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(family=1, n_kv_heads=2, head_dim=512, rope_dim=64), kb.KAMERA_ERR_INVALID_ARGUMENT),
@@ -131,6 +133,39 @@ def test_model_validation(kw, status):
     st, msg = call(model=_model(**kw))
     assert st == status, msg
     assert msg
+
+
+def test_rope_variant_tables_are_validated():
+    import numpy as np
+    ok = kb.make_model("gqa", "bf16", 28, 4, 128, 128, "half_split", 1e6,
+                       inv_freq=np.linspace(1.0, 1e-6, 64),
+                       pair_section=np.repeat([0, 1, 2], [16, 24, 24]))
+    st, msg = call(model=ok)
+    assert st == kb.KAMERA_ERR_WORKSPACE, msg                 # valid up to the workspace
+    bad = kb.make_model("gqa", "bf16", 28, 4, 128, 128, "half_split", 1e6,
+                        inv_freq=np.r_[np.ones(63), np.nan])
+    assert call(model=bad)[0] == kb.KAMERA_ERR_INVALID_ARGUMENT
+    bad = kb.make_model("gqa", "bf16", 28, 4, 128, 128, "half_split", 1e6,
+                        inv_freq=np.r_[np.ones(63), -1.0])
+    assert call(model=bad)[0] == kb.KAMERA_ERR_INVALID_ARGUMENT
+    bad = kb.make_model("gqa", "bf16", 28, 4, 128, 128, "half_split", 1e6,
+                        pair_section=np.repeat([0, 1, 2], [16, 24, 24]))
+    bad.n_sections = 2                                        # entry 2 is not below 2
+    assert call(model=bad)[0] == kb.KAMERA_ERR_INVALID_ARGUMENT
+    part = kb.make_model("gqa", "bf16", 28, 4, 128, 64, "half_split", 1e6)
+    assert call(model=part)[0] == kb.KAMERA_ERR_WORKSPACE     # partial rotary is accepted
+
+
+def test_section_shifts_are_range_checked():
+    import numpy as np
+    m = kb.make_model("gqa", "bf16", 28, 4, 128, 128, "half_split", 1e6,
+                      pair_section=np.repeat([0, 1, 2], [16, 24, 24]))
+    ch = _chunks(1)
+    ch[0].delta_sections[1] = 1 << 31
+    st, msg = call(model=m, chunks=ch)
+    assert st == kb.KAMERA_ERR_INVALID_ARGUMENT and "delta_sections" in msg
+    plain = _model()                                           # no sections: not read
+    assert call(model=plain, chunks=ch)[0] == kb.KAMERA_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -16,7 +16,7 @@ GiB = 1 << 30
 
 def _model(**kw):
     d = dict(family=0, dtype=1, n_layers=2, n_kv_heads=2, head_dim=128, rope_dim=128,
-             rope_layout=0, reserved0=0, rope_theta=1e6)
+             rope_layout=0, n_sections=0, rope_theta=1e6)
     d.update(kw)
     return kb.KameraModel(**d)
 
@@ -74,7 +74,9 @@ def test_compile_functions_are_exported():
 
 def test_struct_sizes_match_the_header_layout():
     assert ctypes.sizeof(kb.KameraFactorsOut) == 48
-    assert ctypes.sizeof(kb.KameraCompileChunk) == 16 + 2 * 24 + 2 * 24 + 2 * 48
+    assert ctypes.sizeof(kb.KameraCompileChunk) == 32 + 2 * 24 + 2 * 24 + 2 * 48
+    assert ctypes.sizeof(kb.KameraModel) == 56
+    assert ctypes.sizeof(kb.KameraChunk) == 32 + 2 * 24 + 2 * 56
 
 
 def test_well_formed_call_reaches_the_workspace_check():
@@ -111,8 +113,9 @@ def test_workspace_bytes_closed_form():
     two = _chunks(m, n=2, n_tokens=1296, m=16)
     assert kb.kamera_compile_workspace_bytes(m, two, 2) > need
     empty = _chunks(m, n_tokens=0)
-    assert kb.kamera_compile_workspace_bytes(m, empty, 1) == 256
-    assert kb.kamera_compile_workspace_bytes(m, None, 0) == 256
+    base = kb.kamera_compile_workspace_bytes(m, None, 0)      # the frequency / section tables
+    assert 4096 < base <= 8192 and base % 256 == 0
+    assert kb.kamera_compile_workspace_bytes(m, empty, 1) == base
     assert kb.kamera_compile_workspace_bytes(m, None, -1) == 0
     assert kb.kamera_compile_workspace_bytes(None, one, 1) == 0
 

@@ -56,9 +56,8 @@ def _sentinel(shape, case) -> torch.Tensor:
 
 
 def model_of(case) -> kb.KameraModel:
-    return kb.KameraModel(kb.FAMILY[case.family], kb.DTYPE[case.dtype], case.n_layers,
-                          case.n_kv_heads, case.head_dim, case.rope_dim, case.layout, 0,
-                          float(case.theta))
+    return kb.make_model(case.family, case.dtype, case.n_layers, case.n_kv_heads,
+                         case.head_dim, case.rope_dim, case.layout, case.theta)
 
 
 def device_items(case, inputs):
