@@ -240,3 +240,26 @@ def compile_patch(conditioned: np.ndarray, canonical: np.ndarray, *, m: int, rot
     U = u[:, :m] * s[:m]
     V = vt[:m].T.copy()
     return {"U": U, "V": V, "UV": U @ V.T, "s": s, "delta": d}
+
+
+def orbit_patch(members: list, canonical: np.ndarray, *, m: int, rotate: bool,
+                layout: int = HALF_SPLIT, theta: float = 1e4, **rope) -> dict:
+    """The orbit patch of one head (technical summary §3, item 1: one patch, averaged over the
+    orderings of a cached set, serves every ordering): the deficits of the chunk in each
+    ordering, each in its own frame, are averaged and the mean is reduced to its top-m SVD
+    factors. `members` lists (conditioned, delta) or (conditioned, delta, pair_delta) per
+    ordering; `rope` holds the model's variant arguments shared by all members (rot_dim,
+    inv_freq)."""
+    total = None
+    for mem in members:
+        cond, delta = mem[0], mem[1]
+        kw = dict(rope)
+        if len(mem) > 2 and mem[2] is not None:
+            kw["pair_delta"] = mem[2]
+        d = deficit(cond, canonical, rotate=rotate, layout=layout, delta=delta, theta=theta, **kw)
+        total = d if total is None else total + d
+    mean = total / len(members)
+    u, s, vt = np.linalg.svd(mean, full_matrices=False)
+    U = u[:, :m] * s[:m]
+    V = vt[:m].T.copy()
+    return {"U": U, "V": V, "UV": U @ V.T, "s": s, "delta": mean}

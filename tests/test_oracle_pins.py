@@ -449,3 +449,61 @@ def test_compile_is_the_best_rank_m_approximation():
     q, _ = np.linalg.qr(rng.standard_normal((D, m)))
     other = r["delta"] @ q @ q.T
     assert np.sum((r["delta"] - other) ** 2) > resid
+
+
+# ----------------------------------------------------------------------------------------
+# orbit patch: the mean deficit over orderings, then its top-m factors
+# ----------------------------------------------------------------------------------------
+
+def _orbit_set(rng, T=40, D=64, K=4, m=6, theta=1e4, layout=oracle.HALF_SPLIT):
+    """K orderings of a chunk: shifts d_k, conditioned = R(d_k) canonical + shared low-rank
+    deficit + an ordering-specific deficit (all fp64)."""
+    canonical = rng.standard_normal((T, D))
+    shared = rng.standard_normal((T, m)) @ rng.standard_normal((m, D)) * 0.1
+    members = []
+    for k in range(K):
+        d = int(rng.integers(-5000, 5000))
+        own = rng.standard_normal((T, 2)) @ rng.standard_normal((2, D)) * 0.02
+        reloc, _ = oracle.segment(canonical, rotate=True, layout=layout, delta=d, theta=theta)
+        members.append((reloc + shared + own, d, own))
+    return canonical, shared, members
+
+
+def test_orbit_patch_of_one_ordering_is_the_compile():
+    rng = np.random.default_rng(31)
+    canonical, _, members = _orbit_set(rng, K=1)
+    a = oracle.orbit_patch([members[0][:2]], canonical, m=6, rotate=True)
+    b = oracle.compile_patch(members[0][0], canonical, m=6, rotate=True, delta=members[0][1])
+    np.testing.assert_allclose(a["UV"], b["UV"], rtol=0, atol=1e-12)
+
+
+def test_orbit_deficit_is_the_mean_of_the_orderings_deficits():
+    """Closed form: each member contributes shared + own; the mean is shared + mean(own)."""
+    rng = np.random.default_rng(32)
+    canonical, shared, members = _orbit_set(rng, K=5)
+    r = oracle.orbit_patch([mm[:2] for mm in members], canonical, m=6, rotate=True)
+    expect = shared + sum(mm[2] for mm in members) / len(members)
+    np.testing.assert_allclose(r["delta"], expect, rtol=0, atol=1e-11)
+
+
+def test_orbit_patch_serves_every_ordering_better_than_no_patch():
+    """With a shared rank-m deficit and small ordering-specific parts, the one orbit patch
+    leaves each ordering with only (roughly) its own part."""
+    rng = np.random.default_rng(33)
+    canonical, shared, members = _orbit_set(rng, K=6)
+    r = oracle.orbit_patch([mm[:2] for mm in members], canonical, m=6, rotate=True)
+    for cond, d, own in members:
+        dk = oracle.deficit(cond, canonical, rotate=True, delta=d)
+        left = np.linalg.norm(dk - r["UV"])
+        assert left < 0.5 * np.linalg.norm(dk)
+        assert left < 3.0 * np.linalg.norm(own) + 1e-9
+
+
+def test_orbit_patch_members_in_the_same_frame_average_conditioned_kv():
+    """All orderings at one shift: the mean deficit is the deficit of the mean conditioned KV."""
+    rng = np.random.default_rng(34)
+    canonical = rng.standard_normal((30, 32))
+    conds = [rng.standard_normal((30, 32)) for _ in range(3)]
+    r = oracle.orbit_patch([(c, 123) for c in conds], canonical, m=4, rotate=True)
+    d = oracle.deficit(sum(conds) / 3, canonical, rotate=True, delta=123)
+    np.testing.assert_allclose(r["delta"], d, rtol=0, atol=1e-12)
