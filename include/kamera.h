@@ -273,6 +273,47 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
                                    int32_t n_chunks, int32_t n_iter, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* ---- Orbit patch ------------------------------------------------------------------------
+ * One patch for every ordering of a cached set (technical summary §3, the reorder window
+ * operation: a single patch, averaged over permutations, serves every ordering). The caller
+ * lists, per chunk, the orderings to average: for each, the chunk's conditioned KV in that
+ * ordering (KV(B | its predecessors there), from the caller's forward pass) and its shift.
+ * The deficits are averaged, each in its own frame,
+ *     Delta_bar = (1/K) sum_k [ KV_k(B|A_k) - R(delta_k) KV(B|empty) ],
+ * and Delta_bar is reduced exactly as kamera_patch_compile reduces Delta (same factors, same
+ * limits, same outputs). On the device the mean of the rotations acts on each pair as
+ * [[mean cos, -mean sin], [mean sin, mean cos]] (fp64 means, one rounding), so each streaming
+ * pass reads the canonical rows once and every ordering's conditioned rows once. With one
+ * ordering the result is bit-identical to kamera_patch_compile. */
+#define KAMERA_ORBIT_MAX_MEMBERS 64
+
+typedef struct kamera_orbit_member {
+  int64_t delta;              /* the chunk's position in this ordering minus its canonical one */
+  int64_t delta_sections[2];  /* as in kamera_chunk */
+  kamera_src conditioned[2];  /* per channel; same layout rules as kamera_src */
+} kamera_orbit_member;
+
+typedef struct kamera_orbit_chunk {
+  int32_t n_tokens;
+  int32_t m;
+  int32_t n_members;                   /* orderings averaged, 1..KAMERA_ORBIT_MAX_MEMBERS */
+  int32_t reserved0;
+  const kamera_orbit_member* members;  /* host, n_members entries, read during the call */
+  kamera_src canonical[2];
+  kamera_factors_out out[2];
+} kamera_orbit_chunk;
+
+/* Workspace bytes for kamera_patch_compile_orbit (geometry only); 0 on invalid arguments. */
+size_t kamera_orbit_compile_workspace_bytes(const kamera_model* model,
+                                            const kamera_orbit_chunk* chunks, int32_t n_chunks);
+
+/* The orbit patch of every chunk (see above), on `stream`. Validation, overlap rules (every
+ * member's conditioned rows are inputs), n_iter and error conventions as kamera_patch_compile. */
+kamera_status kamera_patch_compile_orbit(const kamera_model* model,
+                                         const kamera_orbit_chunk* chunks, int32_t n_chunks,
+                                         int32_t n_iter, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 const char* kamera_status_string(kamera_status status);
 const char* kamera_last_error(void); /* per-thread; "" if none */
 int32_t kamera_version(void);

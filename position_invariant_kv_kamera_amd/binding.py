@@ -75,6 +75,17 @@ class KameraCompileChunk(ctypes.Structure):
 
 
 COMPILE_MAX_RANK = 64
+ORBIT_MAX_MEMBERS = 64
+
+
+class KameraOrbitMember(ctypes.Structure):
+    _fields_ = [("delta", c_i64), ("delta_sections", c_i64 * 2), ("conditioned", KameraSrc * 2)]
+
+
+class KameraOrbitChunk(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i32), ("m", c_i32), ("n_members", c_i32), ("reserved0", c_i32),
+                ("members", ctypes.POINTER(KameraOrbitMember)), ("canonical", KameraSrc * 2),
+                ("out", KameraFactorsOut * 2)]
 
 
 _lib = None
@@ -117,6 +128,13 @@ def load_library() -> ctypes.CDLL:
                                          ctypes.POINTER(KameraCompileChunk), c_i32, c_i32, c_vp,
                                          c_size, c_vp]
     lib.kamera_patch_compile.restype = ctypes.c_int
+    lib.kamera_orbit_compile_workspace_bytes.argtypes = [ctypes.POINTER(KameraModel),
+                                                         ctypes.POINTER(KameraOrbitChunk), c_i32]
+    lib.kamera_orbit_compile_workspace_bytes.restype = c_size
+    lib.kamera_patch_compile_orbit.argtypes = [ctypes.POINTER(KameraModel),
+                                               ctypes.POINTER(KameraOrbitChunk), c_i32, c_i32,
+                                               c_vp, c_size, c_vp]
+    lib.kamera_patch_compile_orbit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -195,6 +213,18 @@ def kamera_compile_workspace_bytes(model, chunks, n_chunks) -> int:
 
 def kamera_patch_compile(model, chunks, n_chunks, n_iter, workspace, workspace_bytes, stream):
     return int(load_library().kamera_patch_compile(
+        ctypes.byref(model) if model is not None else None, chunks, int(n_chunks), int(n_iter),
+        workspace, int(workspace_bytes), stream))
+
+
+def kamera_orbit_compile_workspace_bytes(model, chunks, n_chunks) -> int:
+    return int(load_library().kamera_orbit_compile_workspace_bytes(
+        ctypes.byref(model) if model is not None else None, chunks, int(n_chunks)))
+
+
+def kamera_patch_compile_orbit(model, chunks, n_chunks, n_iter, workspace, workspace_bytes,
+                               stream):
+    return int(load_library().kamera_patch_compile_orbit(
         ctypes.byref(model) if model is not None else None, chunks, int(n_chunks), int(n_iter),
         workspace, int(workspace_bytes), stream))
 
@@ -341,4 +371,54 @@ def run_compile(model: KameraModel, items, *, n_iter: int = 8, workspace: Worksp
     ws = workspace if workspace is not None and workspace.nbytes >= need else Workspace(nbytes=need)
     s = current_stream_ptr() if stream is None else stream
     check(kamera_patch_compile(model, chunks, len(items), n_iter, ws.ptr, ws.nbytes, s))
+    return ws
+
+
+class OrbitItem:
+    """One chunk of an orbit compile: canonical[c] as in CompileItem, `members` a list of
+    (delta, conditioned) or (delta, conditioned, delta_sections) per ordering, conditioned a
+    per-channel list of [layers, tokens, heads*width] views; U, V outputs as in CompileItem."""
+
+    def __init__(self, n_tokens, m, canonical, members, U, V):
+        self.n_tokens, self.m = int(n_tokens), int(m)
+        self.canonical, self.members, self.U, self.V = canonical, members, U, V
+
+
+def orbit_chunks_of(items):
+    arr = (KameraOrbitChunk * max(1, len(items)))()
+    keep = []
+    for i, it in enumerate(items):
+        k = arr[i]
+        k.n_tokens, k.m, k.n_members = it.n_tokens, it.m, len(it.members)
+        mem = (KameraOrbitMember * max(1, len(it.members)))()
+        for q, entry in enumerate(it.members):
+            delta, cond = entry[0], entry[1]
+            ds = entry[2] if len(entry) > 2 else (delta, delta)
+            mem[q].delta = int(delta)
+            mem[q].delta_sections[0], mem[q].delta_sections[1] = int(ds[0]), int(ds[1])
+            for ch in range(2):
+                mem[q].conditioned[ch] = KameraSrc(cond[ch].data_ptr(), cond[ch].stride(0),
+                                                   cond[ch].stride(1))
+        keep.append(mem)
+        k.members = ctypes.cast(mem, ctypes.POINTER(KameraOrbitMember))
+        for ch in range(2):
+            a = it.canonical[ch]
+            k.canonical[ch] = KameraSrc(a.data_ptr(), a.stride(0), a.stride(1))
+            U, V = it.U[ch], it.V[ch]
+            k.out[ch] = KameraFactorsOut(U.data_ptr(), U.stride(0), U.stride(1), V.data_ptr(),
+                                         V.stride(0), V.stride(1))
+    arr._keep = keep
+    return arr
+
+
+def run_orbit_compile(model: KameraModel, items, *, n_iter: int = 8,
+                      workspace: Workspace | None = None, stream=None) -> Workspace:
+    """kamera_patch_compile_orbit over `items` (asynchronous on the stream)."""
+    chunks = orbit_chunks_of(items)
+    need = kamera_orbit_compile_workspace_bytes(model, chunks, len(items))
+    if need == 0:
+        raise KameraError(KAMERA_ERR_INVALID_ARGUMENT, kamera_last_error())
+    ws = workspace if workspace is not None and workspace.nbytes >= need else Workspace(nbytes=need)
+    s = current_stream_ptr() if stream is None else stream
+    check(kamera_patch_compile_orbit(model, chunks, len(items), n_iter, ws.ptr, ws.nbytes, s))
     return ws

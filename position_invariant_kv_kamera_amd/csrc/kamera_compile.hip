@@ -42,27 +42,35 @@ constexpr int kMinSplitTokens = 1024; // Gram split never shorter than this (exc
 constexpr int kGramTilesPerJob = 64;   // jobs with fewer Gram tiles split their tokens
 constexpr double kDeadTol = 1e-12;   // pivot^2 / column norm^2 below this: column collapsed
 
-// One chunk, one channel, all layers and heads (a "unit" is one layer and head).
-struct alignas(16) CJob {
-  const void* canon;
+// One ordering of a chunk (an orbit member; a plain compile has one): its conditioned rows of
+// one channel and its shifts.
+struct alignas(16) CMember {
   const void* cond;
-  void* U;
-  void* V;
-  int64_t canon_ls, canon_ts, cond_ls, cond_ts;
-  int64_t u_ls, u_hs, v_ls, v_hs;
+  int64_t cond_ls, cond_ts;
   int64_t delta;    // shift of section 0 (of every pair without sections)
   int64_t delta_s1; // shifts of sections 1 and 2
   int64_t delta_s2;
+};
+
+// One chunk, one channel, all layers and heads (a "unit" is one layer and head).
+struct alignas(16) CJob {
+  const void* canon;
+  void* U;
+  void* V;
+  int64_t canon_ls, canon_ts;
+  int64_t u_ls, u_hs, v_ls, v_hs;
   int64_t gpart;   // float offset of the partial Gram tiles [unit][pair][split][te][te]
   int64_t gfull;   // float offset of the assembled G [unit][width][width], or -1 (partial is G)
   int64_t xbase;   // float offset of the fp32 bases [unit][width][mp]
   int32_t n_tokens, m, mp, width, heads, rotate, te, nb, n_pairs, splits, split_tokens, n_units;
   int32_t rot_dim;  // features of each head that turn (the rest pass through); pairs rot_dim/2
+  int32_t member_off, n_members;   // this job's orderings in the member table
   int32_t pad0;
 };
 
 struct CParams {
   const CJob* jobs;
+  const CMember* members;
   const int32_t* starts;   // first block of each entry, ascending
   const int32_t* job_of;   // job index of each entry
   float* ws;               // float view of the workspace's data region
@@ -98,16 +106,24 @@ __device__ __forceinline__ int find_entry(const CParams& P, int b) {
 // cos/sin(shift * frequency) per pair: angle and reduction in fp64, one rounding. The
 // frequency is the table entry when the model gives one, else theta^(-2i/rot_dim); the shift
 // is that of the pair's position component (multimodal sections), else the chunk's.
+// With several orderings (an orbit) the table holds the mean of their cos and sin: the mean
+// of the rotations R(delta_k) acts on each pair as [[cbar, -sbar], [sbar, cbar]].
 __device__ void fill_phases(float2* cs, const CJob& J, const CParams& P) {
   const int rot_dim = J.rot_dim;
+  const CMember* mem = P.members + J.member_off;
   for (int i = threadIdx.x; i < rot_dim / 2; i += kThreads) {
     const double inv = P.inv_freq ? P.inv_freq[i]
                                   : pow(P.theta, -2.0 * (double)i / (double)rot_dim);
     const int sec = P.pair_section ? (int)P.pair_section[i] : 0;
-    const int64_t delta = sec == 0 ? J.delta : (sec == 1 ? J.delta_s1 : J.delta_s2);
-    double s, c;
-    sincos((double)delta * inv, &s, &c);
-    cs[i] = make_float2((float)c, (float)s);
+    double cbar = 0.0, sbar = 0.0;
+    for (int k = 0; k < J.n_members; ++k) {
+      const int64_t delta = sec == 0 ? mem[k].delta : (sec == 1 ? mem[k].delta_s1 : mem[k].delta_s2);
+      double s, c;
+      sincos((double)delta * inv, &s, &c);
+      cbar += c;
+      sbar += s;
+    }
+    cs[i] = make_float2((float)(cbar / J.n_members), (float)(sbar / J.n_members));
   }
 }
 
@@ -132,16 +148,41 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) {
 }
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
+// Mean over the job's orderings of the conditioned elements [f, f + 8) of one token row (one
+// ordering: the row itself, exactly).
+template <typename T>
+__device__ __forceinline__ void load_cond8(const CMember* mem, int n_members, int layer,
+                                           int64_t head_off, int tok, int f, float* o) {
+  load8(static_cast<const T*>(mem[0].cond) + layer * mem[0].cond_ls + head_off +
+            tok * mem[0].cond_ts + f, o);
+  if (n_members == 1) return;
+  for (int k = 1; k < n_members; ++k) {
+    float x[8];
+    load8(static_cast<const T*>(mem[k].cond) + layer * mem[k].cond_ls + head_off +
+              tok * mem[k].cond_ts + f, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += x[e];
+  }
+  const float scale = 1.0f / (float)n_members;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= scale;
+}
+
 // Rows [tok0, tok0 + ROWS) of Delta, columns [col0, col0 + ncols), into dst (fp32, row stride
 // ds); rows at or past tok_end are zero. A rotated head is always staged whole (col0 = 0,
 // ncols = width) so that both members of every pair are at hand; its pairs lie in the first
-// rot_dim features, the others pass through.
+// rot_dim features, the others pass through. With several orderings Delta is their mean:
+// mean conditioned rows minus the mean rotation (cs) applied to the canonical rows.
 template <typename T, int ROWS>
-__device__ void stage_delta(const CJob& J, int layout, const float2* cs, int layer, int head,
-                            int tok0, int tok_end, int col0, int ncols, float* dst, int ds) {
+__device__ void stage_delta(const CJob& J, const CParams& P, const float2* cs, int layer,
+                            int head, int tok0, int tok_end, int col0, int ncols, float* dst,
+                            int ds) {
+  const int layout = P.layout;
   const int W = J.width;
-  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + (int64_t)head * W;
-  const T* cond = static_cast<const T*>(J.cond) + layer * J.cond_ls + (int64_t)head * W;
+  const int64_t head_off = (int64_t)head * W;
+  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off;
+  const CMember* mem = P.members + J.member_off;
+  const int K = J.n_members;
   if (J.rotate) {
     // groups of 8 pairs over the turning features [0, R), then groups of 8 features passing
     // through over [R, W)
@@ -160,7 +201,7 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
         }
         float x[8], c[8];
         load8(canon + tok * J.canon_ts + f, x);
-        load8(cond + tok * J.cond_ts + f, c);
+        load_cond8<T>(mem, K, layer, head_off, tok, f, c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) d[f + k] = c[k] - x[k];
         continue;
@@ -175,8 +216,8 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
       float xa[8], xb[8], ca[8], cb[8];
       load8(canon + tok * J.canon_ts + fa, xa);
       load8(canon + tok * J.canon_ts + fb, xb);
-      load8(cond + tok * J.cond_ts + fa, ca);
-      load8(cond + tok * J.cond_ts + fb, cb);
+      load_cond8<T>(mem, K, layer, head_off, tok, fa, ca);
+      load_cond8<T>(mem, K, layer, head_off, tok, fb, cb);
       if (layout == KAMERA_ROPE_HALF_SPLIT) {
         // pair 8q+k = (feature fa+k, feature fb+k)
 #pragma unroll
@@ -217,7 +258,7 @@ __device__ void stage_delta(const CJob& J, int layout, const float2* cs, int lay
       }
       float x[8], c[8];
       load8(canon + tok * J.canon_ts + col0 + 8 * q, x);
-      load8(cond + tok * J.cond_ts + col0 + 8 * q, c);
+      load_cond8<T>(mem, K, layer, head_off, tok, col0 + 8 * q, c);
 #pragma unroll
       for (int k = 0; k < 8; ++k) d[k] = c[k] - x[k];
     }
@@ -282,9 +323,9 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
 
   for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
     __syncthreads();
-    stage_delta<T, kStepTokens>(J, P.layout, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
+    stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
     if (bi != bj)
-      stage_delta<T, kStepTokens>(J, P.layout, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
+      stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
     __syncthreads();
 #pragma unroll 2
     for (int kk = 0; kk < kStepTokens / 4; ++kk) {
@@ -766,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
   const int brow = (lane >> 4) * SV + (lane & 15);
   for (int tok0 = t_lo; tok0 < t_hi; tok0 += STEP) {
     __syncthreads();
-    stage_delta<T, STEP>(J, P.layout, cs, layer, head, tok0, t_hi, 0, D, dl, DS);
+    stage_delta<T, STEP>(J, P, cs, layer, head, tok0, t_hi, 0, D, dl, DS);
     __syncthreads();
     f32x4 acc[4];
 #pragma unroll
@@ -812,8 +853,23 @@ struct Launch {
   size_t off = 0;                   // byte offset of starts (job_of follows)
 };
 
+// A chunk to compile, whichever entry point described it: its orderings (one for a plain
+// compile), canonical rows and output factors.
+struct MemberIn {
+  int64_t delta, delta_s[2];
+  kamera_src cond[2];
+};
+struct ChunkIn {
+  int32_t n_tokens = 0, m = 0;
+  std::vector<MemberIn> members;
+  kamera_src canonical[2];
+  kamera_factors_out out[2];
+};
+
 struct CPlan {
   std::vector<CJob> jobs;
+  std::vector<CMember> members;
+  size_t members_off = 0;
   std::vector<Launch> launches;
   size_t freq_off = 0;   // frequency table (kMaxPairs doubles) and pair sections (kMaxPairs bytes)
   size_t sec_off = 0;
@@ -852,14 +908,11 @@ bool strided_disjoint(int64_t sa, int64_t na, int64_t sb, int64_t nb, int64_t si
   return true;
 }
 
-kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* chunks,
-                           int32_t n_chunks, CPlan* plan) {
-  if (n_chunks < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 0");
-  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
-  const int64_t es = M.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
+kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& chunks,
+                           CPlan* plan) {
   int64_t floats = 0;
-  for (int32_t i = 0; i < n_chunks; ++i) {
-    const kamera_compile_chunk& k = chunks[i];
+  for (int32_t i = 0; i < (int32_t)chunks.size(); ++i) {
+    const ChunkIn& k = chunks[i];
     if (k.n_tokens < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: n_tokens < 0", i);
     if (k.n_tokens == 0) continue;
     if (k.m < 1) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: m must be >= 1", i);
@@ -867,12 +920,17 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
       return fail(KAMERA_ERR_UNSUPPORTED, "chunk %d: m = %d exceeds %d", i, k.m,
                   KAMERA_COMPILE_MAX_RANK);
     auto big = [](int64_t d) { return d >= (int64_t(1) << 31) || d <= -(int64_t(1) << 31); };
-    if (big(k.delta))
-      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta| must be < 2^31", i);
-    for (int sct = 1; sct < M.n_sections; ++sct)
-      if (big(k.delta_sections[sct - 1]))
-        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: |delta_sections[%d]| must be < 2^31",
-                    i, sct - 1);
+    for (size_t q = 0; q < k.members.size(); ++q) {
+      const MemberIn& mb = k.members[q];
+      if (big(mb.delta))
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d member %d: |delta| must be < 2^31",
+                    i, (int)q);
+      for (int sct = 1; sct < M.n_sections; ++sct)
+        if (big(mb.delta_s[sct - 1]))
+          return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                      "chunk %d member %d: |delta_sections[%d]| must be < 2^31", i, (int)q,
+                      sct - 1);
+    }
     for (int ch = 0; ch < 2; ++ch) {
       const Channel g = channel_of(M, ch);
       if (g.rotate && M.rope_dim < g.width && (M.rope_dim % 16 || (g.width - M.rope_dim) % 8))
@@ -892,20 +950,26 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
                     "chunk %d channel %d: m = %d above 32 needs width <= 128", i, ch, k.m);
       CJob J{};
       J.canon = k.canonical[ch].ptr;
-      J.cond = k.conditioned[ch].ptr;
       J.U = k.out[ch].U;
       J.V = k.out[ch].V;
       J.canon_ls = k.canonical[ch].layer_stride;
       J.canon_ts = k.canonical[ch].token_stride;
-      J.cond_ls = k.conditioned[ch].layer_stride;
-      J.cond_ts = k.conditioned[ch].token_stride;
       J.u_ls = k.out[ch].u_layer_stride;
       J.u_hs = k.out[ch].u_head_stride;
       J.v_ls = k.out[ch].v_layer_stride;
       J.v_hs = k.out[ch].v_head_stride;
-      J.delta = k.delta;
-      J.delta_s1 = M.n_sections > 1 ? k.delta_sections[0] : k.delta;
-      J.delta_s2 = M.n_sections > 2 ? k.delta_sections[1] : k.delta;
+      J.member_off = (int32_t)plan->members.size();
+      J.n_members = (int32_t)k.members.size();
+      for (const MemberIn& mb : k.members) {
+        CMember c{};
+        c.cond = mb.cond[ch].ptr;
+        c.cond_ls = mb.cond[ch].layer_stride;
+        c.cond_ts = mb.cond[ch].token_stride;
+        c.delta = mb.delta;
+        c.delta_s1 = M.n_sections > 1 ? mb.delta_s[0] : mb.delta;
+        c.delta_s2 = M.n_sections > 2 ? mb.delta_s[1] : mb.delta;
+        plan->members.push_back(c);
+      }
       J.rot_dim = g.rotate ? M.rope_dim : 0;
       J.n_tokens = k.n_tokens;
       J.m = k.m;
@@ -941,7 +1005,6 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
       plan->jobs.push_back(J);
     }
   }
-  (void)es;
   // launches: one per kernel class present
   auto add = [&](int kind, int cls, int job, int64_t blocks) -> bool {
     Launch* L = nullptr;
@@ -968,6 +1031,8 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
     if (!ok) return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
   }
   size_t off = round_up(plan->jobs.size() * sizeof(CJob), 16);
+  plan->members_off = off;
+  off = round_up(off + plan->members.size() * sizeof(CMember), 16);
   plan->freq_off = off;
   off += kamera::kMaxPairs * sizeof(double);
   plan->sec_off = off;
@@ -983,8 +1048,7 @@ kamera_status plan_compile(const kamera_model& M, const kamera_compile_chunk* ch
   return KAMERA_OK;
 }
 
-kamera_status validate_compile_pointers(const kamera_model& M, const kamera_compile_chunk* chunks,
-                                        int32_t n_chunks) {
+kamera_status validate_compile_pointers(const kamera_model& M, const std::vector<ChunkIn>& chunks) {
   const int64_t es = M.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
   struct Tagged {
     Range r;
@@ -993,15 +1057,19 @@ kamera_status validate_compile_pointers(const kamera_model& M, const kamera_comp
   };
   std::vector<Tagged> outs, ins;
   auto a16 = [&](int64_t stride) { return (stride * es) % 16 == 0; };
-  for (int32_t i = 0; i < n_chunks; ++i) {
-    const kamera_compile_chunk& k = chunks[i];
+  for (int32_t i = 0; i < (int32_t)chunks.size(); ++i) {
+    const ChunkIn& k = chunks[i];
     if (k.n_tokens == 0) continue;
     for (int ch = 0; ch < 2; ++ch) {
       const Channel g = channel_of(M, ch);
       const int64_t row = (int64_t)g.heads * g.width;
-      const kamera_src* srcs[2] = {&k.canonical[ch], &k.conditioned[ch]};
-      const char* names[2] = {"canonical", "conditioned"};
-      for (int s = 0; s < 2; ++s) {
+      std::vector<const kamera_src*> srcs{&k.canonical[ch]};
+      std::vector<const char*> names{"canonical"};
+      for (const MemberIn& mb : k.members) {
+        srcs.push_back(&mb.cond[ch]);
+        names.push_back("conditioned");
+      }
+      for (size_t s = 0; s < srcs.size(); ++s) {
         const kamera_src& x = *srcs[s];
         if (!x.ptr)
           return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: %s is NULL", i, ch,
@@ -1101,30 +1169,80 @@ hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
 
-extern "C" {
 
-size_t kamera_compile_workspace_bytes(const kamera_model* model,
-                                      const kamera_compile_chunk* chunks, int32_t n_chunks) {
-  if (validate_model(model) != KAMERA_OK) return 0;
+// The plain compile: one ordering per chunk.
+kamera_status lower_plain(const kamera_compile_chunk* chunks, int32_t n_chunks,
+                          std::vector<ChunkIn>* out) {
+  if (n_chunks < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 0");
+  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
+  out->resize(n_chunks);
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_compile_chunk& k = chunks[i];
+    ChunkIn& c = (*out)[i];
+    c.n_tokens = k.n_tokens;
+    c.m = k.m;
+    MemberIn mb{};
+    mb.delta = k.delta;
+    mb.delta_s[0] = k.delta_sections[0];
+    mb.delta_s[1] = k.delta_sections[1];
+    for (int ch = 0; ch < 2; ++ch) {
+      mb.cond[ch] = k.conditioned[ch];
+      c.canonical[ch] = k.canonical[ch];
+      c.out[ch] = k.out[ch];
+    }
+    c.members.push_back(mb);
+  }
+  return KAMERA_OK;
+}
+
+// The orbit compile: the orderings each chunk lists.
+kamera_status lower_orbit(const kamera_orbit_chunk* chunks, int32_t n_chunks,
+                          std::vector<ChunkIn>* out) {
+  if (n_chunks < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 0");
+  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
+  out->resize(n_chunks);
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_orbit_chunk& k = chunks[i];
+    ChunkIn& c = (*out)[i];
+    c.n_tokens = k.n_tokens;
+    c.m = k.m;
+    for (int ch = 0; ch < 2; ++ch) {
+      c.canonical[ch] = k.canonical[ch];
+      c.out[ch] = k.out[ch];
+    }
+    if (k.n_tokens == 0) continue;
+    if (k.n_members < 1 || k.n_members > KAMERA_ORBIT_MAX_MEMBERS)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: n_members must be in [1, %d] (got %d)",
+                  i, KAMERA_ORBIT_MAX_MEMBERS, k.n_members);
+    if (!k.members) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: members is NULL", i);
+    for (int32_t q = 0; q < k.n_members; ++q) {
+      const kamera_orbit_member& om = k.members[q];
+      MemberIn mb{};
+      mb.delta = om.delta;
+      mb.delta_s[0] = om.delta_sections[0];
+      mb.delta_s[1] = om.delta_sections[1];
+      for (int ch = 0; ch < 2; ++ch) mb.cond[ch] = om.conditioned[ch];
+      c.members.push_back(mb);
+    }
+  }
+  return KAMERA_OK;
+}
+
+size_t workspace_for(const kamera_model* model, const std::vector<ChunkIn>& chunks) {
   CPlan plan;
-  if (plan_compile(*model, chunks, n_chunks, &plan) != KAMERA_OK) return 0;
+  if (plan_compile(*model, chunks, &plan) != KAMERA_OK) return 0;
   return round_up(std::max<size_t>(plan.total_bytes, 256), 256);
 }
 
-kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compile_chunk* chunks,
-                                   int32_t n_chunks, int32_t n_iter, void* workspace,
-                                   size_t workspace_bytes, void* stream_ptr) {
-  clear_error();
-  kamera_status st = validate_model(model);
-  if (st != KAMERA_OK) return st;
+kamera_status compile(const kamera_model* model, const std::vector<ChunkIn>& chunks,
+                      int32_t n_iter, void* workspace, size_t workspace_bytes, void* stream_ptr) {
   if (n_iter < 1 || n_iter > 100)
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_iter must be in [1, 100] (got %d)", n_iter);
   CPlan plan;
-  st = plan_compile(*model, chunks, n_chunks, &plan);
+  kamera_status st = plan_compile(*model, chunks, &plan);
   if (st != KAMERA_OK) return st;
-  st = validate_compile_pointers(*model, chunks, n_chunks);
+  st = validate_compile_pointers(*model, chunks);
   if (st != KAMERA_OK) return st;
   if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -1136,6 +1254,8 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
 
   std::vector<uint8_t> table(plan.table_bytes, 0);
   std::memcpy(table.data(), plan.jobs.data(), plan.jobs.size() * sizeof(CJob));
+  std::memcpy(table.data() + plan.members_off, plan.members.data(),
+              plan.members.size() * sizeof(CMember));
   const int pairs = model->rope_dim / 2;
   if (model->inv_freq)
     std::memcpy(table.data() + plan.freq_off, model->inv_freq, pairs * sizeof(double));
@@ -1153,6 +1273,7 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
   uint8_t* base = static_cast<uint8_t*>(workspace);
   CParams P{};
   P.jobs = reinterpret_cast<const CJob*>(base);
+  P.members = reinterpret_cast<const CMember*>(base + plan.members_off);
   P.ws = reinterpret_cast<float*>(base + plan.data_off);
   P.theta = model->rope_theta;
   P.inv_freq = model->inv_freq ? reinterpret_cast<const double*>(base + plan.freq_off) : nullptr;
@@ -1173,6 +1294,51 @@ kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compi
     }
   }
   return KAMERA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kamera_compile_workspace_bytes(const kamera_model* model,
+                                      const kamera_compile_chunk* chunks, int32_t n_chunks) {
+  if (validate_model(model) != KAMERA_OK) return 0;
+  std::vector<ChunkIn> in;
+  if (lower_plain(chunks, n_chunks, &in) != KAMERA_OK) return 0;
+  return workspace_for(model, in);
+}
+
+kamera_status kamera_patch_compile(const kamera_model* model, const kamera_compile_chunk* chunks,
+                                   int32_t n_chunks, int32_t n_iter, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  std::vector<ChunkIn> in;
+  st = lower_plain(chunks, n_chunks, &in);
+  if (st != KAMERA_OK) return st;
+  return compile(model, in, n_iter, workspace, workspace_bytes, stream);
+}
+
+size_t kamera_orbit_compile_workspace_bytes(const kamera_model* model,
+                                            const kamera_orbit_chunk* chunks, int32_t n_chunks) {
+  if (validate_model(model) != KAMERA_OK) return 0;
+  std::vector<ChunkIn> in;
+  if (lower_orbit(chunks, n_chunks, &in) != KAMERA_OK) return 0;
+  return workspace_for(model, in);
+}
+
+kamera_status kamera_patch_compile_orbit(const kamera_model* model,
+                                         const kamera_orbit_chunk* chunks, int32_t n_chunks,
+                                         int32_t n_iter, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  clear_error();
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  std::vector<ChunkIn> in;
+  st = lower_orbit(chunks, n_chunks, &in);
+  if (st != KAMERA_OK) return st;
+  return compile(model, in, n_iter, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

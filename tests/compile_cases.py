@@ -155,6 +155,68 @@ def expected(case: Case, inputs: list[dict], c: int, ch: int, layer: int, head: 
     return e
 
 
+# ---- orbit patch ---------------------------------------------------------------------------
+# Orbit inputs: one chunk seen in K orderings at shifts delta_k; ordering k's conditioned KV is
+# element type(R(delta_k) canonical + shared + own_k) with `shared` the planted rank-m deficit
+# of the chunk spec and own_k a rank-2 ordering-specific part with singular values
+# own_level * s_m. The GPU forms the mean deficit from K fp32 sums, so its formation error
+# grows with K and with |KV| / |Delta_bar|: the subspace budget adds
+# 4 (K + 2) (||KV||_F / ||Delta_bar||_F) 2^-24 to the 8 sqrt(n) 2^-24 factor.
+
+def build_orbit(case: Case, deltas, own_level: float = 0.01, rope: dict | None = None) -> dict:
+    rng = np.random.default_rng(case.seed)
+    spec = case.chunks[0]
+    T = spec.n_tokens
+    out = {"canonical": [], "conditioned": [[] for _ in deltas], "deltas": list(deltas)}
+    for ch in range(2):
+        H, W, rot = case.geometry(ch)
+        L = case.n_layers
+        canon = _store(rng.standard_normal((L, T, H * W)), case.dtype)
+        conds = [np.empty_like(canon) for _ in deltas]
+        r = min(spec.m, T, W)
+        for l in range(L):
+            for h in range(H):
+                head = canon[l, :, h * W:(h + 1) * W]
+                s1 = spec.level * math.sqrt(T * W / r)
+                sv = s1 * spec.spread ** (-np.arange(r) / max(1, r - 1))
+                shared = (_orthonormal(rng, T, r) * sv) @ _orthonormal(rng, W, r).T
+                for k, d in enumerate(deltas):
+                    own = (_orthonormal(rng, T, 2) * (own_level * sv[-1])) @ _orthonormal(rng, W, 2).T
+                    sk = ChunkSpec(T, spec.m, d)
+                    moved, _ = oracle.segment(head, rotate=rot, layout=case.layout, delta=d,
+                                              theta=case.theta, **oracle_rope(case, sk, ch, rope))
+                    conds[k][l, :, h * W:(h + 1) * W] = _store(moved + shared + own, case.dtype)
+        out["canonical"].append(canon)
+        for k in range(len(deltas)):
+            out["conditioned"][k].append(conds[k])
+    return out
+
+
+def expected_orbit(case: Case, inp: dict, ch: int, layer: int, head: int,
+                   rope: dict | None = None) -> dict:
+    spec = case.chunks[0]
+    H, W, rot = case.geometry(ch)
+    sl = slice(head * W, (head + 1) * W)
+    canon = inp["canonical"][ch][layer, :, sl]
+    members = []
+    shared_kw = {}
+    for k, d in enumerate(inp["deltas"]):
+        kw = oracle_rope(case, ChunkSpec(spec.n_tokens, spec.m, d), ch, rope)
+        members.append((inp["conditioned"][k][ch][layer, :, sl], d, kw.pop("pair_delta", None)))
+        shared_kw = kw
+    e = oracle.orbit_patch(members, canon, m=spec.m, rotate=rot, layout=case.layout,
+                           theta=case.theta, **shared_kw)
+    s2 = e["s"] ** 2
+    m_eff = min(spec.m, len(s2))
+    gap = s2[m_eff - 1] - (s2[m_eff] if m_eff < len(s2) else 0.0)
+    K = len(members)
+    ratio = np.linalg.norm(oracle.values(canon)) / max(np.linalg.norm(e["delta"]), 1e-300)
+    fac = 8 * math.sqrt(spec.n_tokens) + 4 * (K + 2) * ratio
+    e["eps_sub"] = fac * 2.0 ** -24 * s2.sum() / gap if gap > 0 else math.inf
+    e["full_rank"] = spec.m <= len(s2) and gap > 0 and s2[m_eff - 1] > 0
+    return e
+
+
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -223,3 +223,91 @@ def test_zero_token_chunks_are_skipped():
     assert _compile(m, ch, n=2) == kb.KAMERA_ERR_WORKSPACE
     assert kb.kamera_compile_workspace_bytes(m, ch, 2) == kb.kamera_compile_workspace_bytes(
         m, _chunks(m), 1)
+
+
+# ---- orbit compile -------------------------------------------------------------------------
+
+def _orbit(model, n=1, n_members=3, n_tokens=300, m=16):
+    """n well-formed orbit chunks in the fake address space, each with n_members orderings."""
+    plain = _chunks(model, n=n, n_tokens=n_tokens, m=m)
+    arr = (kb.KameraOrbitChunk * max(1, n))()
+    keep = []
+    slot = 10_000
+    for i in range(n):
+        k = arr[i]
+        k.n_tokens, k.m, k.n_members = n_tokens, m, n_members
+        mem = (kb.KameraOrbitMember * max(1, n_members))()
+        for q in range(n_members):
+            mem[q].delta = 10 * q
+            for ch in range(2):
+                slot += 1
+                row = _row(model, ch)
+                mem[q].conditioned[ch] = kb.KameraSrc(FAKE + slot * GiB, n_tokens * row, row)
+        keep.append(mem)
+        k.members = ctypes.cast(mem, ctypes.POINTER(kb.KameraOrbitMember))
+        for ch in range(2):
+            k.canonical[ch] = plain[i].canonical[ch]
+            k.out[ch] = plain[i].out[ch]
+    arr._keep = (keep, plain)
+    return arr
+
+
+def _orbit_call(model, chunks, n=1, n_iter=8):
+    return kb.kamera_patch_compile_orbit(model, chunks, n, n_iter, None, 0, None)
+
+
+def test_orbit_struct_layout():
+    assert ctypes.sizeof(kb.KameraOrbitMember) == 8 + 16 + 2 * 24
+    assert ctypes.sizeof(kb.KameraOrbitChunk) == 16 + 8 + 2 * 24 + 2 * 48
+
+
+def test_orbit_well_formed_call_reaches_the_workspace_check():
+    m = _model()
+    assert _orbit_call(m, _orbit(m)) == kb.KAMERA_ERR_WORKSPACE
+    mla = _mla()
+    assert _orbit_call(mla, _orbit(mla, m=32)) == kb.KAMERA_ERR_WORKSPACE
+
+
+def test_orbit_of_one_ordering_sizes_like_the_compile():
+    m = _model()
+    one = _orbit(m, n_members=1)
+    plain = _chunks(m)
+    assert kb.kamera_orbit_compile_workspace_bytes(m, one, 1) == \
+        kb.kamera_compile_workspace_bytes(m, plain, 1)
+    more = _orbit(m, n_members=6)
+    # only the member table grows (48 bytes per ordering and channel), rounded to 256
+    assert 0 <= kb.kamera_orbit_compile_workspace_bytes(m, more, 1) - \
+        kb.kamera_compile_workspace_bytes(m, plain, 1) <= 1024
+
+
+@pytest.mark.parametrize("n_members", [0, -1, 65])
+def test_orbit_member_count(n_members):
+    m = _model()
+    ch = _orbit(m, n_members=3)
+    ch[0].n_members = n_members
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert "n_members" in kb.kamera_last_error()
+
+
+def test_orbit_member_problems():
+    m = _model()
+    ch = _orbit(m)
+    ch[0].members = None
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    ch = _orbit(m)
+    ch[0].members[1].conditioned[1].ptr = None
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    ch = _orbit(m)
+    ch[0].members[2].conditioned[0].ptr += 4               # misaligned rows
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_UNSUPPORTED
+    ch = _orbit(m)
+    ch[0].members[2].delta = 1 << 31
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    ch = _orbit(m)
+    ch[0].out[1].U = ch[0].members[1].conditioned[0].ptr   # output on a member's input
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_OVERLAP
+    ch = _orbit(m)
+    ch[0].n_tokens = 0                                      # skipped: members not read
+    ch[0].members = None
+    assert _orbit_call(m, ch) == kb.KAMERA_ERR_WORKSPACE
+    assert _orbit_call(m, ch, n_iter=0) == kb.KAMERA_ERR_INVALID_ARGUMENT

@@ -61,3 +61,18 @@ def test_rotation_invariance_of_the_check():
     m = case.chunks[0].m
     R, _ = np.linalg.qr(np.random.default_rng(3).standard_normal((m, m)))
     assert cc.check_head(e["U"] @ R, e["V"] @ R, e, case.dtype).ok
+
+
+def test_orbit_checker_accepts_the_oracle_and_rejects_one_ordering():
+    """The orbit tolerance passes the oracle's own orbit factors (rounded to bf16) and fails
+    the plain compile of a single ordering (which is not the orbit patch)."""
+    case = cc.Case("orbit_check", "gqa", "bf16", 1, 1, 64, 64, oracle.HALF_SPLIT, 1e4,
+                   [cc.ChunkSpec(120, 8, 0)], seed=5)
+    inp = cc.build_orbit(case, [0, 700, 1400, -300], own_level=0.3)
+    e = cc.expected_orbit(case, inp, 0, 0, 0)
+    U = cc.decode(oracle.to_bf16(e["U"]), "bf16")
+    V = cc.decode(oracle.to_bf16(e["V"]), "bf16")
+    assert cc.check_head(U, V, e, "bf16").ok
+    one = oracle.compile_patch(inp["conditioned"][1][0][0], inp["canonical"][0][0], m=8,
+                               rotate=True, delta=700, theta=1e4)
+    assert not cc.check_head(one["U"], one["V"], e, "bf16").ok
