@@ -314,6 +314,49 @@ kamera_status kamera_patch_compile_orbit(const kamera_model* model,
                                          int32_t n_iter, void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* ---- Consumer side: decode attention and the state merge ----------------------------------
+ * The abstract states that the direct readout of a cached chunk is recovered exactly by the
+ * standard state merge: attention of a query over several chunks equals the log-sum-exp
+ * weighted combination of its attention over each. These calls read the relocated cache.
+ *
+ * kamera_decode_attention: one layer of a GQA/MHA bf16 cache (head_dim 64 or 128). Query j
+ * (n_q_heads heads of head_dim bf16 values at q + j*n_q_heads*head_dim, device) attends to
+ * logical cache tokens [kv_start_j, kv_start_j + kv_len_j) through the page table, with
+ * scores scale * <q_h, k_t>; query head h reads KV head h / (n_q_heads / n_kv_heads) (at
+ * most 16 query heads per KV head). Per query head it writes
+ *     out[(j*n_q_heads + h)*head_dim + f] = sum_t softmax(scores)_t v_tf      (fp32)
+ *     lse[j*n_q_heads + h] = log sum_t exp(score_t)                          (fp32, natural)
+ * (out = 0 and lse = -inf when kv_len == 0). The key range is cut into 512-token segments;
+ * each is attended on its own (Q K^T with bf16 MFMA, exact products; the weights stay fp32
+ * for P V, fp32 MFMA) and the segments are combined with the state merge. Tokens whose page
+ * table entry lies outside [0, n_pages) are left out (masked). */
+typedef struct kamera_attn_query {
+  int32_t kv_start;  /* first logical cache token attended, >= 0 */
+  int32_t kv_len;    /* tokens attended, >= 0 */
+} kamera_attn_query;
+
+#define KAMERA_ATTN_SEGMENT 512
+
+/* Workspace bytes for kamera_decode_attention (0 on invalid arguments). */
+size_t kamera_attention_workspace_bytes(const kamera_model* model, int32_t n_q_heads,
+                                        const kamera_attn_query* queries, int32_t n_queries);
+
+kamera_status kamera_decode_attention(const kamera_model* model, const kamera_cache* cache,
+                                      int32_t layer, const void* q, int32_t n_q_heads,
+                                      const kamera_attn_query* queries, int32_t n_queries,
+                                      float scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* The standard state merge of n_parts attention states over disjoint key sets (device, fp32):
+ *     part_out [n_parts][n_rows][head_dim], part_lse [n_parts][n_rows]
+ *  -> out [n_rows][head_dim], lse [n_rows]:
+ *     L = log sum_i exp(lse_i),  out = sum_i exp(lse_i - L) part_out_i.
+ * Parts with lse = -inf drop out; a row whose parts are all empty gives out = 0, lse = -inf.
+ * out and lse must not overlap the inputs. head_dim <= 1024; no workspace. */
+kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_dim,
+                                 const float* part_out, const float* part_lse, float* out,
+                                 float* lse, void* stream);
+
 const char* kamera_status_string(kamera_status status);
 const char* kamera_last_error(void); /* per-thread; "" if none */
 int32_t kamera_version(void);

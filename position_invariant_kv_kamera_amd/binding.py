@@ -76,6 +76,11 @@ class KameraCompileChunk(ctypes.Structure):
 
 COMPILE_MAX_RANK = 64
 ORBIT_MAX_MEMBERS = 64
+ATTN_SEGMENT = 512
+
+
+class KameraAttnQuery(ctypes.Structure):
+    _fields_ = [("kv_start", c_i32), ("kv_len", c_i32)]
 
 
 class KameraOrbitMember(ctypes.Structure):
@@ -135,6 +140,16 @@ def load_library() -> ctypes.CDLL:
                                                ctypes.POINTER(KameraOrbitChunk), c_i32, c_i32,
                                                c_vp, c_size, c_vp]
     lib.kamera_patch_compile_orbit.restype = ctypes.c_int
+    lib.kamera_attention_workspace_bytes.argtypes = [ctypes.POINTER(KameraModel), c_i32,
+                                                     ctypes.POINTER(KameraAttnQuery), c_i32]
+    lib.kamera_attention_workspace_bytes.restype = c_size
+    lib.kamera_decode_attention.argtypes = [ctypes.POINTER(KameraModel),
+                                            ctypes.POINTER(KameraCache), c_i32, c_vp, c_i32,
+                                            ctypes.POINTER(KameraAttnQuery), c_i32,
+                                            ctypes.c_float, c_vp, c_vp, c_vp, c_size, c_vp]
+    lib.kamera_decode_attention.restype = ctypes.c_int
+    lib.kamera_state_merge.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.kamera_state_merge.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -227,6 +242,25 @@ def kamera_patch_compile_orbit(model, chunks, n_chunks, n_iter, workspace, works
     return int(load_library().kamera_patch_compile_orbit(
         ctypes.byref(model) if model is not None else None, chunks, int(n_chunks), int(n_iter),
         workspace, int(workspace_bytes), stream))
+
+
+def kamera_attention_workspace_bytes(model, n_q_heads, queries, n_queries) -> int:
+    return int(load_library().kamera_attention_workspace_bytes(
+        ctypes.byref(model) if model is not None else None, int(n_q_heads), queries,
+        int(n_queries)))
+
+
+def kamera_decode_attention(model, cache, layer, q, n_q_heads, queries, n_queries, scale, out,
+                            lse, workspace, workspace_bytes, stream):
+    return int(load_library().kamera_decode_attention(
+        ctypes.byref(model) if model is not None else None,
+        ctypes.byref(cache) if cache is not None else None, int(layer), q, int(n_q_heads),
+        queries, int(n_queries), float(scale), out, lse, workspace, int(workspace_bytes), stream))
+
+
+def kamera_state_merge(n_parts, n_rows, head_dim, part_out, part_lse, out, lse, stream):
+    return int(load_library().kamera_state_merge(int(n_parts), int(n_rows), int(head_dim),
+                                                 part_out, part_lse, out, lse, stream))
 
 
 # ---- marshalling of torch tensors (workloads.Batch) into descriptors --------------------
@@ -422,3 +456,33 @@ def run_orbit_compile(model: KameraModel, items, *, n_iter: int = 8,
     s = current_stream_ptr() if stream is None else stream
     check(kamera_patch_compile_orbit(model, chunks, len(items), n_iter, ws.ptr, ws.nbytes, s))
     return ws
+
+
+# ---- consumer side ---------------------------------------------------------------------------
+
+def attn_queries_of(ranges):
+    """A KameraAttnQuery array from (kv_start, kv_len) pairs."""
+    arr = (KameraAttnQuery * max(1, len(ranges)))()
+    for i, (a, n) in enumerate(ranges):
+        arr[i] = KameraAttnQuery(int(a), int(n))
+    return arr
+
+
+def run_decode_attention(model: KameraModel, cache: KameraCache, layer: int, q, ranges, scale,
+                         *, stream=None):
+    """kamera_decode_attention of q ([n_queries, n_q_heads, head_dim] bf16 device tensor) over
+    the given (kv_start, kv_len) ranges; returns (out [n, heads, D] fp32, lse [n, heads])."""
+    import torch
+    n, heads, D = q.shape
+    queries = attn_queries_of(ranges)
+    need = kamera_attention_workspace_bytes(model, heads, queries, n)
+    if need == 0:
+        raise KameraError(KAMERA_ERR_INVALID_ARGUMENT, kamera_last_error())
+    ws = Workspace(nbytes=need, device=q.device)
+    out = torch.empty((n, heads, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((n, heads), dtype=torch.float32, device=q.device)
+    s = current_stream_ptr() if stream is None else stream
+    check(kamera_decode_attention(model, cache, layer, q.data_ptr(), heads, queries, n, scale,
+                                  out.data_ptr(), lse.data_ptr(), ws.ptr, ws.nbytes, s))
+    out._kamera_ws = ws                # keep the workspace alive until the caller syncs
+    return out, lse

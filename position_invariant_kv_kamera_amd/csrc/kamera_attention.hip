@@ -1,0 +1,452 @@
+// kamera_attention.hip — the consumer side on gfx950: decode attention over the relocated,
+// paged KV cache, and the standard state merge.
+//
+// The Kamera abstract states that the direct readout of a cached chunk is recovered exactly
+// by the standard state merge: attention over several key sets equals the log-sum-exp
+// weighted combination of the attention over each. Decode attention is built on it: each
+// 512-token segment of a query's key range is one block, attended on its own, and the
+// segments are merged.
+//
+// attn_segment_kernel<D>: block = (segment, KV head), 4 waves; wave w takes the 16-token
+//   tiles w, w+4, ... of the segment. Per tile: S = Q K^T with v_mfma_f32_16x16x32_bf16 (the
+//   query heads of the KV head are the 16 MFMA rows, padded; q and k are bf16 already, so
+//   the products are exact), online softmax per query row (max and sum across the 16 lanes
+//   that hold a row), then O += P V with v_mfma_f32_16x16x4_f32 (P stays fp32; the V tile
+//   passes through LDS as bf16). The four waves' states are merged in LDS and the segment's
+//   normalised output and lse are written to the workspace.
+// attn_merge_kernel: one block per (query, query head) merges its segments.
+// state_merge_kernel: the same merge over caller-given parts.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "kamera_internal.h"
+
+using namespace kamera::host;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSeg = KAMERA_ATTN_SEGMENT;
+constexpr int kThreads = 256;
+constexpr int kTile = 16;
+constexpr int kMaxGroup = 16;
+
+struct alignas(16) AQuery {
+  int32_t kv_start, kv_len, seg_start, n_segs;
+};
+
+struct AParams {
+  const AQuery* queries;
+  const int32_t* seg_query;   // owning query of each segment
+  const uint16_t* q;          // [n_queries][n_q][D]
+  const uint16_t* kpool;      // the layer's K pool
+  const uint16_t* vpool;      // the layer's V pool
+  const int32_t* page_table;  // or NULL (identity)
+  float* part_o;              // [segments][n_q][D]
+  float* part_lse;            // [segments][n_q]
+  float* out;
+  float* lse;
+  int64_t pool_ts;
+  float scale;
+  int32_t n_queries, n_q, n_kv, group, page_size, page_shift, n_pages;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Element offset of logical token p's row in a pool, or -1 when its page is outside the pool.
+__device__ __forceinline__ int64_t row_of(const AParams& P, int64_t p) {
+  int64_t page, slot;
+  if (P.page_shift >= 0) {
+    page = p >> P.page_shift;
+    slot = p & ((int64_t(1) << P.page_shift) - 1);
+  } else {
+    page = p / P.page_size;
+    slot = p - page * P.page_size;
+  }
+  const int64_t phys = P.page_table ? (int64_t)P.page_table[page] : page;
+  if (phys < 0 || phys >= P.n_pages) return -1;
+  return (phys * P.page_size + slot) * P.pool_ts;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
+  constexpr int KS = D / 32;   // bf16 MFMA k-steps of Q K^T
+  constexpr int NC = D / 16;   // 16-feature column blocks of O
+  constexpr int VS = D + 8;    // LDS row stride of a V tile (bf16): rows start in distinct banks
+  constexpr int PS = 17;       // LDS row stride of a P tile (fp32)
+  __shared__ __align__(16) uint16_t vt[4][kTile * VS];
+  __shared__ float pt[4][kTile * PS];
+  __shared__ float mrg_m[4][kMaxGroup], mrg_l[4][kMaxGroup];
+  __shared__ float mrg_o[4][kMaxGroup * D];
+
+  const int g = blockIdx.x / P.n_kv;
+  const int h = blockIdx.x - g * P.n_kv;
+  const int j = P.seg_query[g];
+  const AQuery Q = P.queries[j];
+  const int s = g - Q.seg_start;
+  const int t_lo = Q.kv_start + s * kSeg;
+  const int t_hi = min(Q.kv_start + Q.kv_len, t_lo + kSeg);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Q rows: query heads h*group + col (rows past the group are zero)
+  bf16x8 qa[KS];
+  {
+    const bool on = col < P.group;
+    const uint16_t* qp = P.q + ((int64_t)j * P.n_q + h * P.group + (on ? col : 0)) * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const u32x4 w = on ? *reinterpret_cast<const u32x4*>(qp + 32 * k + 8 * grp)
+                         : u32x4{0u, 0u, 0u, 0u};
+      qa[k] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  float m[4], l[4];
+  f32x4 o[NC];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int koff = h * D;
+  for (int t0 = t_lo + kTile * wave; t0 < t_hi; t0 += 4 * kTile) {
+    const int tok = t0 + col;
+    const int64_t row = tok < t_hi ? row_of(P, tok) : -1;
+    bf16x8 kb[KS];
+    u32x4 vraw[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (row >= 0) {
+        kb[k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(P.kpool + row + koff + 32 * k + 8 * grp));
+        vraw[k] = *reinterpret_cast<const u32x4*>(P.vpool + row + koff + 32 * k + 8 * grp);
+      } else {
+        kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        vraw[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // S: lane holds query rows 4 grp + r of token col
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], kb[k], sacc, 0, 0, 0);
+    // the V tile goes to LDS (token col, features 32k + 8 grp ..)
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = vraw[k];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sc = row >= 0 ? sacc[r] * P.scale : -INFINITY;
+      float mx = sc;
+      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mn = fmaxf(m[r], mx);
+      float corr = 1.f, p = 0.f;
+      if (mn != -INFINITY) {
+        corr = expf(m[r] - mn);
+        p = expf(sc - mn);
+      }
+      float sum = p;
+      sum += __shfl_xor(sum, 8, 16);
+      sum += __shfl_xor(sum, 4, 16);
+      sum += __shfl_xor(sum, 2, 16);
+      sum += __shfl_xor(sum, 1, 16);
+      l[r] = l[r] * corr + sum;
+      m[r] = mn;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c][r] *= corr;
+      pt[wave][(4 * grp + r) * PS + col] = p;
+    }
+    wave_lds_sync();
+    // O += P V: A[q][k] = P[q][4 k4 + k], B[k][f] = V[4 k4 + k][16 c + f]
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float a = pt[wave][col * PS + 4 * k4 + grp];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float b = bf16_lo(vt[wave][(4 * k4 + grp) * VS + 16 * c + col]);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o[c], 0, 0, 0);
+      }
+    }
+    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+  }
+
+  // merge the four waves' states (rows 4 grp + r of this lane; all 16 lanes of a row group
+  // hold the same m and l)
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * grp + r < kMaxGroup) {
+        mrg_m[wave][4 * grp + r] = m[r];
+        mrg_l[wave][4 * grp + r] = l[r];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mrg_o[wave][(4 * grp + r) * D + 16 * c + col] = o[c][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < P.group * D; idx += kThreads) {
+    const int rw = idx / D, f = idx - rw * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e = expf(mrg_m[w][rw] - M);
+        L += mrg_l[w][rw] * e;
+        acc += mrg_o[w][rw * D + f] * e;
+      }
+    }
+    const int64_t orow = (int64_t)g * P.n_q + h * P.group + rw;
+    P.part_o[orow * D + f] = M == -INFINITY ? 0.f : acc / L;
+    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M + logf(L);
+  }
+}
+
+// Merge n parts of one row: lse of part i at lse_p[i * lse_stride], its output at
+// o_p + i * o_stride. Writes out[0 .. D) and *lse_out.
+__device__ void merge_row(const float* lse_p, int64_t lse_stride, const float* o_p,
+                          int64_t o_stride, int n, int D, float* out, float* lse_out) {
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, lse_p[i * lse_stride]);
+  float Z = 0.f;
+  if (M != -INFINITY)
+    for (int i = 0; i < n; ++i) Z += expf(lse_p[i * lse_stride] - M);
+  for (int f = threadIdx.x; f < D; f += blockDim.x) {
+    float acc = 0.f;
+    if (M != -INFINITY)
+      for (int i = 0; i < n; ++i) {
+        const float e = expf(lse_p[i * lse_stride] - M);
+        if (e != 0.f) acc += e * o_p[i * o_stride + f];
+      }
+    out[f] = M == -INFINITY ? 0.f : acc / Z;
+  }
+  if (threadIdx.x == 0) *lse_out = M == -INFINITY ? -INFINITY : M + logf(Z);
+}
+
+__global__ __launch_bounds__(64) void attn_merge_kernel(AParams P, int D) {
+  const int r = blockIdx.x;
+  const int j = r / P.n_q, qh = r - j * P.n_q;
+  const AQuery Q = P.queries[j];
+  const int64_t base = (int64_t)Q.seg_start * P.n_q + qh;
+  merge_row(P.part_lse + base, P.n_q, P.part_o + base * D, (int64_t)P.n_q * D, Q.n_segs, D,
+            P.out + (int64_t)r * D, P.lse + r);
+}
+
+__global__ __launch_bounds__(64) void state_merge_kernel(const float* part_out,
+                                                         const float* part_lse, float* out,
+                                                         float* lse, int n_parts, int n_rows,
+                                                         int D) {
+  const int r = blockIdx.x;
+  merge_row(part_lse + r, n_rows, part_out + (int64_t)r * D, (int64_t)n_rows * D, n_parts, D,
+            out + (int64_t)r * D, lse + r);
+}
+
+// ---------------------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------------------
+
+struct APlan {
+  std::vector<AQuery> queries;
+  std::vector<int32_t> seg_query;
+  size_t seg_off = 0, part_o_off = 0, part_lse_off = 0, total = 0;
+};
+
+kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
+                                 const kamera_attn_query* queries, int32_t n_queries,
+                                 int64_t capacity, APlan* plan) {
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  if (model->family != KAMERA_FAMILY_GQA)
+    return fail(KAMERA_ERR_UNSUPPORTED, "decode attention supports GQA/MHA caches");
+  if (model->dtype != KAMERA_DTYPE_BF16)
+    return fail(KAMERA_ERR_UNSUPPORTED, "decode attention supports bf16 caches");
+  if (model->head_dim != 64 && model->head_dim != 128)
+    return fail(KAMERA_ERR_UNSUPPORTED, "decode attention needs head_dim 64 or 128 (got %d)",
+                model->head_dim);
+  if (n_q_heads <= 0 || n_q_heads % model->n_kv_heads)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", n_q_heads,
+                model->n_kv_heads);
+  if (n_q_heads / model->n_kv_heads > kMaxGroup)
+    return fail(KAMERA_ERR_UNSUPPORTED, "more than %d query heads per KV head", kMaxGroup);
+  if (n_queries < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_queries must be >= 0");
+  if (n_queries > 0 && !queries) return fail(KAMERA_ERR_INVALID_ARGUMENT, "queries is NULL");
+  if ((int64_t)n_queries * n_q_heads > INT32_MAX)
+    return fail(KAMERA_ERR_UNSUPPORTED, "too many query rows");
+  int64_t segs = 0;
+  plan->queries.resize(n_queries);
+  for (int32_t i = 0; i < n_queries; ++i) {
+    const kamera_attn_query& a = queries[i];
+    if (a.kv_start < 0 || a.kv_len < 0)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "query %d: kv_start and kv_len must be >= 0", i);
+    if (capacity >= 0 && (int64_t)a.kv_start + a.kv_len > capacity)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                  "query %d: tokens [%d, %lld) run past the cache's %lld logical tokens", i,
+                  a.kv_start, (long long)a.kv_start + a.kv_len, (long long)capacity);
+    const int n = (a.kv_len + kSeg - 1) / kSeg;
+    plan->queries[i] = AQuery{a.kv_start, a.kv_len, (int32_t)segs, n};
+    for (int k = 0; k < n; ++k) plan->seg_query.push_back(i);
+    segs += n;
+  }
+  if (segs * model->n_kv_heads > INT32_MAX)
+    return fail(KAMERA_ERR_UNSUPPORTED, "too many attention segments");
+  const size_t D = model->head_dim;
+  plan->seg_off = round_up(plan->queries.size() * sizeof(AQuery), 16);
+  plan->part_o_off = round_up(plan->seg_off + plan->seg_query.size() * sizeof(int32_t), 256);
+  plan->part_lse_off = round_up(plan->part_o_off + segs * n_q_heads * D * sizeof(float), 256);
+  plan->total = round_up(plan->part_lse_off + segs * n_q_heads * sizeof(float), 256);
+  plan->total = std::max<size_t>(plan->total, 256);
+  return KAMERA_OK;
+}
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kamera_attention_workspace_bytes(const kamera_model* model, int32_t n_q_heads,
+                                        const kamera_attn_query* queries, int32_t n_queries) {
+  APlan plan;
+  if (attention_geometry(model, n_q_heads, queries, n_queries, -1, &plan) != KAMERA_OK) return 0;
+  return plan.total;
+}
+
+kamera_status kamera_decode_attention(const kamera_model* model, const kamera_cache* cache,
+                                      int32_t layer, const void* q, int32_t n_q_heads,
+                                      const kamera_attn_query* queries, int32_t n_queries,
+                                      float scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream_ptr) {
+  clear_error();
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  st = validate_cache(*model, cache);
+  if (st != KAMERA_OK) return st;
+  const int64_t capacity = (int64_t)cache->n_logical_pages * cache->page_size;
+  APlan plan;
+  st = attention_geometry(model, n_q_heads, queries, n_queries, capacity, &plan);
+  if (st != KAMERA_OK) return st;
+  if (layer < 0 || layer >= model->n_layers)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, model->n_layers);
+  if (!std::isfinite(scale)) return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (n_queries > 0 && (!q || !out || !lse))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "q, out and lse must not be NULL");
+  if (q && !aligned16(q)) return fail(KAMERA_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+  // 16-byte row loads from both pools
+  if (!aligned16(cache->pool[0]) || !aligned16(cache->pool[1]) || cache->token_stride % 8 ||
+      cache->layer_stride % 8)
+    return fail(KAMERA_ERR_UNSUPPORTED, "cache rows must start on 16-byte boundaries");
+  const size_t D = model->head_dim;
+  const size_t rows = (size_t)n_queries * n_q_heads;
+  if (n_queries > 0 && (ranges_overlap(out, rows * D * 4, lse, rows * 4) ||
+                        ranges_overlap(out, rows * D * 4, q, rows * D * 2) ||
+                        ranges_overlap(lse, rows * 4, q, rows * D * 2)))
+    return fail(KAMERA_ERR_OVERLAP, "q, out and lse must not overlap");
+  if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                plan.total);
+  if (n_queries == 0) return KAMERA_OK;
+
+  std::vector<uint8_t> table(plan.part_o_off, 0);
+  std::memcpy(table.data(), plan.queries.data(), plan.queries.size() * sizeof(AQuery));
+  if (!plan.seg_query.empty())
+    std::memcpy(table.data() + plan.seg_off, plan.seg_query.data(),
+                plan.seg_query.size() * sizeof(int32_t));
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  st = upload(table, workspace, stream);
+  if (st != KAMERA_OK) return st;
+
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  AParams P{};
+  P.queries = reinterpret_cast<const AQuery*>(base);
+  P.seg_query = reinterpret_cast<const int32_t*>(base + plan.seg_off);
+  P.q = static_cast<const uint16_t*>(q);
+  P.kpool = static_cast<const uint16_t*>(cache->pool[0]) + (int64_t)layer * cache->layer_stride;
+  P.vpool = static_cast<const uint16_t*>(cache->pool[1]) + (int64_t)layer * cache->layer_stride;
+  P.page_table = cache->page_table;
+  P.part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+  P.part_lse = reinterpret_cast<float*>(base + plan.part_lse_off);
+  P.out = out;
+  P.lse = lse;
+  P.pool_ts = cache->token_stride;
+  P.scale = scale;
+  P.n_queries = n_queries;
+  P.n_q = n_q_heads;
+  P.n_kv = model->n_kv_heads;
+  P.group = n_q_heads / model->n_kv_heads;
+  P.page_size = cache->page_size;
+  P.page_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if (cache->page_size == (1 << b)) P.page_shift = b;
+  P.n_pages = cache->n_pages;
+  const int64_t seg_blocks = (int64_t)plan.seg_query.size() * model->n_kv_heads;
+  if (seg_blocks > 0) {
+    const dim3 grid((unsigned)seg_blocks), block(kThreads);
+    if (D == 128) attn_segment_kernel<128><<<grid, block, 0, stream>>>(P);
+    else attn_segment_kernel<64><<<grid, block, 0, stream>>>(P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(KAMERA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
+  }
+  attn_merge_kernel<<<dim3((unsigned)rows), dim3(64), 0, stream>>>(P, (int)D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_dim,
+                                 const float* part_out, const float* part_lse, float* out,
+                                 float* lse, void* stream_ptr) {
+  clear_error();
+  if (n_parts < 0 || n_rows < 0)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_parts and n_rows must be >= 0");
+  if (head_dim <= 0 || head_dim > 1024)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "head_dim must be in [1, 1024] (got %d)", head_dim);
+  if (n_rows == 0) return KAMERA_OK;
+  if (!out || !lse || (n_parts > 0 && (!part_out || !part_lse)))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "NULL buffer");
+  const size_t po = (size_t)n_parts * n_rows * head_dim * 4, pl = (size_t)n_parts * n_rows * 4;
+  const size_t oo = (size_t)n_rows * head_dim * 4, ol = (size_t)n_rows * 4;
+  if (ranges_overlap(out, oo, lse, ol) || (n_parts > 0 && (ranges_overlap(out, oo, part_out, po) ||
+                                                           ranges_overlap(out, oo, part_lse, pl) ||
+                                                           ranges_overlap(lse, ol, part_out, po) ||
+                                                           ranges_overlap(lse, ol, part_lse, pl))))
+    return fail(KAMERA_ERR_OVERLAP, "out and lse must not overlap the parts or each other");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  state_merge_kernel<<<dim3((unsigned)n_rows), dim3(64), 0, stream>>>(part_out, part_lse, out, lse,
+                                                                       n_parts, n_rows, head_dim);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+}  // extern "C"

@@ -148,6 +148,7 @@ Range view_range(const void* p, int64_t ls, int64_t n_layers, int64_t ts, int64_
                  int64_t row_elems, int64_t esize);
 bool overlaps(const Range& a, const Range& b);
 kamera_status validate_model(const kamera_model* m);
+kamera_status validate_cache(const kamera_model& m, const kamera_cache* c);
 // Copies `bytes` into the device workspace through a pinned staging ring, on `stream`.
 kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream);
 int env_int(const char* name, int dflt);

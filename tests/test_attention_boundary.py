@@ -1,0 +1,100 @@
+"""Decode attention and the state merge at the C-ABI boundary, without a GPU: exports,
+sizing and host validation. Every call is rejected before anything is enqueued (a NULL
+workspace is the backstop for the attention call; the merge calls here all fail earlier)."""
+import ctypes
+import math
+
+import pytest
+
+from position_invariant_kv_kamera_amd import binding as kb
+
+FAKE = 0x7F0000000000
+GiB = 1 << 30
+
+
+def _model(**kw):
+    d = dict(family="gqa", dtype="bf16", n_layers=4, n_kv_heads=4, head_dim=128, rope_dim=128,
+             rope_layout="half_split", theta=1e6)
+    d.update(kw)
+    return kb.make_model(**d)
+
+
+def _cache(model):
+    c = kb.KameraCache()
+    row = model.n_kv_heads * model.head_dim
+    c.pool[0] = FAKE
+    c.pool[1] = FAKE + 8 * GiB
+    c.layer_stride = 1000 * 16 * row
+    c.token_stride = row
+    c.page_table = None
+    c.n_logical_pages = 1000
+    c.page_size = 16
+    c.n_pages = 1000
+    return c
+
+
+def _call(model=None, cache=None, layer=0, n_q_heads=28, ranges=((0, 100),), scale=0.088,
+          q=FAKE + 20 * GiB, out=FAKE + 21 * GiB, lse=FAKE + 22 * GiB):
+    model = model or _model()
+    cache = cache or _cache(model)
+    qs = kb.attn_queries_of(ranges)
+    return kb.kamera_decode_attention(model, cache, layer, q, n_q_heads, qs, len(ranges), scale,
+                                      out, lse, None, 0, None)
+
+
+def test_exports_and_layout():
+    names = set(kb.header_functions())
+    assert {"kamera_decode_attention", "kamera_state_merge",
+            "kamera_attention_workspace_bytes"} <= names
+    assert ctypes.sizeof(kb.KameraAttnQuery) == 8
+
+
+def test_well_formed_call_reaches_the_workspace_check():
+    assert _call() == kb.KAMERA_ERR_WORKSPACE
+    assert _call(_model(head_dim=64, rope_dim=64), n_q_heads=16) == kb.KAMERA_ERR_WORKSPACE
+
+
+def test_workspace_bytes():
+    m = _model()
+    qs = kb.attn_queries_of([(0, 1000), (5, 0), (0, 512)])
+    need = kb.kamera_attention_workspace_bytes(m, 28, qs, 3)
+    segs = 2 + 0 + 1
+    assert need >= segs * 28 * 128 * 4 + segs * 28 * 4
+    assert need % 256 == 0
+    assert kb.kamera_attention_workspace_bytes(m, 27, qs, 3) == 0       # not a multiple of 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(model=_model(family="mla", n_kv_heads=1, head_dim=512, rope_dim=64)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(dtype="f32")), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(head_dim=96, rope_dim=96)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=30), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(n_q_heads=68), kb.KAMERA_ERR_UNSUPPORTED),                  # 17 per KV head
+    (dict(layer=4), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(layer=-1), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(ranges=((-1, 10),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(ranges=((0, -1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(ranges=((15990, 11),)), kb.KAMERA_ERR_INVALID_ARGUMENT),    # past 16000 tokens
+    (dict(scale=math.inf), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 20 * GiB + 2), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(lse=FAKE + 21 * GiB + 64), kb.KAMERA_ERR_OVERLAP),          # lse inside out
+])
+def test_validation(kw, status):
+    assert _call(**kw) == status
+    assert kb.kamera_last_error()
+
+
+def test_zero_queries_and_empty_ranges_are_valid():
+    assert _call(ranges=()) == kb.KAMERA_ERR_WORKSPACE
+    assert _call(ranges=((7, 0),)) == kb.KAMERA_ERR_WORKSPACE
+
+
+def test_state_merge_validation():
+    P, O, L, R = FAKE, FAKE + GiB, FAKE + 2 * GiB, FAKE + 3 * GiB
+    assert kb.kamera_state_merge(-1, 4, 128, P, L, O, R, None) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert kb.kamera_state_merge(2, 4, 0, P, L, O, R, None) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert kb.kamera_state_merge(2, 4, 2048, P, L, O, R, None) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert kb.kamera_state_merge(2, 4, 128, None, L, O, R, None) == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert kb.kamera_state_merge(2, 4, 128, P, L, P + 64, R, None) == kb.KAMERA_ERR_OVERLAP
+    assert kb.kamera_state_merge(2, 0, 128, None, None, None, None, None) == kb.KAMERA_OK

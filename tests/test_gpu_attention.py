@@ -1,0 +1,185 @@
+"""Decode attention over the paged cache and the state merge on the GPU (through the C ABI)
+against the fp64 oracle (oracle/attention.py).
+
+The cache is filled directly with seeded bf16 values (the attention reads whatever the
+relocation wrote; its own inputs do not come from the HIP path here).
+
+Tolerance (derived): the scores' products are exact (bf16 x bf16) and summed in fp32 over D
+terms, so |ds_t| <= eps_s = 2 D 2^-24 max_t(scale sum_d |q_d k_td|) + 2^-24 max|s|; the
+softmax weights then carry a relative error <= 2 eps_s + c u (u = 2^-24, c = 64 + number of
+16-token tiles for the fp32 exp, running sums and the merges), so
+    |o_g - o|_f <= (2 eps_s + c u) sum_t w_t |v_tf|,   |lse_g - lse| <= eps_s + c u (1 + |lse|).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from position_invariant_kv_kamera_amd import binding as kb
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def _bits_to_f64(t):
+    b = t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Setup:
+    def __init__(self, n_layers=2, n_kv=4, D=128, page_size=16, n_pages=320, n_logical=300,
+                 shuffled=True, bad_pages=(), seed=0):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.D, self.n_kv, self.ps = D, n_kv, page_size
+        row = n_kv * D
+        self.pools = [torch.randn((n_layers, n_pages, page_size, row), generator=g,
+                                  device="cuda").to(torch.bfloat16) for _ in range(2)]
+        rng = np.random.default_rng(seed)
+        self.table = None
+        if shuffled:
+            t = rng.permutation(n_pages)[:n_logical].astype(np.int32)
+            for b in bad_pages:
+                t[b] = n_pages + 3                      # outside the pool: masked
+            self.table = t
+            self.table_dev = torch.from_numpy(t).cuda()
+        self.model = kb.make_model("gqa", "bf16", n_layers, n_kv, D, D, "half_split", 1e6)
+        c = kb.KameraCache()
+        c.pool[0] = self.pools[0].data_ptr()
+        c.pool[1] = self.pools[1].data_ptr()
+        c.layer_stride = self.pools[0].stride(0)
+        c.token_stride = row
+        c.page_table = None if self.table is None else self.table_dev.data_ptr()
+        c.n_logical_pages = n_logical
+        c.page_size = page_size
+        c.n_pages = n_pages
+        self.cache = c
+        self.host = [_bits_to_f64(p) for p in self.pools]      # [L, pages, ps, row]
+        self.n_pages = n_pages
+
+    def rows(self, layer, ch, start, n):
+        """Rows of logical tokens [start, start + n) whose page is inside the pool."""
+        p = np.arange(start, start + n)
+        page, slot = p // self.ps, p % self.ps
+        phys = page if self.table is None else self.table[page].astype(np.int64)
+        ok = (phys >= 0) & (phys < self.n_pages)
+        return self.host[ch][layer][phys[ok], slot[ok]]
+
+
+def _expect(setup, layer, q64, start, n, n_q, scale):
+    """Oracle (o, lse, o_tol, lse_tol) for one query: q64 [n_q, D]."""
+    D, G = setup.D, n_q // setup.n_kv
+    K, V = setup.rows(layer, 0, start, n), setup.rows(layer, 1, start, n)
+    o = np.zeros((n_q, D))
+    lse = np.full(n_q, -np.inf)
+    otol = np.zeros((n_q, D))
+    ltol = np.zeros(n_q)
+    tiles = -(-max(n, 1) // 16)
+    c = 64 + tiles
+    for h in range(setup.n_kv):
+        qh = q64[h * G:(h + 1) * G]
+        Kh, Vh = K[:, h * D:(h + 1) * D], V[:, h * D:(h + 1) * D]
+        oh, lh = att.decode_attention(qh, Kh, Vh, scale)
+        o[h * G:(h + 1) * G], lse[h * G:(h + 1) * G] = oh, lh
+        if Kh.shape[0]:
+            s = scale * qh @ Kh.T
+            eps = 2 * D * U * att.score_bounds(qh, Kh, scale).max(axis=1) + U * np.abs(s).max(axis=1)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            w /= w.sum(axis=1, keepdims=True)
+            otol[h * G:(h + 1) * G] = (2 * eps + c * U)[:, None] * (w @ np.abs(Vh))
+            ltol[h * G:(h + 1) * G] = eps + c * U * (1 + np.abs(lh))
+    return o, lse, otol, ltol
+
+
+def _run_and_check(setup, layer, ranges, n_q, scale, seed=1):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randn((len(ranges), n_q, setup.D), generator=g, device="cuda").to(torch.bfloat16)
+    print(f"[attn] D={setup.D} n_q={n_q} ranges={list(ranges)[:6]}... layer={layer}", flush=True)
+    out, lse = kb.run_decode_attention(setup.model, setup.cache, layer, q, ranges, scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    q64 = _bits_to_f64(q)
+    worst = 0.0
+    for j, (a, n) in enumerate(ranges):
+        o, l, otol, ltol = _expect(setup, layer, q64[j], a, n, n_q, scale)
+        if np.all(np.isneginf(l)):
+            assert np.all(out[j] == 0) and np.all(np.isneginf(lse[j])), f"query {j}: empty range"
+            continue
+        err = np.abs(out[j] - o)
+        assert np.all(err <= otol + 1e-30), (j, float((err / (otol + 1e-30)).max()))
+        lerr = np.abs(lse[j] - l)
+        assert np.all(lerr <= ltol), (j, float((lerr / ltol).max()))
+        worst = max(worst, float((err / (otol + 1e-30)).max()), float((lerr / ltol).max()))
+    print(f"[attn] worst error / tolerance {worst:.3g}", flush=True)
+    return out, lse
+
+
+RANGES = [(0, 1), (0, 17), (5, 511), (0, 512), (3, 513), (100, 2000), (0, 4096), (7, 0),
+          (4000, 800)]
+
+
+def test_decode_attention_paged_shuffled_gqa7():
+    s = Setup()
+    _run_and_check(s, 1, RANGES, 28, 1 / math.sqrt(128))
+
+
+def test_decode_attention_head64_group8_dense_odd_pages():
+    s = Setup(D=64, n_kv=2, page_size=12, n_pages=400, n_logical=400, shuffled=False, seed=3)
+    _run_and_check(s, 0, [(0, 4800), (11, 13), (1000, 1025)], 16, 0.125, seed=4)
+
+
+def test_decode_attention_mha_one_head_per_kv():
+    s = Setup(n_kv=8, n_pages=64, n_logical=64, seed=5)
+    _run_and_check(s, 0, [(0, 1024), (16, 300)], 8, 1 / math.sqrt(128), seed=6)
+
+
+def test_pages_outside_the_pool_are_masked():
+    s = Setup(bad_pages=(2, 3, 40), seed=7)
+    _run_and_check(s, 0, [(0, 100), (20, 700), (32, 16)], 28, 0.09, seed=8)
+
+
+def test_state_merge_of_segments_equals_attention_over_the_whole():
+    """The state-merge identity on the device: attention over [0, 1500) equals the merge of
+    the attention over [0, 700) and [700, 1500) (both checked against the oracle)."""
+    s = Setup(seed=9)
+    n_q, scale = 28, 1 / math.sqrt(128)
+    whole_o, whole_l = _run_and_check(s, 0, [(0, 1500)], n_q, scale, seed=10)
+    a_o, a_l = _run_and_check(s, 0, [(0, 700)], n_q, scale, seed=10)
+    b_o, b_l = _run_and_check(s, 0, [(700, 800)], n_q, scale, seed=10)
+    part_o = torch.from_numpy(np.stack([a_o, b_o]).astype(np.float32)).cuda()   # [2, 1, n_q, D]
+    part_l = torch.from_numpy(np.stack([a_l, b_l]).astype(np.float32)).cuda()
+    out = torch.empty((n_q, s.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_q,), dtype=torch.float32, device="cuda")
+    kb.check(kb.kamera_state_merge(2, n_q, s.D, part_o.data_ptr(), part_l.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr(), kb.current_stream_ptr()))
+    torch.cuda.synchronize()
+    ref_o, ref_l = att.state_merge([a_o[0], b_o[0]], [a_l[0], b_l[0]])
+    np.testing.assert_allclose(out.cpu().numpy(), ref_o, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_l, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(out.cpu().numpy(), whole_o[0], rtol=0, atol=2e-5)
+    np.testing.assert_allclose(lse.cpu().numpy(), whole_l[0], rtol=0, atol=2e-5)
+
+
+def test_state_merge_with_empty_parts():
+    rows, D = 5, 64
+    rng = np.random.default_rng(12)
+    po = rng.standard_normal((3, rows, D)).astype(np.float32)
+    pl = rng.standard_normal((3, rows)).astype(np.float32)
+    pl[1, :] = -np.inf                      # part 1 empty everywhere
+    pl[:, 4] = -np.inf                      # row 4 empty in every part
+    po[1, :] = 0
+    po[:, 4] = 0
+    dpo, dpl = torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda()
+    out = torch.empty((rows, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    kb.check(kb.kamera_state_merge(3, rows, D, dpo.data_ptr(), dpl.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), kb.current_stream_ptr()))
+    torch.cuda.synchronize()
+    ref_o, ref_l = att.state_merge(list(po.astype(np.float64)), list(pl.astype(np.float64)))
+    np.testing.assert_allclose(out.cpu().numpy(), ref_o, rtol=0, atol=1e-5)
+    got_l = lse.cpu().numpy()
+    assert np.isneginf(got_l[4]) and np.all(out.cpu().numpy()[4] == 0)
+    np.testing.assert_allclose(got_l[:4], ref_l[:4], rtol=0, atol=1e-5)
