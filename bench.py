@@ -6,7 +6,9 @@ scatter, for every chunk, layer, channel and head. Inputs are resident in HBM be
 
 Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s). The
 line also carries "patch_compile": the time kamera_patch_compile takes to form the same
-batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass.
+batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass, and
+"decode_attention": the consumer-side decode attention (with its state merge) on a
+64-sequence x 16K-token paged cache.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--compile-steps N]
 """
@@ -124,7 +126,7 @@ def cpu_baseline(batch, budget_s: float) -> dict:
 FP32_PEAK_TFLOPS = 157.3       # dense fp32 (MFMA and vector alike)
 
 
-def compile_leg(p, batch, reuse_ms: float, steps: int, stream) -> dict:
+def compile_leg(p, batch, reuse_ms: float, steps: int, stream, orbit_steps: int = 2) -> dict:
     """Time kamera_patch_compile over the same chunks (one step = the whole batch's patches at
     the workload's largest rank). The conditioned KV is the canonical KV plus Gaussian noise;
     the compile does the same work whatever the values."""
@@ -167,6 +169,15 @@ def compile_leg(p, batch, reuse_ms: float, steps: int, stream) -> dict:
     floor_ms = max(io_bytes / (HBM_PEAK_GBPS * 1e9),
                    (gram_flops + proj_flops) / (FP32_PEAK_TFLOPS * 1e12)) * 1e3
 
+    result = {"ms_per_batch": round(ms, 3), "steps": steps, "rank": m, "n_iter": n_iter,
+              "input_bytes": in_bytes, "reuse_ms_per_batch": round(reuse_ms, 4),
+              "compile_over_reuse": round(ms / reuse_ms, 2), "io_bytes": io_bytes,
+              "gram_flops": gram_flops, "project_flops": proj_flops,
+              "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4),
+              "floor": "max(bytes / 8 TB/s, (Gram + projection flops) / 157.3 TFLOP/s fp32)",
+              "timed_with": "hip events on the launch stream"}
+    if orbit_steps <= 0:
+        return result
     # orbit patch over 3 orderings per chunk (each ordering's conditioned rows are one more
     # input per streaming pass)
     K = 3
@@ -183,24 +194,76 @@ def compile_leg(p, batch, reuse_ms: float, steps: int, stream) -> dict:
     ows = kb.run_orbit_compile(model, orbit_items, n_iter=n_iter)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(max(1, steps // 2)):
+    for _ in range(orbit_steps):
         kb.run_orbit_compile(model, orbit_items, n_iter=n_iter, workspace=ows,
                              stream=stream.cuda_stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    orbit_ms = e0.elapsed_time(e1) / max(1, steps // 2)
+    orbit_ms = e0.elapsed_time(e1) / orbit_steps
     orbit_io = io_bytes + 2 * (K - 1) * in_bytes // 2
     del orbit_items, ows
-    return {"ms_per_batch": round(ms, 3), "steps": steps, "rank": m, "n_iter": n_iter,
-            "input_bytes": in_bytes,
-            "reuse_ms_per_batch": round(reuse_ms, 4),
-            "compile_over_reuse": round(ms / reuse_ms, 2),
-            "io_bytes": io_bytes, "gram_flops": gram_flops, "project_flops": proj_flops,
-            "floor_ms": round(floor_ms, 3), "frac_of_floor": round(floor_ms / ms, 4),
-            "floor": "max(bytes / 8 TB/s, (Gram + projection flops) / 157.3 TFLOP/s fp32)",
-            "orbit": {"orderings": K, "ms_per_batch": round(orbit_ms, 3), "io_bytes": orbit_io,
-                      "ms_over_compile": round(orbit_ms / ms, 3)},
-            "timed_with": "hip events on the launch stream"}
+    result["orbit"] = {"orderings": K, "ms_per_batch": round(orbit_ms, 3), "io_bytes": orbit_io,
+                       "ms_over_compile": round(orbit_ms / ms, 3), "steps": orbit_steps}
+    return result
+
+
+def attention_leg(steps: int, stream) -> dict:
+    """Decode attention on one layer of a Qwen2.5-VL-7B-like cache (4 KV heads x 128, 28 query
+    heads): 64 sequences x 16384 tokens each, paged 16 with a shuffled page table, one query
+    token per sequence. Bytes = every K and V row read once."""
+    import numpy as np
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+
+    n_seq, ctx, n_kv, D, n_q, ps = 64, 16384, 4, 128, 28, 16
+    n_pages = n_seq * ctx // ps
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    row = n_kv * D
+    pools = [torch.randn((1, n_pages, ps, row), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(2)]
+    table = torch.from_numpy(np.random.default_rng(77).permutation(n_pages).astype(np.int32)).cuda()
+    model = kb.make_model("gqa", "bf16", 1, n_kv, D, D, "half_split", 1e6)
+    cache = kb.KameraCache()
+    cache.pool[0], cache.pool[1] = pools[0].data_ptr(), pools[1].data_ptr()
+    cache.layer_stride = pools[0].stride(0)
+    cache.token_stride = row
+    cache.page_table = table.data_ptr()
+    cache.n_logical_pages = n_pages
+    cache.page_size = ps
+    cache.n_pages = n_pages
+    q = torch.randn((n_seq, n_q, D), generator=g, device="cuda").to(torch.bfloat16)
+    ranges = [(i * ctx, ctx) for i in range(n_seq)]
+    queries = kb.attn_queries_of(ranges)
+    need = kb.kamera_attention_workspace_bytes(model, n_q, queries, n_seq)
+    ws = kb.Workspace(nbytes=need)
+    out = torch.empty((n_seq, n_q, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_seq, n_q), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        kb.check(kb.kamera_decode_attention(model, cache, 0, q.data_ptr(), n_q, queries, n_seq,
+                                            1.0 / D ** 0.5, out.data_ptr(), lse.data_ptr(),
+                                            ws.ptr, ws.nbytes, sp))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kv_bytes = 2 * n_seq * ctx * row * 2
+    gbps = kv_bytes / (ms * 1e-3) / 1e9
+    del pools, table, q, out, lse, ws
+    return {"shape": f"{n_seq} sequences x {ctx} tokens, {n_kv} KV heads x {D}, {n_q} query heads, "
+                     f"paged {ps} shuffled, one layer",
+            "ms_per_call": round(ms, 4), "kv_bytes": kv_bytes, "achieved_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": steps,
+            "timed_with": "hip events on the launch stream (segment + merge kernels)"}
 
 
 def _read_csv(path):
@@ -351,10 +414,38 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
     print(out_md.read_text())
 
 
+def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> None:
+    """profiles/decode_attention.md from a rocprofv3 --kernel-trace --stats run (named `kt`)
+    of bench.py and that run's JSON line."""
+    d = Path(prof_dir)
+    rec = [json.loads(l) for l in Path(bench_log).read_text().splitlines()
+           if l.startswith("{") and '"metric"' in l][-1]
+    da = rec["decode_attention"]
+    rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
+    seg = [r for r in rows if "attn_segment_kernel" in r["Name"]]
+    mrg = [r for r in rows if "attn_merge_kernel" in r["Name"]]
+    lines = ["# decode attention (consumer side)", "", "Commands (R = repository root on the GPU box):", ""]
+    lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
+    lines += [f"Shape: {da['shape']}. Bytes per call: K and V once = {da['kv_bytes'] / 1e9:.3f} GB.",
+              f"HIP events in this run: {da['ms_per_call']} ms per call (both kernels) = "
+              f"{da['achieved_gbps']} GB/s ({da['hbm_frac']} of 8 TB/s).", "",
+              "| kernel | calls | avg us | GB/s (K+V bytes / avg) | of 8 TB/s |", "|---|---|---|---|---|"]
+    for r in seg + mrg:
+        avg = float(r["AverageNs"])
+        gb = da["kv_bytes"] / avg if "segment" in r["Name"] else float("nan")
+        lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
+                     f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
+    out_md = ROOT / "profiles" / "decode_attention.md"
+    out_md.write_text("\n".join(lines) + "\n")
+    print(out_md.read_text())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 CSV output in DIR and exit")
+    ap.add_argument("--summarize-attention-profile", metavar="DIR",
+                    help="write the decode-attention summary from rocprofv3 CSV output in DIR and exit")
     ap.add_argument("--summarize-compile-profile", metavar="DIR",
                     help="write the patch-compile summary from rocprofv3 CSV output in DIR and exit")
     ap.add_argument("--profile-command", default="", help="commands recorded in the summary (';'-separated)")
@@ -367,7 +458,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--compile-steps", type=int, default=5,
                     help="timed kamera_patch_compile calls over the same batch (0: skip)")
+    ap.add_argument("--orbit-steps", type=int, default=2,
+                    help="timed orbit compiles (3 orderings) in the compile leg (0: skip)")
+    ap.add_argument("--attention-steps", type=int, default=20,
+                    help="timed kamera_decode_attention calls on a 64 x 16K decode (0: skip)")
     args = ap.parse_args()
+    if args.summarize_attention_profile:
+        summarize_attention_profile(args.summarize_attention_profile, args.profile_command,
+                                    args.profile_bench_log)
+        return
     if args.summarize_compile_profile:
         summarize_compile_profile(args.summarize_compile_profile, args.workload,
                                   args.profile_command, args.profile_bench_log)
@@ -486,7 +585,11 @@ def main():
         out["roofline"]["traffic_note"] = "counters were taken on older kernel sources"
     if args.compile_steps > 0:
         print("[bench] timing the patch compile over the same batch", file=sys.stderr, flush=True)
-        out["patch_compile"] = compile_leg(p, batch, ev_avg, args.compile_steps, stream)
+        out["patch_compile"] = compile_leg(p, batch, ev_avg, args.compile_steps, stream,
+                                           args.orbit_steps)
+    if args.attention_steps > 0:
+        print("[bench] timing decode attention", file=sys.stderr, flush=True)
+        out["decode_attention"] = attention_leg(args.attention_steps, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)

@@ -14,147 +14,21 @@
 #include <vector>
 
 #include "../../include/kamera.h"
+#include "kamera_host.h"
 #include "kamera_internal.h"
 
 using kamera::JobDesc;
 using kamera::LaunchParams;
 
-namespace kamera {
-namespace host {
-
-thread_local std::string g_last_error;
-
-kamera_status fail(kamera_status st, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return st;
-}
-
-void clear_error() { g_last_error.clear(); }
-const char* last_error() { return g_last_error.c_str(); }
-
 using kamera::kHeaderBytes;
 using kamera::kFreqOffset;
 using kamera::kSectionOffset;
 using kamera::kTablesEnd;
+using namespace kamera::host;
+
+namespace {
+
 constexpr int64_t kTargetBlocks = 70000;   // grid size the tiles-per-wave choice aims under
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-Channel channel_of(const kamera_model& m, int c) {
-  if (m.family == KAMERA_FAMILY_MLA)
-    return c == KAMERA_CH_ROT ? Channel{1, m.rope_dim, true} : Channel{1, m.head_dim, false};
-  return Channel{m.n_kv_heads, m.head_dim, c == KAMERA_CH_ROT};
-}
-
-Range view_range(const void* p, int64_t ls, int64_t n_layers, int64_t ts, int64_t n_tokens,
-                 int64_t row_elems, int64_t esize) {
-  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-  const int64_t last = (n_layers - 1) * ls + (n_tokens - 1) * ts + row_elems;
-  return Range{b, b + static_cast<uintptr_t>(last * esize)};
-}
-
-bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
-
-kamera_status validate_model(const kamera_model* m) {
-  if (!m) return fail(KAMERA_ERR_INVALID_ARGUMENT, "model is NULL");
-  if (m->family != KAMERA_FAMILY_GQA && m->family != KAMERA_FAMILY_MLA)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "unknown model family %d", m->family);
-  if (m->dtype != KAMERA_DTYPE_F32 && m->dtype != KAMERA_DTYPE_BF16)
-    return fail(KAMERA_ERR_UNSUPPORTED, "unsupported dtype %d", m->dtype);
-  if (m->n_layers <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_layers must be > 0");
-  if (m->rope_layout != KAMERA_ROPE_HALF_SPLIT && m->rope_layout != KAMERA_ROPE_INTERLEAVED)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "unknown rope_layout %d", m->rope_layout);
-  if (!std::isfinite(m->rope_theta) || !(m->rope_theta > 1.0))
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 1");
-  if (m->head_dim <= 0 || m->head_dim % 2)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "head_dim must be even and > 0 (got %d)",
-                m->head_dim);
-  if (m->rope_dim <= 0 || m->rope_dim % 2)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_dim must be even and > 0 (got %d)",
-                m->rope_dim);
-  if (m->rope_dim > 2 * kamera::kMaxPairs)
-    return fail(KAMERA_ERR_UNSUPPORTED, "rope_dim %d exceeds %d", m->rope_dim,
-                2 * kamera::kMaxPairs);
-  if (m->family == KAMERA_FAMILY_GQA) {
-    if (m->n_kv_heads <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_kv_heads must be > 0");
-    if (m->rope_dim > m->head_dim)
-      return fail(KAMERA_ERR_INVALID_ARGUMENT, "rope_dim (%d) exceeds head_dim (%d)",
-                  m->rope_dim, m->head_dim);
-  } else if (m->n_kv_heads != 1) {
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "MLA needs n_kv_heads == 1 (got %d)",
-                m->n_kv_heads);
-  }
-  const int pairs = m->rope_dim / 2;
-  if (m->inv_freq) {
-    for (int i = 0; i < pairs; ++i)
-      if (!std::isfinite(m->inv_freq[i]) || m->inv_freq[i] < 0.0)
-        return fail(KAMERA_ERR_INVALID_ARGUMENT, "inv_freq[%d] must be finite and >= 0", i);
-  }
-  if (m->n_sections < 0 || m->n_sections > KAMERA_MAX_SECTIONS)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_sections must be in [0, %d] (got %d)",
-                KAMERA_MAX_SECTIONS, m->n_sections);
-  if ((m->n_sections > 0) != (m->pair_section != nullptr))
-    return fail(KAMERA_ERR_INVALID_ARGUMENT,
-                "pair_section must be given exactly when n_sections > 0");
-  if (m->pair_section) {
-    for (int i = 0; i < pairs; ++i)
-      if (m->pair_section[i] >= m->n_sections)
-        return fail(KAMERA_ERR_INVALID_ARGUMENT, "pair_section[%d] = %d is not below n_sections",
-                    i, (int)m->pair_section[i]);
-  }
-  return KAMERA_OK;
-}
-
-kamera_status validate_cache(const kamera_model& m, const kamera_cache* c) {
-  if (!c) return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache is NULL");
-  if (!c->pool[0] || !c->pool[1]) return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache pool is NULL");
-  if (c->page_size <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "page_size must be > 0");
-  if (c->n_pages <= 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_pages must be > 0");
-  if (c->n_logical_pages <= 0)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_logical_pages must be > 0");
-  if (!c->page_table && c->n_logical_pages > c->n_pages)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT,
-                "identity page table needs n_logical_pages (%d) <= n_pages (%d)",
-                c->n_logical_pages, c->n_pages);
-  if ((int64_t)c->n_logical_pages * c->page_size > INT32_MAX)
-    return fail(KAMERA_ERR_UNSUPPORTED, "cache holds more than 2^31-1 logical tokens");
-  if (c->token_stride <= 0 || c->layer_stride < 0)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache strides must be positive");
-  const int64_t slots = (int64_t)c->n_pages * c->page_size;
-  for (int ch = 0; ch < 2; ++ch) {
-    const Channel g = channel_of(m, ch);
-    if ((int64_t)g.heads * g.width > c->token_stride)
-      return fail(KAMERA_ERR_INVALID_ARGUMENT,
-                  "cache token_stride (%lld) is shorter than channel %d's row (%d)",
-                  (long long)c->token_stride, ch, g.heads * g.width);
-  }
-  if (m.n_layers > 1 && c->layer_stride < slots * c->token_stride)
-    return fail(KAMERA_ERR_INVALID_ARGUMENT, "cache layer_stride overlaps the next layer");
-  // the two channel pools may share rows (MLA), but must not write the same elements
-  const int64_t es = m.dtype == KAMERA_DTYPE_F32 ? 4 : 2;
-  const Channel g0 = channel_of(m, 0), g1 = channel_of(m, 1);
-  const Range r0 = view_range(c->pool[0], c->layer_stride, m.n_layers, c->token_stride, slots,
-                              (int64_t)g0.heads * g0.width, es);
-  const Range r1 = view_range(c->pool[1], c->layer_stride, m.n_layers, c->token_stride, slots,
-                              (int64_t)g1.heads * g1.width, es);
-  if (overlaps(r0, r1)) {
-    const int64_t d = ((int64_t)reinterpret_cast<intptr_t>(c->pool[0]) -
-                       (int64_t)reinterpret_cast<intptr_t>(c->pool[1]));
-    const int64_t w0 = (int64_t)g0.heads * g0.width * es, w1 = (int64_t)g1.heads * g1.width * es;
-    const int64_t row = c->token_stride * es;
-    const bool disjoint_rows = (d >= w1 && d + w0 <= row) || (-d >= w0 && -d + w1 <= row);
-    if (!disjoint_rows)
-      return fail(KAMERA_ERR_OVERLAP, "the two channel pools write the same elements");
-  }
-  return KAMERA_OK;
-}
 
 enum class Op { Reuse, Relocate, Patch };
 
@@ -240,74 +114,7 @@ kamera_status validate_chunks(const kamera_model& m, const kamera_cache& c,
   return KAMERA_OK;
 }
 
-// ---------------------------------------------------------------------------------------
-// pinned staging ring for the job table (host -> workspace copy)
-// ---------------------------------------------------------------------------------------
 
-struct StagingSlot {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
-};
-
-struct DeviceRing {
-  std::mutex mu;
-  StagingSlot slot[4];
-  unsigned next = 0;
-};
-
-DeviceRing* ring_for(int device) {
-  static DeviceRing rings[64];   // process lifetime; never torn down (no exit-time HIP calls)
-  return (device >= 0 && device < 64) ? &rings[device] : nullptr;
-}
-
-kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  DeviceRing* ring = ring_for(dev);
-  if (!ring) return fail(KAMERA_ERR_UNSUPPORTED, "device index %d out of range", dev);
-  std::lock_guard<std::mutex> lock(ring->mu);
-  StagingSlot& s = ring->slot[ring->next++ % 4];
-  if (s.pending) {
-    e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
-    s.pending = false;
-  }
-  if (!s.done) {
-    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
-  }
-  if (s.cap < bytes.size()) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    const size_t cap = round_up(bytes.size(), size_t(1) << 16);
-    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipHostMalloc: %s", hipGetErrorString(e));
-    s.cap = cap;
-  }
-  std::memcpy(s.host, bytes.data(), bytes.size());
-  e = hipMemcpyAsync(workspace, s.host, bytes.size(), hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-  e = hipEventRecord(s.done, stream);
-  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  s.pending = true;
-  return KAMERA_OK;
-}
-
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return v && *v ? std::atoi(v) : dflt;
-}
-
-}  // namespace host
-}  // namespace kamera
-
-using namespace kamera::host;
-
-namespace {
 
 // ---------------------------------------------------------------------------------------
 // packing
@@ -477,7 +284,7 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
 kamera_status run(const kamera_model* model, const kamera_cache* cache, const kamera_chunk* chunks,
                   int32_t n_chunks, void* workspace, size_t workspace_bytes, void* stream_ptr,
                   Op op) {
-  g_last_error.clear();
+  clear_error();
   kamera_status st = validate_model(model);
   if (st != KAMERA_OK) return st;
   st = validate_cache(*model, cache);
@@ -604,7 +411,7 @@ kamera_status kamera_patch(const kamera_model* model, const kamera_cache* cache,
 }
 
 kamera_status kamera_read_fault_count(const void* workspace, void* stream, uint32_t* count) {
-  g_last_error.clear();
+  clear_error();
   if (!workspace || !count) return fail(KAMERA_ERR_INVALID_ARGUMENT, "NULL argument");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(count, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
@@ -649,7 +456,7 @@ const char* kamera_status_string(kamera_status status) {
   return "unknown status";
 }
 
-const char* kamera_last_error(void) { return g_last_error.c_str(); }
+const char* kamera_last_error(void) { return last_error(); }
 
 int32_t kamera_version(void) { return KAMERA_VERSION; }
 

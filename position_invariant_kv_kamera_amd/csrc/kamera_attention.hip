@@ -23,6 +23,7 @@
 #include <cstring>
 #include <vector>
 
+#include "kamera_host.h"
 #include "kamera_internal.h"
 
 using namespace kamera::host;
@@ -226,22 +227,51 @@ __global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
 }
 
 // Merge n parts of one row: lse of part i at lse_p[i * lse_stride], its output at
-// o_p + i * o_stride. Writes out[0 .. D) and *lse_out.
+// o_p + i * o_stride. Writes out[0 .. D) and *lse_out. The part weights exp(lse_i - M) are
+// formed once per row (in chunks of kMergeChunk parts through LDS), then every feature is a
+// weighted sum.
+constexpr int kMergeChunk = 256;
 __device__ void merge_row(const float* lse_p, int64_t lse_stride, const float* o_p,
                           int64_t o_stride, int n, int D, float* out, float* lse_out) {
+  __shared__ float red[64];
+  __shared__ float wts[kMergeChunk];
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, lse_p[i * lse_stride]);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, lse_p[i * lse_stride]);
+  red[threadIdx.x] = M;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int t = 1; t < (int)blockDim.x; ++t) M = fmaxf(M, red[t]);
+    red[0] = M;
+  }
+  __syncthreads();
+  M = red[0];
+  __syncthreads();
+  float acc[16];   // features threadIdx.x + 64 k (D <= 1024)
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
   float Z = 0.f;
-  if (M != -INFINITY)
-    for (int i = 0; i < n; ++i) Z += expf(lse_p[i * lse_stride] - M);
-  for (int f = threadIdx.x; f < D; f += blockDim.x) {
-    float acc = 0.f;
-    if (M != -INFINITY)
-      for (int i = 0; i < n; ++i) {
-        const float e = expf(lse_p[i * lse_stride] - M);
-        if (e != 0.f) acc += e * o_p[i * o_stride + f];
+  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
+    const int cn = min(kMergeChunk, n - c0);
+    for (int i = threadIdx.x; i < cn; i += blockDim.x)
+      wts[i] = M == -INFINITY ? 0.f : expf(lse_p[(c0 + i) * lse_stride] - M);
+    __syncthreads();
+    for (int i = 0; i < cn; ++i) {
+      const float e = wts[i];
+      Z += e;
+      if (e == 0.f) continue;
+      const float* oi = o_p + (int64_t)(c0 + i) * o_stride;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int f = threadIdx.x + 64 * k;
+        if (f < D) acc[k] += e * oi[f];
       }
-    out[f] = M == -INFINITY ? 0.f : acc / Z;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int f = threadIdx.x + 64 * k;
+    if (f < D) out[f] = M == -INFINITY ? 0.f : acc[k] / Z;
   }
   if (threadIdx.x == 0) *lse_out = M == -INFINITY ? -INFINITY : M + logf(Z);
 }

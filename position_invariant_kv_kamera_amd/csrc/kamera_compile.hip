@@ -26,6 +26,7 @@
 #include <cstring>
 #include <vector>
 
+#include "kamera_host.h"
 #include "kamera_internal.h"
 
 using namespace kamera::host;
