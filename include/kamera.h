@@ -326,15 +326,19 @@ kamera_status kamera_patch_compile_orbit(const kamera_model* model,
  * most 16 query heads per KV head). Per query head it writes
  *     out[(j*n_q_heads + h)*head_dim + f] = sum_t softmax(scores)_t v_tf      (fp32)
  *     lse[j*n_q_heads + h] = log sum_t exp(score_t)                          (fp32, natural)
- * (out = 0 and lse = -inf when kv_len == 0). The key range is cut into 512-token segments;
+ * (out = 0 and lse = -inf when kv_len == 0). The key ranges are cut into segments of 2048,
+ * 1024 or KAMERA_ATTN_SEGMENT tokens (the longest that still gives the call 2048 blocks);
  * each is attended on its own (Q K^T with bf16 MFMA, exact products; the weights stay fp32
- * for P V, fp32 MFMA) and the segments are combined with the state merge. Tokens whose page
- * table entry lies outside [0, n_pages) are left out (masked). */
+ * for P V, fp32 MFMA) and the segments are combined with the state merge, so results depend
+ * on the call's total work only at fp32 rounding level. Tokens whose page table entry lies
+ * outside [0, n_pages) are left out (masked). */
 typedef struct kamera_attn_query {
   int32_t kv_start;  /* first logical cache token attended, >= 0 */
   int32_t kv_len;    /* tokens attended, >= 0 */
 } kamera_attn_query;
 
+/* Shortest key segment one block of kamera_decode_attention attends (calls with enough work
+ * take 1024 or 2048). */
 #define KAMERA_ATTN_SEGMENT 512
 
 /* Workspace bytes for kamera_decode_attention (0 on invalid arguments). */

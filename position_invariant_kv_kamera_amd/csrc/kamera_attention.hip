@@ -4,8 +4,8 @@
 // The Kamera abstract states that the direct readout of a cached chunk is recovered exactly
 // by the standard state merge: attention over several key sets equals the log-sum-exp
 // weighted combination of the attention over each. Decode attention is built on it: each
-// 512-token segment of a query's key range is one block, attended on its own, and the
-// segments are merged.
+// segment (2048, 1024 or 512 tokens, per call) of a query's key range is one block, attended
+// on its own, and the segments are merged.
 //
 // attn_segment_kernel<D>: block = (segment, KV head), 4 waves; wave w takes the 16-token
 //   tiles w, w+4, ... of the segment. Per tile: S = Q K^T with v_mfma_f32_16x16x32_bf16 (the
@@ -34,7 +34,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSeg = KAMERA_ATTN_SEGMENT;
+// Segment length: the longest of 2048, 1024 and 512 tokens that still gives the call at least
+// kTargetSegBlocks blocks (long segments amortise a block's set-up and merge; short ones keep a
+// single long context spread over the chip).
+constexpr int kSegChoices[3] = {2048, 1024, KAMERA_ATTN_SEGMENT};
+constexpr int64_t kTargetSegBlocks = 2048;
 constexpr int kThreads = 256;
 constexpr int kTile = 16;
 constexpr int kMaxGroup = 16;
@@ -57,6 +61,7 @@ struct AParams {
   int64_t pool_ts;
   float scale;
   int32_t n_queries, n_q, n_kv, group, page_size, page_shift, n_pages;
+  int32_t seg;                // tokens per segment
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -65,19 +70,33 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Element offset of logical token p's row in a pool, or -1 when its page is outside the pool.
-__device__ __forceinline__ int64_t row_of(const AParams& P, int64_t p) {
-  int64_t page, slot;
+// Logical token p -> (logical page, slot).
+__device__ __forceinline__ void page_slot(const AParams& P, int64_t p, int64_t* page,
+                                          int64_t* slot) {
   if (P.page_shift >= 0) {
-    page = p >> P.page_shift;
-    slot = p & ((int64_t(1) << P.page_shift) - 1);
+    *page = p >> P.page_shift;
+    *slot = p & ((int64_t(1) << P.page_shift) - 1);
   } else {
-    page = p / P.page_size;
-    slot = p - page * P.page_size;
+    *page = p / P.page_size;
+    *slot = p - *page * P.page_size;
   }
-  const int64_t phys = P.page_table ? (int64_t)P.page_table[page] : page;
+}
+
+// Physical page of token p (its table entry), or -1 for no token.
+__device__ __forceinline__ int32_t page_entry(const AParams& P, int64_t p, bool on) {
+  if (!on) return -1;
+  int64_t page, slot;
+  page_slot(P, p, &page, &slot);
+  return P.page_table ? P.page_table[page] : (int32_t)page;
+}
+
+// Element offset of token p's row given its table entry, or -1 (no token, or a page outside
+// the pool).
+__device__ __forceinline__ int64_t row_at(const AParams& P, int64_t p, int32_t phys) {
   if (phys < 0 || phys >= P.n_pages) return -1;
-  return (phys * P.page_size + slot) * P.pool_ts;
+  int64_t page, slot;
+  page_slot(P, p, &page, &slot);
+  return ((int64_t)phys * P.page_size + slot) * P.pool_ts;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -91,15 +110,15 @@ __global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
   __shared__ __align__(16) uint16_t vt[4][kTile * VS];
   __shared__ float pt[4][kTile * PS];
   __shared__ float mrg_m[4][kMaxGroup], mrg_l[4][kMaxGroup];
-  __shared__ float mrg_o[4][kMaxGroup * D];
+  __shared__ float mrg_o[kMaxGroup * D];   // the waves' weighted outputs, summed in order
 
   const int g = blockIdx.x / P.n_kv;
   const int h = blockIdx.x - g * P.n_kv;
   const int j = P.seg_query[g];
   const AQuery Q = P.queries[j];
   const int s = g - Q.seg_start;
-  const int t_lo = Q.kv_start + s * kSeg;
-  const int t_hi = min(Q.kv_start + Q.kv_len, t_lo + kSeg);
+  const int t_lo = Q.kv_start + s * P.seg;
+  const int t_hi = min(Q.kv_start + Q.kv_len, t_lo + P.seg);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
 
@@ -126,22 +145,35 @@ __global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
   for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int koff = h * D;
-  for (int t0 = t_lo + kTile * wave; t0 < t_hi; t0 += 4 * kTile) {
-    const int tok = t0 + col;
-    const int64_t row = tok < t_hi ? row_of(P, tok) : -1;
-    bf16x8 kb[KS];
-    u32x4 vraw[KS];
+  // software pipeline: the K and V rows of the next tile are in flight while this tile is
+  // computed; their page-table entries were fetched one tile earlier still
+  auto load_tile = [&](int64_t row, bf16x8* kb, u32x4* vr) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       if (row >= 0) {
         kb[k] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(P.kpool + row + koff + 32 * k + 8 * grp));
-        vraw[k] = *reinterpret_cast<const u32x4*>(P.vpool + row + koff + 32 * k + 8 * grp);
+        vr[k] = *reinterpret_cast<const u32x4*>(P.vpool + row + koff + 32 * k + 8 * grp);
       } else {
         kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vraw[k] = u32x4{0u, 0u, 0u, 0u};
+        vr[k] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  int t0 = t_lo + kTile * wave;
+  int64_t row = t0 + col < t_hi ? row_at(P, t0 + col, page_entry(P, t0 + col, true)) : -1;
+  int32_t pe_next = page_entry(P, t0 + 4 * kTile + col, t0 + 4 * kTile + col < t_hi);
+  bf16x8 kb[KS];
+  u32x4 vraw[KS];
+  load_tile(row, kb, vraw);
+  for (; t0 < t_hi; t0 += 4 * kTile) {
+    const int t1 = t0 + 4 * kTile;
+    const int64_t row_next = t1 + col < t_hi ? row_at(P, t1 + col, pe_next) : -1;
+    bf16x8 kb_n[KS];
+    u32x4 vraw_n[KS];
+    load_tile(row_next, kb_n, vraw_n);
+    pe_next = page_entry(P, t1 + 4 * kTile + col, t1 + 4 * kTile + col < t_hi);
+
     // S: lane holds query rows 4 grp + r of token col
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -188,40 +220,58 @@ __global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
       }
     }
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+    row = row_next;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      kb[k] = kb_n[k];
+      vraw[k] = vraw_n[k];
+    }
   }
 
   // merge the four waves' states (rows 4 grp + r of this lane; all 16 lanes of a row group
-  // hold the same m and l)
+  // hold the same m and l): weights exp(m_w - M), outputs summed wave by wave in a fixed order
   if (col == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (4 * grp + r < kMaxGroup) {
-        mrg_m[wave][4 * grp + r] = m[r];
-        mrg_l[wave][4 * grp + r] = l[r];
-      }
+      mrg_m[wave][4 * grp + r] = m[r];
+      mrg_l[wave][4 * grp + r] = l[r];
     }
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mrg_o[wave][(4 * grp + r) * D + 16 * c + col] = o[c][r];
   __syncthreads();
+  float wgt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rw = 4 * grp + r;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
+    wgt[r] = M == -INFINITY ? 0.f : expf(m[r] - M);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* dst = &mrg_o[(4 * grp + r) * D + 16 * c + col];
+          const float v = o[c][r] * wgt[r];
+          *dst = w == 0 ? v : *dst + v;
+        }
+    }
+    __syncthreads();
+  }
   for (int idx = threadIdx.x; idx < P.group * D; idx += kThreads) {
     const int rw = idx / D, f = idx - rw * D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
-    float L = 0.f, acc = 0.f;
+    float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float e = expf(mrg_m[w][rw] - M);
-        L += mrg_l[w][rw] * e;
-        acc += mrg_o[w][rw * D + f] * e;
-      }
+      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * expf(mrg_m[w][rw] - M);
     }
     const int64_t orow = (int64_t)g * P.n_q + h * P.group + rw;
-    P.part_o[orow * D + f] = M == -INFINITY ? 0.f : acc / L;
+    P.part_o[orow * D + f] = M == -INFINITY ? 0.f : mrg_o[rw * D + f] / L;
     if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M + logf(L);
   }
 }
@@ -301,6 +351,7 @@ __global__ __launch_bounds__(64) void state_merge_kernel(const float* part_out,
 struct APlan {
   std::vector<AQuery> queries;
   std::vector<int32_t> seg_query;
+  int32_t seg = KAMERA_ATTN_SEGMENT;
   size_t seg_off = 0, part_o_off = 0, part_lse_off = 0, total = 0;
 };
 
@@ -326,8 +377,6 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
   if (n_queries > 0 && !queries) return fail(KAMERA_ERR_INVALID_ARGUMENT, "queries is NULL");
   if ((int64_t)n_queries * n_q_heads > INT32_MAX)
     return fail(KAMERA_ERR_UNSUPPORTED, "too many query rows");
-  int64_t segs = 0;
-  plan->queries.resize(n_queries);
   for (int32_t i = 0; i < n_queries; ++i) {
     const kamera_attn_query& a = queries[i];
     if (a.kv_start < 0 || a.kv_len < 0)
@@ -336,7 +385,23 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
       return fail(KAMERA_ERR_INVALID_ARGUMENT,
                   "query %d: tokens [%d, %lld) run past the cache's %lld logical tokens", i,
                   a.kv_start, (long long)a.kv_start + a.kv_len, (long long)capacity);
-    const int n = (a.kv_len + kSeg - 1) / kSeg;
+  }
+  plan->seg = kSegChoices[2];
+  for (int c = 0; c < 3; ++c) {
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < n_queries; ++i)
+      blocks += (queries[i].kv_len + kSegChoices[c] - 1) / kSegChoices[c];
+    if (blocks * model->n_kv_heads >= kTargetSegBlocks) {
+      plan->seg = kSegChoices[c];
+      break;
+    }
+  }
+  const int seg = plan->seg;
+  int64_t segs = 0;
+  plan->queries.resize(n_queries);
+  for (int32_t i = 0; i < n_queries; ++i) {
+    const kamera_attn_query& a = queries[i];
+    const int n = (a.kv_len + seg - 1) / seg;
     plan->queries[i] = AQuery{a.kv_start, a.kv_len, (int32_t)segs, n};
     for (int k = 0; k < n; ++k) plan->seg_query.push_back(i);
     segs += n;
@@ -438,6 +503,7 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
   for (int b = 0; b < 31; ++b)
     if (cache->page_size == (1 << b)) P.page_shift = b;
   P.n_pages = cache->n_pages;
+  P.seg = plan.seg;
   const int64_t seg_blocks = (int64_t)plan.seg_query.size() * model->n_kv_heads;
   if (seg_blocks > 0) {
     const dim3 grid((unsigned)seg_blocks), block(kThreads);

@@ -183,3 +183,30 @@ def test_state_merge_with_empty_parts():
     got_l = lse.cpu().numpy()
     assert np.isneginf(got_l[4]) and np.all(out.cpu().numpy()[4] == 0)
     np.testing.assert_allclose(got_l[:4], ref_l[:4], rtol=0, atol=1e-5)
+
+
+def _segment_tokens(ranges, n_kv):
+    """The segment length the library picks: the longest of 2048, 1024, 512 that still gives
+    the call 2048 blocks (segments x KV heads)."""
+    for seg in (2048, 1024, 512):
+        if sum(-(-n // seg) for _, n in ranges) * n_kv >= 2048:
+            return seg
+    return 512
+
+
+def test_many_queries_take_2048_token_segments():
+    s = Setup(n_kv=8, n_pages=400, n_logical=350, seed=13)
+    ranges = [((17 * i) % 5000, 1 + (i % 37)) for i in range(250)]
+    ranges += [(0, 5000), (1, 4999), (100, 4097), (2047, 2049), (0, 2048), (600, 4000),
+               (3, 5597), (0, 5600), (2048, 2048), (4000, 1)]
+    assert _segment_tokens(ranges, 8) == 2048
+    _run_and_check(s, 0, ranges, 16, 1 / math.sqrt(128), seed=14)
+
+
+def test_mid_size_calls_take_1024_token_segments():
+    s = Setup(n_kv=8, n_pages=400, n_logical=350, seed=15)
+    ranges = [(i % 300, 1 + (i % 5)) for i in range(200)]
+    ranges += [(i * 37, 4096) for i in range(20)]
+    ranges += [(1023, 1025), (5000, 600)]
+    assert _segment_tokens(ranges, 8) == 1024
+    _run_and_check(s, 1, ranges, 8, 0.1, seed=16)
