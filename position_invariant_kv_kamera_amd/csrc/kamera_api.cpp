@@ -28,7 +28,9 @@ using namespace kamera::host;
 
 namespace {
 
-constexpr int64_t kTargetBlocks = 70000;   // grid size the tiles-per-wave choice aims under
+// Largest grid of one launch: 2^23 blocks of 256 threads keeps the work-item count of the
+// dispatch (a 32-bit quantity) below 2^31.
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 23;
 
 enum class Op { Reuse, Relocate, Patch };
 
@@ -123,6 +125,7 @@ kamera_status validate_chunks(const kamera_model& m, const kamera_cache& c,
 struct Plan {
   std::vector<JobDesc> mfma, valu;
   int mfma_max_m = 0;
+  int xcd_remap = 0;   // LaunchParams::xcd_remap of the MFMA launches
   int64_t mfma_blocks = 0, valu_blocks = 0;
 };
 
@@ -237,24 +240,28 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
       }
     }
   }
-  // Token groups of the MFMA jobs: each wave gets `tpw` tiles of one window. Equal blocks end
-  // on a partly filled last round, so short waves (many blocks) shrink that tail; but every
-  // block reloads its V operand (16 KB per window at m = 64), so rank > 32 takes long waves.
-  // Measured on MI355X: the smallest tpw in {4, 8, 16, 32, 64} whose grid stays within
-  // ~70K blocks, at least 32 when some m > 32.
-  auto tgroups = [](const JobDesc& j, int tpw) {
-    const int sub = 4 / std::min(4, j.n_windows);
-    return std::max(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
+  // Token groups of the MFMA jobs: each wave gets `tpw` tiles of one window. Short waves
+  // (many small blocks) keep the chip evenly loaded to the end; but every block reloads its V
+  // operand (16 KB per window at m = 64), so rank > 32 takes long waves. Measured on MI355X:
+  // 4 tiles for m <= 32 (2 and 8 tiles were 1-7 % slower, 16 and 32 up to 8 %), 32 for
+  // m <= 64 (4 tiles: -18 %); larger only when the grid would exceed kMaxGridBlocks.
+  auto tgroups = [](const JobDesc& j, int64_t tpw) {
+    const int64_t sub = 4 / std::min(4, j.n_windows);
+    return std::max<int64_t>(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
   };
-  auto blocks_at = [&](int tpw) {
+  auto blocks_at = [&](int64_t tpw) {
     int64_t b = 0;
     for (const JobDesc& j : plan->mfma) b += (int64_t)m.n_layers * j.n_wgroups * tgroups(j, tpw);
     return b;
   };
-  int tpw = plan->mfma_max_m > 32 ? 32 : 4;
-  while (tpw < 64 && blocks_at(tpw) > kTargetBlocks) tpw *= 2;
-  tpw = std::max(1, env_int("KAMERA_TILES_PER_WAVE", tpw));
-  for (JobDesc& j : plan->mfma) j.n_tgroups = tgroups(j, tpw);
+  int64_t tpw = plan->mfma_max_m > 32 ? 32 : 4;
+  tpw = std::max(1, env_int("KAMERA_TILES_PER_WAVE", (int)tpw));
+  while (tpw < (int64_t(1) << 30) && blocks_at(tpw) > kMaxGridBlocks) tpw *= 2;
+  for (JobDesc& j : plan->mfma) j.n_tgroups = (int32_t)tgroups(j, tpw);
+  // Short waves mean many blocks per (layer, window group), each loading the same V operand:
+  // runs of 4 blocks kept on one XCD then find it in that XCD's L2 (measured +1 % on 4 KV
+  // heads x 1296-token chunks at m = 16, neutral at m = 32; with long waves it cost 1-5 %).
+  plan->xcd_remap = env_int("KAMERA_XCD_REMAP", tpw <= 4 ? 4 : 0);
 
   // grouped by window width (one launch each), heaviest jobs first inside a group so that a
   // mixed batch does not end on a tail of patched work
@@ -271,13 +278,14 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
     for (JobDesc& j : jobs) {
       j.block_start = (int32_t)b;
       b += (int64_t)m.n_layers * j.n_wgroups * j.n_tgroups;
-      if (b > INT32_MAX) return false;
+      if (b > kMaxGridBlocks) return false;
     }
     *total = b;
     return true;
   };
   if (!assign(plan->mfma, &plan->mfma_blocks) || !assign(plan->valu, &plan->valu_blocks))
-    return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
+    return fail(KAMERA_ERR_UNSUPPORTED,
+                "batch needs more than 2^23 blocks in one launch: split it into smaller calls");
   return KAMERA_OK;
 }
 
@@ -349,7 +357,7 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
                                         : nullptr;
   lp.fault_counter = static_cast<uint32_t*>(workspace);
   lp.mode = op == Op::Patch ? kamera::MODE_PATCH : kamera::MODE_REUSE;
-  lp.xcd_remap = env_int("KAMERA_XCD_REMAP", 0);
+  lp.xcd_remap = plan.xcd_remap;
   lp.n_layers = model->n_layers;
   lp.block_order = env_int("KAMERA_BLOCK_ORDER", 0);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -371,6 +379,7 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
     lo = hi;
   }
   lp.block_base = 0;
+  lp.xcd_remap = 0;
   if (!plan.valu.empty()) {
     lp.jobs = reinterpret_cast<const JobDesc*>(ws + valu_off);
     lp.block_starts = reinterpret_cast<const int32_t*>(ws + valu_bs_off);

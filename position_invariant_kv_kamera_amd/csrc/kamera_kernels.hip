@@ -98,14 +98,22 @@ __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
   else *q = v;
 }
 
-// Logical block -> block index so that each XCD (blocks are dealt round-robin over the 8
-// XCDs) works through one contiguous range of logical blocks: neighbouring blocks share
-// patch factors and page-table lines, which then stay in that XCD's L2.
-__device__ __forceinline__ int remap_block(int b, int total, int enable) {
-  if (!enable) return b;
+// Hardware block -> logical block. Blocks are dealt round-robin over the 8 XCDs, each with its
+// own L2. mode 1: each XCD works through one contiguous range of logical blocks. mode T >= 2:
+// runs of T consecutive logical blocks stay on one XCD and successive runs go round the XCDs,
+// so neighbouring blocks (which share patch factors and page-table lines) meet in one L2 while
+// heavy and light jobs stay spread over all XCDs; blocks past the last whole 8 T round keep
+// their index.
+__device__ __forceinline__ int remap_block(int b, int total, int mode) {
+  if (mode <= 0) return b;
   const int xcd = b & 7, idx = b >> 3;
-  const int per = total >> 3, rem = total & 7;
-  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  if (mode == 1) {
+    const int per = total >> 3, rem = total & 7;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  }
+  const int full = total / (8 * mode) * (8 * mode);
+  if (b >= full) return b;
+  return ((idx / mode) * 8 + xcd) * mode + idx % mode;
 }
 
 // The job whose block range holds `blk`: block_starts is ascending, so the job index is the
