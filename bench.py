@@ -369,7 +369,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
     pc = rec["patch_compile"]
     calls = pc["steps"] + 1                     # one untimed call, then the timed ones
     rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
-    kinds = {"gram_kernel": [], "subspace": [], "project_kernel": []}
+    kinds = {"gram_kernel": [], "subspace": [], "project": []}
     for r in rows:
         for k in kinds:
             if k in r["Name"]:
@@ -395,7 +395,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
             tf = gram_f / (per_call_us * 1e-6) / 1e12
             lines.append(f"| gram (Delta^T Delta, fp32 MFMA) | {n} | {per_call_us:.1f} | mfma fp32 | "
                          f"{tf:.1f} TFLOP/s | {tf / FP32_PEAK_TFLOPS:.3f} |")
-        elif k == "project_kernel":
+        elif k == "project":
             gbps = read2 / (per_call_us * 1e-6) / 1e9
             lines.append(f"| project (U = Delta V) | {n} | {per_call_us:.1f} | hbm | "
                          f"{gbps:.0f} GB/s | {gbps / HBM_PEAK_GBPS:.3f} |")

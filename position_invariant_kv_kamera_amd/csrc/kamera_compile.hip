@@ -841,6 +841,258 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
 }
 
 // ---------------------------------------------------------------------------------------
+// project_stream: U = Delta X with Delta formed in registers (no LDS staging of Delta).
+// The sum over a head's features may be taken in any order, so each lane contracts the
+// features it loaded itself: lane 16g + n holds token t0 + n and S slots (pieces of 8
+// features) per 128-feature slab; MFMA step s takes element s%8 of slot s/8 as A[n][g], and X
+// sits in LDS with its rows permuted to match (row 4s + g holds the feature that lane group g
+// contracts at step s). Both members of every RoPE pair sit in one lane:
+//   contiguous layout: slot p of lane group g is piece 16c + 4p + g of slab c, so one load
+//     instruction covers 64 contiguous bytes of each of 16 token rows; half-split partners
+//     (pieces i and i + R/16) share a lane when R is a multiple of 64, interleaved pairs
+//     always do;
+//   pair-unit layout (half-split, R not a multiple of 64, S even): the pieces are listed as
+//     pairs (i, i + R/16) followed by the pass-through pieces, and lane group g takes list
+//     positions gS .. gS + S - 1.
+// Each wave keeps the loads of its next (tile, slab) in flight while it computes the current
+// one. Other shapes use project_kernel.
+// ---------------------------------------------------------------------------------------
+
+#ifndef KAMERA_PROJ_TOKENS
+#define KAMERA_PROJ_TOKENS 512
+#endif
+constexpr int kStreamTokens = KAMERA_PROJ_TOKENS;   // tokens per block (512: 8 tiles per wave)
+
+#define CGLOBAL __attribute__((address_space(1)))
+
+// Piece (8 features) held by lane group g in slot p of slab c.
+__host__ __device__ inline int stream_piece(int g, int p, int c, int S, int unit_layout, int hp) {
+  if (!unit_layout) return 16 * c + 4 * p + g;
+  const int pos = g * S + p;
+  if (pos < 2 * hp) return (pos & 1) ? hp + (pos >> 1) : (pos >> 1);
+  return pos;
+}
+
+// LDS row stride (floats) of the permuted X: the four rows one MFMA step reads (16 floats
+// each) land in distinct banks; wider heads take the plain stride to bound the LDS.
+__host__ __device__ inline int stream_sv(int width, int mp) {
+  if (width > 128) return mp;
+  return mp == 16 ? 16 : (mp == 64 ? 80 : 48);
+}
+
+template <typename T>
+struct Piece {
+  u32x4 w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_piece(const T* p, Piece<T>& o) {
+  const CGLOBAL u32x4* q = (const CGLOBAL u32x4*)p;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) o.w[k] = q[k];
+}
+
+__device__ __forceinline__ void piece_floats(const Piece<uint16_t>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(a.w[0][k] << 16);
+    o[2 * k + 1] = __uint_as_float(a.w[0][k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void piece_floats(const Piece<float>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = __uint_as_float(a.w[0][k]);
+    o[4 + k] = __uint_as_float(a.w[1][k]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 2, 8))) void project_stream_kernel(CParams P) {
+  extern __shared__ __align__(16) float vs[];   // permuted X [width][SV]
+  __shared__ float2 cs[64];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int local = blockIdx.x - P.starts[e];
+  const int tblocks = (J.n_tokens + kStreamTokens - 1) / kStreamTokens;
+  const int unit = local / tblocks, tb = local - unit * tblocks;
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int W = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
+  const int S = min(W, 128) / 32;            // slots per lane per slab
+  const int nslab = (W + 127) / 128;
+  const int R = J.rotate ? J.rot_dim : 0;
+  const int hp = R / 16;
+  const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
+  const int unit_layout = (J.rotate && !inter && R % 64 != 0) ? 1 : 0;
+  const int SV = stream_sv(W, mp);
+  const int nrb = mp / 16;
+
+  if (J.rotate) fill_phases(cs, J, P);
+  const float* xg = P.ws + J.xbase + (int64_t)unit * W * mp;
+  for (int idx = tid; idx < W * mp; idx += kThreads) {
+    const int k = idx / mp, r = idx - k * mp;
+    const int sg = k >> 2, gg = k & 3;
+    const int c = sg / (8 * S), within = sg - c * 8 * S;
+    const int f = 8 * stream_piece(gg, within >> 3, c, S, unit_layout, hp) + (within & 7);
+    vs[k * SV + r] = xg[(int64_t)f * mp + r];
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  // this lane's slots: feature offset, and for a rotated head the role (0 pass-through,
+  // 1 first member of a half-split pair, 2 second member, 3 interleaved pairs), the first
+  // pair index and the partner slot
+  int off[4], kind[4], pair0[4], part[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = p < S ? stream_piece(g, p, 0, S, unit_layout, hp) : 0;
+    off[p] = 8 * i;
+    kind[p] = 0;
+    pair0[p] = 0;
+    part[p] = p;
+    if (p < S && J.rotate) {
+      int pi = -1;
+      if (inter) {
+        if (i < R / 8) { kind[p] = 3; pair0[p] = 4 * i; }
+      } else if (i < hp) {
+        kind[p] = 1; pair0[p] = 8 * i; pi = i + hp;
+      } else if (i < 2 * hp) {
+        kind[p] = 2; pair0[p] = 8 * (i - hp); pi = i - hp;
+      }
+      if (pi >= 0)
+        for (int q = 0; q < S; ++q)
+          if (stream_piece(g, q, 0, S, unit_layout, hp) == pi) part[p] = q;
+    }
+  }
+
+  const CMember* mem = P.members + J.member_off;
+  const int K = J.n_members;
+  const int64_t head_off = (int64_t)head * W;
+  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off;
+  const T* cond0 = static_cast<const T*>(mem[0].cond) + layer * mem[0].cond_ls + head_off;
+  T* U = static_cast<T*>(J.U) + layer * J.u_ls + head * J.u_hs;
+  const int t_lo = tb * kStreamTokens, t_hi = min(J.n_tokens, t_lo + kStreamTokens);
+  const int ntile = (t_hi - t_lo + 15) / 16;
+  const int mine = wave < ntile ? (ntile - wave + 3) / 4 : 0;
+  const int total = mine * nslab;
+
+  struct Buf {
+    Piece<T> x[4], c[4];
+  };
+  auto load_unit = [&](int u, Buf& b) {
+    const int it = u / nslab, c = u - it * nslab;
+    const int tok = t_lo + 16 * (wave + 4 * it) + n;
+    const bool ok = tok < t_hi;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p < S && ok) {
+        load_piece(canon + (int64_t)tok * J.canon_ts + 128 * c + off[p], b.x[p]);
+        load_piece(cond0 + (int64_t)tok * mem[0].cond_ts + 128 * c + off[p], b.c[p]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(T) / 2); ++k) {
+          b.x[p].w[k] = u32x4{0u, 0u, 0u, 0u};
+          b.c[p].w[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+
+  Buf cur, nxt;
+  f32x4 acc[4];
+  if (total > 0) load_unit(0, cur);
+  for (int u = 0; u < total; ++u) {
+    if (u + 1 < total) load_unit(u + 1, nxt);
+    const int it = u / nslab, c = u - it * nslab;
+    const int tile_tok = t_lo + 16 * (wave + 4 * it);
+    const int tok = tile_tok + n;
+    if (c == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // per slot: Delta = conditioned - R(delta) canonical, then its 8 MFMA steps
+    // (U tile += Delta X, v_mfma_f32_16x16x4f32 per 16-column block)
+    const int row0 = 4 * (c * 8 * S) + g;
+    const float inv_k = 1.0f / (float)K;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p >= S) continue;
+      float d[8], x[8];
+      piece_floats(cur.c[p], d);
+      if (K > 1) {
+        // several orderings: the mean of their conditioned rows
+        if (tok < t_hi) {
+          for (int k = 1; k < K; ++k) {
+            const T* ck = static_cast<const T*>(mem[k].cond) + layer * mem[k].cond_ls +
+                          head_off + (int64_t)tok * mem[k].cond_ts + 128 * c + off[p];
+            Piece<T> pc;
+            load_piece(ck, pc);
+            float y[8];
+            piece_floats(pc, y);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += y[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] *= inv_k;
+      }
+      piece_floats(cur.x[p], x);
+      const int kd = kind[p];
+      if (kd == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = d[q] - x[q];
+      } else if (kd == 3) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float2 r = cs[pair0[p] + j];
+          const float a = x[2 * j], b = x[2 * j + 1];
+          d[2 * j] = d[2 * j] - (a * r.x - b * r.y);
+          d[2 * j + 1] = d[2 * j + 1] - (b * r.x + a * r.y);
+        }
+      } else {
+        const int q0 = part[p];
+        Piece<T> praw;
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(T) / 2); ++k)
+          praw.w[k] = q0 == 0 ? cur.x[0].w[k]
+                    : q0 == 1 ? cur.x[1].w[k] : q0 == 2 ? cur.x[2].w[k] : cur.x[3].w[k];
+        float y[8];
+        piece_floats(praw, y);
+        const float sg = kd == 1 ? -1.f : 1.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float2 r = cs[pair0[p] + q];
+          d[q] = d[q] - (x[q] * r.x + (sg * y[q]) * r.y);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float* br = vs + (row0 + 4 * (8 * p + q)) * SV + n;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (b < nrb) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(d[q], br[16 * b], acc[b], 0, 0, 0);
+      }
+    }
+    if (c == nslab - 1) {
+      // lane holds U rows tile_tok + 4g + i, column 16q + n
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = 16 * q + n;
+        if (q < nrb && col < m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tile_tok + 4 * g + i;
+            if (t < t_hi) store_elem(U + (int64_t)t * m + col, acc[q][i]);
+          }
+        }
+      }
+    }
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // host: validation, plan, launches
 // ---------------------------------------------------------------------------------------
 
@@ -848,11 +1100,18 @@ enum Kind { kGram = 0, kSubspace = 1, kProject = 2 };
 
 struct Launch {
   int kind;
-  int cls;                          // gram: NB; subspace: 0..4; project: 0..1
+  int cls;                          // gram: NB; subspace: 0..4; project: 0..1, 2 = streamed
   std::vector<int32_t> starts, job_of;
   int64_t blocks = 0;
   size_t off = 0;                   // byte offset of starts (job_of follows)
+  size_t lds = 0;                   // dynamic LDS bytes (streamed projection)
 };
+
+// Can project_stream_kernel take this job? Both members of every pair must fit one lane.
+bool stream_eligible(const CJob& J, int layout) {
+  if (!J.rotate || layout != KAMERA_ROPE_HALF_SPLIT || J.rot_dim % 64 == 0) return true;
+  return (std::min(J.width, 128) / 32) % 2 == 0;
+}
 
 // A chunk to compile, whichever entry point described it: its orderings (one for a plain
 // compile), canonical rows and output factors.
@@ -1007,7 +1266,7 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     }
   }
   // launches: one per kernel class present
-  auto add = [&](int kind, int cls, int job, int64_t blocks) -> bool {
+  auto add = [&](int kind, int cls, int job, int64_t blocks, size_t lds = 0) -> bool {
     Launch* L = nullptr;
     for (auto& l : plan->launches)
       if (l.kind == kind && l.cls == cls) L = &l;
@@ -1021,14 +1280,19 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     L->starts.push_back((int32_t)L->blocks);
     L->job_of.push_back(job);
     L->blocks += blocks;
+    L->lds = std::max(L->lds, lds);
     return true;
   };
   for (size_t j = 0; j < plan->jobs.size(); ++j) {
     const CJob& J = plan->jobs[j];
-    const int tblocks = (J.n_tokens + kProjTokens - 1) / kProjTokens;
+    const bool stream = stream_eligible(J, M.rope_layout);
+    const int tblocks = stream ? (J.n_tokens + kStreamTokens - 1) / kStreamTokens
+                               : (J.n_tokens + kProjTokens - 1) / kProjTokens;
+    const size_t lds = stream ? (size_t)J.width * stream_sv(J.width, J.mp) * sizeof(float) : 0;
     bool ok = add(kGram, J.te / 32, (int)j, (int64_t)J.n_units * J.n_pairs * J.splits) &&
               add(kSubspace, subspace_class(J.width, J.mp), (int)j, J.n_units) &&
-              add(kProject, J.width <= 128 ? 0 : 1, (int)j, (int64_t)J.n_units * tblocks);
+              add(kProject, stream ? 2 : (J.width <= 128 ? 0 : 1), (int)j,
+                  (int64_t)J.n_units * tblocks, lds);
     if (!ok) return fail(KAMERA_ERR_UNSUPPORTED, "batch needs more than 2^31-1 blocks");
   }
   size_t off = round_up(plan->jobs.size() * sizeof(CJob), 16);
@@ -1162,8 +1426,17 @@ hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
       break;
     }
     case kProject:
-      if (L.cls == 0) project_kernel<T, 128, 4><<<grid, block, 0, stream>>>(P);
-      else project_kernel<T, 512, 2><<<grid, block, 0, stream>>>(P);
+      if (L.cls == 2) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&project_stream_kernel<T>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+        if (e != hipSuccess) return e;
+        project_stream_kernel<T><<<grid, block, L.lds, stream>>>(P);
+      } else if (L.cls == 0) {
+        project_kernel<T, 128, 4><<<grid, block, 0, stream>>>(P);
+      } else {
+        project_kernel<T, 512, 2><<<grid, block, 0, stream>>>(P);
+      }
       break;
     default: return hipErrorInvalidValue;
   }

@@ -132,6 +132,19 @@ def test_compile_with_partial_rotary():
     _compile_variant(case, {})
 
 
+@pytest.mark.parametrize("head_dim,rope_dim,layout", [
+    (128, 96, oracle.HALF_SPLIT),     # pairs (i, i + 48): pieces paired across lane groups
+    (128, 32, oracle.HALF_SPLIT),
+    (64, 32, oracle.HALF_SPLIT),
+    (128, 32, oracle.INTERLEAVED),
+])
+def test_compile_with_partial_rotary_other_widths(head_dim, rope_dim, layout):
+    case = cc.Case(f"partial_{rope_dim}_of_{head_dim}_{layout}", "gqa", "bf16", 2, 2, head_dim,
+                   rope_dim, layout, 1e4,
+                   [cc.ChunkSpec(333, 16, -4321), cc.ChunkSpec(40, 32, 77)], seed=23)
+    _compile_variant(case, {})
+
+
 def test_compile_with_sections_and_table():
     sec = np.repeat(np.array([0, 1, 2], np.uint8), [16, 24, 24])
     table = np.sort(10.0 ** np.random.default_rng(3).uniform(-6, 0, 64))[::-1].copy()
