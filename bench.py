@@ -153,7 +153,7 @@ def compile_leg(p, batch, reuse_ms: float, steps: int, stream, orbit_steps: int 
             units = p.n_layers * H
             in_bytes += 2 * units * T * W * es
             io_bytes += 2 * 2 * units * T * W * es + units * (T + W) * m * es
-            gram_flops += 2.0 * units * T * W * W
+            gram_flops += 1.0 * units * T * W * (W + 1)   # distinct entries of G (symmetric)
             proj_flops += 2.0 * units * T * W * m
         items.append(kb.CompileItem(T, m, p.deltas[c], list(ct.src), cond, U, V))
     model = kb.model_of(p)
@@ -369,7 +369,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
     pc = rec["patch_compile"]
     calls = pc["steps"] + 1                     # one untimed call, then the timed ones
     rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
-    kinds = {"gram_kernel": [], "subspace": [], "project": []}
+    kinds = {"gram": [], "subspace": [], "project": []}
     for r in rows:
         for k in kinds:
             if k in r["Name"]:
@@ -391,7 +391,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
         tot_ns = sum(float(r["TotalDurationNs"]) for r in rs)
         n = sum(int(r["Calls"]) for r in rs)
         per_call_us = tot_ns / calls / 1e3
-        if k == "gram_kernel":
+        if k == "gram":
             tf = gram_f / (per_call_us * 1e-6) / 1e12
             lines.append(f"| gram (Delta^T Delta, fp32 MFMA) | {n} | {per_call_us:.1f} | mfma fp32 | "
                          f"{tf:.1f} TFLOP/s | {tf / FP32_PEAK_TFLOPS:.3f} |")
@@ -401,7 +401,8 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
                          f"{gbps:.0f} GB/s | {gbps / HBM_PEAK_GBPS:.3f} |")
         else:
             lines.append(f"| subspace iteration | {n} | {per_call_us:.1f} | latency | - | - |")
-    lines += ["", "Gram flops per call: 2 n D^2 per head (full product) = "
+    lines += ["", "Gram flops per call: n D (D + 1) per head (the distinct entries of the "
+              "symmetric product) = "
               f"{gram_f / 1e9:.1f} GFLOP; projection bytes per call: both inputs once = "
               f"{read2 / 1e9:.3f} GB.", "",
               "## rocprofv3 --kernel-trace --stats (top kernels)", "",

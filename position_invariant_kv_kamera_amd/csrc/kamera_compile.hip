@@ -66,7 +66,7 @@ struct alignas(16) CJob {
   int32_t n_tokens, m, mp, width, heads, rotate, te, nb, n_pairs, splits, split_tokens, n_units;
   int32_t rot_dim;  // features of each head that turn (the rest pass through); pairs rot_dim/2
   int32_t member_off, n_members;   // this job's orderings in the member table
-  int32_t pad0;
+  int32_t gperm;   // 1: G is stored with its rows and columns permuted (gram_stream_kernel)
 };
 
 struct CParams {
@@ -354,6 +354,228 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         out[(r0 + 16 * x + 4 * (lane >> 4) + i) * TE + c0 + 16 * y + (lane & 15)] = acc[x][y][i];
+}
+
+#define CGLOBAL __attribute__((address_space(1)))
+
+// Piece (8 features) held by lane group g in slot p of slab c.
+__host__ __device__ inline int stream_piece(int g, int p, int c, int S, int unit_layout, int hp) {
+  if (!unit_layout) return 16 * c + 4 * p + g;
+  const int pos = g * S + p;
+  if (pos < 2 * hp) return (pos & 1) ? hp + (pos >> 1) : (pos >> 1);
+  return pos;
+}
+
+// LDS row stride (floats) of the permuted X: the four rows one MFMA step reads (16 floats
+// each) land in distinct banks; wider heads take the plain stride to bound the LDS.
+__host__ __device__ inline int stream_sv(int width, int mp) {
+  if (width > 128) return mp;
+  return mp == 16 ? 16 : (mp == 64 ? 80 : 48);
+}
+
+template <typename T>
+struct Piece {
+  u32x4 w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_piece(const T* p, Piece<T>& o) {
+  const CGLOBAL u32x4* q = (const CGLOBAL u32x4*)p;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) o.w[k] = q[k];
+}
+
+__device__ __forceinline__ void piece_floats(const Piece<uint16_t>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(a.w[0][k] << 16);
+    o[2 * k + 1] = __uint_as_float(a.w[0][k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void piece_floats(const Piece<float>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = __uint_as_float(a.w[0][k]);
+    o[4 + k] = __uint_as_float(a.w[1][k]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// gram_stream: G = Delta^T Delta for 128-wide heads with Delta formed in registers.
+// The sum runs over tokens in any order and G may be stored in any symmetric permutation, so
+// each lane multiplies what it loaded itself: at step s lane 16g + n holds token
+// t + 4s + g, features 8n .. 8n + 7 (the 16 lanes of a group read one whole 256-byte row).
+// Stored order: row 16b + i of G' is feature 8i + b, so element b of every lane's piece is
+// the MFMA operand of 16-feature block b (A[i][k] = Delta[token k][8i + b] and
+// B[k][j] = Delta[token k][8j + b']), and one v_mfma_f32_16x16x4f32 per block pair
+// b <= b' (36 of 64: G is symmetric) adds four tokens. Half-split RoPE partners sit R/16
+// lanes apart in the group and are fetched with a lane permute. The four waves take
+// contiguous quarters of the block's tokens and their partial sums are added in LDS in wave
+// order, so the result does not depend on timing.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kGramPrefetch = 4;   // steps of 4 tokens kept in flight per wave
+
+__host__ __device__ inline int gperm_row(int f) { return 16 * (f & 7) + (f >> 3); }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 8)))
+void gram_stream_kernel(CParams P) {
+  __shared__ float red[36 * 256];
+  __shared__ float2 cs[64];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  int local = blockIdx.x - P.starts[e];
+  const int split = local % J.splits;
+  const int unit = local / J.splits;
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int t_lo = split * J.split_tokens;
+  const int t_hi = min(J.n_tokens, t_lo + J.split_tokens);
+  // this wave's quarter of the tokens, in steps of 4
+  const int q4 = ((t_hi - t_lo + 15) / 16) * 4;
+  const int w_lo = t_lo + wave * q4, w_hi = min(t_hi, w_lo + q4);
+  const int nsteps = w_hi > w_lo ? (w_hi - w_lo + 3) / 4 : 0;
+
+  if (J.rotate) {
+    fill_phases(cs, J, P);
+    __syncthreads();
+  }
+  // this lane's piece of the row: features 8n .. 8n + 7; its RoPE role
+  const int R = J.rotate ? J.rot_dim : 0;
+  const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
+  const int hp = R / 16;
+  int kind = 0, pair0 = 0, src_lane = lane;
+  if (J.rotate && n < R / 8) {
+    if (inter) {
+      kind = 3;
+      pair0 = 4 * n;
+    } else if (n < hp) {
+      kind = 1;
+      pair0 = 8 * n;
+      src_lane = (lane & ~15) | (n + hp);
+    } else {
+      kind = 2;
+      pair0 = 8 * (n - hp);
+      src_lane = (lane & ~15) | (n - hp);
+    }
+  }
+
+  const CMember* mem = P.members + J.member_off;
+  const int K = J.n_members;
+  const int64_t head_off = (int64_t)head * 128;
+  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off + 8 * n;
+  const T* cond0 = static_cast<const T*>(mem[0].cond) + layer * mem[0].cond_ls + head_off + 8 * n;
+
+  Piece<T> px[kGramPrefetch], pc[kGramPrefetch];
+  auto load_step = [&](int st, Piece<T>& x, Piece<T>& c) {
+    const int tok = w_lo + 4 * st + g;
+    if (st < nsteps && tok < w_hi) {
+      load_piece(canon + (int64_t)tok * J.canon_ts, x);
+      load_piece(cond0 + (int64_t)tok * mem[0].cond_ts, c);
+    } else {
+#pragma unroll
+      for (int k = 0; k < (int)(sizeof(T) / 2); ++k) {
+        x.w[k] = u32x4{0u, 0u, 0u, 0u};
+        c.w[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kGramPrefetch; ++k) load_step(k, px[k], pc[k]);
+
+  f32x4 acc[36];
+#pragma unroll
+  for (int k = 0; k < 36; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float inv_k = 1.0f / (float)K;
+
+  for (int st0 = 0; st0 < nsteps; st0 += kGramPrefetch) {
+#pragma unroll
+    for (int k = 0; k < kGramPrefetch; ++k) {
+      const int st = st0 + k;
+      if (st >= nsteps) break;
+      // the partner piece (half-split pairs), then this step's slot refilled
+      Piece<T> py;
+#pragma unroll
+      for (int w = 0; w < (int)(sizeof(T) / 2); ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          py.w[w][q] = (uint32_t)__shfl((int)px[k].w[w][q], src_lane);
+      float x[8], y[8], d[8];
+      piece_floats(px[k], x);
+      piece_floats(py, y);
+      piece_floats(pc[k], d);
+      const int tok = w_lo + 4 * st + g;
+      load_step(st + kGramPrefetch, px[k], pc[k]);
+      if (K > 1) {
+        if (tok < w_hi) {
+          for (int mk = 1; mk < K; ++mk) {
+            Piece<T> pm;
+            load_piece(static_cast<const T*>(mem[mk].cond) + layer * mem[mk].cond_ls + head_off +
+                           8 * n + (int64_t)tok * mem[mk].cond_ts, pm);
+            float z[8];
+            piece_floats(pm, z);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += z[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] *= inv_k;
+      }
+      if (kind == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = d[q] - x[q];
+      } else if (kind == 3) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float2 r = cs[pair0 + j];
+          const float a = x[2 * j], b = x[2 * j + 1];
+          d[2 * j] = d[2 * j] - (a * r.x - b * r.y);
+          d[2 * j + 1] = d[2 * j + 1] - (b * r.x + a * r.y);
+        }
+      } else {
+        const float sg = kind == 1 ? -1.f : 1.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float2 r = cs[pair0 + q];
+          d[q] = d[q] - (x[q] * r.x + (sg * y[q]) * r.y);
+        }
+      }
+      int blk = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int b2 = b; b2 < 8; ++b2) {
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(d[b], d[b2], acc[blk], 0, 0, 0);
+          ++blk;
+        }
+    }
+  }
+
+  // partial sums of the four waves, added in wave order
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int k = 0; k < 36; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* dst = red + k * 256 + (4 * g + r) * 16 + n;
+          *dst = w == 0 ? acc[k][r] : *dst + acc[k][r];
+        }
+    }
+    __syncthreads();
+  }
+  // G' (permuted order) to the workspace, both triangles
+  float* gout = P.ws + J.gpart + ((int64_t)unit * J.splits + split) * (128 * 128);
+  int blk = 0;
+  for (int b = 0; b < 8; ++b)
+    for (int b2 = b; b2 < 8; ++b2, ++blk) {
+      const float* src = red + blk * 256;
+      const int i = tid >> 4, j = tid & 15;
+      gout[(16 * b + i) * 128 + 16 * b2 + j] = src[i * 16 + j];
+      if (b2 != b) gout[(16 * b2 + i) * 128 + 16 * b + j] = src[j * 16 + i];
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -702,6 +924,8 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
 
   const int r0 = lane, r1 = lane + 64;
   const int c0 = r0 < D ? r0 : 0, c1 = r1 < D ? r1 : 0;
+  // G stored permuted (gram_stream_kernel): element (k, c) at (p(k), p(c))
+  const int gp0 = J.gperm ? gperm_row(c0) : c0, gp1 = J.gperm ? gperm_row(c1) : c1;
   for (int h = 0; h < 2; ++h) {
     const int r = lane + 64 * h;
     if (r >= D) continue;
@@ -717,8 +941,9 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
     for (int c = 0; c < MP; ++c) y0[c] = y1[c] = 0.f;
 #pragma unroll 8
     for (int k = 0; k < D; ++k) {
-      const float g0 = G[(int64_t)k * D + c0];
-      const float g1 = G[(int64_t)k * D + c1];
+      const int64_t gk = (int64_t)(J.gperm ? gperm_row(k) : k) * D;
+      const float g0 = G[gk + gp0];
+      const float g1 = G[gk + gp1];
       const float4* xr = reinterpret_cast<const float4*>(buf + k * BS);
 #pragma unroll
       for (int q = 0; q < MP / 4; ++q) {
@@ -862,50 +1087,6 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
 #define KAMERA_PROJ_TOKENS 512
 #endif
 constexpr int kStreamTokens = KAMERA_PROJ_TOKENS;   // tokens per block (512: 8 tiles per wave)
-
-#define CGLOBAL __attribute__((address_space(1)))
-
-// Piece (8 features) held by lane group g in slot p of slab c.
-__host__ __device__ inline int stream_piece(int g, int p, int c, int S, int unit_layout, int hp) {
-  if (!unit_layout) return 16 * c + 4 * p + g;
-  const int pos = g * S + p;
-  if (pos < 2 * hp) return (pos & 1) ? hp + (pos >> 1) : (pos >> 1);
-  return pos;
-}
-
-// LDS row stride (floats) of the permuted X: the four rows one MFMA step reads (16 floats
-// each) land in distinct banks; wider heads take the plain stride to bound the LDS.
-__host__ __device__ inline int stream_sv(int width, int mp) {
-  if (width > 128) return mp;
-  return mp == 16 ? 16 : (mp == 64 ? 80 : 48);
-}
-
-template <typename T>
-struct Piece {
-  u32x4 w[sizeof(T) / 2];
-};
-
-template <typename T>
-__device__ __forceinline__ void load_piece(const T* p, Piece<T>& o) {
-  const CGLOBAL u32x4* q = (const CGLOBAL u32x4*)p;
-#pragma unroll
-  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) o.w[k] = q[k];
-}
-
-__device__ __forceinline__ void piece_floats(const Piece<uint16_t>& a, float* o) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[2 * k] = __uint_as_float(a.w[0][k] << 16);
-    o[2 * k + 1] = __uint_as_float(a.w[0][k] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void piece_floats(const Piece<float>& a, float* o) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[k] = __uint_as_float(a.w[0][k]);
-    o[4 + k] = __uint_as_float(a.w[1][k]);
-  }
-}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 2, 8))) void project_stream_kernel(CParams P) {
@@ -1100,7 +1281,7 @@ enum Kind { kGram = 0, kSubspace = 1, kProject = 2 };
 
 struct Launch {
   int kind;
-  int cls;                          // gram: NB; subspace: 0..4; project: 0..1, 2 = streamed
+  int cls;                          // gram: NB, 0 = streamed; subspace: 0..4; project: 0..1, 2 = streamed
   std::vector<int32_t> starts, job_of;
   int64_t blocks = 0;
   size_t off = 0;                   // byte offset of starts (job_of follows)
@@ -1231,6 +1412,7 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
         plan->members.push_back(c);
       }
       J.rot_dim = g.rotate ? M.rope_dim : 0;
+      J.gperm = g.width == 128 ? 1 : 0;   // gram_stream_kernel
       J.n_tokens = k.n_tokens;
       J.m = k.m;
       J.mp = (k.m + 15) / 16 * 16;
@@ -1289,7 +1471,8 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     const int tblocks = stream ? (J.n_tokens + kStreamTokens - 1) / kStreamTokens
                                : (J.n_tokens + kProjTokens - 1) / kProjTokens;
     const size_t lds = stream ? (size_t)J.width * stream_sv(J.width, J.mp) * sizeof(float) : 0;
-    bool ok = add(kGram, J.te / 32, (int)j, (int64_t)J.n_units * J.n_pairs * J.splits) &&
+    bool ok = add(kGram, J.gperm ? 0 : J.te / 32, (int)j,
+                  (int64_t)J.n_units * J.n_pairs * J.splits) &&
               add(kSubspace, subspace_class(J.width, J.mp), (int)j, J.n_units) &&
               add(kProject, stream ? 2 : (J.width <= 128 ? 0 : 1), (int)j,
                   (int64_t)J.n_units * tblocks, lds);
@@ -1400,6 +1583,7 @@ hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
   switch (L.kind) {
     case kGram:
       switch (L.cls) {
+        case 0: gram_stream_kernel<T><<<grid, block, 0, stream>>>(P); break;
         case 1: gram_kernel<T, 1><<<grid, block, 0, stream>>>(P); break;
         case 2: gram_kernel<T, 2><<<grid, block, 0, stream>>>(P); break;
         case 3: gram_kernel<T, 3><<<grid, block, 0, stream>>>(P); break;
