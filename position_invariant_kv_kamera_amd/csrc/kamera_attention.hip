@@ -101,8 +101,11 @@ __device__ __forceinline__ int64_t row_at(const AParams& P, int64_t p, int32_t p
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
+// Compiled for 3 waves per SIMD: 151 VGPRs at D = 128, no spills (the unconstrained choice,
+// 184 registers at 2 waves per SIMD, streamed ~12 % slower; 4 waves spill).
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_segment_kernel(AParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void attn_segment_kernel(AParams P) {
   constexpr int KS = D / 32;   // bf16 MFMA k-steps of Q K^T
   constexpr int NC = D / 16;   // 16-feature column blocks of O
   constexpr int VS = D + 8;    // LDS row stride of a V tile (bf16): rows start in distinct banks
