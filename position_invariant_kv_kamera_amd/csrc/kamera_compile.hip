@@ -935,27 +935,47 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
   wave_lds_sync();
 
   for (int round = 0; round < P.n_iter; ++round) {
-    // Y = G X for rows r0, r1 (G symmetric: column r read as row r)
+    // Y = G X for rows r0, r1. G is symmetric, so each lane reads its own rows of G along
+    // their stored order with 16-byte loads (stored column kappa is feature k = q(kappa)),
+    // keeping the next 16 columns in flight while it uses the current ones.
     float y0[MP], y1[MP];
 #pragma unroll
     for (int c = 0; c < MP; ++c) y0[c] = y1[c] = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-      const int64_t gk = (int64_t)(J.gperm ? gperm_row(k) : k) * D;
-      const float g0 = G[gk + gp0];
-      const float g1 = G[gk + gp1];
-      const float4* xr = reinterpret_cast<const float4*>(buf + k * BS);
+    const float* g0row = G + (int64_t)gp0 * D;
+    const float* g1row = G + (int64_t)gp1 * D;
+    f32x4 ra[4], rb[4];
 #pragma unroll
-      for (int q = 0; q < MP / 4; ++q) {
-        const float4 x = xr[q];
-        y0[4 * q] += g0 * x.x;
-        y0[4 * q + 1] += g0 * x.y;
-        y0[4 * q + 2] += g0 * x.z;
-        y0[4 * q + 3] += g0 * x.w;
-        y1[4 * q] += g1 * x.x;
-        y1[4 * q + 1] += g1 * x.y;
-        y1[4 * q + 2] += g1 * x.z;
-        y1[4 * q + 3] += g1 * x.w;
+    for (int c = 0; c < 4; ++c) {
+      ra[c] = ((const CGLOBAL f32x4*)g0row)[c];
+      rb[c] = ((const CGLOBAL f32x4*)g1row)[c];
+    }
+    for (int kc0 = 0; kc0 < D; kc0 += 16) {   // D is a multiple of 32
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kc = kc0 + 4 * c;
+        const f32x4 ga = ra[c], gb = rb[c];
+        const int kn = kc + 16 < D ? kc + 16 : kc;   // past the end: reload (unused)
+        ra[c] = ((const CGLOBAL f32x4*)(g0row + kn))[0];
+        rb[c] = ((const CGLOBAL f32x4*)(g1row + kn))[0];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kap = kc + t;
+          const int k = J.gperm ? 8 * (kap & 15) + (kap >> 4) : kap;
+          const float g0 = ga[t], g1 = gb[t];
+          const float4* xr = reinterpret_cast<const float4*>(buf + k * BS);
+#pragma unroll
+          for (int q = 0; q < MP / 4; ++q) {
+            const float4 x = xr[q];
+            y0[4 * q] += g0 * x.x;
+            y0[4 * q + 1] += g0 * x.y;
+            y0[4 * q + 2] += g0 * x.z;
+            y0[4 * q + 3] += g0 * x.w;
+            y1[4 * q] += g1 * x.x;
+            y1[4 * q + 1] += g1 * x.y;
+            y1[4 * q + 2] += g1 * x.z;
+            y1[4 * q + 3] += g1 * x.w;
+          }
+        }
       }
     }
     wave_lds_sync();   // every lane has read X
