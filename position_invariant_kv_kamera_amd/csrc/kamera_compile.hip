@@ -794,11 +794,10 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
 // ---------------------------------------------------------------------------------------
 // subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
 // wave-synchronous. MP = mp exactly. Per wave in LDS:
-//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (the
-//       triangular step runs over columns from last to first, so each x_j only replaces a
-//       y_j no later column needs);
-//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), then its Cholesky factor L (lower) and L^-1
-//       (strict upper, transposed: (L^-1)_rj at [j][r]); its diagonal is inv.
+//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
+//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
+//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
+//       inv holds 1 / diag(L) (0 for a collapsed column).
 // Lane l owns rows l and l + 64.
 // ---------------------------------------------------------------------------------------
 
@@ -830,47 +829,67 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
     lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   wave_lds_sync();
-  // Cholesky, left-looking: lane i owns row i
+  // Cholesky, right-looking: lane i owns row i of S, which becomes row i of L. Step j: the
+  // owner of row j takes the pivot (collapsed when what is left of s_jj is at most kDeadTol
+  // times its starting value), the rows below scale column j, then each updates its own part
+  // of the trailing matrix (its next diagonal included, so the next pivot needs no wait).
   const int i = lane;
+  const double sii0 = i < m ? lm[i * SS + i] : 0.0;
   for (int j = 0; j < m; ++j) {
-    double dot = 0.0;
-    if (i >= j && i < m)
-      for (int a = 0; a < j; ++a) dot += lm[i * SS + a] * lm[j * SS + a];
     if (i == j) {
-      const double sjj = lm[j * SS + j];
-      const double d = sjj - dot;
-      const bool dk = d <= kDeadTol * sjj;
+      const double d = lm[j * SS + j];
+      const bool dk = d <= kDeadTol * sii0;
       const double ljj = dk ? 0.0 : sqrt(d);
       lm[j * SS + j] = ljj;
       inv[j] = dk ? 0.0 : 1.0 / ljj;
       dead[j] = dk ? 1 : 0;
     }
     wave_lds_sync();
-    if (i > j && i < m) lm[i * SS + j] = (lm[i * SS + j] - dot) * inv[j];
-    wave_lds_sync();
-  }
-  // L^-1: lane j solves L z = e_j; z_r (r > j) goes to lm[j][r]
-  if (i < m) {
-    const int j = i;
-    for (int r = j + 1; r < m; ++r) {
-      double acc = lm[r * SS + j] * inv[j];
-      for (int a = j + 1; a < r; ++a) acc += lm[r * SS + a] * lm[j * SS + a];
-      lm[j * SS + r] = -acc * inv[r];
+    double lij = 0.0;
+    if (i > j && i < m) {
+      lij = lm[i * SS + j] * inv[j];
+      lm[i * SS + j] = lij;
     }
+    wave_lds_sync();
+    if (i > j && i < m)
+      for (int k = j + 1; k <= i; ++k) lm[i * SS + k] -= lij * lm[k * SS + j];
   }
   wave_lds_sync();
-  // X = Y L^-T: x_rj = y_rj inv_j + sum_{a<j} y_ra (L^-1)_ja, columns last to first, in place
-  for (int h = 0; h < 2; ++h) {
-    const int r = lane + 64 * h;
-    if (r >= D) continue;
-    float* row = buf + r * BS;
-    for (int j = m - 1; j >= 0; --j) {
-      double acc = (double)row[j] * inv[j];
-#pragma unroll 4
-      for (int a = 0; a < j; ++a) acc += (double)row[a] * lm[a * SS + j];
-      float v = (float)acc;
-      if (reseed_round >= 0 && dead[j]) v = seed_value(r, j, reseed_round + 1);
-      row[j] = v;
+  // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
+  // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
+  // pivot, so a reseeded x_ra adds nothing to the columns after it.
+  {
+    const int r0 = lane, r1 = lane + 64;
+    const bool on0 = r0 < D, on1 = r1 < D;
+    float* row0 = buf + r0 * BS;
+    float* row1 = buf + (on1 ? r1 : r0) * BS;
+    for (int j = 0; j < m; ++j) {
+      const double* lj = lm + j * SS;
+      double p0[4] = {0.0, 0.0, 0.0, 0.0}, p1[4] = {0.0, 0.0, 0.0, 0.0};
+      int a = 0;
+      for (; a + 4 <= j; a += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const double l = lj[a + u];
+          p0[u] += (double)row0[a + u] * l;
+          p1[u] += (double)row1[a + u] * l;
+        }
+      }
+      for (; a < j; ++a) {
+        const double l = lj[a];
+        p0[0] += (double)row0[a] * l;
+        p1[0] += (double)row1[a] * l;
+      }
+      const double s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
+      const double s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+      float v0 = (float)(((double)row0[j] - s0) * inv[j]);
+      float v1 = (float)(((double)row1[j] - s1) * inv[j]);
+      if (reseed_round >= 0 && dead[j]) {
+        v0 = seed_value(r0, j, reseed_round + 1);
+        v1 = seed_value(r1, j, reseed_round + 1);
+      }
+      if (on0) row0[j] = v0;
+      if (on1) row1[j] = v1;
     }
   }
   wave_lds_sync();
