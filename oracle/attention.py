@@ -11,10 +11,17 @@ attention over each chunk. Definitions (one query head, scores s_t = scale * <q,
     lse = log sum_t exp(s_t),   o = sum_t exp(s_t - lse) v_t
     merge of parts (o_i, lse_i):  L = log sum_i exp(lse_i),  o = sum_i exp(lse_i - L) o_i
 An empty part has lse = -inf and o = 0 and drops out of a merge.
+
+chunk_attention: decode attention over cached chunks that are read where they are stored,
+never relocated. Each chunk contributes the keys and values the reuse operator defines for it
+(relocation by its shift plus its rank-m patch, the technical summary's reuse equation), kept
+exact in fp64; the result is attention over all chunks' tokens together.
 """
 from __future__ import annotations
 
 import numpy as np
+
+import oracle as _core
 
 
 def decode_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
@@ -48,3 +55,33 @@ def state_merge(outs: list, lses: list):
 def score_bounds(q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
     """sum_d |q_d k_td| * scale per head and token: the scale of each score's terms."""
     return abs(scale) * (np.abs(np.asarray(q, np.float64)) @ np.abs(np.asarray(K, np.float64)).T)
+
+
+def chunk_keys_values(chunk: dict, *, layout: int, theta: float, rot_dim: int | None = None,
+                      inv_freq=None, pair_section=None):
+    """(K', V') of one chunk and one KV head in fp64: K' = R(delta) K + Uk Vk^T and
+    V' = V + Uv Vv^T (the reuse operator's rows, unrounded). chunk: 'K', 'V' (tokens x D, in
+    the model's element type), 'delta' (and 'section_delta' when pair_section is given),
+    optional 'Uk', 'Vk', 'Uv', 'Vv'."""
+    pd = None
+    if pair_section is not None:
+        pd = _core.pair_deltas(pair_section, chunk["section_delta"])
+    k, _ = _core.segment(chunk["K"], rotate=True, layout=layout, delta=int(chunk["delta"]),
+                         theta=theta, U=chunk.get("Uk"), V=chunk.get("Vk"), rot_dim=rot_dim,
+                         inv_freq=inv_freq, pair_delta=pd)
+    v, _ = _core.segment(chunk["V"], rotate=False, U=chunk.get("Uv"), V=chunk.get("Vv"))
+    return k, v
+
+
+def chunk_attention(q: np.ndarray, chunks: list, scale: float, *, layout: int, theta: float,
+                    rot_dim: int | None = None, inv_freq=None, pair_section=None):
+    """q (heads x D, fp64) over the tokens of every chunk (see chunk_keys_values) ->
+    (o (heads x D), lse (heads,))."""
+    D = np.asarray(q).shape[1]
+    Ks, Vs = [np.zeros((0, D))], [np.zeros((0, D))]
+    for c in chunks:
+        k, v = chunk_keys_values(c, layout=layout, theta=theta, rot_dim=rot_dim,
+                                 inv_freq=inv_freq, pair_section=pair_section)
+        Ks.append(k)
+        Vs.append(v)
+    return decode_attention(q, np.concatenate(Ks), np.concatenate(Vs), scale)
