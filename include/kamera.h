@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KAMERA_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define KAMERA_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 typedef enum kamera_status {
   KAMERA_OK = 0,
@@ -360,6 +360,52 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
 kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_dim,
                                  const float* part_out, const float* part_lse, float* out,
                                  float* lse, void* stream);
+
+/* ---- Attention over chunks read in place ---------------------------------------------
+ * Decode attention, one query token per sequence, over cached chunks that are never
+ * relocated (the consumer side of the reuse equation, technical summary §2; chunks are
+ * combined by the abstract's state merge). Each chunk keeps its canonical rows (chunk-local
+ * positions 0 .. n_tokens-1, as kamera_chunk.src) and its patch, and is read as the reuse
+ * operator would have written it,
+ *     k'_t = R(delta) k_t + U_K(t) V_K^T,      v'_t = v_t + U_V(t) V_V^T,
+ * without forming k' or v': R(delta) is orthogonal, so <q, R(delta) k> = <R(-delta) q, k>
+ * (the query turns by -delta, once per chunk), the key patch adds U_K(t) . (V_K^T q) to the
+ * score and the value patch adds (sum_t p_t U_V(t)) V_V^T to the output. Per query and query
+ * head:  out = sum over the tokens of its chunks of softmax_t(scale <q, k'_t>) v'_t,  and lse.
+ * q: [n_queries][n_q_heads][head_dim] bf16 (device); out: [n_queries][n_q_heads][head_dim]
+ * fp32; lse: [n_queries][n_q_heads] fp32 (a query with no tokens gets out = 0, lse = -inf).
+ * Supported: GQA/MHA bf16, head_dim 64 or 128 (RoPE as described by kamera_model: rope_dim,
+ * layout, frequency table, sections), up to 16 query heads per KV head, patch ranks m in
+ * [0, 64] per channel. Canonical rows, q and their strides must be 16-byte aligned.
+ * Precision: the turned query and V_K^T q are fp32, split into two bf16 terms each for bf16
+ * MFMA (products exact, fp32 sums); softmax and P V as in kamera_decode_attention. */
+typedef struct kamera_attn_chunk {
+  int32_t n_tokens;
+  int32_t reserved0;             /* 0 */
+  int64_t delta;                 /* as kamera_chunk.delta */
+  int64_t delta_sections[2];     /* as kamera_chunk.delta_sections */
+  kamera_src src[2];             /* canonical K and V rows of all layers */
+  kamera_patch_ref patch[2];     /* as kamera_chunk.patch; m <= 64 (0: none) */
+} kamera_attn_chunk;
+
+/* The chunks query j attends: chunks[first_chunk .. first_chunk + n_chunks). */
+typedef struct kamera_chunk_query {
+  int32_t first_chunk;
+  int32_t n_chunks;
+} kamera_chunk_query;
+
+/* Workspace bytes for kamera_chunk_attention (0 on invalid arguments). */
+size_t kamera_chunk_attention_workspace_bytes(const kamera_model* model, int32_t n_q_heads,
+                                              const kamera_attn_chunk* chunks, int32_t n_chunks,
+                                              const kamera_chunk_query* queries,
+                                              int32_t n_queries);
+
+kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
+                                     const kamera_attn_chunk* chunks, int32_t n_chunks,
+                                     const kamera_chunk_query* queries, int32_t n_queries,
+                                     const void* q, int32_t n_q_heads, float scale, float* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 const char* kamera_status_string(kamera_status status);
 const char* kamera_last_error(void); /* per-thread; "" if none */

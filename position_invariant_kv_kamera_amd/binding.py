@@ -83,6 +83,16 @@ class KameraAttnQuery(ctypes.Structure):
     _fields_ = [("kv_start", c_i32), ("kv_len", c_i32)]
 
 
+class KameraAttnChunk(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i32), ("reserved0", c_i32), ("delta", c_i64),
+                ("delta_sections", c_i64 * 2), ("src", KameraSrc * 2),
+                ("patch", KameraPatchRef * 2)]
+
+
+class KameraChunkQuery(ctypes.Structure):
+    _fields_ = [("first_chunk", c_i32), ("n_chunks", c_i32)]
+
+
 class KameraOrbitMember(ctypes.Structure):
     _fields_ = [("delta", c_i64), ("delta_sections", c_i64 * 2), ("conditioned", KameraSrc * 2)]
 
@@ -150,6 +160,15 @@ def load_library() -> ctypes.CDLL:
     lib.kamera_decode_attention.restype = ctypes.c_int
     lib.kamera_state_merge.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.kamera_state_merge.restype = ctypes.c_int
+    lib.kamera_chunk_attention_workspace_bytes.argtypes = [
+        ctypes.POINTER(KameraModel), c_i32, ctypes.POINTER(KameraAttnChunk), c_i32,
+        ctypes.POINTER(KameraChunkQuery), c_i32]
+    lib.kamera_chunk_attention_workspace_bytes.restype = c_size
+    lib.kamera_chunk_attention.argtypes = [
+        ctypes.POINTER(KameraModel), c_i32, ctypes.POINTER(KameraAttnChunk), c_i32,
+        ctypes.POINTER(KameraChunkQuery), c_i32, c_vp, c_i32, ctypes.c_float, c_vp, c_vp, c_vp,
+        c_size, c_vp]
+    lib.kamera_chunk_attention.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -459,6 +478,74 @@ def run_orbit_compile(model: KameraModel, items, *, n_iter: int = 8,
 
 
 # ---- consumer side ---------------------------------------------------------------------------
+
+def kamera_chunk_attention_workspace_bytes(model, n_q_heads, chunks, n_chunks, queries,
+                                           n_queries) -> int:
+    return int(load_library().kamera_chunk_attention_workspace_bytes(
+        ctypes.byref(model) if model is not None else None, int(n_q_heads), chunks,
+        int(n_chunks), queries, int(n_queries)))
+
+
+def kamera_chunk_attention(model, layer, chunks, n_chunks, queries, n_queries, q, n_q_heads,
+                           scale, out, lse, workspace, workspace_bytes, stream):
+    return int(load_library().kamera_chunk_attention(
+        ctypes.byref(model) if model is not None else None, int(layer), chunks, int(n_chunks),
+        queries, int(n_queries), q, int(n_q_heads), float(scale), out, lse, workspace,
+        int(workspace_bytes), stream))
+
+
+def attn_chunks_of(items):
+    """A KameraAttnChunk array from dicts: 'n_tokens', 'delta', optional 'delta_sections',
+    'src' (two (ptr, layer_stride, token_stride)), optional 'patch' (two
+    (m, U ptr, u_layer_stride, u_head_stride, V ptr, v_layer_stride, v_head_stride) or None)."""
+    arr = (KameraAttnChunk * max(1, len(items)))()
+    for i, it in enumerate(items):
+        c = KameraAttnChunk()
+        c.n_tokens = int(it["n_tokens"])
+        c.delta = int(it["delta"])
+        ds = it.get("delta_sections", (it["delta"], it["delta"]))
+        c.delta_sections[0], c.delta_sections[1] = int(ds[0]), int(ds[1])
+        for ch in range(2):
+            ptr, ls, ts = it["src"][ch]
+            c.src[ch] = KameraSrc(ptr, int(ls), int(ts))
+            pr = (it.get("patch") or (None, None))[ch]
+            if pr is not None:
+                m, U, uls, uhs, V, vls, vhs = pr
+                c.patch[ch] = KameraPatchRef(int(m), 0, U, int(uls), int(uhs), V, int(vls),
+                                             int(vhs))
+        arr[i] = c
+    return arr
+
+
+def chunk_queries_of(spans):
+    """A KameraChunkQuery array from (first_chunk, n_chunks) pairs."""
+    arr = (KameraChunkQuery * max(1, len(spans)))()
+    for i, (a, n) in enumerate(spans):
+        arr[i] = KameraChunkQuery(int(a), int(n))
+    return arr
+
+
+def run_chunk_attention(model: KameraModel, layer: int, chunk_items, spans, q, scale, *,
+                        stream=None):
+    """kamera_chunk_attention of q ([n_queries, n_q_heads, head_dim] bf16 device tensor), query j
+    over chunks spans[j] = (first, count) of chunk_items; returns (out fp32, lse)."""
+    import torch
+    n, heads, D = q.shape
+    chunks = attn_chunks_of(chunk_items)
+    queries = chunk_queries_of(spans)
+    need = kamera_chunk_attention_workspace_bytes(model, heads, chunks, len(chunk_items), queries, n)
+    if need == 0:
+        raise KameraError(KAMERA_ERR_INVALID_ARGUMENT, kamera_last_error())
+    ws = Workspace(nbytes=need, device=q.device)
+    out = torch.empty((n, heads, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((n, heads), dtype=torch.float32, device=q.device)
+    s = current_stream_ptr() if stream is None else stream
+    check(kamera_chunk_attention(model, layer, chunks, len(chunk_items), queries, n,
+                                 q.data_ptr(), heads, scale, out.data_ptr(), lse.data_ptr(),
+                                 ws.ptr, ws.nbytes, s))
+    out._kamera_ws = ws
+    return out, lse
+
 
 def attn_queries_of(ranges):
     """A KameraAttnQuery array from (kv_start, kv_len) pairs."""

@@ -347,6 +347,356 @@ __global__ __launch_bounds__(64) void state_merge_kernel(const float* part_out,
             out + (int64_t)r * D, lse + r);
 }
 
+
+// ---------------------------------------------------------------------------------------
+// chunk_attn_kernel<D>: attention over chunks read in place. Block = (segment of one chunk,
+// KV head), 4 waves over 16-token tiles as attn_segment_kernel. The score contraction runs
+// over the head's features and then over the key patch's rank:
+//   s_t = <q', k_t> + <w, U_K(t)>,   q' = R(-delta) q,   w = V_K^T q,
+// both fp32 and split into bf16 high and low parts (two exact-product MFMA passes each). The
+// value patch rides along P V: each 16-token V tile in LDS is followed by the tokens' U_V
+// rows, so the same MFMAs accumulate z = sum_t p_t U_V(t) next to o; after the wave merge the
+// block adds z V_V^T and normalises.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kMaxViewRank = 64;
+
+struct alignas(16) VChunk {
+  const uint16_t* k;    // canonical K rows of the layer: token t, head h at k + t*k_ts + h*D
+  const uint16_t* v;
+  const uint16_t* uk;   // U_K of the layer (head h at + h*uk_hs, token t at + t*mk), or NULL
+  const uint16_t* vk;   // V_K of the layer (head h at + h*vk_hs, feature f at + f*mk)
+  const uint16_t* uv;
+  const uint16_t* vv;
+  int64_t k_ts, v_ts;
+  int64_t uk_hs, vk_hs, uv_hs, vv_hs;
+  int64_t delta, delta_s1, delta_s2;
+  int32_t n_tokens, mk, mv;
+  int32_t vec_u;        // U rows may be read 16 bytes at a time (both channels)
+};
+
+struct alignas(16) VSeg {
+  int32_t chunk, t_lo, t_hi, query;
+};
+
+struct VParams {
+  const VChunk* chunks;
+  const VSeg* segs;
+  const uint16_t* q;
+  float* part_o;
+  float* part_lse;
+  const double* inv_freq;       // device (workspace) or NULL
+  const uint8_t* pair_section;  // device (workspace) or NULL
+  double theta;
+  float scale;
+  int32_t n_q, n_kv, group, rot_dim, layout;
+};
+
+// 8 consecutive bf16 of a U row from element r0 (zeros at and past m).
+__device__ __forceinline__ u32x4 load_u8(const uint16_t* row, int r0, int m, bool vec) {
+  if (r0 >= m) return u32x4{0u, 0u, 0u, 0u};
+  if (vec && r0 + 8 <= m) return *reinterpret_cast<const u32x4*>(row + r0);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = r0 + 2 * e < m ? row[r0 + 2 * e] : 0u;
+    const uint32_t hi = r0 + 2 * e + 1 < m ? row[r0 + 2 * e + 1] : 0u;
+    w[e] = lo | (hi << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Eight fp32 values as two bf16x8 terms: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split8(const float* x, bf16x8* hi, bf16x8* lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
+    const float r0 = x[2 * e] - __uint_as_float((uint32_t)h0 << 16);
+    const float r1 = x[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16);
+    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[e] = (uint32_t)bf16_rne(r0) | ((uint32_t)bf16_rne(r1) << 16);
+  }
+  *hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  *lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void chunk_attn_kernel(VParams P) {
+  constexpr int KS = D / 32;                 // bf16 k-steps over the features
+  constexpr int PK = kMaxViewRank / 32;      // bf16 k-steps over the key patch rank
+  constexpr int NC = D / 16;                 // column blocks of o
+  constexpr int NZ = kMaxViewRank / 16;      // column blocks of z
+  constexpr int VS = D + kMaxViewRank + 8;   // LDS row: V row, then the token's U_V row
+  constexpr int PSTR = 17;
+  constexpr int MW = D + kMaxViewRank;       // merged row: o, then z
+  __shared__ __align__(16) uint16_t vt[4][kTile * VS];
+  __shared__ float pt[4][kTile * PSTR];
+  __shared__ float mrg_m[4][kMaxGroup], mrg_l[4][kMaxGroup];
+  __shared__ float mrg_o[kMaxGroup * MW];    // also holds the query rows during set-up
+  __shared__ float wsh[kMaxGroup][kMaxViewRank + 1];
+  __shared__ float2 cs[64];
+
+  const int sidx = blockIdx.x / P.n_kv;
+  const int h = blockIdx.x - sidx * P.n_kv;
+  const VSeg S = P.segs[sidx];
+  const VChunk& C = P.chunks[S.chunk];
+  const int j = S.query;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int mk = C.mk, mv = C.mv;
+  const bool vec = C.vec_u != 0;
+
+  // set-up: the chunk's phases, the query rows (fp32, in mrg_o) and w = V_K^T q
+  const int R = P.rot_dim;
+  for (int i = tid; i < R / 2; i += kThreads) {
+    const double inv = P.inv_freq ? P.inv_freq[i] : pow(P.theta, -2.0 * (double)i / (double)R);
+    const int sec = P.pair_section ? (int)P.pair_section[i] : 0;
+    const int64_t d = sec == 0 ? C.delta : (sec == 1 ? C.delta_s1 : C.delta_s2);
+    double sn, cn;
+    sincos((double)d * inv, &sn, &cn);
+    cs[i] = make_float2((float)cn, (float)sn);
+  }
+  float* qs = mrg_o;   // [group][D]
+  const uint16_t* qrow0 = P.q + ((int64_t)j * P.n_q + h * P.group) * D;
+  for (int idx = tid; idx < P.group * D; idx += kThreads)
+    qs[idx] = __uint_as_float((uint32_t)qrow0[idx] << 16);
+  __syncthreads();
+  // V_K of head h staged in LDS (the V tiles are not in use yet)
+  uint16_t* stage = &vt[0][0];
+  if (mk > 0) {
+    const uint16_t* vkh = C.vk + h * C.vk_hs;
+    for (int idx = tid; idx < D * mk; idx += kThreads) stage[idx] = vkh[idx];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < P.group * mk; idx += kThreads) {
+    const int row = idx / mk, r = idx - row * mk;
+    float acc = 0.f;
+    for (int f = 0; f < D; ++f) acc += qs[row * D + f] * bf16_lo(stage[f * mk + r]);
+    wsh[row][r] = acc;
+  }
+  __syncthreads();
+
+  // operands of this lane: query row col, features 32k + 8 grp + e, turned by -delta
+  bf16x8 qh[KS], ql[KS], wh[PK], wl[PK];
+  {
+    const bool on = col < P.group;
+    const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = 32 * k + 8 * grp + e;
+        float v = 0.f;
+        if (on) {
+          v = qs[col * D + f];
+          if (f < R) {
+            int pair, other;
+            bool first;
+            if (inter) {
+              pair = f >> 1;
+              first = (f & 1) == 0;
+              other = first ? f + 1 : f - 1;
+            } else {
+              first = f < R / 2;
+              pair = first ? f : f - R / 2;
+              other = first ? f + R / 2 : f - R / 2;
+            }
+            const float y = qs[col * D + other];
+            const float2 r = cs[pair];
+            // R(-delta): first' = x c + y s, second' = x c - y s (x: own, y: partner)
+            v = first ? v * r.x + y * r.y : v * r.x - y * r.y;
+          }
+        }
+        x[e] = v;
+      }
+      split8(x, &qh[k], &ql[k]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * s2 + 8 * grp + e;
+        x[e] = on && r < mk ? wsh[col][r] : 0.f;
+      }
+      split8(x, &wh[s2], &wl[s2]);
+    }
+  }
+  __syncthreads();   // qs (in mrg_o) is free again
+
+  float m[4], l[4];
+  f32x4 o[NC], z[NZ];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NZ; ++c) z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kh = C.k + h * D;
+  const uint16_t* vh = C.v + h * D;
+  const uint16_t* ukh = mk > 0 ? C.uk + h * C.uk_hs : nullptr;
+  const uint16_t* uvh = mv > 0 ? C.uv + h * C.uv_hs : nullptr;
+  for (int t0 = S.t_lo + kTile * wave; t0 < S.t_hi; t0 += 4 * kTile) {
+    const int t = t0 + col;
+    const bool valid = t < S.t_hi;
+    bf16x8 kb[KS];
+    u32x4 vraw[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (valid) {
+        kb[k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp));
+        vraw[k] = *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp);
+      } else {
+        kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        vraw[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // S = Q' K^T + W U_K^T: lane holds query rows 4 grp + r of token col
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[k], kb[k], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[k], kb[k], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2) {
+      if (32 * s2 < mk) {
+        const u32x4 u = valid ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
+                              : u32x4{0u, 0u, 0u, 0u};
+        const bf16x8 ub = __builtin_bit_cast(bf16x8, u);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh[s2], ub, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl[s2], ub, sacc, 0, 0, 0);
+      }
+    }
+    // V rows and U_V rows of the tile to LDS (token col)
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = vraw[k];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxViewRank / 32; ++s2) {
+      const u32x4 u = valid && 32 * s2 < mv
+                          ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
+                          : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + D + 32 * s2 + 8 * grp]) = u;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sc = valid ? sacc[r] * P.scale : -INFINITY;
+      float mx = sc;
+      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mn = fmaxf(m[r], mx);
+      float corr = 1.f, p = 0.f;
+      if (mn != -INFINITY) {
+        corr = expf(m[r] - mn);
+        p = expf(sc - mn);
+      }
+      float sum = p;
+      sum += __shfl_xor(sum, 8, 16);
+      sum += __shfl_xor(sum, 4, 16);
+      sum += __shfl_xor(sum, 2, 16);
+      sum += __shfl_xor(sum, 1, 16);
+      l[r] = l[r] * corr + sum;
+      m[r] = mn;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c][r] *= corr;
+#pragma unroll
+      for (int c = 0; c < NZ; ++c) z[c][r] *= corr;
+      pt[wave][(4 * grp + r) * PSTR + col] = p;
+    }
+    wave_lds_sync();
+    // o += P V and z += P U_V: A[q][k] = P[q][4 k4 + k], B[k][f] = row 4 k4 + k of the tile
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float a = pt[wave][col * PSTR + 4 * k4 + grp];
+      const uint16_t* vr = &vt[wave][(4 * k4 + grp) * VS];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bf16_lo(vr[16 * c + col]), o[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < NZ; ++c)
+        if (16 * c < mv)
+          z[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bf16_lo(vr[D + 16 * c + col]), z[c],
+                                                      0, 0, 0);
+    }
+    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+  }
+
+  // merge the four waves' states (as attn_segment_kernel), o and z together
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mrg_m[wave][4 * grp + r] = m[r];
+      mrg_l[wave][4 * grp + r] = l[r];
+    }
+  }
+  __syncthreads();
+  float wgt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rw = 4 * grp + r;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
+    wgt[r] = M == -INFINITY ? 0.f : expf(m[r] - M);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = &mrg_o[(4 * grp + r) * MW];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const float v = o[c][r] * wgt[r];
+          dst[16 * c + col] = w == 0 ? v : dst[16 * c + col] + v;
+        }
+#pragma unroll
+        for (int c = 0; c < NZ; ++c) {
+          const float v = z[c][r] * wgt[r];
+          dst[D + 16 * c + col] = w == 0 ? v : dst[D + 16 * c + col] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // V_V of head h staged in LDS (every wave is past its last tile)
+  if (mv > 0) {
+    const uint16_t* vvh = C.vv + h * C.vv_hs;
+    for (int idx = tid; idx < D * mv; idx += kThreads) stage[idx] = vvh[idx];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < P.group * D; idx += kThreads) {
+    const int rw = idx / D, f = idx - rw * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
+    float L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * expf(mrg_m[w][rw] - M);
+    }
+    float acc = mrg_o[rw * MW + f];
+    for (int r = 0; r < mv; ++r) acc += mrg_o[rw * MW + D + r] * bf16_lo(stage[f * mv + r]);
+    const int64_t orow = (int64_t)sidx * P.n_q + h * P.group + rw;
+    P.part_o[orow * D + f] = M == -INFINITY ? 0.f : acc / L;
+    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M + logf(L);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------------------
@@ -417,6 +767,112 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
   plan->part_lse_off = round_up(plan->part_o_off + segs * n_q_heads * D * sizeof(float), 256);
   plan->total = round_up(plan->part_lse_off + segs * n_q_heads * sizeof(float), 256);
   plan->total = std::max<size_t>(plan->total, 256);
+  return KAMERA_OK;
+}
+
+
+// Relocation-free read: validation and layout of the device tables.
+struct VPlan {
+  std::vector<VSeg> segs;
+  std::vector<AQuery> queries;   // seg_start / n_segs per query, for attn_merge_kernel
+  int32_t seg = KAMERA_ATTN_SEGMENT;
+  size_t freq_off = 0, sec_off = 0, chunk_off = 0, seg_off = 0, query_off = 0;
+  size_t part_o_off = 0, part_lse_off = 0, total = 0;
+};
+
+kamera_status chunk_attention_geometry(const kamera_model* model, int32_t n_q_heads,
+                                       const kamera_attn_chunk* chunks, int32_t n_chunks,
+                                       const kamera_chunk_query* queries, int32_t n_queries,
+                                       VPlan* plan) {
+  kamera_status st = validate_model(model);
+  if (st != KAMERA_OK) return st;
+  if (model->family != KAMERA_FAMILY_GQA)
+    return fail(KAMERA_ERR_UNSUPPORTED, "chunk attention supports GQA/MHA models");
+  if (model->dtype != KAMERA_DTYPE_BF16)
+    return fail(KAMERA_ERR_UNSUPPORTED, "chunk attention supports bf16 rows");
+  if (model->head_dim != 64 && model->head_dim != 128)
+    return fail(KAMERA_ERR_UNSUPPORTED, "chunk attention needs head_dim 64 or 128 (got %d)",
+                model->head_dim);
+  if (n_q_heads <= 0 || n_q_heads % model->n_kv_heads)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", n_q_heads,
+                model->n_kv_heads);
+  if (n_q_heads / model->n_kv_heads > kMaxGroup)
+    return fail(KAMERA_ERR_UNSUPPORTED, "more than %d query heads per KV head", kMaxGroup);
+  if (n_chunks < 0 || n_queries < 0)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "n_chunks and n_queries must be >= 0");
+  if (n_chunks > 0 && !chunks) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunks is NULL");
+  if (n_queries > 0 && !queries) return fail(KAMERA_ERR_INVALID_ARGUMENT, "queries is NULL");
+  if ((int64_t)n_queries * n_q_heads > INT32_MAX)
+    return fail(KAMERA_ERR_UNSUPPORTED, "too many query rows");
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_attn_chunk& c = chunks[i];
+    if (c.n_tokens < 0) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d: n_tokens < 0", i);
+    for (int ch = 0; ch < 2; ++ch) {
+      const kamera_patch_ref& pr = c.patch[ch];
+      if (pr.m < 0 || pr.m > kMaxViewRank)
+        return fail(pr.m < 0 ? KAMERA_ERR_INVALID_ARGUMENT : KAMERA_ERR_UNSUPPORTED,
+                    "chunk %d channel %d: m = %d outside [0, %d]", i, ch, pr.m, kMaxViewRank);
+      if (c.n_tokens == 0) continue;
+      const kamera_src& sr = c.src[ch];
+      if (!sr.ptr) return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: src is NULL", i, ch);
+      if (!aligned16(sr.ptr) || sr.token_stride % 8 || sr.layer_stride % 8)
+        return fail(KAMERA_ERR_UNSUPPORTED,
+                    "chunk %d channel %d: canonical rows must start on 16-byte boundaries", i, ch);
+      if (sr.token_stride < (int64_t)model->n_kv_heads * model->head_dim)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                    "chunk %d channel %d: token stride shorter than a row", i, ch);
+      if (pr.m > 0 && (!pr.U || !pr.V))
+        return fail(KAMERA_ERR_INVALID_ARGUMENT, "chunk %d channel %d: m > 0 needs U and V", i, ch);
+    }
+  }
+  plan->queries.resize(n_queries);
+  for (int32_t i = 0; i < n_queries; ++i) {
+    const kamera_chunk_query& a = queries[i];
+    if (a.first_chunk < 0 || a.n_chunks < 0 || (int64_t)a.first_chunk + a.n_chunks > n_chunks)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT, "query %d: chunks [%d, %lld) outside [0, %d)", i,
+                  a.first_chunk, (long long)a.first_chunk + a.n_chunks, n_chunks);
+  }
+  // segment length: as kamera_decode_attention, segments never cross a chunk
+  auto blocks_at = [&](int seg) {
+    int64_t b = 0;
+    for (int32_t i = 0; i < n_queries; ++i)
+      for (int32_t c = 0; c < queries[i].n_chunks; ++c)
+        b += (chunks[queries[i].first_chunk + c].n_tokens + seg - 1) / seg;
+    return b * model->n_kv_heads;
+  };
+  plan->seg = kSegChoices[2];
+  for (int c = 0; c < 3; ++c)
+    if (blocks_at(kSegChoices[c]) >= kTargetSegBlocks) {
+      plan->seg = kSegChoices[c];
+      break;
+    }
+  const int seg = plan->seg;
+  for (int32_t i = 0; i < n_queries; ++i) {
+    const int32_t first = (int32_t)plan->segs.size();
+    int64_t tokens = 0;
+    for (int32_t c = 0; c < queries[i].n_chunks; ++c) {
+      const int32_t ci = queries[i].first_chunk + c;
+      const int32_t n = chunks[ci].n_tokens;
+      tokens += n;
+      for (int32_t t = 0; t < n; t += seg)
+        plan->segs.push_back(VSeg{ci, t, std::min(n, t + seg), i});
+    }
+    plan->queries[i] = AQuery{0, (int32_t)std::min<int64_t>(tokens, INT32_MAX), first,
+                              (int32_t)plan->segs.size() - first};
+  }
+  if ((int64_t)plan->segs.size() * model->n_kv_heads > INT32_MAX)
+    return fail(KAMERA_ERR_UNSUPPORTED, "too many attention segments");
+  const size_t D = model->head_dim;
+  plan->freq_off = 0;
+  plan->sec_off = plan->freq_off + 64 * sizeof(double);
+  plan->chunk_off = round_up(plan->sec_off + 64, 16);
+  plan->seg_off = round_up(plan->chunk_off + (size_t)n_chunks * sizeof(VChunk), 16);
+  plan->query_off = round_up(plan->seg_off + plan->segs.size() * sizeof(VSeg), 16);
+  plan->part_o_off = round_up(plan->query_off + plan->queries.size() * sizeof(AQuery), 256);
+  const size_t segs = plan->segs.size();
+  plan->part_lse_off = round_up(plan->part_o_off + segs * n_q_heads * D * sizeof(float), 256);
+  plan->total = round_up(plan->part_lse_off + segs * n_q_heads * sizeof(float), 256);
   return KAMERA_OK;
 }
 
@@ -517,6 +973,136 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
       return fail(KAMERA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
   }
   attn_merge_kernel<<<dim3((unsigned)rows), dim3(64), 0, stream>>>(P, (int)D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+size_t kamera_chunk_attention_workspace_bytes(const kamera_model* model, int32_t n_q_heads,
+                                              const kamera_attn_chunk* chunks, int32_t n_chunks,
+                                              const kamera_chunk_query* queries,
+                                              int32_t n_queries) {
+  VPlan plan;
+  if (chunk_attention_geometry(model, n_q_heads, chunks, n_chunks, queries, n_queries, &plan) !=
+      KAMERA_OK)
+    return 0;
+  return plan.total;
+}
+
+kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
+                                     const kamera_attn_chunk* chunks, int32_t n_chunks,
+                                     const kamera_chunk_query* queries, int32_t n_queries,
+                                     const void* q, int32_t n_q_heads, float scale, float* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream_ptr) {
+  clear_error();
+  VPlan plan;
+  kamera_status st =
+      chunk_attention_geometry(model, n_q_heads, chunks, n_chunks, queries, n_queries, &plan);
+  if (st != KAMERA_OK) return st;
+  if (layer < 0 || layer >= model->n_layers)
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, model->n_layers);
+  if (!std::isfinite(scale)) return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (n_queries > 0 && (!q || !out || !lse))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "q, out and lse must not be NULL");
+  if (q && !aligned16(q)) return fail(KAMERA_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+  const size_t D = model->head_dim;
+  const size_t rows = (size_t)n_queries * n_q_heads;
+  if (n_queries > 0 && (ranges_overlap(out, rows * D * 4, lse, rows * 4) ||
+                        ranges_overlap(out, rows * D * 4, q, rows * D * 2) ||
+                        ranges_overlap(lse, rows * 4, q, rows * D * 2)))
+    return fail(KAMERA_ERR_OVERLAP, "q, out and lse must not overlap");
+  if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(KAMERA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                plan.total);
+  if (n_queries == 0) return KAMERA_OK;
+
+  std::vector<uint8_t> table(plan.part_o_off, 0);
+  const int pairs = model->rope_dim / 2;
+  if (model->inv_freq) std::memcpy(table.data() + plan.freq_off, model->inv_freq, pairs * sizeof(double));
+  if (model->pair_section) std::memcpy(table.data() + plan.sec_off, model->pair_section, pairs);
+  const int64_t es = 2;
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_attn_chunk& c = chunks[i];
+    VChunk v{};
+    v.n_tokens = c.n_tokens;
+    v.delta = c.delta;
+    v.delta_s1 = model->n_sections > 1 ? c.delta_sections[0] : c.delta;
+    v.delta_s2 = model->n_sections > 2 ? c.delta_sections[1] : c.delta;
+    if (c.n_tokens > 0) {
+      v.k = static_cast<const uint16_t*>(c.src[0].ptr) + (int64_t)layer * c.src[0].layer_stride;
+      v.v = static_cast<const uint16_t*>(c.src[1].ptr) + (int64_t)layer * c.src[1].layer_stride;
+      v.k_ts = c.src[0].token_stride;
+      v.v_ts = c.src[1].token_stride;
+    }
+    bool vec = true;
+    for (int ch = 0; ch < 2; ++ch) {
+      const kamera_patch_ref& pr = c.patch[ch];
+      const int m = c.n_tokens > 0 ? pr.m : 0;
+      const uint16_t* U = m ? static_cast<const uint16_t*>(pr.U) + (int64_t)layer * pr.u_layer_stride : nullptr;
+      const uint16_t* V = m ? static_cast<const uint16_t*>(pr.V) + (int64_t)layer * pr.v_layer_stride : nullptr;
+      if (m && (!aligned16(U) || (pr.u_head_stride * es) % 16 || (m * es) % 16)) vec = false;
+      if (ch == 0) {
+        v.mk = m;
+        v.uk = U;
+        v.vk = V;
+        v.uk_hs = pr.u_head_stride;
+        v.vk_hs = pr.v_head_stride;
+      } else {
+        v.mv = m;
+        v.uv = U;
+        v.vv = V;
+        v.uv_hs = pr.u_head_stride;
+        v.vv_hs = pr.v_head_stride;
+      }
+    }
+    v.vec_u = vec ? 1 : 0;
+    std::memcpy(table.data() + plan.chunk_off + i * sizeof(VChunk), &v, sizeof v);
+  }
+  if (!plan.segs.empty())
+    std::memcpy(table.data() + plan.seg_off, plan.segs.data(), plan.segs.size() * sizeof(VSeg));
+  std::memcpy(table.data() + plan.query_off, plan.queries.data(),
+              plan.queries.size() * sizeof(AQuery));
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  st = upload(table, workspace, stream);
+  if (st != KAMERA_OK) return st;
+
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  VParams P{};
+  P.chunks = reinterpret_cast<const VChunk*>(base + plan.chunk_off);
+  P.segs = reinterpret_cast<const VSeg*>(base + plan.seg_off);
+  P.q = static_cast<const uint16_t*>(q);
+  P.part_o = reinterpret_cast<float*>(base + plan.part_o_off);
+  P.part_lse = reinterpret_cast<float*>(base + plan.part_lse_off);
+  P.inv_freq = model->inv_freq ? reinterpret_cast<const double*>(base + plan.freq_off) : nullptr;
+  P.pair_section = model->pair_section ? base + plan.sec_off : nullptr;
+  P.theta = model->rope_theta;
+  P.scale = scale;
+  P.n_q = n_q_heads;
+  P.n_kv = model->n_kv_heads;
+  P.group = n_q_heads / model->n_kv_heads;
+  P.rot_dim = model->rope_dim;
+  P.layout = model->rope_layout;
+  const int64_t seg_blocks = (int64_t)plan.segs.size() * model->n_kv_heads;
+  if (seg_blocks > 0) {
+    const dim3 grid((unsigned)seg_blocks), block(kThreads);
+    if (D == 128) chunk_attn_kernel<128><<<grid, block, 0, stream>>>(P);
+    else chunk_attn_kernel<64><<<grid, block, 0, stream>>>(P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(KAMERA_ERR_HIP, "chunk attention kernel launch: %s", hipGetErrorString(e));
+  }
+  AParams M{};
+  M.queries = reinterpret_cast<const AQuery*>(base + plan.query_off);
+  M.part_o = P.part_o;
+  M.part_lse = P.part_lse;
+  M.out = out;
+  M.lse = lse;
+  M.n_q = n_q_heads;
+  attn_merge_kernel<<<dim3((unsigned)rows), dim3(64), 0, stream>>>(M, (int)D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return KAMERA_OK;

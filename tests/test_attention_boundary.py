@@ -98,3 +98,80 @@ def test_state_merge_validation():
     assert kb.kamera_state_merge(2, 4, 128, None, L, O, R, None) == kb.KAMERA_ERR_INVALID_ARGUMENT
     assert kb.kamera_state_merge(2, 4, 128, P, L, P + 64, R, None) == kb.KAMERA_ERR_OVERLAP
     assert kb.kamera_state_merge(2, 0, 128, None, None, None, None, None) == kb.KAMERA_OK
+
+
+# ---- attention over chunks read in place --------------------------------------------------
+
+def _view(n_tokens=300, m=(16, 16), delta=500, row=512, aligned=True):
+    base = FAKE + (0 if aligned else 2)
+    patch = [None, None]
+    for ch in range(2):
+        if m[ch]:
+            patch[ch] = (m[ch], FAKE + (30 + ch) * GiB, 4 * 2000 * m[ch], 2000 * m[ch],
+                         FAKE + (32 + ch) * GiB, 4 * 128 * m[ch], 128 * m[ch])
+    return {"n_tokens": n_tokens, "delta": delta,
+            "src": [(base, 2000 * row, row), (base + 4 * GiB, 2000 * row, row)],
+            "patch": patch}
+
+
+def _chunk_call(model=None, views=None, spans=((0, 2),), n_q_heads=28, layer=0, scale=0.088,
+                q=FAKE + 20 * GiB, out=FAKE + 21 * GiB, lse=FAKE + 22 * GiB):
+    model = model or _model()
+    views = views if views is not None else [_view(), _view(40, (0, 8), -7)]
+    ch = kb.attn_chunks_of(views)
+    qs = kb.chunk_queries_of(spans)
+    return kb.kamera_chunk_attention(model, layer, ch, len(views), qs, len(spans), q, n_q_heads,
+                                     scale, out, lse, None, 0, None)
+
+
+def test_chunk_attention_exports_and_layout():
+    names = set(kb.header_functions())
+    assert {"kamera_chunk_attention", "kamera_chunk_attention_workspace_bytes"} <= names
+    assert ctypes.sizeof(kb.KameraAttnChunk) == ctypes.sizeof(kb.KameraChunk) == 192
+    assert ctypes.sizeof(kb.KameraChunkQuery) == 8
+
+
+def test_chunk_attention_well_formed_call_reaches_the_workspace_check():
+    assert _chunk_call() == kb.KAMERA_ERR_WORKSPACE
+    m64 = _model(head_dim=64, rope_dim=32, rope_layout="interleaved")
+    views = [_view(row=256), _view(5, (64, 0), 3, row=256)]
+    assert _chunk_call(m64, views, n_q_heads=16) == kb.KAMERA_ERR_WORKSPACE
+
+
+def test_chunk_attention_workspace_bytes_grow_with_segments():
+    m = _model()
+    views = [_view(3000), _view(0), _view(700)]
+    small = kb.kamera_chunk_attention_workspace_bytes(m, 28, kb.attn_chunks_of(views[:1]), 1,
+                                                      kb.chunk_queries_of([(0, 1)]), 1)
+    big = kb.kamera_chunk_attention_workspace_bytes(m, 28, kb.attn_chunks_of(views), 3,
+                                                    kb.chunk_queries_of([(0, 3), (1, 2)]), 2)
+    assert 0 < small < big and small % 256 == 0 and big % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(model=_model(family="mla", head_dim=512, rope_dim=64, n_kv_heads=1)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(dtype="f32")), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(head_dim=96, rope_dim=96)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=30), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(n_q_heads=4 * 17), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(views=[_view(m=(65, 0))], spans=((0, 1),)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(views=[_view(m=(-1, 0))], spans=((0, 1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(views=[_view(n_tokens=-1)], spans=((0, 1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(views=[_view(aligned=False)], spans=((0, 1),)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(spans=((1, 2),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(spans=((-1, 1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(layer=4), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.inf), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 20 * GiB + 2), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 20 * GiB), kb.KAMERA_ERR_OVERLAP),
+])
+def test_chunk_attention_rejects(kw, status):
+    assert _chunk_call(**kw) == status
+    assert kb.kamera_last_error()
+
+
+def test_chunk_attention_rejects_a_patch_without_factors():
+    v = _view(m=(0, 0))
+    v["patch"] = [(8, None, 0, 0, None, 0, 0), None]
+    assert _chunk_call(views=[v], spans=((0, 1),)) == kb.KAMERA_ERR_INVALID_ARGUMENT
