@@ -8,9 +8,10 @@ Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM G
 line also carries "patch_compile": the time kamera_patch_compile takes to form the same
 batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass, and
 "decode_attention": the consumer-side decode attention (with its state merge) on a
-64-sequence x 16K-token paged cache.
+64-sequence x 16K-token paged cache, and "chunk_attention": the same decode read from 16
+canonical chunks per sequence in place (query turned per chunk, rank-16 patches on K and V).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--compile-steps N]
+                    [--compile-steps N] [--attention-steps N] [--chunk-attention-steps N]
 """
 from __future__ import annotations
 
@@ -266,6 +267,74 @@ def attention_leg(steps: int, stream) -> dict:
             "timed_with": "hip events on the launch stream (segment + merge kernels)"}
 
 
+def chunk_attention_leg(steps: int, stream) -> dict:
+    """Attention over chunks read in place, shaped like the decode leg: 64 sequences x 16
+    canonical chunks of 1024 tokens, 4 KV heads x 128, 28 query heads, one layer, each chunk
+    with its own shift (uniform in [0, 65536)) and rank-16 patches on K and V. Bytes = every
+    canonical K and V row, every U_K and U_V row, and each chunk's V_K and V_V once."""
+    import numpy as np
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+
+    n_seq, n_ck, T, n_kv, D, n_q, m = 64, 16, 1024, 4, 128, 28, 16
+    n_chunks = n_seq * n_ck
+    row = n_kv * D
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78)
+    K = torch.randn((n_chunks, T, row), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((n_chunks, T, row), generator=g, device="cuda").to(torch.bfloat16)
+    UK, UV = [(0.05 * torch.randn((n_chunks, n_kv, T, m), generator=g, device="cuda")).to(torch.bfloat16)
+              for _ in range(2)]
+    VK, VV = [(0.05 * torch.randn((n_chunks, n_kv, D, m), generator=g, device="cuda")).to(torch.bfloat16)
+              for _ in range(2)]
+    deltas = np.random.default_rng(78).integers(0, 65536, n_chunks)
+    es = 2
+    items = []
+    for c in range(n_chunks):
+        items.append({"n_tokens": T, "delta": int(deltas[c]),
+                      "src": [(K.data_ptr() + c * K.stride(0) * es, K.stride(0), row),
+                              (V.data_ptr() + c * V.stride(0) * es, V.stride(0), row)],
+                      "patch": [(m, UK.data_ptr() + c * UK.stride(0) * es, UK.stride(0), UK.stride(1),
+                                 VK.data_ptr() + c * VK.stride(0) * es, VK.stride(0), VK.stride(1)),
+                                (m, UV.data_ptr() + c * UV.stride(0) * es, UV.stride(0), UV.stride(1),
+                                 VV.data_ptr() + c * VV.stride(0) * es, VV.stride(0), VV.stride(1))]})
+    chunks = kb.attn_chunks_of(items)
+    queries = kb.chunk_queries_of([(s * n_ck, n_ck) for s in range(n_seq)])
+    model = kb.make_model("gqa", "bf16", 1, n_kv, D, D, "half_split", 1e6)
+    q = torch.randn((n_seq, n_q, D), generator=g, device="cuda").to(torch.bfloat16)
+    need = kb.kamera_chunk_attention_workspace_bytes(model, n_q, chunks, n_chunks, queries, n_seq)
+    ws = kb.Workspace(nbytes=need)
+    out = torch.empty((n_seq, n_q, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_seq, n_q), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        kb.check(kb.kamera_chunk_attention(model, 0, chunks, n_chunks, queries, n_seq,
+                                           q.data_ptr(), n_q, 1.0 / D ** 0.5, out.data_ptr(),
+                                           lse.data_ptr(), ws.ptr, ws.nbytes, sp))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kv_bytes = 2 * n_chunks * T * row * es
+    patch_bytes = 2 * n_chunks * n_kv * (T + D) * m * es
+    gbps = (kv_bytes + patch_bytes) / (ms * 1e-3) / 1e9
+    del K, V, UK, UV, VK, VV, q, out, lse, ws
+    return {"shape": f"{n_seq} sequences x {n_ck} chunks x {T} tokens, {n_kv} KV heads x {D}, "
+                     f"{n_q} query heads, rank {m} patches on K and V, one layer",
+            "ms_per_call": round(ms, 4), "bytes": kv_bytes + patch_bytes,
+            "achieved_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "steps": steps,
+            "timed_with": "hip events on the launch stream (chunk + merge kernels)"}
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -425,6 +494,8 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
     rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
     seg = [r for r in rows if "attn_segment_kernel" in r["Name"]]
     mrg = [r for r in rows if "attn_merge_kernel" in r["Name"]]
+    chk = [r for r in rows if "chunk_attn_kernel" in r["Name"]]
+    ca = rec.get("chunk_attention")
     lines = ["# decode attention (consumer side)", "", "Commands (R = repository root on the GPU box):", ""]
     lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
     lines += [f"Shape: {da['shape']}. Bytes per call: K and V once = {da['kv_bytes'] / 1e9:.3f} GB.",
@@ -436,6 +507,19 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
         gb = da["kv_bytes"] / avg if "segment" in r["Name"] else float("nan")
         lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
                      f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
+    if ca and chk:
+        lines += ["", f"Attention over chunks read in place: {ca['shape']}. Bytes per call: "
+                  f"canonical K and V, U_K and U_V rows and each chunk's V_K, V_V once = "
+                  f"{ca['bytes'] / 1e9:.3f} GB. HIP events: {ca['ms_per_call']} ms per call "
+                  f"(chunk + merge kernels) = {ca['achieved_gbps']} GB/s ({ca['hbm_frac']} of "
+                  f"8 TB/s). The merge kernel's launches are counted with the decode ones above.",
+                  "", "| kernel | calls | avg us | GB/s (bytes / avg) | of 8 TB/s |",
+                  "|---|---|---|---|---|"]
+        for r in chk:
+            avg = float(r["AverageNs"])
+            gb = ca["bytes"] / avg
+            lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
+                         f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
     out_md = ROOT / "profiles" / "decode_attention.md"
     out_md.write_text("\n".join(lines) + "\n")
     print(out_md.read_text())
@@ -463,6 +547,8 @@ def main():
                     help="timed orbit compiles (3 orderings) in the compile leg (0: skip)")
     ap.add_argument("--attention-steps", type=int, default=20,
                     help="timed kamera_decode_attention calls on a 64 x 16K decode (0: skip)")
+    ap.add_argument("--chunk-attention-steps", type=int, default=20,
+                    help="timed kamera_chunk_attention calls on 64 x 16 chunks of 1024 (0: skip)")
     args = ap.parse_args()
     if args.summarize_attention_profile:
         summarize_attention_profile(args.summarize_attention_profile, args.profile_command,
@@ -591,6 +677,9 @@ def main():
     if args.attention_steps > 0:
         print("[bench] timing decode attention", file=sys.stderr, flush=True)
         out["decode_attention"] = attention_leg(args.attention_steps, stream)
+    if args.chunk_attention_steps > 0:
+        print("[bench] timing attention over chunks read in place", file=sys.stderr, flush=True)
+        out["chunk_attention"] = chunk_attention_leg(args.chunk_attention_steps, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)

@@ -425,13 +425,14 @@ __device__ __forceinline__ void split8(const float* x, bf16x8* hi, bf16x8* lo) {
   *lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// KMAX: the largest patch rank in the launch, rounded up to 16, 32 or 64 (register budget).
+template <int D, int KMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 && KMAX <= 32 ? 3 : 2, 8)))
 void chunk_attn_kernel(VParams P) {
   constexpr int KS = D / 32;                 // bf16 k-steps over the features
-  constexpr int PK = kMaxViewRank / 32;      // bf16 k-steps over the key patch rank
+  constexpr int PK = (KMAX + 31) / 32;       // bf16 k-steps over the key patch rank
   constexpr int NC = D / 16;                 // column blocks of o
-  constexpr int NZ = kMaxViewRank / 16;      // column blocks of z
+  constexpr int NZ = KMAX / 16;              // column blocks of z
   constexpr int VS = D + kMaxViewRank + 8;   // LDS row: V row, then the token's U_V row
   constexpr int PSTR = 17;
   constexpr int MW = D + kMaxViewRank;       // merged row: o, then z
@@ -476,9 +477,11 @@ void chunk_attn_kernel(VParams P) {
   __syncthreads();
   for (int idx = tid; idx < P.group * mk; idx += kThreads) {
     const int row = idx / mk, r = idx - row * mk;
-    float acc = 0.f;
-    for (int f = 0; f < D; ++f) acc += qs[row * D + f] * bf16_lo(stage[f * mk + r]);
-    wsh[row][r] = acc;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: D is a multiple of 4
+    for (int f = 0; f < D; f += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += qs[row * D + f + u] * bf16_lo(stage[(f + u) * mk + r]);
+    wsh[row][r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   __syncthreads();
 
@@ -547,35 +550,47 @@ void chunk_attn_kernel(VParams P) {
   const uint16_t* vh = C.v + h * D;
   const uint16_t* ukh = mk > 0 ? C.uk + h * C.uk_hs : nullptr;
   const uint16_t* uvh = mv > 0 ? C.uv + h * C.uv_hs : nullptr;
+  // software pipeline: the next tile's K, V, U_K and U_V rows are in flight while this one
+  // is computed
+  struct Tile {
+    u32x4 k[KS], v[KS], uk[PK], uv[PK];
+  };
+  auto load_tile = [&](int t, Tile& x) {
+    const bool ok = t < S.t_hi;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      x.k[k] = ok ? *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+      x.v[k] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uk[s2] = ok && 32 * s2 < mk ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uv[s2] = ok && 32 * s2 < mv ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  };
+  Tile cur, nxt;
+  load_tile(S.t_lo + kTile * wave + col, cur);
   for (int t0 = S.t_lo + kTile * wave; t0 < S.t_hi; t0 += 4 * kTile) {
     const int t = t0 + col;
     const bool valid = t < S.t_hi;
-    bf16x8 kb[KS];
-    u32x4 vraw[KS];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      if (valid) {
-        kb[k] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp));
-        vraw[k] = *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp);
-      } else {
-        kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vraw[k] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    load_tile(t + 4 * kTile, nxt);
     // S = Q' K^T + W U_K^T: lane holds query rows 4 grp + r of token col
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[k], kb[k], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[k], kb[k], sacc, 0, 0, 0);
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, cur.k[k]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[k], kb, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[k], kb, sacc, 0, 0, 0);
     }
 #pragma unroll
     for (int s2 = 0; s2 < PK; ++s2) {
       if (32 * s2 < mk) {
-        const u32x4 u = valid ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
-                              : u32x4{0u, 0u, 0u, 0u};
-        const bf16x8 ub = __builtin_bit_cast(bf16x8, u);
+        const bf16x8 ub = __builtin_bit_cast(bf16x8, cur.uk[s2]);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh[s2], ub, sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl[s2], ub, sacc, 0, 0, 0);
       }
@@ -583,14 +598,10 @@ void chunk_attn_kernel(VParams P) {
     // V rows and U_V rows of the tile to LDS (token col)
 #pragma unroll
     for (int k = 0; k < KS; ++k)
-      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = vraw[k];
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = cur.v[k];
 #pragma unroll
-    for (int s2 = 0; s2 < kMaxViewRank / 32; ++s2) {
-      const u32x4 u = valid && 32 * s2 < mv
-                          ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
-                          : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + D + 32 * s2 + 8 * grp]) = u;
-    }
+    for (int s2 = 0; s2 < PK; ++s2)
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + D + 32 * s2 + 8 * grp]) = cur.uv[s2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float sc = valid ? sacc[r] * P.scale : -INFINITY;
@@ -634,6 +645,7 @@ void chunk_attn_kernel(VParams P) {
                                                       0, 0, 0);
     }
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+    cur = nxt;
   }
 
   // merge the four waves' states (as attn_segment_kernel), o and z together
@@ -1089,8 +1101,19 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
   const int64_t seg_blocks = (int64_t)plan.segs.size() * model->n_kv_heads;
   if (seg_blocks > 0) {
     const dim3 grid((unsigned)seg_blocks), block(kThreads);
-    if (D == 128) chunk_attn_kernel<128><<<grid, block, 0, stream>>>(P);
-    else chunk_attn_kernel<64><<<grid, block, 0, stream>>>(P);
+    int mmax = 0;
+    for (int32_t i = 0; i < n_chunks; ++i)
+      if (chunks[i].n_tokens > 0)
+        mmax = std::max(mmax, std::max(chunks[i].patch[0].m, chunks[i].patch[1].m));
+    if (D == 128) {
+      if (mmax <= 16) chunk_attn_kernel<128, 16><<<grid, block, 0, stream>>>(P);
+      else if (mmax <= 32) chunk_attn_kernel<128, 32><<<grid, block, 0, stream>>>(P);
+      else chunk_attn_kernel<128, 64><<<grid, block, 0, stream>>>(P);
+    } else {
+      if (mmax <= 16) chunk_attn_kernel<64, 16><<<grid, block, 0, stream>>>(P);
+      else if (mmax <= 32) chunk_attn_kernel<64, 32><<<grid, block, 0, stream>>>(P);
+      else chunk_attn_kernel<64, 64><<<grid, block, 0, stream>>>(P);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
       return fail(KAMERA_ERR_HIP, "chunk attention kernel launch: %s", hipGetErrorString(e));
