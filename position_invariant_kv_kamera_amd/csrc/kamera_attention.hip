@@ -373,6 +373,8 @@ struct alignas(16) VChunk {
   int64_t delta, delta_s1, delta_s2;
   int32_t n_tokens, mk, mv;
   int32_t vec_u;        // U rows may be read 16 bytes at a time (both channels)
+  int32_t vec_v;        // V factors of a head may be copied 16 bytes at a time (both channels)
+  int32_t pad0[3];
 };
 
 struct alignas(16) VSeg {
@@ -404,6 +406,16 @@ __device__ __forceinline__ u32x4 load_u8(const uint16_t* row, int r0, int m, boo
     w[e] = lo | (hi << 16);
   }
   return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// n bf16 from src to LDS dst (n a multiple of 8 when vec), 16 bytes per thread when vec.
+__device__ __forceinline__ void stage_rows(const uint16_t* src, int n, bool vec, uint16_t* dst) {
+  if (vec) {
+    for (int i = threadIdx.x; i < n / 8; i += kThreads)
+      reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+  } else {
+    for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
+  }
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
@@ -453,6 +465,37 @@ void chunk_attn_kernel(VParams P) {
   const int mk = C.mk, mv = C.mv;
   const bool vec = C.vec_u != 0;
 
+  const uint16_t* kh = C.k + h * D;
+  const uint16_t* vh = C.v + h * D;
+  const uint16_t* ukh = mk > 0 ? C.uk + h * C.uk_hs : nullptr;
+  const uint16_t* uvh = mv > 0 ? C.uv + h * C.uv_hs : nullptr;
+  // software pipeline: the next tile's K, V, U_K and U_V rows are in flight while this one
+  // is computed
+  struct Tile {
+    u32x4 k[KS], v[KS], uk[PK], uv[PK];
+  };
+  auto load_tile = [&](int t, Tile& x) {
+    const bool ok = t < S.t_hi;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      x.k[k] = ok ? *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+      x.v[k] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uk[s2] = ok && 32 * s2 < mk ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uv[s2] = ok && 32 * s2 < mv ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  };
+  // the first tile's loads go out before the set-up, so their latency overlaps it
+  Tile cur;
+  load_tile(S.t_lo + kTile * wave + col, cur);
+
   // set-up: the chunk's phases, the query rows (fp32, in mrg_o) and w = V_K^T q
   const int R = P.rot_dim;
   for (int i = tid; i < R / 2; i += kThreads) {
@@ -470,10 +513,7 @@ void chunk_attn_kernel(VParams P) {
   __syncthreads();
   // V_K of head h staged in LDS (the V tiles are not in use yet)
   uint16_t* stage = &vt[0][0];
-  if (mk > 0) {
-    const uint16_t* vkh = C.vk + h * C.vk_hs;
-    for (int idx = tid; idx < D * mk; idx += kThreads) stage[idx] = vkh[idx];
-  }
+  if (mk > 0) stage_rows(C.vk + h * C.vk_hs, D * mk, C.vec_v != 0, stage);
   __syncthreads();
   for (int idx = tid; idx < P.group * mk; idx += kThreads) {
     const int row = idx / mk, r = idx - row * mk;
@@ -546,35 +586,7 @@ void chunk_attn_kernel(VParams P) {
 #pragma unroll
   for (int c = 0; c < NZ; ++c) z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kh = C.k + h * D;
-  const uint16_t* vh = C.v + h * D;
-  const uint16_t* ukh = mk > 0 ? C.uk + h * C.uk_hs : nullptr;
-  const uint16_t* uvh = mv > 0 ? C.uv + h * C.uv_hs : nullptr;
-  // software pipeline: the next tile's K, V, U_K and U_V rows are in flight while this one
-  // is computed
-  struct Tile {
-    u32x4 k[KS], v[KS], uk[PK], uv[PK];
-  };
-  auto load_tile = [&](int t, Tile& x) {
-    const bool ok = t < S.t_hi;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      x.k[k] = ok ? *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp)
-                  : u32x4{0u, 0u, 0u, 0u};
-      x.v[k] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < PK; ++s2)
-      x.uk[s2] = ok && 32 * s2 < mk ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
-                                    : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int s2 = 0; s2 < PK; ++s2)
-      x.uv[s2] = ok && 32 * s2 < mv ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
-                                    : u32x4{0u, 0u, 0u, 0u};
-  };
-  Tile cur, nxt;
-  load_tile(S.t_lo + kTile * wave + col, cur);
+  Tile nxt;
   for (int t0 = S.t_lo + kTile * wave; t0 < S.t_hi; t0 += 4 * kTile) {
     const int t = t0 + col;
     const bool valid = t < S.t_hi;
@@ -686,10 +698,7 @@ void chunk_attn_kernel(VParams P) {
     __syncthreads();
   }
   // V_V of head h staged in LDS (every wave is past its last tile)
-  if (mv > 0) {
-    const uint16_t* vvh = C.vv + h * C.vv_hs;
-    for (int idx = tid; idx < D * mv; idx += kThreads) stage[idx] = vvh[idx];
-  }
+  if (mv > 0) stage_rows(C.vv + h * C.vv_hs, D * mv, C.vec_v != 0, stage);
   __syncthreads();
   for (int idx = tid; idx < P.group * D; idx += kThreads) {
     const int rw = idx / D, f = idx - rw * D;
@@ -1050,13 +1059,15 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
       v.k_ts = c.src[0].token_stride;
       v.v_ts = c.src[1].token_stride;
     }
-    bool vec = true;
+    bool vec = true, vecv = true;
     for (int ch = 0; ch < 2; ++ch) {
       const kamera_patch_ref& pr = c.patch[ch];
       const int m = c.n_tokens > 0 ? pr.m : 0;
       const uint16_t* U = m ? static_cast<const uint16_t*>(pr.U) + (int64_t)layer * pr.u_layer_stride : nullptr;
       const uint16_t* V = m ? static_cast<const uint16_t*>(pr.V) + (int64_t)layer * pr.v_layer_stride : nullptr;
       if (m && (!aligned16(U) || (pr.u_head_stride * es) % 16 || (m * es) % 16)) vec = false;
+      if (m && (!aligned16(V) || (pr.v_head_stride * es) % 16 || (model->head_dim * m) % 8))
+        vecv = false;
       if (ch == 0) {
         v.mk = m;
         v.uk = U;
@@ -1072,6 +1083,7 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
       }
     }
     v.vec_u = vec ? 1 : 0;
+    v.vec_v = vecv ? 1 : 0;
     std::memcpy(table.data() + plan.chunk_off + i * sizeof(VChunk), &v, sizeof v);
   }
   if (!plan.segs.empty())
