@@ -829,30 +829,94 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
     lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   wave_lds_sync();
-  // Cholesky, right-looking: lane i owns row i of S, which becomes row i of L. Step j: the
-  // owner of row j takes the pivot (collapsed when what is left of s_jj is at most kDeadTol
-  // times its starting value), the rows below scale column j, then each updates its own part
-  // of the trailing matrix (its next diagonal included, so the next pivot needs no wait).
-  const int i = lane;
-  const double sii0 = i < m ? lm[i * SS + i] : 0.0;
-  for (int j = 0; j < m; ++j) {
-    if (i == j) {
-      const double d = lm[j * SS + j];
-      const bool dk = d <= kDeadTol * sii0;
+  if constexpr (MP <= 32) {
+    // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
+    // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
+    // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
+    // the lanes holding column j scale it and publish it in LDS, then each lane updates its
+    // own part of the trailing matrix. The same operations in the same order as the LDS
+    // version below, with one LDS round trip per step instead of a chain of them.
+    constexpr int LPR = 64 / MP, CPL = MP / LPR;
+    const int ri = lane % MP, cb = lane / MP, c0 = cb * CPL;
+    double sv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int col = c0 + c;
+      sv[c] = (ri < m && col < m) ? (ri >= col ? lm[ri * SS + col] : lm[col * SS + ri]) : 0.0;
+    }
+    double* colj = lm + 1;   // the strict upper part of row 0 is free until the end
+    wave_lds_sync();
+    for (int j = 0; j < m; ++j) {
+      const int jc = j % CPL, jb = j / CPL;
+      double pv = 0.0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (c == jc) pv = sv[c];
+      const uint64_t pb = __builtin_bit_cast(uint64_t, pv);
+      const int src = j + MP * jb;
+      const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, src);
+      const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), src);
+      const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
+      const double s0 = lm[j * SS + j];   // s_jj before elimination (lm still holds S)
+      const bool dk = d <= kDeadTol * s0;
       const double ljj = dk ? 0.0 : sqrt(d);
-      lm[j * SS + j] = ljj;
-      inv[j] = dk ? 0.0 : 1.0 / ljj;
-      dead[j] = dk ? 1 : 0;
+      const double iv = dk ? 0.0 : 1.0 / ljj;
+      if (lane == 0) {
+        inv[j] = iv;
+        dead[j] = dk ? 1 : 0;
+      }
+      if (cb == jb) {
+        double v = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (c == jc) v = sv[c];
+        v = ri == j ? ljj : (ri > j ? v * iv : v);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (c == jc) sv[c] = v;
+        colj[ri] = ri > j && ri < m ? v : 0.0;
+      }
+      wave_lds_sync();
+      const double lij = colj[ri];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int col = c0 + c;
+        if (col > j && col <= ri && ri < m) sv[c] -= lij * colj[col];
+      }
+      wave_lds_sync();   // colj is rewritten by the next step
     }
-    wave_lds_sync();
-    double lij = 0.0;
-    if (i > j && i < m) {
-      lij = lm[i * SS + j] * inv[j];
-      lm[i * SS + j] = lij;
+    // L (lower triangle) back to LDS for the forward substitution
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int col = c0 + c;
+      if (ri < m && col <= ri) lm[ri * SS + col] = sv[c];
     }
-    wave_lds_sync();
-    if (i > j && i < m)
-      for (int k = j + 1; k <= i; ++k) lm[i * SS + k] -= lij * lm[k * SS + j];
+  } else {
+    // Cholesky, right-looking: lane i owns row i of S, which becomes row i of L. Step j: the
+    // owner of row j takes the pivot (collapsed when what is left of s_jj is at most kDeadTol
+    // times its starting value), the rows below scale column j, then each updates its own part
+    // of the trailing matrix (its next diagonal included, so the next pivot needs no wait).
+    const int i = lane;
+    const double sii0 = i < m ? lm[i * SS + i] : 0.0;
+    for (int j = 0; j < m; ++j) {
+      if (i == j) {
+        const double d = lm[j * SS + j];
+        const bool dk = d <= kDeadTol * sii0;
+        const double ljj = dk ? 0.0 : sqrt(d);
+        lm[j * SS + j] = ljj;
+        inv[j] = dk ? 0.0 : 1.0 / ljj;
+        dead[j] = dk ? 1 : 0;
+      }
+      wave_lds_sync();
+      double lij = 0.0;
+      if (i > j && i < m) {
+        lij = lm[i * SS + j] * inv[j];
+        lm[i * SS + j] = lij;
+      }
+      wave_lds_sync();
+      if (i > j && i < m)
+        for (int k = j + 1; k <= i; ++k) lm[i * SS + k] -= lij * lm[k * SS + j];
+    }
   }
   wave_lds_sync();
   // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
