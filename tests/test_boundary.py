@@ -293,3 +293,20 @@ def test_workloads_plans_are_consistent():
     q = wl.plan("qwen25vl_gqa_bf16")
     assert all(-32768 <= d <= 32768 for d in q.deltas)
     assert wl.plan("qwen25vl_gqa_bf16").deltas == q.deltas          # seeded
+
+
+def test_a_batch_past_the_grid_limit_is_rejected_before_any_device_call():
+    """One fp32 chunk of 2^30 tokens would need more than 2^23 blocks of the VALU kernel (64
+    tokens each): the plan refuses it (UNSUPPORTED) instead of launching an oversized grid."""
+    model = _model(dtype=0, n_layers=1, n_kv_heads=1, head_dim=128, rope_dim=128)
+    n = 1 << 30
+    cache = _cache(layer_stride=n * 128, token_stride=128, n_logical_pages=n // 16,
+                   n_pages=n // 16, pool=(ctypes.c_void_p * 2)(FAKE, FAKE + (1 << 42)))
+    ch = (kb.KameraChunk * 1)()
+    ch[0].n_tokens = n
+    ch[0].delta = 3
+    for c in range(2):
+        ch[0].src[c] = kb.KameraSrc(FAKE + (1 << 43) + (c << 41), n * 128, 128)
+    need = kb.kamera_workspace_bytes(1)
+    st, msg = call(model, cache, ch, 1, ws=FAKE + (1 << 44), ws_bytes=need)
+    assert st == kb.KAMERA_ERR_UNSUPPORTED and "2^23" in msg
