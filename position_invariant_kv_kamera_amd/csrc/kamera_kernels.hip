@@ -117,16 +117,22 @@ __device__ __forceinline__ int remap_block(int b, int total, int mode) {
 }
 
 // The job whose block range holds `blk`: block_starts is ascending, so the job index is the
-// number of starts <= blk, minus one. Each wave counts with one ballot per 64 jobs.
+// number of starts <= blk, minus one. One ballot over every 64th start finds the group of 64
+// jobs, a second ballot the job inside it: two dependent loads however many jobs there are
+// (up to 4096; more take one extra ballot per 4096).
 __device__ __forceinline__ int find_job(const int32_t* block_starts, int n_jobs, int blk) {
   const int lane = threadIdx.x & 63;
-  int count = 0;
-  for (int base = 0; base < n_jobs; base += 64) {
-    const int j = base + lane;
-    const bool le = j < n_jobs && gp(block_starts)[j] <= blk;
-    count += __popcll(__ballot(le));
+  const KGLOBAL int32_t* bs = gp(block_starts);
+  int groups = 0;
+  for (int g0 = 0; 64 * g0 < n_jobs; g0 += 64) {
+    const int gi = g0 + lane;
+    const int c = __popcll(__ballot(64 * gi < n_jobs && bs[64 * gi] <= blk));
+    groups += c;
+    if (c < 64) break;
   }
-  return count - 1;
+  const int base = 64 * (groups - 1);
+  const int j = base + lane;
+  return base + __popcll(__ballot(j < n_jobs && bs[j] <= blk)) - 1;
 }
 
 // cos/sin(delta * theta^(-2i/rot_dim)) for every pair i: angle and range reduction in fp64,
