@@ -331,7 +331,13 @@ kamera_status kamera_patch_compile_orbit(const kamera_model* model,
  * each is attended on its own (Q K^T with bf16 MFMA, exact products; the weights stay fp32
  * for P V, fp32 MFMA) and the segments are combined with the state merge, so results depend
  * on the call's total work only at fp32 rounding level. Tokens whose page table entry lies
- * outside [0, n_pages) are left out (masked). */
+ * outside [0, n_pages) are left out (masked).
+ * An MLA cache (kv_lora_rank head_dim = 512, rope_dim = 64, one latent row per token shared
+ * by every query head, up to 16 query heads) is read in the absorbed form: query rows are
+ * [q_c (512) | q_r (64)] (576 bf16 values per head), scores scale * (<q_c, c_KV_t> +
+ * <q_r, k_rope_t>) with c_KV from pool[1] and k_rope from pool[0], and out holds the 512-wide
+ * latent readout sum_t softmax(scores)_t c_KV_t per head (the caller's up-projection
+ * follows). */
 typedef struct kamera_attn_query {
   int32_t kv_start;  /* first logical cache token attended, >= 0 */
   int32_t kv_len;    /* tokens attended, >= 0 */

@@ -557,10 +557,12 @@ def attn_queries_of(ranges):
 
 def run_decode_attention(model: KameraModel, cache: KameraCache, layer: int, q, ranges, scale,
                          *, stream=None):
-    """kamera_decode_attention of q ([n_queries, n_q_heads, head_dim] bf16 device tensor) over
-    the given (kv_start, kv_len) ranges; returns (out [n, heads, D] fp32, lse [n, heads])."""
+    """kamera_decode_attention of q ([n_queries, n_q_heads, head_dim] bf16 device tensor; MLA:
+    [.., 576] = [q_c | q_r]) over the given (kv_start, kv_len) ranges; returns
+    (out [n, heads, head_dim] fp32, lse [n, heads])."""
     import torch
-    n, heads, D = q.shape
+    n, heads, _ = q.shape
+    D = model.head_dim                 # out rows: head_dim (MLA: the 512-wide latent)
     queries = attn_queries_of(ranges)
     need = kamera_attention_workspace_bytes(model, heads, queries, n)
     if need == 0:

@@ -279,6 +279,168 @@ void attn_segment_kernel(AParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// mla_segment_kernel: decode attention over an MLA cache in the absorbed form. Every query
+// head reads the same single latent row, so the block's 16 MFMA rows are the query heads and
+// the block covers one segment. The four waves take the same 16-token tiles: wave w owns
+// latent features [128 w, 128 w + 128), its slice of the score (the rows as keys) and of the
+// output (the same rows as values), and wave 0 also the k_rope part of the score. The partial
+// scores meet in LDS and are summed in wave order, every wave forms the same softmax, and each
+// accumulates its own 128 output features: no wave merge is needed at the end.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kMlaLatent = 512, kMlaRope = 64;
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void mla_segment_kernel(AParams P) {
+  constexpr int DL = kMlaLatent, DQ = kMlaLatent + kMlaRope;
+  constexpr int WS = DL / 4;          // latent features per wave
+  constexpr int KSW = WS / 32;        // bf16 k-steps of the wave's latent slice
+  constexpr int KSR = kMlaRope / 32;  // bf16 k-steps of k_rope (wave 0)
+  constexpr int NCW = WS / 16;        // output column blocks per wave
+  constexpr int VS = WS + 8;
+  constexpr int PSTR = 17;
+  __shared__ __align__(16) uint16_t vt[4][kTile * VS];
+  __shared__ float pt[4][kTile * PSTR];
+  __shared__ float sc[2][4][kTile * PSTR];   // partial scores, double-buffered by tile
+
+  const int g = blockIdx.x;
+  const int j = P.seg_query[g];
+  const AQuery Q = P.queries[j];
+  const int s = g - Q.seg_start;
+  const int t_lo = Q.kv_start + s * P.seg;
+  const int t_hi = min(Q.kv_start + Q.kv_len, t_lo + P.seg);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int f0 = WS * wave;
+
+  // query operands: head col (rows past n_q are zero)
+  bf16x8 qa[KSW], qr[KSR];
+  {
+    const bool on = col < P.n_q;
+    const uint16_t* qp = P.q + ((int64_t)j * P.n_q + (on ? col : 0)) * DQ;
+#pragma unroll
+    for (int k = 0; k < KSW; ++k)
+      qa[k] = __builtin_bit_cast(bf16x8, on ? *reinterpret_cast<const u32x4*>(qp + f0 + 32 * k + 8 * grp)
+                                            : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int k = 0; k < KSR; ++k)
+      qr[k] = __builtin_bit_cast(bf16x8, on && wave == 0
+                                             ? *reinterpret_cast<const u32x4*>(qp + DL + 32 * k + 8 * grp)
+                                             : u32x4{0u, 0u, 0u, 0u});
+  }
+  float m[4], l[4];
+  f32x4 o[NCW];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // rows of the next tile are in flight while this one is computed
+  auto load_tile = [&](int64_t row, u32x4* lat, u32x4* rope) {
+#pragma unroll
+    for (int k = 0; k < KSW; ++k)
+      lat[k] = row >= 0 ? *reinterpret_cast<const u32x4*>(P.vpool + row + f0 + 32 * k + 8 * grp)
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < KSR; ++k)
+      rope[k] = row >= 0 && wave == 0
+                    ? *reinterpret_cast<const u32x4*>(P.kpool + row + 32 * k + 8 * grp)
+                    : u32x4{0u, 0u, 0u, 0u};
+  };
+  int64_t row = t_lo + col < t_hi ? row_at(P, t_lo + col, page_entry(P, t_lo + col, true)) : -1;
+  u32x4 lat[KSW], rope[KSR];
+  load_tile(row, lat, rope);
+  int it = 0;
+  for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
+    const int t1 = t0 + kTile;
+    const int64_t row_next =
+        t1 + col < t_hi ? row_at(P, t1 + col, page_entry(P, t1 + col, true)) : -1;
+    u32x4 lat_n[KSW], rope_n[KSR];
+    load_tile(row_next, lat_n, rope_n);
+
+    // this wave's part of S: lane holds query rows 4 grp + r of token col
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KSW; ++k)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], __builtin_bit_cast(bf16x8, lat[k]),
+                                                     sacc, 0, 0, 0);
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < KSR; ++k)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr[k], __builtin_bit_cast(bf16x8, rope[k]),
+                                                       sacc, 0, 0, 0);
+    }
+    float* scw = sc[it & 1][wave];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) scw[(4 * grp + r) * PSTR + col] = sacc[r];
+    // the latent slice of the tile is also the V operand of this wave's output features
+#pragma unroll
+    for (int k = 0; k < KSW; ++k)
+      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = lat[k];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int idx = (4 * grp + r) * PSTR + col;
+      const float tot = ((sc[it & 1][0][idx] + sc[it & 1][1][idx]) + sc[it & 1][2][idx]) +
+                        sc[it & 1][3][idx];
+      const float sv = row >= 0 ? tot * P.scale : -INFINITY;
+      float mx = sv;
+      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mn = fmaxf(m[r], mx);
+      float corr = 1.f, p = 0.f;
+      if (mn != -INFINITY) {
+        corr = expf(m[r] - mn);
+        p = expf(sv - mn);
+      }
+      float sum = p;
+      sum += __shfl_xor(sum, 8, 16);
+      sum += __shfl_xor(sum, 4, 16);
+      sum += __shfl_xor(sum, 2, 16);
+      sum += __shfl_xor(sum, 1, 16);
+      l[r] = l[r] * corr + sum;
+      m[r] = mn;
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) o[c][r] *= corr;
+      pt[wave][(4 * grp + r) * PSTR + col] = p;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float a = pt[wave][col * PSTR + 4 * k4 + grp];
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        const float b = bf16_lo(vt[wave][(4 * k4 + grp) * VS + 16 * c + col]);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o[c], 0, 0, 0);
+      }
+    }
+    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+    row = row_next;
+#pragma unroll
+    for (int k = 0; k < KSW; ++k) lat[k] = lat_n[k];
+#pragma unroll
+    for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k];
+  }
+  // every wave holds the same m and l: its own output features, normalised
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hq = 4 * grp + r;
+    if (hq >= P.n_q) continue;
+    const int64_t orow = (int64_t)g * P.n_q + hq;
+    const bool empty = m[r] == -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c)
+      P.part_o[orow * DL + f0 + 16 * c + col] = empty ? 0.f : o[c][r] / l[r];
+    if (wave == 0 && col == 0) P.part_lse[orow] = empty ? -INFINITY : m[r] + logf(l[r]);
+  }
+}
+
 // Merge n parts of one row: lse of part i at lse_p[i * lse_stride], its output at
 // o_p + i * o_stride. Writes out[0 .. D) and *lse_out. The part weights exp(lse_i - M) are
 // formed once per row (in chunks of kMergeChunk parts through LDS), then every feature is a
@@ -734,13 +896,17 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
                                  int64_t capacity, APlan* plan) {
   kamera_status st = validate_model(model);
   if (st != KAMERA_OK) return st;
-  if (model->family != KAMERA_FAMILY_GQA)
-    return fail(KAMERA_ERR_UNSUPPORTED, "decode attention supports GQA/MHA caches");
   if (model->dtype != KAMERA_DTYPE_BF16)
     return fail(KAMERA_ERR_UNSUPPORTED, "decode attention supports bf16 caches");
-  if (model->head_dim != 64 && model->head_dim != 128)
+  if (model->family == KAMERA_FAMILY_MLA) {
+    if (model->head_dim != kMlaLatent || model->rope_dim != kMlaRope)
+      return fail(KAMERA_ERR_UNSUPPORTED,
+                  "MLA decode attention needs a %d-wide latent and %d-wide k_rope (got %d, %d)",
+                  kMlaLatent, kMlaRope, model->head_dim, model->rope_dim);
+  } else if (model->head_dim != 64 && model->head_dim != 128) {
     return fail(KAMERA_ERR_UNSUPPORTED, "decode attention needs head_dim 64 or 128 (got %d)",
                 model->head_dim);
+  }
   if (n_q_heads <= 0 || n_q_heads % model->n_kv_heads)
     return fail(KAMERA_ERR_INVALID_ARGUMENT,
                 "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", n_q_heads,
@@ -938,10 +1104,12 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
       cache->layer_stride % 8)
     return fail(KAMERA_ERR_UNSUPPORTED, "cache rows must start on 16-byte boundaries");
   const size_t D = model->head_dim;
+  const bool mla = model->family == KAMERA_FAMILY_MLA;
+  const size_t DQ = mla ? (size_t)kMlaLatent + kMlaRope : D;   // query row length
   const size_t rows = (size_t)n_queries * n_q_heads;
   if (n_queries > 0 && (ranges_overlap(out, rows * D * 4, lse, rows * 4) ||
-                        ranges_overlap(out, rows * D * 4, q, rows * D * 2) ||
-                        ranges_overlap(lse, rows * 4, q, rows * D * 2)))
+                        ranges_overlap(out, rows * D * 4, q, rows * DQ * 2) ||
+                        ranges_overlap(lse, rows * 4, q, rows * DQ * 2)))
     return fail(KAMERA_ERR_OVERLAP, "q, out and lse must not overlap");
   if (!workspace) return fail(KAMERA_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -987,7 +1155,8 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
   const int64_t seg_blocks = (int64_t)plan.seg_query.size() * model->n_kv_heads;
   if (seg_blocks > 0) {
     const dim3 grid((unsigned)seg_blocks), block(kThreads);
-    if (D == 128) attn_segment_kernel<128><<<grid, block, 0, stream>>>(P);
+    if (mla) mla_segment_kernel<<<grid, block, 0, stream>>>(P);
+    else if (D == 128) attn_segment_kernel<128><<<grid, block, 0, stream>>>(P);
     else attn_segment_kernel<64><<<grid, block, 0, stream>>>(P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

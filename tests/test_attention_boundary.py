@@ -52,6 +52,11 @@ def test_exports_and_layout():
 def test_well_formed_call_reaches_the_workspace_check():
     assert _call() == kb.KAMERA_ERR_WORKSPACE
     assert _call(_model(head_dim=64, rope_dim=64), n_q_heads=16) == kb.KAMERA_ERR_WORKSPACE
+    mla = _model(family="mla", n_kv_heads=1, head_dim=512, rope_dim=64)
+    assert _call(mla, n_q_heads=16) == kb.KAMERA_ERR_WORKSPACE
+    # MLA query rows are 576 wide: q overlapping out by its true extent is caught
+    rows = 16
+    assert _call(mla, n_q_heads=16, q=FAKE + 21 * GiB - rows * 576 * 2 + 64) == kb.KAMERA_ERR_OVERLAP
 
 
 def test_workspace_bytes():
@@ -65,7 +70,9 @@ def test_workspace_bytes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(model=_model(family="mla", n_kv_heads=1, head_dim=512, rope_dim=64)), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(family="mla", n_kv_heads=1, head_dim=512, rope_dim=64)), kb.KAMERA_ERR_UNSUPPORTED),   # 28 heads > 16
+    (dict(model=_model(family="mla", n_kv_heads=1, head_dim=256, rope_dim=64), n_q_heads=16), kb.KAMERA_ERR_UNSUPPORTED),
+    (dict(model=_model(family="mla", n_kv_heads=1, head_dim=512, rope_dim=32), n_q_heads=16), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(model=_model(dtype="f32")), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(model=_model(head_dim=96, rope_dim=96)), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(n_q_heads=30), kb.KAMERA_ERR_INVALID_ARGUMENT),

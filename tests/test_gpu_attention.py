@@ -210,3 +210,101 @@ def test_mid_size_calls_take_1024_token_segments():
     ranges += [(1023, 1025), (5000, 600)]
     assert _segment_tokens(ranges, 8) == 1024
     _run_and_check(s, 1, ranges, 8, 0.1, seed=16)
+
+
+# ---- MLA cache (absorbed form) -------------------------------------------------------------
+
+class MlaSetup:
+    """Pools of one layer-pair MLA cache: rows [c_KV (512) | k_rope (64)] shared (pool[1] is
+    the row start, pool[0] 512 elements in) or two separate pools."""
+
+    def __init__(self, n_layers=2, page_size=16, n_pages=300, n_logical=280, shared=True,
+                 bad_pages=(), seed=0):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        rng = np.random.default_rng(seed)
+        self.ps, self.n_pages = page_size, n_pages
+        t = rng.permutation(n_pages)[:n_logical].astype(np.int32)
+        for b in bad_pages:
+            t[b] = -1                                  # outside the pool: masked
+        self.table = t
+        self.table_dev = torch.from_numpy(t).cuda()
+        self.model = kb.make_model("mla", "bf16", n_layers, 1, 512, 64, "half_split", 1e4)
+        c = kb.KameraCache()
+        if shared:
+            self.rows = torch.randn((n_layers, n_pages, page_size, 576), generator=g,
+                                    device="cuda").to(torch.bfloat16)
+            c.pool[1] = self.rows.data_ptr()
+            c.pool[0] = self.rows.data_ptr() + 512 * 2
+            c.layer_stride = self.rows.stride(0)
+            c.token_stride = 576
+            host = _bits_to_f64(self.rows)
+            self.lat, self.rope = host[..., :512], host[..., 512:]
+        else:
+            self.lat_t = torch.randn((n_layers, n_pages, page_size, 512), generator=g,
+                                     device="cuda").to(torch.bfloat16)
+            self.rope_t = torch.randn((n_layers, n_pages, page_size, 512), generator=g,
+                                      device="cuda").to(torch.bfloat16)   # rows of 512, 64 used
+            c.pool[1] = self.lat_t.data_ptr()
+            c.pool[0] = self.rope_t.data_ptr()
+            c.layer_stride = self.lat_t.stride(0)
+            c.token_stride = 512
+            self.lat = _bits_to_f64(self.lat_t)
+            self.rope = _bits_to_f64(self.rope_t)[..., :64]
+        c.page_table = self.table_dev.data_ptr()
+        c.n_logical_pages = n_logical
+        c.page_size = page_size
+        c.n_pages = n_pages
+        self.cache = c
+
+    def kv(self, layer, start, n):
+        p = np.arange(start, start + n)
+        phys = self.table[p // self.ps].astype(np.int64)
+        ok = (phys >= 0) & (phys < self.n_pages)
+        lat = self.lat[layer][phys[ok], (p % self.ps)[ok]]
+        rope = self.rope[layer][phys[ok], (p % self.ps)[ok]]
+        return np.concatenate([lat, rope], axis=1), lat
+
+
+def _run_mla(s, layer, ranges, n_q, scale, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randn((len(ranges), n_q, 576), generator=g, device="cuda").to(torch.bfloat16)
+    print(f"[attn-mla] n_q={n_q} ranges={list(ranges)[:6]} layer={layer}", flush=True)
+    out, lse = kb.run_decode_attention(s.model, s.cache, layer, q, ranges, scale)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (len(ranges), n_q, 512)
+    out = out.cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    q64 = _bits_to_f64(q)
+    worst = 0.0
+    for j, (a, n) in enumerate(ranges):
+        K, V = s.kv(layer, a, n)
+        o, l = att.decode_attention(q64[j], K, V, scale)
+        if K.shape[0] == 0:
+            assert np.all(out[j] == 0) and np.all(np.isneginf(lse[j])), f"query {j}: empty"
+            continue
+        sc = scale * q64[j] @ K.T
+        eps = 2 * (576 + 4) * U * att.score_bounds(q64[j], K, scale).max(axis=1) + U * np.abs(sc).max(axis=1)
+        w = np.exp(sc - sc.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        c = 64 + -(-max(n, 1) // 16)
+        otol = (2 * eps + c * U)[:, None] * (w @ np.abs(V))
+        ltol = eps + c * U * (1 + np.abs(l))
+        err = np.abs(out[j] - o)
+        assert np.all(err <= otol + 1e-30), (j, float((err / (otol + 1e-30)).max()))
+        lerr = np.abs(lse[j] - l)
+        assert np.all(lerr <= ltol), (j, float((lerr / ltol).max()))
+        worst = max(worst, float((err / (otol + 1e-30)).max()), float((lerr / ltol).max()))
+    print(f"[attn-mla] worst error / tolerance {worst:.3g}", flush=True)
+
+
+def test_mla_decode_shared_rows_16_heads_masked_pages():
+    s = MlaSetup(bad_pages=(3, 50), seed=21)
+    _run_mla(s, 1, [(0, 1), (0, 17), (5, 511), (100, 2000), (0, 4480), (7, 0)], 16,
+             1 / math.sqrt(192), seed=22)
+
+
+def test_mla_decode_separate_pools_fewer_heads():
+    s = MlaSetup(shared=False, n_pages=200, n_logical=200, page_size=12, seed=23)
+    _run_mla(s, 0, [(0, 2400), (11, 13), (1000, 1025)], 5, 0.07, seed=24)
