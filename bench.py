@@ -8,7 +8,8 @@ Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM G
 line also carries "patch_compile": the time kamera_patch_compile takes to form the same
 batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass, and
 "decode_attention": the consumer-side decode attention (with its state merge) on a
-64-sequence x 16K-token paged cache, and "chunk_attention": the same decode read from 16
+64-sequence x 16K-token paged cache ("decode_attention_mla": the same over an MLA cache), and
+"chunk_attention": the same decode read from 16
 canonical chunks per sequence in place (query turned per chunk, rank-16 patches on K and V).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--compile-steps N] [--attention-steps N] [--chunk-attention-steps N]
@@ -267,6 +268,62 @@ def attention_leg(steps: int, stream) -> dict:
             "timed_with": "hip events on the launch stream (segment + merge kernels)"}
 
 
+def mla_attention_leg(steps: int, stream) -> dict:
+    """Decode attention over one layer of a DeepSeek-V2-Lite-like MLA cache (rows [c_KV 512 |
+    k_rope 64], 16 query heads reading the one latent row): 64 sequences x 16384 tokens, paged
+    16 with a shuffled page table. Bytes = every latent and k_rope row read once."""
+    import numpy as np
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+
+    n_seq, ctx, n_q, ps = 64, 16384, 16, 16
+    n_pages = n_seq * ctx // ps
+    g = torch.Generator(device="cuda")
+    g.manual_seed(79)
+    rows = torch.randn((1, n_pages, ps, 576), generator=g, device="cuda").to(torch.bfloat16)
+    table = torch.from_numpy(np.random.default_rng(79).permutation(n_pages).astype(np.int32)).cuda()
+    model = kb.make_model("mla", "bf16", 1, 1, 512, 64, "half_split", 1e4)
+    cache = kb.KameraCache()
+    cache.pool[1], cache.pool[0] = rows.data_ptr(), rows.data_ptr() + 512 * 2
+    cache.layer_stride = rows.stride(0)
+    cache.token_stride = 576
+    cache.page_table = table.data_ptr()
+    cache.n_logical_pages = n_pages
+    cache.page_size = ps
+    cache.n_pages = n_pages
+    q = torch.randn((n_seq, n_q, 576), generator=g, device="cuda").to(torch.bfloat16)
+    queries = kb.attn_queries_of([(i * ctx, ctx) for i in range(n_seq)])
+    need = kb.kamera_attention_workspace_bytes(model, n_q, queries, n_seq)
+    ws = kb.Workspace(nbytes=need)
+    out = torch.empty((n_seq, n_q, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_seq, n_q), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        kb.check(kb.kamera_decode_attention(model, cache, 0, q.data_ptr(), n_q, queries, n_seq,
+                                            1.0 / 192 ** 0.5, out.data_ptr(), lse.data_ptr(),
+                                            ws.ptr, ws.nbytes, sp))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kv_bytes = n_seq * ctx * 576 * 2
+    gbps = kv_bytes / (ms * 1e-3) / 1e9
+    del rows, table, q, out, lse, ws
+    return {"shape": f"{n_seq} sequences x {ctx} tokens, MLA rows c_KV 512 + k_rope 64, "
+                     f"{n_q} query heads, paged {ps} shuffled, one layer",
+            "ms_per_call": round(ms, 4), "kv_bytes": kv_bytes, "achieved_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": steps,
+            "timed_with": "hip events on the launch stream (segment + merge kernels)"}
+
+
 def chunk_attention_leg(steps: int, stream) -> dict:
     """Attention over chunks read in place, shaped like the decode leg: 64 sequences x 16
     canonical chunks of 1024 tokens, 4 KV heads x 128, 28 query heads, one layer, each chunk
@@ -495,7 +552,9 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
     seg = [r for r in rows if "attn_segment_kernel" in r["Name"]]
     mrg = [r for r in rows if "attn_merge_kernel" in r["Name"]]
     chk = [r for r in rows if "chunk_attn_kernel" in r["Name"]]
+    mla = [r for r in rows if "mla_segment_kernel" in r["Name"]]
     ca = rec.get("chunk_attention")
+    dm = rec.get("decode_attention_mla")
     lines = ["# decode attention (consumer side)", "", "Commands (R = repository root on the GPU box):", ""]
     lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
     lines += [f"Shape: {da['shape']}. Bytes per call: K and V once = {da['kv_bytes'] / 1e9:.3f} GB.",
@@ -507,6 +566,17 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
         gb = da["kv_bytes"] / avg if "segment" in r["Name"] else float("nan")
         lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
                      f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
+    if dm and mla:
+        lines += ["", f"MLA cache: {dm['shape']}. Bytes per call: latent and k_rope rows once = "
+                  f"{dm['kv_bytes'] / 1e9:.3f} GB. HIP events: {dm['ms_per_call']} ms per call "
+                  f"(segment + merge kernels) = {dm['achieved_gbps']} GB/s ({dm['hbm_frac']} of 8 TB/s).",
+                  "", "| kernel | calls | avg us | GB/s (bytes / avg) | of 8 TB/s |",
+                  "|---|---|---|---|---|"]
+        for r in mla:
+            avg = float(r["AverageNs"])
+            gb = dm["kv_bytes"] / avg
+            lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
+                         f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
     if ca and chk:
         lines += ["", f"Attention over chunks read in place: {ca['shape']}. Bytes per call: "
                   f"canonical K and V, U_K and U_V rows and each chunk's V_K, V_V once = "
@@ -677,6 +747,8 @@ def main():
     if args.attention_steps > 0:
         print("[bench] timing decode attention", file=sys.stderr, flush=True)
         out["decode_attention"] = attention_leg(args.attention_steps, stream)
+        print("[bench] timing decode attention over an MLA cache", file=sys.stderr, flush=True)
+        out["decode_attention_mla"] = mla_attention_leg(args.attention_steps, stream)
     if args.chunk_attention_steps > 0:
         print("[bench] timing attention over chunks read in place", file=sys.stderr, flush=True)
         out["chunk_attention"] = chunk_attention_leg(args.chunk_attention_steps, stream)
