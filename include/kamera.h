@@ -361,8 +361,11 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
  *     part_out [n_parts][n_rows][head_dim], part_lse [n_parts][n_rows]
  *  -> out [n_rows][head_dim], lse [n_rows]:
  *     L = log sum_i exp(lse_i),  out = sum_i exp(lse_i - L) part_out_i.
- * Parts with lse = -inf drop out; a row whose parts are all empty gives out = 0, lse = -inf.
- * out and lse must not overlap the inputs. head_dim <= 1024; no workspace. */
+ * Parts with lse = -inf drop out (their part_out values are not read); a row whose parts are
+ * all empty gives out = 0, lse = -inf. out and lse must not overlap the inputs.
+ * head_dim <= 1024; any float alignment (16-byte loads when part_out is 16-byte aligned and
+ * head_dim % 4 == 0); the sums run in a fixed order (repeat calls agree bit for bit);
+ * no workspace. */
 kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_dim,
                                  const float* part_out, const float* part_lse, float* out,
                                  float* lse, void* stream);

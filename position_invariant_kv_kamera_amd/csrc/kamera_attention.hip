@@ -290,8 +290,14 @@ void attn_segment_kernel(AParams P) {
 // ---------------------------------------------------------------------------------------
 
 constexpr int kMlaLatent = 512, kMlaRope = 64;
+#ifndef KAMERA_MLA_PREFETCH
+#define KAMERA_MLA_PREFETCH 1   // tiles whose rows are in flight ahead of the one computed
+#endif
+#ifndef KAMERA_MLA_WAVES_PER_EU
+#define KAMERA_MLA_WAVES_PER_EU 3
+#endif
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KAMERA_MLA_WAVES_PER_EU, 8)))
 void mla_segment_kernel(AParams P) {
   constexpr int DL = kMlaLatent, DQ = kMlaLatent + kMlaRope;
   constexpr int WS = DL / 4;          // latent features per wave
@@ -351,17 +357,25 @@ void mla_segment_kernel(AParams P) {
                     ? *reinterpret_cast<const u32x4*>(P.kpool + row + 32 * k + 8 * grp)
                     : u32x4{0u, 0u, 0u, 0u};
   };
-  int64_t row = t_lo + col < t_hi ? row_at(P, t_lo + col, page_entry(P, t_lo + col, true)) : -1;
-  u32x4 lat[KSW], rope[KSR];
-  load_tile(row, lat, rope);
+  // rows of the next KAMERA_MLA_PREFETCH tiles are in flight (a ring of tile buffers)
+  constexpr int PF = KAMERA_MLA_PREFETCH;
+  auto row_of = [&](int t0) -> int64_t {
+    return t0 + col < t_hi ? row_at(P, t0 + col, page_entry(P, t0 + col, true)) : -1;
+  };
+  int64_t rows[PF + 1];
+  u32x4 lat_r[PF + 1][KSW], rope_r[PF + 1][KSR];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    rows[k] = row_of(t_lo + kTile * k);
+    load_tile(rows[k], lat_r[k], rope_r[k]);
+  }
   int it = 0;
   for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
-    const int t1 = t0 + kTile;
-    const int64_t row_next =
-        t1 + col < t_hi ? row_at(P, t1 + col, page_entry(P, t1 + col, true)) : -1;
-    u32x4 lat_n[KSW], rope_n[KSR];
-    load_tile(row_next, lat_n, rope_n);
-
+    rows[PF] = row_of(t0 + kTile * PF);
+    load_tile(rows[PF], lat_r[PF], rope_r[PF]);
+    const int64_t row = rows[0];
+    u32x4* lat = lat_r[0];
+    u32x4* rope = rope_r[0];
     // this wave's part of S: lane holds query rows 4 grp + r of token col
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -421,11 +435,14 @@ void mla_segment_kernel(AParams P) {
       }
     }
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
-    row = row_next;
 #pragma unroll
-    for (int k = 0; k < KSW; ++k) lat[k] = lat_n[k];
+    for (int q = 0; q < PF; ++q) {
+      rows[q] = rows[q + 1];
 #pragma unroll
-    for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k];
+      for (int k = 0; k < KSW; ++k) lat_r[q][k] = lat_r[q + 1][k];
+#pragma unroll
+      for (int k = 0; k < KSR; ++k) rope_r[q][k] = rope_r[q + 1][k];
+    }
   }
   // every wave holds the same m and l: its own output features, normalised
 #pragma unroll
@@ -443,70 +460,105 @@ void mla_segment_kernel(AParams P) {
 
 // Merge n parts of one row: lse of part i at lse_p[i * lse_stride], its output at
 // o_p + i * o_stride. Writes out[0 .. D) and *lse_out. The part weights exp(lse_i - M) are
-// formed once per row (in chunks of kMergeChunk parts through LDS), then every feature is a
-// weighted sum.
+// formed once per row (in chunks of kMergeChunk parts through LDS). The row's features are cut
+// into columns of VW floats (VW = 4: 16-byte loads, D % 4 == 0 and o_p 16-byte aligned); when
+// a row has fewer columns than the block has threads, G = kMergeThreads / columns groups of
+// threads take every G-th part, so many parts are in flight at once, and the groups' sums are
+// added in group order through LDS. A part of weight 0 (lse = -inf) is skipped, whatever its
+// output holds.
 constexpr int kMergeChunk = 256;
+constexpr int kMergeThreads = 256;
+template <int VW>
 __device__ void merge_row(const float* lse_p, int64_t lse_stride, const float* o_p,
                           int64_t o_stride, int n, int D, float* out, float* lse_out) {
-  __shared__ float red[64];
+  typedef float fv __attribute__((ext_vector_type(VW)));
+  constexpr int NCOL = VW == 4 ? 1 : 4;   // columns per thread (D <= 1024)
+  __shared__ float red[kMergeThreads / 64];
   __shared__ float wts[kMergeChunk];
+  __shared__ __align__(16) float part_sum[kMergeThreads * VW];
+  const int tid = threadIdx.x;
   float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, lse_p[i * lse_stride]);
-  red[threadIdx.x] = M;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int t = 1; t < (int)blockDim.x; ++t) M = fmaxf(M, red[t]);
-    red[0] = M;
-  }
-  __syncthreads();
-  M = red[0];
-  __syncthreads();
-  float acc[16];   // features threadIdx.x + 64 k (D <= 1024)
+  for (int i = tid; i < n; i += kMergeThreads) M = fmaxf(M, lse_p[i * lse_stride]);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int C = D / VW;                              // columns of the row
+  const int T = min(C, kMergeThreads);               // threads per group
+  const int G = kMergeThreads / T;                   // groups
+  const int grp = tid / T, c0 = tid - grp * T;
+  const bool active = grp < G;
+  fv acc[NCOL];
+#pragma unroll
+  for (int k = 0; k < NCOL; ++k) acc[k] = fv(0.f);
   float Z = 0.f;
-  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
-    const int cn = min(kMergeChunk, n - c0);
-    for (int i = threadIdx.x; i < cn; i += blockDim.x)
-      wts[i] = M == -INFINITY ? 0.f : expf(lse_p[(c0 + i) * lse_stride] - M);
+  for (int p0 = 0; p0 < n; p0 += kMergeChunk) {
+    const int cn = min(kMergeChunk, n - p0);
+    __syncthreads();   // the previous chunk's weights are no longer read
+    for (int i = tid; i < cn; i += kMergeThreads)
+      wts[i] = M == -INFINITY ? 0.f : expf(lse_p[(p0 + i) * lse_stride] - M);
     __syncthreads();
-    for (int i = 0; i < cn; ++i) {
+    for (int i = 0; i < cn; ++i) Z += wts[i];
+    if (!active) continue;
+#pragma unroll 4
+    for (int i = grp; i < cn; i += G) {
       const float e = wts[i];
-      Z += e;
       if (e == 0.f) continue;
-      const float* oi = o_p + (int64_t)(c0 + i) * o_stride;
+      const float* oi = o_p + (int64_t)(p0 + i) * o_stride;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int f = threadIdx.x + 64 * k;
-        if (f < D) acc[k] += e * oi[f];
+      for (int k = 0; k < NCOL; ++k) {
+        const int c = c0 + T * k;
+        if (c < C) acc[k] += e * *reinterpret_cast<const fv*>(oi + VW * c);
       }
     }
+  }
+  if (G > 1) {   // one column per thread: add the groups' sums in group order
+    if (active) *reinterpret_cast<fv*>(&part_sum[VW * tid]) = acc[0];
     __syncthreads();
+    if (grp == 0) {
+      fv t = *reinterpret_cast<const fv*>(&part_sum[VW * c0]);
+      for (int g2 = 1; g2 < G; ++g2) t += *reinterpret_cast<const fv*>(&part_sum[VW * (g2 * T + c0)]);
+      acc[0] = t;
+    }
   }
+  if (grp == 0) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int f = threadIdx.x + 64 * k;
-    if (f < D) out[f] = M == -INFINITY ? 0.f : acc[k] / Z;
+    for (int k = 0; k < NCOL; ++k) {
+      const int c = c0 + T * k;
+      if (c >= C) continue;
+#pragma unroll
+      for (int v = 0; v < VW; ++v) out[VW * c + v] = M == -INFINITY ? 0.f : acc[k][v] / Z;
+    }
   }
-  if (threadIdx.x == 0) *lse_out = M == -INFINITY ? -INFINITY : M + logf(Z);
+  if (tid == 0) *lse_out = M == -INFINITY ? -INFINITY : M + logf(Z);
 }
 
-__global__ __launch_bounds__(64) void attn_merge_kernel(AParams P, int D) {
+// Row r of the (query, query head) rows: the parts are the query's segments.
+template <int VW>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AParams P, int D) {
   const int r = blockIdx.x;
   const int j = r / P.n_q, qh = r - j * P.n_q;
   const AQuery Q = P.queries[j];
   const int64_t base = (int64_t)Q.seg_start * P.n_q + qh;
-  merge_row(P.part_lse + base, P.n_q, P.part_o + base * D, (int64_t)P.n_q * D, Q.n_segs, D,
-            P.out + (int64_t)r * D, P.lse + r);
+  merge_row<VW>(P.part_lse + base, P.n_q, P.part_o + base * D, (int64_t)P.n_q * D, Q.n_segs, D,
+                P.out + (int64_t)r * D, P.lse + r);
 }
 
-__global__ __launch_bounds__(64) void state_merge_kernel(const float* part_out,
-                                                         const float* part_lse, float* out,
-                                                         float* lse, int n_parts, int n_rows,
-                                                         int D) {
+template <int VW>
+__global__ __launch_bounds__(kMergeThreads) void state_merge_kernel(const float* part_out,
+                                                                    const float* part_lse,
+                                                                    float* out, float* lse,
+                                                                    int n_parts, int n_rows, int D) {
   const int r = blockIdx.x;
-  merge_row(part_lse + r, n_rows, part_out + (int64_t)r * D, (int64_t)n_rows * D, n_parts, D,
-            out + (int64_t)r * D, lse + r);
+  merge_row<VW>(part_lse + r, n_rows, part_out + (int64_t)r * D, (int64_t)n_rows * D, n_parts, D,
+                out + (int64_t)r * D, lse + r);
+}
+
+// Parts in the workspace start 256-byte aligned and every head width the attention calls take
+// is a multiple of 4, so their merges always read 16 bytes at a time.
+void launch_attn_merge(const AParams& P, int64_t rows, int D, hipStream_t stream) {
+  attn_merge_kernel<4><<<dim3((unsigned)rows), dim3(kMergeThreads), 0, stream>>>(P, D);
 }
 
 
@@ -1162,7 +1214,7 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
     if (e != hipSuccess)
       return fail(KAMERA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
   }
-  attn_merge_kernel<<<dim3((unsigned)rows), dim3(64), 0, stream>>>(P, (int)D);
+  launch_attn_merge(P, rows, (int)D, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return KAMERA_OK;
@@ -1306,7 +1358,7 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
   M.out = out;
   M.lse = lse;
   M.n_q = n_q_heads;
-  attn_merge_kernel<<<dim3((unsigned)rows), dim3(64), 0, stream>>>(M, (int)D);
+  launch_attn_merge(M, rows, (int)D, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return KAMERA_OK;
@@ -1331,8 +1383,13 @@ kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_d
                                                            ranges_overlap(lse, ol, part_lse, pl))))
     return fail(KAMERA_ERR_OVERLAP, "out and lse must not overlap the parts or each other");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  state_merge_kernel<<<dim3((unsigned)n_rows), dim3(64), 0, stream>>>(part_out, part_lse, out, lse,
-                                                                       n_parts, n_rows, head_dim);
+  const bool vec = head_dim % 4 == 0 && reinterpret_cast<uintptr_t>(part_out) % 16 == 0;
+  if (vec)
+    state_merge_kernel<4><<<dim3((unsigned)n_rows), dim3(kMergeThreads), 0, stream>>>(
+        part_out, part_lse, out, lse, n_parts, n_rows, head_dim);
+  else
+    state_merge_kernel<1><<<dim3((unsigned)n_rows), dim3(kMergeThreads), 0, stream>>>(
+        part_out, part_lse, out, lse, n_parts, n_rows, head_dim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return KAMERA_OK;

@@ -185,6 +185,54 @@ def test_state_merge_with_empty_parts():
     np.testing.assert_allclose(got_l[:4], ref_l[:4], rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("n_parts,rows,D,offset", [
+    (5, 3, 37, 0),       # odd width: one float per column, 6 groups of threads over the parts
+    (7, 4, 128, 1),      # part_out 4 bytes past 16-byte alignment: one float per column
+    (9, 2, 300, 0),      # 75 columns of 4: 3 groups, the block's last 31 threads idle
+    (600, 2, 1024, 0),   # 256 columns of 4, parts in 3 chunks of weights
+    (40, 3, 999, 0),     # 999 columns of 1: four columns per thread
+])
+def test_state_merge_widths_alignments_and_many_parts(n_parts, rows, D, offset):
+    """Every merge layout against the fp64 state merge. Empty parts (lse = -inf) hold NaN on
+    the device: their outputs must not be read. Bound (derived): each feature is a sum of at
+    most n_parts + 8 fp32 terms e_i o_i / Z, so |out - ref| <= (n_parts + 8) u sum_i w_i |o_i|
+    + 2 u |ref|, and |lse - ref| <= (n_parts + 8) u + u |ref|."""
+    rng = np.random.default_rng(1000 + D)
+    po = rng.standard_normal((n_parts, rows, D)).astype(np.float32)
+    pl = (3.0 * rng.standard_normal((n_parts, rows))).astype(np.float32)
+    empty = rng.random((n_parts, rows)) < 0.2
+    empty[:, -1] = True                                  # the last row has no parts at all
+    pl[empty] = -np.inf
+    dev_po = po.copy()
+    dev_po[empty] = np.nan
+    po[empty] = 0.0
+    flat = torch.zeros(offset + dev_po.size, dtype=torch.float32)
+    flat[offset:] = torch.from_numpy(dev_po.reshape(-1))
+    dflat, dpl = flat.cuda(), torch.from_numpy(pl).cuda()
+    out = torch.empty((rows, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    args = (n_parts, rows, D, dflat.data_ptr() + 4 * offset, dpl.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), kb.current_stream_ptr())
+    kb.check(kb.kamera_state_merge(*args))
+    torch.cuda.synchronize()
+    got_o, got_l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = att.state_merge(list(po.astype(np.float64)), list(pl.astype(np.float64)))
+    assert np.isneginf(got_l[-1]) and np.all(got_o[-1] == 0)
+    live = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(got_l), live)
+    M = np.where(live, ref_l, 0.0)
+    w = np.where(np.isfinite(pl), np.exp(pl.astype(np.float64) - M), 0.0)   # parts x rows
+    bound = (n_parts + 8) * U * np.einsum("pr,prd->rd", w, np.abs(po.astype(np.float64)))
+    bound += 2 * U * np.abs(ref_o)
+    assert np.all(np.abs(got_o - ref_o) <= bound + 1e-30)
+    assert np.all(np.abs(got_l[live] - ref_l[live]) <= (n_parts + 8) * U + U * np.abs(ref_l[live]))
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    kb.check(kb.kamera_state_merge(*args[:5], out2.data_ptr(), lse2.data_ptr(), args[7]))
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
 def _segment_tokens(ranges, n_kv):
     """The segment length the library picks: the longest of 2048, 1024, 512 that still gives
     the call 2048 blocks (segments x KV heads)."""
