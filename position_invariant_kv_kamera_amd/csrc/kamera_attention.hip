@@ -43,6 +43,31 @@ constexpr int kThreads = 256;
 constexpr int kTile = 16;
 constexpr int kMaxGroup = 16;
 
+// Max and sum over the 16 lanes of one DPP row (lanes 16 r .. 16 r + 15), every lane taking the
+// result: combine with the partner lane in the pair, then in the quad (quad_perm), then with the
+// mirrored lane of the half row and of the row. At each step both lanes of a partner pair combine
+// the same two values, so all 16 lanes end with the same bits.
+template <int CTRL>
+__device__ inline float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E;            // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;    // row_half_mirror, row_mirror
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp_row<kDppSwap1>(v));
+  v = fmaxf(v, dpp_row<kDppSwap2>(v));
+  v = fmaxf(v, dpp_row<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_row<kDppMirror>(v));
+}
+__device__ inline float row16_sum(float v) {
+  v += dpp_row<kDppSwap1>(v);
+  v += dpp_row<kDppSwap2>(v);
+  v += dpp_row<kDppHalfMirror>(v);
+  return v + dpp_row<kDppMirror>(v);
+}
+
+
 struct alignas(16) AQuery {
   int32_t kv_start, kv_len, seg_start, n_segs;
 };
@@ -189,22 +214,14 @@ void attn_segment_kernel(AParams P) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float sc = row >= 0 ? sacc[r] * P.scale : -INFINITY;
-      float mx = sc;
-      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mx = row16_max(sc);
       const float mn = fmaxf(m[r], mx);
       float corr = 1.f, p = 0.f;
       if (mn != -INFINITY) {
         corr = expf(m[r] - mn);
         p = expf(sc - mn);
       }
-      float sum = p;
-      sum += __shfl_xor(sum, 8, 16);
-      sum += __shfl_xor(sum, 4, 16);
-      sum += __shfl_xor(sum, 2, 16);
-      sum += __shfl_xor(sum, 1, 16);
+      const float sum = row16_sum(p);
       l[r] = l[r] * corr + sum;
       m[r] = mn;
 #pragma unroll
@@ -402,22 +419,14 @@ void mla_segment_kernel(AParams P) {
       const float tot = ((sc[it & 1][0][idx] + sc[it & 1][1][idx]) + sc[it & 1][2][idx]) +
                         sc[it & 1][3][idx];
       const float sv = row >= 0 ? tot * P.scale : -INFINITY;
-      float mx = sv;
-      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mx = row16_max(sv);
       const float mn = fmaxf(m[r], mx);
       float corr = 1.f, p = 0.f;
       if (mn != -INFINITY) {
         corr = expf(m[r] - mn);
         p = expf(sv - mn);
       }
-      float sum = p;
-      sum += __shfl_xor(sum, 8, 16);
-      sum += __shfl_xor(sum, 4, 16);
-      sum += __shfl_xor(sum, 2, 16);
-      sum += __shfl_xor(sum, 1, 16);
+      const float sum = row16_sum(p);
       l[r] = l[r] * corr + sum;
       m[r] = mn;
 #pragma unroll
@@ -831,22 +840,14 @@ void chunk_attn_kernel(VParams P) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float sc = valid ? sacc[r] * P.scale : -INFINITY;
-      float mx = sc;
-      mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+      const float mx = row16_max(sc);
       const float mn = fmaxf(m[r], mx);
       float corr = 1.f, p = 0.f;
       if (mn != -INFINITY) {
         corr = expf(m[r] - mn);
         p = expf(sc - mn);
       }
-      float sum = p;
-      sum += __shfl_xor(sum, 8, 16);
-      sum += __shfl_xor(sum, 4, 16);
-      sum += __shfl_xor(sum, 2, 16);
-      sum += __shfl_xor(sum, 1, 16);
+      const float sum = row16_sum(p);
       l[r] = l[r] * corr + sum;
       m[r] = mn;
 #pragma unroll
