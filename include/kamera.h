@@ -328,9 +328,11 @@ kamera_status kamera_patch_compile_orbit(const kamera_model* model,
  *     lse[j*n_q_heads + h] = log sum_t exp(score_t)                          (fp32, natural)
  * (out = 0 and lse = -inf when kv_len == 0). The key ranges are cut into segments of 2048,
  * 1024 or KAMERA_ATTN_SEGMENT tokens (the longest that still gives the call 2048 blocks);
- * each is attended on its own (Q K^T with bf16 MFMA, exact products; the weights stay fp32
- * for P V, fp32 MFMA) and the segments are combined with the state merge, so results depend
- * on the call's total work only at fp32 rounding level. Tokens whose page table entry lies
+ * each is attended on its own (Q K^T with bf16 MFMA, exact products; scores in base 2, the
+ * fp32 dot product times scale log2(e) rounded once to fp32, weights 2^(s - max) from the
+ * hardware exp2; the weights stay fp32 for P V, fp32 MFMA) and the segments are combined with
+ * the state merge, so results depend on the call's total work only at fp32 rounding level.
+ * scale and scale log2(e) must be finite in fp32. Tokens whose page table entry lies
  * outside [0, n_pages) are left out (masked).
  * An MLA cache (kv_lora_rank head_dim = 512, rope_dim = 64, one latent row per token shared
  * by every query head, up to 16 query heads) is read in the absorbed form: query rows are

@@ -54,17 +54,69 @@ __device__ inline float dpp_row(float v) {
 }
 constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E;            // quad_perm [1,0,3,2], [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;    // row_half_mirror, row_mirror
-__device__ inline float row16_max(float v) {
-  v = fmaxf(v, dpp_row<kDppSwap1>(v));
-  v = fmaxf(v, dpp_row<kDppSwap2>(v));
-  v = fmaxf(v, dpp_row<kDppHalfMirror>(v));
-  return fmaxf(v, dpp_row<kDppMirror>(v));
-}
 __device__ inline float row16_sum(float v) {
   v += dpp_row<kDppSwap1>(v);
   v += dpp_row<kDppSwap2>(v);
   v += dpp_row<kDppHalfMirror>(v);
   return v + dpp_row<kDppMirror>(v);
+}
+// The max runs on integer keys that order like the floats (non-NaN), so each step is one fused
+// DPP integer max.
+__device__ inline int order_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ inline float order_key_inv(int k) {
+  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff));
+}
+template <int CTRL>
+__device__ inline int dpp_row_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+__device__ inline float row16_max(float v) {
+  int k = order_key(v);
+  k = max(k, dpp_row_i<kDppSwap1>(k));
+  k = max(k, dpp_row_i<kDppSwap2>(k));
+  k = max(k, dpp_row_i<kDppHalfMirror>(k));
+  return order_key_inv(max(k, dpp_row_i<kDppMirror>(k)));
+}
+
+// Scores run in base-2 units: the host folds log2(e) into the scale (one fp32 rounding), the
+// weights are 2^(s - m) from the hardware exp2, and a state's lse is converted back to the
+// natural log when it is written: lse = m ln 2 + ln l.
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax step of the 4 query rows a lane holds (rows 4 grp + r, token col of the tile):
+// s2 are this tile's scores (base 2, -inf for masked tokens). Updates m and l, writes the
+// weights p to prow[r * pstride] and returns each row's correction 2^(m_old - m_new) in corr.
+__device__ inline void softmax_step(const float (&s2)[4], float (&m)[4], float (&l)[4],
+                                    float (&corr)[4], float* prow, int pstride) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float mn = fmaxf(m[r], row16_max(s2[r]));
+    float p = 0.f;
+    corr[r] = 1.f;
+    if (mn != -INFINITY) {
+      corr[r] = exp2_hw(m[r] - mn);
+      p = exp2_hw(s2[r] - mn);
+    }
+    l[r] = l[r] * corr[r] + row16_sum(p);
+    m[r] = mn;
+    prow[r * pstride] = p;
+  }
+}
+
+// o[c][r] *= corr[r], skipped when no lane's running max moved (every corr is then exactly 1).
+template <int NC>
+__device__ inline void rescale_rows(f32x4 (&o)[NC], const float (&corr)[4]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[c][r] *= corr[r];
+}
+__device__ inline bool any_moved(const float (&corr)[4]) {
+  return __any(corr[0] != 1.f || corr[1] != 1.f || corr[2] != 1.f || corr[3] != 1.f);
 }
 
 
@@ -84,7 +136,7 @@ struct AParams {
   float* out;
   float* lse;
   int64_t pool_ts;
-  float scale;
+  float scale;                  // the call's scale times log2(e): scores in base-2 units
   int32_t n_queries, n_q, n_kv, group, page_size, page_shift, n_pages;
   int32_t seg;                // tokens per segment
 };
@@ -211,23 +263,11 @@ void attn_segment_kernel(AParams P) {
 #pragma unroll
     for (int k = 0; k < KS; ++k)
       *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = vraw[k];
+    float s2[4], corr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sc = row >= 0 ? sacc[r] * P.scale : -INFINITY;
-      const float mx = row16_max(sc);
-      const float mn = fmaxf(m[r], mx);
-      float corr = 1.f, p = 0.f;
-      if (mn != -INFINITY) {
-        corr = expf(m[r] - mn);
-        p = expf(sc - mn);
-      }
-      const float sum = row16_sum(p);
-      l[r] = l[r] * corr + sum;
-      m[r] = mn;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) o[c][r] *= corr;
-      pt[wave][(4 * grp + r) * PS + col] = p;
-    }
+    for (int r = 0; r < 4; ++r) s2[r] = row >= 0 ? sacc[r] * P.scale : -INFINITY;
+    softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PS + col], PS);
+    if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
     // O += P V: A[q][k] = P[q][4 k4 + k], B[k][f] = V[4 k4 + k][16 c + f]
 #pragma unroll
@@ -265,7 +305,7 @@ void attn_segment_kernel(AParams P) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
-    wgt[r] = M == -INFINITY ? 0.f : expf(m[r] - M);
+    wgt[r] = M == -INFINITY ? 0.f : exp2_hw(m[r] - M);
   }
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
@@ -288,11 +328,11 @@ void attn_segment_kernel(AParams P) {
     float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * expf(mrg_m[w][rw] - M);
+      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * exp2_hw(mrg_m[w][rw] - M);
     }
     const int64_t orow = (int64_t)g * P.n_q + h * P.group + rw;
     P.part_o[orow * D + f] = M == -INFINITY ? 0.f : mrg_o[rw * D + f] / L;
-    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M + logf(L);
+    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
   }
 }
 
@@ -413,26 +453,16 @@ void mla_segment_kernel(AParams P) {
     for (int k = 0; k < KSW; ++k)
       *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = lat[k];
     __syncthreads();
+    float s2[4], corr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int idx = (4 * grp + r) * PSTR + col;
       const float tot = ((sc[it & 1][0][idx] + sc[it & 1][1][idx]) + sc[it & 1][2][idx]) +
                         sc[it & 1][3][idx];
-      const float sv = row >= 0 ? tot * P.scale : -INFINITY;
-      const float mx = row16_max(sv);
-      const float mn = fmaxf(m[r], mx);
-      float corr = 1.f, p = 0.f;
-      if (mn != -INFINITY) {
-        corr = expf(m[r] - mn);
-        p = expf(sv - mn);
-      }
-      const float sum = row16_sum(p);
-      l[r] = l[r] * corr + sum;
-      m[r] = mn;
-#pragma unroll
-      for (int c = 0; c < NCW; ++c) o[c][r] *= corr;
-      pt[wave][(4 * grp + r) * PSTR + col] = p;
+      s2[r] = row >= 0 ? tot * P.scale : -INFINITY;
     }
+    softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PSTR + col], PSTR);
+    if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -463,7 +493,7 @@ void mla_segment_kernel(AParams P) {
 #pragma unroll
     for (int c = 0; c < NCW; ++c)
       P.part_o[orow * DL + f0 + 16 * c + col] = empty ? 0.f : o[c][r] / l[r];
-    if (wave == 0 && col == 0) P.part_lse[orow] = empty ? -INFINITY : m[r] + logf(l[r]);
+    if (wave == 0 && col == 0) P.part_lse[orow] = empty ? -INFINITY : m[r] * kLn2 + logf(l[r]);
   }
 }
 
@@ -613,7 +643,7 @@ struct VParams {
   const double* inv_freq;       // device (workspace) or NULL
   const uint8_t* pair_section;  // device (workspace) or NULL
   double theta;
-  float scale;
+  float scale;                  // the call's scale times log2(e): scores in base-2 units
   int32_t n_q, n_kv, group, rot_dim, layout;
 };
 
@@ -837,24 +867,13 @@ void chunk_attn_kernel(VParams P) {
 #pragma unroll
     for (int s2 = 0; s2 < PK; ++s2)
       *reinterpret_cast<u32x4*>(&vt[wave][col * VS + D + 32 * s2 + 8 * grp]) = cur.uv[s2];
+    float s2[4], corr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sc = valid ? sacc[r] * P.scale : -INFINITY;
-      const float mx = row16_max(sc);
-      const float mn = fmaxf(m[r], mx);
-      float corr = 1.f, p = 0.f;
-      if (mn != -INFINITY) {
-        corr = expf(m[r] - mn);
-        p = expf(sc - mn);
-      }
-      const float sum = row16_sum(p);
-      l[r] = l[r] * corr + sum;
-      m[r] = mn;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) o[c][r] *= corr;
-#pragma unroll
-      for (int c = 0; c < NZ; ++c) z[c][r] *= corr;
-      pt[wave][(4 * grp + r) * PSTR + col] = p;
+    for (int r = 0; r < 4; ++r) s2[r] = valid ? sacc[r] * P.scale : -INFINITY;
+    softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PSTR + col], PSTR);
+    if (any_moved(corr)) {
+      rescale_rows(o, corr);
+      rescale_rows(z, corr);
     }
     wave_lds_sync();
     // o += P V and z += P U_V: A[q][k] = P[q][4 k4 + k], B[k][f] = row 4 k4 + k of the tile
@@ -891,7 +910,7 @@ void chunk_attn_kernel(VParams P) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][rw]);
-    wgt[r] = M == -INFINITY ? 0.f : expf(m[r] - M);
+    wgt[r] = M == -INFINITY ? 0.f : exp2_hw(m[r] - M);
   }
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
@@ -923,13 +942,13 @@ void chunk_attn_kernel(VParams P) {
     float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * expf(mrg_m[w][rw] - M);
+      for (int w = 0; w < 4; ++w) L += mrg_l[w][rw] * exp2_hw(mrg_m[w][rw] - M);
     }
     float acc = mrg_o[rw * MW + f];
     for (int r = 0; r < mv; ++r) acc += mrg_o[rw * MW + D + r] * bf16_lo(stage[f * mv + r]);
     const int64_t orow = (int64_t)sidx * P.n_q + h * P.group + rw;
     P.part_o[orow * D + f] = M == -INFINITY ? 0.f : acc / L;
-    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M + logf(L);
+    if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
   }
 }
 
@@ -1148,7 +1167,8 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
   if (st != KAMERA_OK) return st;
   if (layer < 0 || layer >= model->n_layers)
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, model->n_layers);
-  if (!std::isfinite(scale)) return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!std::isfinite(scale) || !std::isfinite((float)((double)scale * 1.4426950408889634)))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite (also times log2(e))");
   if (n_queries > 0 && (!q || !out || !lse))
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "q, out and lse must not be NULL");
   if (q && !aligned16(q)) return fail(KAMERA_ERR_UNSUPPORTED, "q must be 16-byte aligned");
@@ -1194,7 +1214,7 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
   P.out = out;
   P.lse = lse;
   P.pool_ts = cache->token_stride;
-  P.scale = scale;
+  P.scale = (float)((double)scale * 1.4426950408889634);   // scores in base-2 units
   P.n_queries = n_queries;
   P.n_q = n_q_heads;
   P.n_kv = model->n_kv_heads;
@@ -1245,7 +1265,8 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
   if (st != KAMERA_OK) return st;
   if (layer < 0 || layer >= model->n_layers)
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, model->n_layers);
-  if (!std::isfinite(scale)) return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!std::isfinite(scale) || !std::isfinite((float)((double)scale * 1.4426950408889634)))
+    return fail(KAMERA_ERR_INVALID_ARGUMENT, "scale must be finite (also times log2(e))");
   if (n_queries > 0 && (!q || !out || !lse))
     return fail(KAMERA_ERR_INVALID_ARGUMENT, "q, out and lse must not be NULL");
   if (q && !aligned16(q)) return fail(KAMERA_ERR_UNSUPPORTED, "q must be 16-byte aligned");
@@ -1326,7 +1347,7 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
   P.inv_freq = model->inv_freq ? reinterpret_cast<const double*>(base + plan.freq_off) : nullptr;
   P.pair_section = model->pair_section ? base + plan.sec_off : nullptr;
   P.theta = model->rope_theta;
-  P.scale = scale;
+  P.scale = (float)((double)scale * 1.4426950408889634);   // scores in base-2 units
   P.n_q = n_q_heads;
   P.n_kv = model->n_kv_heads;
   P.group = n_q_heads / model->n_kv_heads;

@@ -83,6 +83,7 @@ def test_workspace_bytes():
     (dict(ranges=((0, -1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(ranges=((15990, 11),)), kb.KAMERA_ERR_INVALID_ARGUMENT),    # past 16000 tokens
     (dict(scale=math.inf), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(scale=3e38), kb.KAMERA_ERR_INVALID_ARGUMENT),     # times log2(e) overflows fp32
     (dict(q=None), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 20 * GiB + 2), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(lse=FAKE + 21 * GiB + 64), kb.KAMERA_ERR_OVERLAP),          # lse inside out
@@ -169,6 +170,7 @@ def test_chunk_attention_workspace_bytes_grow_with_segments():
     (dict(spans=((-1, 1),)), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(layer=4), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(scale=math.inf), kb.KAMERA_ERR_INVALID_ARGUMENT),
+    (dict(scale=3e38), kb.KAMERA_ERR_INVALID_ARGUMENT),     # times log2(e) overflows fp32
     (dict(q=None), kb.KAMERA_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 20 * GiB + 2), kb.KAMERA_ERR_UNSUPPORTED),
     (dict(out=FAKE + 20 * GiB), kb.KAMERA_ERR_OVERLAP),

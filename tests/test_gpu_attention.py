@@ -5,7 +5,8 @@ The cache is filled directly with seeded bf16 values (the attention reads whatev
 relocation wrote; its own inputs do not come from the HIP path here).
 
 Tolerance (derived): the scores' products are exact (bf16 x bf16) and summed in fp32 over D
-terms, so |ds_t| <= eps_s = 2 D 2^-24 max_t(scale sum_d |q_d k_td|) + 2^-24 max|s|; the
+terms, then scaled by fl(scale log2 e) (the kernels work in base 2: two roundings), so
+|ds_t| <= eps_s = 2 D 2^-24 max_t(scale sum_d |q_d k_td|) + 2 2^-24 max|s|; the
 softmax weights then carry a relative error <= 2 eps_s + c u (u = 2^-24, c = 64 + number of
 16-token tiles for the fp32 exp, running sums and the merges), so
     |o_g - o|_f <= (2 eps_s + c u) sum_t w_t |v_tf|,   |lse_g - lse| <= eps_s + c u (1 + |lse|).
@@ -85,7 +86,8 @@ def _expect(setup, layer, q64, start, n, n_q, scale):
         o[h * G:(h + 1) * G], lse[h * G:(h + 1) * G] = oh, lh
         if Kh.shape[0]:
             s = scale * qh @ Kh.T
-            eps = 2 * D * U * att.score_bounds(qh, Kh, scale).max(axis=1) + U * np.abs(s).max(axis=1)
+            eps = (2 * D * U * att.score_bounds(qh, Kh, scale).max(axis=1)
+                   + 2 * U * np.abs(s).max(axis=1))
             w = np.exp(s - s.max(axis=1, keepdims=True))
             w /= w.sum(axis=1, keepdims=True)
             otol[h * G:(h + 1) * G] = (2 * eps + c * U)[:, None] * (w @ np.abs(Vh))
@@ -333,7 +335,8 @@ def _run_mla(s, layer, ranges, n_q, scale, seed):
             assert np.all(out[j] == 0) and np.all(np.isneginf(lse[j])), f"query {j}: empty"
             continue
         sc = scale * q64[j] @ K.T
-        eps = 2 * (576 + 4) * U * att.score_bounds(q64[j], K, scale).max(axis=1) + U * np.abs(sc).max(axis=1)
+        eps = (2 * (576 + 4) * U * att.score_bounds(q64[j], K, scale).max(axis=1)
+               + 2 * U * np.abs(sc).max(axis=1))
         w = np.exp(sc - sc.max(axis=1, keepdims=True))
         w /= w.sum(axis=1, keepdims=True)
         c = 64 + -(-max(n, 1) // 16)

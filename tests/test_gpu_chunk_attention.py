@@ -4,7 +4,8 @@ the reuse operator defines them, attended exactly).
 
 Tolerance (derived): the query turned by -delta and w = V_K^T q are fp32 (rotation: two
 products and a sum; w: D products summed) and each is split into two bf16 terms, so every
-score term carries a relative error below 2^-15 + (D + m) 2^-24 < 2^-13 of its magnitude
+score term carries a relative error below 2^-15 + (D + m + 2) 2^-24 < 2^-13 (the last two
+roundings: the scale, times log2 e, for the kernel's base-2 scores) of its magnitude
 bound B_t = scale (sum_d |q~_d||k_td| + sum_r W~_r |U_K,tr|), with q~_d = |q_a| + |q_b| on a
 rotated pair and W~_r = sum_d |q_d||V_K,dr|. With eps = 2^-13 max_t B_t, the softmax weights
 carry a relative error below 2 eps + c u (u = 2^-24, c = 64 + tiles + m_V for the exp, running
