@@ -178,6 +178,46 @@ __device__ __forceinline__ int64_t row_at(const AParams& P, int64_t p, int32_t p
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
+// P V of one 16-token tile on bf16 MFMA (16x16x16) without rounding the fp32 weights: each
+// weight p is cut by truncation into hi (p with its low 16 bits cleared), mid (the same of
+// p - hi) and lo = p - hi - mid. Both subtractions are exact (Sterbenz) and lo keeps at most 8
+// significant bits, so hi + mid + lo = p exactly and each product with a bf16 value is exact in
+// fp32; the three terms are accumulated small first.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct PSplit {
+  s16x4 hi, mid, lo;
+};
+__device__ inline PSplit split_weights(const float* w4) {
+  PSplit s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hb = __float_as_uint(w4[j]) & 0xffff0000u;
+    const float r = w4[j] - __uint_as_float(hb);
+    const uint32_t mb = __float_as_uint(r) & 0xffff0000u;
+    const float r2 = r - __uint_as_float(mb);
+    s.hi[j] = (short)(hb >> 16);
+    s.mid[j] = (short)(mb >> 16);
+    s.lo[j] = (short)(__float_as_uint(r2) >> 16);
+  }
+  return s;
+}
+// o[c] += P V[:, 16 c ..] for c < n_blocks: lane (col, grp) holds the weights of query row col
+// for tokens 4 grp .. 4 grp + 3 (A operand) and reads V rows 4 grp + j, feature 16 c + col from
+// vcol = &V[4 grp][col] (bf16, row stride vs; B operand).
+template <int NC>
+__device__ inline void pv_accumulate(f32x4 (&o)[NC], const PSplit& w, const uint16_t* vcol, int vs,
+                                     int n_blocks = NC) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c >= n_blocks) continue;
+    const uint16_t* v = vcol + 16 * c;
+    const s16x4 b = s16x4{(short)v[0], (short)v[vs], (short)v[2 * vs], (short)v[3 * vs]};
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.lo, b, o[c], 0, 0, 0);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.mid, b, o[c], 0, 0, 0);
+    o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.hi, b, o[c], 0, 0, 0);
+  }
+}
+
 // Compiled for 3 waves per SIMD: 151 VGPRs at D = 128, no spills (the unconstrained choice,
 // 184 registers at 2 waves per SIMD, streamed ~12 % slower; 4 waves spill).
 template <int D>
@@ -269,16 +309,8 @@ void attn_segment_kernel(AParams P) {
     softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PS + col], PS);
     if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
-    // O += P V: A[q][k] = P[q][4 k4 + k], B[k][f] = V[4 k4 + k][16 c + f]
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float a = pt[wave][col * PS + 4 * k4 + grp];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float b = bf16_lo(vt[wave][(4 * k4 + grp) * VS + 16 * c + col]);
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o[c], 0, 0, 0);
-      }
-    }
+    // O += P V
+    pv_accumulate(o, split_weights(&pt[wave][col * PS + 4 * grp]), &vt[wave][4 * grp * VS + col], VS);
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
     row = row_next;
 #pragma unroll
@@ -347,14 +379,10 @@ void attn_segment_kernel(AParams P) {
 // ---------------------------------------------------------------------------------------
 
 constexpr int kMlaLatent = 512, kMlaRope = 64;
-#ifndef KAMERA_MLA_PREFETCH
-#define KAMERA_MLA_PREFETCH 1   // tiles whose rows are in flight ahead of the one computed
-#endif
-#ifndef KAMERA_MLA_WAVES_PER_EU
-#define KAMERA_MLA_WAVES_PER_EU 3
-#endif
+// Rows of masked tokens are read from here (zeros), so tile loads need no select.
+__device__ __align__(16) uint16_t kZeroRow[kMlaLatent + kMlaRope];
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KAMERA_MLA_WAVES_PER_EU, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void mla_segment_kernel(AParams P) {
   constexpr int DL = kMlaLatent, DQ = kMlaLatent + kMlaRope;
   constexpr int WS = DL / 4;          // latent features per wave
@@ -402,37 +430,21 @@ void mla_segment_kernel(AParams P) {
 #pragma unroll
   for (int c = 0; c < NCW; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // rows of the next tile are in flight while this one is computed
-  auto load_tile = [&](int64_t row, u32x4* lat, u32x4* rope) {
-#pragma unroll
-    for (int k = 0; k < KSW; ++k)
-      lat[k] = row >= 0 ? *reinterpret_cast<const u32x4*>(P.vpool + row + f0 + 32 * k + 8 * grp)
-                        : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < KSR; ++k)
-      rope[k] = row >= 0 && wave == 0
-                    ? *reinterpret_cast<const u32x4*>(P.kpool + row + 32 * k + 8 * grp)
-                    : u32x4{0u, 0u, 0u, 0u};
-  };
-  // rows of the next KAMERA_MLA_PREFETCH tiles are in flight (a ring of tile buffers)
-  constexpr int PF = KAMERA_MLA_PREFETCH;
   auto row_of = [&](int t0) -> int64_t {
     return t0 + col < t_hi ? row_at(P, t0 + col, page_entry(P, t0 + col, true)) : -1;
   };
-  int64_t rows[PF + 1];
-  u32x4 lat_r[PF + 1][KSW], rope_r[PF + 1][KSR];
+  // this wave's latent slice of token col's row (wave 0 also its k_rope)
+  auto load_tile = [&](int64_t row, u32x4 (&lat)[KSW], u32x4 (&rope)[KSR]) {
+    const uint16_t* lp = (row >= 0 ? P.vpool + row : kZeroRow) + f0 + 8 * grp;
 #pragma unroll
-  for (int k = 0; k < PF; ++k) {
-    rows[k] = row_of(t_lo + kTile * k);
-    load_tile(rows[k], lat_r[k], rope_r[k]);
-  }
-  int it = 0;
-  for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
-    rows[PF] = row_of(t0 + kTile * PF);
-    load_tile(rows[PF], lat_r[PF], rope_r[PF]);
-    const int64_t row = rows[0];
-    u32x4* lat = lat_r[0];
-    u32x4* rope = rope_r[0];
+    for (int k = 0; k < KSW; ++k) lat[k] = *reinterpret_cast<const u32x4*>(lp + 32 * k);
+    if (wave == 0) {
+      const uint16_t* rp = (row >= 0 ? P.kpool + row : kZeroRow) + 8 * grp;
+#pragma unroll
+      for (int k = 0; k < KSR; ++k) rope[k] = *reinterpret_cast<const u32x4*>(rp + 32 * k);
+    }
+  };
+  auto tile_step = [&](int64_t row, const u32x4 (&lat)[KSW], const u32x4 (&rope)[KSR], int it) {
     // this wave's part of S: lane holds query rows 4 grp + r of token col
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -464,24 +476,28 @@ void mla_segment_kernel(AParams P) {
     softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PSTR + col], PSTR);
     if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float a = pt[wave][col * PSTR + 4 * k4 + grp];
-#pragma unroll
-      for (int c = 0; c < NCW; ++c) {
-        const float b = bf16_lo(vt[wave][(4 * k4 + grp) * VS + 16 * c + col]);
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, o[c], 0, 0, 0);
-      }
-    }
+    pv_accumulate(o, split_weights(&pt[wave][col * PSTR + 4 * grp]), &vt[wave][4 * grp * VS + col],
+                  VS);
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+  };
+  // the rows of the next tile are in flight while one is computed. The k_rope registers of
+  // waves 1-3 are zero and stay zero: their k_rope MFMA sits under a wave-uniform branch that the
+  // compiler may issue with an empty exec mask, and the MFMA then still runs on its operands.
+  u32x4 lat[KSW], rope[KSR], lat_n[KSW], rope_n[KSR];
 #pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      rows[q] = rows[q + 1];
+  for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k] = u32x4{0u, 0u, 0u, 0u};
+  int64_t row = row_of(t_lo);
+  load_tile(row, lat, rope);
+  int it = 0;
+  for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
+    const int64_t row_n = row_of(t0 + kTile);
+    load_tile(row_n, lat_n, rope_n);
+    tile_step(row, lat, rope, it);
+    row = row_n;
 #pragma unroll
-      for (int k = 0; k < KSW; ++k) lat_r[q][k] = lat_r[q + 1][k];
+    for (int k = 0; k < KSW; ++k) lat[k] = lat_n[k];
 #pragma unroll
-      for (int k = 0; k < KSR; ++k) rope_r[q][k] = rope_r[q + 1][k];
-    }
+    for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k];
   }
   // every wave holds the same m and l: its own output features, normalised
 #pragma unroll
@@ -876,19 +892,12 @@ void chunk_attn_kernel(VParams P) {
       rescale_rows(z, corr);
     }
     wave_lds_sync();
-    // o += P V and z += P U_V: A[q][k] = P[q][4 k4 + k], B[k][f] = row 4 k4 + k of the tile
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float a = pt[wave][col * PSTR + 4 * k4 + grp];
-      const uint16_t* vr = &vt[wave][(4 * k4 + grp) * VS];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bf16_lo(vr[16 * c + col]), o[c], 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < NZ; ++c)
-        if (16 * c < mv)
-          z[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bf16_lo(vr[D + 16 * c + col]), z[c],
-                                                      0, 0, 0);
+    // o += P V and z += P U_V (the U_V rows follow the V rows of the tile)
+    {
+      const PSplit w = split_weights(&pt[wave][col * PSTR + 4 * grp]);
+      const uint16_t* vcol = &vt[wave][4 * grp * VS + col];
+      pv_accumulate(o, w, vcol, VS);
+      pv_accumulate(z, w, vcol + D, VS, (mv + 15) / 16);
     }
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
     cur = nxt;
