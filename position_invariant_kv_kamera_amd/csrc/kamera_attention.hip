@@ -430,9 +430,11 @@ void mla_segment_kernel(AParams P) {
 #pragma unroll
   for (int c = 0; c < NCW; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto row_of = [&](int t0) -> int64_t {
-    return t0 + col < t_hi ? row_at(P, t0 + col, page_entry(P, t0 + col, true)) : -1;
+  // row of token t0 + col from its page entry pe (-1 past the segment or masked)
+  auto row_of = [&](int t0, int32_t pe) -> int64_t {
+    return t0 + col < t_hi ? row_at(P, t0 + col, pe) : -1;
   };
+  auto entry_of = [&](int t0) { return page_entry(P, t0 + col, t0 + col < t_hi); };
   // this wave's latent slice of token col's row (wave 0 also its k_rope)
   auto load_tile = [&](int64_t row, u32x4 (&lat)[KSW], u32x4 (&rope)[KSR]) {
     const uint16_t* lp = (row >= 0 ? P.vpool + row : kZeroRow) + f0 + 8 * grp;
@@ -486,12 +488,15 @@ void mla_segment_kernel(AParams P) {
   u32x4 lat[KSW], rope[KSR], lat_n[KSW], rope_n[KSR];
 #pragma unroll
   for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k] = u32x4{0u, 0u, 0u, 0u};
-  int64_t row = row_of(t_lo);
+  // page-table entries are fetched one tile ahead of the rows they locate
+  int64_t row = row_of(t_lo, entry_of(t_lo));
+  int32_t pe_n = entry_of(t_lo + kTile);
   load_tile(row, lat, rope);
   int it = 0;
   for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
-    const int64_t row_n = row_of(t0 + kTile);
+    const int64_t row_n = row_of(t0 + kTile, pe_n);
     load_tile(row_n, lat_n, rope_n);
+    pe_n = entry_of(t0 + 2 * kTile);
     tile_step(row, lat, rope, it);
     row = row_n;
 #pragma unroll
