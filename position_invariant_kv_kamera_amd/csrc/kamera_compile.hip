@@ -35,6 +35,16 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Subspace iteration: Y = G X on fp32 MFMA (1) or fp32 VALU FMA (0); S = Y^T Y on fp64 MFMA
+// (1) or fp64 VALU FMA (0).
+#ifndef KAMERA_SUBSPACE_MFMA
+#define KAMERA_SUBSPACE_MFMA 1
+#endif
+#ifndef KAMERA_ORTH_MFMA
+#define KAMERA_ORTH_MFMA 1
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kStepTokens = 32;      // tokens of Delta staged in LDS per step
@@ -812,6 +822,38 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
                           int reseed_round) {
   constexpr int BS = MP + 4, SS = MP + 1;
   const int lane = threadIdx.x & 63;
+#if KAMERA_ORTH_MFMA
+  // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
+  // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
+  // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
+  // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
+  // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
+  // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
+  // all the factorisation reads.
+  {
+    const int li = lane & 15, kk = lane >> 4;
+    const int nt = (m + 15) / 16;
+    for (int ta = 0; ta < nt; ++ta) {
+      for (int tb = 0; tb <= ta; ++tb) {
+        f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
+        const float* ya = buf + kk * BS + 16 * ta + li;
+        const float* yb = buf + kk * BS + 16 * tb + li;
+        for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
+          const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
+          const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
+          s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
+        }
+        // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
+          if (row < m && col <= row) lm[row * SS + col] = s0[v] + s1[v];
+        }
+      }
+    }
+  }
+#else
   // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
   const int npair = m * (m + 1) / 2;
   for (int q = lane; q < npair; q += 64) {
@@ -828,6 +870,7 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
     }
     lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
+#endif
   wave_lds_sync();
   if constexpr (MP <= 32) {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
@@ -959,8 +1002,83 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
   wave_lds_sync();
 }
 
+#if KAMERA_SUBSPACE_MFMA
+// Y = G X for one head, in place in buf (rows of X become rows of Y), on
+// v_mfma_f32_16x16x4f32 in G's stored order: K runs over the stored columns kappa, and row
+// block rb of the output holds the stored rows 16 rb .. 16 rb + 15 of Y (feature q(rho) for
+// stored row rho; GP: G is stored in the symmetric permutation, q(rho) = 8 (rho % 16) +
+// rho / 16, else q is the identity). At step (t, u) lane 16 kk + i gives
+// A = G_stored[16 rb + i][kappa] and B = X[q(kappa)][16 cb + i], kappa = 16 t + 4 kk + u:
+// the round's B operands are read from LDS into registers once (X may then be overwritten by
+// Y), and one 16-byte load of a stored row feeds four steps; each piece of G is replaced by
+// the next row block's as soon as it is used, so those loads are in flight while the rest of
+// the block is multiplied. Even and odd t accumulate apart. D is a multiple of 32, at most 128.
+template <int MP, bool GP>
+__device__ __forceinline__ void gx_mfma(const float* G, float* buf, int D) {
+  constexpr int BS = MP + 4, NCB = MP / 16;
+  const int lane = threadIdx.x & 63;
+  const int nrb = D / 16;
+  const int li = lane & 15, kk = lane >> 4;
+  // q(16 t + 4 kk + u) = kbase + kstep(t, u)
+  const float* xb = buf + (GP ? 32 * kk : 4 * kk) * BS + li;
+  float bx[8][4][NCB];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ks = GP ? 8 * u + t : 16 * t + u;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) bx[t][u][cb] = t < nrb ? xb[ks * BS + 16 * cb] : 0.f;
+    }
+  wave_lds_sync();   // every lane has read X
+  const float* grow = G + (int64_t)li * D + 4 * kk;
+  f32x4 ga[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    ga[t] = t < nrb ? ((const CGLOBAL f32x4*)(grow + 16 * t))[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < nrb; ++rb) {
+    const int rn = rb + 1 < nrb ? rb + 1 : rb;   // past the end: reload (unused)
+    const float* gnext = grow + (int64_t)16 * rn * D;
+    f32x4 acc[2][NCB];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[e][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < nrb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            acc[t & 1][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[t][u], bx[t][u][cb],
+                                                                  acc[t & 1][cb], 0, 0, 0);
+        ga[t] = ((const CGLOBAL f32x4*)(gnext + 16 * t))[0];   // next row block's piece
+      }
+    }
+    // lane 16 kk + i holds stored rows 16 rb + 4 kk + v, columns 16 cb + i
+    float* yb = buf + (GP ? 8 * (4 * kk) * BS + rb * BS : (16 * rb + 4 * kk) * BS) + li;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        yb[(GP ? 8 * v : v) * BS + 16 * cb] = acc[0][cb][v] + acc[1][cb][v];
+  }
+  wave_lds_sync();
+}
+#endif
+
+// Waves per SIMD the subspace kernel is compiled for (MFMA form): a round's X operands, a row
+// block of G and the accumulators are live together.
+#if KAMERA_SUBSPACE_MFMA
+#define KAMERA_SUBSPACE_OCCUPANCY(MP) \
+  __attribute__((amdgpu_waves_per_eu((MP) <= 16 ? 3 : ((MP) <= 32 ? 2 : 1), 8)))
+#else
+#define KAMERA_SUBSPACE_OCCUPANCY(MP)
+#endif
+
 template <typename T, int MP, int WPB>
-__global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
+__global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspace_wave_kernel(CParams P) {
   constexpr int BS = MP + 4, SS = MP + 1;
   __shared__ __align__(16) float buf_s[WPB][128 * BS];
   __shared__ double lm_s[WPB][MP * SS];
@@ -1005,10 +1123,12 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
     G = gf;
   }
 
+#if !KAMERA_SUBSPACE_MFMA
   const int r0 = lane, r1 = lane + 64;
   const int c0 = r0 < D ? r0 : 0, c1 = r1 < D ? r1 : 0;
   // G stored permuted (gram_stream_kernel): element (k, c) at (p(k), p(c))
   const int gp0 = J.gperm ? gperm_row(c0) : c0, gp1 = J.gperm ? gperm_row(c1) : c1;
+#endif
   for (int h = 0; h < 2; ++h) {
     const int r = lane + 64 * h;
     if (r >= D) continue;
@@ -1018,6 +1138,10 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
   wave_lds_sync();
 
   for (int round = 0; round < P.n_iter; ++round) {
+#if KAMERA_SUBSPACE_MFMA
+    if (J.gperm) gx_mfma<MP, true>(G, buf, D);
+    else gx_mfma<MP, false>(G, buf, D);
+#else
     // Y = G X for rows r0, r1. G is symmetric, so each lane reads its own rows of G along
     // their stored order with 16-byte loads (stored column kappa is feature k = q(kappa)),
     // keeping the next 16 columns in flight while it uses the current ones.
@@ -1075,6 +1199,7 @@ __global__ __launch_bounds__(64 * WPB) void subspace_wave_kernel(CParams P) {
         row[q] = make_float4(y1[4 * q], y1[4 * q + 1], y1[4 * q + 2], y1[4 * q + 3]);
     }
     wave_lds_sync();
+#endif
     orth_wave<MP>(buf, lm, inv, dead, D, m, round);
   }
   // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
