@@ -540,7 +540,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
             lines.append(f"| project (U = Delta V) | {n} | {per_call_us:.1f} | hbm | "
                          f"{gbps:.0f} GB/s | {gbps / HBM_PEAK_GBPS:.3f} |")
         else:
-            lines.append(f"| subspace iteration | {n} | {per_call_us:.1f} | latency | - | - |")
+            lines.append(f"| subspace iteration | {n} | {per_call_us:.1f} | issue (MFMA products, fp64 factorisation chains) | - | - |")
     lines += ["", "Gram flops per call: n D (D + 1) per head (the distinct entries of the "
               "symmetric product) = "
               f"{gram_f / 1e9:.1f} GFLOP; projection bytes per call: both inputs once = "

@@ -448,10 +448,6 @@ void gram_stream_kernel(CParams P) {
   const int w_lo = t_lo + wave * q4, w_hi = min(t_hi, w_lo + q4);
   const int nsteps = w_hi > w_lo ? (w_hi - w_lo + 3) / 4 : 0;
 
-  if (J.rotate) {
-    fill_phases(cs, J, P);
-    __syncthreads();
-  }
   // this lane's piece of the row: features 8n .. 8n + 7; its RoPE role
   const int R = J.rotate ? J.rot_dim : 0;
   const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
@@ -494,6 +490,11 @@ void gram_stream_kernel(CParams P) {
   };
 #pragma unroll
   for (int k = 0; k < kGramPrefetch; ++k) load_step(k, px[k], pc[k]);
+  // the phase table after the first loads, so their latency overlaps it
+  if (J.rotate) {
+    fill_phases(cs, J, P);
+    __syncthreads();
+  }
 
   f32x4 acc[36];
 #pragma unroll
@@ -1337,17 +1338,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int SV = stream_sv(W, mp);
   const int nrb = mp / 16;
 
-  if (J.rotate) fill_phases(cs, J, P);
-  const float* xg = P.ws + J.xbase + (int64_t)unit * W * mp;
-  for (int idx = tid; idx < W * mp; idx += kThreads) {
-    const int k = idx / mp, r = idx - k * mp;
-    const int sg = k >> 2, gg = k & 3;
-    const int c = sg / (8 * S), within = sg - c * 8 * S;
-    const int f = 8 * stream_piece(gg, within >> 3, c, S, unit_layout, hp) + (within & 7);
-    vs[k * SV + r] = xg[(int64_t)f * mp + r];
-  }
-  __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   // this lane's slots: feature offset, and for a rotated head the role (0 pass-through,
   // 1 first member of a half-split pair, 2 second member, 3 interleaved pairs), the first
@@ -1408,9 +1398,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     }
   };
 
+  // the first unit's loads go out before the block's set-up (phase table, X in LDS), so
+  // their latency overlaps it
   Buf cur, nxt;
   f32x4 acc[4];
   if (total > 0) load_unit(0, cur);
+
+  if (J.rotate) fill_phases(cs, J, P);
+  const float* xg = P.ws + J.xbase + (int64_t)unit * W * mp;
+  for (int idx = tid; idx < W * mp; idx += kThreads) {
+    const int k = idx / mp, r = idx - k * mp;
+    const int sg = k >> 2, gg = k & 3;
+    const int c = sg / (8 * S), within = sg - c * 8 * S;
+    const int f = 8 * stream_piece(gg, within >> 3, c, S, unit_layout, hp) + (within & 7);
+    vs[k * SV + r] = xg[(int64_t)f * mp + r];
+  }
+  __syncthreads();
+
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) load_unit(u + 1, nxt);
     const int it = u / nslab, c = u - it * nslab;
