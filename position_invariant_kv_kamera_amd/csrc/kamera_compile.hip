@@ -608,271 +608,13 @@ __device__ __forceinline__ float seed_value(int i, int j, int round) {
   return (h & 1u) ? 1.f : -1.f;
 }
 
-// X = orth(Y), a Cholesky QR in fp64: S = Y^T Y (fp32 products are exact in fp64), L L^T = S
-// (left-looking, lane i of wave 0 owns row i), L^-1 (lane j owns column j), then
-// X = Y L^-T with fp64 accumulation, so nothing is rounded before the final fp32 store.
-// Collapsed columns (pivot^2 <= kDeadTol * S_jj) give x_j = 0, or a fresh +-1 column when
-// reseed_round >= 0 (the next round's G X spreads it).
-template <int MMAX>
-__device__ void orth(const float* ys, float* xs, double* ss, double* li, double* inv, int* dead,
-                     int D, int m, int mp, int reseed_round) {
-  constexpr int SS = MMAX + 1;   // padded row stride of S, L and L^-1 (doubles)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int YS = D + 1;
-  const int npair = m * (m + 1) / 2;
-  for (int q = tid; q < npair; q += kThreads) {
-    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
-    while (a * (a + 1) / 2 > q) --a;
-    while ((a + 1) * (a + 2) / 2 <= q) ++a;
-    const int b = q - a * (a + 1) / 2;
-    const float* ya = ys + a * YS;
-    const float* yb = ys + b * YS;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
-#pragma unroll 2
-    for (int i = 0; i < D; i += 4) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += (double)ya[i + k] * (double)yb[i + k];
-    }
-    ss[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);   // lower triangle, a >= b
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int i = lane;
-    for (int j = 0; j < m; ++j) {
-      double dot = 0.0;
-      if (i >= j && i < m)
-        for (int a = 0; a < j; ++a) dot += ss[i * SS + a] * ss[j * SS + a];
-      if (i == j) {
-        const double sjj = ss[j * SS + j];
-        const double d = sjj - dot;
-        const bool dk = d <= kDeadTol * sjj;
-        const double ljj = dk ? 0.0 : sqrt(d);
-        ss[j * SS + j] = ljj;
-        inv[j] = dk ? 0.0 : 1.0 / ljj;
-        dead[j] = dk ? 1 : 0;
-      }
-      wave_lds_sync();
-      if (i > j && i < m) ss[i * SS + j] = (ss[i * SS + j] - dot) * inv[j];
-      wave_lds_sync();
-    }
-    // L^-1: lane j solves L z = e_j; rows >= m and the strict upper triangle are zero
-    if (i < mp) {
-      const int j = i;
-      for (int r = 0; r < mp; ++r) li[r * SS + j] = 0.0;
-      if (j < m) {
-        li[j * SS + j] = inv[j];
-        for (int r = j + 1; r < m; ++r) {
-          double acc = 0.0;
-          for (int a = j; a < r; ++a) acc += ss[r * SS + a] * li[a * SS + j];
-          li[r * SS + j] = -acc * inv[r];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // X = Y L^-T: x[i][j] = sum_{a <= j} y[i][a] * li[j][a]
-  const int groups = (m + 15) / 16;
-  for (int u = tid; u < D * groups; u += kThreads) {
-    const int i = u % D, jg = u / D;
-    double acc[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = 0.0;
-    const int a_end = min(m, 16 * jg + 16);
-#pragma unroll 2
-    for (int a = 0; a < a_end; ++a) {
-      const double y = (double)ys[a * YS + i];
-      const double* lr = li + (16 * jg) * SS + a;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc[c] += y * lr[c * SS];
-    }
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int j = 16 * jg + c;
-      if (j < m) {
-        float v = (float)acc[c];
-        if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
-        xs[i * mp + j] = v;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-template <typename T, int DMAX, int MMAX>
-__global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
-  __shared__ __align__(16) float xs[DMAX * MMAX];
-  __shared__ float ys[MMAX * (DMAX + 1)];
-  __shared__ double ss[MMAX * (MMAX + 1)];
-  __shared__ double li[MMAX * (MMAX + 1)];
-  __shared__ double inv[MMAX];
-  __shared__ int dead[MMAX];
-
-  const int e = find_entry(P, blockIdx.x);
-  const CJob& J = P.jobs[P.job_of[e]];
-  const int unit = blockIdx.x - P.starts[e];
-  const int layer = unit / J.heads, head = unit - layer * J.heads;
-  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
-
-  // G: the single partial, or the sum of the partial tiles assembled in the workspace
-  const float* G;
-  if (J.gfull < 0) {
-    G = P.ws + J.gpart + (int64_t)unit * D * D;
-  } else {
-    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
-    const int te = J.te, te2 = te * te;
-    for (int pair = 0; pair < J.n_pairs; ++pair) {
-      int bi, bj;
-      pair_tiles(pair, J.nb, &bi, &bj);
-      const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
-      const float4* part4 = reinterpret_cast<const float4*>(part);
-#pragma unroll 4
-      for (int i4 = tid; i4 < te2 / 4; i4 += kThreads) {
-        float4 v = part4[i4];
-#pragma unroll 4
-        for (int s = 1; s < J.splits; ++s) {
-          const float4 w = part4[(int64_t)s * (te2 / 4) + i4];
-          v.x += w.x;
-          v.y += w.y;
-          v.z += w.z;
-          v.w += w.w;
-        }
-        const int ii = (4 * i4) / te, jj = 4 * i4 - ii * te;
-        *reinterpret_cast<float4*>(gf + (bi * te + ii) * D + bj * te + jj) = v;
-        if (bi != bj) {
-          const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) gf[(bj * te + jj + c) * D + bi * te + ii] = vv[c];
-        }
-      }
-    }
-    __syncthreads();
-    G = gf;
-  }
-
-  for (int idx = tid; idx < D * mp; idx += kThreads) {
-    const int i = idx / mp, j = idx - i * mp;
-    xs[idx] = j < m ? seed_value(i, j, 0) : 0.f;
-  }
-
-  const int YS = D + 1;
-  const int groups = mp / 16;
-  __syncthreads();
-
-  for (int round = 0; round < P.n_iter; ++round) {
-    // Y = G X (G symmetric: column i read as row i)
-    for (int u = tid; u < D * groups; u += kThreads) {
-      const int i = u % D, cg = u / D;
-      float acc[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc[c] = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < D; ++k) {
-        const float g = G[(int64_t)k * D + i];
-        const float4* xr = reinterpret_cast<const float4*>(xs + k * mp + 16 * cg);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 x = xr[q];
-          acc[4 * q] += g * x.x;
-          acc[4 * q + 1] += g * x.y;
-          acc[4 * q + 2] += g * x.z;
-          acc[4 * q + 3] += g * x.w;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 16; ++c) ys[(16 * cg + c) * YS + i] = acc[c];
-    }
-    __syncthreads();
-    orth<MMAX>(ys, xs, ss, li, inv, dead, D, m, mp, round);
-  }
-  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
-  for (int idx = tid; idx < D * m; idx += kThreads) {
-    const int i = idx / m, j = idx - i * m;
-    ys[j * YS + i] = xs[i * mp + j];
-  }
-  __syncthreads();
-  orth<MMAX>(ys, xs, ss, li, inv, dead, D, m, mp, -1);
-
-  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
-  float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
-  for (int idx = tid; idx < D * mp; idx += kThreads) {
-    const int i = idx / mp, j = idx - i * mp;
-    const float v = xs[idx];
-    xg[idx] = v;
-    if (j < m) store_elem(V + i * m + j, v);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
-// wave-synchronous. MP = mp exactly. Per wave in LDS:
-//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
-//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
-//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
-//       inv holds 1 / diag(L) (0 for a collapsed column).
-// Lane l owns rows l and l + 64.
-// ---------------------------------------------------------------------------------------
-
-__device__ __forceinline__ void wave_global_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
+// Cholesky factor of S in place, by one wave (wave-synchronous): lm holds S's lower triangle
+// (row stride MP + 1, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
+// (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
-__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
-                          int reseed_round) {
-  constexpr int BS = MP + 4, SS = MP + 1;
+__device__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
+  constexpr int SS = MP + 1;
   const int lane = threadIdx.x & 63;
-#if KAMERA_ORTH_MFMA
-  // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
-  // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
-  // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
-  // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
-  // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
-  // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
-  // all the factorisation reads.
-  {
-    const int li = lane & 15, kk = lane >> 4;
-    const int nt = (m + 15) / 16;
-    for (int ta = 0; ta < nt; ++ta) {
-      for (int tb = 0; tb <= ta; ++tb) {
-        f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
-        const float* ya = buf + kk * BS + 16 * ta + li;
-        const float* yb = buf + kk * BS + 16 * tb + li;
-        for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
-          const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
-          const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
-          s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
-        }
-        // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-          if (row < m && col <= row) lm[row * SS + col] = s0[v] + s1[v];
-        }
-      }
-    }
-  }
-#else
-  // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
-  const int npair = m * (m + 1) / 2;
-  for (int q = lane; q < npair; q += 64) {
-    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
-    while (a * (a + 1) / 2 > q) --a;
-    while ((a + 1) * (a + 2) / 2 <= q) ++a;
-    const int b = q - a * (a + 1) / 2;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
-#pragma unroll 2
-    for (int r = 0; r < D; r += 4) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
-    }
-    lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
-#endif
-  wave_lds_sync();
   if constexpr (MP <= 32) {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
     // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
@@ -962,6 +704,293 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
         for (int k = j + 1; k <= i; ++k) lm[i * SS + k] -= lij * lm[k * SS + j];
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// subspace (wide heads, 256 .. 512 features: the MLA latent): one block of 4 waves per unit.
+// LDS: xs [D][mp+1] fp32 X (odd row stride: a thread's own row is conflict-free), ys [mp][D+1]
+// fp32 Y (transposed), ss [MMAX][MMAX+1] fp64 S and then L.
+//   Y = G X    fp32 MFMA 16x16x4, wave w takes row blocks w, w + 4, ... (G read from the
+//              workspace, 16 bytes of a row per lane per K block, next block in flight);
+//   S = Y^T Y  fp64 MFMA 16x16x4 over all D rows, the lower tiles dealt to the waves;
+//   L L^T = S  by wave 0 (cholesky_wave);
+//   X = Y L^-T forward substitution, one row per thread at a time, the row's x in registers
+//              (fp64 sums of the fp32 x already formed, as in the per-wave form).
+// ---------------------------------------------------------------------------------------
+
+template <int MMAX>
+__device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D, int mp) {
+  constexpr int NCB = MMAX / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kk = lane >> 4;
+  const int nrb = D / 16;   // at most 32: 8 row blocks per wave
+  const int nt = D / 16;
+  const int XS = mp + 1, YS = D + 1;
+  f32x4 acc[8][NCB];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[s][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A = G[16 rb + i][kappa], kappa = 16 t + 4 kk + u; B = X[kappa][16 cb + i]
+  const float* grow = G + (int64_t)li * D + 4 * kk;
+  f32x4 ga[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int rb = wave + 4 * s;
+    ga[s] = rb < nrb ? ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D))[0]
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int t = 0; t < nt; ++t) {
+    const int tn = t + 1 < nt ? t + 1 : t;   // past the end: reload (unused)
+    float bv[4][NCB];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        bv[u][cb] = 16 * cb < mp ? xs[(16 * t + 4 * kk + u) * XS + 16 * cb + li] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int rb = wave + 4 * s;
+      if (rb < nrb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            acc[s][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[s][u], bv[u][cb], acc[s][cb], 0, 0, 0);
+        ga[s] = ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D + 16 * tn))[0];
+      }
+    }
+  }
+  // lane 16 kk + i holds rows 16 rb + 4 kk + v, columns 16 cb + i
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int rb = wave + 4 * s;
+    if (rb < nrb) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        if (16 * cb < mp)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ys[(16 * cb + li) * YS + 16 * rb + 4 * kk + v] = acc[s][cb][v];
+    }
+  }
+}
+
+// X = orth(Y) (Cholesky QR, fp64). Collapsed columns give x_j = 0, or a fresh +-1 column when
+// reseed_round >= 0 (the next round's G X spreads it); a collapsed column has l_aj = 0 below
+// its pivot, so a reseeded x_a adds nothing to the columns after it.
+template <int MMAX>
+__device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, int* dead, int D,
+                           int m, int mp, int reseed_round) {
+  constexpr int SS = MMAX + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int XS = mp + 1, YS = D + 1;
+  {
+    // S = Y^T Y: tile (a, b), a >= b, on v_mfma_f64_16x16x4f64; lane 16k + i takes
+    // Y[r + k][16 a + i] and Y[r + k][16 b + i]; its output register v is row 16 a + k + 4v,
+    // column 16 b + i. Two accumulators over alternate groups of four rows.
+    const int li = lane & 15, kk = lane >> 4;
+    const int nt = (m + 15) / 16;
+    const int ntiles = nt * (nt + 1) / 2;
+    for (int q = wave; q < ntiles; q += kThreads / 64) {
+      int ta = 0;
+      while ((ta + 1) * (ta + 2) / 2 <= q) ++ta;
+      const int tb = q - ta * (ta + 1) / 2;
+      const float* ya = ys + (16 * ta + li) * YS + kk;
+      const float* yb = ys + (16 * tb + li) * YS + kk;
+      f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
+      for (int r = 0; r < D; r += 8) {   // D is a multiple of 128
+        s0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r], (double)yb[r], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r + 4], (double)yb[r + 4], s1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
+        if (row < m && col <= row) ss[row * SS + col] = s0[v] + s1[v];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m);
+  __syncthreads();
+  // X = Y L^-T: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj
+  for (int i = tid; i < D; i += kThreads) {
+    float xv[MMAX];
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j) {
+      xv[j] = 0.f;
+      if (j < m) {
+        const double* lj = ss + j * SS;
+        double p0 = 0.0, p1 = 0.0;
+#pragma unroll
+        for (int a = 0; a < j; ++a) {
+          if (a & 1) p1 += (double)xv[a] * lj[a];
+          else p0 += (double)xv[a] * lj[a];
+        }
+        float v = (float)(((double)ys[j * YS + i] - (p0 + p1)) * inv[j]);
+        if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
+        xv[j] = v;
+      }
+    }
+    float* xr = xs + i * XS;
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j)
+      if (j < mp) xr[j] = xv[j];
+  }
+  __syncthreads();
+}
+
+template <typename T, int DMAX, int MMAX>
+__global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
+  __shared__ __align__(16) float xs[DMAX * (MMAX + 1)];
+  __shared__ float ys[MMAX * (DMAX + 1)];
+  __shared__ double ss[MMAX * (MMAX + 1)];
+  __shared__ double inv[MMAX];
+  __shared__ int dead[MMAX];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int unit = blockIdx.x - P.starts[e];
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
+  const int XS = mp + 1, YS = D + 1;
+
+  // G: the single partial, or the sum of the partial tiles assembled in the workspace
+  const float* G;
+  if (J.gfull < 0) {
+    G = P.ws + J.gpart + (int64_t)unit * D * D;
+  } else {
+    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
+    const int te = J.te, te2 = te * te;
+    for (int pair = 0; pair < J.n_pairs; ++pair) {
+      int bi, bj;
+      pair_tiles(pair, J.nb, &bi, &bj);
+      const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
+      const float4* part4 = reinterpret_cast<const float4*>(part);
+#pragma unroll 4
+      for (int i4 = tid; i4 < te2 / 4; i4 += kThreads) {
+        float4 v = part4[i4];
+#pragma unroll 4
+        for (int s = 1; s < J.splits; ++s) {
+          const float4 w = part4[(int64_t)s * (te2 / 4) + i4];
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        const int ii = (4 * i4) / te, jj = 4 * i4 - ii * te;
+        *reinterpret_cast<float4*>(gf + (bi * te + ii) * D + bj * te + jj) = v;
+        if (bi != bj) {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) gf[(bj * te + jj + c) * D + bi * te + ii] = vv[c];
+        }
+      }
+    }
+    __syncthreads();
+    G = gf;
+  }
+
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int i = idx / mp, j = idx - i * mp;
+    xs[i * XS + j] = j < m ? seed_value(i, j, 0) : 0.f;
+  }
+  __syncthreads();
+
+  for (int round = 0; round < P.n_iter; ++round) {
+    gx_mfma_block<MMAX>(G, xs, ys, D, mp);
+    __syncthreads();
+    orth_block<MMAX>(ys, xs, ss, inv, dead, D, m, mp, round);
+  }
+  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
+  for (int idx = tid; idx < D * m; idx += kThreads) {
+    const int i = idx / m, j = idx - i * m;
+    ys[j * YS + i] = xs[i * XS + j];
+  }
+  __syncthreads();
+  orth_block<MMAX>(ys, xs, ss, inv, dead, D, m, mp, -1);
+
+  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
+  float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int i = idx / mp, j = idx - i * mp;
+    const float v = xs[i * XS + j];
+    xg[idx] = v;
+    if (j < m) store_elem(V + i * m + j, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
+// wave-synchronous. MP = mp exactly. Per wave in LDS:
+//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
+//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
+//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
+//       inv holds 1 / diag(L) (0 for a collapsed column).
+// Lane l owns rows l and l + 64.
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void wave_global_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int MP>
+__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
+                          int reseed_round) {
+  constexpr int BS = MP + 4, SS = MP + 1;
+  const int lane = threadIdx.x & 63;
+#if KAMERA_ORTH_MFMA
+  // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
+  // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
+  // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
+  // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
+  // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
+  // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
+  // all the factorisation reads.
+  {
+    const int li = lane & 15, kk = lane >> 4;
+    const int nt = (m + 15) / 16;
+    for (int ta = 0; ta < nt; ++ta) {
+      for (int tb = 0; tb <= ta; ++tb) {
+        f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
+        const float* ya = buf + kk * BS + 16 * ta + li;
+        const float* yb = buf + kk * BS + 16 * tb + li;
+        for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
+          const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
+          const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
+          s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
+        }
+        // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
+          if (row < m && col <= row) lm[row * SS + col] = s0[v] + s1[v];
+        }
+      }
+    }
+  }
+#else
+  // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
+  const int npair = m * (m + 1) / 2;
+  for (int q = lane; q < npair; q += 64) {
+    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
+    while (a * (a + 1) / 2 > q) --a;
+    while ((a + 1) * (a + 2) / 2 <= q) ++a;
+    const int b = q - a * (a + 1) / 2;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
+#pragma unroll 2
+    for (int r = 0; r < D; r += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
+    }
+    lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+#endif
+  wave_lds_sync();
+  cholesky_wave<MP>(lm, inv, dead, m);
   wave_lds_sync();
   // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
   // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
