@@ -276,6 +276,36 @@ __device__ void stage_delta(const CJob& J, const CParams& P, const float2* cs, i
   }
 }
 
+#define CGLOBAL __attribute__((address_space(1)))
+
+// Eight consecutive features of a row, as loaded (16 bytes per bf16 piece).
+template <typename T>
+struct Piece {
+  u32x4 w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_piece(const T* p, Piece<T>& o) {
+  const CGLOBAL u32x4* q = (const CGLOBAL u32x4*)p;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) o.w[k] = q[k];
+}
+
+__device__ __forceinline__ void piece_floats(const Piece<uint16_t>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(a.w[0][k] << 16);
+    o[2 * k + 1] = __uint_as_float(a.w[0][k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void piece_floats(const Piece<float>& a, float* o) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = __uint_as_float(a.w[0][k]);
+    o[4 + k] = __uint_as_float(a.w[1][k]);
+  }
+}
+
 // Tile pair index -> (bi, bj), bi <= bj, row-major over the upper triangle of nb x nb tiles.
 __device__ __forceinline__ void pair_tiles(int pair, int nb, int* bi, int* bj) {
   int p = pair;
@@ -332,12 +362,7 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
-    __syncthreads();
-    stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
-    if (bi != bj)
-      stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
-    __syncthreads();
+  auto mfma_step = [&]() {
 #pragma unroll 2
     for (int kk = 0; kk < kStepTokens / 4; ++kk) {
       const int row = (kk * 4 + (lane >> 4)) * DS + (lane & 15);
@@ -353,6 +378,74 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
         for (int y = 0; y < NB; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
     }
+  };
+
+  bool done = false;
+  if constexpr (NB == 4) {
+    if (!J.rotate && J.n_members == 1) {
+      // Unrotated head, one ordering (the MLA latent): Delta = conditioned - canonical needs
+      // no phase table, so the next step's rows are loaded into registers while this step's
+      // MFMAs run. Thread item k < 2 of a tile: row (tid + 256 k) / 16 of the step, features
+      // 8 ((tid + 256 k) % 16) .. + 7 of the tile.
+      const int64_t head_off = (int64_t)head * J.width;
+      const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off;
+      const CMember& m0 = P.members[J.member_off];
+      const T* cond = static_cast<const T*>(m0.cond) + layer * m0.cond_ls + head_off;
+      const int ntile = bi == bj ? 1 : 2;
+      Piece<T> px[2][2], pc[2][2];
+      auto load_rows = [&](int tok0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int g = threadIdx.x + kThreads * k;
+            const int tok = tok0 + (g >> 4);
+            const int col = (tt ? bj : bi) * TE + 8 * (g & 15);
+            if (tt < ntile && tok < t_hi) {
+              load_piece(canon + (int64_t)tok * J.canon_ts + col, px[tt][k]);
+              load_piece(cond + (int64_t)tok * m0.cond_ts + col, pc[tt][k]);
+            } else {
+#pragma unroll
+              for (int w = 0; w < (int)(sizeof(T) / 2); ++w) {
+                px[tt][k].w[w] = u32x4{0u, 0u, 0u, 0u};
+                pc[tt][k].w[w] = u32x4{0u, 0u, 0u, 0u};
+              }
+            }
+          }
+      };
+      if (t_lo < t_hi) load_rows(t_lo);
+      for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+        __syncthreads();   // the previous step's MFMAs are done with di / dj
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            if (tt < ntile) {
+              const int g = threadIdx.x + kThreads * k;
+              float x[8], c[8];
+              piece_floats(px[tt][k], x);
+              piece_floats(pc[tt][k], c);
+              float* d = (tt ? dj : di) + (g >> 4) * DS + 8 * (g & 15);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+            }
+          }
+        __syncthreads();
+        if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
+        mfma_step();
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+      __syncthreads();
+      stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bi * TE, TE, di, DS);
+      if (bi != bj)
+        stage_delta<T, kStepTokens>(J, P, cs, layer, head, tok0, t_hi, bj * TE, TE, dj, DS);
+      __syncthreads();
+      mfma_step();
+    }
   }
 
   float* out = P.ws + J.gpart +
@@ -365,8 +458,6 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
       for (int i = 0; i < 4; ++i)
         out[(r0 + 16 * x + 4 * (lane >> 4) + i) * TE + c0 + 16 * y + (lane & 15)] = acc[x][y][i];
 }
-
-#define CGLOBAL __attribute__((address_space(1)))
 
 // Piece (8 features) held by lane group g in slot p of slab c.
 __host__ __device__ inline int stream_piece(int g, int p, int c, int S, int unit_layout, int hp) {
@@ -381,33 +472,6 @@ __host__ __device__ inline int stream_piece(int g, int p, int c, int S, int unit
 __host__ __device__ inline int stream_sv(int width, int mp) {
   if (width > 128) return mp;
   return mp == 16 ? 16 : (mp == 64 ? 80 : 48);
-}
-
-template <typename T>
-struct Piece {
-  u32x4 w[sizeof(T) / 2];
-};
-
-template <typename T>
-__device__ __forceinline__ void load_piece(const T* p, Piece<T>& o) {
-  const CGLOBAL u32x4* q = (const CGLOBAL u32x4*)p;
-#pragma unroll
-  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) o.w[k] = q[k];
-}
-
-__device__ __forceinline__ void piece_floats(const Piece<uint16_t>& a, float* o) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[2 * k] = __uint_as_float(a.w[0][k] << 16);
-    o[2 * k + 1] = __uint_as_float(a.w[0][k] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void piece_floats(const Piece<float>& a, float* o) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[k] = __uint_as_float(a.w[0][k]);
-    o[4 + k] = __uint_as_float(a.w[1][k]);
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -748,17 +812,19 @@ __device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D,
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         bv[u][cb] = 16 * cb < mp ? xs[(16 * t + 4 * kk + u) * XS + 16 * cb + li] : 0.f;
+    // consecutive MFMAs go to different accumulators (row blocks), so none waits on the last
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int rb = wave + 4 * s;
-      if (rb < nrb) {
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+      for (int s = 0; s < 8; ++s)
+        if (wave + 4 * s < nrb)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
             acc[s][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[s][u], bv[u][cb], acc[s][cb], 0, 0, 0);
-        ga[s] = ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D + 16 * tn))[0];
-      }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int rb = wave + 4 * s;
+      if (rb < nrb) ga[s] = ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D + 16 * tn))[0];
     }
   }
   // lane 16 kk + i holds rows 16 rb + 4 kk + v, columns 16 cb + i
@@ -787,7 +853,7 @@ __device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, 
   {
     // S = Y^T Y: tile (a, b), a >= b, on v_mfma_f64_16x16x4f64; lane 16k + i takes
     // Y[r + k][16 a + i] and Y[r + k][16 b + i]; its output register v is row 16 a + k + 4v,
-    // column 16 b + i. Two accumulators over alternate groups of four rows.
+    // column 16 b + i. Four accumulators over rotating groups of four rows.
     const int li = lane & 15, kk = lane >> 4;
     const int nt = (m + 15) / 16;
     const int ntiles = nt * (nt + 1) / 2;
@@ -797,15 +863,19 @@ __device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, 
       const int tb = q - ta * (ta + 1) / 2;
       const float* ya = ys + (16 * ta + li) * YS + kk;
       const float* yb = ys + (16 * tb + li) * YS + kk;
-      f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
-      for (int r = 0; r < D; r += 8) {   // D is a multiple of 128
-        s0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r], (double)yb[r], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r + 4], (double)yb[r + 4], s1, 0, 0, 0);
+      f64x4 sa[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sa[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int r = 0; r < D; r += 16) {   // D is a multiple of 128
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sa[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r + 4 * c], (double)yb[r + 4 * c],
+                                                       sa[c], 0, 0, 0);
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-        if (row < m && col <= row) ss[row * SS + col] = s0[v] + s1[v];
+        if (row < m && col <= row) ss[row * SS + col] = (sa[0][v] + sa[1][v]) + (sa[2][v] + sa[3][v]);
       }
     }
   }
