@@ -672,8 +672,18 @@ __device__ __forceinline__ float seed_value(int i, int j, int round) {
   return (h & 1u) ? 1.f : -1.f;
 }
 
+// Storage of S and L (lower triangle, fp64) for one unit of rank class MP: square with row
+// stride MP + 1 up to MP = 32 (the register Cholesky uses the strict upper part of row 0 as
+// scratch), packed by rows above (half the LDS, so more units fit on a CU).
+template <int MP>
+__host__ __device__ constexpr int lm_size() { return MP <= 32 ? MP * (MP + 1) : MP * (MP + 1) / 2; }
+template <int MP>
+__device__ __forceinline__ int lidx(int r, int c) {
+  return MP <= 32 ? r * (MP + 1) + c : r * (r + 1) / 2 + c;
+}
+
 // Cholesky factor of S in place, by one wave (wave-synchronous): lm holds S's lower triangle
-// (row stride MP + 1, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
+// (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
 // (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
 __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
@@ -747,25 +757,25 @@ __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
     // times its starting value), the rows below scale column j, then each updates its own part
     // of the trailing matrix (its next diagonal included, so the next pivot needs no wait).
     const int i = lane;
-    const double sii0 = i < m ? lm[i * SS + i] : 0.0;
+    const double sii0 = i < m ? lm[lidx<MP>(i, i)] : 0.0;
     for (int j = 0; j < m; ++j) {
       if (i == j) {
-        const double d = lm[j * SS + j];
+        const double d = lm[lidx<MP>(j, j)];
         const bool dk = d <= kDeadTol * sii0;
         const double ljj = dk ? 0.0 : sqrt(d);
-        lm[j * SS + j] = ljj;
+        lm[lidx<MP>(j, j)] = ljj;
         inv[j] = dk ? 0.0 : 1.0 / ljj;
         dead[j] = dk ? 1 : 0;
       }
       wave_lds_sync();
       double lij = 0.0;
       if (i > j && i < m) {
-        lij = lm[i * SS + j] * inv[j];
-        lm[i * SS + j] = lij;
+        lij = lm[lidx<MP>(i, j)] * inv[j];
+        lm[lidx<MP>(i, j)] = lij;
       }
       wave_lds_sync();
       if (i > j && i < m)
-        for (int k = j + 1; k <= i; ++k) lm[i * SS + k] -= lij * lm[k * SS + j];
+        for (int k = j + 1; k <= i; ++k) lm[lidx<MP>(i, k)] -= lij * lm[lidx<MP>(k, j)];
     }
   }
 }
@@ -1008,7 +1018,7 @@ __device__ __forceinline__ void wave_global_sync() {
 template <int MP>
 __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
                           int reseed_round) {
-  constexpr int BS = MP + 4, SS = MP + 1;
+  constexpr int BS = MP + 4;
   const int lane = threadIdx.x & 63;
 #if KAMERA_ORTH_MFMA
   // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
@@ -1036,7 +1046,7 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-          if (row < m && col <= row) lm[row * SS + col] = s0[v] + s1[v];
+          if (row < m && col <= row) lm[lidx<MP>(row, col)] = s0[v] + s1[v];
         }
       }
     }
@@ -1056,7 +1066,7 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
       for (int k = 0; k < 4; ++k)
         acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
     }
-    lm[a * SS + b] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    lm[lidx<MP>(a, b)] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 #endif
   wave_lds_sync();
@@ -1071,7 +1081,7 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
     float* row0 = buf + r0 * BS;
     float* row1 = buf + (on1 ? r1 : r0) * BS;
     for (int j = 0; j < m; ++j) {
-      const double* lj = lm + j * SS;
+      const double* lj = lm + lidx<MP>(j, 0);
       double p0[4] = {0.0, 0.0, 0.0, 0.0}, p1[4] = {0.0, 0.0, 0.0, 0.0};
       int a = 0;
       for (; a + 4 <= j; a += 4) {
@@ -1179,9 +1189,9 @@ __device__ __forceinline__ void gx_mfma(const float* G, float* buf, int D) {
 
 template <typename T, int MP, int WPB>
 __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspace_wave_kernel(CParams P) {
-  constexpr int BS = MP + 4, SS = MP + 1;
+  constexpr int BS = MP + 4;
   __shared__ __align__(16) float buf_s[WPB][128 * BS];
-  __shared__ double lm_s[WPB][MP * SS];
+  __shared__ double lm_s[WPB][lm_size<MP>()];
   __shared__ double inv_s[WPB][MP];
   __shared__ int dead_s[WPB][MP];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
