@@ -167,6 +167,19 @@ def _variant(base, **kw):
     return dataclasses.replace(p, **kw)
 
 
+def _paged(base, page_size, slack=1.25, seed=11, **kw):
+    """The base plan written through a shuffled table of pages of `page_size` tokens (sizes
+    that are not powers of two take the kernel's division path), 25 % spare pages."""
+    p = _variant(base, **kw)
+    total = max(o + L for o, L in zip(p.dst_offsets, p.chunk_tokens))
+    n_logical = -(-total // page_size)
+    n_pages = int(n_logical * slack) + 1
+    rng = np.random.Generator(np.random.PCG64(seed))
+    table = rng.permutation(n_pages)[:n_logical].astype(np.int32)
+    return dataclasses.replace(p, page_size=page_size, n_pages=n_pages, page_table=table,
+                               n_logical_pages=n_logical)
+
+
 EDGE = {
     "rank5_scalar_uv_loads": lambda: _variant("qwen25vl_gqa_bf16", m=5),
     "rank8_partial_kstep": lambda: _variant("qwen25vl_gqa_bf16", m=8),
@@ -183,6 +196,10 @@ EDGE = {
     "three_heads": lambda: _variant("qwen25vl_gqa_bf16", n_kv_heads=3),
     "max_abs_delta": lambda: _variant("qwen25vl_gqa_bf16", deltas=[2**31 - 1, -(2**31 - 1), 0, 1, -1]),
     "empty_chunk_in_batch": lambda: _variant("qwen25vl_gqa_bf16", chunk_tokens=[1296, 0, 37, 1, 200]),
+    "page12_shuffled": lambda: _paged("qwen25vl_gqa_bf16", 12),
+    "page24_reorder_rank64": lambda: _paged("mha7b_reorder_bf16", 24),
+    "page1_window": lambda: _paged("qwen3vl_window_bf16", 1),
+    "page7_mla": lambda: _paged("dsv2lite_mla_bf16", 7),
 }
 
 
