@@ -782,24 +782,26 @@ __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
 
 // ---------------------------------------------------------------------------------------
 // subspace (wide heads, 256 .. 512 features: the MLA latent): one block of 4 waves per unit.
-// LDS: xs [D][mp+1] fp32 X (odd row stride: a thread's own row is conflict-free), ys [mp][D+1]
-// fp32 Y (transposed), ss [MMAX][MMAX+1] fp64 S and then L.
+// LDS: xs [D][mp+1] fp32, holding X, then Y = G X, then X = orth(Y) (odd row stride: a thread's
+// own row is conflict-free), ss [MMAX][MMAX+1] fp64 S and then L: 76 KB for the 512-wide latent
+// at rank 32, so two blocks share a CU.
 //   Y = G X    fp32 MFMA 16x16x4, wave w takes row blocks w, w + 4, ... (G read from the
-//              workspace, 16 bytes of a row per lane per K block, next block in flight);
+//              workspace, 16 bytes of a row per lane per K block, next block in flight); Y
+//              stays in the accumulators until every wave has read X, then replaces it;
 //   S = Y^T Y  fp64 MFMA 16x16x4 over all D rows, the lower tiles dealt to the waves;
 //   L L^T = S  by wave 0 (cholesky_wave);
-//   X = Y L^-T forward substitution, one row per thread at a time, the row's x in registers
-//              (fp64 sums of the fp32 x already formed, as in the per-wave form).
+//   X = Y L^-T forward substitution in place, one row per thread at a time (fp64 sums of the
+//              fp32 x already formed, as in the per-wave form).
 // ---------------------------------------------------------------------------------------
 
 template <int MMAX>
-__device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D, int mp) {
+__device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
   constexpr int NCB = MMAX / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
   const int nrb = D / 16;   // at most 32: 8 row blocks per wave
   const int nt = D / 16;
-  const int XS = mp + 1, YS = D + 1;
+  const int XS = mp + 1;
   f32x4 acc[8][NCB];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -837,6 +839,7 @@ __device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D,
       if (rb < nrb) ga[s] = ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D + 16 * tn))[0];
     }
   }
+  __syncthreads();   // every wave has read X: Y replaces it
   // lane 16 kk + i holds rows 16 rb + 4 kk + v, columns 16 cb + i
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -846,7 +849,7 @@ __device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D,
       for (int cb = 0; cb < NCB; ++cb)
         if (16 * cb < mp)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) ys[(16 * cb + li) * YS + 16 * rb + 4 * kk + v] = acc[s][cb][v];
+          for (int v = 0; v < 4; ++v) xs[(16 * rb + 4 * kk + v) * XS + 16 * cb + li] = acc[s][cb][v];
     }
   }
 }
@@ -855,11 +858,11 @@ __device__ void gx_mfma_block(const float* G, const float* xs, float* ys, int D,
 // reseed_round >= 0 (the next round's G X spreads it); a collapsed column has l_aj = 0 below
 // its pivot, so a reseeded x_a adds nothing to the columns after it.
 template <int MMAX>
-__device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, int* dead, int D,
-                           int m, int mp, int reseed_round) {
+__device__ void orth_block(float* xs, double* ss, double* inv, int* dead, int D, int m, int mp,
+                           int reseed_round) {
   constexpr int SS = MMAX + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int XS = mp + 1, YS = D + 1;
+  const int XS = mp + 1;
   {
     // S = Y^T Y: tile (a, b), a >= b, on v_mfma_f64_16x16x4f64; lane 16k + i takes
     // Y[r + k][16 a + i] and Y[r + k][16 b + i]; its output register v is row 16 a + k + 4v,
@@ -871,16 +874,16 @@ __device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, 
       int ta = 0;
       while ((ta + 1) * (ta + 2) / 2 <= q) ++ta;
       const int tb = q - ta * (ta + 1) / 2;
-      const float* ya = ys + (16 * ta + li) * YS + kk;
-      const float* yb = ys + (16 * tb + li) * YS + kk;
+      const float* ya = xs + kk * XS + 16 * ta + li;
+      const float* yb = xs + kk * XS + 16 * tb + li;
       f64x4 sa[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) sa[c] = f64x4{0.0, 0.0, 0.0, 0.0};
       for (int r = 0; r < D; r += 16) {   // D is a multiple of 128
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          sa[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[r + 4 * c], (double)yb[r + 4 * c],
-                                                       sa[c], 0, 0, 0);
+          sa[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[(r + 4 * c) * XS],
+                                                       (double)yb[(r + 4 * c) * XS], sa[c], 0, 0, 0);
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -892,37 +895,31 @@ __device__ void orth_block(const float* ys, float* xs, double* ss, double* inv, 
   __syncthreads();
   if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m);
   __syncthreads();
-  // X = Y L^-T: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj
+  // X = Y L^-T in place: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj; the row's earlier x are
+  // already in place, y_ij is read before x_ij replaces it (columns from m on stay zero)
   for (int i = tid; i < D; i += kThreads) {
-    float xv[MMAX];
-#pragma unroll
-    for (int j = 0; j < MMAX; ++j) {
-      xv[j] = 0.f;
-      if (j < m) {
-        const double* lj = ss + j * SS;
-        double p0 = 0.0, p1 = 0.0;
-#pragma unroll
-        for (int a = 0; a < j; ++a) {
-          if (a & 1) p1 += (double)xv[a] * lj[a];
-          else p0 += (double)xv[a] * lj[a];
-        }
-        float v = (float)(((double)ys[j * YS + i] - (p0 + p1)) * inv[j]);
-        if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
-        xv[j] = v;
-      }
-    }
     float* xr = xs + i * XS;
-#pragma unroll
-    for (int j = 0; j < MMAX; ++j)
-      if (j < mp) xr[j] = xv[j];
+    for (int j = 0; j < m; ++j) {
+      const double* lj = ss + j * SS;
+      double p0 = 0.0, p1 = 0.0;
+      int a = 0;
+      for (; a + 2 <= j; a += 2) {
+        p0 += (double)xr[a] * lj[a];
+        p1 += (double)xr[a + 1] * lj[a + 1];
+      }
+      if (a < j) p0 += (double)xr[a] * lj[a];
+      float v = (float)(((double)xr[j] - (p0 + p1)) * inv[j]);
+      if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
+      xr[j] = v;
+    }
   }
   __syncthreads();
 }
 
 template <typename T, int DMAX, int MMAX>
-__global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void subspace_kernel(CParams P) {
   __shared__ __align__(16) float xs[DMAX * (MMAX + 1)];
-  __shared__ float ys[MMAX * (DMAX + 1)];
   __shared__ double ss[MMAX * (MMAX + 1)];
   __shared__ double inv[MMAX];
   __shared__ int dead[MMAX];
@@ -932,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
   const int unit = blockIdx.x - P.starts[e];
   const int layer = unit / J.heads, head = unit - layer * J.heads;
   const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
-  const int XS = mp + 1, YS = D + 1;
+  const int XS = mp + 1;
 
   // G: the single partial, or the sum of the partial tiles assembled in the workspace
   const float* G;
@@ -977,17 +974,12 @@ __global__ __launch_bounds__(kThreads) void subspace_kernel(CParams P) {
   __syncthreads();
 
   for (int round = 0; round < P.n_iter; ++round) {
-    gx_mfma_block<MMAX>(G, xs, ys, D, mp);
+    gx_mfma_block<MMAX>(G, xs, D, mp);
     __syncthreads();
-    orth_block<MMAX>(ys, xs, ss, inv, dead, D, m, mp, round);
+    orth_block<MMAX>(xs, ss, inv, dead, D, m, mp, round);
   }
   // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
-  for (int idx = tid; idx < D * m; idx += kThreads) {
-    const int i = idx / m, j = idx - i * m;
-    ys[j * YS + i] = xs[i * XS + j];
-  }
-  __syncthreads();
-  orth_block<MMAX>(ys, xs, ss, inv, dead, D, m, mp, -1);
+  orth_block<MMAX>(xs, ss, inv, dead, D, m, mp, -1);
 
   T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
   float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
