@@ -686,70 +686,78 @@ __device__ __forceinline__ int lidx(int r, int c) {
 // (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
 // (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
-__device__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
-  constexpr int SS = MP + 1;
+__device__ void cholesky_wave(double* lm, double* inv, int* dead, int m, double* scratch) {
   const int lane = threadIdx.x & 63;
-  if constexpr (MP <= 32) {
+  if constexpr (MP <= 32 || MP == 64) {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
     // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
     // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
     // the lanes holding column j scale it and publish it in LDS, then each lane updates its
     // own part of the trailing matrix. The same operations in the same order as the LDS
-    // version below, with one LDS round trip per step instead of a chain of them.
+    // version below, with one LDS round trip per step instead of a chain of them. At MP = 64
+    // a lane holds a whole row (64 doubles) and the published column goes to `scratch` (the
+    // packed triangle has no free upper part).
     constexpr int LPR = 64 / MP, CPL = MP / LPR;
     const int ri = lane % MP, cb = lane / MP, c0 = cb * CPL;
     double sv[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int col = c0 + c;
-      sv[c] = (ri < m && col < m) ? (ri >= col ? lm[ri * SS + col] : lm[col * SS + ri]) : 0.0;
+      sv[c] = (ri < m && col < m) ? (ri >= col ? lm[lidx<MP>(ri, col)] : lm[lidx<MP>(col, ri)])
+                                  : 0.0;
     }
-    double* colj = lm + 1;   // the strict upper part of row 0 is free until the end
+    // the strict upper part of row 0 of the square layout is free until the end
+    double* colj = MP <= 32 ? lm + 1 : scratch;
     wave_lds_sync();
-    for (int j = 0; j < m; ++j) {
-      const int jc = j % CPL, jb = j / CPL;
-      double pv = 0.0;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (c == jc) pv = sv[c];
-      const uint64_t pb = __builtin_bit_cast(uint64_t, pv);
-      const int src = j + MP * jb;
-      const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, src);
-      const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), src);
-      const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
-      const double s0 = lm[j * SS + j];   // s_jj before elimination (lm still holds S)
-      const bool dk = d <= kDeadTol * s0;
-      const double ljj = dk ? 0.0 : sqrt(d);
-      const double iv = dk ? 0.0 : 1.0 / ljj;
-      if (lane == 0) {
-        inv[j] = iv;
-        dead[j] = dk ? 1 : 0;
-      }
-      if (cb == jb) {
-        double v = 0.0;
+    // at MP = 64 the steps are unrolled, so every register index below is static
+    constexpr int kUnrollSteps = MP == 64 ? 64 : 1;
+#pragma unroll kUnrollSteps
+    for (int j = 0; j < MP; ++j) {
+      if (j < m) {
+        const int jc = j % CPL, jb = j / CPL;
+        double pv = 0.0;
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
-          if (c == jc) v = sv[c];
-        v = ri == j ? ljj : (ri > j ? v * iv : v);
+          if (c == jc) pv = sv[c];
+        const uint64_t pb = __builtin_bit_cast(uint64_t, pv);
+        const int src = j + MP * jb;
+        const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, src);
+        const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), src);
+        const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
+        const double s0 = lm[lidx<MP>(j, j)];   // s_jj before elimination (lm still holds S)
+        const bool dk = d <= kDeadTol * s0;
+        const double ljj = dk ? 0.0 : sqrt(d);
+        const double iv = dk ? 0.0 : 1.0 / ljj;
+        if (lane == 0) {
+          inv[j] = iv;
+          dead[j] = dk ? 1 : 0;
+        }
+        if (cb == jb) {
+          double v = 0.0;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          if (c == jc) sv[c] = v;
-        colj[ri] = ri > j && ri < m ? v : 0.0;
-      }
-      wave_lds_sync();
-      const double lij = colj[ri];
+          for (int c = 0; c < CPL; ++c)
+            if (c == jc) v = sv[c];
+          v = ri == j ? ljj : (ri > j ? v * iv : v);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int col = c0 + c;
-        if (col > j && col <= ri && ri < m) sv[c] -= lij * colj[col];
+          for (int c = 0; c < CPL; ++c)
+            if (c == jc) sv[c] = v;
+          colj[ri] = ri > j && ri < m ? v : 0.0;
+        }
+        wave_lds_sync();
+        const double lij = colj[ri];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int col = c0 + c;
+          if (col > j && col <= ri && ri < m) sv[c] -= lij * colj[col];
+        }
+        wave_lds_sync();   // colj is rewritten by the next step
       }
-      wave_lds_sync();   // colj is rewritten by the next step
     }
     // L (lower triangle) back to LDS for the forward substitution
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int col = c0 + c;
-      if (ri < m && col <= ri) lm[ri * SS + col] = sv[c];
+      if (ri < m && col <= ri) lm[lidx<MP>(ri, col)] = sv[c];
     }
   } else {
     // Cholesky, right-looking: lane i owns row i of S, which becomes row i of L. Step j: the
@@ -893,7 +901,7 @@ __device__ void orth_block(float* xs, double* ss, double* inv, int* dead, int D,
     }
   }
   __syncthreads();
-  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m);
+  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m, nullptr);
   __syncthreads();
   // X = Y L^-T in place: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj; the row's earlier x are
   // already in place, y_ij is read before x_ij replaces it (columns from m on stay zero)
@@ -1008,8 +1016,8 @@ __device__ __forceinline__ void wave_global_sync() {
 }
 
 template <int MP>
-__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
-                          int reseed_round) {
+__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, double* scratch, int D,
+                          int m, int reseed_round) {
   constexpr int BS = MP + 4;
   const int lane = threadIdx.x & 63;
 #if KAMERA_ORTH_MFMA
@@ -1062,7 +1070,7 @@ __device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D,
   }
 #endif
   wave_lds_sync();
-  cholesky_wave<MP>(lm, inv, dead, m);
+  cholesky_wave<MP>(lm, inv, dead, m, scratch);
   wave_lds_sync();
   // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
   // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
@@ -1186,6 +1194,7 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
   __shared__ double lm_s[WPB][lm_size<MP>()];
   __shared__ double inv_s[WPB][MP];
   __shared__ int dead_s[WPB][MP];
+  __shared__ double cj_s[WPB][MP > 32 ? MP : 1];   // published column of the Cholesky (MP 64)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = blockIdx.x * WPB + w;
   if (u >= P.n_total) return;   // whole wave; no block-wide barrier follows
@@ -1193,6 +1202,7 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
   double* lm = lm_s[w];
   double* inv = inv_s[w];
   int* dead = dead_s[w];
+  double* cj = cj_s[w];
 
   const int e = find_entry(P, u);
   const CJob& J = P.jobs[P.job_of[e]];
@@ -1302,10 +1312,10 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
     }
     wave_lds_sync();
 #endif
-    orth_wave<MP>(buf, lm, inv, dead, D, m, round);
+    orth_wave<MP>(buf, lm, inv, dead, cj, D, m, round);
   }
   // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
-  orth_wave<MP>(buf, lm, inv, dead, D, m, -1);
+  orth_wave<MP>(buf, lm, inv, dead, cj, D, m, -1);
 
   T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
   float* xg = P.ws + J.xbase + (int64_t)unit * D * MP;
