@@ -245,9 +245,15 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
   // operand (16 KB per window at m = 64), so rank > 32 takes long waves. Measured on MI355X:
   // 4 tiles for m <= 32 (2 and 8 tiles were 1-7 % slower, 16 and 32 up to 8 %), 32 for
   // m <= 64 (4 tiles: -18 %); larger only when the grid would exceed kMaxGridBlocks.
-  auto tgroups = [](const JobDesc& j, int64_t tpw) {
+  // With the short-wave default of 4 tiles, a job whose tile count splits evenly into 3s but
+  // not into 4s takes 3 (81-tile chunks of 1296 tokens: 27 equal token groups instead of 21
+  // of 3 or 4 tiles).
+  const int even_tpw = env_int("KAMERA_EVEN_TPW", 1);
+  auto tgroups = [even_tpw](const JobDesc& j, int64_t tpw) {
     const int64_t sub = 4 / std::min(4, j.n_windows);
-    return std::max<int64_t>(1, (j.n_tiles + tpw * sub - 1) / (tpw * sub));
+    const int64_t t = (even_tpw && tpw == 4 && sub == 1 && j.n_tiles % 4 != 0 &&
+                       j.n_tiles % 3 == 0) ? 3 : tpw;
+    return std::max<int64_t>(1, (j.n_tiles + t * sub - 1) / (t * sub));
   };
   auto blocks_at = [&](int64_t tpw) {
     int64_t b = 0;
