@@ -13,11 +13,14 @@
 //   gram      partial Gram tiles Delta_s^T Delta_s over token splits s with fp32 MFMA
 //             16x16x4; one tile pair (bi <= bj) of G per block; Delta is formed on the fly
 //             (canonical rows rotated in fp32 with cos/sin from fp64, as the reuse kernels do);
-//   subspace  one block per head: sums the partials into G, then block power iteration
-//             X <- orth(G X) from a fixed +-1 start. orth() is a Cholesky QR: S = Y^T Y, its
-//             Cholesky factor L and L^-1 in fp64, X = Y L^-T accumulated in fp64. Columns that
-//             collapse (Y rank deficient) are re-seeded between rounds and zero after the last;
-//             a final orth() of X alone restores orthonormality to fp32 rounding;
+//   subspace  one wave per head (widths up to 128) or one block of four waves per head (the
+//             wide MLA latent): sums the partials into G where there are several, then block
+//             power iteration X <- orth(G X) from a fixed +-1 start, G X on fp32 MFMA. orth() is
+//             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64 (in
+//             registers up to rank 32 and at rank 64), X = Y L^-T by forward substitution with
+//             fp64 sums. Columns that collapse (Y rank deficient) are re-seeded between rounds
+//             and zero after the last; a final orth() of X alone restores orthonormality to
+//             fp32 rounding;
 //   project   U = Delta X with the fp32 X kept in the workspace (a second pass over the inputs).
 #include <hip/hip_runtime.h>
 
@@ -653,13 +656,8 @@ void gram_stream_kernel(CParams P) {
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// subspace: one block per unit, for widths above 128 (an MLA latent). DMAX >= width,
-// MMAX >= mp (a multiple of 16). G is read from the workspace (L2) in every round.
-// LDS: xs [width][mp] fp32 (row-major), ys [mp][width+1] fp32 (column-major, padded),
-//      ss [m][MMAX+1] fp64: S = Y^T Y, overwritten column by column with its Cholesky factor L,
-//      li [mp][MMAX+1] fp64: L^-1.
-// ---------------------------------------------------------------------------------------
+// Shared by both subspace kernels: the fixed +-1 start, the storage of S and L, and the
+// Cholesky factorisation.
 
 __device__ __forceinline__ float seed_value(int i, int j, int round) {
   uint32_t h = (uint32_t)i * 0x9E3779B1u ^ ((uint32_t)j + 0x7F4A7C15u) * 0x85EBCA77u ^
@@ -1004,8 +1002,9 @@ void subspace_kernel(CParams P) {
 // wave-synchronous. MP = mp exactly. Per wave in LDS:
 //   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
 //       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
-//   lm  [MP][MP+1] fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
-//       inv holds 1 / diag(L) (0 for a collapsed column).
+//   lm  (layout lidx) fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
+//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also an MP-double scratch
+//       for the register Cholesky's published column.
 // Lane l owns rows l and l + 64.
 // ---------------------------------------------------------------------------------------
 
