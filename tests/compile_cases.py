@@ -298,3 +298,10 @@ def full_case() -> Case:
     tokens, rank 16)."""
     return Case("qwen25vl_chunk", "gqa", "bf16", 28, 4, 128, 128, oracle.HALF_SPLIT, 1e6,
                 [ChunkSpec(1296, 16, 20000)], seed=11)
+
+
+def full_mla_case() -> Case:
+    """One chunk at the full DeepSeek-V2-Lite-like MLA geometry (27 layers, rows of a 512-wide
+    latent and a 64-wide rotary part, 2048 tokens, rank 32)."""
+    return Case("dsv2lite_mla_chunk", "mla", "bf16", 27, 1, 512, 64, oracle.HALF_SPLIT, 1e4,
+                [ChunkSpec(2048, 32, 40000)], seed=12, mla_shared_rows=True)

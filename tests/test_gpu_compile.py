@@ -239,3 +239,18 @@ def test_full_size_chunk_sampled_heads():
         _, V = outputs(case, items, 0, ch)
         g = np.einsum("lhfr,lhfs->lhrs", V, V)
         assert np.max(np.abs(g - np.eye(16))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
+
+
+def test_full_size_mla_chunk_sampled_heads():
+    """A full 27-layer, 2048-token MLA chunk (the latent's Gram over 64 token steps without
+    splits, its block-per-head subspace); every head's factors are orthonormal, six sampled
+    layers of both channels are checked against the oracle."""
+    case = cc.full_mla_case()
+    inputs, items = run(case)
+    rng = np.random.default_rng(6)
+    heads = [(0, 0), (26, 0)] + [(int(rng.integers(27)), 0) for _ in range(4)]
+    check_case(case, inputs, items, heads=heads)
+    for ch in range(2):
+        _, V = outputs(case, items, 0, ch)
+        g = np.einsum("lhfr,lhfs->lhrs", V, V)
+        assert np.max(np.abs(g - np.eye(32))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
