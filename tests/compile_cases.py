@@ -305,3 +305,10 @@ def full_mla_case() -> Case:
     latent and a 64-wide rotary part, 2048 tokens, rank 32)."""
     return Case("dsv2lite_mla_chunk", "mla", "bf16", 27, 1, 512, 64, oracle.HALF_SPLIT, 1e4,
                 [ChunkSpec(2048, 32, 40000)], seed=12, mla_shared_rows=True)
+
+
+def full_rank64_case() -> Case:
+    """The 7B-like MHA reorder geometry at rank 64 (32 heads x 128, interleaved RoPE, 4096
+    tokens), on 4 of its 32 layers: the per-head shapes of the full compile."""
+    return Case("mha7b_chunk_rank64", "gqa", "bf16", 4, 32, 128, 128, oracle.INTERLEAVED, 1e4,
+                [ChunkSpec(4096, 64, 12288)], seed=13)

@@ -254,3 +254,18 @@ def test_full_size_mla_chunk_sampled_heads():
         _, V = outputs(case, items, 0, ch)
         g = np.einsum("lhfr,lhfs->lhrs", V, V)
         assert np.max(np.abs(g - np.eye(32))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
+
+
+def test_rank64_chunk_sampled_heads():
+    """Rank 64 at the MHA reorder workload's per-head geometry (4096 tokens, 32 heads, the
+    register factorisation of rank 64): every head orthonormal, eight sampled heads checked
+    against the oracle."""
+    case = cc.full_rank64_case()
+    inputs, items = run(case)
+    rng = np.random.default_rng(7)
+    heads = [(0, 0), (3, 31)] + [(int(rng.integers(4)), int(rng.integers(32))) for _ in range(6)]
+    check_case(case, inputs, items, heads=heads)
+    for ch in range(2):
+        _, V = outputs(case, items, 0, ch)
+        g = np.einsum("lhfr,lhfs->lhrs", V, V)
+        assert np.max(np.abs(g - np.eye(64))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
