@@ -685,6 +685,7 @@ __device__ __forceinline__ int lidx(int r, int c) {
 // (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
 __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m, double* scratch) {
+  static_assert(MP % 16 == 0 && MP <= 64, "rank classes are 16, 32, 48 and 64");
   const int lane = threadIdx.x & 63;
   if constexpr (MP <= 32 || MP == 64) {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
@@ -866,6 +867,8 @@ __device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
 template <int MMAX>
 __device__ void orth_block(float* xs, double* ss, double* inv, int* dead, int D, int m, int mp,
                            int reseed_round) {
+  // the square S/L layout and the register factorisation without a separate scratch column
+  static_assert(MMAX <= 32, "wide heads take ranks up to 32");
   constexpr int SS = MMAX + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int XS = mp + 1;
