@@ -3,16 +3,25 @@
 One step = one kamera_reuse_batch call over the whole batch: work decomposition, fp64 phase
 generation, streaming of the canonical KV, rotation, the rank-m patch, and the page-table
 scatter, for every chunk, layer, channel and head. Inputs are resident in HBM before timing.
+The headline workload is the largest that fits one GPU: the 7B-like MHA reorder batch (32
+layers, 32 heads x 128, 16 chunks of 4096 tokens, rank-64 patches, paged), 86.4 GB moved per
+step.
 
-Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s). The
-line also carries "patch_compile": the time kamera_patch_compile takes to form the same
-batch's patches (deficit, Gram, subspace iteration, projection), next to one reuse pass, and
-"decode_attention": the consumer-side decode attention (with its state merge) on a
-64-sequence x 16K-token paged cache ("decode_attention_mla": the same over an MLA cache), and
-"chunk_attention": the same decode read from 16
-canonical chunks per sequence in place (query turned per chunk, rank-16 patches on K and V).
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--compile-steps N] [--attention-steps N] [--chunk-attention-steps N]
+Prints one JSON line (metric: relocated + patched KV tokens/s and achieved HBM GB/s), which
+also carries:
+  "configs": a compact record per other workload (the Qwen2.5-VL-like GQA batch, the
+    DeepSeek-V2-Lite-like MLA batch, the Qwen3-VL-like sliding window, and the tiny fp32 case
+    as a latency), each timed on its own;
+  "cpu_baseline": the fp64 oracle on a bounded sample of the headline batch, host cores;
+  "patch_compile": kamera_patch_compile (deficit, Gram, subspace iteration, projection) on a
+    few chunks of the headline batch, next to one reuse pass over the same chunks, with the
+    orbit compile over 3 orderings;
+  "decode_attention" / "decode_attention_mla": the consumer-side decode attention (with its
+    state merge) on a 64-sequence x 16K-token paged cache, GQA and MLA;
+  "chunk_attention": the same decode read from 16 canonical chunks per sequence in place.
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs A,B|none]
+                    [--no-cpu-baseline] [--compile-steps N] [--compile-chunks N]
+                    [--attention-steps N] [--chunk-attention-steps N]
 """
 from __future__ import annotations
 
@@ -29,7 +38,11 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
-DEFAULT_WORKLOAD = "qwen25vl_gqa_bf16"
+# the largest workload that fits one GPU (86.4 GB moved per step)
+DEFAULT_WORKLOAD = "mha7b_reorder_bf16"
+# the other workloads, each timed after the headline into a compact record (the fp32 one is
+# latency bound and reported in microseconds)
+OTHER_CONFIGS = ["qwen25vl_gqa_bf16", "dsv2lite_mla_bf16", "qwen3vl_window_bf16", "tiny_gqa_f32"]
 METRIC = "relocated+patched KV tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
 CALIB_BYTES = 2 << 30
 KERNEL_SOURCES = ["position_invariant_kv_kamera_amd/csrc/kamera_kernels.hip",
@@ -80,10 +93,23 @@ def traffic_from_profile(workload: str):
     return d.get("traffic_bytes"), d.get("kernel")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(batch, budget_s: float) -> dict:
-    """The oracle, as it is, on the chunks of the same batch in order (all layers, channels and
-    heads; starting over when the batch is done) until about `budget_s` seconds of CPU work,
-    scaled to tokens/s."""
+    """The oracle, as it is, on (chunk, layer) units of the same batch in order (every channel
+    and head of the layer; chunk by chunk, starting over when the batch is done) until about
+    `budget_s` seconds of CPU work. A token counts once all its layers are done, so the rate is
+    (layer-token units / n_layers) per second, comparable with the GPU's tokens/s. Host copies
+    of the inputs are made per unit and are not timed."""
     import numpy as np
     import torch
     import oracle
@@ -92,50 +118,71 @@ def cpu_baseline(batch, budget_s: float) -> dict:
     layout = 0 if p.rope_layout == "half_split" else 1
 
     def host(t):
+        if t is None:
+            return None
         t = t.detach().contiguous().cpu()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     busy = 0.0
-    tokens = 0
-    chunks = 0
+    layer_tokens = 0
+    units = 0
     while busy < budget_s:
-        c = chunks % p.n_chunks
+        c = (units // p.n_layers) % p.n_chunks
+        l = units % p.n_layers
         ct = batch.chunks[c]
-        srcs = [host(ct.src[ch]) for ch in range(2)]
-        Us = [host(ct.U[ch]) if ct.U[ch] is not None else None for ch in range(2)]
-        Vs = [host(ct.V[ch]) if ct.V[ch] is not None else None for ch in range(2)]
+        srcs = [host(ct.src[ch][l]) for ch in range(2)]
+        Us = [host(ct.U[ch][l]) if ct.U[ch] is not None else None for ch in range(2)]
+        Vs = [host(ct.V[ch][l]) if ct.V[ch] is not None else None for ch in range(2)]
         t0 = time.perf_counter()
-        for l in range(p.n_layers):
-            for ch in range(2):
-                W = p.width(ch)
-                for h in range(p.heads(ch)):
-                    x = np.ascontiguousarray(srcs[ch][l][:, h * W:(h + 1) * W])
-                    U = None if Us[ch] is None else Us[ch][l, h]
-                    V = None if Vs[ch] is None else Vs[ch][l, h]
-                    e = oracle.expected_head(x, rotate=(ch == 0), layout=layout,
-                                             delta=p.deltas[c], theta=p.theta, U=U, V=V)
-                    if not e["copy"]:
-                        oracle.to_bf16(e["z"]) if p.dtype == "bf16" else oracle.to_f32(e["z"])
+        for ch in range(2):
+            W = p.width(ch)
+            for h in range(p.heads(ch)):
+                x = np.ascontiguousarray(srcs[ch][:, h * W:(h + 1) * W])
+                U = None if Us[ch] is None else Us[ch][h]
+                V = None if Vs[ch] is None else Vs[ch][h]
+                e = oracle.expected_head(x, rotate=(ch == 0), layout=layout,
+                                         delta=p.deltas[c], theta=p.theta, U=U, V=V)
+                if not e["copy"]:
+                    oracle.to_bf16(e["z"]) if p.dtype == "bf16" else oracle.to_f32(e["z"])
         busy += time.perf_counter() - t0
-        tokens += p.chunk_tokens[c]
-        chunks += 1
-    passes = chunks / p.n_chunks
-    return {"value": tokens / busy, "unit": "tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{chunks} chunk evaluations ({passes:.2f} passes over the {p.n_chunks} "
-                      f"chunks; {tokens} tokens x {p.n_layers} layers x 2 channels), "
-                      f"{busy:.1f} s of oracle time"}
+        layer_tokens += p.chunk_tokens[c]
+        units += 1
+    return {"value": layer_tokens / p.n_layers / busy, "unit": "tokens/s",
+            "cores": oracle.threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{units} (chunk, layer) units of {p.name} in batch order "
+                      f"({units / (p.n_chunks * p.n_layers):.4f} of the batch; "
+                      f"{layer_tokens} token-layers, every channel and head), "
+                      f"{busy:.1f} s of oracle time on {oracle.threads()} OpenMP threads"}
 
 
 FP32_PEAK_TFLOPS = 157.3       # dense fp32 (MFMA and vector alike)
 
 
-def compile_leg(p, batch, reuse_ms: float, steps: int, stream, orbit_steps: int = 2) -> dict:
-    """Time kamera_patch_compile over the same chunks (one step = the whole batch's patches at
-    the workload's largest rank). The conditioned KV is the canonical KV plus Gaussian noise;
-    the compile does the same work whatever the values."""
+def compile_leg(p, batch, steps: int, stream, orbit_steps: int = 2,
+                max_chunks: int | None = None) -> dict:
+    """Time kamera_patch_compile over the first `max_chunks` chunks of the batch (all when
+    None; one step = those chunks' patches at the workload's largest rank), next to one reuse
+    pass over the same chunks. The conditioned KV is the canonical KV plus Gaussian noise; the
+    compile does the same work whatever the values."""
     import torch
     from position_invariant_kv_kamera_amd import binding as kb
+
+    n_sub = p.n_chunks if max_chunks is None else min(p.n_chunks, max_chunks)
+    # one reuse pass over the same chunks, for the compile / reuse cost ratio
+    model0, cache0 = kb.model_of(p), kb.cache_of(batch)
+    chunks0 = kb.chunks_of(batch)
+    ws0 = kb.Workspace(n_sub)
+    sp = stream.cuda_stream
+    for _ in range(3):
+        kb.check(kb.kamera_reuse_batch(model0, cache0, chunks0, n_sub, ws0.ptr, ws0.nbytes, sp))
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(10):
+        kb.check(kb.kamera_reuse_batch(model0, cache0, chunks0, n_sub, ws0.ptr, ws0.nbytes, sp))
+    r1.record(stream)
+    torch.cuda.synchronize()
+    reuse_ms = r0.elapsed_time(r1) / 10
 
     m = max(p.m_rot + p.m_plain) or 16
     n_iter = 8
@@ -144,7 +191,7 @@ def compile_leg(p, batch, reuse_ms: float, steps: int, stream, orbit_steps: int 
     items = []
     es = p.elem_bytes
     io_bytes = in_bytes = gram_flops = proj_flops = 0
-    for c, ct in enumerate(batch.chunks):
+    for c, ct in enumerate(batch.chunks[:n_sub]):
         T = p.chunk_tokens[c]
         cond, U, V = [], [], []
         for ch in range(2):
@@ -173,7 +220,8 @@ def compile_leg(p, batch, reuse_ms: float, steps: int, stream, orbit_steps: int 
     floor_ms = max(io_bytes / (HBM_PEAK_GBPS * 1e9),
                    (gram_flops + proj_flops) / (FP32_PEAK_TFLOPS * 1e12)) * 1e3
 
-    result = {"ms_per_batch": round(ms, 3), "steps": steps, "rank": m, "n_iter": n_iter,
+    result = {"chunks": f"{n_sub} of the {p.n_chunks} chunks of {p.name}",
+              "ms_per_batch": round(ms, 3), "steps": steps, "rank": m, "n_iter": n_iter,
               "input_bytes": in_bytes, "reuse_ms_per_batch": round(reuse_ms, 4),
               "compile_over_reuse": round(ms / reuse_ms, 2), "io_bytes": io_bytes,
               "gram_flops": gram_flops, "project_flops": proj_flops,
@@ -611,6 +659,78 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
     print(out_md.read_text())
 
 
+def config_of(p) -> dict:
+    return {"workload": p.name, "family": p.family, "layers": p.n_layers,
+            "kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rope_dim": p.rope_dim,
+            "rope_layout": p.rope_layout, "chunks": p.n_chunks,
+            "chunk_tokens": p.chunk_tokens[0], "rank": max(p.m_rot + p.m_plain),
+            "cache": "dense" if p.page_table is None else f"paged{p.page_size}",
+            "parallelism": "none (1 GPU)"}
+
+
+def time_reuse(p, batch, steps: int, warmup: int, stream) -> dict:
+    """`warmup` untimed kamera_reuse_batch calls over the whole batch, then `steps` timed ones:
+    HIP events around every call on the launch stream, and the wall clock around them all
+    (bracketed by device synchronisation)."""
+    import torch
+    from position_invariant_kv_kamera_amd import binding as kb
+
+    ws = kb.Workspace(p.n_chunks)
+    model, cache, chunks = kb.model_of(p), kb.cache_of(batch), kb.chunks_of(batch)
+    sptr = stream.cuda_stream
+
+    def step():
+        kb.check(kb.kamera_reuse_batch(model, cache, chunks, p.n_chunks, ws.ptr, ws.nbytes, sptr))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean = sum(ev) / len(ev)
+    return {"ev_mean": mean, "wall_ms": wall * 1e3 / steps,
+            "kernel_ms": {"mean": round(mean, 4), "p10": round(ev[len(ev) // 10], 4),
+                          "p50": round(ev[len(ev) // 2], 4),
+                          "p90": round(ev[(9 * len(ev)) // 10], 4)}}
+
+
+def config_record(name: str, steps: int, warmup: int, stream) -> dict:
+    """One workload timed on its own (materialized, timed, freed): kernel time by HIP events,
+    tokens/s, algorithmic GB/s and its fraction of 8 TB/s, and the HBM traffic of the
+    committed counter summary when it was taken on the current kernel sources."""
+    import torch
+    from position_invariant_kv_kamera_amd import workloads as wl
+
+    p = wl.plan(name)
+    batch = wl.materialize(p, "cuda")
+    t = time_reuse(p, batch, steps, warmup, stream)
+    del batch
+    ab = algorithmic_bytes(p)["total"]
+    ms = t["ev_mean"]
+    gbps = ab / (ms * 1e-3) / 1e9
+    traffic, tinfo = traffic_from_profile(name)
+    rec = {"kernel_ms": t["kernel_ms"], "tokens_per_s": round(p.total_tokens / (ms * 1e-3), 1),
+           "algorithmic_bytes": ab, "achieved_gbps": round(gbps, 1),
+           "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+           "traffic_over_algorithmic": round(traffic / ab, 4) if traffic else None,
+           "steps": steps, "dtype": p.dtype, "config": config_of(p)}
+    if tinfo == "stale":
+        rec["traffic_note"] = "counters were taken on older kernel sources"
+    if p.dtype == "f32":   # latency bound: the figure is the call's duration
+        rec["latency_us"] = {k: round(v * 1e3, 2) for k, v in t["kernel_ms"].items()}
+    torch.cuda.synchronize()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -635,6 +755,13 @@ def main():
                     help="timed kamera_decode_attention calls on a 64 x 16K decode (0: skip)")
     ap.add_argument("--chunk-attention-steps", type=int, default=20,
                     help="timed kamera_chunk_attention calls on 64 x 16 chunks of 1024 (0: skip)")
+    ap.add_argument("--compile-chunks", type=int, default=4,
+                    help="chunks of the batch the compile leg forms patches for (0: all)")
+    ap.add_argument("--configs", default=",".join(OTHER_CONFIGS),
+                    help="workloads timed after the headline, one compact record each "
+                         "('none': skip)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed reuse calls per additional workload")
     args = ap.parse_args()
     if args.summarize_attention_profile:
         summarize_attention_profile(args.summarize_attention_profile, args.profile_command,
@@ -663,39 +790,57 @@ def main():
         sys.exit(1)
     kb.load_library()   # raises if the HIP library is missing
 
+    kb.check(kb.kamera_init())   # the staging ring: set up before anything is timed
+    stream = torch.cuda.current_stream()
+
     p = wl.plan(args.workload)
     print(f"[bench] materializing {args.workload} on cuda:0", file=sys.stderr, flush=True)
     batch = wl.materialize(p, "cuda")
-    ws = kb.Workspace(p.n_chunks)
-    model, cache, chunks = kb.model_of(p), kb.cache_of(batch), kb.chunks_of(batch)
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-
-    def step():
-        kb.check(kb.kamera_reuse_batch(model, cache, chunks, p.n_chunks, ws.ptr, ws.nbytes, sptr))
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    ev_avg = sum(ev_ms) / len(ev_ms)
-    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] timing {args.steps} reuse steps on {args.workload}", file=sys.stderr, flush=True)
+    t = time_reuse(p, batch, args.steps, args.warmup, stream)
+    ev_avg, ms_per_step = t["ev_mean"], t["wall_ms"]
 
     ab = algorithmic_bytes(p)
     gbps = ab["total"] / (ev_avg * 1e-3) / 1e9
-    tokens = p.total_tokens
-    value = tokens / (ms_per_step * 1e-3)
+    value = p.total_tokens / (ms_per_step * 1e-3)
+    traffic, tinfo = traffic_from_profile(args.workload)
+    flops = patch_flops(p)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": config_of(p),
+        "achieved_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "kernel_ms": t["kernel_ms"],
+        "mfma_util": round(flops / (ev_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab["total"],
+                     "kernel": "kamera_mfma_kernel", "timed_with": "hip events on the launch stream"},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if tinfo == "stale":
+        out["roofline"]["traffic_note"] = "counters were taken on older kernel sources"
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)
+    if args.compile_steps > 0:
+        print("[bench] timing the patch compile", file=sys.stderr, flush=True)
+        out["patch_compile"] = compile_leg(p, batch, args.compile_steps, stream, args.orbit_steps,
+                                           args.compile_chunks or None)
+    del batch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     # context: the runtime's device-to-device copy, and a plain elementwise stream kernel
     # (bitwise_not over 2 GiB of int32: 2 GiB read, 2 GiB written; it also calibrates the
@@ -717,49 +862,18 @@ def main():
     copy_gbps = timed(lambda: dst.copy_(buf))
     stream_gbps = timed(lambda: torch.bitwise_not(buf, out=dst))
     del buf, dst
+    out["device_copy_gbps"] = round(copy_gbps, 1)
+    out["stream_kernel_gbps"] = round(stream_gbps, 1)
+    out["frac_of_stream_kernel"] = round(gbps / stream_gbps, 4)
 
-    traffic, tinfo = traffic_from_profile(args.workload)
-    flops = patch_flops(p)
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if p.dtype == "bf16" else "f32",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "family": p.family, "layers": p.n_layers,
-                   "kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rope_dim": p.rope_dim,
-                   "rope_layout": p.rope_layout, "chunks": p.n_chunks,
-                   "chunk_tokens": p.chunk_tokens[0], "rank": max(p.m_rot + p.m_plain),
-                   "cache": "dense" if p.page_table is None else f"paged{p.page_size}",
-                   "parallelism": "none (1 GPU)"},
-        "achieved_gbps": round(gbps, 1),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "device_copy_gbps": round(copy_gbps, 1),
-        "stream_kernel_gbps": round(stream_gbps, 1),
-        "frac_of_stream_kernel": round(gbps / stream_gbps, 4),
-        "kernel_ms": {"mean": round(ev_avg, 4), "p10": round(ev_ms[len(ev_ms) // 10], 4),
-                      "p50": round(ev_ms[len(ev_ms) // 2], 4),
-                      "p90": round(ev_ms[(9 * len(ev_ms)) // 10], 4)},
-        "mfma_util": round(flops / (ev_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": ab["total"],
-                     "kernel": "kamera_mfma_kernel", "timed_with": "hip events on the launch stream"},
-        "kernel_source_sha": kernel_source_hash(),
-    }
-    if tinfo == "stale":
-        out["roofline"]["traffic_note"] = "counters were taken on older kernel sources"
-    if args.compile_steps > 0:
-        print("[bench] timing the patch compile over the same batch", file=sys.stderr, flush=True)
-        out["patch_compile"] = compile_leg(p, batch, ev_avg, args.compile_steps, stream,
-                                           args.orbit_steps)
+    configs = [c for c in args.configs.split(",") if c and c != "none" and c != args.workload]
+    if configs:
+        out["configs"] = {}
+    for name in configs:
+        print(f"[bench] per-config record: {name}", file=sys.stderr, flush=True)
+        out["configs"][name] = config_record(name, args.config_steps, args.warmup, stream)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     if args.attention_steps > 0:
         print("[bench] timing decode attention", file=sys.stderr, flush=True)
         out["decode_attention"] = attention_leg(args.attention_steps, stream)
@@ -768,9 +882,6 @@ def main():
     if args.chunk_attention_steps > 0:
         print("[bench] timing attention over chunks read in place", file=sys.stderr, flush=True)
         out["chunk_attention"] = chunk_attention_leg(args.chunk_attention_steps, stream)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

@@ -28,19 +28,31 @@
  * Memory. Every tensor pointer in these structs is device memory owned by the caller. The
  * structs themselves and the chunk array are host memory, read only during the call. The
  * library never allocates device memory: the caller passes a workspace of at least
- * kamera_workspace_bytes(n_chunks) bytes (device memory, 256-byte aligned).
+ * kamera_workspace_bytes(n_chunks) bytes (device memory, 256-byte aligned), into which each
+ * call copies its job table.
+ *
+ * Staging. That copy starts from a per-device ring of pinned host memory (32 MiB, 256 calls in
+ * flight), the library's only allocation: made once per device by kamera_init(), or by the
+ * first compute call on a device that was not initialised. A compute call never allocates or
+ * frees after that and never blocks the host: when every ring region it could use still feeds
+ * a copy the device has not reached, it returns KAMERA_ERR_BUSY having enqueued nothing
+ * (synchronise the stream, or let it progress, and call again). A table larger than the ring
+ * (a batch of more than ~70,000 chunks) is KAMERA_ERR_UNSUPPORTED.
  *
  * Streams. The compute calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  * and return without synchronising. A device fault surfaces at the caller's next sync. The
  * workspace must not be reused by another call until this call's work has finished on the
- * stream (calls on one stream serialise by themselves).
+ * stream (calls on one stream serialise by themselves). A stream that is being captured into
+ * a graph is rejected (KAMERA_ERR_UNSUPPORTED): the captured copy would replay from a ring
+ * region that later calls reuse.
  *
  * Errors. Compute calls validate every argument on the host before anything is enqueued; on
  * any error they return a status != KAMERA_OK, enqueue nothing, and set a per-thread message
  * readable with kamera_last_error(). No C++ exception crosses this ABI.
  *
- * Thread safety. Calls are reentrant; the only mutable global state is the per-thread error
- * message.
+ * Thread safety. Calls are reentrant. Mutable global state: the per-thread error message and
+ * the per-device staging rings (each guarded by its own mutex, held only while a call claims a
+ * region; kept until the process ends).
  */
 #ifndef KAMERA_H_
 #define KAMERA_H_
@@ -52,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KAMERA_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define KAMERA_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 typedef enum kamera_status {
   KAMERA_OK = 0,
@@ -60,7 +72,8 @@ typedef enum kamera_status {
   KAMERA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (dtype, head width, m > 256) */
   KAMERA_ERR_OVERLAP = 3,          /* a chunk's source range overlaps the destination pool */
   KAMERA_ERR_WORKSPACE = 4,        /* workspace missing, misaligned or too small */
-  KAMERA_ERR_HIP = 5               /* a HIP runtime call failed (message holds its text) */
+  KAMERA_ERR_HIP = 5,              /* a HIP runtime call failed (message holds its text) */
+  KAMERA_ERR_BUSY = 6              /* every staging region is still in flight; nothing enqueued */
 } kamera_status;
 
 typedef enum kamera_family {
@@ -172,6 +185,11 @@ typedef struct kamera_chunk {
   kamera_src src[2];         /* per channel */
   kamera_patch_ref patch[2]; /* per channel */
 } kamera_chunk;
+
+/* Sets up the current device's staging ring (see "Staging" above). Idempotent; returns
+ * KAMERA_ERR_HIP if the pinned allocation fails. Call it once per device before timed or
+ * latency-critical work so that no compute call makes the allocation. */
+kamera_status kamera_init(void);
 
 /* Bytes of workspace the compute calls need for n_chunks chunks (0 if n_chunks < 0). */
 size_t kamera_workspace_bytes(int32_t n_chunks);

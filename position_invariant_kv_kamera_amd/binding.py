@@ -23,6 +23,7 @@ KAMERA_ERR_UNSUPPORTED = 2
 KAMERA_ERR_OVERLAP = 3
 KAMERA_ERR_WORKSPACE = 4
 KAMERA_ERR_HIP = 5
+KAMERA_ERR_BUSY = 6
 
 FAMILY = {"gqa": 0, "mla": 1}
 DTYPE = {"f32": 0, "bf16": 1}
@@ -122,6 +123,8 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = compute
         fn.restype = ctypes.c_int
+    lib.kamera_init.argtypes = []
+    lib.kamera_init.restype = ctypes.c_int
     lib.kamera_workspace_bytes.argtypes = [c_i32]
     lib.kamera_workspace_bytes.restype = c_size
     lib.kamera_read_fault_count.argtypes = [c_vp, c_vp, ctypes.POINTER(ctypes.c_uint32)]
@@ -187,6 +190,10 @@ class KameraError(RuntimeError):
 
 
 # ---- the C calls, same names -----------------------------------------------------------
+
+def kamera_init() -> int:
+    return int(load_library().kamera_init())
+
 
 def kamera_workspace_bytes(n_chunks: int) -> int:
     return int(load_library().kamera_workspace_bytes(n_chunks))

@@ -401,6 +401,11 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
 
 extern "C" {
 
+kamera_status kamera_init(void) {
+  clear_error();
+  return init_current_device();
+}
+
 size_t kamera_workspace_bytes(int32_t n_chunks) {
   if (n_chunks < 0) return 0;
   // up to three jobs per chunk: channel 0 (two when a key head is partially rotary), channel 1
@@ -467,6 +472,7 @@ const char* kamera_status_string(kamera_status status) {
     case KAMERA_ERR_OVERLAP: return "source overlaps destination";
     case KAMERA_ERR_WORKSPACE: return "workspace missing or too small";
     case KAMERA_ERR_HIP: return "HIP runtime error";
+    case KAMERA_ERR_BUSY: return "staging ring busy";
   }
   return "unknown status";
 }

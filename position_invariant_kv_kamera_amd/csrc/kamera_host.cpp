@@ -1,7 +1,7 @@
 // kamera_host.cpp — host helpers shared by every entry point of libkamera.so: the per-thread
 // error message, model and cache validation, view ranges, and the pinned staging ring that
 // copies job tables into the caller's workspace.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
@@ -149,59 +149,132 @@ kamera_status validate_cache(const kamera_model& m, const kamera_cache* c) {
 }
 
 // ---------------------------------------------------------------------------------------
-// pinned staging ring for the job table (host -> workspace copy)
+// pinned staging ring for the job tables (host -> workspace copies)
 // ---------------------------------------------------------------------------------------
+//
+// One ring per device, set up once (kamera_init, or the first compute call on the device):
+// kStagingBytes of pinned host memory and kMaxInFlight events. Every call copies its table
+// into the next free region of the ring and enqueues one hipMemcpyAsync from there, followed by
+// an event. A region is handed out again only once its event has completed, which is checked
+// with hipEventQuery and never waited for: when the regions a call needs are all still in
+// flight the call fails with KAMERA_ERR_BUSY and enqueues nothing. After set-up nothing here
+// allocates or frees, and nothing blocks the host.
 
-struct StagingSlot {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
-};
-
-struct DeviceRing {
+struct Ring {
   std::mutex mu;
-  StagingSlot slot[4];
-  unsigned next = 0;
+  bool ready = false;
+  uint8_t* host = nullptr;
+  hipEvent_t ev[kMaxInFlight];
+  size_t lo[kMaxInFlight], hi[kMaxInFlight];  // byte range of each in-flight entry
+  int first = 0, count = 0;                   // FIFO of in-flight entries
+  size_t head = 0;                            // where the next region starts
 };
 
-DeviceRing* ring_for(int device) {
-  static DeviceRing rings[64];   // process lifetime; never torn down (no exit-time HIP calls)
-  return (device >= 0 && device < 64) ? &rings[device] : nullptr;
+Ring* ring_for(int device) {
+  static Ring rings[kMaxDevices];   // process lifetime; never torn down (no exit-time HIP calls)
+  return (device >= 0 && device < kMaxDevices) ? &rings[device] : nullptr;
 }
 
-kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream) {
+namespace {
+
+// Allocates the ring of the current device (caller holds r.mu).
+kamera_status ring_setup(Ring& r) {
+  if (r.ready) return KAMERA_OK;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, kStagingBytes, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipHostMalloc: %s", hipGetErrorString(e));
+  for (int i = 0; i < kMaxInFlight; ++i) {
+    e = hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int k = 0; k < i; ++k) (void)hipEventDestroy(r.ev[k]);
+      (void)hipHostFree(h);
+      return fail(KAMERA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  r.host = static_cast<uint8_t*>(h);
+  r.first = r.count = 0;
+  r.head = 0;
+  r.ready = true;
+  return KAMERA_OK;
+}
+
+kamera_status current_ring(Ring** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  DeviceRing* ring = ring_for(dev);
-  if (!ring) return fail(KAMERA_ERR_UNSUPPORTED, "device index %d out of range", dev);
-  std::lock_guard<std::mutex> lock(ring->mu);
-  StagingSlot& s = ring->slot[ring->next++ % 4];
-  if (s.pending) {
-    e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
-    s.pending = false;
+  Ring* r = ring_for(dev);
+  if (!r) return fail(KAMERA_ERR_UNSUPPORTED, "device index %d is not below %d", dev, kMaxDevices);
+  *out = r;
+  return KAMERA_OK;
+}
+
+}  // namespace
+
+kamera_status init_current_device() {
+  Ring* r = nullptr;
+  kamera_status st = current_ring(&r);
+  if (st != KAMERA_OK) return st;
+  std::lock_guard<std::mutex> lock(r->mu);
+  return ring_setup(*r);
+}
+
+kamera_status check_stream(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(KAMERA_ERR_UNSUPPORTED,
+                "the stream is being captured: a captured call would replay a copy from a "
+                "staging region later calls reuse");
+  return KAMERA_OK;
+}
+
+kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream) {
+  const size_t n = bytes.size();
+  if (n > kStagingBytes)
+    return fail(KAMERA_ERR_UNSUPPORTED,
+                "a table of %zu bytes exceeds the staging ring (%zu bytes): split the batch", n,
+                kStagingBytes);
+  kamera_status st = check_stream(stream);
+  if (st != KAMERA_OK) return st;
+  Ring* r = nullptr;
+  st = current_ring(&r);
+  if (st != KAMERA_OK) return st;
+  std::lock_guard<std::mutex> lock(r->mu);
+  st = ring_setup(*r);
+  if (st != KAMERA_OK) return st;
+  // retire the entries whose copies have completed (oldest first)
+  while (r->count > 0) {
+    const hipError_t q = hipEventQuery(r->ev[r->first]);
+    if (q == hipErrorNotReady) break;
+    if (q != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventQuery: %s", hipGetErrorString(q));
+    r->first = (r->first + 1) % kMaxInFlight;
+    --r->count;
   }
-  if (!s.done) {
-    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  if (r->count == 0) r->head = 0;
+  size_t lo = r->head;
+  if (lo + n > kStagingBytes) lo = 0;   // wrap: regions are contiguous
+  const size_t hi = lo + n;
+  bool clash = r->count == kMaxInFlight;
+  for (int k = 0; k < r->count && !clash; ++k) {
+    const int i = (r->first + k) % kMaxInFlight;
+    clash = lo < r->hi[i] && r->lo[i] < hi;
   }
-  if (s.cap < bytes.size()) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    const size_t cap = round_up(bytes.size(), size_t(1) << 16);
-    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipHostMalloc: %s", hipGetErrorString(e));
-    s.cap = cap;
-  }
-  std::memcpy(s.host, bytes.data(), bytes.size());
-  e = hipMemcpyAsync(workspace, s.host, bytes.size(), hipMemcpyHostToDevice, stream);
+  if (clash)
+    return fail(KAMERA_ERR_BUSY,
+                "the staging ring holds the tables of %d calls the device has not reached; "
+                "synchronise the stream (or wait) and call again",
+                r->count);
+  std::memcpy(r->host + lo, bytes.data(), n);
+  hipError_t e = hipMemcpyAsync(workspace, r->host + lo, n, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-  e = hipEventRecord(s.done, stream);
+  const int slot = (r->first + r->count) % kMaxInFlight;
+  e = hipEventRecord(r->ev[slot], stream);
   if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  s.pending = true;
+  r->lo[slot] = lo;
+  r->hi[slot] = hi;
+  ++r->count;
+  r->head = round_up(hi, 256);
   return KAMERA_OK;
 }
 

@@ -2,7 +2,7 @@
 // public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 #include "../../include/kamera.h"
@@ -34,7 +34,18 @@ Range view_range(const void* p, int64_t ls, int64_t n_layers, int64_t ts, int64_
 bool overlaps(const Range& a, const Range& b);
 kamera_status validate_model(const kamera_model* m);
 kamera_status validate_cache(const kamera_model& m, const kamera_cache* c);
-// Copies `bytes` into the device workspace through a pinned staging ring, on `stream`.
+// Staging ring of one device: pinned host bytes and the most calls whose copies may be in
+// flight at once.
+constexpr size_t kStagingBytes = size_t(32) << 20;
+constexpr int kMaxInFlight = 256;
+constexpr int kMaxDevices = 64;
+// Sets up the current device's staging ring (the library's one allocation; idempotent).
+kamera_status init_current_device();
+// KAMERA_ERR_UNSUPPORTED when `stream` is being captured into a graph.
+kamera_status check_stream(hipStream_t stream);
+// Copies `bytes` into the device workspace through the current device's staging ring, on
+// `stream` (sets the ring up on first use). Never allocates after set-up and never waits:
+// KAMERA_ERR_BUSY when every region it could use is still in flight.
 kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream);
 int env_int(const char* name, int dflt);
 

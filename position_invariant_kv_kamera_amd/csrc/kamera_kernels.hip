@@ -653,9 +653,12 @@ __global__ __launch_bounds__(kBlockThreads) void kamera_valu_kernel(const Launch
     const KGLOBAL T* in = P.mode == MODE_PATCH ? out
                                        : src + layer * J.src_ls + (int64_t)t * J.src_ts +
                                              (int64_t)head * J.head_stride;
-    if (!rotate && m == 0) {   // bit copy
-      out[fa] = in[fa];
-      out[fb] = in[fb];
+    if (!rotate && m == 0) {   // bit copy through an integer type of the element's width
+      using Bits = std::conditional_t<sizeof(T) == 4, uint32_t, uint16_t>;
+      const KGLOBAL Bits* ib = reinterpret_cast<const KGLOBAL Bits*>(in);
+      KGLOBAL Bits* ob = reinterpret_cast<KGLOBAL Bits*>(out);
+      ob[fa] = ib[fa];
+      ob[fb] = ib[fb];
       continue;
     }
     float xa = ld<T>(in + fa), xb = ld<T>(in + fb);

@@ -30,8 +30,8 @@ def test_every_header_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kb.kamera_version() == 10200
-    for st in range(6):
+    assert kb.kamera_version() == 10300
+    for st in range(7):
         assert kb.kamera_status_string(st) not in ("", "unknown status")
     assert kb.kamera_status_string(99) == "unknown status"
 

@@ -61,9 +61,7 @@ def test_full_size_sampled_rows_and_properties(name):
     kb.run_batch("reuse", batch)
     torch.cuda.synchronize()
     rep = sample_rows(batch, 1500, seed=11)
-    print(f"[kamera] sampled: {rep.elements} elements fail={rep.float_fail} "
-          f"copy_mismatch={rep.copy_mismatches} cancel={rep.cancel} max_ulp={rep.max_ulp:.3f} "
-          f"max_err/S={rep.max_rel_s:.2e}", flush=True)
+    print(f"[kamera] sampled: {rep.line()}", flush=True)
     assert rep.ok, rep.details
     assert count_sentinel_damage(batch) == 0
     if p.dtype == "bf16":

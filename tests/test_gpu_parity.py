@@ -37,9 +37,7 @@ def run(op, batch, **kw):
 
 
 def assert_report(rep, label):
-    print(f"[kamera] {label}: {rep.elements} elements, {rep.copies} copied, "
-          f"fail={rep.float_fail} copy_mismatch={rep.copy_mismatches} sentinel_bad={rep.sentinel_bad} "
-          f"cancel={rep.cancel} max_ulp={rep.max_ulp:.3f} max_err/S={rep.max_rel_s:.2e}", flush=True)
+    print(f"[kamera] {label}: {rep.line()}", flush=True)
     assert rep.ok, rep.details
 
 
