@@ -204,6 +204,23 @@ kamera_status kamera_reuse_batch(const kamera_model* model, const kamera_cache* 
                                  const kamera_chunk* chunks, int32_t n_chunks, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* kamera_reuse_batch for callers that cannot allocate (code that must not call hipMalloc or
+ * hipFree: tight serving loops, harnesses that forbid allocation). Same validation, kernels and
+ * results (bit for bit), but no workspace argument: the job tables go to a device array of
+ * fixed size inside the library, one per GPU, kept until the process ends. The call allocates
+ * nothing and frees nothing, and never blocks the host (KAMERA_ERR_BUSY as for the other
+ * calls).
+ *   Needs kamera_init() on the current device first (it locates the array and sets up the
+ *   staging ring); otherwise KAMERA_ERR_UNSUPPORTED and nothing is enqueued.
+ *   Limit: 1932 chunks per call (1 MiB of tables); more is KAMERA_ERR_UNSUPPORTED.
+ *   Every call on one GPU reuses that GPU's array: calls whose work may overlap on the device
+ *   (different streams with no ordering between them) race; calls on one stream are ordered.
+ *   Rows skipped for an out-of-range page-table entry are counted in the array and are not
+ *   readable (kamera_read_fault_count reads a caller's workspace). */
+kamera_status kamera_reuse_batch_noalloc(const kamera_model* model, const kamera_cache* cache,
+                                         const kamera_chunk* chunks, int32_t n_chunks,
+                                         void* stream);
+
 /* Relocation only, R(delta) with no patch (patch fields are ignored). Bit-identical to
  * kamera_reuse_batch with every m set to 0; channel 1 is then an exact bit copy. */
 kamera_status kamera_relocate(const kamera_model* model, const kamera_cache* cache,

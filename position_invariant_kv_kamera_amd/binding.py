@@ -123,6 +123,10 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = compute
         fn.restype = ctypes.c_int
+    lib.kamera_reuse_batch_noalloc.argtypes = [ctypes.POINTER(KameraModel),
+                                                ctypes.POINTER(KameraCache),
+                                                ctypes.POINTER(KameraChunk), c_i32, c_vp]
+    lib.kamera_reuse_batch_noalloc.restype = ctypes.c_int
     lib.kamera_init.argtypes = []
     lib.kamera_init.restype = ctypes.c_int
     lib.kamera_workspace_bytes.argtypes = [c_i32]
@@ -209,6 +213,12 @@ def _compute(name, model, cache, chunks, n_chunks, workspace, workspace_bytes, s
 def kamera_reuse_batch(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):
     return _compute("kamera_reuse_batch", model, cache, chunks, n_chunks, workspace,
                     workspace_bytes, stream)
+
+
+def kamera_reuse_batch_noalloc(model, cache, chunks, n_chunks, stream):
+    return int(load_library().kamera_reuse_batch_noalloc(
+        ctypes.byref(model) if model is not None else None,
+        ctypes.byref(cache) if cache is not None else None, chunks, int(n_chunks), stream))
 
 
 def kamera_relocate(model, cache, chunks, n_chunks, workspace, workspace_bytes, stream):

@@ -12,8 +12,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkamera.so"
-SOURCES = [CSRC / "kamera_host.cpp", CSRC / "kamera_api.cpp", CSRC / "kamera_kernels.hip", CSRC / "kamera_compile.hip",
-           CSRC / "kamera_attention.hip"]
+SOURCES = [CSRC / "kamera_host.cpp", CSRC / "kamera_api.cpp", CSRC / "kamera_kernels.hip",
+           CSRC / "kamera_noalloc.hip", CSRC / "kamera_compile.hip", CSRC / "kamera_attention.hip"]
 ARCH = os.environ.get("KAMERA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -295,9 +295,12 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
   return KAMERA_OK;
 }
 
+// The reuse path: validation, planning, table upload and launches. The device tables go to
+// `workspace` (the caller's, or the no-allocation entry point's static scratch); with
+// allow_setup false the upload refuses to set up a staging ring that kamera_init() did not.
 kamera_status run(const kamera_model* model, const kamera_cache* cache, const kamera_chunk* chunks,
                   int32_t n_chunks, void* workspace, size_t workspace_bytes, void* stream_ptr,
-                  Op op) {
+                  Op op, bool allow_setup = true) {
   clear_error();
   kamera_status st = validate_model(model);
   if (st != KAMERA_OK) return st;
@@ -340,7 +343,7 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
     std::memcpy(staging.data() + kSectionOffset, model->pair_section, pairs);
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  st = upload(staging, workspace, stream);
+  st = upload(staging, workspace, stream, allow_setup);
   if (st != KAMERA_OK) return st;
 
   LaunchParams lp;
@@ -399,11 +402,20 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
 
 }  // namespace
 
+namespace kamera {
+kamera_status reuse_batch_tables_at(const kamera_model* model, const kamera_cache* cache,
+                                    const kamera_chunk* chunks, int32_t n_chunks, void* tables,
+                                    size_t tables_bytes, void* stream) {
+  return run(model, cache, chunks, n_chunks, tables, tables_bytes, stream, Op::Reuse, false);
+}
+}  // namespace kamera
+
 extern "C" {
 
 kamera_status kamera_init(void) {
   clear_error();
-  return init_current_device();
+  const kamera_status st = init_current_device();
+  return st != KAMERA_OK ? st : kamera::scratch_setup();
 }
 
 size_t kamera_workspace_bytes(int32_t n_chunks) {

@@ -229,7 +229,8 @@ kamera_status check_stream(hipStream_t stream) {
   return KAMERA_OK;
 }
 
-kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream) {
+kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream,
+                     bool allow_setup) {
   const size_t n = bytes.size();
   if (n > kStagingBytes)
     return fail(KAMERA_ERR_UNSUPPORTED,
@@ -241,6 +242,10 @@ kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStre
   st = current_ring(&r);
   if (st != KAMERA_OK) return st;
   std::lock_guard<std::mutex> lock(r->mu);
+  if (!r->ready && !allow_setup)
+    return fail(KAMERA_ERR_UNSUPPORTED,
+                "kamera_init() has not been called on this device (this call allocates nothing, "
+                "so it cannot set up the staging ring)");
   st = ring_setup(*r);
   if (st != KAMERA_OK) return st;
   // retire the entries whose copies have completed (oldest first)

@@ -44,9 +44,11 @@ kamera_status init_current_device();
 // KAMERA_ERR_UNSUPPORTED when `stream` is being captured into a graph.
 kamera_status check_stream(hipStream_t stream);
 // Copies `bytes` into the device workspace through the current device's staging ring, on
-// `stream` (sets the ring up on first use). Never allocates after set-up and never waits:
+// `stream` (sets the ring up on first use when allow_setup, else KAMERA_ERR_UNSUPPORTED if
+// kamera_init() has not run on the device). Never allocates after set-up and never waits:
 // KAMERA_ERR_BUSY when every region it could use is still in flight.
-kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream);
+kamera_status upload(const std::vector<uint8_t>& bytes, void* workspace, hipStream_t stream,
+                     bool allow_setup = true);
 int env_int(const char* name, int dflt);
 
 }  // namespace host

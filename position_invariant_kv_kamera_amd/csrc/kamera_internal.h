@@ -122,4 +122,13 @@ hipError_t launch_mfma(const LaunchParams& p, int win_width, int kmode, hipStrea
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_valu(const LaunchParams& p, int dtype, hipStream_t stream);
 
+// kamera_reuse_batch with its device tables at `tables` (tables_bytes long, 256-byte aligned)
+// and no staging set-up (kamera_api.cpp).
+kamera_status reuse_batch_tables_at(const kamera_model* model, const kamera_cache* cache,
+                                    const kamera_chunk* chunks, int32_t n_chunks, void* tables,
+                                    size_t tables_bytes, void* stream);
+// Looks up this device's copy of the no-allocation entry point's scratch array (once per
+// device; kamera_noalloc.hip). Called by kamera_init().
+kamera_status scratch_setup();
+
 }  // namespace kamera

@@ -129,7 +129,14 @@ hipError_t hipStreamSynchronize(hipStream_t) {
 const char* hipGetErrorString(hipError_t) { return "mock error"; }
 }
 
+namespace mock {
+int scratch_setups = 0;
+}
 namespace kamera {
+kamera_status scratch_setup() {   // the no-allocation entry point's symbol lookup
+  ++mock::scratch_setups;
+  return KAMERA_OK;
+}
 hipError_t launch_mfma(const LaunchParams& p, int win_width, int kmode, hipStream_t) {
   ++mock::launches;
   mock::last_launch = p;
@@ -237,6 +244,7 @@ int main() {
   CHECK(kamera_init() == KAMERA_OK);
   CHECK(mock::host_mallocs == 1);
   CHECK(mock::event_creates == 256);
+  CHECK(mock::scratch_setups == 1);
   CHECK(kamera_init() == KAMERA_OK);
   CHECK(mock::host_mallocs == 1 && mock::event_creates == 256);
 
@@ -349,6 +357,22 @@ int main() {
     CHECK(fx.reuse(c, wsb, stream) == KAMERA_OK);
     CHECK(mock::host_mallocs == 2 && mock::event_creates == 512);
     mock::device = 0;
+  }
+
+  // the no-allocation path never sets a ring up: on a device kamera_init() has not seen it is
+  // refused with nothing allocated or enqueued
+  {
+    mock::device = 2;
+    auto c = fx.chunks(2, 16);
+    const int mallocs0 = mock::host_mallocs, copies0 = mock::memcpys, launches0 = mock::launches;
+    CHECK(kamera::reuse_batch_tables_at(&fx.model, &fx.cache, c.data(), 2, fx.ws_ptr, wsb,
+                                        stream) == KAMERA_ERR_UNSUPPORTED);
+    CHECK(mock::host_mallocs == mallocs0 && mock::memcpys == copies0 &&
+          mock::launches == launches0);
+    mock::device = 0;
+    CHECK(kamera::reuse_batch_tables_at(&fx.model, &fx.cache, c.data(), 2, fx.ws_ptr, wsb,
+                                        stream) == KAMERA_OK);
+    CHECK(mock::host_mallocs == mallocs0);
   }
 
   // nothing above allocated after set-up, freed, or waited on the host
