@@ -374,8 +374,11 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   for (size_t lo = 0; lo < plan.mfma.size();) {
     size_t hi = lo;
     int max_m = 0;
-    while (hi < plan.mfma.size() && plan.mfma[hi].win_width == plan.mfma[lo].win_width)
+    bool scalar_uv = false;   // a patched job whose U or V rows cannot take 16-byte loads
+    while (hi < plan.mfma.size() && plan.mfma[hi].win_width == plan.mfma[lo].win_width) {
+      scalar_uv |= plan.mfma[hi].m > 0 && !plan.mfma[hi].vec_uv;
       max_m = std::max(max_m, plan.mfma[hi++].m);
+    }
     lp.jobs = reinterpret_cast<const JobDesc*>(ws + mfma_off) + lo;
     lp.block_starts = reinterpret_cast<const int32_t*>(ws + mfma_bs_off) + lo;
     lp.n_jobs = (int32_t)(hi - lo);
@@ -383,7 +386,9 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
     const int64_t last = hi < plan.mfma.size() ? plan.mfma[hi].block_start : plan.mfma_blocks;
     lp.block_base = first;
     lp.total_blocks = (int32_t)(last - first);
-    hipError_t e = kamera::launch_mfma(lp, plan.mfma[lo].win_width, kmode_for(max_m), stream);
+    // the rank-class variants read U and V with 16-byte loads only; the streamed one takes any
+    const int kmode = scalar_uv ? -1 : kmode_for(max_m);
+    hipError_t e = kamera::launch_mfma(lp, plan.mfma[lo].win_width, kmode, stream);
     if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "MFMA kernel launch: %s", hipGetErrorString(e));
     lo = hi;
   }

@@ -276,14 +276,16 @@ __device__ __forceinline__ void load_tile(const LaunchParams& P, const WindowCtx
       in.raw[r] = have ? ld_stream(row + 32 * r + 8 * g) : u32x4{0u, 0u, 0u, 0u};
   }
   if constexpr (K::k16) {
-    in.u16 = (valid && C.m > 0) ? load_k4(C.U + (int64_t)t * C.m, 4 * g, C.m, C.vec_uv)
+    // the rank-class variants only run jobs whose U and V rows take 16-byte loads (the host
+    // sends the others to the streamed variant), so no scalar fallback sits in the tile loop
+    in.u16 = (valid && C.m > 0) ? load_k4(C.U + (int64_t)t * C.m, 4 * g, C.m, 1)
                                 : short4_t{0, 0, 0, 0};
   }
   if constexpr (K::s32 > 0) {
 #pragma unroll
     for (int s = 0; s < K::s32; ++s)
       in.u32[s] = (s < C.steps32 && valid)
-                      ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, C.vec_uv, true)
+                      ? load_k8(C.U + (int64_t)t * C.m, 32 * s + 8 * g, C.m, 1, true)
                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 }
@@ -302,7 +304,7 @@ __device__ __forceinline__ void load_vfrags(const WindowCtx& C, int g, int n, VF
   if constexpr (K::k16) {
 #pragma unroll
     for (int T = 0; T < NT; ++T)
-      vf.a16[T] = load_k4(C.V + (int64_t)tile_row_feature(T, n) * C.m, 4 * g, C.m, C.vec_uv);
+      vf.a16[T] = load_k4(C.V + (int64_t)tile_row_feature(T, n) * C.m, 4 * g, C.m, 1);
   }
   if constexpr (K::s32 > 0) {
 #pragma unroll
@@ -310,7 +312,7 @@ __device__ __forceinline__ void load_vfrags(const WindowCtx& C, int g, int n, VF
 #pragma unroll
       for (int T = 0; T < NT; ++T)
         vf.a32[s][T] = s < C.steps32 ? load_k8(C.V + (int64_t)tile_row_feature(T, n) * C.m,
-                                               32 * s + 8 * g, C.m, C.vec_uv, false)
+                                               32 * s + 8 * g, C.m, 1, false)
                                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 }
