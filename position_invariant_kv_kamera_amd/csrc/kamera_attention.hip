@@ -10,10 +10,17 @@
 // attn_segment_kernel<D>: block = (segment, KV head), 4 waves; wave w takes the 16-token
 //   tiles w, w+4, ... of the segment. Per tile: S = Q K^T with v_mfma_f32_16x16x32_bf16 (the
 //   query heads of the KV head are the 16 MFMA rows, padded; q and k are bf16 already, so
-//   the products are exact), online softmax per query row (max and sum across the 16 lanes
-//   that hold a row), then O += P V with v_mfma_f32_16x16x4_f32 (P stays fp32; the V tile
-//   passes through LDS as bf16). The four waves' states are merged in LDS and the segment's
-//   normalised output and lse are written to the workspace.
+//   the products are exact), online softmax per query row in base 2 (max and sum across the
+//   16 lanes that hold a row, by DPP row operations), then O += P V on
+//   v_mfma_f32_16x16x16_bf16: each fp32 weight is cut exactly into three bf16 terms (hi by
+//   truncation, mid = trunc(p - hi), lo = p - hi - mid), so every product is exact and the sum
+//   keeps fp32 weights; the V tile passes through LDS as bf16. The four waves' states are
+//   merged in LDS and the segment's normalised output and lse are written to the workspace.
+// mla_segment_kernel: the same over an MLA cache in the absorbed form; the four waves split
+//   the 512 latent features, wave 0 also takes k_rope. The k_rope score MFMA is issued by the
+//   compiler for every wave under wave 0's condition (an empty exec mask elsewhere), and an MFMA
+//   still reads its operands then, so the other waves keep their k_rope operand registers at
+//   zero (stale -inf there once turned 0 x -inf into NaN scores).
 // attn_merge_kernel: one block per (query, query head) merges its segments.
 // state_merge_kernel: the same merge over caller-given parts.
 #include <hip/hip_runtime.h>
