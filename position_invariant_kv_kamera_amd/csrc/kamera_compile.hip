@@ -122,7 +122,7 @@ __device__ __forceinline__ int find_entry(const CParams& P, int b) {
 // is that of the pair's position component (multimodal sections), else the chunk's.
 // With several orderings (an orbit) the table holds the mean of their cos and sin: the mean
 // of the rotations R(delta_k) acts on each pair as [[cbar, -sbar], [sbar, cbar]].
-__device__ void fill_phases(float2* cs, const CJob& J, const CParams& P) {
+__device__ __forceinline__ void fill_phases(float2* cs, const CJob& J, const CParams& P) {
   const int rot_dim = J.rot_dim;
   const CMember* mem = P.members + J.member_off;
   for (int i = threadIdx.x; i < rot_dim / 2; i += kThreads) {
@@ -188,7 +188,7 @@ __device__ __forceinline__ void load_cond8(const CMember* mem, int n_members, in
 // rot_dim features, the others pass through. With several orderings Delta is their mean:
 // mean conditioned rows minus the mean rotation (cs) applied to the canonical rows.
 template <typename T, int ROWS>
-__device__ void stage_delta(const CJob& J, const CParams& P, const float2* cs, int layer,
+__device__ __forceinline__ void stage_delta(const CJob& J, const CParams& P, const float2* cs, int layer,
                             int head, int tok0, int tok_end, int col0, int ncols, float* dst,
                             int ds) {
   const int layout = P.layout;
@@ -684,18 +684,74 @@ __device__ __forceinline__ int lidx(int r, int c) {
 // (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
 // (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
-__device__ void cholesky_wave(double* lm, double* inv, int* dead, int m, double* scratch) {
+__device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead, int m,
+                                              double* scratch) {
   static_assert(MP % 16 == 0 && MP <= 64, "rank classes are 16, 32, 48 and 64");
   const int lane = threadIdx.x & 63;
-  if constexpr (MP <= 32 || MP == 64) {
+  if constexpr (MP == 64) {
+    // Rank 64, in registers, as a loop whose body is the same for every step: lane ri holds
+    // row ri of S, and its registers shift left by one column per step, so the pivot column j
+    // is always sv[0] and every register index is static. Step j: the pivot comes from lane j
+    // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
+    // lane ri scales its entry of column j, stores it as L[ri][j] and publishes it in `scratch`
+    // (128 entries, zero past the rows that have one), then updates the rest of its row as
+    // s_r,j+c -= l_rj l_j+c,j while shifting it. The operations and their order are those of
+    // the other register form, so L comes out bit for bit the same; entries right of the
+    // diagonal are updated too and never read.
+    const int ri = lane;
+    double sv[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c)
+      sv[c] = (ri < m && c < m) ? (ri >= c ? lm[lidx<64>(ri, c)] : lm[lidx<64>(c, ri)]) : 0.0;
+    scratch[64 + ri] = 0.0;   // colj[j + c] past row 63 reads zeros
+    wave_lds_sync();
+#pragma unroll 1
+    for (int j = 0; j < m; ++j) {
+      const uint64_t pb = __builtin_bit_cast(uint64_t, sv[0]);
+      const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, j);
+      const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), j);
+      const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
+      const double s0 = lm[lidx<64>(j, j)];   // s_jj before elimination (not yet overwritten)
+      const bool dk = d <= kDeadTol * s0;
+      const double ljj = dk ? 0.0 : sqrt(d);
+      const double iv = dk ? 0.0 : 1.0 / ljj;
+      if (lane == 0) {
+        inv[j] = iv;
+        dead[j] = dk ? 1 : 0;
+      }
+      const double v = ri == j ? ljj : (ri > j ? sv[0] * iv : sv[0]);
+      const double lij = ri > j && ri < m ? v : 0.0;
+      scratch[ri] = lij;
+      wave_lds_sync();   // every lane has read s_jj before lane j stores l_jj over it
+      if (ri >= j && ri < m) lm[lidx<64>(ri, j)] = v;
+      // the column's entries below the pivot, all loaded before they are used (read one at a
+      // time next to their use, each LDS read would wait for the one before)
+      const double2* colj = reinterpret_cast<const double2*>(scratch + j + 1 - ((j + 1) & 1));
+      double cv[64];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const double2 w = colj[q];
+        cv[2 * q] = w.x;
+        cv[2 * q + 1] = w.y;
+      }
+      // cv[k] holds scratch[j + 1 + k], or scratch[j + k] when j + 1 is odd (16-byte reads)
+      if ((j + 1) & 1) {
+#pragma unroll
+        for (int c = 1; c < 64; ++c) sv[c - 1] = sv[c] - lij * cv[c];
+      } else {
+#pragma unroll
+        for (int c = 1; c < 64; ++c) sv[c - 1] = sv[c] - lij * cv[c - 1];
+      }
+      sv[63] = 0.0;
+      wave_lds_sync();   // scratch is rewritten by the next step
+    }
+  } else if constexpr (MP <= 32) {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
     // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
     // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
     // the lanes holding column j scale it and publish it in LDS, then each lane updates its
     // own part of the trailing matrix. The same operations in the same order as the LDS
-    // version below, with one LDS round trip per step instead of a chain of them. At MP = 64
-    // a lane holds a whole row (64 doubles) and the published column goes to `scratch` (the
-    // packed triangle has no free upper part).
+    // version below, with one LDS round trip per step instead of a chain of them.
     constexpr int LPR = 64 / MP, CPL = MP / LPR;
     const int ri = lane % MP, cb = lane / MP, c0 = cb * CPL;
     double sv[CPL];
@@ -706,11 +762,8 @@ __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m, double*
                                   : 0.0;
     }
     // the strict upper part of row 0 of the square layout is free until the end
-    double* colj = MP <= 32 ? lm + 1 : scratch;
+    double* colj = lm + 1;
     wave_lds_sync();
-    // at MP = 64 the steps are unrolled, so every register index below is static
-    constexpr int kUnrollSteps = MP == 64 ? 64 : 1;
-#pragma unroll kUnrollSteps
     for (int j = 0; j < MP; ++j) {
       if (j < m) {
         const int jc = j % CPL, jb = j / CPL;
@@ -801,24 +854,29 @@ __device__ void cholesky_wave(double* lm, double* inv, int* dead, int m, double*
 //              fp32 x already formed, as in the per-wave form).
 // ---------------------------------------------------------------------------------------
 
-template <int MMAX>
-__device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
+template <int DMAX, int MMAX>
+__device__ void gx_mfma_block(const float* G, float* xs_generic, int D, int mp) {
+  // X lives in LDS: said explicitly, since the compiler may keep this function out of line
+  // (inlining it costs the 512-wide rank-16 kernel its registers), where a generic pointer
+  // would make every access a FLAT one
+  __attribute__((address_space(3))) float* xs = (__attribute__((address_space(3))) float*)xs_generic;
   constexpr int NCB = MMAX / 16;
+  constexpr int NS = DMAX / 64;   // row blocks per wave (D / 16 of them over 4 waves)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
-  const int nrb = D / 16;   // at most 32: 8 row blocks per wave
+  const int nrb = D / 16;
   const int nt = D / 16;
   const int XS = mp + 1;
-  f32x4 acc[8][NCB];
+  f32x4 acc[NS][NCB];
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[s][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // A = G[16 rb + i][kappa], kappa = 16 t + 4 kk + u; B = X[kappa][16 cb + i]
   const float* grow = G + (int64_t)li * D + 4 * kk;
-  f32x4 ga[8];
+  f32x4 ga[NS];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int rb = wave + 4 * s;
     ga[s] = rb < nrb ? ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D))[0]
                      : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -835,13 +893,13 @@ __device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int s = 0; s < NS; ++s)
         if (wave + 4 * s < nrb)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
             acc[s][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[s][u], bv[u][cb], acc[s][cb], 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const int rb = wave + 4 * s;
       if (rb < nrb) ga[s] = ((const CGLOBAL f32x4*)(grow + (int64_t)16 * rb * D + 16 * tn))[0];
     }
@@ -849,7 +907,7 @@ __device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
   __syncthreads();   // every wave has read X: Y replaces it
   // lane 16 kk + i holds rows 16 rb + 4 kk + v, columns 16 cb + i
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int rb = wave + 4 * s;
     if (rb < nrb) {
 #pragma unroll
@@ -865,8 +923,8 @@ __device__ void gx_mfma_block(const float* G, float* xs, int D, int mp) {
 // reseed_round >= 0 (the next round's G X spreads it); a collapsed column has l_aj = 0 below
 // its pivot, so a reseeded x_a adds nothing to the columns after it.
 template <int MMAX>
-__device__ void orth_block(float* xs, double* ss, double* inv, int* dead, int D, int m, int mp,
-                           int reseed_round) {
+__device__ __forceinline__ void orth_block(float* xs, double* ss, double* inv, int* dead,
+                                           int D, int m, int mp, int reseed_round) {
   // the square S/L layout and the register factorisation without a separate scratch column
   static_assert(MMAX <= 32, "wide heads take ranks up to 32");
   constexpr int SS = MMAX + 1;
@@ -983,7 +1041,7 @@ void subspace_kernel(CParams P) {
   __syncthreads();
 
   for (int round = 0; round < P.n_iter; ++round) {
-    gx_mfma_block<MMAX>(G, xs, D, mp);
+    gx_mfma_block<DMAX, MMAX>(G, xs, D, mp);
     __syncthreads();
     orth_block<MMAX>(xs, ss, inv, dead, D, m, mp, round);
   }
@@ -1006,7 +1064,7 @@ void subspace_kernel(CParams P) {
 //   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
 //       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
 //   lm  (layout lidx) fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
-//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also an MP-double scratch
+//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also a 2 MP-double scratch
 //       for the register Cholesky's published column.
 // Lane l owns rows l and l + 64.
 // ---------------------------------------------------------------------------------------
@@ -1018,7 +1076,7 @@ __device__ __forceinline__ void wave_global_sync() {
 }
 
 template <int MP>
-__device__ void orth_wave(float* buf, double* lm, double* inv, int* dead, double* scratch, int D,
+__device__ __forceinline__ void orth_wave(float* buf, double* lm, double* inv, int* dead, double* scratch, int D,
                           int m, int reseed_round) {
   constexpr int BS = MP + 4;
   const int lane = threadIdx.x & 63;
@@ -1196,7 +1254,7 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
   __shared__ double lm_s[WPB][lm_size<MP>()];
   __shared__ double inv_s[WPB][MP];
   __shared__ int dead_s[WPB][MP];
-  __shared__ double cj_s[WPB][MP > 32 ? MP : 1];   // published column of the Cholesky (MP 64)
+  __shared__ __align__(16) double cj_s[WPB][MP > 32 ? 2 * MP : 2];   // published column of the Cholesky (MP 64)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = blockIdx.x * WPB + w;
   if (u >= P.n_total) return;   // whole wave; no block-wide barrier follows
