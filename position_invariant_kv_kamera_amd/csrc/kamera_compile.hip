@@ -679,6 +679,9 @@ template <int MP>
 __device__ __forceinline__ int lidx(int r, int c) {
   return MP <= 32 ? r * (MP + 1) + c : r * (r + 1) / 2 + c;
 }
+// L of rank class 64 after the factorisation: packed by columns (column c holds rows c..63,
+// zero from row m on), followed by 64 doubles of padding that 16-byte column reads may touch.
+__device__ __forceinline__ int lcol64(int r, int c) { return c * 64 - c * (c - 1) / 2 + (r - c); }
 
 // Cholesky factor of S in place, by one wave (wave-synchronous): lm holds S's lower triangle
 // (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
@@ -695,15 +698,19 @@ __device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead
     // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
     // lane ri scales its entry of column j, stores it as L[ri][j] and publishes it in `scratch`
     // (128 entries, zero past the rows that have one), then updates the rest of its row as
-    // s_r,j+c -= l_rj l_j+c,j while shifting it. The operations and their order are those of
-    // the other register form, so L comes out bit for bit the same; entries right of the
-    // diagonal are updated too and never read.
+    // s_r,j+c -= l_rj l_j+c,j (one fused multiply-add each) while shifting it; entries right
+    // of the diagonal are updated too and never read. L is stored column-major (lcol64), the
+    // layout the rank-64 forward substitution reads; S's diagonal waits in `inv`.
     const int ri = lane;
     double sv[64];
 #pragma unroll
     for (int c = 0; c < 64; ++c)
       sv[c] = (ri < m && c < m) ? (ri >= c ? lm[lidx<64>(ri, c)] : lm[lidx<64>(c, ri)]) : 0.0;
+    // s_jj before elimination, read at step j just before 1 / l_jj replaces it
+    const double sdiag = ri < m ? lm[lidx<64>(ri, ri)] : 0.0;
     scratch[64 + ri] = 0.0;   // colj[j + c] past row 63 reads zeros
+    wave_lds_sync();          // S is in registers: L may now overwrite it
+    inv[ri] = sdiag;
     wave_lds_sync();
 #pragma unroll 1
     for (int j = 0; j < m; ++j) {
@@ -711,7 +718,7 @@ __device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead
       const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, j);
       const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), j);
       const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
-      const double s0 = lm[lidx<64>(j, j)];   // s_jj before elimination (not yet overwritten)
+      const double s0 = inv[j];
       const bool dk = d <= kDeadTol * s0;
       const double ljj = dk ? 0.0 : sqrt(d);
       const double iv = dk ? 0.0 : 1.0 / ljj;
@@ -722,25 +729,28 @@ __device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead
       const double v = ri == j ? ljj : (ri > j ? sv[0] * iv : sv[0]);
       const double lij = ri > j && ri < m ? v : 0.0;
       scratch[ri] = lij;
-      wave_lds_sync();   // every lane has read s_jj before lane j stores l_jj over it
-      if (ri >= j && ri < m) lm[lidx<64>(ri, j)] = v;
-      // the column's entries below the pivot, all loaded before they are used (read one at a
-      // time next to their use, each LDS read would wait for the one before)
-      const double2* colj = reinterpret_cast<const double2*>(scratch + j + 1 - ((j + 1) & 1));
-      double cv[64];
+      // L column-major (column j from its diagonal down, zero past row m - 1)
+      if (ri >= j) lm[lcol64(ri, j)] = ri < m ? v : 0.0;
+      wave_lds_sync();
+      // the column's entries below the pivot, 16 at a time, the next 16 in flight while the
+      // current ones are used (read one at a time next to their use, each LDS read would wait
+      // for the one before; read all at once, the row and the column would not fit in the
+      // 256 registers a VALU instruction can address)
+      const double* colj = scratch + j;
+      double cv[2][16];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        const double2 w = colj[q];
-        cv[2 * q] = w.x;
-        cv[2 * q + 1] = w.y;
-      }
-      // cv[k] holds scratch[j + 1 + k], or scratch[j + k] when j + 1 is odd (16-byte reads)
-      if ((j + 1) & 1) {
+      for (int k = 0; k < 16; ++k) cv[0][k] = colj[1 + k];
 #pragma unroll
-        for (int c = 1; c < 64; ++c) sv[c - 1] = sv[c] - lij * cv[c];
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        if (q < 3) {
 #pragma unroll
-        for (int c = 1; c < 64; ++c) sv[c - 1] = sv[c] - lij * cv[c - 1];
+          for (int k = 0; k < 16; ++k) cv[(q + 1) & 1][k] = colj[17 + 16 * q + k];
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int c = 1 + 16 * q + k;
+          if (c < 64) sv[c - 1] = __builtin_fma(-lij, cv[q & 1][k], sv[c]);
+        }
       }
       sv[63] = 0.0;
       wave_lds_sync();   // scratch is rewritten by the next step
@@ -1135,7 +1145,47 @@ __device__ __forceinline__ void orth_wave(float* buf, double* lm, double* inv, i
   // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
   // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
   // pivot, so a reseeded x_ra adds nothing to the columns after it.
-  {
+  if constexpr (MP == 64) {
+    // Right-looking, the sums in registers, one row per lane at a time (rows lane, then
+    // lane + 64): after step j, acc[k] holds sum_{a<=j} x_a l_{j+1+k,a}, fp64 fused
+    // multiply-adds in order of a. Step j forms x_j, then adds x_j times column j of L (from
+    // the column-major L, 16 entries at a time with the next 16 in flight) while shifting the
+    // sums by one column. Reads past column j's last row land in later columns or the padding
+    // and only reach sums past column 63, which are never used.
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int r = lane + 64 * half;
+      const bool on = r < D;
+      float* row = buf + (on ? r : lane) * BS;
+      double acc[64];
+#pragma unroll
+      for (int k = 0; k < 64; ++k) acc[k] = 0.0;
+#pragma unroll 1
+      for (int j = 0; j < m; ++j) {
+        float v = (float)(((double)row[j] - acc[0]) * inv[j]);
+        if (reseed_round >= 0 && dead[j]) v = seed_value(r, j, reseed_round + 1);
+        if (on) row[j] = v;
+        const double x = (double)v;
+        const double* lcol = lm + lcol64(j, j);
+        double lv[2][16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) lv[0][k] = lcol[1 + k];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < 3) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) lv[(q + 1) & 1][k] = lcol[17 + 16 * q + k];
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int c = 16 * q + k;   // acc[c] takes row j + 1 + c of column j
+            if (c < 63) acc[c] = __builtin_fma(x, lv[q & 1][k], acc[c + 1]);
+          }
+        }
+        acc[63] = 0.0;
+      }
+    }
+  } else {
     const int r0 = lane, r1 = lane + 64;
     const bool on0 = r0 < D, on1 = r1 < D;
     float* row0 = buf + r0 * BS;
@@ -1251,7 +1301,7 @@ template <typename T, int MP, int WPB>
 __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspace_wave_kernel(CParams P) {
   constexpr int BS = MP + 4;
   __shared__ __align__(16) float buf_s[WPB][128 * BS];
-  __shared__ double lm_s[WPB][lm_size<MP>()];
+  __shared__ __align__(16) double lm_s[WPB][lm_size<MP>() + (MP == 64 ? 64 : 0)];
   __shared__ double inv_s[WPB][MP];
   __shared__ int dead_s[WPB][MP];
   __shared__ __align__(16) double cj_s[WPB][MP > 32 ? 2 * MP : 2];   // published column of the Cholesky (MP 64)
