@@ -489,27 +489,37 @@ void mla_segment_kernel(AParams P) {
                   VS);
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
   };
-  // the rows of the next tile are in flight while one is computed. The k_rope registers of
-  // waves 1-3 are zero and stay zero: their k_rope MFMA sits under a wave-uniform branch that the
-  // compiler may issue with an empty exec mask, and the MFMA then still runs on its operands.
-  u32x4 lat[KSW], rope[KSR], lat_n[KSW], rope_n[KSR];
+  // the rows of the next two tiles are in flight while one is computed (one tile ahead: 6.7 %
+  // slower; three: past three waves per SIMD). The k_rope registers of waves 1-3 are zero and
+  // stay zero: their k_rope MFMA sits under a wave-uniform branch that the compiler may issue
+  // with an empty exec mask, and the MFMA then still runs on its operands.
+  u32x4 lat[KSW], rope[KSR], lat_n[KSW], rope_n[KSR], lat_nn[KSW], rope_nn[KSR];
 #pragma unroll
-  for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k] = u32x4{0u, 0u, 0u, 0u};
+  for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k] = rope_nn[k] = u32x4{0u, 0u, 0u, 0u};
   // page-table entries are fetched one tile ahead of the rows they locate
   int64_t row = row_of(t_lo, entry_of(t_lo));
-  int32_t pe_n = entry_of(t_lo + kTile);
+  int64_t row_n = row_of(t_lo + kTile, entry_of(t_lo + kTile));
+  int32_t pe_nn = entry_of(t_lo + 2 * kTile);
   load_tile(row, lat, rope);
+  load_tile(row_n, lat_n, rope_n);
   int it = 0;
   for (int t0 = t_lo; t0 < t_hi; t0 += kTile, ++it) {
-    const int64_t row_n = row_of(t0 + kTile, pe_n);
-    load_tile(row_n, lat_n, rope_n);
-    pe_n = entry_of(t0 + 2 * kTile);
+    const int64_t row_nn = row_of(t0 + 2 * kTile, pe_nn);
+    load_tile(row_nn, lat_nn, rope_nn);
+    pe_nn = entry_of(t0 + 3 * kTile);
     tile_step(row, lat, rope, it);
     row = row_n;
+    row_n = row_nn;
 #pragma unroll
-    for (int k = 0; k < KSW; ++k) lat[k] = lat_n[k];
+    for (int k = 0; k < KSW; ++k) {
+      lat[k] = lat_n[k];
+      lat_n[k] = lat_nn[k];
+    }
 #pragma unroll
-    for (int k = 0; k < KSR; ++k) rope[k] = rope_n[k];
+    for (int k = 0; k < KSR; ++k) {
+      rope[k] = rope_n[k];
+      rope_n[k] = rope_nn[k];
+    }
   }
   // every wave holds the same m and l: its own output features, normalised
 #pragma unroll
@@ -773,36 +783,78 @@ void chunk_attn_kernel(VParams P) {
       x.uv[s2] = ok && 32 * s2 < mv ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
                                     : u32x4{0u, 0u, 0u, 0u};
   };
-  // the first tile's loads go out before the set-up, so their latency overlaps it
+  // Every global load of the set-up goes out first, with the first tile's, so the set-up waits
+  // for one round trip: the phase inputs (pair tid), the query rows (8 bytes per thread) and
+  // V_K of head h (16 bytes at a time, up to four per thread, when its rows allow it).
+  const int R = P.rot_dim;   // at most D <= 2 * kThreads: one pair per thread
+  const int ip = max(0, min(tid, R / 2 - 1));
+  const double inv_in = P.inv_freq && R > 0 ? P.inv_freq[ip] : 0.0;
+  const int sec_in = P.pair_section && R > 0 ? (int)P.pair_section[ip] : 0;
+  const uint16_t* qrow0 = P.q + ((int64_t)j * P.n_q + h * P.group) * D;
+  const bool qon = tid < P.group * D / 4;
+  const uint2 qpiece = qon ? reinterpret_cast<const uint2*>(qrow0)[tid] : make_uint2(0u, 0u);
+  constexpr int kVkPieces = D * kMaxViewRank / 8 / kThreads;   // per thread, 16 bytes each
+  const bool vk_vec = mk > 0 && C.vec_v != 0;
+  const uint16_t* vkh = mk > 0 ? C.vk + h * C.vk_hs : nullptr;
+  u32x4 vkp[kVkPieces];
+#pragma unroll
+  for (int q = 0; q < kVkPieces; ++q) {
+    const int idx = tid + kThreads * q;
+    vkp[q] = vk_vec && idx < D * mk / 8 ? reinterpret_cast<const u32x4*>(vkh)[idx]
+                                        : u32x4{0u, 0u, 0u, 0u};
+  }
   Tile cur;
   load_tile(S.t_lo + kTile * wave + col, cur);
 
   // set-up: the chunk's phases, the query rows (fp32, in mrg_o) and w = V_K^T q
-  const int R = P.rot_dim;
-  for (int i = tid; i < R / 2; i += kThreads) {
-    const double inv = P.inv_freq ? P.inv_freq[i] : pow(P.theta, -2.0 * (double)i / (double)R);
-    const int sec = P.pair_section ? (int)P.pair_section[i] : 0;
+  if (tid < R / 2) {
+    const double inv = P.inv_freq ? inv_in : pow(P.theta, -2.0 * (double)tid / (double)R);
+    const int sec = P.pair_section ? sec_in : 0;
     const int64_t d = sec == 0 ? C.delta : (sec == 1 ? C.delta_s1 : C.delta_s2);
     double sn, cn;
     sincos((double)d * inv, &sn, &cn);
-    cs[i] = make_float2((float)cn, (float)sn);
+    cs[tid] = make_float2((float)cn, (float)sn);
   }
   float* qs = mrg_o;   // [group][D]
-  const uint16_t* qrow0 = P.q + ((int64_t)j * P.n_q + h * P.group) * D;
-  for (int idx = tid; idx < P.group * D; idx += kThreads)
-    qs[idx] = __uint_as_float((uint32_t)qrow0[idx] << 16);
-  __syncthreads();
+  if (qon) {
+    qs[4 * tid] = __uint_as_float(qpiece.x << 16);
+    qs[4 * tid + 1] = __uint_as_float(qpiece.x & 0xffff0000u);
+    qs[4 * tid + 2] = __uint_as_float(qpiece.y << 16);
+    qs[4 * tid + 3] = __uint_as_float(qpiece.y & 0xffff0000u);
+  }
   // V_K of head h staged in LDS (the V tiles are not in use yet)
   uint16_t* stage = &vt[0][0];
-  if (mk > 0) stage_rows(C.vk + h * C.vk_hs, D * mk, C.vec_v != 0, stage);
-  __syncthreads();
-  for (int idx = tid; idx < P.group * mk; idx += kThreads) {
-    const int row = idx / mk, r = idx - row * mk;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: D is a multiple of 4
-    for (int f = 0; f < D; f += 4)
+  if (vk_vec) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += qs[row * D + f + u] * bf16_lo(stage[(f + u) * mk + r]);
-    wsh[row][r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    for (int q = 0; q < kVkPieces; ++q) {
+      const int idx = tid + kThreads * q;
+      if (idx < D * mk / 8) reinterpret_cast<u32x4*>(stage)[idx] = vkp[q];
+    }
+  } else if (mk > 0) {
+    stage_rows(vkh, D * mk, false, stage);
+  }
+  __syncthreads();
+  // w = V_K^T q on v_mfma_f32_16x16x32_bf16 (q and V_K are bf16, so every product is exact;
+  // fp32 sums): wave c takes the rank columns 16 c .. 16 c + 15, the query heads are the rows
+  if (wave < (mk + 15) / 16) {
+    const int r = 16 * wave + col;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      uint16_t a[8], b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = 32 * k + 8 * grp + e;
+        a[e] = col < P.group ? (uint16_t)(__builtin_bit_cast(uint32_t, qs[col * D + f]) >> 16) : 0;
+        b[e] = r < mk ? stage[f * mk + r] : 0;
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+    // lane (grp, col): query heads 4 grp + i, rank r
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i < P.group && r < mk) wsh[4 * grp + i][r] = acc[i];
   }
   __syncthreads();
 
