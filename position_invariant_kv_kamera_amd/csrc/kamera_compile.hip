@@ -1533,6 +1533,33 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
 // one. Other shapes use project_kernel.
 // ---------------------------------------------------------------------------------------
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Eight fp32 values as bf16 high parts (round to nearest) and the bf16 of what is left.
+__device__ __forceinline__ void split8_bf16(const float* x, bf16x8* hi, bf16x8* lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
+    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[e] = (uint32_t)bf16_rne(x[2 * e] - __uint_as_float((uint32_t)h0 << 16)) |
+           ((uint32_t)bf16_rne(x[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16)) << 16);
+  }
+  *hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  *lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+// Dynamic LDS of the streamed projection: bf16 data keeps X^T as bf16 high and low parts
+// (rows of width + 8), fp32 data X in fp32 with stream_sv columns.
+__host__ __device__ inline size_t stream_lds_bytes(int width, int mp, bool bf16) {
+  return bf16 ? (size_t)2 * mp * (width + 8) * sizeof(uint16_t)
+              : (size_t)width * stream_sv(width, mp) * sizeof(float);
+}
+
 #ifndef KAMERA_PROJ_TOKENS
 #define KAMERA_PROJ_TOKENS 512
 #endif
@@ -1627,12 +1654,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 
   if (J.rotate) fill_phases(cs, J, P);
   const float* xg = P.ws + J.xbase + (int64_t)unit * W * mp;
-  for (int idx = tid; idx < W * mp; idx += kThreads) {
-    const int k = idx / mp, r = idx - k * mp;
-    const int sg = k >> 2, gg = k & 3;
-    const int c = sg / (8 * S), within = sg - c * 8 * S;
-    const int f = 8 * stream_piece(gg, within >> 3, c, S, unit_layout, hp) + (within & 7);
-    vs[k * SV + r] = xg[(int64_t)f * mp + r];
+  // bf16 data: X^T as bf16 high and low parts, row r (rank column) holding the features in
+  // order (row stride W + 8: the 16 rows an MFMA operand reads start in distinct banks);
+  // fp32 data: X with its rows permuted to the lanes' contraction order
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const int XW = W + 8;
+  uint16_t* xth = reinterpret_cast<uint16_t*>(vs);
+  uint16_t* xtl = xth + mp * XW;
+  if constexpr (kBf16) {
+    for (int idx = tid; idx < W * mp; idx += kThreads) {
+      const int f = idx / mp, r = idx - f * mp;
+      const float x = xg[idx];
+      const uint16_t h = bf16_rne(x);
+      xth[r * XW + f] = h;
+      xtl[r * XW + f] = bf16_rne(x - __uint_as_float((uint32_t)h << 16));
+    }
+  } else {
+    for (int idx = tid; idx < W * mp; idx += kThreads) {
+      const int k = idx / mp, r = idx - k * mp;
+      const int sg = k >> 2, gg = k & 3;
+      const int c = sg / (8 * S), within = sg - c * 8 * S;
+      const int f = 8 * stream_piece(gg, within >> 3, c, S, unit_layout, hp) + (within & 7);
+      vs[k * SV + r] = xg[(int64_t)f * mp + r];
+    }
   }
   __syncthreads();
 
@@ -1700,12 +1744,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           d[q] = d[q] - (x[q] * r.x + (sg * y[q]) * r.y);
         }
       }
+      if constexpr (kBf16) {
+        // U tile += Delta X on v_mfma_f32_16x16x32_bf16: the lane's 8 features are one k-step's
+        // A operand (token n), the same 8 features of X^T row 16 b + n its B operand; Delta and
+        // X are cut into bf16 high and low parts (round to nearest) and the three products
+        // other than low x low are summed small first (dropped: at most ~2^-16 of |Delta X|
+        // per term, far below the bf16 rounding of U)
+        bf16x8 dh, dl;
+        split8_bf16(d, &dh, &dl);
+        const int f0 = 128 * c + off[p];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float* br = vs + (row0 + 4 * (8 * p + q)) * SV + n;
+        for (int b = 0; b < 4; ++b) {
+          if (b < nrb) {
+            const int r = 16 * b + n;
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xth + r * XW + f0);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(xtl + r * XW + f0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dl, xh, acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dh, xl, acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dh, xh, acc[b], 0, 0, 0);
+          }
+        }
+      } else {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (b < nrb) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(d[q], br[16 * b], acc[b], 0, 0, 0);
+        for (int q = 0; q < 8; ++q) {
+          const float* br = vs + (row0 + 4 * (8 * p + q)) * SV + n;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b < nrb) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(d[q], br[16 * b], acc[b], 0, 0, 0);
+        }
       }
     }
     if (c == nslab - 1) {
@@ -1923,7 +1989,7 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     const bool stream = stream_eligible(J, M.rope_layout);
     const int tblocks = stream ? (J.n_tokens + kStreamTokens - 1) / kStreamTokens
                                : (J.n_tokens + kProjTokens - 1) / kProjTokens;
-    const size_t lds = stream ? (size_t)J.width * stream_sv(J.width, J.mp) * sizeof(float) : 0;
+    const size_t lds = stream ? stream_lds_bytes(J.width, J.mp, M.dtype == KAMERA_DTYPE_BF16) : 0;
     bool ok = add(kGram, J.gperm ? 0 : J.te / 32, (int)j,
                   (int64_t)J.n_units * J.n_pairs * J.splits) &&
               add(kSubspace, subspace_class(J.width, J.mp), (int)j, J.n_units) &&
