@@ -278,6 +278,11 @@ def small_cases() -> list[Case]:
              [ChunkSpec(64, 32, -7)], seed=7),
         Case("mla_f32_latent128", "mla", "f32", 1, 1, 128, 32, HS, 1e4,
              [ChunkSpec(130, 16, 4096)], seed=8),
+        # rank class 64 below its width (columns m..63 empty), and the fp32 rank-64 path
+        Case("gqa_bf16_rank56_interleaved", "gqa", "bf16", 1, 2, 128, 128, IL, 1e4,
+             [ChunkSpec(260, 56, 321)], seed=12),
+        Case("gqa_f32_rank64", "gqa", "f32", 1, 1, 128, 128, HS, 1e6,
+             [ChunkSpec(200, 64, -77)], seed=13),
     ]
 
 
@@ -290,6 +295,9 @@ def degenerate_cases() -> list[Case]:
         # fewer tokens than m: Delta has rank 5, the rank-16 truncation is Delta itself
         Case("tokens_below_rank", "gqa", "f32", 1, 2, 64, 64, HS, 1e4,
              [ChunkSpec(5, 16, 12)], seed=10),
+        # the same at rank 64: 40 tokens leave 24 collapsed columns
+        Case("tokens_below_rank64", "gqa", "bf16", 1, 2, 128, 128, HS, 1e6,
+             [ChunkSpec(40, 64, 5)], seed=14),
     ]
 
 

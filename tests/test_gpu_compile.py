@@ -145,8 +145,9 @@ def test_zero_deficit_gives_a_zero_patch():
                 assert np.max(np.abs(g - np.eye(g.shape[0]))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
 
 
-def test_fewer_tokens_than_rank_reconstructs_delta():
-    case = cc.degenerate_cases()[1]
+@pytest.mark.parametrize("idx", [1, 2], ids=["rank16", "rank64"])
+def test_fewer_tokens_than_rank_reconstructs_delta(idx):
+    case = cc.degenerate_cases()[idx]
     inputs, items = run(case)
     check_case(case, inputs, items)
 
