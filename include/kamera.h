@@ -138,7 +138,14 @@ typedef struct kamera_model {
  * Logical token p of the cache lives in physical page page_table[p / page_size], slot
  * p % page_size. page_table == NULL means the identity table (a dense cache).
  * Table entries outside [0, n_pages) are never written through: the rows they address are
- * skipped and counted (kamera_read_fault_count). */
+ * skipped and counted (kamera_read_fault_count).
+ * Debug mode: with the environment variable KAMERA_VALIDATE set to a non-zero integer, the
+ * reuse-operator calls (kamera_reuse_batch, kamera_reuse_batch_noalloc, kamera_relocate,
+ * kamera_patch) first copy the page table to the host, after the stream's earlier work, and
+ * synchronise the stream: a batch that writes through an entry outside [0, n_pages), or whose
+ * tokens land twice on one physical slot (two logical pages sharing a physical page), is then
+ * rejected with KAMERA_ERR_INVALID_ARGUMENT before anything is enqueued. In this mode the
+ * calls block the host and return KAMERA_ERR_UNSUPPORTED on a capturing stream. */
 typedef struct kamera_cache {
   void* pool[2];
   int64_t layer_stride;       /* elements */

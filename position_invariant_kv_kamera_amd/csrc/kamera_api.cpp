@@ -1,6 +1,6 @@
 // kamera_api.cpp — host runtime behind include/kamera.h: argument validation, work packing
-// and kernel launch. Every check runs before the first HIP call, so a rejected call has no
-// side effect on the device.
+// and kernel launch. Every check runs before anything is enqueued (the optional deep check of
+// the page table only reads it), so a rejected call has no side effect on the device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -113,6 +113,60 @@ kamera_status validate_chunks(const kamera_model& m, const kamera_cache& c,
     if (spans[i].first < spans[i - 1].second)
       return fail(KAMERA_ERR_INVALID_ARGUMENT,
                   "two chunks write logical cache token %lld", (long long)spans[i].first);
+  return KAMERA_OK;
+}
+
+// Deep validation (environment variable KAMERA_VALIDATE non-zero): the page table lives in
+// device memory, so the argument checks above cannot see its entries. This copies it to the
+// host (after the stream's earlier work, which may have written it) and checks that every
+// logical page a chunk writes maps into [0, n_pages) and that no two written tokens share a
+// physical slot. It synchronises the stream, so it refuses a capturing one. Nothing is
+// written to the device.
+kamera_status validate_table_contents(const kamera_cache& c, const kamera_chunk* chunks,
+                                      int32_t n_chunks, hipStream_t stream) {
+  if (!c.page_table) return KAMERA_OK;   // identity table: checked against n_pages already
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return fail(KAMERA_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(KAMERA_ERR_UNSUPPORTED,
+                "KAMERA_VALIDATE reads the page table and synchronises; the stream is capturing");
+  std::vector<int32_t> table(c.n_logical_pages);
+  e = hipMemcpyAsync(table.data(), c.page_table, table.size() * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(KAMERA_ERR_HIP, "reading the page table: %s", hipGetErrorString(e));
+  struct Use {
+    int32_t phys, slot_lo, slot_hi, logical, chunk;
+  };
+  std::vector<Use> uses;
+  const int32_t ps = c.page_size;
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    const kamera_chunk& k = chunks[i];
+    if (k.n_tokens <= 0) continue;
+    const int64_t first = k.dst_token_offset, end = first + k.n_tokens;
+    for (int64_t lp = first / ps; lp * ps < end; ++lp) {
+      const int32_t phys = table[lp];
+      if (phys < 0 || phys >= c.n_pages)
+        return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                    "chunk %d: page_table[%lld] = %d is outside [0, %d)", i, (long long)lp, phys,
+                    c.n_pages);
+      const int64_t lo = std::max(first, lp * ps), hi = std::min(end, (lp + 1) * ps);
+      uses.push_back({phys, (int32_t)(lo - lp * ps), (int32_t)(hi - lp * ps), (int32_t)lp, i});
+    }
+  }
+  std::sort(uses.begin(), uses.end(), [](const Use& a, const Use& b) {
+    return a.phys != b.phys ? a.phys < b.phys : a.slot_lo < b.slot_lo;
+  });
+  for (size_t j = 1; j < uses.size(); ++j) {
+    const Use &a = uses[j - 1], &b = uses[j];
+    if (a.phys == b.phys && b.slot_lo < a.slot_hi)
+      return fail(KAMERA_ERR_INVALID_ARGUMENT,
+                  "logical pages %d (chunk %d) and %d (chunk %d) both write slot %d of physical "
+                  "page %d",
+                  a.logical, a.chunk, b.logical, b.chunk, b.slot_lo, b.phys);
+  }
   return KAMERA_OK;
 }
 
@@ -314,6 +368,11 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   const size_t need = kamera_workspace_bytes(n_chunks);
   if (workspace_bytes < need)
     return fail(KAMERA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (env_int("KAMERA_VALIDATE", 0)) {
+    st = validate_table_contents(*cache, chunks, n_chunks, stream);
+    if (st != KAMERA_OK) return st;
+  }
 
   Plan plan;
   st = build_plan(*model, *cache, chunks, n_chunks, op, &plan);
@@ -342,7 +401,6 @@ kamera_status run(const kamera_model* model, const kamera_cache* cache, const ka
   if (model->pair_section)
     std::memcpy(staging.data() + kSectionOffset, model->pair_section, pairs);
 
-  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   st = upload(staging, workspace, stream, allow_setup);
   if (st != KAMERA_OK) return st;
 

@@ -256,6 +256,45 @@ def test_out_of_range_page_entries_are_skipped_and_counted():
         assert bool((rows.view(torch.int16) == wl.SENTINEL_BF16).all())
 
 
+def _first_full_page(p, c):
+    """A logical page that chunk c writes from its first slot to its last."""
+    lp = -(-p.dst_offsets[c] // p.page_size)
+    assert (lp + 1) * p.page_size <= p.dst_offsets[c] + p.chunk_tokens[c]
+    return lp
+
+
+@pytest.mark.parametrize("op", ["reuse", "relocate", "patch"])
+@pytest.mark.parametrize("damage", ["out_of_range", "negative", "aliased"])
+def test_validate_mode_rejects_a_bad_table_before_enqueueing(monkeypatch, op, damage):
+    """KAMERA_VALIDATE=1: a table entry outside the pool, or two written logical pages mapped
+    to one physical page, is refused on the host with INVALID_ARGUMENT, and nothing reaches
+    the cache."""
+    monkeypatch.setenv("KAMERA_VALIDATE", "1")
+    p = SMALL["mha7b_reorder_bf16"]()
+    table = p.page_table.copy()
+    a, b = _first_full_page(p, 0), _first_full_page(p, 1)
+    table[b] = {"out_of_range": p.n_pages + 5, "negative": -1, "aliased": table[a]}[damage]
+    batch = wl.materialize(dataclasses.replace(p, page_table=table), DEV)
+    print(f"[kamera] validate {op} {damage}", flush=True)
+    with pytest.raises(kb.KameraError) as err:
+        kb.run_batch(op, batch)
+    torch.cuda.synchronize()
+    assert err.value.status == kb.KAMERA_ERR_INVALID_ARGUMENT
+    assert ("outside" if damage != "aliased" else "both write") in str(err.value)
+    for pool in batch.pool_storage:
+        assert bool((pool.view(torch.int16) == wl.SENTINEL_BF16).all())
+
+
+def test_validate_mode_passes_a_good_table(monkeypatch):
+    """KAMERA_VALIDATE=1 on a valid shuffled table (page size 7, 25 % spare pages): the call
+    goes through and matches the oracle, as without the check."""
+    monkeypatch.setenv("KAMERA_VALIDATE", "1")
+    p = _paged("dsv2lite_mla_bf16", 7)
+    batch = wl.materialize(p, DEV)
+    run("reuse", batch)
+    assert_report(compare_batch(batch, "reuse"), "validated paged MLA")
+
+
 def test_workspace_reused_across_calls_of_different_sizes():
     big = wl.materialize(SMALL["qwen25vl_gqa_bf16"](), DEV)
     ws = kb.Workspace(big.plan.n_chunks)
