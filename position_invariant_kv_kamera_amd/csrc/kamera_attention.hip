@@ -730,21 +730,26 @@ __device__ __forceinline__ void split8(const float* x, bf16x8* hi, bf16x8* lo) {
 
 // KMAX: the largest patch rank in the launch, rounded up to 16, 32 or 64 (register budget).
 template <int D, int KMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 && KMAX <= 32 ? 3 : 2, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 32 ? 3 : 2, 8)))
 void chunk_attn_kernel(VParams P) {
   constexpr int KS = D / 32;                 // bf16 k-steps over the features
   constexpr int PK = (KMAX + 31) / 32;       // bf16 k-steps over the key patch rank
   constexpr int NC = D / 16;                 // column blocks of o
   constexpr int NZ = KMAX / 16;              // column blocks of z
-  constexpr int VS = D + kMaxViewRank + 8;   // LDS row: V row, then the token's U_V row
+  constexpr int VS = D + 32 * PK + 8;        // LDS row: V row, then the token's U_V row (whole k-steps)
   constexpr int PSTR = 17;
-  constexpr int MW = D + kMaxViewRank;       // merged row: o, then z
+  constexpr int MW = D + KMAX;               // merged row: o, then z
+  constexpr int NQ = 2 * KS + 2 * PK;        // score A operands of a lane: q' and w, hi and lo
+  static_assert(kTile * 4 * VS >= D * KMAX, "V_K and V_V are staged in the V tiles");
   __shared__ __align__(16) uint16_t vt[4][kTile * VS];
   __shared__ float pt[4][kTile * PSTR];
   __shared__ float mrg_m[4][kMaxGroup], mrg_l[4][kMaxGroup];
   __shared__ float mrg_o[kMaxGroup * MW];    // also holds the query rows during set-up
-  __shared__ float wsh[kMaxGroup][kMaxViewRank + 1];
+  __shared__ float wsh[kMaxGroup][KMAX + 1];
   __shared__ float2 cs[64];
+  // The score operands are the same in every wave: built once, read from LDS at each tile
+  // (kept in registers they would cost 40 of them and one wave per SIMD).
+  __shared__ __align__(16) u32x4 qop[NQ][64];
 
   const int sidx = blockIdx.x / P.n_kv;
   const int h = blockIdx.x - sidx * P.n_kv;
@@ -793,7 +798,7 @@ void chunk_attn_kernel(VParams P) {
   const uint16_t* qrow0 = P.q + ((int64_t)j * P.n_q + h * P.group) * D;
   const bool qon = tid < P.group * D / 4;
   const uint2 qpiece = qon ? reinterpret_cast<const uint2*>(qrow0)[tid] : make_uint2(0u, 0u);
-  constexpr int kVkPieces = D * kMaxViewRank / 8 / kThreads;   // per thread, 16 bytes each
+  constexpr int kVkPieces = (D * KMAX / 8 + kThreads - 1) / kThreads;   // per thread, 16 B each
   const bool vk_vec = mk > 0 && C.vec_v != 0;
   const uint16_t* vkh = mk > 0 ? C.vk + h * C.vk_hs : nullptr;
   u32x4 vkp[kVkPieces];
@@ -858,9 +863,10 @@ void chunk_attn_kernel(VParams P) {
   }
   __syncthreads();
 
-  // operands of this lane: query row col, features 32k + 8 grp + e, turned by -delta
-  bf16x8 qh[KS], ql[KS], wh[PK], wl[PK];
-  {
+  // operands of lane (col, grp): query row col, features 32k + 8 grp + e, turned by -delta;
+  // built by wave 0 into qop: [q' hi, q' lo] per k-step, then [w hi, w lo] per rank step
+  if (wave == 0) {
+    bf16x8 qh[KS], ql[KS], wh[PK], wl[PK];
     const bool on = col < P.group;
     const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
 #pragma unroll
@@ -904,8 +910,18 @@ void chunk_attn_kernel(VParams P) {
       }
       split8(x, &wh[s2], &wl[s2]);
     }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      qop[2 * k][lane] = __builtin_bit_cast(u32x4, qh[k]);
+      qop[2 * k + 1][lane] = __builtin_bit_cast(u32x4, ql[k]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2) {
+      qop[2 * KS + 2 * s2][lane] = __builtin_bit_cast(u32x4, wh[s2]);
+      qop[2 * KS + 2 * s2 + 1][lane] = __builtin_bit_cast(u32x4, wl[s2]);
+    }
   }
-  __syncthreads();   // qs (in mrg_o) is free again
+  __syncthreads();   // qs (in mrg_o) is free again; qop is complete
 
   float m[4], l[4];
   f32x4 o[NC], z[NZ];
@@ -929,15 +945,19 @@ void chunk_attn_kernel(VParams P) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const bf16x8 kb = __builtin_bit_cast(bf16x8, cur.k[k]);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[k], kb, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[k], kb, sacc, 0, 0, 0);
+      const bf16x8 qh = __builtin_bit_cast(bf16x8, qop[2 * k][lane]);
+      const bf16x8 ql = __builtin_bit_cast(bf16x8, qop[2 * k + 1][lane]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kb, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kb, sacc, 0, 0, 0);
     }
 #pragma unroll
     for (int s2 = 0; s2 < PK; ++s2) {
       if (32 * s2 < mk) {
         const bf16x8 ub = __builtin_bit_cast(bf16x8, cur.uk[s2]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh[s2], ub, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl[s2], ub, sacc, 0, 0, 0);
+        const bf16x8 wh = __builtin_bit_cast(bf16x8, qop[2 * KS + 2 * s2][lane]);
+        const bf16x8 wl = __builtin_bit_cast(bf16x8, qop[2 * KS + 2 * s2 + 1][lane]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, ub, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, ub, sacc, 0, 0, 0);
       }
     }
     // V rows and U_V rows of the tile to LDS (token col)
