@@ -826,7 +826,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab["total"],
-                     "kernel": "kamera_mfma_kernel", "timed_with": "hip events on the launch stream"},
+                     "kernel": "kamera_mfma_kernel" if p.dtype == "bf16" else "kamera_valu_kernel",
+                     "timed_with": "hip events on the launch stream"},
         "kernel_source_sha": kernel_source_hash(),
     }
     if tinfo == "stale":

@@ -287,8 +287,7 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
           j.wph = 1;
           j.n_windows = g.heads;
           j.n_wgroups = (g.heads + 3) / 4;
-          j.n_tiles = k.n_tokens;
-          j.n_tgroups = (k.n_tokens + kamera::kValuTokensPerBlock - 1) / kamera::kValuTokensPerBlock;
+          j.n_tiles = k.n_tokens;   // n_tgroups is set below, as for the MFMA jobs
           plan->valu.push_back(j);
         }
       }
@@ -322,6 +321,18 @@ kamera_status build_plan(const kamera_model& m, const kamera_cache& c, const kam
   // runs of 4 blocks kept on one XCD then find it in that XCD's L2 (measured +1 % on 4 KV
   // heads x 1296-token chunks at m = 16, neutral at m = 32; with long waves it cost 1-5 %).
   plan->xcd_remap = env_int("KAMERA_XCD_REMAP", tpw <= 4 ? 4 : 0);
+  // VALU token groups: up to kValuTokensPerBlock tokens per block, fewer while the launch
+  // would have under kValuMinBlocks blocks (a thread walks its items one after another, so a
+  // small batch on a few blocks is one long latency chain; results do not depend on it).
+  auto valu_blocks_at = [&](int64_t tpb) {
+    int64_t b = 0;
+    for (const JobDesc& j : plan->valu)
+      b += (int64_t)m.n_layers * j.n_wgroups * ((j.n_tiles + tpb - 1) / tpb);
+    return b;
+  };
+  int64_t tpb = kamera::kValuTokensPerBlock;
+  while (tpb > 1 && valu_blocks_at(tpb) < kamera::kValuMinBlocks) tpb /= 2;
+  for (JobDesc& j : plan->valu) j.n_tgroups = (int32_t)std::max<int64_t>(1, (j.n_tiles + tpb - 1) / tpb);
 
   // grouped by window width (one launch each), heaviest jobs first inside a group so that a
   // mixed batch does not end on a tail of patched work

@@ -71,7 +71,8 @@ struct LaunchParams {
 // Kernel geometry
 constexpr int kBlockThreads = 256;      // 4 waves of 64
 constexpr int kTileTokens = 16;         // MFMA N dimension
-constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path
+constexpr int kValuTokensPerBlock = 64; // tokens per block on the VALU path (at most)
+constexpr int kValuMinBlocks = 1024;    // fewer tokens per block until a VALU launch has this many
 constexpr int kMaxPairs = 512;          // LDS phase table (rot_dim <= 1024)
 // Workspace front: [header (fault counter) | inv_freq table (kMaxPairs doubles) |
 // pair sections (kMaxPairs bytes) | job tables ...]
