@@ -16,9 +16,10 @@
 //   subspace  one wave per head (widths up to 128) or one block of four waves per head (the
 //             wide MLA latent): sums the partials into G where there are several, then block
 //             power iteration X <- orth(G X) from a fixed +-1 start, G X on fp32 MFMA. orth() is
-//             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64 (in
-//             registers up to rank 32 and at rank 64), X = Y L^-T by forward substitution with
-//             fp64 sums. Columns that collapse (Y rank deficient) are re-seeded between rounds
+//             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64, X = Y L^-T
+//             (up to rank 32: L in registers and forward substitution with fp64 sums; ranks 48
+//             and 64: both in 16 x 16 blocks on fp64 MFMA, orth_blocked). Columns that
+//             collapse (Y rank deficient) are re-seeded between rounds
 //             and zero after the last; a final orth() of X alone restores orthonormality to
 //             fp32 rounding;
 //   project   U = Delta X with the fp32 X kept in the workspace (a second pass over the inputs).
@@ -672,96 +673,29 @@ __device__ __forceinline__ float seed_value(int i, int j, int round) {
 
 // Storage of S and L (lower triangle, fp64) for one unit of rank class MP: square with row
 // stride MP + 1 up to MP = 32 (the register Cholesky uses the strict upper part of row 0 as
-// scratch), packed by rows above (half the LDS, so more units fit on a CU).
+// scratch; lidx), packed by columns above (orth_blocked; half the LDS, so more units fit on a
+// CU).
 template <int MP>
 __host__ __device__ constexpr int lm_size() { return MP <= 32 ? MP * (MP + 1) : MP * (MP + 1) / 2; }
 template <int MP>
 __device__ __forceinline__ int lidx(int r, int c) {
-  return MP <= 32 ? r * (MP + 1) + c : r * (r + 1) / 2 + c;
+  static_assert(MP <= 32, "the square layout serves the rank classes up to 32");
+  return r * (MP + 1) + c;
 }
-// L of rank class 64 after the factorisation: packed by columns (column c holds rows c..63,
-// zero from row m on), followed by 64 doubles of padding that 16-byte column reads may touch.
-__device__ __forceinline__ int lcol64(int r, int c) { return c * 64 - c * (c - 1) / 2 + (r - c); }
 
 // Cholesky factor of S in place, by one wave (wave-synchronous): lm holds S's lower triangle
 // (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
 // (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
 template <int MP>
-__device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead, int m,
-                                              double* scratch) {
-  static_assert(MP % 16 == 0 && MP <= 64, "rank classes are 16, 32, 48 and 64");
+__device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
+  static_assert(MP % 16 == 0 && MP <= 32, "the rank classes above 32 use orth_blocked");
   const int lane = threadIdx.x & 63;
-  if constexpr (MP == 64) {
-    // Rank 64, in registers, as a loop whose body is the same for every step: lane ri holds
-    // row ri of S, and its registers shift left by one column per step, so the pivot column j
-    // is always sv[0] and every register index is static. Step j: the pivot comes from lane j
-    // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
-    // lane ri scales its entry of column j, stores it as L[ri][j] and publishes it in `scratch`
-    // (128 entries, zero past the rows that have one), then updates the rest of its row as
-    // s_r,j+c -= l_rj l_j+c,j (one fused multiply-add each) while shifting it; entries right
-    // of the diagonal are updated too and never read. L is stored column-major (lcol64), the
-    // layout the rank-64 forward substitution reads; S's diagonal waits in `inv`.
-    const int ri = lane;
-    double sv[64];
-#pragma unroll
-    for (int c = 0; c < 64; ++c)
-      sv[c] = (ri < m && c < m) ? (ri >= c ? lm[lidx<64>(ri, c)] : lm[lidx<64>(c, ri)]) : 0.0;
-    // s_jj before elimination, read at step j just before 1 / l_jj replaces it
-    const double sdiag = ri < m ? lm[lidx<64>(ri, ri)] : 0.0;
-    scratch[64 + ri] = 0.0;   // colj[j + c] past row 63 reads zeros
-    wave_lds_sync();          // S is in registers: L may now overwrite it
-    inv[ri] = sdiag;
-    wave_lds_sync();
-#pragma unroll 1
-    for (int j = 0; j < m; ++j) {
-      const uint64_t pb = __builtin_bit_cast(uint64_t, sv[0]);
-      const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, j);
-      const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), j);
-      const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
-      const double s0 = inv[j];
-      const bool dk = d <= kDeadTol * s0;
-      const double ljj = dk ? 0.0 : sqrt(d);
-      const double iv = dk ? 0.0 : 1.0 / ljj;
-      if (lane == 0) {
-        inv[j] = iv;
-        dead[j] = dk ? 1 : 0;
-      }
-      const double v = ri == j ? ljj : (ri > j ? sv[0] * iv : sv[0]);
-      const double lij = ri > j && ri < m ? v : 0.0;
-      scratch[ri] = lij;
-      // L column-major (column j from its diagonal down, zero past row m - 1)
-      if (ri >= j) lm[lcol64(ri, j)] = ri < m ? v : 0.0;
-      wave_lds_sync();
-      // the column's entries below the pivot, 16 at a time, the next 16 in flight while the
-      // current ones are used (read one at a time next to their use, each LDS read would wait
-      // for the one before; read all at once, the row and the column would not fit in the
-      // 256 registers a VALU instruction can address)
-      const double* colj = scratch + j;
-      double cv[2][16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) cv[0][k] = colj[1 + k];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q < 3) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) cv[(q + 1) & 1][k] = colj[17 + 16 * q + k];
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int c = 1 + 16 * q + k;
-          if (c < 64) sv[c - 1] = __builtin_fma(-lij, cv[q & 1][k], sv[c]);
-        }
-      }
-      sv[63] = 0.0;
-      wave_lds_sync();   // scratch is rewritten by the next step
-    }
-  } else if constexpr (MP <= 32) {
+  {
     // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
     // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
     // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
     // the lanes holding column j scale it and publish it in LDS, then each lane updates its
-    // own part of the trailing matrix. The same operations in the same order as the LDS
-    // version below, with one LDS round trip per step instead of a chain of them.
+    // own part of the trailing matrix: one LDS round trip per step.
     constexpr int LPR = 64 / MP, CPL = MP / LPR;
     const int ri = lane % MP, cb = lane / MP, c0 = cb * CPL;
     double sv[CPL];
@@ -820,32 +754,6 @@ __device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead
     for (int c = 0; c < CPL; ++c) {
       const int col = c0 + c;
       if (ri < m && col <= ri) lm[lidx<MP>(ri, col)] = sv[c];
-    }
-  } else {
-    // Cholesky, right-looking: lane i owns row i of S, which becomes row i of L. Step j: the
-    // owner of row j takes the pivot (collapsed when what is left of s_jj is at most kDeadTol
-    // times its starting value), the rows below scale column j, then each updates its own part
-    // of the trailing matrix (its next diagonal included, so the next pivot needs no wait).
-    const int i = lane;
-    const double sii0 = i < m ? lm[lidx<MP>(i, i)] : 0.0;
-    for (int j = 0; j < m; ++j) {
-      if (i == j) {
-        const double d = lm[lidx<MP>(j, j)];
-        const bool dk = d <= kDeadTol * sii0;
-        const double ljj = dk ? 0.0 : sqrt(d);
-        lm[lidx<MP>(j, j)] = ljj;
-        inv[j] = dk ? 0.0 : 1.0 / ljj;
-        dead[j] = dk ? 1 : 0;
-      }
-      wave_lds_sync();
-      double lij = 0.0;
-      if (i > j && i < m) {
-        lij = lm[lidx<MP>(i, j)] * inv[j];
-        lm[lidx<MP>(i, j)] = lij;
-      }
-      wave_lds_sync();
-      if (i > j && i < m)
-        for (int k = j + 1; k <= i; ++k) lm[lidx<MP>(i, k)] -= lij * lm[lidx<MP>(k, j)];
     }
   }
 }
@@ -970,7 +878,7 @@ __device__ __forceinline__ void orth_block(float* xs, double* ss, double* inv, i
     }
   }
   __syncthreads();
-  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m, nullptr);
+  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m);
   __syncthreads();
   // X = Y L^-T in place: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj; the row's earlier x are
   // already in place, y_ij is read before x_ij replaces it (columns from m on stay zero)
@@ -1085,141 +993,320 @@ __device__ __forceinline__ void wave_global_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Rank classes above 32 (48 and 64): orth() in 16 x 16 blocks, the products on fp64 MFMA
+// 16x16x4 (lane 16 k + i supplies A[i][k] and B[k][i] and receives rows k + 4 v, column i of
+// the product in register v). S and then L live in one packed lower triangle stored by columns
+// (lcol), and after the factorisation each diagonal block holds T_KK = L_KK^-1 in place of
+// L_KK, which is what the substitution needs.
+//   S = Y^T Y        all lower tiles at once, four rows of Y per step (fp32 products exact in
+//                    fp64, fp64 sums);
+//   L L^T = S        right-looking by block column K: the 16 x 16 diagonal block is factored by
+//                    lanes 0..15 in registers (lane i holds row i; the pivot and the published
+//                    column come by readlane), T_KK is formed alongside (column a by lane a,
+//                    right-looking on the same published entries), then the panel
+//                    L_IK = S_IK T_KK^T and the trailing update S_IJ -= L_IK L_JK^T run on MFMA;
+//   X = Y L^-T       by block column J and 16-row tile: Z^T = Y_J^T - L_J,<J X_<J^T (the
+//                    transposed product leaves Z in exactly the A-operand layout), then
+//                    X_J = Z T_JJ^T.
+// A collapsed column (what is left of its pivot at most kDeadTol times its starting value) gets
+// 1 / l_jj = 0: its row of T and its column of L below the pivot are zero, so, as in the
+// unblocked form, its x (re-seeded between rounds, zero after the last) feeds no later column.
+// The blocked form computes the same quantities as the unblocked one in another order of
+// fp64 additions.
 template <int MP>
-__device__ __forceinline__ void orth_wave(float* buf, double* lm, double* inv, int* dead, double* scratch, int D,
-                          int m, int reseed_round) {
-  constexpr int BS = MP + 4;
+__device__ __forceinline__ int lcol(int r, int c) { return c * MP - c * (c - 1) / 2 + (r - c); }
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+template <int MP>
+__device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv, int* dead, int D,
+                                             int m, int reseed_round) {
+  static_assert(MP == 48 || MP == 64, "blocked orth() serves the rank classes 48 and 64");
+  constexpr int BS = MP + 4, NB = MP / 16, NT = NB * (NB + 1) / 2;
   const int lane = threadIdx.x & 63;
-#if KAMERA_ORTH_MFMA
-  // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
-  // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
-  // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
-  // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
-  // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
-  // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
-  // all the factorisation reads.
+  const int li = lane & 15, kk = lane >> 4;
+  const int nrt = D / 16;   // D is a multiple of 32
+
+  // S = Y^T Y, lower tiles (a, b <= a)
   {
-    const int li = lane & 15, kk = lane >> 4;
-    const int nt = (m + 15) / 16;
-    for (int ta = 0; ta < nt; ++ta) {
-      for (int tb = 0; tb <= ta; ++tb) {
-        f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
-        const float* ya = buf + kk * BS + 16 * ta + li;
-        const float* yb = buf + kk * BS + 16 * tb + li;
-        for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
-          const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
-          const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
-          s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
-        }
-        // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
+    f64x4 st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int r = 0; r < D; r += 4) {
+      const float* yr = buf + (r + kk) * BS + li;
+      double y[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) y[b] = (double)yr[16 * b];
+      int t = 0;
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b, ++t) st[t] = mfma_f64(y[a], y[b], st[t]);
+    }
+    int t = 0;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b <= a; ++b, ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-          if (row < m && col <= row) lm[lidx<MP>(row, col)] = s0[v] + s1[v];
+          const int row = 16 * a + kk + 4 * v, col = 16 * b + li;
+          if (row >= col) lm[lcol<MP>(row, col)] = st[t][v];
         }
+  }
+  wave_lds_sync();
+  if (lane < MP) inv[lane] = lm[lcol<MP>(lane, lane)];   // starting diagonal (dead-column test)
+  wave_lds_sync();
+
+  // L L^T = S by block columns; diagonal blocks end up holding T_KK = L_KK^-1
+#pragma unroll
+  for (int K = 0; K < NB; ++K) {
+    const int g0 = 16 * K;
+    double sv[16], s0[16], tv[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      sv[c] = li >= c ? lm[lcol<MP>(g0 + li, g0 + c)] : lm[lcol<MP>(g0 + c, g0 + li)];
+      s0[c] = inv[g0 + c];
+      tv[c] = c == li ? 1.0 : 0.0;   // column li of T, solved right-looking
+    }
+    // step j: lane i's sv[0] is entry (i, j) of what is left of the block (its row shifts by
+    // one column per step, so every index is static); the steps have no branch, so one step's
+    // updates can overlap the next pivot's square root and reciprocal
+    uint32_t dbits = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const double d = readlane_f64(sv[0], j);
+      const bool real = g0 + j < m;
+      const bool dk = real && d <= kDeadTol * s0[j];
+      const bool live = real && !dk;
+      // 1 / sqrt(d): the hardware estimate and two Newton steps (a shorter dependent chain
+      // than a correctly rounded square root followed by a division)
+      double rq = __builtin_amdgcn_rsq(d);
+      rq = __builtin_fma(0.5 * rq, __builtin_fma(-d * rq, rq, 1.0), rq);
+      rq = __builtin_fma(0.5 * rq, __builtin_fma(-d * rq, rq, 1.0), rq);
+      const double ljj = live ? d * rq : 0.0;
+      const double iv = live ? rq : 0.0;
+      dbits |= dk ? 1u << j : 0u;
+      const double lij = li > j ? sv[0] * iv : 0.0;
+      const double tj = tv[j] * iv;
+      tv[j] = tj;
+#pragma unroll
+      for (int c = 1; c < 16 - j; ++c) {
+        const double lc = readlane_f64(lij, j + c);   // L[j + c][j]
+        sv[c - 1] = __builtin_fma(-lij, lc, sv[c]);
+        tv[j + c] = __builtin_fma(-lc, tj, tv[j + c]);
       }
     }
-  }
-#else
-  // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
-  const int npair = m * (m + 1) / 2;
-  for (int q = lane; q < npair; q += 64) {
-    int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
-    while (a * (a + 1) / 2 > q) --a;
-    while ((a + 1) * (a + 2) / 2 <= q) ++a;
-    const int b = q - a * (a + 1) / 2;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
-#pragma unroll 2
-    for (int r = 0; r < D; r += 4) {
+    if (lane < 16) dead[g0 + lane] = (dbits >> lane) & 1u;
+    wave_lds_sync();   // every lane has read the diagonal block
+    if (kk == 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
+      for (int n = 0; n < 16; ++n)
+        if (n >= li) lm[lcol<MP>(g0 + n, g0 + li)] = tv[n];
     }
-    lm[lidx<MP>(a, b)] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
-#endif
-  wave_lds_sync();
-  cholesky_wave<MP>(lm, inv, dead, m, scratch);
-  wave_lds_sync();
-  // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
-  // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
-  // pivot, so a reseeded x_ra adds nothing to the columns after it.
-  if constexpr (MP == 64) {
-    // Right-looking, the sums in registers, one row per lane at a time (rows lane, then
-    // lane + 64): after step j, acc[k] holds sum_{a<=j} x_a l_{j+1+k,a}, fp64 fused
-    // multiply-adds in order of a. Step j forms x_j, then adds x_j times column j of L (from
-    // the column-major L, 16 entries at a time with the next 16 in flight) while shifting the
-    // sums by one column. Reads past column j's last row land in later columns or the padding
-    // and only reach sums past column 63, which are never used.
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      const int r = lane + 64 * half;
-      const bool on = r < D;
-      float* row = buf + (on ? r : lane) * BS;
-      double acc[64];
+    wave_lds_sync();
+    if (K + 1 < NB) {
+      // panel: L_IK = S_IK T_KK^T (B operand: T[li][4 s + kk])
+      double bt[4];
 #pragma unroll
-      for (int k = 0; k < 64; ++k) acc[k] = 0.0;
-#pragma unroll 1
-      for (int j = 0; j < m; ++j) {
-        float v = (float)(((double)row[j] - acc[0]) * inv[j]);
-        if (reseed_round >= 0 && dead[j]) v = seed_value(r, j, reseed_round + 1);
-        if (on) row[j] = v;
-        const double x = (double)v;
-        const double* lcol = lm + lcol64(j, j);
-        double lv[2][16];
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int cc = 4 * s2 + kk;
+        bt[s2] = li >= cc ? lm[lcol<MP>(g0 + li, g0 + cc)] : 0.0;
+      }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) lv[0][k] = lcol[1 + k];
+      for (int I = K + 1; I < NB; ++I) {
+        double a[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q < 3) {
+        for (int s2 = 0; s2 < 4; ++s2) a[s2] = lm[lcol<MP>(16 * I + li, g0 + 4 * s2 + kk)];
+        f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int k = 0; k < 16; ++k) lv[(q + 1) & 1][k] = lcol[17 + 16 * q + k];
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma_f64(a[s2], bt[s2], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lm[lcol<MP>(16 * I + kk + 4 * v, g0 + li)] = acc[v];
+      }
+      wave_lds_sync();
+      // trailing update: S_IJ -= L_IK L_JK^T for K < J <= I
+#pragma unroll
+      for (int J = K + 1; J < NB; ++J) {
+        double b[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) b[s2] = lm[lcol<MP>(16 * J + li, g0 + 4 * s2 + kk)];
+#pragma unroll
+        for (int I = J; I < NB; ++I) {
+          f64x4 acc;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 16 * I + kk + 4 * v, col = 16 * J + li;
+            acc[v] = row >= col ? lm[lcol<MP>(row, col)] : 0.0;
           }
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int c = 16 * q + k;   // acc[c] takes row j + 1 + c of column j
-            if (c < 63) acc[c] = __builtin_fma(x, lv[q & 1][k], acc[c + 1]);
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc = mfma_f64(-lm[lcol<MP>(16 * I + li, g0 + 4 * s2 + kk)], b[s2], acc);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 16 * I + kk + 4 * v, col = 16 * J + li;
+            if (row >= col) lm[lcol<MP>(row, col)] = acc[v];
           }
         }
-        acc[63] = 0.0;
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // X = Y L^-T in place, block column J, two 16-row tiles at a time
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    double la[4 * (NB - 1)];   // -L[16 J + li][4 q + kk], q < 4 J
+#pragma unroll
+    for (int q = 0; q < 4 * J; ++q) la[q] = -lm[lcol<MP>(16 * J + li, 4 * q + kk)];
+    double bt[4];               // T_JJ[li][4 s + kk]
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int cc = 4 * s2 + kk;
+      bt[s2] = li >= cc ? lm[lcol<MP>(16 * J + li, 16 * J + cc)] : 0.0;
+    }
+    const int col = 16 * J + li;   // the output column of this lane
+    const bool reseed = reseed_round >= 0 && col < m && dead[col] != 0;
+    for (int rt = 0; rt < nrt; rt += 2) {
+      f64x4 z[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* yrow = buf + (16 * (rt + h) + li) * BS;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) z[h][v] = (double)yrow[16 * J + kk + 4 * v];
+      }
+#pragma unroll
+      for (int q = 0; q < 4 * J; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          z[h] = mfma_f64(la[q], (double)buf[(16 * (rt + h) + li) * BS + 4 * q + kk], z[h]);
+      // lane 16 kk + li holds Z[16 rt + li][16 J + kk + 4 v] in register v: A[li][4 v + kk]
+      f64x4 x[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) x[h] = mfma_f64(z[h][s2], bt[s2], x[h]);
+      // lane 16 kk + li holds X[16 rt + kk + 4 v][16 J + li]
+      if (col < m) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = 16 * (rt + h) + kk + 4 * v;
+            buf[r * BS + col] = reseed ? seed_value(r, col, reseed_round + 1) : (float)x[h][v];
+          }
       }
     }
+    wave_lds_sync();
+  }
+}
+
+template <int MP>
+__device__ __forceinline__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
+                                          int reseed_round) {
+  if constexpr (MP > 32) {
+    orth_blocked<MP>(buf, lm, inv, dead, D, m, reseed_round);
   } else {
-    const int r0 = lane, r1 = lane + 64;
-    const bool on0 = r0 < D, on1 = r1 < D;
-    float* row0 = buf + r0 * BS;
-    float* row1 = buf + (on1 ? r1 : r0) * BS;
-    for (int j = 0; j < m; ++j) {
-      const double* lj = lm + lidx<MP>(j, 0);
-      double p0[4] = {0.0, 0.0, 0.0, 0.0}, p1[4] = {0.0, 0.0, 0.0, 0.0};
-      int a = 0;
-      for (; a + 4 <= j; a += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const double l = lj[a + u];
-          p0[u] += (double)row0[a + u] * l;
-          p1[u] += (double)row1[a + u] * l;
+    constexpr int BS = MP + 4;
+    const int lane = threadIdx.x & 63;
+#if KAMERA_ORTH_MFMA
+    // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
+    // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
+    // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
+    // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
+    // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
+    // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
+    // all the factorisation reads.
+    {
+      const int li = lane & 15, kk = lane >> 4;
+      const int nt = (m + 15) / 16;
+      for (int ta = 0; ta < nt; ++ta) {
+        for (int tb = 0; tb <= ta; ++tb) {
+          f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
+          const float* ya = buf + kk * BS + 16 * ta + li;
+          const float* yb = buf + kk * BS + 16 * tb + li;
+          for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
+            const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
+            const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
+            s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
+          }
+          // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
+            if (row < m && col <= row) lm[lidx<MP>(row, col)] = s0[v] + s1[v];
+          }
         }
       }
-      for (; a < j; ++a) {
-        const double l = lj[a];
-        p0[0] += (double)row0[a] * l;
-        p1[0] += (double)row1[a] * l;
-      }
-      const double s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
-      const double s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-      float v0 = (float)(((double)row0[j] - s0) * inv[j]);
-      float v1 = (float)(((double)row1[j] - s1) * inv[j]);
-      if (reseed_round >= 0 && dead[j]) {
-        v0 = seed_value(r0, j, reseed_round + 1);
-        v1 = seed_value(r1, j, reseed_round + 1);
-      }
-      if (on0) row0[j] = v0;
-      if (on1) row1[j] = v1;
     }
+#else
+    // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
+    const int npair = m * (m + 1) / 2;
+    for (int q = lane; q < npair; q += 64) {
+      int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
+      while (a * (a + 1) / 2 > q) --a;
+      while ((a + 1) * (a + 2) / 2 <= q) ++a;
+      const int b = q - a * (a + 1) / 2;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
+  #pragma unroll 2
+      for (int r = 0; r < D; r += 4) {
+  #pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
+      }
+      lm[lidx<MP>(a, b)] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+#endif
+    wave_lds_sync();
+    cholesky_wave<MP>(lm, inv, dead, m);
+    wave_lds_sync();
+    // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
+    // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
+    // pivot, so a reseeded x_ra adds nothing to the columns after it.
+      const int r0 = lane, r1 = lane + 64;
+      const bool on0 = r0 < D, on1 = r1 < D;
+      float* row0 = buf + r0 * BS;
+      float* row1 = buf + (on1 ? r1 : r0) * BS;
+      for (int j = 0; j < m; ++j) {
+        const double* lj = lm + lidx<MP>(j, 0);
+        double p0[4] = {0.0, 0.0, 0.0, 0.0}, p1[4] = {0.0, 0.0, 0.0, 0.0};
+        int a = 0;
+        for (; a + 4 <= j; a += 4) {
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const double l = lj[a + u];
+            p0[u] += (double)row0[a + u] * l;
+            p1[u] += (double)row1[a + u] * l;
+          }
+        }
+        for (; a < j; ++a) {
+          const double l = lj[a];
+          p0[0] += (double)row0[a] * l;
+          p1[0] += (double)row1[a] * l;
+        }
+        const double s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
+        const double s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+        float v0 = (float)(((double)row0[j] - s0) * inv[j]);
+        float v1 = (float)(((double)row1[j] - s1) * inv[j]);
+        if (reseed_round >= 0 && dead[j]) {
+          v0 = seed_value(r0, j, reseed_round + 1);
+          v1 = seed_value(r1, j, reseed_round + 1);
+        }
+        if (on0) row0[j] = v0;
+        if (on1) row1[j] = v1;
+      }
+    wave_lds_sync();
   }
-  wave_lds_sync();
 }
 
 #if KAMERA_SUBSPACE_MFMA
@@ -1301,10 +1388,9 @@ template <typename T, int MP, int WPB>
 __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspace_wave_kernel(CParams P) {
   constexpr int BS = MP + 4;
   __shared__ __align__(16) float buf_s[WPB][128 * BS];
-  __shared__ __align__(16) double lm_s[WPB][lm_size<MP>() + (MP == 64 ? 64 : 0)];
+  __shared__ __align__(16) double lm_s[WPB][lm_size<MP>()];
   __shared__ double inv_s[WPB][MP];
   __shared__ int dead_s[WPB][MP];
-  __shared__ __align__(16) double cj_s[WPB][MP > 32 ? 2 * MP : 2];   // published column of the Cholesky (MP 64)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = blockIdx.x * WPB + w;
   if (u >= P.n_total) return;   // whole wave; no block-wide barrier follows
@@ -1312,7 +1398,6 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
   double* lm = lm_s[w];
   double* inv = inv_s[w];
   int* dead = dead_s[w];
-  double* cj = cj_s[w];
 
   const int e = find_entry(P, u);
   const CJob& J = P.jobs[P.job_of[e]];
@@ -1422,10 +1507,10 @@ __global__ __launch_bounds__(64 * WPB) KAMERA_SUBSPACE_OCCUPANCY(MP) void subspa
     }
     wave_lds_sync();
 #endif
-    orth_wave<MP>(buf, lm, inv, dead, cj, D, m, round);
+    orth_wave<MP>(buf, lm, inv, dead, D, m, round);
   }
   // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
-  orth_wave<MP>(buf, lm, inv, dead, cj, D, m, -1);
+  orth_wave<MP>(buf, lm, inv, dead, D, m, -1);
 
   T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
   float* xg = P.ws + J.xbase + (int64_t)unit * D * MP;
