@@ -1650,6 +1650,25 @@ __host__ __device__ inline size_t stream_lds_bytes(int width, int mp, bool bf16)
 #endif
 constexpr int kStreamTokens = KAMERA_PROJ_TOKENS;   // tokens per block (512: 8 tiles per wave)
 
+// A finished 16-token tile of U held by one lane (its 4 column blocks x 4 rows) until it is
+// stored, in the output element type.
+template <typename T> struct UTile;
+template <> struct UTile<uint16_t> {
+  uint32_t w[8];
+  __device__ __forceinline__ void put(int k, float v) {
+    const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)v);   // RNE
+    w[k >> 1] = (k & 1) ? (w[k >> 1] | (h << 16)) : h;
+  }
+  __device__ __forceinline__ void store(uint16_t* p, int k) const {
+    *p = (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+  }
+};
+template <> struct UTile<float> {
+  float w[16];
+  __device__ __forceinline__ void put(int k, float v) { w[k] = v; }
+  __device__ __forceinline__ void store(float* p, int k) const { *p = w[k]; }
+};
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 2, 8))) void project_stream_kernel(CParams P) {
   extern __shared__ __align__(16) float vs[];   // permuted X [width][SV]
@@ -1765,8 +1784,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   }
   __syncthreads();
 
+  // A tile's U is stored during the next tile, just after that tile's loads are issued. The
+  // wait for the next rows (before they become the current ones) covers every earlier memory
+  // operation, since loads and stores share one counter; stored this way, the stores have had
+  // a tile's compute to complete by then, instead of being issued just before the wait.
+  UTile<T> prev;
+  int prev_tok = -1;   // first token of the tile in prev, or -1
+  auto flush = [&]() {
+    if (prev_tok < 0) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = 16 * q + n;
+      if (q < nrb && col < m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = prev_tok + 4 * g + i;
+          if (t < t_hi) prev.store(U + (int64_t)t * m + col, 4 * q + i);
+        }
+      }
+    }
+    prev_tok = -1;
+  };
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) load_unit(u + 1, nxt);
+    flush();
     const int it = u / nslab, c = u - it * nslab;
     const int tile_tok = t_lo + 16 * (wave + 4 * it);
     const int tok = tile_tok + n;
@@ -1862,19 +1903,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     if (c == nslab - 1) {
       // lane holds U rows tile_tok + 4g + i, column 16q + n
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 16 * q + n;
-        if (q < nrb && col < m) {
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tile_tok + 4 * g + i;
-            if (t < t_hi) store_elem(U + (int64_t)t * m + col, acc[q][i]);
-          }
-        }
-      }
+        for (int i = 0; i < 4; ++i) prev.put(4 * q + i, acc[q][i]);
+      prev_tok = tile_tok;
     }
     cur = nxt;
   }
+  flush();
 }
 
 // ---------------------------------------------------------------------------------------
