@@ -14,8 +14,9 @@
 //   16 lanes that hold a row, by DPP row operations), then O += P V on
 //   v_mfma_f32_16x16x16_bf16: each fp32 weight is cut exactly into three bf16 terms (hi by
 //   truncation, mid = trunc(p - hi), lo = p - hi - mid), so every product is exact and the sum
-//   keeps fp32 weights; the V tile passes through LDS as bf16. The four waves' states are
-//   merged in LDS and the segment's normalised output and lse are written to the workspace.
+//   keeps fp32 weights; the V tile passes through LDS as bf16 (the MLA and chunk kernels read
+//   its MFMA operands with the LDS transpose read). The four waves' states are merged in LDS
+//   and the segment's normalised output and lse are written to the workspace.
 // mla_segment_kernel: the same over an MLA cache in the absorbed form; the four waves split
 //   the 512 latent features, wave 0 also takes k_rope. The k_rope score MFMA is issued by the
 //   compiler for every wave under wave 0's condition (an empty exec mask elsewhere), and an MFMA
@@ -209,16 +210,28 @@ __device__ inline PSplit split_weights(const float* w4) {
   return s;
 }
 // o[c] += P V[:, 16 c ..] for c < n_blocks: lane (col, grp) holds the weights of query row col
-// for tokens 4 grp .. 4 grp + 3 (A operand) and reads V rows 4 grp + j, feature 16 c + col from
-// vcol = &V[4 grp][col] (bf16, row stride vs; B operand).
-template <int NC>
+// for tokens 4 grp .. 4 grp + 3 (A operand) and takes V rows 4 grp + j, feature 16 c + col
+// (bf16, row stride vs, vcol = &V[4 grp][col]; B operand). TR: with one LDS transpose read
+// (ds_read_b64_tr_b16): lane s of a 16-lane group points at row s / 4 of its group's four rows,
+// features 4 (s % 4) .. + 3 of the block, and lane i receives feature i of the four rows (the
+// lane layout was checked on the device); else with four 2-byte reads. The transpose read
+// took the MLA and chunk kernels 3 % faster and the GQA decode 0.5 % slower (interleaved A/B).
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <bool TR, int NC>
 __device__ inline void pv_accumulate(f32x4 (&o)[NC], const PSplit& w, const uint16_t* vcol, int vs,
                                      int n_blocks = NC) {
+  const int col = threadIdx.x & 15;
+  const uint16_t* tr = vcol - col + (col >> 2) * vs + 4 * (col & 3);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (c >= n_blocks) continue;
-    const uint16_t* v = vcol + 16 * c;
-    const s16x4 b = s16x4{(short)v[0], (short)v[vs], (short)v[2 * vs], (short)v[3 * vs]};
+    s16x4 b;
+    if constexpr (TR) {
+      b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr + 16 * c));
+    } else {
+      const uint16_t* v = vcol + 16 * c;
+      b = s16x4{(short)v[0], (short)v[vs], (short)v[2 * vs], (short)v[3 * vs]};
+    }
     o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.lo, b, o[c], 0, 0, 0);
     o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.mid, b, o[c], 0, 0, 0);
     o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(w.hi, b, o[c], 0, 0, 0);
@@ -317,7 +330,7 @@ void attn_segment_kernel(AParams P) {
     if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
     // O += P V
-    pv_accumulate(o, split_weights(&pt[wave][col * PS + 4 * grp]), &vt[wave][4 * grp * VS + col], VS);
+    pv_accumulate<false>(o, split_weights(&pt[wave][col * PS + 4 * grp]), &vt[wave][4 * grp * VS + col], VS);
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
     row = row_next;
 #pragma unroll
@@ -485,7 +498,7 @@ void mla_segment_kernel(AParams P) {
     softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PSTR + col], PSTR);
     if (any_moved(corr)) rescale_rows(o, corr);
     wave_lds_sync();
-    pv_accumulate(o, split_weights(&pt[wave][col * PSTR + 4 * grp]), &vt[wave][4 * grp * VS + col],
+    pv_accumulate<true>(o, split_weights(&pt[wave][col * PSTR + 4 * grp]), &vt[wave][4 * grp * VS + col],
                   VS);
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
   };
@@ -980,8 +993,8 @@ void chunk_attn_kernel(VParams P) {
     {
       const PSplit w = split_weights(&pt[wave][col * PSTR + 4 * grp]);
       const uint16_t* vcol = &vt[wave][4 * grp * VS + col];
-      pv_accumulate(o, w, vcol, VS);
-      pv_accumulate(z, w, vcol + D, VS, (mv + 15) / 16);
+      pv_accumulate<true>(o, w, vcol, VS);
+      pv_accumulate<true>(z, w, vcol + D, VS, (mv + 15) / 16);
     }
     wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
     cur = nxt;
