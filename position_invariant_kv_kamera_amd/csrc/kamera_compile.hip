@@ -11,8 +11,10 @@
 //
 // Kernels (one launch per class of tile / LDS size present in the batch):
 //   gram      partial Gram tiles Delta_s^T Delta_s over token splits s with fp32 MFMA
-//             16x16x4; one tile pair (bi <= bj) of G per block; Delta is formed on the fly
-//             (canonical rows rotated in fp32 with cos/sin from fp64, as the reuse kernels do);
+//             16x16x4 (unrotated bf16 heads of one ordering, the MLA latent: bf16 MFMA
+//             16x16x32 on an exact high/low bf16 split of Delta); one tile pair (bi <= bj) of G
+//             per block; Delta is formed on the fly (canonical rows rotated in fp32 with cos/sin
+//             from fp64, as the reuse kernels do);
 //   subspace  one wave per head (widths up to 128) or one block of four waves per head (the
 //             wide MLA latent): sums the partials into G where there are several, then block
 //             power iteration X <- orth(G X) from a fixed +-1 start, G X on fp32 MFMA. orth() is
@@ -40,6 +42,29 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Eight fp32 values as bf16 high parts (round to nearest) and the bf16 of what is left.
+__device__ __forceinline__ void split8_bf16(const float* x, bf16x8* hi, bf16x8* lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
+    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[e] = (uint32_t)bf16_rne(x[2 * e] - __uint_as_float((uint32_t)h0 << 16)) |
+           ((uint32_t)bf16_rne(x[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16)) << 16);
+  }
+  *hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  *lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
 
 // Subspace iteration: Y = G X on fp32 MFMA (1) or fp32 VALU FMA (0); S = Y^T Y on fp64 MFMA
 // (1) or fp64 VALU FMA (0).
@@ -332,8 +357,10 @@ __device__ __forceinline__ void pair_tiles(int pair, int nb, int* bi, int* bj) {
 // 4(l/16)..4(l/16)+3 of column l%16.
 // ---------------------------------------------------------------------------------------
 
+// Compiled for 3 waves per SIMD: the bf16 path of NB = 4 then keeps its accumulators and
+// operands in 162 VGPRs (the compiler's own choice, 2 waves, was 4.6 % slower on the MLA batch).
 template <typename T, int NB>
-__global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void gram_kernel(CParams P) {
   constexpr int TE = 32 * NB;
   constexpr int DS = TE + 16;   // row stride: the four token rows of an operand fall in
                                 // different LDS banks
@@ -418,25 +445,92 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(CParams P) {
           }
       };
       if (t_lo < t_hi) load_rows(t_lo);
-      for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
-        __syncthreads();   // the previous step's MFMAs are done with di / dj
+      if constexpr (sizeof(T) == 2) {
+        // bf16 rows: Delta = conditioned - canonical (exact in fp32) is cut into bf16 high and
+        // low parts, h = RNE(Delta), l = RNE(Delta - h), and the Gram is summed on
+        // v_mfma_f32_16x16x32_bf16 as l l + l h + h l + h h (products exact in fp32, fp32 sums).
+        // The difference of two bf16 values needs at most 16 significant bits when their
+        // exponents differ by less than 8, and h + l is then Delta exactly; otherwise l is
+        // rounded (at most 2^-18 of |Delta|). A 32-token step is one K step. The parts sit in
+        // LDS as [token][feature]; an operand (eight tokens of one feature per lane) is two LDS
+        // transpose reads (ds_read_b64_tr_b16: lane s of a 16-lane group points at row s / 4,
+        // features 4 (s % 4) .. + 3, and lane i receives feature i of the four rows).
+        constexpr int RS = TE + 16;   // bf16 row stride of a part
+        uint16_t* dih = reinterpret_cast<uint16_t*>(di);
+        uint16_t* dil = dih + kStepTokens * RS;
+        uint16_t* djh = reinterpret_cast<uint16_t*>(dj);
+        uint16_t* djl = djh + kStepTokens * RS;
+        const uint16_t* bh = bi == bj ? dih : djh;
+        const uint16_t* bl = bi == bj ? dil : djl;
+        const int li = lane & 15, kg = lane >> 4;
+        const int tro = (8 * kg + (li >> 2)) * RS + 4 * (li & 3);   // this lane's transpose-read offset
+        auto operand = [&](const uint16_t* part, int f0) {
+          const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(part + tro + f0));
+          const s16x4 b =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(part + tro + 4 * RS + f0));
+          return __builtin_bit_cast(bf16x8, s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+        };
+        for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+          __syncthreads();   // the previous step's MFMAs are done with the parts
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            if (tt < ntile) {
-              const int g = threadIdx.x + kThreads * k;
-              float x[8], c[8];
-              piece_floats(px[tt][k], x);
-              piece_floats(pc[tt][k], c);
-              float* d = (tt ? dj : di) + (g >> 4) * DS + 8 * (g & 15);
+            for (int k = 0; k < 2; ++k) {
+              if (tt < ntile) {
+                const int g = threadIdx.x + kThreads * k;
+                float x[8], c[8], d[8];
+                piece_floats(px[tt][k], x);
+                piece_floats(pc[tt][k], c);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+                for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+                bf16x8 h, l;
+                split8_bf16(d, &h, &l);
+                const int at = (g >> 4) * RS + 8 * (g & 15);
+                *reinterpret_cast<bf16x8*>((tt ? djh : dih) + at) = h;
+                *reinterpret_cast<bf16x8*>((tt ? djl : dil) + at) = l;
+              }
+            }
+          __syncthreads();
+          if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
+          bf16x8 bhv[NB], blv[NB];
+#pragma unroll
+          for (int y = 0; y < NB; ++y) {
+            bhv[y] = operand(bh, c0 + 16 * y);
+            blv[y] = operand(bl, c0 + 16 * y);
+          }
+#pragma unroll
+          for (int x = 0; x < NB; ++x) {
+            const bf16x8 ah = operand(dih, r0 + 16 * x), al = operand(dil, r0 + 16 * x);
+#pragma unroll
+            for (int y = 0; y < NB; ++y) {
+              acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, blv[y], acc[x][y], 0, 0, 0);
+              acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bhv[y], acc[x][y], 0, 0, 0);
+              acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, blv[y], acc[x][y], 0, 0, 0);
+              acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bhv[y], acc[x][y], 0, 0, 0);
             }
           }
-        __syncthreads();
-        if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
-        mfma_step();
+        }
+      } else {
+        for (int tok0 = t_lo; tok0 < t_hi; tok0 += kStepTokens) {
+          __syncthreads();   // the previous step's MFMAs are done with di / dj
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              if (tt < ntile) {
+                const int g = threadIdx.x + kThreads * k;
+                float x[8], c[8];
+                piece_floats(px[tt][k], x);
+                piece_floats(pc[tt][k], c);
+                float* d = (tt ? dj : di) + (g >> 4) * DS + 8 * (g & 15);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+              }
+            }
+          __syncthreads();
+          if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
+          mfma_step();
+        }
       }
       done = true;
     }
@@ -1617,26 +1711,6 @@ __global__ __launch_bounds__(kThreads) void project_kernel(CParams P) {
 // Each wave keeps the loads of its next (tile, slab) in flight while it computes the current
 // one. Other shapes use project_kernel.
 // ---------------------------------------------------------------------------------------
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
-// Eight fp32 values as bf16 high parts (round to nearest) and the bf16 of what is left.
-__device__ __forceinline__ void split8_bf16(const float* x, bf16x8* hi, bf16x8* lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint16_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
-    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[e] = (uint32_t)bf16_rne(x[2 * e] - __uint_as_float((uint32_t)h0 << 16)) |
-           ((uint32_t)bf16_rne(x[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16)) << 16);
-  }
-  *hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
-  *lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
-}
 
 // Dynamic LDS of the streamed projection: bf16 data keeps X^T as bf16 high and low parts
 // (rows of width + 8), fp32 data X in fp32 with stream_sv columns.
