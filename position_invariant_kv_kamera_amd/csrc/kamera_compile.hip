@@ -106,6 +106,7 @@ struct alignas(16) CJob {
   int32_t rot_dim;  // features of each head that turn (the rest pass through); pairs rot_dim/2
   int32_t member_off, n_members;   // this job's orderings in the member table
   int32_t gperm;   // 1: G is stored with its rows and columns permuted (gram_stream_kernel)
+  int32_t gsplit;  // 1: G by gram_split_kernel (128-wide bf16 heads, natural order)
 };
 
 struct CParams {
@@ -749,6 +750,225 @@ void gram_stream_kernel(CParams P) {
       gout[(16 * b + i) * 128 + 16 * b2 + j] = src[i * 16 + j];
       if (b2 != b) gout[(16 * b2 + i) * 128 + 16 * b + j] = src[j * 16 + i];
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// gram_split_kernel: the Gram of 128-wide bf16 heads on bf16 MFMA. Delta (fp32, formed as
+// stage_delta forms it) is cut into bf16 high and low parts by round to nearest, h = RNE(Delta),
+// l = RNE(Delta - h) (the subtraction is exact), and each 16 x 16 block pair (a <= b) of G sums
+// l l, l h, h l, h h on v_mfma_f32_16x16x32_bf16 (products exact in fp32, fp32 sums). For an
+// unrotated head of one ordering Delta is the difference of two bf16 values, and h + l is
+// Delta exactly unless their exponents differ by 8 or more; otherwise (and for rotated heads,
+// whose Delta has 24 significant bits) l is rounded, by at most 2^-18 of |Delta|, an error that
+// varies in sign from token to token and so mostly cancels in the sum over tokens (a third part
+// made the products exact to fp32 but the whole compile 4 % slower). A step stages 32 tokens of
+// the parts in LDS as [token][feature] (a thread forms 16 features of one token: both members
+// of its RoPE pairs, or 16 features passing through) and is one K step; wave w takes the 9
+// block pairs (w, w..7) and (7 - w, 7 - w..7), its operands (eight tokens of one feature per
+// lane) by LDS transpose reads (ds_read_b64_tr_b16). Rows are loaded two steps ahead (three
+// register buffers in rotation, so no register copy waits for a load). G is written in natural
+// feature order, both triangles, exactly symmetric (gperm = 0).
+// ---------------------------------------------------------------------------------------
+
+constexpr int kSplitStep = 32;   // tokens per step: one K step of the bf16 MFMA
+
+// MULTI: several orderings (their conditioned rows are averaged); a separate instantiation, so
+// that the plain one has no load under a branch in its step loop.
+template <typename T, bool MULTI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void gram_split_kernel(CParams P) {
+  static_assert(sizeof(T) == 2, "bf16 rows");
+  constexpr int RS = 128 + 16;   // bf16 row stride of a part
+  __shared__ __align__(16) uint16_t parts[2][kSplitStep * RS];
+  __shared__ float2 cs[64];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int local = blockIdx.x - P.starts[e];
+  const int split = local % J.splits;
+  const int unit = local / J.splits;
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t_lo = split * J.split_tokens;
+  const int t_hi = min(J.n_tokens, t_lo + J.split_tokens);
+  const int nsteps = t_hi > t_lo ? (t_hi - t_lo + kSplitStep - 1) / kSplitStep : 0;
+
+  // this thread's item of a step: token row r, feature group q (features fa..fa+7, fb..fb+7)
+  const int r = tid >> 3, q = tid & 7;
+  const int R = J.rotate ? J.rot_dim : 0;   // a multiple of 16 (host)
+  const bool half = P.layout == KAMERA_ROPE_HALF_SPLIT;
+  const int gr = R / 16;
+  const bool turn = q < gr;
+  const int fa = turn ? (half ? 8 * q : 16 * q) : R + 16 * (q - gr);
+  const int fb = turn ? (half ? R / 2 + 8 * q : 16 * q + 8) : fa + 8;
+  const CMember* mem = P.members + J.member_off;
+  const int K = J.n_members;
+  const int64_t head_off = (int64_t)head * 128;
+  const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off;
+  const T* cond0 = static_cast<const T*>(mem[0].cond) + layer * mem[0].cond_ls + head_off;
+  // row strides in registers: a barrier is a memory fence, after which fields read through J
+  // would be loaded again (and a load's wait would also wait for the rows in flight)
+  const int64_t canon_ts = J.canon_ts, cond_ts = mem[0].cond_ts;
+
+  // The row loads are issued unconditionally (a token past the split reads the split's first
+  // row and is zeroed when staged): the compiler can then wait for one buffer's loads with a
+  // partial count, where a load under a branch makes it wait for every load in flight.
+  struct Rows {
+    Piece<T> xa, xb, ca, cb;
+    bool ok;
+  };
+  auto load_rows = [&](int st, Rows& b) {
+    const int tok0 = t_lo + kSplitStep * st + r;
+    b.ok = st < nsteps && tok0 < t_hi;
+    const int64_t tok = b.ok ? tok0 : t_lo;
+    load_piece(canon + tok * canon_ts + fa, b.xa);
+    load_piece(canon + tok * canon_ts + fb, b.xb);
+    load_piece(cond0 + tok * cond_ts + fa, b.ca);
+    load_piece(cond0 + tok * cond_ts + fb, b.cb);
+  };
+  auto stage = [&](int st, const Rows& b) {
+    const int tok = t_lo + kSplitStep * st + r;
+    float xa[8], xb[8], da[8], db[8];
+    piece_floats(b.xa, xa);
+    piece_floats(b.xb, xb);
+    piece_floats(b.ca, da);
+    piece_floats(b.cb, db);
+    if (!b.ok) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xa[i] = xb[i] = da[i] = db[i] = 0.f;
+    }
+    if (MULTI && b.ok) {
+      // several orderings: the mean of their conditioned rows
+      for (int k = 1; k < K; ++k) {
+        const T* ck = static_cast<const T*>(mem[k].cond) + layer * mem[k].cond_ls + head_off +
+                      (int64_t)tok * mem[k].cond_ts;
+        float ya[8], yb[8];
+        load8(ck + fa, ya);
+        load8(ck + fb, yb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          da[i] += ya[i];
+          db[i] += yb[i];
+        }
+      }
+      const float inv_k = 1.0f / (float)K;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        da[i] *= inv_k;
+        db[i] *= inv_k;
+      }
+    }
+    if (!turn) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        da[i] = da[i] - xa[i];
+        db[i] = db[i] - xb[i];
+      }
+    } else if (half) {
+      // pair 8 q + i = (feature fa + i, feature fb + i)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = cs[8 * q + i].x, sn = cs[8 * q + i].y;
+        const float x = xa[i], y = xb[i];
+        da[i] = da[i] - (x * c - y * sn);
+        db[i] = db[i] - (y * c + x * sn);
+      }
+    } else {
+      // pairs 8 q .. 8 q + 3 are adjacent features of piece a, 8 q + 4 .. 8 q + 7 of piece b
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = cs[8 * q + i].x, sn = cs[8 * q + i].y;
+        const float x = xa[2 * i], y = xa[2 * i + 1];
+        da[2 * i] = da[2 * i] - (x * c - y * sn);
+        da[2 * i + 1] = da[2 * i + 1] - (y * c + x * sn);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = cs[8 * q + 4 + i].x, sn = cs[8 * q + 4 + i].y;
+        const float x = xb[2 * i], y = xb[2 * i + 1];
+        db[2 * i] = db[2 * i] - (x * c - y * sn);
+        db[2 * i + 1] = db[2 * i + 1] - (y * c + x * sn);
+      }
+    }
+    bf16x8 h, l;
+    split8_bf16(da, &h, &l);
+    *reinterpret_cast<bf16x8*>(parts[0] + r * RS + fa) = h;
+    *reinterpret_cast<bf16x8*>(parts[1] + r * RS + fa) = l;
+    split8_bf16(db, &h, &l);
+    *reinterpret_cast<bf16x8*>(parts[0] + r * RS + fb) = h;
+    *reinterpret_cast<bf16x8*>(parts[1] + r * RS + fb) = l;
+  };
+
+  const int li = lane & 15, kg = lane >> 4;
+  const int tro = (8 * kg + (li >> 2)) * RS + 4 * (li & 3);   // transpose-read offset
+  auto operand = [&](int p, int blk) {
+    const uint16_t* src = parts[p] + tro + 16 * blk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 4 * RS));
+    return __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  const int first = 8 - wave;   // slots of row block `wave`; the rest are row block 7 - wave
+  f32x4 acc[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto products = [&]() {
+    bf16x8 ah, al;
+#pragma unroll
+    for (int sl = 0; sl < 9; ++sl) {
+      const int a = sl < first ? wave : 7 - wave;
+      const int b = sl < first ? wave + sl : 7 - wave + (sl - first);
+      if (sl == 0 || sl == first) {
+        ah = operand(0, a);
+        al = operand(1, a);
+      }
+      const bf16x8 bh = operand(0, b), bl = operand(1, b);
+      acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl, acc[sl], 0, 0, 0);
+      acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[sl], 0, 0, 0);
+      acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[sl], 0, 0, 0);
+      acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[sl], 0, 0, 0);
+    }
+  };
+
+  if (nsteps == 0) {   // an empty split (no rows to read): its partial G is zero
+    float* gz = P.ws + J.gpart + ((int64_t)unit * J.splits + split) * (128 * 128);
+    for (int i = tid; i < 128 * 128; i += kThreads) gz[i] = 0.f;
+    return;
+  }
+  Rows b0, b1, b2;
+  load_rows(0, b0);
+  load_rows(1, b1);
+  // the phase table after the first loads, so their latency overlaps it (the first step's
+  // barrier publishes it)
+  if (J.rotate) fill_phases(cs, J, P);
+  auto step = [&](int st, const Rows& cur, Rows& ahead) {
+    __syncthreads();   // the previous step's products are done with the parts
+    stage(st, cur);
+    __syncthreads();
+    load_rows(st + 2, ahead);   // into the buffer staged one step ago
+    products();
+  };
+  // whole rounds of three steps (steps past the split stage zeros): no branch in the loop
+  for (int st = 0; st < nsteps; st += 3) {
+    step(st, b0, b2);
+    step(st + 1, b1, b0);
+    step(st + 2, b2, b1);
+  }
+
+  // both triangles of each block pair, mirrored so that G is exactly symmetric
+  float* gout = P.ws + J.gpart + ((int64_t)unit * J.splits + split) * (128 * 128);
+#pragma unroll
+  for (int sl = 0; sl < 9; ++sl) {
+    const int a = sl < first ? wave : 7 - wave;
+    const int b = sl < first ? wave + sl : 7 - wave + (sl - first);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * a + 4 * kg + v, col = 16 * b + li;
+      if (a != b || row >= col) {
+        gout[row * 128 + col] = acc[sl][v];
+        gout[col * 128 + row] = acc[sl][v];
+      }
+    }
+  }
 }
 
 // Shared by both subspace kernels: the fixed +-1 start, the storage of S and L, and the
@@ -2126,7 +2346,11 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
         plan->members.push_back(c);
       }
       J.rot_dim = g.rotate ? M.rope_dim : 0;
-      J.gperm = g.width == 128 ? 1 : 0;   // gram_stream_kernel
+      // 128-wide heads: gram_split_kernel for bf16 rows whose turning features come in whole
+      // 16-feature groups (G in natural order), else gram_stream_kernel (G permuted)
+      J.gsplit = M.dtype == KAMERA_DTYPE_BF16 && g.width == 128 &&
+                 (!g.rotate || M.rope_dim % 16 == 0) ? 1 : 0;
+      J.gperm = g.width == 128 && !J.gsplit ? 1 : 0;
       J.n_tokens = k.n_tokens;
       J.m = k.m;
       J.mp = (k.m + 15) / 16 * 16;
@@ -2185,7 +2409,7 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     const int tblocks = stream ? (J.n_tokens + kStreamTokens - 1) / kStreamTokens
                                : (J.n_tokens + kProjTokens - 1) / kProjTokens;
     const size_t lds = stream ? stream_lds_bytes(J.width, J.mp, M.dtype == KAMERA_DTYPE_BF16) : 0;
-    bool ok = add(kGram, J.gperm ? 0 : J.te / 32, (int)j,
+    bool ok = add(kGram, J.gsplit ? (J.n_members > 1 ? 6 : 5) : (J.gperm ? 0 : J.te / 32), (int)j,
                   (int64_t)J.n_units * J.n_pairs * J.splits) &&
               add(kSubspace, subspace_class(J.width, J.mp), (int)j, J.n_units) &&
               add(kProject, stream ? 2 : (J.width <= 128 ? 0 : 1), (int)j,
@@ -2302,6 +2526,14 @@ hipError_t launch_one(const Launch& L, CParams P, hipStream_t stream) {
         case 2: gram_kernel<T, 2><<<grid, block, 0, stream>>>(P); break;
         case 3: gram_kernel<T, 3><<<grid, block, 0, stream>>>(P); break;
         case 4: gram_kernel<T, 4><<<grid, block, 0, stream>>>(P); break;
+        case 5:
+        case 6:
+          if constexpr (sizeof(T) == 2) {
+            if (L.cls == 5) gram_split_kernel<T, false><<<grid, block, 0, stream>>>(P);
+            else gram_split_kernel<T, true><<<grid, block, 0, stream>>>(P);
+            break;
+          }
+          return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
       }
       break;
