@@ -424,26 +424,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
       const CMember& m0 = P.members[J.member_off];
       const T* cond = static_cast<const T*>(m0.cond) + layer * m0.cond_ls + head_off;
       const int ntile = bi == bj ? 1 : 2;
+      // Row loads are unconditional (a token past the split reads the split's first row, and
+      // a diagonal pair loads its one tile twice; both are zeroed or ignored when staged) and
+      // the row strides sit in registers: a load under a branch, or a field read through J
+      // after a barrier (a memory fence), would make the compiler wait for every load in
+      // flight instead of this step's.
+      const int64_t canon_ts = J.canon_ts, cond_ts = m0.cond_ts;
       Piece<T> px[2][2], pc[2][2];
+      bool pok[2];
       auto load_rows = [&](int tok0) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int k = 0; k < 2; ++k) {
+          const int g = threadIdx.x + kThreads * k;
+          const int tok = tok0 + (g >> 4);
+          pok[k] = tok < t_hi;
+          const int64_t tk = pok[k] ? tok : t_lo;
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int g = threadIdx.x + kThreads * k;
-            const int tok = tok0 + (g >> 4);
+          for (int tt = 0; tt < 2; ++tt) {
             const int col = (tt ? bj : bi) * TE + 8 * (g & 15);
-            if (tt < ntile && tok < t_hi) {
-              load_piece(canon + (int64_t)tok * J.canon_ts + col, px[tt][k]);
-              load_piece(cond + (int64_t)tok * m0.cond_ts + col, pc[tt][k]);
-            } else {
-#pragma unroll
-              for (int w = 0; w < (int)(sizeof(T) / 2); ++w) {
-                px[tt][k].w[w] = u32x4{0u, 0u, 0u, 0u};
-                pc[tt][k].w[w] = u32x4{0u, 0u, 0u, 0u};
-              }
-            }
+            load_piece(canon + tk * canon_ts + col, px[tt][k]);
+            load_piece(cond + tk * cond_ts + col, pc[tt][k]);
           }
+        }
       };
       if (t_lo < t_hi) load_rows(t_lo);
       if constexpr (sizeof(T) == 2) {
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
                 piece_floats(px[tt][k], x);
                 piece_floats(pc[tt][k], c);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+                for (int e = 0; e < 8; ++e) d[e] = pok[k] ? c[e] - x[e] : 0.f;
                 bf16x8 h, l;
                 split8_bf16(d, &h, &l);
                 const int at = (g >> 4) * RS + 8 * (g & 15);
@@ -492,7 +494,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
               }
             }
           __syncthreads();
-          if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
+          load_rows(tok0 + kStepTokens);   // past the split: clamped, never staged
+          // keep the next rows' loads here, ahead of this step's products (left to itself the
+          // compiler moves them to the next step, just before their use)
+          __builtin_amdgcn_sched_barrier(0);
           bf16x8 bhv[NB], blv[NB];
 #pragma unroll
           for (int y = 0; y < NB; ++y) {
@@ -525,11 +530,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
                 piece_floats(pc[tt][k], c);
                 float* d = (tt ? dj : di) + (g >> 4) * DS + 8 * (g & 15);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d[e] = c[e] - x[e];
+                for (int e = 0; e < 8; ++e) d[e] = pok[k] ? c[e] - x[e] : 0.f;
               }
             }
           __syncthreads();
-          if (tok0 + kStepTokens < t_hi) load_rows(tok0 + kStepTokens);
+          load_rows(tok0 + kStepTokens);   // past the split: clamped, never staged
           mfma_step();
         }
       }
