@@ -583,8 +583,16 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
         per_call_us = tot_ns / calls / 1e3
         if k == "gram":
             tf = gram_f / (per_call_us * 1e-6) / 1e12
-            lines.append(f"| gram (Delta^T Delta, fp32 MFMA) | {n} | {per_call_us:.1f} | mfma fp32 | "
-                         f"{tf:.1f} TFLOP/s | {tf / FP32_PEAK_TFLOPS:.3f} |")
+            if rec.get("dtype") == "bf16":
+                # bf16 rows: the Gram runs on bf16 MFMA over high/low parts of Delta, far from
+                # that unit's peak; it is bounded by reading its inputs
+                gbps = read2 / (per_call_us * 1e-6) / 1e9
+                lines.append(f"| gram (Delta^T Delta, bf16 MFMA on split parts; {tf:.0f} TFLOP/s of "
+                             f"distinct entries) | {n} | {per_call_us:.1f} | hbm | "
+                             f"{gbps:.0f} GB/s | {gbps / HBM_PEAK_GBPS:.3f} |")
+            else:
+                lines.append(f"| gram (Delta^T Delta, fp32 MFMA) | {n} | {per_call_us:.1f} | mfma fp32 | "
+                             f"{tf:.1f} TFLOP/s | {tf / FP32_PEAK_TFLOPS:.3f} |")
         elif k == "project":
             gbps = read2 / (per_call_us * 1e-6) / 1e9
             lines.append(f"| project (U = Delta V) | {n} | {per_call_us:.1f} | hbm | "
@@ -593,7 +601,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
             lines.append(f"| subspace iteration | {n} | {per_call_us:.1f} | issue (MFMA products, fp64 factorisation chains) | - | - |")
     lines += ["", "Gram flops per call: n D (D + 1) per head (the distinct entries of the "
               "symmetric product) = "
-              f"{gram_f / 1e9:.1f} GFLOP; projection bytes per call: both inputs once = "
+              f"{gram_f / 1e9:.1f} GFLOP; Gram and projection bytes per call: both inputs once = "
               f"{read2 / 1e9:.3f} GB.", "",
               "## rocprofv3 --kernel-trace --stats (top kernels)", "",
               "| kernel | calls | avg us | total % |", "|---|---|---|---|"]
