@@ -283,8 +283,10 @@ typedef struct kamera_factors_out {
  * as kamera_src), the shift delta between the two (position of the chunk in the conditioned
  * pass minus its canonical position), the rank m (both channels) and the output factors.
  * Supported: rotated channel width a multiple of 32 up to 128; unrotated width that, or a
- * multiple of 128 up to 512; m in [1, 64], m <= width, and m <= 32 for widths above 128. Input
- * rows must start on 16-byte boundaries (pointer and strides), else KAMERA_ERR_UNSUPPORTED.
+ * multiple of 128 up to 512; a partially rotary head with rope_dim a multiple of 16 and
+ * head_dim - rope_dim a multiple of 8; m in [1, 64], m <= width, and m <= 32 for widths above
+ * 128. Input rows must start on 16-byte boundaries (pointer and strides), else
+ * KAMERA_ERR_UNSUPPORTED.
  * A chunk with n_tokens == 0 is skipped and its outputs are not written. Where Delta offers
  * fewer than m independent directions (Delta = 0, n_tokens < m), the surplus columns of V are
  * zero or directions on which Delta vanishes to rounding, and U's columns there are ~0. */
@@ -302,7 +304,8 @@ typedef struct kamera_compile_chunk {
 
 /* Bytes of workspace kamera_patch_compile needs for these chunks (fp32 Gram matrices and bases
  * of every layer and head, plus the job table); depends only on the model and each chunk's
- * n_tokens and m (pointers are not read). 0 if the arguments are invalid. */
+ * n_tokens and m (pointers are not read). 0 if the arguments are invalid or unsupported
+ * (kamera_last_error() says which check failed). */
 size_t kamera_compile_workspace_bytes(const kamera_model* model,
                                       const kamera_compile_chunk* chunks, int32_t n_chunks);
 

@@ -137,6 +137,8 @@ def test_n_iter_range(n_iter):
     (dict(head_dim=48, rope_dim=48), {}, kb.KAMERA_ERR_UNSUPPORTED),      # not a multiple of 32
     (dict(head_dim=256, rope_dim=256), {}, kb.KAMERA_ERR_UNSUPPORTED),    # rotated width > 128
     (dict(head_dim=32, rope_dim=32), dict(m=33), kb.KAMERA_ERR_INVALID_ARGUMENT),  # m > width
+    (dict(head_dim=128, rope_dim=40), {}, kb.KAMERA_ERR_UNSUPPORTED),     # partial, 40 % 16
+    (dict(head_dim=128, rope_dim=124), {}, kb.KAMERA_ERR_UNSUPPORTED),    # pass-through 4 wide
 ])
 def test_geometry_validation(kw, chunk_kw, status):
     m = _model(**kw)

@@ -135,6 +135,7 @@ def test_compile_with_partial_rotary():
     (128, 32, oracle.HALF_SPLIT),
     (64, 32, oracle.HALF_SPLIT),
     (128, 32, oracle.INTERLEAVED),
+    (128, 48, oracle.INTERLEAVED),    # three whole 16-feature groups turn, five pass through
 ])
 def test_compile_with_partial_rotary_other_widths(head_dim, rope_dim, layout):
     case = cc.Case(f"partial_{rope_dim}_of_{head_dim}_{layout}", "gqa", "bf16", 2, 2, head_dim,
