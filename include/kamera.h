@@ -372,7 +372,9 @@ kamera_status kamera_patch_compile_orbit(const kamera_model* model,
  *     out[(j*n_q_heads + h)*head_dim + f] = sum_t softmax(scores)_t v_tf      (fp32)
  *     lse[j*n_q_heads + h] = log sum_t exp(score_t)                          (fp32, natural)
  * (out = 0 and lse = -inf when kv_len == 0). The key ranges are cut into segments of 2048,
- * 1024 or KAMERA_ATTN_SEGMENT tokens (the longest that still gives the call 2048 blocks);
+ * 1024 or KAMERA_ATTN_SEGMENT tokens (4096 too with n_kv_heads a multiple of 4), the longest
+ * that still gives the call 2048 blocks (one per segment and KV head), or 512 blocks where
+ * n_kv_heads is a multiple of 4 (one per segment and quad of KV heads, reading whole rows);
  * each is attended on its own (Q K^T with bf16 MFMA, exact products; scores in base 2, the
  * fp32 dot product times scale log2(e) rounded once to fp32, weights 2^(s - max) from the
  * hardware exp2; the weights stay fp32 for P V, fp32 MFMA) and the segments are combined with
@@ -391,7 +393,7 @@ typedef struct kamera_attn_query {
 } kamera_attn_query;
 
 /* Shortest key segment one block of kamera_decode_attention attends (calls with enough work
- * take 1024 or 2048). */
+ * take 1024, 2048 or 4096). */
 #define KAMERA_ATTN_SEGMENT 512
 
 /* Workspace bytes for kamera_decode_attention (0 on invalid arguments). */

@@ -4,11 +4,14 @@
 // The Kamera abstract states that the direct readout of a cached chunk is recovered exactly
 // by the standard state merge: attention over several key sets equals the log-sum-exp
 // weighted combination of the attention over each. Decode attention is built on it: each
-// segment (2048, 1024 or 512 tokens, per call) of a query's key range is one block, attended
-// on its own, and the segments are merged.
+// segment (4096, 2048, 1024 or 512 tokens, per call) of a query's key range is attended on its
+// own, and the segments are merged.
 //
-// attn_segment_kernel<D>: block = (segment, KV head), 4 waves; wave w takes the 16-token
-//   tiles w, w+4, ... of the segment. Per tile: S = Q K^T with v_mfma_f32_16x16x32_bf16 (the
+// attn_rows_kernel<D>: GQA/MHA with n_kv_heads a multiple of 4: block = (segment, quad of KV
+//   heads), wave w takes KV head 4 q + w over every 16-token tile of the segment, so each
+//   tile's rows are read across four heads at once; each wave writes its head's part.
+// attn_segment_kernel<D>: other head counts: block = (segment, KV head), 4 waves; wave w takes
+//   the 16-token tiles w, w+4, ... of the segment. Per tile: S = Q K^T with v_mfma_f32_16x16x32_bf16 (the
 //   query heads of the KV head are the 16 MFMA rows, padded; q and k are bf16 already, so
 //   the products are exact), online softmax per query row in base 2 (max and sum across the
 //   16 lanes that hold a row, by DPP row operations), then O += P V on
@@ -42,11 +45,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Segment length: the longest of 2048, 1024 and 512 tokens that still gives the call at least
-// kTargetSegBlocks blocks (long segments amortise a block's set-up and merge; short ones keep a
-// single long context spread over the chip).
-constexpr int kSegChoices[3] = {2048, 1024, KAMERA_ATTN_SEGMENT};
+// Segment length: the longest of the choices that still gives the call at least
+// kTargetSegBlocks blocks, or kTargetRowBlocks for attn_rows_kernel (long segments amortise a
+// block's set-up and merge; short ones keep a single long context spread over the chip). On
+// 64 x 16K tokens of 4 KV heads the rows kernel took 0.389 ms per call at 512 blocks (2048-token
+// segments), 0.410 at 1024, 0.428 at 2048 and 0.42 at 256 (4096-token segments); the MLA
+// kernel is fastest at 2048 blocks.
+constexpr int kSegChoices[4] = {4096, 2048, 1024, KAMERA_ATTN_SEGMENT};
 constexpr int64_t kTargetSegBlocks = 2048;
+constexpr int64_t kTargetRowBlocks = 512;   // attn_rows_kernel
 constexpr int kThreads = 256;
 constexpr int kTile = 16;
 constexpr int kMaxGroup = 16;
@@ -238,15 +245,107 @@ __device__ inline void pv_accumulate(f32x4 (&o)[NC], const PSplit& w, const uint
   }
 }
 
+// One wave's pass over KV head h for query j: the 16-token tiles starting at t0, t0 + step, ...
+// below t_hi, into the online-softmax state of the head's query rows (lane: rows 4 grp + r, m
+// and l in base 2, o unnormalised; all 16 lanes of a row group hold the same m and l). vt and
+// pt are the wave's own LDS tiles.
+template <int D>
+__device__ __forceinline__ void attend_tiles(const AParams& P, int j, int h, int t0, int t_hi,
+                                             int step, uint16_t* vt, float* pt, float (&m)[4],
+                                             float (&l)[4], f32x4 (&o)[D / 16]) {
+  constexpr int KS = D / 32;   // bf16 MFMA k-steps of Q K^T
+  constexpr int NC = D / 16;   // 16-feature column blocks of O
+  constexpr int VS = D + 8;    // LDS row stride of a V tile (bf16): rows start in distinct banks
+  constexpr int PS = 17;       // LDS row stride of a P tile (fp32)
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Q rows: query heads h*group + col (rows past the group are zero)
+  bf16x8 qa[KS];
+  {
+    const bool on = col < P.group;
+    const uint16_t* qp = P.q + ((int64_t)j * P.n_q + h * P.group + (on ? col : 0)) * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const u32x4 w = on ? *reinterpret_cast<const u32x4*>(qp + 32 * k + 8 * grp)
+                         : u32x4{0u, 0u, 0u, 0u};
+      qa[k] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int koff = h * D;
+  auto load_tile = [&](int64_t row, bf16x8* kb, u32x4* vr) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (row >= 0) {
+        kb[k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(P.kpool + row + koff + 32 * k + 8 * grp));
+        vr[k] = *reinterpret_cast<const u32x4*>(P.vpool + row + koff + 32 * k + 8 * grp);
+      } else {
+        kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        vr[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto row_of = [&](int t, int32_t pe) { return t + col < t_hi ? row_at(P, t + col, pe) : -1; };
+  auto entry_of = [&](int t) { return page_entry(P, t + col, t + col < t_hi); };
+  auto tile_step = [&](int64_t row, const bf16x8* kb, const u32x4* vraw) {
+    // S: lane holds query rows 4 grp + r of token col
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], kb[k], sacc, 0, 0, 0);
+    // the V tile goes to LDS (token col, features 32k + 8 grp ..)
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      *reinterpret_cast<u32x4*>(&vt[col * VS + 32 * k + 8 * grp]) = vraw[k];
+    float s2[4], corr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s2[r] = row >= 0 ? sacc[r] * P.scale : -INFINITY;
+    softmax_step(s2, m, l, corr, &pt[4 * grp * PS + col], PS);
+    if (any_moved(corr)) rescale_rows(o, corr);
+    wave_lds_sync();
+    // O += P V
+    pv_accumulate<false>(o, split_weights(&pt[col * PS + 4 * grp]), &vt[4 * grp * VS + col], VS);
+    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+  };
+  // software pipeline: the K and V rows of the next tile are in flight while this tile is
+  // computed (two tiles ahead, at two waves per SIMD, was 5 % slower in attn_rows_kernel);
+  // page-table entries are fetched one tile before the rows they locate
+  bf16x8 kb[KS], kb_n[KS];
+  u32x4 vraw[KS], vraw_n[KS];
+  int64_t row = row_of(t0, entry_of(t0));
+  int32_t pe_n = entry_of(t0 + step);
+  load_tile(row, kb, vraw);
+  for (; t0 < t_hi; t0 += step) {
+    const int64_t row_n = row_of(t0 + step, pe_n);
+    load_tile(row_n, kb_n, vraw_n);
+    pe_n = entry_of(t0 + 2 * step);
+    tile_step(row, kb, vraw);
+    row = row_n;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      kb[k] = kb_n[k];
+      vraw[k] = vraw_n[k];
+    }
+  }
+}
+
 // Compiled for 3 waves per SIMD: 151 VGPRs at D = 128, no spills (the unconstrained choice,
 // 184 registers at 2 waves per SIMD, streamed ~12 % slower; 4 waves spill).
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void attn_segment_kernel(AParams P) {
-  constexpr int KS = D / 32;   // bf16 MFMA k-steps of Q K^T
-  constexpr int NC = D / 16;   // 16-feature column blocks of O
-  constexpr int VS = D + 8;    // LDS row stride of a V tile (bf16): rows start in distinct banks
-  constexpr int PS = 17;       // LDS row stride of a P tile (fp32)
+  constexpr int NC = D / 16;
+  constexpr int VS = D + 8;
+  constexpr int PS = 17;
   __shared__ __align__(16) uint16_t vt[4][kTile * VS];
   __shared__ float pt[4][kTile * PS];
   __shared__ float mrg_m[4][kMaxGroup], mrg_l[4][kMaxGroup];
@@ -262,83 +361,9 @@ void attn_segment_kernel(AParams P) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
 
-  // Q rows: query heads h*group + col (rows past the group are zero)
-  bf16x8 qa[KS];
-  {
-    const bool on = col < P.group;
-    const uint16_t* qp = P.q + ((int64_t)j * P.n_q + h * P.group + (on ? col : 0)) * D;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const u32x4 w = on ? *reinterpret_cast<const u32x4*>(qp + 32 * k + 8 * grp)
-                         : u32x4{0u, 0u, 0u, 0u};
-      qa[k] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
   float m[4], l[4];
   f32x4 o[NC];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int koff = h * D;
-  // software pipeline: the K and V rows of the next tile are in flight while this tile is
-  // computed; their page-table entries were fetched one tile earlier still
-  auto load_tile = [&](int64_t row, bf16x8* kb, u32x4* vr) {
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      if (row >= 0) {
-        kb[k] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(P.kpool + row + koff + 32 * k + 8 * grp));
-        vr[k] = *reinterpret_cast<const u32x4*>(P.vpool + row + koff + 32 * k + 8 * grp);
-      } else {
-        kb[k] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vr[k] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  int t0 = t_lo + kTile * wave;
-  int64_t row = t0 + col < t_hi ? row_at(P, t0 + col, page_entry(P, t0 + col, true)) : -1;
-  int32_t pe_next = page_entry(P, t0 + 4 * kTile + col, t0 + 4 * kTile + col < t_hi);
-  bf16x8 kb[KS];
-  u32x4 vraw[KS];
-  load_tile(row, kb, vraw);
-  for (; t0 < t_hi; t0 += 4 * kTile) {
-    const int t1 = t0 + 4 * kTile;
-    const int64_t row_next = t1 + col < t_hi ? row_at(P, t1 + col, pe_next) : -1;
-    bf16x8 kb_n[KS];
-    u32x4 vraw_n[KS];
-    load_tile(row_next, kb_n, vraw_n);
-    pe_next = page_entry(P, t1 + 4 * kTile + col, t1 + 4 * kTile + col < t_hi);
-
-    // S: lane holds query rows 4 grp + r of token col
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], kb[k], sacc, 0, 0, 0);
-    // the V tile goes to LDS (token col, features 32k + 8 grp ..)
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-      *reinterpret_cast<u32x4*>(&vt[wave][col * VS + 32 * k + 8 * grp]) = vraw[k];
-    float s2[4], corr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s2[r] = row >= 0 ? sacc[r] * P.scale : -INFINITY;
-    softmax_step(s2, m, l, corr, &pt[wave][4 * grp * PS + col], PS);
-    if (any_moved(corr)) rescale_rows(o, corr);
-    wave_lds_sync();
-    // O += P V
-    pv_accumulate<false>(o, split_weights(&pt[wave][col * PS + 4 * grp]), &vt[wave][4 * grp * VS + col], VS);
-    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
-    row = row_next;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      kb[k] = kb_n[k];
-      vraw[k] = vraw_n[k];
-    }
-  }
+  attend_tiles<D>(P, j, h, t_lo + kTile * wave, t_hi, 4 * kTile, vt[wave], pt[wave], m, l, o);
 
   // merge the four waves' states (rows 4 grp + r of this lane; all 16 lanes of a row group
   // hold the same m and l): weights exp(m_w - M), outputs summed wave by wave in a fixed order
@@ -385,6 +410,49 @@ void attn_segment_kernel(AParams P) {
     const int64_t orow = (int64_t)g * P.n_q + h * P.group + rw;
     P.part_o[orow * D + f] = M == -INFINITY ? 0.f : mrg_o[rw * D + f] / L;
     if (f == 0) P.part_lse[orow] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
+  }
+}
+
+// attn_rows_kernel<D>: the same segment attention with a block reading whole cache rows:
+// block = (segment, quad of KV heads), wave w takes KV head 4 q + w, and the four waves step
+// through the same 16-token tiles, so every tile's rows are read across all four heads at once
+// rather than as four separate head-wide pieces by four blocks. (A read-only probe over a
+// shuffled paged cache of 1 KB rows streamed 0.76 of 8 TB/s in this order against 0.66 with
+// one head per block.) Each wave holds its head's whole segment state, so the block writes its
+// parts with no merge of the waves. Used when n_kv_heads is a multiple of 4.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void attn_rows_kernel(AParams P) {
+  constexpr int NC = D / 16;
+  constexpr int VS = D + 8;
+  constexpr int PS = 17;
+  __shared__ __align__(16) uint16_t vt[4][kTile * VS];
+  __shared__ float pt[4][kTile * PS];
+
+  const int quads = P.n_kv >> 2;
+  const int g = blockIdx.x / quads;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = 4 * (blockIdx.x - g * quads) + wave;
+  const int j = P.seg_query[g];
+  const AQuery Q = P.queries[j];
+  const int s = g - Q.seg_start;
+  const int t_lo = Q.kv_start + s * P.seg;
+  const int t_hi = min(Q.kv_start + Q.kv_len, t_lo + P.seg);
+  const int col = lane & 15, grp = lane >> 4;
+
+  float m[4], l[4];
+  f32x4 o[NC];
+  attend_tiles<D>(P, j, h, t_lo, t_hi, kTile, vt[wave], pt[wave], m, l, o);
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rw = 4 * grp + r;
+    if (rw >= P.group) continue;
+    const int64_t orow = (int64_t)g * P.n_q + h * P.group + rw;
+    const bool none = m[r] == -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) P.part_o[orow * D + 16 * c + col] = none ? 0.f : o[c][r] / l[r];
+    if (col == 0) P.part_lse[orow] = none ? -INFINITY : m[r] * kLn2 + logf(l[r]);
   }
 }
 
@@ -1069,6 +1137,15 @@ struct APlan {
   size_t seg_off = 0, part_o_off = 0, part_lse_off = 0, total = 0;
 };
 
+// Blocks per key segment of kamera_decode_attention: one per quad of KV heads where
+// attn_rows_kernel runs (GQA/MHA with n_kv_heads a multiple of 4), else one per KV head.
+bool rows_kernel_for(const kamera_model* model) {
+  return model->family == KAMERA_FAMILY_GQA && model->n_kv_heads % 4 == 0;
+}
+int32_t blocks_per_segment(const kamera_model* model) {
+  return rows_kernel_for(model) ? model->n_kv_heads / 4 : model->n_kv_heads;
+}
+
 kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
                                  const kamera_attn_query* queries, int32_t n_queries,
                                  int64_t capacity, APlan* plan) {
@@ -1104,12 +1181,13 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
                   "query %d: tokens [%d, %lld) run past the cache's %lld logical tokens", i,
                   a.kv_start, (long long)a.kv_start + a.kv_len, (long long)capacity);
   }
-  plan->seg = kSegChoices[2];
-  for (int c = 0; c < 3; ++c) {
+  plan->seg = kSegChoices[3];
+  for (int c = rows_kernel_for(model) ? 0 : 1; c < 4; ++c) {
     int64_t blocks = 0;
     for (int32_t i = 0; i < n_queries; ++i)
       blocks += (queries[i].kv_len + kSegChoices[c] - 1) / kSegChoices[c];
-    if (blocks * model->n_kv_heads >= kTargetSegBlocks) {
+    if (blocks * blocks_per_segment(model) >=
+        (rows_kernel_for(model) ? kTargetRowBlocks : kTargetSegBlocks)) {
       plan->seg = kSegChoices[c];
       break;
     }
@@ -1124,7 +1202,7 @@ kamera_status attention_geometry(const kamera_model* model, int32_t n_q_heads,
     for (int k = 0; k < n; ++k) plan->seg_query.push_back(i);
     segs += n;
   }
-  if (segs * model->n_kv_heads > INT32_MAX)
+  if (segs * blocks_per_segment(model) > INT32_MAX)
     return fail(KAMERA_ERR_UNSUPPORTED, "too many attention segments");
   const size_t D = model->head_dim;
   plan->seg_off = round_up(plan->queries.size() * sizeof(AQuery), 16);
@@ -1206,8 +1284,8 @@ kamera_status chunk_attention_geometry(const kamera_model* model, int32_t n_q_he
         b += (chunks[queries[i].first_chunk + c].n_tokens + seg - 1) / seg;
     return b * model->n_kv_heads;
   };
-  plan->seg = kSegChoices[2];
-  for (int c = 0; c < 3; ++c)
+  plan->seg = kSegChoices[3];
+  for (int c = 1; c < 4; ++c)
     if (blocks_at(kSegChoices[c]) >= kTargetSegBlocks) {
       plan->seg = kSegChoices[c];
       break;
@@ -1331,10 +1409,13 @@ kamera_status kamera_decode_attention(const kamera_model* model, const kamera_ca
     if (cache->page_size == (1 << b)) P.page_shift = b;
   P.n_pages = cache->n_pages;
   P.seg = plan.seg;
-  const int64_t seg_blocks = (int64_t)plan.seg_query.size() * model->n_kv_heads;
+  const int64_t seg_blocks = (int64_t)plan.seg_query.size() * blocks_per_segment(model);
   if (seg_blocks > 0) {
     const dim3 grid((unsigned)seg_blocks), block(kThreads);
+    const bool rows_kernel = rows_kernel_for(model);
     if (mla) mla_segment_kernel<<<grid, block, 0, stream>>>(P);
+    else if (rows_kernel && D == 128) attn_rows_kernel<128><<<grid, block, 0, stream>>>(P);
+    else if (rows_kernel) attn_rows_kernel<64><<<grid, block, 0, stream>>>(P);
     else if (D == 128) attn_segment_kernel<128><<<grid, block, 0, stream>>>(P);
     else attn_segment_kernel<64><<<grid, block, 0, stream>>>(P);
     hipError_t e = hipGetLastError();

@@ -133,6 +133,18 @@ def test_decode_attention_head64_group8_dense_odd_pages():
     _run_and_check(s, 0, [(0, 4800), (11, 13), (1000, 1025)], 16, 0.125, seed=4)
 
 
+def test_decode_attention_head64_four_kv_heads():
+    """Whole-row blocks (a quad of KV heads per block) at head_dim 64, page size 8."""
+    s = Setup(D=64, n_kv=4, page_size=8, n_pages=700, n_logical=600, seed=17)
+    _run_and_check(s, 1, RANGES, 12, 0.125)
+
+
+def test_decode_attention_one_kv_head_sixteen_query_heads():
+    """One KV head (a block per head) with the largest query group."""
+    s = Setup(n_kv=1, seed=19)
+    _run_and_check(s, 0, RANGES, 16, 1 / math.sqrt(128))
+
+
 def test_decode_attention_mha_one_head_per_kv():
     s = Setup(n_kv=8, n_pages=64, n_logical=64, seed=5)
     _run_and_check(s, 0, [(0, 1024), (16, 300)], 8, 1 / math.sqrt(128), seed=6)
@@ -237,16 +249,18 @@ def test_state_merge_widths_alignments_and_many_parts(n_parts, rows, D, offset):
 
 def _segment_tokens(ranges, n_kv):
     """The segment length the library picks: the longest of 2048, 1024, 512 that still gives
-    the call 2048 blocks (segments x KV heads)."""
+    the call 2048 blocks (segments x blocks per segment: one per quad of KV heads when
+    n_kv is a multiple of 4, else one per KV head)."""
+    per_segment = n_kv // 4 if n_kv % 4 == 0 else n_kv
     for seg in (2048, 1024, 512):
-        if sum(-(-n // seg) for _, n in ranges) * n_kv >= 2048:
+        if sum(-(-n // seg) for _, n in ranges) * per_segment >= 2048:
             return seg
     return 512
 
 
 def test_many_queries_take_2048_token_segments():
     s = Setup(n_kv=8, n_pages=400, n_logical=350, seed=13)
-    ranges = [((17 * i) % 5000, 1 + (i % 37)) for i in range(250)]
+    ranges = [((17 * i) % 5000, 1 + (i % 37)) for i in range(1010)]
     ranges += [(0, 5000), (1, 4999), (100, 4097), (2047, 2049), (0, 2048), (600, 4000),
                (3, 5597), (0, 5600), (2048, 2048), (4000, 1)]
     assert _segment_tokens(ranges, 8) == 2048
@@ -255,7 +269,7 @@ def test_many_queries_take_2048_token_segments():
 
 def test_mid_size_calls_take_1024_token_segments():
     s = Setup(n_kv=8, n_pages=400, n_logical=350, seed=15)
-    ranges = [(i % 300, 1 + (i % 5)) for i in range(200)]
+    ranges = [(i % 300, 1 + (i % 5)) for i in range(960)]
     ranges += [(i * 37, 4096) for i in range(20)]
     ranges += [(1023, 1025), (5000, 600)]
     assert _segment_tokens(ranges, 8) == 1024
