@@ -25,6 +25,9 @@
 //   compiler for every wave under wave 0's condition (an empty exec mask elsewhere), and an MFMA
 //   still reads its operands then, so the other waves keep their k_rope operand registers at
 //   zero (stale -inf there once turned 0 x -inf into NaN scores).
+// chunk_rows_kernel / chunk_attn_kernel: attention over chunks read in place (relocation
+//   folded into the query, the patch into the scores and values), blocks as the two decode
+//   kernels above.
 // attn_merge_kernel: one block per (query, query head) merges its segments.
 // state_merge_kernel: the same merge over caller-given parts.
 #include <hip/hip_runtime.h>
@@ -1126,6 +1129,311 @@ void chunk_attn_kernel(VParams P) {
   }
 }
 
+// chunk_rows_kernel<D, KMAX>: the same attention over chunks read in place with a block reading
+// whole rows: block = (segment of one chunk, quad of KV heads), wave w takes KV head 4 q + w over
+// every 16-token tile of the segment (as attn_rows_kernel) and does its head's set-up and patch
+// term itself: w = V_K^T q on bf16 MFMA from V_K staged in the wave's LDS, the score operands
+// (q' and w, high and low bf16 parts) held in registers, and at the end o += z V_V^T on bf16
+// MFMA with z cut into three exact bf16 terms (as the P V weights) and V_V staged in the wave's
+// LDS. Used when n_kv_heads is a multiple of 4 and no patch rank exceeds 32.
+template <int D, int KMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void chunk_rows_kernel(VParams P) {
+  static_assert(KMAX == 16 || KMAX == 32, "rank classes of the whole-row kernel");
+  constexpr int KS = D / 32;                 // bf16 k-steps over the features
+  constexpr int PK = 1;                      // bf16 k-steps over the key patch rank
+  constexpr int NC = D / 16;                 // column blocks of o
+  constexpr int NZ = KMAX / 16;              // column blocks of z
+  constexpr int VS = D + 32 * PK + 8;        // LDS row: V row, then the token's U_V row
+  constexpr int PSTR = 17;
+  constexpr int WS = KMAX + 1;               // LDS row stride of w and z (fp32)
+  // One wave's LDS. In the tile loop: its V tile (V rows, then U_V rows) and P tile. In the
+  // set-up and at the end: a factor of the head (V_K, then the head's query rows; V_V at the
+  // end; bf16) and w or z (16 rows x WS, fp32).
+  constexpr int kLoopBytes = kTile * VS * 2 + kTile * PSTR * 4;
+  constexpr int kFactorBytes = D * KMAX * 2 > kMaxGroup * D * 2 ? D * KMAX * 2 : kMaxGroup * D * 2;
+  constexpr int kSetBytes = kFactorBytes + kMaxGroup * WS * 4;
+  constexpr int kWaveBytes = ((kLoopBytes > kSetBytes ? kLoopBytes : kSetBytes) + 15) / 16 * 16;
+  __shared__ __align__(16) uint8_t wbuf[4][kWaveBytes];
+  __shared__ float2 cs[64];
+
+  const int quads = P.n_kv >> 2;
+  const int sidx = blockIdx.x / quads;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = 4 * (blockIdx.x - sidx * quads) + wave;
+  const VSeg S = P.segs[sidx];
+  const VChunk& C = P.chunks[S.chunk];
+  const int j = S.query;
+  const int mk = C.mk, mv = C.mv;
+  const bool vec = C.vec_u != 0;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(wbuf[wave]);
+  float* pt = reinterpret_cast<float*>(wbuf[wave] + kTile * VS * 2);
+  uint16_t* fac = reinterpret_cast<uint16_t*>(wbuf[wave]);
+  float* wz = reinterpret_cast<float*>(wbuf[wave] + kFactorBytes);
+
+  const uint16_t* kh = C.k + h * D;
+  const uint16_t* vh = C.v + h * D;
+  const uint16_t* ukh = mk > 0 ? C.uk + h * C.uk_hs : nullptr;
+  const uint16_t* uvh = mv > 0 ? C.uv + h * C.uv_hs : nullptr;
+  // software pipeline: the next tile's K, V, U_K and U_V rows are in flight while this one
+  // is computed
+  struct Tile {
+    u32x4 k[KS], v[KS], uk[PK], uv[PK];
+  };
+  auto load_tile = [&](int t, Tile& x) {
+    const bool ok = t < S.t_hi;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      x.k[k] = ok ? *reinterpret_cast<const u32x4*>(kh + (int64_t)t * C.k_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+      x.v[k] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)t * C.v_ts + 32 * k + 8 * grp)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uk[s2] = ok && 32 * s2 < mk ? load_u8(ukh + (int64_t)t * mk, 32 * s2 + 8 * grp, mk, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      x.uv[s2] = ok && 32 * s2 < mv ? load_u8(uvh + (int64_t)t * mv, 32 * s2 + 8 * grp, mv, vec)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  };
+  // The set-up's global loads go out together with the first tile's: the phase inputs (pair
+  // tid of the block), the head's query rows as MFMA A operands (query row col, features
+  // 32 k + 8 grp ..; zero past the group) and V_K of the head (16 bytes per lane at a time
+  // when its rows allow).
+  const int R = P.rot_dim;   // at most D <= 2 * kThreads: one pair per thread
+  const int ip = max(0, min(tid, R / 2 - 1));
+  const double inv_in = P.inv_freq && R > 0 ? P.inv_freq[ip] : 0.0;
+  const int sec_in = P.pair_section && R > 0 ? (int)P.pair_section[ip] : 0;
+  const bool qon = col < P.group;
+  const uint16_t* qrow = P.q + ((int64_t)j * P.n_q + h * P.group + (qon ? col : 0)) * D;
+  u32x4 qa[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+    qa[k] = qon ? *reinterpret_cast<const u32x4*>(qrow + 32 * k + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
+  constexpr int kVkPieces = (D * KMAX / 8 + 63) / 64;   // per lane, 16 bytes each
+  const bool vk_vec = mk > 0 && C.vec_v != 0;
+  const uint16_t* vkh = mk > 0 ? C.vk + h * C.vk_hs : nullptr;
+  u32x4 vkp[kVkPieces];
+#pragma unroll
+  for (int q = 0; q < kVkPieces; ++q) {
+    const int idx = lane + 64 * q;
+    vkp[q] = vk_vec && idx < D * mk / 8 ? reinterpret_cast<const u32x4*>(vkh)[idx]
+                                        : u32x4{0u, 0u, 0u, 0u};
+  }
+  Tile cur;
+  load_tile(S.t_lo + col, cur);
+
+  // the chunk's phases (shared by the four heads)
+  if (tid < R / 2) {
+    const double inv = P.inv_freq ? inv_in : pow(P.theta, -2.0 * (double)tid / (double)R);
+    const int sec = P.pair_section ? sec_in : 0;
+    const int64_t d = sec == 0 ? C.delta : (sec == 1 ? C.delta_s1 : C.delta_s2);
+    double sn, cn;
+    sincos((double)d * inv, &sn, &cn);
+    cs[tid] = make_float2((float)cn, (float)sn);
+  }
+  // V_K of the head to the wave's LDS, [feature][rank]
+  if (vk_vec) {
+#pragma unroll
+    for (int q = 0; q < kVkPieces; ++q) {
+      const int idx = lane + 64 * q;
+      if (idx < D * mk / 8) reinterpret_cast<u32x4*>(fac)[idx] = vkp[q];
+    }
+  } else if (mk > 0) {
+    for (int i = lane; i < D * mk; i += 64) fac[i] = vkh[i];
+  }
+  __syncthreads();   // the phases are complete; so is each wave's V_K
+  // w = V_K^T q on v_mfma_f32_16x16x32_bf16 (q and V_K are bf16, so every product is exact;
+  // fp32 sums): rows the query heads, columns the ranks 16 c .. 16 c + 15
+#pragma unroll
+  for (int c = 0; c < NZ; ++c) {
+    if (16 * c >= mk) break;
+    const int r = 16 * c + col;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint16_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = r < mk ? fac[(32 * k + 8 * grp + e) * mk + r] : 0;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[k]),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+    // lane (grp, col): query heads 4 grp + i, rank r
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i < P.group && r < mk) wz[(4 * grp + i) * WS + r] = acc[i];
+  }
+  wave_lds_sync();   // V_K is read; w is complete
+  // the head's query rows to the wave's LDS in V_K's place (bf16, rows of D)
+  if (qon) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      *reinterpret_cast<u32x4*>(&fac[col * D + 32 * k + 8 * grp]) = qa[k];
+  }
+  wave_lds_sync();
+
+  // score operands of lane (col, grp), in registers: query row col, features 32 k + 8 grp + e,
+  // turned by -delta, then w of the same row, each as high and low bf16 parts
+  bf16x8 qh[KS], ql[KS], wh[PK], wl[PK];
+  {
+    const bool inter = P.layout != KAMERA_ROPE_HALF_SPLIT;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = 32 * k + 8 * grp + e;
+        float v = 0.f;
+        if (qon) {
+          v = __uint_as_float((uint32_t)fac[col * D + f] << 16);
+          if (f < R) {
+            int pair, other;
+            bool first;
+            if (inter) {
+              pair = f >> 1;
+              first = (f & 1) == 0;
+              other = first ? f + 1 : f - 1;
+            } else {
+              first = f < R / 2;
+              pair = first ? f : f - R / 2;
+              other = first ? f + R / 2 : f - R / 2;
+            }
+            const float y = __uint_as_float((uint32_t)fac[col * D + other] << 16);
+            const float2 r = cs[pair];
+            // R(-delta): first' = x c + y s, second' = x c - y s (x: own, y: partner)
+            v = first ? v * r.x + y * r.y : v * r.x - y * r.y;
+          }
+        }
+        x[e] = v;
+      }
+      split8(x, &qh[k], &ql[k]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * s2 + 8 * grp + e;
+        x[e] = qon && r < mk ? wz[col * WS + r] : 0.f;
+      }
+      split8(x, &wh[s2], &wl[s2]);
+    }
+  }
+  wave_lds_sync();   // the query rows and w are read: the tiles may take the wave's LDS
+
+  float m[4], l[4];
+  f32x4 o[NC], z[NZ];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NZ; ++c) z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Tile nxt;
+  for (int t0 = S.t_lo; t0 < S.t_hi; t0 += kTile) {
+    const int t = t0 + col;
+    const bool valid = t < S.t_hi;
+    load_tile(t + kTile, nxt);
+    // S = Q' K^T + W U_K^T: lane holds query rows 4 grp + r of token col
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, cur.k[k]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[k], kb, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[k], kb, sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2) {
+      if (32 * s2 < mk) {
+        const bf16x8 ub = __builtin_bit_cast(bf16x8, cur.uk[s2]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh[s2], ub, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl[s2], ub, sacc, 0, 0, 0);
+      }
+    }
+    // V rows and U_V rows of the tile to LDS (token col)
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      *reinterpret_cast<u32x4*>(&vt[col * VS + 32 * k + 8 * grp]) = cur.v[k];
+#pragma unroll
+    for (int s2 = 0; s2 < PK; ++s2)
+      *reinterpret_cast<u32x4*>(&vt[col * VS + D + 32 * s2 + 8 * grp]) = cur.uv[s2];
+    float s2[4], corr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s2[r] = valid ? sacc[r] * P.scale : -INFINITY;
+    softmax_step(s2, m, l, corr, &pt[4 * grp * PSTR + col], PSTR);
+    if (any_moved(corr)) {
+      rescale_rows(o, corr);
+      rescale_rows(z, corr);
+    }
+    wave_lds_sync();
+    // o += P V and z += P U_V (the U_V rows follow the V rows of the tile)
+    {
+      const PSplit w = split_weights(&pt[col * PSTR + 4 * grp]);
+      const uint16_t* vcol = &vt[4 * grp * VS + col];
+      pv_accumulate<true>(o, w, vcol, VS);
+      pv_accumulate<true>(z, w, vcol + D, VS, (mv + 15) / 16);
+    }
+    wave_lds_sync();   // the next tile rewrites this wave's P and V tiles
+    cur = nxt;
+  }
+
+  // o += z V_V^T on v_mfma_f32_16x16x16_bf16: z (rows the query heads, columns the ranks) cut
+  // into three exact bf16 terms through LDS, V_V of the head staged [feature][rank]; z is zero
+  // at ranks past mv (the U_V loads are zero there)
+  if (mv > 0) {
+    const uint16_t* vvh = C.vv + h * C.vv_hs;
+    if (C.vec_v != 0) {
+      for (int i = lane; i < D * mv / 8; i += 64)
+        reinterpret_cast<u32x4*>(fac)[i] = reinterpret_cast<const u32x4*>(vvh)[i];
+    } else {
+      for (int i = lane; i < D * mv; i += 64) fac[i] = vvh[i];
+    }
+#pragma unroll
+    for (int c = 0; c < NZ; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wz[(4 * grp + i) * WS + 16 * c + col] = z[c][i];
+    wave_lds_sync();
+#pragma unroll
+    for (int kb = 0; kb < NZ; ++kb) {
+      if (16 * kb >= mv) break;
+      float zw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zw[e] = wz[col * WS + 16 * kb + 4 * grp + e];
+      const PSplit zs = split_weights(zw);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        s16x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * kb + 4 * grp + e;
+          b[e] = r < mv ? (short)fac[(16 * c + col) * mv + r] : (short)0;
+        }
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(zs.lo, b, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(zs.mid, b, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(zs.hi, b, o[c], 0, 0, 0);
+      }
+    }
+  }
+  // this wave's state is the segment's for head h: normalised output and lse
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rw = 4 * grp + r;
+    if (rw >= P.group) continue;
+    const int64_t orow = (int64_t)sidx * P.n_q + h * P.group + rw;
+    const bool none = m[r] == -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) P.part_o[orow * D + 16 * c + col] = none ? 0.f : o[c][r] / l[r];
+    if (col == 0) P.part_lse[orow] = none ? -INFINITY : m[r] * kLn2 + logf(l[r]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------------------
@@ -1219,6 +1527,8 @@ struct VPlan {
   std::vector<VSeg> segs;
   std::vector<AQuery> queries;   // seg_start / n_segs per query, for attn_merge_kernel
   int32_t seg = KAMERA_ATTN_SEGMENT;
+  int32_t mmax = 0;      // the largest patch rank of a chunk with tokens
+  bool rows = false;     // chunk_rows_kernel (else chunk_attn_kernel)
   size_t freq_off = 0, sec_off = 0, chunk_off = 0, seg_off = 0, query_off = 0;
   size_t part_o_off = 0, part_lse_off = 0, total = 0;
 };
@@ -1276,17 +1586,25 @@ kamera_status chunk_attention_geometry(const kamera_model* model, int32_t n_q_he
       return fail(KAMERA_ERR_INVALID_ARGUMENT, "query %d: chunks [%d, %lld) outside [0, %d)", i,
                   a.first_chunk, (long long)a.first_chunk + a.n_chunks, n_chunks);
   }
+  // the kernel: whole-row blocks (a quad of KV heads) where the heads come in quads and no
+  // patch rank exceeds 32
+  plan->mmax = 0;
+  for (int32_t i = 0; i < n_chunks; ++i)
+    if (chunks[i].n_tokens > 0)
+      plan->mmax = std::max(plan->mmax, std::max(chunks[i].patch[0].m, chunks[i].patch[1].m));
+  plan->rows = model->n_kv_heads % 4 == 0 && plan->mmax <= 32;
+  const int64_t per_seg = plan->rows ? model->n_kv_heads / 4 : model->n_kv_heads;
   // segment length: as kamera_decode_attention, segments never cross a chunk
   auto blocks_at = [&](int seg) {
     int64_t b = 0;
     for (int32_t i = 0; i < n_queries; ++i)
       for (int32_t c = 0; c < queries[i].n_chunks; ++c)
         b += (chunks[queries[i].first_chunk + c].n_tokens + seg - 1) / seg;
-    return b * model->n_kv_heads;
+    return b * per_seg;
   };
   plan->seg = kSegChoices[3];
-  for (int c = 1; c < 4; ++c)
-    if (blocks_at(kSegChoices[c]) >= kTargetSegBlocks) {
+  for (int c = plan->rows ? 0 : 1; c < 4; ++c)
+    if (blocks_at(kSegChoices[c]) >= (plan->rows ? kTargetRowBlocks : kTargetSegBlocks)) {
       plan->seg = kSegChoices[c];
       break;
     }
@@ -1304,7 +1622,7 @@ kamera_status chunk_attention_geometry(const kamera_model* model, int32_t n_q_he
     plan->queries[i] = AQuery{0, (int32_t)std::min<int64_t>(tokens, INT32_MAX), first,
                               (int32_t)plan->segs.size() - first};
   }
-  if ((int64_t)plan->segs.size() * model->n_kv_heads > INT32_MAX)
+  if ((int64_t)plan->segs.size() * per_seg > INT32_MAX)
     return fail(KAMERA_ERR_UNSUPPORTED, "too many attention segments");
   const size_t D = model->head_dim;
   plan->freq_off = 0;
@@ -1540,14 +1858,17 @@ kamera_status kamera_chunk_attention(const kamera_model* model, int32_t layer,
   P.group = n_q_heads / model->n_kv_heads;
   P.rot_dim = model->rope_dim;
   P.layout = model->rope_layout;
-  const int64_t seg_blocks = (int64_t)plan.segs.size() * model->n_kv_heads;
+  const int64_t seg_blocks =
+      (int64_t)plan.segs.size() * (plan.rows ? model->n_kv_heads / 4 : model->n_kv_heads);
   if (seg_blocks > 0) {
     const dim3 grid((unsigned)seg_blocks), block(kThreads);
-    int mmax = 0;
-    for (int32_t i = 0; i < n_chunks; ++i)
-      if (chunks[i].n_tokens > 0)
-        mmax = std::max(mmax, std::max(chunks[i].patch[0].m, chunks[i].patch[1].m));
-    if (D == 128) {
+    const int mmax = plan.mmax;
+    if (plan.rows) {
+      if (D == 128 && mmax <= 16) chunk_rows_kernel<128, 16><<<grid, block, 0, stream>>>(P);
+      else if (D == 128) chunk_rows_kernel<128, 32><<<grid, block, 0, stream>>>(P);
+      else if (mmax <= 16) chunk_rows_kernel<64, 16><<<grid, block, 0, stream>>>(P);
+      else chunk_rows_kernel<64, 32><<<grid, block, 0, stream>>>(P);
+    } else if (D == 128) {
       if (mmax <= 16) chunk_attn_kernel<128, 16><<<grid, block, 0, stream>>>(P);
       else if (mmax <= 32) chunk_attn_kernel<128, 32><<<grid, block, 0, stream>>>(P);
       else chunk_attn_kernel<128, 64><<<grid, block, 0, stream>>>(P);

@@ -197,6 +197,23 @@ def test_partial_rotary_mha_rank_zero_and_rank64():
     _run(case, 1, 1 / math.sqrt(128), seed=6)
 
 
+def test_whole_row_blocks_head64_interleaved_unaligned_ranks():
+    """Four KV heads (one whole-row block per segment) at head_dim 64 with ranks that are not
+    multiples of 8 (the U rows and factors go through the 2-byte paths)."""
+    specs = [(257, 100, 0, 32), (33, 7, 12, 20), (16, 0, 8, 8), (400, -2000, 32, 5)]
+    case = Case(4, 64, 64, oracle.INTERLEAVED, 1e4, specs, [(0, 4), (1, 2), (3, 1)], G=3,
+                seed=11)
+    _run(case, 0, 0.125, seed=12)
+
+
+def test_whole_row_blocks_eight_heads_rank32_partial_rotary():
+    """Eight KV heads (two whole-row blocks per segment), rank-32 class, partial rotary."""
+    specs = [(500, 65536, 32, 24), (123, -65536, 1, 32), (1100, 4096, 17, 0)]
+    case = Case(8, 128, 64, oracle.HALF_SPLIT, 1e4, specs, [(0, 2), (1, 1), (2, 1)], G=2,
+                seed=13)
+    _run(case, 1, 1 / math.sqrt(128), seed=14)
+
+
 def test_frequency_table_and_sections():
     sec = np.repeat(np.array([0, 1, 2], np.uint8), [16, 24, 24])
     table = np.sort(10.0 ** np.random.default_rng(3).uniform(-6, 0, 64))[::-1].copy()
