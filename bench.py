@@ -628,9 +628,9 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
            if l.startswith("{") and '"metric"' in l][-1]
     da = rec["decode_attention"]
     rows = _read_csv(sorted(d.glob("**/kt_kernel_stats.csv"))[0])
-    seg = [r for r in rows if "attn_segment_kernel" in r["Name"]]
+    seg = [r for r in rows if "attn_segment_kernel" in r["Name"] or "attn_rows_kernel" in r["Name"]]
     mrg = [r for r in rows if "attn_merge_kernel" in r["Name"]]
-    chk = [r for r in rows if "chunk_attn_kernel" in r["Name"]]
+    chk = [r for r in rows if "chunk_attn_kernel" in r["Name"] or "chunk_rows_kernel" in r["Name"]]
     mla = [r for r in rows if "mla_segment_kernel" in r["Name"]]
     ca = rec.get("chunk_attention")
     dm = rec.get("decode_attention_mla")
@@ -642,7 +642,7 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
               "| kernel | calls | avg us | GB/s (K+V bytes / avg) | of 8 TB/s |", "|---|---|---|---|---|"]
     for r in seg + mrg:
         avg = float(r["AverageNs"])
-        gb = da["kv_bytes"] / avg if "segment" in r["Name"] else float("nan")
+        gb = da["kv_bytes"] / avg if "merge" not in r["Name"] else float("nan")
         lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {avg / 1e3:.1f} | "
                      f"{gb:.0f} | {gb / HBM_PEAK_GBPS:.3f} |")
     if dm and mla:
