@@ -139,6 +139,12 @@ def test_decode_attention_head64_four_kv_heads():
     _run_and_check(s, 1, RANGES, 12, 0.125)
 
 
+def test_decode_attention_twelve_kv_heads_full_groups():
+    """Three quads of KV heads per segment, 16 query heads per KV head (the largest group)."""
+    s = Setup(D=64, n_kv=12, page_size=16, n_pages=320, n_logical=300, seed=21)
+    _run_and_check(s, 0, RANGES, 192, 0.125, seed=22)
+
+
 def test_decode_attention_one_kv_head_sixteen_query_heads():
     """One KV head (a block per head) with the largest query group."""
     s = Setup(n_kv=1, seed=19)

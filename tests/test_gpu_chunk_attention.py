@@ -214,6 +214,14 @@ def test_whole_row_blocks_eight_heads_rank32_partial_rotary():
     _run(case, 1, 1 / math.sqrt(128), seed=14)
 
 
+def test_whole_row_blocks_twelve_heads_full_groups_interleaved():
+    """Three quads of KV heads, 16 query heads per KV head, rank-16 class with odd ranks."""
+    specs = [(130, 777, 16, 3), (47, -9, 5, 16), (260, 1 << 20, 0, 11)]
+    case = Case(12, 64, 64, oracle.INTERLEAVED, 1e4, specs, [(0, 3), (1, 1), (2, 1)], G=16,
+                seed=15)
+    _run(case, 0, 0.125, seed=16)
+
+
 def test_frequency_table_and_sections():
     sec = np.repeat(np.array([0, 1, 2], np.uint8), [16, 24, 24])
     table = np.sort(10.0 ** np.random.default_rng(3).uniform(-6, 0, 64))[::-1].copy()
