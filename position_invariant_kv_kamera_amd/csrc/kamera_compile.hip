@@ -19,8 +19,9 @@
 //             wide MLA latent): sums the partials into G where there are several, then block
 //             power iteration X <- orth(G X) from a fixed +-1 start, G X on fp32 MFMA. orth() is
 //             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64, X = Y L^-T
-//             (up to rank 32: L in registers and forward substitution with fp64 sums; ranks 48
-//             and 64: both in 16 x 16 blocks on fp64 MFMA, orth_blocked). Columns that
+//             (heads up to 128 wide at rank up to 32: L in registers and forward substitution
+//             with fp64 sums; rank 48 and 64, and every rank of the wide heads: both in 16 x 16
+//             blocks on fp64 MFMA, chol_blocked and subst_blocked). Columns that
 //             collapse (Y rank deficient) are re-seeded between rounds
 //             and zero after the last; a final orth() of X alone restores orthonormality to
 //             fp32 rounding;
@@ -1079,16 +1080,14 @@ __device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead
 
 // ---------------------------------------------------------------------------------------
 // subspace (wide heads, 256 .. 512 features: the MLA latent): one block of 4 waves per unit.
-// LDS: xs [D][mp+1] fp32, holding X, then Y = G X, then X = orth(Y) (odd row stride: a thread's
-// own row is conflict-free), ss [MMAX][MMAX+1] fp64 S and then L: 76 KB for the 512-wide latent
-// at rank 32, so two blocks share a CU.
+// LDS: xs [D][MMAX+1] fp32, holding X, then Y = G X, then X = orth(Y) (odd row stride), ss
+// fp64 S and then L (packed lower): 76 KB for the 512-wide latent at rank 32, so two blocks
+// share a CU.
 //   Y = G X    fp32 MFMA 16x16x4, wave w takes row blocks w, w + 4, ... (G read from the
 //              workspace, 16 bytes of a row per lane per K block, next block in flight); Y
 //              stays in the accumulators until every wave has read X, then replaces it;
-//   S = Y^T Y  fp64 MFMA 16x16x4 over all D rows, the lower tiles dealt to the waves;
-//   L L^T = S  by wave 0 (cholesky_wave);
-//   X = Y L^-T forward substitution in place, one row per thread at a time (fp64 sums of the
-//              fp32 x already formed, as in the per-wave form).
+//   X = orth(Y) orth_wide: S = Y^T Y, the blocked Cholesky and the blocked substitution, all
+//              on fp64 MFMA.
 // ---------------------------------------------------------------------------------------
 
 template <int DMAX, int MMAX>
@@ -1156,182 +1155,6 @@ __device__ void gx_mfma_block(const float* G, float* xs_generic, int D, int mp) 
   }
 }
 
-// X = orth(Y) (Cholesky QR, fp64). Collapsed columns give x_j = 0, or a fresh +-1 column when
-// reseed_round >= 0 (the next round's G X spreads it); a collapsed column has l_aj = 0 below
-// its pivot, so a reseeded x_a adds nothing to the columns after it.
-template <int MMAX>
-__device__ __forceinline__ void orth_block(float* xs, double* ss, double* inv, int* dead,
-                                           int D, int m, int mp, int reseed_round) {
-  // the square S/L layout and the register factorisation without a separate scratch column
-  static_assert(MMAX <= 32, "wide heads take ranks up to 32");
-  constexpr int SS = MMAX + 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int XS = mp + 1;
-  {
-    // S = Y^T Y: tile (a, b), a >= b, on v_mfma_f64_16x16x4f64; lane 16k + i takes
-    // Y[r + k][16 a + i] and Y[r + k][16 b + i]; its output register v is row 16 a + k + 4v,
-    // column 16 b + i. Four accumulators over rotating groups of four rows.
-    const int li = lane & 15, kk = lane >> 4;
-    const int nt = (m + 15) / 16;
-    const int ntiles = nt * (nt + 1) / 2;
-    for (int q = wave; q < ntiles; q += kThreads / 64) {
-      int ta = 0;
-      while ((ta + 1) * (ta + 2) / 2 <= q) ++ta;
-      const int tb = q - ta * (ta + 1) / 2;
-      const float* ya = xs + kk * XS + 16 * ta + li;
-      const float* yb = xs + kk * XS + 16 * tb + li;
-      f64x4 sa[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sa[c] = f64x4{0.0, 0.0, 0.0, 0.0};
-      for (int r = 0; r < D; r += 16) {   // D is a multiple of 128
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sa[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[(r + 4 * c) * XS],
-                                                       (double)yb[(r + 4 * c) * XS], sa[c], 0, 0, 0);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-        if (row < m && col <= row) ss[row * SS + col] = (sa[0][v] + sa[1][v]) + (sa[2][v] + sa[3][v]);
-      }
-    }
-  }
-  __syncthreads();
-  if (wave == 0) cholesky_wave<MMAX>(ss, inv, dead, m);
-  __syncthreads();
-  // X = Y L^-T in place: x_ij = (y_ij - sum_{a<j} x_ia l_ja) / l_jj; the row's earlier x are
-  // already in place, y_ij is read before x_ij replaces it (columns from m on stay zero)
-  for (int i = tid; i < D; i += kThreads) {
-    float* xr = xs + i * XS;
-    for (int j = 0; j < m; ++j) {
-      const double* lj = ss + j * SS;
-      double p0 = 0.0, p1 = 0.0;
-      int a = 0;
-      for (; a + 2 <= j; a += 2) {
-        p0 += (double)xr[a] * lj[a];
-        p1 += (double)xr[a + 1] * lj[a + 1];
-      }
-      if (a < j) p0 += (double)xr[a] * lj[a];
-      float v = (float)(((double)xr[j] - (p0 + p1)) * inv[j]);
-      if (reseed_round >= 0 && dead[j]) v = seed_value(i, j, reseed_round + 1);
-      xr[j] = v;
-    }
-  }
-  __syncthreads();
-}
-
-template <typename T, int DMAX, int MMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void subspace_kernel(CParams P) {
-  __shared__ __align__(16) float xs[DMAX * (MMAX + 1)];
-  __shared__ double ss[MMAX * (MMAX + 1)];
-  __shared__ double inv[MMAX];
-  __shared__ int dead[MMAX];
-
-  const int e = find_entry(P, blockIdx.x);
-  const CJob& J = P.jobs[P.job_of[e]];
-  const int unit = blockIdx.x - P.starts[e];
-  const int layer = unit / J.heads, head = unit - layer * J.heads;
-  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
-  const int XS = mp + 1;
-
-  // G: the single partial, or the sum of the partial tiles assembled in the workspace
-  const float* G;
-  if (J.gfull < 0) {
-    G = P.ws + J.gpart + (int64_t)unit * D * D;
-  } else {
-    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
-    const int te = J.te, te2 = te * te;
-    for (int pair = 0; pair < J.n_pairs; ++pair) {
-      int bi, bj;
-      pair_tiles(pair, J.nb, &bi, &bj);
-      const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
-      const float4* part4 = reinterpret_cast<const float4*>(part);
-#pragma unroll 4
-      for (int i4 = tid; i4 < te2 / 4; i4 += kThreads) {
-        float4 v = part4[i4];
-#pragma unroll 4
-        for (int s = 1; s < J.splits; ++s) {
-          const float4 w = part4[(int64_t)s * (te2 / 4) + i4];
-          v.x += w.x;
-          v.y += w.y;
-          v.z += w.z;
-          v.w += w.w;
-        }
-        const int ii = (4 * i4) / te, jj = 4 * i4 - ii * te;
-        *reinterpret_cast<float4*>(gf + (bi * te + ii) * D + bj * te + jj) = v;
-        if (bi != bj) {
-          const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) gf[(bj * te + jj + c) * D + bi * te + ii] = vv[c];
-        }
-      }
-    }
-    __syncthreads();
-    G = gf;
-  }
-
-  for (int idx = tid; idx < D * mp; idx += kThreads) {
-    const int i = idx / mp, j = idx - i * mp;
-    xs[i * XS + j] = j < m ? seed_value(i, j, 0) : 0.f;
-  }
-  __syncthreads();
-
-  for (int round = 0; round < P.n_iter; ++round) {
-    gx_mfma_block<DMAX, MMAX>(G, xs, D, mp);
-    __syncthreads();
-    orth_block<MMAX>(xs, ss, inv, dead, D, m, mp, round);
-  }
-  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
-  orth_block<MMAX>(xs, ss, inv, dead, D, m, mp, -1);
-
-  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
-  float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
-  for (int idx = tid; idx < D * mp; idx += kThreads) {
-    const int i = idx / mp, j = idx - i * mp;
-    const float v = xs[i * XS + j];
-    xg[idx] = v;
-    if (j < m) store_elem(V + i * m + j, v);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
-// wave-synchronous. MP = mp exactly. Per wave in LDS:
-//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
-//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
-//   lm  (layout lidx) fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
-//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also a 2 MP-double scratch
-//       for the register Cholesky's published column.
-// Lane l owns rows l and l + 64.
-// ---------------------------------------------------------------------------------------
-
-__device__ __forceinline__ void wave_global_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Rank classes above 32 (48 and 64): orth() in 16 x 16 blocks, the products on fp64 MFMA
-// 16x16x4 (lane 16 k + i supplies A[i][k] and B[k][i] and receives rows k + 4 v, column i of
-// the product in register v). S and then L live in one packed lower triangle stored by columns
-// (lcol), and after the factorisation each diagonal block holds T_KK = L_KK^-1 in place of
-// L_KK, which is what the substitution needs.
-//   S = Y^T Y        all lower tiles at once, four rows of Y per step (fp32 products exact in
-//                    fp64, fp64 sums);
-//   L L^T = S        right-looking by block column K: the 16 x 16 diagonal block is factored by
-//                    lanes 0..15 in registers (lane i holds row i; the pivot and the published
-//                    column come by readlane), T_KK is formed alongside (column a by lane a,
-//                    right-looking on the same published entries), then the panel
-//                    L_IK = S_IK T_KK^T and the trailing update S_IJ -= L_IK L_JK^T run on MFMA;
-//   X = Y L^-T       by block column J and 16-row tile: Z^T = Y_J^T - L_J,<J X_<J^T (the
-//                    transposed product leaves Z in exactly the A-operand layout), then
-//                    X_J = Z T_JJ^T.
-// A collapsed column (what is left of its pivot at most kDeadTol times its starting value) gets
-// 1 / l_jj = 0: its row of T and its column of L below the pivot are zero, so, as in the
-// unblocked form, its x (re-seeded between rounds, zero after the last) feeds no later column.
-// The blocked form computes the same quantities as the unblocked one in another order of
-// fp64 additions.
 template <int MP>
 __device__ __forceinline__ int lcol(int r, int c) { return c * MP - c * (c - 1) / 2 + (r - c); }
 
@@ -1346,43 +1169,15 @@ __device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
+// L L^T = S by 16 x 16 block columns, by one whole wave: lm holds S (lower, lcol layout) on
+// entry and L on exit, with each diagonal block holding T_KK = L_KK^-1 instead of L_KK; inv
+// and dead as in the unblocked form (a collapsed column gets 1 / l_jj = 0).
 template <int MP>
-__device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv, int* dead, int D,
-                                             int m, int reseed_round) {
-  static_assert(MP == 48 || MP == 64, "blocked orth() serves the rank classes 48 and 64");
-  constexpr int BS = MP + 4, NB = MP / 16, NT = NB * (NB + 1) / 2;
+__device__ __forceinline__ void chol_blocked(double* lm, double* inv, int* dead, int m) {
+  static_assert(MP % 16 == 0 && MP <= 64, "16-column blocks, rank classes up to 64");
+  constexpr int NB = MP / 16;
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, kk = lane >> 4;
-  const int nrt = D / 16;   // D is a multiple of 32
-
-  // S = Y^T Y, lower tiles (a, b <= a)
-  {
-    f64x4 st[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) st[t] = f64x4{0.0, 0.0, 0.0, 0.0};
-    for (int r = 0; r < D; r += 4) {
-      const float* yr = buf + (r + kk) * BS + li;
-      double y[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) y[b] = (double)yr[16 * b];
-      int t = 0;
-#pragma unroll
-      for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b <= a; ++b, ++t) st[t] = mfma_f64(y[a], y[b], st[t]);
-    }
-    int t = 0;
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int b = 0; b <= a; ++b, ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 16 * a + kk + 4 * v, col = 16 * b + li;
-          if (row >= col) lm[lcol<MP>(row, col)] = st[t][v];
-        }
-  }
-  wave_lds_sync();
   if (lane < MP) inv[lane] = lm[lcol<MP>(lane, lane)];   // starting diagonal (dead-column test)
   wave_lds_sync();
 
@@ -1412,7 +1207,6 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
       double rq = __builtin_amdgcn_rsq(d);
       rq = __builtin_fma(0.5 * rq, __builtin_fma(-d * rq, rq, 1.0), rq);
       rq = __builtin_fma(0.5 * rq, __builtin_fma(-d * rq, rq, 1.0), rq);
-      const double ljj = live ? d * rq : 0.0;
       const double iv = live ? rq : 0.0;
       dbits |= dk ? 1u << j : 0u;
       const double lij = li > j ? sv[0] * iv : 0.0;
@@ -1481,10 +1275,21 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
     }
   }
 
-  // X = Y L^-T in place, block column J, two 16-row tiles at a time
+}
+
+// X = Y L^-T in place for the 16-row tiles rt_first, rt_first + 1, rt_first + rt_step, ... below
+// rt_end (rows of bs floats in buf), by one whole wave, from chol_blocked's factor: per block
+// column J, Z^T = Y_J^T - L_J,<J X_<J^T, then X_J = Z T_JJ^T, two row tiles at a time.
+template <int MP>
+__device__ __forceinline__ void subst_blocked(float* buf, int bs, const double* lm, const int* dead,
+                                              int m, int rt_first, int rt_end, int rt_step,
+                                              int reseed_round) {
+  constexpr int NB = MP / 16;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, kk = lane >> 4;
 #pragma unroll
   for (int J = 0; J < NB; ++J) {
-    double la[4 * (NB - 1)];   // -L[16 J + li][4 q + kk], q < 4 J
+    double la[NB > 1 ? 4 * (NB - 1) : 1];   // -L[16 J + li][4 q + kk], q < 4 J
 #pragma unroll
     for (int q = 0; q < 4 * J; ++q) la[q] = -lm[lcol<MP>(16 * J + li, 4 * q + kk)];
     double bt[4];               // T_JJ[li][4 s + kk]
@@ -1495,11 +1300,11 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
     }
     const int col = 16 * J + li;   // the output column of this lane
     const bool reseed = reseed_round >= 0 && col < m && dead[col] != 0;
-    for (int rt = 0; rt < nrt; rt += 2) {
+    for (int rt = rt_first; rt < rt_end; rt += rt_step) {
       f64x4 z[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float* yrow = buf + (16 * (rt + h) + li) * BS;
+        const float* yrow = buf + (16 * (rt + h) + li) * bs;
 #pragma unroll
         for (int v = 0; v < 4; ++v) z[h][v] = (double)yrow[16 * J + kk + 4 * v];
       }
@@ -1507,7 +1312,7 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
       for (int q = 0; q < 4 * J; ++q)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          z[h] = mfma_f64(la[q], (double)buf[(16 * (rt + h) + li) * BS + 4 * q + kk], z[h]);
+          z[h] = mfma_f64(la[q], (double)buf[(16 * (rt + h) + li) * bs + 4 * q + kk], z[h]);
       // lane 16 kk + li holds Z[16 rt + li][16 J + kk + 4 v] in register v: A[li][4 v + kk]
       f64x4 x[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
@@ -1521,12 +1326,214 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int r = 16 * (rt + h) + kk + 4 * v;
-            buf[r * BS + col] = reseed ? seed_value(r, col, reseed_round + 1) : (float)x[h][v];
+            buf[r * bs + col] = reseed ? seed_value(r, col, reseed_round + 1) : (float)x[h][v];
           }
       }
     }
     wave_lds_sync();
   }
+}
+
+// X = orth(Y) for the wide heads (Cholesky QR, fp64) in 16 x 16 blocks, X in LDS in rows of
+// MP + 1 floats: S = Y^T Y on fp64 MFMA over all D rows (fp32 products exact in fp64, fp64
+// sums; the lower tiles dealt to the waves) into the packed layout, the blocked Cholesky by
+// wave 0 (chol_blocked), and X = Y L^-T on fp64 MFMA by all four waves (subst_blocked), wave w
+// taking the row-tile pairs 2 w, 2 w + 8, ... . Collapsed columns give x_j = 0, or a fresh
+// +-1 column when reseed_round >= 0 (the next round's G X spreads it). Replaces a form with
+// the factorisation on one wave's scalar registers and the substitution one row per thread:
+// MLA latent compile 18.3 -> 16.2 ms.
+template <int MP>
+__device__ __forceinline__ void orth_wide(float* xs, double* lm, double* inv, int* dead, int D,
+                                          int m, int reseed_round) {
+  static_assert(MP == 16 || MP == 32, "wide heads take ranks up to 32");
+  constexpr int XS = MP + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    const int li = lane & 15, kk = lane >> 4;
+    constexpr int nt = MP / 16;
+    constexpr int ntiles = nt * (nt + 1) / 2;
+    for (int q = wave; q < ntiles; q += kThreads / 64) {
+      int ta = 0;
+      while ((ta + 1) * (ta + 2) / 2 <= q) ++ta;
+      const int tb = q - ta * (ta + 1) / 2;
+      const float* ya = xs + kk * XS + 16 * ta + li;
+      const float* yb = xs + kk * XS + 16 * tb + li;
+      f64x4 sa[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sa[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int r = 0; r < D; r += 16) {   // D is a multiple of 128
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sa[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ya[(r + 4 * c) * XS],
+                                                       (double)yb[(r + 4 * c) * XS], sa[c], 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
+        if (col <= row) lm[lcol<MP>(row, col)] = (sa[0][v] + sa[1][v]) + (sa[2][v] + sa[3][v]);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) chol_blocked<MP>(lm, inv, dead, m);
+  __syncthreads();
+  subst_blocked<MP>(xs, XS, lm, dead, m, 2 * wave, D / 16, 8, reseed_round);
+  __syncthreads();
+}
+
+template <typename T, int DMAX, int MMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void subspace_kernel(CParams P) {
+  __shared__ __align__(16) float xs[DMAX * (MMAX + 1)];
+  __shared__ double ss[MMAX * (MMAX + 1)];
+  __shared__ double inv[MMAX];
+  __shared__ int dead[MMAX];
+
+  const int e = find_entry(P, blockIdx.x);
+  const CJob& J = P.jobs[P.job_of[e]];
+  const int unit = blockIdx.x - P.starts[e];
+  const int layer = unit / J.heads, head = unit - layer * J.heads;
+  const int D = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
+  // X rows in LDS are MMAX + 1 floats whatever mp is (columns from m on stay zero)
+  constexpr int XS = MMAX + 1;
+
+  // G: the single partial, or the sum of the partial tiles assembled in the workspace
+  const float* G;
+  if (J.gfull < 0) {
+    G = P.ws + J.gpart + (int64_t)unit * D * D;
+  } else {
+    float* gf = P.ws + J.gfull + (int64_t)unit * D * D;
+    const int te = J.te, te2 = te * te;
+    for (int pair = 0; pair < J.n_pairs; ++pair) {
+      int bi, bj;
+      pair_tiles(pair, J.nb, &bi, &bj);
+      const float* part = P.ws + J.gpart + (int64_t)(unit * J.n_pairs + pair) * J.splits * te2;
+      const float4* part4 = reinterpret_cast<const float4*>(part);
+#pragma unroll 4
+      for (int i4 = tid; i4 < te2 / 4; i4 += kThreads) {
+        float4 v = part4[i4];
+#pragma unroll 4
+        for (int s = 1; s < J.splits; ++s) {
+          const float4 w = part4[(int64_t)s * (te2 / 4) + i4];
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        const int ii = (4 * i4) / te, jj = 4 * i4 - ii * te;
+        *reinterpret_cast<float4*>(gf + (bi * te + ii) * D + bj * te + jj) = v;
+        if (bi != bj) {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) gf[(bj * te + jj + c) * D + bi * te + ii] = vv[c];
+        }
+      }
+    }
+    __syncthreads();
+    G = gf;
+  }
+
+  for (int idx = tid; idx < D * MMAX; idx += kThreads) {
+    const int i = idx / MMAX, j = idx - i * MMAX;
+    xs[i * XS + j] = j < m ? seed_value(i, j, 0) : 0.f;
+  }
+  __syncthreads();
+
+  for (int round = 0; round < P.n_iter; ++round) {
+    gx_mfma_block<DMAX, MMAX>(G, xs, D, MMAX);
+    __syncthreads();
+    orth_wide<MMAX>(xs, ss, inv, dead, D, m, round);
+  }
+  // last pass on X alone: orthonormal to fp32 rounding, collapsed columns zero
+  orth_wide<MMAX>(xs, ss, inv, dead, D, m, -1);
+
+  T* V = static_cast<T*>(J.V) + layer * J.v_ls + head * J.v_hs;
+  float* xg = P.ws + J.xbase + (int64_t)unit * D * mp;
+  for (int idx = tid; idx < D * mp; idx += kThreads) {
+    const int i = idx / mp, j = idx - i * mp;
+    const float v = xs[i * XS + j];
+    xg[idx] = v;
+    if (j < m) store_elem(V + i * m + j, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
+// wave-synchronous. MP = mp exactly. Per wave in LDS:
+//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
+//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
+//   lm  (layout lidx) fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
+//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also a 2 MP-double scratch
+//       for the register Cholesky's published column.
+// Lane l owns rows l and l + 64.
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void wave_global_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Rank classes above 32 (48 and 64): orth() in 16 x 16 blocks, the products on fp64 MFMA
+// 16x16x4 (lane 16 k + i supplies A[i][k] and B[k][i] and receives rows k + 4 v, column i of
+// the product in register v). S and then L live in one packed lower triangle stored by columns
+// (lcol), and after the factorisation each diagonal block holds T_KK = L_KK^-1 in place of
+// L_KK, which is what the substitution needs.
+//   S = Y^T Y        all lower tiles at once, four rows of Y per step (fp32 products exact in
+//                    fp64, fp64 sums);
+//   L L^T = S        right-looking by block column K: the 16 x 16 diagonal block is factored by
+//                    lanes 0..15 in registers (lane i holds row i; the pivot and the published
+//                    column come by readlane), T_KK is formed alongside (column a by lane a,
+//                    right-looking on the same published entries), then the panel
+//                    L_IK = S_IK T_KK^T and the trailing update S_IJ -= L_IK L_JK^T run on MFMA;
+//   X = Y L^-T       by block column J and 16-row tile: Z^T = Y_J^T - L_J,<J X_<J^T (the
+//                    transposed product leaves Z in exactly the A-operand layout), then
+//                    X_J = Z T_JJ^T.
+// A collapsed column (what is left of its pivot at most kDeadTol times its starting value) gets
+// 1 / l_jj = 0: its row of T and its column of L below the pivot are zero, so, as in the
+// unblocked form, its x (re-seeded between rounds, zero after the last) feeds no later column.
+// The blocked form computes the same quantities as the unblocked one in another order of
+// fp64 additions.
+
+template <int MP>
+__device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv, int* dead, int D,
+                                             int m, int reseed_round) {
+  static_assert(MP == 48 || MP == 64, "blocked orth() serves the rank classes 48 and 64");
+  constexpr int BS = MP + 4, NB = MP / 16, NT = NB * (NB + 1) / 2;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, kk = lane >> 4;
+  const int nrt = D / 16;   // D is a multiple of 32
+
+  // S = Y^T Y, lower tiles (a, b <= a)
+  {
+    f64x4 st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int r = 0; r < D; r += 4) {
+      const float* yr = buf + (r + kk) * BS + li;
+      double y[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) y[b] = (double)yr[16 * b];
+      int t = 0;
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b, ++t) st[t] = mfma_f64(y[a], y[b], st[t]);
+    }
+    int t = 0;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b <= a; ++b, ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * a + kk + 4 * v, col = 16 * b + li;
+          if (row >= col) lm[lcol<MP>(row, col)] = st[t][v];
+        }
+  }
+  wave_lds_sync();
+  chol_blocked<MP>(lm, inv, dead, m);
+  subst_blocked<MP>(buf, BS, lm, dead, m, 0, nrt, 2, reseed_round);
 }
 
 template <int MP>

@@ -283,6 +283,12 @@ def small_cases() -> list[Case]:
              [ChunkSpec(260, 56, 321)], seed=12),
         Case("gqa_f32_rank64", "gqa", "f32", 1, 1, 128, 128, HS, 1e6,
              [ChunkSpec(200, 64, -77)], seed=13),
+        # 512-wide latent heads: the rank-16 class, and ranks 12 and 32 in one launch (the
+        # rank-12 heads then run in the rank-32 class with 20 empty columns)
+        Case("mla_bf16_rank16", "mla", "bf16", 1, 1, 512, 64, HS, 1e4,
+             [ChunkSpec(200, 16, 42)], seed=16, mla_shared_rows=True),
+        Case("mla_bf16_ranks_12_and_32", "mla", "bf16", 1, 1, 512, 64, HS, 1e4,
+             [ChunkSpec(260, 12, 555), ChunkSpec(180, 32, -90)], seed=17),
     ]
 
 
@@ -298,6 +304,9 @@ def degenerate_cases() -> list[Case]:
         # the same at rank 64: 40 tokens leave 24 collapsed columns
         Case("tokens_below_rank64", "gqa", "bf16", 1, 2, 128, 128, HS, 1e6,
              [ChunkSpec(40, 64, 5)], seed=14),
+        # and on 512-wide latent heads at rank 32: 20 tokens leave 12 collapsed columns
+        Case("mla_tokens_below_rank32", "mla", "bf16", 1, 1, 512, 64, HS, 1e4,
+             [ChunkSpec(20, 32, 3)], seed=18),
     ]
 
 

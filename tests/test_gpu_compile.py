@@ -145,7 +145,7 @@ def test_zero_deficit_gives_a_zero_patch():
                 assert np.max(np.abs(g - np.eye(g.shape[0]))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
 
 
-@pytest.mark.parametrize("idx", [1, 2], ids=["rank16", "rank64"])
+@pytest.mark.parametrize("idx", [1, 2, 3], ids=["rank16", "rank64", "mla_rank32"])
 def test_fewer_tokens_than_rank_reconstructs_delta(idx):
     case = cc.degenerate_cases()[idx]
     inputs, items = run(case)
@@ -165,6 +165,21 @@ def test_deterministic_and_independent_of_the_batch():
         for a in (again, pair):
             assert np.array_equal(_bits(items[0].U[ch]), _bits(a[0].U[ch]))
             assert np.array_equal(_bits(items[0].V[ch]), _bits(a[0].V[ch]))
+
+
+def test_wide_heads_independent_of_the_launch_rank_class():
+    """A rank-12 MLA chunk compiles to the same bits alone (rank-16 class) and beside a rank-32
+    chunk (its latent heads then run in the rank-32 class)."""
+    base = cc.Case("mla_alone", "mla", "bf16", 1, 1, 512, 64, oracle.HALF_SPLIT, 1e4,
+                   [cc.ChunkSpec(260, 12, 555)], seed=17)
+    inputs, items = run(base)
+    both = cc.Case(**{**base.__dict__, "name": "mla_pair",
+                      "chunks": base.chunks + [cc.ChunkSpec(180, 32, -90)]})
+    extra = cc.build(cc.Case(**{**both.__dict__, "seed": 98}))
+    _, pair = run(both, [inputs[0], extra[1]])
+    for ch in range(2):
+        assert np.array_equal(_bits(items[0].U[ch]), _bits(pair[0].U[ch]))
+        assert np.array_equal(_bits(items[0].V[ch]), _bits(pair[0].V[ch]))
 
 
 def test_compiled_patch_restores_the_conditioned_kv():
