@@ -18,10 +18,9 @@
 //   subspace  one wave per head (widths up to 128) or one block of four waves per head (the
 //             wide MLA latent): sums the partials into G where there are several, then block
 //             power iteration X <- orth(G X) from a fixed +-1 start, G X on fp32 MFMA. orth() is
-//             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64, X = Y L^-T
-//             (heads up to 128 wide at rank up to 32: L in registers and forward substitution
-//             with fp64 sums; rank 48 and 64, and every rank of the wide heads: both in 16 x 16
-//             blocks on fp64 MFMA, chol_blocked and subst_blocked). Columns that
+//             a Cholesky QR: S = Y^T Y on fp64 MFMA, its Cholesky factor L in fp64, X = Y L^-T,
+//             the factorisation and the substitution in 16 x 16 blocks on fp64 MFMA
+//             (chol_blocked, subst_blocked). Columns that
 //             collapse (Y rank deficient) are re-seeded between rounds
 //             and zero after the last; a final orth() of X alone restores orthonormality to
 //             fp32 rounding;
@@ -67,13 +66,9 @@ __device__ __forceinline__ void split8_bf16(const float* x, bf16x8* hi, bf16x8* 
 }
 
 
-// Subspace iteration: Y = G X on fp32 MFMA (1) or fp32 VALU FMA (0); S = Y^T Y on fp64 MFMA
-// (1) or fp64 VALU FMA (0).
+// Subspace iteration: Y = G X on fp32 MFMA (1) or fp32 VALU FMA (0).
 #ifndef KAMERA_SUBSPACE_MFMA
 #define KAMERA_SUBSPACE_MFMA 1
-#endif
-#ifndef KAMERA_ORTH_MFMA
-#define KAMERA_ORTH_MFMA 1
 #endif
 
 constexpr int kThreads = 256;
@@ -991,92 +986,10 @@ __device__ __forceinline__ float seed_value(int i, int j, int round) {
   return (h & 1u) ? 1.f : -1.f;
 }
 
-// Storage of S and L (lower triangle, fp64) for one unit of rank class MP: square with row
-// stride MP + 1 up to MP = 32 (the register Cholesky uses the strict upper part of row 0 as
-// scratch; lidx), packed by columns above (orth_blocked; half the LDS, so more units fit on a
-// CU).
+// Storage of S and L (lower triangle, fp64) for one unit of rank class MP, packed by columns
+// (lcol).
 template <int MP>
-__host__ __device__ constexpr int lm_size() { return MP <= 32 ? MP * (MP + 1) : MP * (MP + 1) / 2; }
-template <int MP>
-__device__ __forceinline__ int lidx(int r, int c) {
-  static_assert(MP <= 32, "the square layout serves the rank classes up to 32");
-  return r * (MP + 1) + c;
-}
-
-// Cholesky factor of S in place, by one wave (wave-synchronous): lm holds S's lower triangle
-// (layout lidx, doubles) and receives L's; inv = 1 / diag(L), 0 for a collapsed column
-// (what is left of s_jj at most kDeadTol times its starting value), which dead flags.
-template <int MP>
-__device__ __forceinline__ void cholesky_wave(double* lm, double* inv, int* dead, int m) {
-  static_assert(MP % 16 == 0 && MP <= 32, "the rank classes above 32 use orth_blocked");
-  const int lane = threadIdx.x & 63;
-  {
-    // Cholesky, right-looking, in registers: lane l holds row l % MP of S, columns
-    // [CPL (l / MP), CPL (l / MP + 1)). Step j: every lane reads the pivot from its holder
-    // (collapsed when what is left of s_jj is at most kDeadTol times its starting value),
-    // the lanes holding column j scale it and publish it in LDS, then each lane updates its
-    // own part of the trailing matrix: one LDS round trip per step.
-    constexpr int LPR = 64 / MP, CPL = MP / LPR;
-    const int ri = lane % MP, cb = lane / MP, c0 = cb * CPL;
-    double sv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int col = c0 + c;
-      sv[c] = (ri < m && col < m) ? (ri >= col ? lm[lidx<MP>(ri, col)] : lm[lidx<MP>(col, ri)])
-                                  : 0.0;
-    }
-    // the strict upper part of row 0 of the square layout is free until the end
-    double* colj = lm + 1;
-    wave_lds_sync();
-    for (int j = 0; j < MP; ++j) {
-      if (j < m) {
-        const int jc = j % CPL, jb = j / CPL;
-        double pv = 0.0;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          if (c == jc) pv = sv[c];
-        const uint64_t pb = __builtin_bit_cast(uint64_t, pv);
-        const int src = j + MP * jb;
-        const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, src);
-        const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), src);
-        const double d = __builtin_bit_cast(double, ((uint64_t)phi << 32) | plo);
-        const double s0 = lm[lidx<MP>(j, j)];   // s_jj before elimination (lm still holds S)
-        const bool dk = d <= kDeadTol * s0;
-        const double ljj = dk ? 0.0 : sqrt(d);
-        const double iv = dk ? 0.0 : 1.0 / ljj;
-        if (lane == 0) {
-          inv[j] = iv;
-          dead[j] = dk ? 1 : 0;
-        }
-        if (cb == jb) {
-          double v = 0.0;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            if (c == jc) v = sv[c];
-          v = ri == j ? ljj : (ri > j ? v * iv : v);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            if (c == jc) sv[c] = v;
-          colj[ri] = ri > j && ri < m ? v : 0.0;
-        }
-        wave_lds_sync();
-        const double lij = colj[ri];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int col = c0 + c;
-          if (col > j && col <= ri && ri < m) sv[c] -= lij * colj[col];
-        }
-        wave_lds_sync();   // colj is rewritten by the next step
-      }
-    }
-    // L (lower triangle) back to LDS for the forward substitution
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int col = c0 + c;
-      if (ri < m && col <= ri) lm[lidx<MP>(ri, col)] = sv[c];
-    }
-  }
-}
+__host__ __device__ constexpr int lm_size() { return MP * (MP + 1) / 2; }
 
 // ---------------------------------------------------------------------------------------
 // subspace (wide heads, 256 .. 512 features: the MLA latent): one block of 4 waves per unit.
@@ -1460,11 +1373,9 @@ void subspace_kernel(CParams P) {
 // ---------------------------------------------------------------------------------------
 // subspace_wave: widths up to 128, one wave per unit and WPB units per block; every step is
 // wave-synchronous. MP = mp exactly. Per wave in LDS:
-//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y) (forward
-//       substitution row by row: each x_j replaces y_j once x_0 .. x_{j-1} are known);
-//   lm  (layout lidx) fp64: S = Y^T Y (lower), overwritten by its Cholesky factor L (lower);
-//       inv holds 1 / diag(L) (0 for a collapsed column); at rank 64 also a 2 MP-double scratch
-//       for the register Cholesky's published column.
+//   buf [128][MP+4] fp32: X, overwritten by Y = G X, overwritten again by X = orth(Y);
+//   lm  (layout lcol) fp64: S = Y^T Y (lower), overwritten by its blocked Cholesky factor;
+//       inv holds the starting diagonal, dead the collapsed columns.
 // Lane l owns rows l and l + 64.
 // ---------------------------------------------------------------------------------------
 
@@ -1474,7 +1385,7 @@ __device__ __forceinline__ void wave_global_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Rank classes above 32 (48 and 64): orth() in 16 x 16 blocks, the products on fp64 MFMA
+// Every rank class (16 .. 64): orth() in 16 x 16 blocks, the products on fp64 MFMA
 // 16x16x4 (lane 16 k + i supplies A[i][k] and B[k][i] and receives rows k + 4 v, column i of
 // the product in register v). S and then L live in one packed lower triangle stored by columns
 // (lcol), and after the factorisation each diagonal block holds T_KK = L_KK^-1 in place of
@@ -1490,15 +1401,17 @@ __device__ __forceinline__ void wave_global_sync() {
 //                    transposed product leaves Z in exactly the A-operand layout), then
 //                    X_J = Z T_JJ^T.
 // A collapsed column (what is left of its pivot at most kDeadTol times its starting value) gets
-// 1 / l_jj = 0: its row of T and its column of L below the pivot are zero, so, as in the
-// unblocked form, its x (re-seeded between rounds, zero after the last) feeds no later column.
-// The blocked form computes the same quantities as the unblocked one in another order of
-// fp64 additions.
+// 1 / l_jj = 0: its row of T and its column of L below the pivot are zero, so its x (re-seeded
+// between rounds, zero after the last) feeds no later column. The blocked form computes the
+// same quantities as a column-by-column Cholesky QR in another order of fp64 additions; it
+// replaced that form (the factorisation in one wave's registers and the substitution one row
+// per lane, column after column) at every rank: compile of the Qwen2.5-VL-like batch (rank 16)
+// 3.34 -> 3.11 ms, of the MLA batch (its 64-wide k_rope heads at rank 32) 16.4 -> 15.4 ms.
 
 template <int MP>
 __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv, int* dead, int D,
                                              int m, int reseed_round) {
-  static_assert(MP == 48 || MP == 64, "blocked orth() serves the rank classes 48 and 64");
+  static_assert(MP % 16 == 0 && MP <= 64, "rank classes 16 .. 64");
   constexpr int BS = MP + 4, NB = MP / 16, NT = NB * (NB + 1) / 2;
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, kk = lane >> 4;
@@ -1539,100 +1452,7 @@ __device__ __forceinline__ void orth_blocked(float* buf, double* lm, double* inv
 template <int MP>
 __device__ __forceinline__ void orth_wave(float* buf, double* lm, double* inv, int* dead, int D, int m,
                                           int reseed_round) {
-  if constexpr (MP > 32) {
-    orth_blocked<MP>(buf, lm, inv, dead, D, m, reseed_round);
-  } else {
-    constexpr int BS = MP + 4;
-    const int lane = threadIdx.x & 63;
-#if KAMERA_ORTH_MFMA
-    // S = Y^T Y on v_mfma_f64_16x16x4f64, one 16x16 tile (a, b) of S at a time: A = Y^T rows
-    // 16a.., B = Y columns 16b.., both read as the same element pattern (lane 16k + i takes
-    // Y[r + k][16 a + i] and Y[r + k][16 b + i]), four rows of Y per step in two alternating
-    // accumulators. fp32 products are exact in fp64 and the sums are fp64. The fp64 MFMA's output
-    // tile is laid out differently from the fp32 16x16x4 one: lane 16k + i, register v holds row
-    // k + 4v, column i (checked on the device). Tiles a >= b hold the lower triangle, which is
-    // all the factorisation reads.
-    {
-      const int li = lane & 15, kk = lane >> 4;
-      const int nt = (m + 15) / 16;
-      for (int ta = 0; ta < nt; ++ta) {
-        for (int tb = 0; tb <= ta; ++tb) {
-          f64x4 s0 = {0.0, 0.0, 0.0, 0.0}, s1 = {0.0, 0.0, 0.0, 0.0};
-          const float* ya = buf + kk * BS + 16 * ta + li;
-          const float* yb = buf + kk * BS + 16 * tb + li;
-          for (int r = 0; r < D; r += 8) {   // width is a multiple of 32
-            const double a0 = (double)ya[r * BS], b0 = (double)yb[r * BS];
-            const double a1 = (double)ya[(r + 4) * BS], b1 = (double)yb[(r + 4) * BS];
-            s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, s1, 0, 0, 0);
-          }
-          // lane 16k + i holds rows 16 ta + k + 4v, column 16 tb + i
-  #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = 16 * ta + kk + 4 * v, col = 16 * tb + li;
-            if (row < m && col <= row) lm[lidx<MP>(row, col)] = s0[v] + s1[v];
-          }
-        }
-      }
-    }
-#else
-    // S = Y^T Y, lower triangle (fp32 products are exact in fp64)
-    const int npair = m * (m + 1) / 2;
-    for (int q = lane; q < npair; q += 64) {
-      int a = (int)((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
-      while (a * (a + 1) / 2 > q) --a;
-      while ((a + 1) * (a + 2) / 2 <= q) ++a;
-      const int b = q - a * (a + 1) / 2;
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};   // width is a multiple of 32
-  #pragma unroll 2
-      for (int r = 0; r < D; r += 4) {
-  #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          acc[k] += (double)buf[(r + k) * BS + a] * (double)buf[(r + k) * BS + b];
-      }
-      lm[lidx<MP>(a, b)] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
-#endif
-    wave_lds_sync();
-    cholesky_wave<MP>(lm, inv, dead, m);
-    wave_lds_sync();
-    // X = Y L^-T by forward substitution in place, rows r0 = lane and r1 = lane + 64 together:
-    // x_rj = (y_rj - sum_{a<j} x_ra l_ja) / l_jj. A collapsed column has l_aj = 0 below its
-    // pivot, so a reseeded x_ra adds nothing to the columns after it.
-      const int r0 = lane, r1 = lane + 64;
-      const bool on0 = r0 < D, on1 = r1 < D;
-      float* row0 = buf + r0 * BS;
-      float* row1 = buf + (on1 ? r1 : r0) * BS;
-      for (int j = 0; j < m; ++j) {
-        const double* lj = lm + lidx<MP>(j, 0);
-        double p0[4] = {0.0, 0.0, 0.0, 0.0}, p1[4] = {0.0, 0.0, 0.0, 0.0};
-        int a = 0;
-        for (; a + 4 <= j; a += 4) {
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const double l = lj[a + u];
-            p0[u] += (double)row0[a + u] * l;
-            p1[u] += (double)row1[a + u] * l;
-          }
-        }
-        for (; a < j; ++a) {
-          const double l = lj[a];
-          p0[0] += (double)row0[a] * l;
-          p1[0] += (double)row1[a] * l;
-        }
-        const double s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
-        const double s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-        float v0 = (float)(((double)row0[j] - s0) * inv[j]);
-        float v1 = (float)(((double)row1[j] - s1) * inv[j]);
-        if (reseed_round >= 0 && dead[j]) {
-          v0 = seed_value(r0, j, reseed_round + 1);
-          v1 = seed_value(r1, j, reseed_round + 1);
-        }
-        if (on0) row0[j] = v0;
-        if (on1) row1[j] = v1;
-      }
-    wave_lds_sync();
-  }
+  orth_blocked<MP>(buf, lm, inv, dead, D, m, reseed_round);
 }
 
 #if KAMERA_SUBSPACE_MFMA
