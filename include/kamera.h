@@ -436,7 +436,9 @@ kamera_status kamera_state_merge(int32_t n_parts, int32_t n_rows, int32_t head_d
  * layout, frequency table, sections), up to 16 query heads per KV head, patch ranks m in
  * [0, 64] per channel. Canonical rows, q and their strides must be 16-byte aligned.
  * Precision: the turned query and V_K^T q are fp32, split into two bf16 terms each for bf16
- * MFMA (products exact, fp32 sums); softmax and P V as in kamera_decode_attention. */
+ * MFMA (products exact, fp32 sums); softmax and P V as in kamera_decode_attention; the value
+ * patch term (sum_t p_t U_V(t)) V_V^T with exact products and fp32 sums. Chunks are cut into
+ * segments as in kamera_decode_attention (segments never cross a chunk). */
 typedef struct kamera_attn_chunk {
   int32_t n_tokens;
   int32_t reserved0;             /* 0 */
