@@ -336,6 +336,28 @@ class MlaSetup:
         return np.concatenate([lat, rope], axis=1), lat
 
 
+def check_mla_query(q64, K, V, n, scale, out, lse, j):
+    """One MLA query (q64 [n_q, 576], rows K [n, 576] and V [n, 512] in fp64) against the
+    oracle under the derived tolerance; returns the worst error / tolerance."""
+    o, l = att.decode_attention(q64, K, V, scale)
+    if K.shape[0] == 0:
+        assert np.all(out == 0) and np.all(np.isneginf(lse)), f"query {j}: empty"
+        return 0.0
+    sc = scale * q64 @ K.T
+    eps = (2 * (576 + 4) * U * att.score_bounds(q64, K, scale).max(axis=1)
+           + 2 * U * np.abs(sc).max(axis=1))
+    w = np.exp(sc - sc.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    c = 64 + -(-max(n, 1) // 16)
+    otol = (2 * eps + c * U)[:, None] * (w @ np.abs(V))
+    ltol = eps + c * U * (1 + np.abs(l))
+    err = np.abs(out - o)
+    assert np.all(err <= otol + 1e-30), (j, float((err / (otol + 1e-30)).max()))
+    lerr = np.abs(lse - l)
+    assert np.all(lerr <= ltol), (j, float((lerr / ltol).max()))
+    return max(float((err / (otol + 1e-30)).max()), float((lerr / ltol).max()))
+
+
 def _run_mla(s, layer, ranges, n_q, scale, seed):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
@@ -350,23 +372,7 @@ def _run_mla(s, layer, ranges, n_q, scale, seed):
     worst = 0.0
     for j, (a, n) in enumerate(ranges):
         K, V = s.kv(layer, a, n)
-        o, l = att.decode_attention(q64[j], K, V, scale)
-        if K.shape[0] == 0:
-            assert np.all(out[j] == 0) and np.all(np.isneginf(lse[j])), f"query {j}: empty"
-            continue
-        sc = scale * q64[j] @ K.T
-        eps = (2 * (576 + 4) * U * att.score_bounds(q64[j], K, scale).max(axis=1)
-               + 2 * U * np.abs(sc).max(axis=1))
-        w = np.exp(sc - sc.max(axis=1, keepdims=True))
-        w /= w.sum(axis=1, keepdims=True)
-        c = 64 + -(-max(n, 1) // 16)
-        otol = (2 * eps + c * U)[:, None] * (w @ np.abs(V))
-        ltol = eps + c * U * (1 + np.abs(l))
-        err = np.abs(out[j] - o)
-        assert np.all(err <= otol + 1e-30), (j, float((err / (otol + 1e-30)).max()))
-        lerr = np.abs(lse[j] - l)
-        assert np.all(lerr <= ltol), (j, float((lerr / ltol).max()))
-        worst = max(worst, float((err / (otol + 1e-30)).max()), float((lerr / ltol).max()))
+        worst = max(worst, check_mla_query(q64[j], K, V, n, scale, out[j], lse[j], j))
     print(f"[attn-mla] worst error / tolerance {worst:.3g}", flush=True)
 
 
