@@ -341,7 +341,7 @@ __device__ __forceinline__ void attend_tiles(const AParams& P, int j, int h, int
   }
 }
 
-// Compiled for 3 waves per SIMD: 151 VGPRs at D = 128, no spills (the unconstrained choice,
+// Compiled for 3 waves per SIMD: 160 VGPRs at D = 128, no spills (the unconstrained choice,
 // 184 registers at 2 waves per SIMD, streamed ~12 % slower; 4 waves spill).
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
