@@ -274,7 +274,7 @@ def test_full_size_mla_chunk_sampled_heads():
 
 def test_rank64_chunk_sampled_heads():
     """Rank 64 at the MHA reorder workload's per-head geometry (4096 tokens, 32 heads, the
-    register factorisation of rank 64): every head orthonormal, eight sampled heads checked
+    blocked factorisation of rank 64): every head orthonormal, eight sampled heads checked
     against the oracle."""
     case = cc.full_rank64_case()
     inputs, items = run(case)

@@ -111,3 +111,30 @@ def test_orbit_with_sections_per_ordering():
         _check(case, inp, items, rope=rope)
     finally:
         cc.oracle_rope = orig
+
+
+def test_orbit_rank64_at_the_full_head_geometry_sampled_heads():
+    """The orbit at the MHA reorder workload's per-head geometry and rank (4096 tokens, 32
+    heads x 128, interleaved RoPE, rank 64, three orderings, as the benchmark's orbit leg), on
+    one layer: every head's V orthonormal, sampled heads of both channels against the oracle."""
+    case = cc.Case("orbit_rank64_full_heads", "gqa", "bf16", 1, 32, 128, 128, oracle.INTERLEAVED,
+                   1e4, [cc.ChunkSpec(4096, 64, 0)], seed=44)
+    deltas = [0, 4096, 8192]
+    inp = cc.build_orbit(case, deltas)
+    items = _orbit_items(case, inp)
+    print(f"[orbit] case={case.name} members={len(deltas)}", flush=True)
+    kb.run_orbit_compile(model_of(case), items, n_iter=case.n_iter)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for ch in range(2):
+        U, V = outputs(case, items, 0, ch)
+        assert np.all(np.isfinite(U)) and np.all(np.isfinite(V))
+        g = np.einsum("lhfr,lhfs->lhrs", V, V)
+        assert np.max(np.abs(g - np.eye(64))) <= 2 * 2.0 ** -8 * 1.02 + 2.0 ** -20
+        for h in [0, 31] + [int(x) for x in rng.integers(32, size=2)]:
+            e = cc.expected_orbit(case, inp, ch, 0, h)
+            r = cc.check_head(U[0, h], V[0, h], e, case.dtype)
+            worst = max(worst, r.patch_excess, r.proj_excess)
+            assert r.ok, (case.name, ch, h, r)
+    print(f"[orbit] {case.name}: worst excess {worst:.3g}", flush=True)
