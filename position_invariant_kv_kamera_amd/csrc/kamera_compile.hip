@@ -103,6 +103,7 @@ struct alignas(16) CJob {
   int32_t member_off, n_members;   // this job's orderings in the member table
   int32_t gperm;   // 1: G is stored with its rows and columns permuted (gram_stream_kernel)
   int32_t gsplit;  // 1: G by gram_split_kernel (128-wide bf16 heads, natural order)
+  int32_t ptok;    // tokens per block of the streamed projection (a multiple of 16)
 };
 
 struct CParams {
@@ -1771,10 +1772,13 @@ __host__ __device__ inline size_t stream_lds_bytes(int width, int mp, bool bf16)
               : (size_t)width * stream_sv(width, mp) * sizeof(float);
 }
 
-#ifndef KAMERA_PROJ_TOKENS
-#define KAMERA_PROJ_TOKENS 512
-#endif
-constexpr int kStreamTokens = KAMERA_PROJ_TOKENS;   // tokens per block (512: 8 tiles per wave)
+// Tokens per block of the streamed projection: the longest of 2048, 1024 and 512 that still
+// gives the launch kProjMinBlocks blocks, each job's tokens cut into equal 16-token multiples
+// (long blocks stage X in LDS fewer times; measured on 2 chunks of the rank-64 MHA batch:
+// 512 tokens 9.73 ms, 1024 9.48, 2048 9.40; the Qwen2.5-VL-like batch, 7168 heads of 1296
+// tokens, kept 512: one 1296-token block per head was 1.7 % slower).
+constexpr int kStreamTokenCaps[3] = {2048, 1024, 512};
+constexpr int64_t kProjMinBlocks = 16384;
 
 // A finished 16-token tile of U held by one lane (its 4 column blocks x 4 rows) until it is
 // stored, in the output element type.
@@ -1803,7 +1807,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int e = find_entry(P, blockIdx.x);
   const CJob& J = P.jobs[P.job_of[e]];
   const int local = blockIdx.x - P.starts[e];
-  const int tblocks = (J.n_tokens + kStreamTokens - 1) / kStreamTokens;
+  const int tblocks = (J.n_tokens + J.ptok - 1) / J.ptok;
   const int unit = local / tblocks, tb = local - unit * tblocks;
   const int layer = unit / J.heads, head = unit - layer * J.heads;
   const int W = J.width, m = J.m, mp = J.mp, tid = threadIdx.x;
@@ -1849,7 +1853,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const T* canon = static_cast<const T*>(J.canon) + layer * J.canon_ls + head_off;
   const T* cond0 = static_cast<const T*>(mem[0].cond) + layer * mem[0].cond_ls + head_off;
   T* U = static_cast<T*>(J.U) + layer * J.u_ls + head * J.u_hs;
-  const int t_lo = tb * kStreamTokens, t_hi = min(J.n_tokens, t_lo + kStreamTokens);
+  const int t_lo = tb * J.ptok, t_hi = min(J.n_tokens, t_lo + J.ptok);
   const int ntile = (t_hi - t_lo + 15) / 16;
   const int mine = wave < ntile ? (ntile - wave + 3) / 4 : 0;
   const int total = mine * nslab;
@@ -2235,10 +2239,30 @@ kamera_status plan_compile(const kamera_model& M, const std::vector<ChunkIn>& ch
     L->lds = std::max(L->lds, lds);
     return true;
   };
+  {
+    auto ptok_at = [](int n, int cap) {
+      const int nb = std::max(1, (n + cap - 1) / cap);
+      return std::max(16, ((n + nb - 1) / nb + 15) / 16 * 16);
+    };
+    int cap = kStreamTokenCaps[2];
+    for (int c = 0; c < 3; ++c) {
+      int64_t b = 0;
+      for (const CJob& J : plan->jobs)
+        if (stream_eligible(J, M.rope_layout)) {
+          const int pt = ptok_at(J.n_tokens, kStreamTokenCaps[c]);
+          b += (int64_t)J.n_units * ((J.n_tokens + pt - 1) / pt);
+        }
+      if (b >= env_int("KAMERA_PROJ_MIN_BLOCKS", (int)kProjMinBlocks)) {
+        cap = kStreamTokenCaps[c];
+        break;
+      }
+    }
+    for (CJob& J : plan->jobs) J.ptok = ptok_at(J.n_tokens, cap);
+  }
   for (size_t j = 0; j < plan->jobs.size(); ++j) {
     const CJob& J = plan->jobs[j];
     const bool stream = stream_eligible(J, M.rope_layout);
-    const int tblocks = stream ? (J.n_tokens + kStreamTokens - 1) / kStreamTokens
+    const int tblocks = stream ? (J.n_tokens + J.ptok - 1) / J.ptok
                                : (J.n_tokens + kProjTokens - 1) / kProjTokens;
     const size_t lds = stream ? stream_lds_bytes(J.width, J.mp, M.dtype == KAMERA_DTYPE_BF16) : 0;
     bool ok = add(kGram, J.gsplit ? (J.n_members > 1 ? 6 : 5) : (J.gperm ? 0 : J.te / 32), (int)j,

@@ -182,6 +182,22 @@ def test_wide_heads_independent_of_the_launch_rank_class():
         assert np.array_equal(_bits(items[0].V[ch]), _bits(pair[0].V[ch]))
 
 
+def test_projection_block_length_leaves_the_bits_unchanged(monkeypatch):
+    """U rows are formed token by token, so the streamed projection's tokens per block (512 by
+    default at this size; 2048, cut into equal 16-token multiples, when the block-count floor is
+    lowered) change no bit; 3000 tokens split into two blocks of 1504 there."""
+    case = cc.Case("proj_blocks", "gqa", "bf16", 1, 2, 128, 128, oracle.HALF_SPLIT, 1e6,
+                   [cc.ChunkSpec(3000, 16, 321), cc.ChunkSpec(4096, 32, -77)], seed=19)
+    inputs, items = run(case)
+    check_case(case, inputs, items)
+    monkeypatch.setenv("KAMERA_PROJ_MIN_BLOCKS", "1")
+    _, long_blocks = run(case, inputs)
+    for i in range(2):
+        for ch in range(2):
+            assert np.array_equal(_bits(items[i].U[ch]), _bits(long_blocks[i].U[ch]))
+            assert np.array_equal(_bits(items[i].V[ch]), _bits(long_blocks[i].V[ch]))
+
+
 def test_compiled_patch_restores_the_conditioned_kv():
     """Relocate + compiled patch (kamera_reuse_batch) reproduces KV(B|A): within the rank-m
     residual of the deficit, the patch tolerance and one rounding of the output."""
