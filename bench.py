@@ -463,7 +463,7 @@ def summarize_profile(prof_dir: str, workload: str, command: str, bench_log: str
     p = __import__("position_invariant_kv_kamera_amd.workloads", fromlist=["plan"]).plan(workload)
     ab = algorithmic_bytes(p)["total"]
     lines = [f"# kamera_mfma_kernel on {workload}", "",
-             "Commands (R = repository root on the GPU box):", ""]
+             "Commands (R = repository root on the machine that ran them):", ""]
     lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
     stats = sorted(d.glob("**/kt_kernel_stats.csv"))
     avg_ns = None
@@ -573,7 +573,7 @@ def summarize_compile_profile(prof_dir: str, workload: str, command: str, bench_
                 kinds[k].append(r)
     io = pc["io_bytes"]
     lines = [f"# patch compile on {workload}", "",
-             "Commands (R = repository root on the GPU box):", ""]
+             "Commands (R = repository root on the machine that ran them):", ""]
     lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
     lines += [f"Per compile call: rank {pc['rank']}, {pc['n_iter']} subspace rounds; "
               f"{pc['ms_per_batch']} ms by HIP events in this run "
@@ -634,7 +634,7 @@ def summarize_attention_profile(prof_dir: str, command: str, bench_log: str) -> 
     mla = [r for r in rows if "mla_segment_kernel" in r["Name"]]
     ca = rec.get("chunk_attention")
     dm = rec.get("decode_attention_mla")
-    lines = ["# decode attention (consumer side)", "", "Commands (R = repository root on the GPU box):", ""]
+    lines = ["# decode attention (consumer side)", "", "Commands (R = repository root on the machine that ran them):", ""]
     lines += [f"    {c.strip()}" for c in command.split(";") if c.strip()] + [""]
     lines += [f"Shape: {da['shape']}. Bytes per call: K and V once = {da['kv_bytes'] / 1e9:.3f} GB.",
               f"HIP events in this run: {da['ms_per_call']} ms per call (both kernels) = "

@@ -13,7 +13,7 @@ if str(TESTS) not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
